@@ -1,0 +1,330 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test would fail for a plausible slip in the oracle: a dropped term or
+a wrong operand in the SwiGLU expert, a transposed weight, a wrong softmax
+(not renormalised, not shifted, unscaled), a wrong tie order, a wrong
+permutation key or an off-by-one in the offsets.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from tests import brute
+from workloads import CONFIGS, make_custom_layer, make_layer, to_f64
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _arrays(layer):
+    sh = None
+    if layer.ws_gate is not None:
+        sh = (to_f64(layer.ws_gate), to_f64(layer.ws_up), to_f64(layer.ws_down))
+    return dict(x=to_f64(layer.x), w_router=to_f64(layer.w_router),
+                bias=to_f64(layer.router_bias), k=to_f64(layer.k),
+                w_gate=to_f64(layer.w_gate), w_up=to_f64(layer.w_up),
+                w_down=to_f64(layer.w_down), shared=sh)
+
+
+def _oracle_forward(a, k_max, scale=1.0, tokens=None, k=None, invalid="raise"):
+    return oracle.forward(a["x"], a["w_router"], a["bias"], a["k"] if k is None else k,
+                          k_max, a["w_gate"], a["w_up"], a["w_down"], shared=a["shared"],
+                          routed_scale=scale, tokens=tokens, invalid=invalid)
+
+
+# ---------------------------------------------------------------- golden
+
+def test_hand_worked_example():
+    g = json.load(open(os.path.join(HERE, "golden", "hand_worked_layer.json")))
+    arr = lambda v: np.array(v, dtype=np.float64)
+    out, r = oracle.forward(arr(g["x"]), arr(g["w_router"]), None, np.array(g["k"]), 2,
+                            arr(g["w_gate"]), arr(g["w_up"]), arr(g["w_down"]))
+    assert r["ids"].tolist() == g["expected_ids"]
+    exp_w = [eval(s, {"math": math}) for s in g["expected_weights_expr"]]
+    exp_o = [eval(s, {"math": math}) for s in g["expected_out_expr"]]
+    np.testing.assert_allclose(r["w"], exp_w, rtol=1e-7)   # from fp32 logits 2, 1
+    np.testing.assert_allclose(out[0], exp_o, rtol=1e-7)
+
+
+# ---------------------------------------------------------------- router
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_logits_match_exact_rational(dtype):
+    """fp32(float64 sum) equals the exact rational dot product rounded to
+    float64 then float32, on inputs where the two can only differ by a
+    straddle of probability ~1e-9."""
+    L = make_custom_layer(T=6, d=40, E=5, I=8, k=[1] * 6, dtype=dtype, zipf=1.1, seed=3)
+    x, wr, b = to_f64(L.x), to_f64(L.w_router), to_f64(L.router_bias)
+    got = oracle.router_logits(x, wr, b)
+    for t in range(6):
+        for e in range(5):
+            exact = sum((Fraction(float(x[t, i])) * Fraction(float(wr[e, i]))
+                         for i in range(40)), Fraction(float(b[e])))
+            assert got[t, e] == np.float32(float(exact))
+
+
+def test_topk_matches_rank_counting_with_ties():
+    """Selection and order equal the rank-counting characterisation (fewer
+    than k experts beat the picked one; a tie is won by the lower index),
+    including many exact float32 ties and -0.0 vs +0.0."""
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        E = int(rng.integers(1, 40))
+        levels = rng.integers(0, 4, size=E).astype(np.float32) - 1.5
+        lg = levels.copy()
+        lg[rng.random(E) < 0.1] = np.float32(-0.0)
+        lg[rng.random(E) < 0.1] = np.float32(0.0)
+        for k in range(0, E + 1):
+            got = oracle.select_experts(lg, k).tolist()
+            assert got == brute.brute_select(lg.tolist(), k)
+
+
+def test_weights_are_renormalised_softmax():
+    L = make_custom_layer(T=20, d=64, E=16, I=8, k=list(range(1, 17)) + [3, 5, 7, 16], seed=1)
+    a = _arrays(L)
+    r = oracle.route(a["x"], a["w_router"], None, a["k"], 16, routed_scale=2.5)
+    for t in range(20):
+        s, e = r["tok_off"][t], r["tok_off"][t + 1]
+        sel = r["ids"][s:e]
+        ref = 2.5 * scipy.special.softmax(r["logits"][t, sel].astype(np.float64))
+        np.testing.assert_allclose(r["w"][s:e], ref, rtol=1e-13)
+        # equivalently: the full softmax over E, renormalised to the selected set
+        full = scipy.special.softmax(r["logits"][t].astype(np.float64))
+        np.testing.assert_allclose(r["w"][s:e], 2.5 * full[sel] / full[sel].sum(), rtol=1e-12)
+
+
+def test_silu_matches_library():
+    z = np.linspace(-30, 30, 1001)
+    np.testing.assert_allclose(oracle.silu(z), z * scipy.special.expit(z), rtol=1e-14, atol=1e-300)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+
+
+# ---------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("with_shared", [False, True])
+def test_forward_matches_brute_force(seed, with_shared):
+    rng = np.random.default_rng(seed)
+    T, d, E, I = 5, 8, 4, 6
+    k = rng.integers(0, E + 1, size=T).tolist()
+    L = make_custom_layer(T=T, d=d, E=E, I=I, k=k, I_shared=5 if with_shared else 0,
+                          zipf=0.5, seed=seed)
+    a = _arrays(L)
+    out, r = _oracle_forward(a, E, scale=1.7)
+    sh = None
+    if with_shared:
+        sh = tuple(brute.tolist64(m) for m in a["shared"])
+    bout, bids, bw = brute.brute_layer(brute.tolist64(a["x"]), brute.tolist64(a["w_router"]),
+                                       brute.tolist64(a["bias"]), k,
+                                       brute.tolist64(a["w_gate"]), brute.tolist64(a["w_up"]),
+                                       brute.tolist64(a["w_down"]), shared=sh, scale=1.7)
+    for t in range(T):
+        s, e = r["tok_off"][t], r["tok_off"][t + 1]
+        assert r["ids"][s:e].tolist() == bids[t]
+        np.testing.assert_allclose(r["w"][s:e], bw[t], rtol=1e-12)
+    np.testing.assert_allclose(out, np.array(bout), rtol=1e-10, atol=1e-12)
+
+
+def test_tiny_fp32_workload_matches_brute_force():
+    L = make_layer(CONFIGS["tiny_fp32"].with_(T=4))
+    a = _arrays(L)
+    out, r = _oracle_forward(a, 2)
+    bout, bids, _ = brute.brute_layer(brute.tolist64(a["x"]), brute.tolist64(a["w_router"]), None,
+                                      [2] * 4, brute.tolist64(a["w_gate"]),
+                                      brute.tolist64(a["w_up"]), brute.tolist64(a["w_down"]))
+    assert [r["ids"][2 * t:2 * t + 2].tolist() for t in range(4)] == bids
+    np.testing.assert_allclose(out, np.array(bout), rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- identities
+
+def _dense_moe(a, scale=1.0):
+    """Dense reference in torch float64: softmax over ALL experts, every
+    expert evaluated on every token, weighted sum (the k_t = E limit)."""
+    x = torch.tensor(a["x"])
+    lg = torch.tensor(oracle.router_logits(a["x"], a["w_router"], a["bias"]).astype(np.float64))
+    p = torch.softmax(lg, dim=1) * scale
+    out = torch.zeros_like(x)
+    for e in range(a["w_gate"].shape[0]):
+        g = x @ torch.tensor(a["w_gate"][e]).T
+        u = x @ torch.tensor(a["w_up"][e]).T
+        y = (torch.nn.functional.silu(g) * u) @ torch.tensor(a["w_down"][e]).T
+        out += p[:, e:e + 1] * y
+    return out.numpy()
+
+
+def test_dense_limit_k_equals_E():
+    E = 6
+    L = make_custom_layer(T=7, d=32, E=E, I=16, k=[E] * 7, zipf=1.1, seed=4)
+    a = _arrays(L)
+    out, _ = _oracle_forward(a, E, scale=1.3)
+    np.testing.assert_allclose(out, _dense_moe(a, 1.3), rtol=1e-11, atol=1e-13)
+
+
+def test_k1_is_the_argmax_expert():
+    L = make_custom_layer(T=9, d=32, E=5, I=16, k=[1] * 9, seed=5)
+    a = _arrays(L)
+    out, r = _oracle_forward(a, 1, scale=0.75)
+    lg = oracle.router_logits(a["x"], a["w_router"], None)
+    x = torch.tensor(a["x"])
+    for t in range(9):
+        e = int(np.argmax(lg[t]))          # first maximum = lower index on ties
+        assert r["ids"][t] == e and r["w"][t] == 0.75
+        y = (torch.nn.functional.silu(x[t] @ torch.tensor(a["w_gate"][e]).T)
+             * (x[t] @ torch.tensor(a["w_up"][e]).T)) @ torch.tensor(a["w_down"][e]).T
+        np.testing.assert_allclose(out[t], 0.75 * y.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_neuron_additivity_eq2():
+    """MoE-Prism Eq. (2): the expert output is the sum over intermediate
+    neurons c of a_c(x) times row c of W_down (column c in [out, in] layout)."""
+    L = make_custom_layer(T=3, d=16, E=1, I=10, k=[1] * 3, seed=6)
+    a = _arrays(L)
+    y = oracle.swiglu_expert(a["x"], a["w_gate"][0], a["w_up"][0], a["w_down"][0])
+    acc = np.zeros_like(y)
+    for c in range(10):
+        ac = scipy.special.expit(a["x"] @ a["w_gate"][0][c]) * (a["x"] @ a["w_gate"][0][c]) \
+            * (a["x"] @ a["w_up"][0][c])
+        acc += ac[:, None] * a["w_down"][0][:, c][None, :]
+    np.testing.assert_allclose(y, acc, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("N", [2, 4])
+@pytest.mark.parametrize("contiguous", [True, False])
+def test_split_expert_identity(N, contiguous):
+    """MoE-Prism Eq. (3) plus the expanded linear gate: cut each expert into
+    N equal neuron sets, repeat each router row N times, run k_sub = N*k with
+    routed scaling N: the output equals the unsplit layer (each of the N tied
+    copies gets w_e / N and the sub-experts sum to the expert)."""
+    E, I, d, T = 4, 8, 16, 6
+    k = [1, 2, 3, 4, 2, 1]
+    L = make_custom_layer(T=T, d=d, E=E, I=I, k=k, zipf=0.3, seed=8)
+    a = _arrays(L)
+    base, _ = _oracle_forward(a, E)
+    rng = np.random.default_rng(N)
+    parts = [np.arange(I) if contiguous else rng.permutation(I) for _ in range(E)]
+    Is = I // N
+    sg = np.stack([a["w_gate"][e][parts[e][n * Is:(n + 1) * Is]] for e in range(E) for n in range(N)])
+    su = np.stack([a["w_up"][e][parts[e][n * Is:(n + 1) * Is]] for e in range(E) for n in range(N)])
+    sd = np.stack([a["w_down"][e][:, parts[e][n * Is:(n + 1) * Is]] for e in range(E) for n in range(N)])
+    wr = np.repeat(a["w_router"], N, axis=0)
+    b = np.repeat(a["bias"], N)
+    out, r = oracle.forward(a["x"], wr, b, np.array(k) * N, E * N, sg, su, sd, routed_scale=N)
+    np.testing.assert_allclose(out, base, rtol=1e-12, atol=1e-13)
+    # every selected copy carries exactly the parent's weight / N
+    rb = oracle.route(a["x"], a["w_router"], a["bias"], np.array(k), E)
+    for t in range(T):
+        s, e = r["tok_off"][t], r["tok_off"][t + 1]
+        assert (r["ids"][s:e] // N).tolist() == np.repeat(rb["ids"][rb["tok_off"][t]:rb["tok_off"][t + 1]], N).tolist()
+
+
+def test_split_identity_partial_budget_ties():
+    """k_sub = N*k - 1: the tie among the last expert's N copies is broken to
+    the lower index, so its first N-1 sub-experts run, each at the weight
+    N*exp(l_e)/Z' with Z' the renormaliser over the selected copies."""
+    E, I, d, T, N = 5, 8, 16, 4, 4
+    k = [2, 3, 1, 4]
+    L = make_custom_layer(T=T, d=d, E=E, I=I, k=k, seed=9)
+    a = _arrays(L)
+    Is = I // N
+    sg = a["w_gate"].reshape(E * N, Is, d)
+    su = a["w_up"].reshape(E * N, Is, d)
+    sd = np.stack([a["w_down"][e][:, n * Is:(n + 1) * Is] for e in range(E) for n in range(N)])
+    wr = np.repeat(a["w_router"], N, axis=0)
+    ksub = np.array(k) * N - 1
+    out, _ = oracle.forward(a["x"], wr, None, ksub, E * N, sg, su, sd, routed_scale=N)
+    lg = oracle.router_logits(a["x"], a["w_router"], None).astype(np.float64)
+    for t in range(T):
+        order = oracle.select_experts(lg[t].astype(np.float32), k[t]).tolist()
+        ref = np.zeros(d)
+        z = sum(N * math.exp(lg[t, e]) for e in order[:-1]) + (N - 1) * math.exp(lg[t, order[-1]])
+        for i, e in enumerate(order):
+            nsub = N if i < len(order) - 1 else N - 1
+            for n in range(nsub):
+                y = oracle.swiglu_expert(a["x"][t:t + 1], sg[e * N + n], su[e * N + n], sd[e * N + n])[0]
+                ref += N * math.exp(lg[t, e]) / z * y
+        np.testing.assert_allclose(out[t], ref, rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------- permutation
+
+@pytest.mark.parametrize("cfg", ["qwen3_30b_a3b_decode", "tiny_fp32"])
+def test_permutation_invariants(cfg):
+    c = CONFIGS[cfg]
+    L = make_custom_layer(T=c.T, d=64, E=c.E, I=64, k=make_layer(c.with_(d=64, I=64, T=c.T)).k,
+                          k_max=c.k_max, zipf=c.zipf_bias, seed=11)
+    a = _arrays(L)
+    r = oracle.route(a["x"], a["w_router"], a["bias"], a["k"], c.k_max)
+    p = oracle.permute(r["tok_off"], r["ids"], c.E)
+    A = int(r["tok_off"][-1])
+    assert p["counts"].sum() == A == int(a["k"].sum())
+    assert p["expert_off"][0] == 0 and (np.diff(p["expert_off"]) == p["counts"]).all()
+    tok_of_a = np.repeat(np.arange(c.T), np.diff(r["tok_off"]))
+    order = np.lexsort((tok_of_a, r["ids"]))          # library sort by (expert, token)
+    assert (p["perm_src"] == order).all()
+    assert (p["perm_tok"] == tok_of_a[order]).all()
+    assert (p["inv_perm"][p["perm_src"]] == np.arange(A)).all()
+    assert sorted(p["perm_src"].tolist()) == list(range(A))
+    assert p["n_active"] == len(set(r["ids"].tolist()))
+    for e in range(c.E):
+        seg = p["perm_tok"][p["expert_off"][e]:p["expert_off"][e + 1]]
+        assert (np.diff(seg) > 0).all()
+        assert all(e in r["ids"][r["tok_off"][t]:r["tok_off"][t + 1]] for t in seg)
+
+
+def test_permutation_degenerate():
+    p = oracle.permute(np.zeros(1, np.int64), np.zeros(0, np.int64), 4)
+    assert p["counts"].tolist() == [0] * 4 and p["n_active"] == 0
+    assert p["perm_tok"].size == 0
+    p = oracle.permute(np.array([0, 0, 1, 1]), np.array([3]), 4)
+    assert p["perm_tok"].tolist() == [1] and p["expert_off"].tolist() == [0, 0, 0, 0, 1]
+
+
+# ---------------------------------------------------------------- batch semantics
+
+def test_batch_composition_invariance():
+    """A token's output depends only on its own x and k (no batch-max k)."""
+    L = make_custom_layer(T=12, d=32, E=8, I=16, k=[1, 8, 2, 0, 5, 3, 8, 1, 4, 6, 7, 2],
+                          I_shared=8, seed=12)
+    a = _arrays(L)
+    full, _ = _oracle_forward(a, 8)
+    perm = np.random.default_rng(0).permutation(12)
+    sub, _ = _oracle_forward(a, 8, tokens=perm[:5])
+    np.testing.assert_array_equal(sub, full[perm[:5]])
+    shuffled = dict(a, x=a["x"][perm], k=a["k"][perm])
+    outp, _ = _oracle_forward(shuffled, 8)
+    np.testing.assert_allclose(outp, full[perm], rtol=1e-13, atol=1e-15)
+
+
+def test_invalid_k():
+    L = make_custom_layer(T=4, d=16, E=4, I=8, k=[1, 2, 1, 1], I_shared=4, seed=13)
+    a = _arrays(L)
+    bad = np.array([1, -1, 5, 2])
+    with pytest.raises(ValueError):
+        _oracle_forward(a, 4, k=bad)
+    out, r = _oracle_forward(a, 4, k=bad, invalid="zero")
+    assert r["status"] == 1 and r["k"].tolist() == [1, 0, 0, 2]
+    shared_only = oracle.swiglu_expert(a["x"][1:3], *a["shared"])
+    np.testing.assert_allclose(out[1:3], shared_only, rtol=1e-14)
+
+
+def test_zero_input_ties_to_lowest_index():
+    """x = 0 makes every logit equal the bias; equal biases tie, so the
+    lowest indices win, and SiLU(0) = 0 makes the routed output exactly 0."""
+    L = make_custom_layer(T=3, d=16, E=6, I=8, k=[3, 1, 6], seed=14)
+    a = _arrays(L)
+    a["x"][:] = 0.0
+    out, r = _oracle_forward(a, 6)
+    assert r["ids"].tolist() == [0, 1, 2, 0, 0, 1, 2, 3, 4, 5]
+    np.testing.assert_allclose(r["w"][:3], [1 / 3] * 3, rtol=1e-15)
+    assert not out.any()
+
+
+def test_activated_weight_bytes():
+    assert oracle.activated_weight_bytes(8, 4096, 14336, 2) == 3 * 8 * 4096 * 14336 * 2
