@@ -1,0 +1,263 @@
+"""Benchmark of the MoE layer forward with per-token top-k on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--eager]
+                    [--no-cpu-baseline]
+
+One step = one moe_forward over one batch (router + top-k, histogram/scan/
+permutation, gate/up + SwiGLU, down projection, shared expert if any, weighted
+combine), on a seeded synthetic layer already resident in HBM.  By default the
+step is replayed from a captured HIP graph (the library's launch grids depend
+only on the layer shape, so one graph serves every k mix); --eager times plain
+launches instead.  Prints one JSON line.
+
+Beside the layer throughput it reports, for the dominant kernel (the gate/up
+SwiGLU FFN), the algorithmic bytes (decode) or FLOPs (prefill) per launch over
+its average launch time measured with HIP events on its own stream, against
+the MI355X peak; and the CPU oracle timed on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at mixed per-token k; % HBM roofline (decode) / % MFMA (prefill)"
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 (matrix and vector)
+DEFAULT_WORKLOAD = "mixtral_decode"
+PREFILL = {"subexpert_prefill", "dsv3_prefill"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--eager", action="store_true", help="time plain launches instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="tokens in the CPU-oracle sample (0 = workload default)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_layer_token_amd", "csrc")
+    for f in ("ffn_stream.hip", "common.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """Per-launch HBM bytes of the gate/up kernel from the committed rocprofv3
+    counter runs, or None when absent or taken on other kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(layer, n_tokens: int):
+    """The oracle as it stands, on the first n_tokens of the same batch, with
+    the layer's weights already in host memory."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    from workloads import to_f64
+
+    cfg = layer.cfg
+    tokens = np.arange(min(n_tokens, cfg.T))
+    r = oracle.route(to_f64(layer.x[:len(tokens)]), to_f64(layer.w_router), to_f64(layer.router_bias),
+                     to_f64(layer.k[:len(tokens)]), cfg.k_max, cfg.routed_scale)
+    used = sorted(set(r["ids"].tolist()))
+    host = lambda t: t.float().cpu().numpy()
+    # host copies (fp32, exact) of the experts the sample reaches; unused ones are never read
+    wg = {e: host(layer.w_gate[e]) for e in used}
+    wu = {e: host(layer.w_up[e]) for e in used}
+    wd = {e: host(layer.w_down[e]) for e in used}
+    sh = None
+    if layer.ws_gate is not None:
+        sh = (host(layer.ws_gate), host(layer.ws_up), host(layer.ws_down))
+    x, wr = host(layer.x), host(layer.w_router)
+    b = None if layer.router_bias is None else host(layer.router_bias)
+    k = layer.k.cpu().numpy()
+    threads = max(p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()) \
+        if threadpoolctl.threadpool_info() else 1
+    t0 = time.perf_counter()
+    oracle.forward(x, wr, b, k, cfg.k_max, wg, wu, wd, shared=sh, routed_scale=cfg.routed_scale,
+                   tokens=tokens)
+    dt = time.perf_counter() - t0
+    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {len(tokens)} of {cfg.T} tokens of {cfg.name} "
+                      f"({len(used)} experts reached), float64 numpy oracle, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus above 1 is not supported "
+              "(multi-GPU sharding of the layer is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_token_amd as moe
+    from workloads import CONFIGS, make_layer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe._lib.load()
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] drawing {cfg.name}", file=sys.stderr, flush=True)
+    layer = make_layer(cfg, dev)
+    torch.cuda.synchronize()
+
+    T, d, E, I = cfg.T, cfg.d, cfg.E, cfg.I
+    Is = cfg.I_shared
+    desc = moe.make_desc(T, d, E, I, cfg.k_max, I_shared=Is, dtype=layer.x.dtype,
+                         routed_scale=cfg.routed_scale)
+    ws = moe.alloc_workspace(desc, moe.MOE_OP_FORWARD, dev)
+    out = torch.empty((T, d), dtype=layer.x.dtype, device=dev)
+    stats = torch.empty(E + 2, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    sh = (layer.ws_gate, layer.ws_up, layer.ws_down) if Is else (None, None, None)
+
+    def step():
+        moe.moe_forward(desc, layer.x, layer.w_router, layer.router_bias, layer.k, layer.w_gate,
+                        layer.w_up, layer.w_down, *sh, out, stats, status, ws)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        step()
+    stream.synchronize()
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+    run = graph.replay if graph is not None else step
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            run()
+        stream.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        t_start.record(stream)
+        for _ in range(args.steps):
+            run()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    assert int(status.item()) == 0
+    st = stats.cpu().numpy()
+    n_act, A = int(st[E]), int(st[E + 1])
+    esz = layer.x.element_size()
+
+    # ---- dominant kernel: gate/up SwiGLU FFN, timed alone on its stream ----
+    tok_off = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    ids = torch.empty(T * cfg.k_max, dtype=torch.int32, device=dev)
+    wts = torch.empty(T * cfg.k_max, dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    eoff = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    ptok = torch.empty(T * cfg.k_max, dtype=torch.int32, device=dev)
+    psrc = torch.empty_like(ptok)
+    inv = torch.empty_like(ptok)
+    nact = torch.empty(1, dtype=torch.int32, device=dev)
+    h = torch.empty((T * cfg.k_max, I), dtype=layer.x.dtype, device=dev)
+    with torch.cuda.stream(stream):
+        moe.moe_route(desc, layer.x, layer.w_router, layer.router_bias, layer.k, tok_off, ids, wts, status,
+                      moe.alloc_workspace(desc, moe.MOE_OP_ROUTE, dev))
+        moe.moe_permute(desc, tok_off, ids, counts, eoff, ptok, psrc, inv, nact,
+                        moe.alloc_workspace(desc, moe.MOE_OP_PERMUTE, dev))
+        for _ in range(max(3, args.warmup // 4)):
+            moe.moe_ffn_gateup(desc, layer.x, layer.w_gate, layer.w_up, eoff, ptok, h)
+        k_start = torch.cuda.Event(enable_timing=True)
+        k_end = torch.cuda.Event(enable_timing=True)
+        k_start.record(stream)
+        for _ in range(args.steps):
+            moe.moe_ffn_gateup(desc, layer.x, layer.w_gate, layer.w_up, eoff, ptok, h)
+        k_end.record(stream)
+        torch.cuda.synchronize()
+    k_ms = k_start.elapsed_time(k_end) / args.steps
+    gu_bytes = 2 * n_act * I * d * esz + T * d * esz + A * I * esz   # weights + x rows + H
+    gu_flops = 4.0 * d * I * A
+    if cfg.name in PREFILL:
+        peak = PEAK_BF16_TFLOPS if esz == 2 else PEAK_FP32_TFLOPS
+        ach = gu_flops / (k_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4)}
+    else:
+        ach = gu_bytes / (k_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = "ffn_stream_kernel (gate/up + SwiGLU)"
+    roof["avg_launch_us"] = round(k_ms * 1e3, 2)
+    roof["algorithmic_per_launch"] = gu_flops if cfg.name in PREFILL else gu_bytes
+    roof["traffic"] = measured_traffic(cfg.name)
+
+    # ---- whole layer against its own roofline ----
+    w_bytes = 3 * n_act * d * I * esz
+    all_bytes = w_bytes + 3 * d * Is * esz + E * d * esz + 2 * T * d * esz
+    ffn_flops = 6.0 * d * I * A + 6.0 * d * Is * T
+    layer_s = ms_step * 1e-3
+    layer_info = {"activated_weight_GBps": round(w_bytes / layer_s / 1e9, 1),
+                  "activated_weight_frac_hbm": round(w_bytes / layer_s / 1e9 / PEAK_HBM_GBS, 4),
+                  "all_bytes_GBps": round(all_bytes / layer_s / 1e9, 1),
+                  "ffn_TFLOPs": round(ffn_flops / layer_s / 1e12, 2),
+                  "ffn_frac_mfma": round(ffn_flops / layer_s / 1e12 /
+                                         (PEAK_BF16_TFLOPS if esz == 2 else PEAK_FP32_TFLOPS), 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample or {"mixtral_decode": 64, "qwen3_30b_a3b_decode": 256, "tiny_fp32": 16,
+                                "subexpert_prefill": 64, "dsv3_decode": 16, "dsv3_prefill": 16}[cfg.name]
+        print(f"[bench] timing the CPU oracle on {n} tokens", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(layer, n)
+
+    k_desc = "/".join(str(v) for v in cfg.k_values)
+    rec = {
+        "metric": METRIC,
+        "value": round(T / layer_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if esz == 2 else "f32",
+        "data": "synthetic (seeded Gaussian layer, random-init weights)",
+        "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "I": I, "I_shared": Is,
+                   "k_values": k_desc, "k_max": cfg.k_max, "A": A, "n_active": n_act,
+                   "execution": "eager" if args.eager else "hip_graph", "wall_s": round(wall, 3)},
+        "layer": layer_info,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

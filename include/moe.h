@@ -1,0 +1,227 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer forward with a per-token
+ * routing top-k.
+ *
+ * The problem statement follows the pages: hidden states, a linear router,
+ * stacked SwiGLU experts and an externally supplied per-token budget k_t
+ * (MoE-Prism, arXiv 2510.19366, §I and §III-C1: each request carries its own
+ * routing top-k target, counted in routed experts and excluding shared
+ * experts, §II-B).  The forward is split into the steps a serving stack runs
+ * between attention blocks:
+ *
+ *   moe_route    router logits, top-k_t selection, renormalised softmax weights
+ *   moe_permute  per-expert histogram, exclusive scan, (expert, token) permutation
+ *   moe_ffn      grouped SwiGLU expert FFN over the permuted rows (+ shared expert)
+ *   moe_combine  routing-weight-scaled sum back to token order
+ *   moe_forward  all of the above in one call
+ *
+ * Every entry point is asynchronous on the caller's stream, allocates nothing,
+ * never synchronises and never reads device memory on the host.  Launch grids
+ * depend only on the descriptor, never on the k values or on the routing, so a
+ * captured HIP graph of any entry point replays correctly for any k vector
+ * (MoE-Prism §III-D: k must not become a graph-specialisation dimension).
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ *  - Pointers are device pointers unless stated.  Tensors are dense and
+ *    row-major.  Activation, weight, H, Y and out buffers must be 16-byte
+ *    aligned.  The caller owns every buffer.
+ *  - "ELT" is the element type chosen by desc->dtype: float (MOE_F32) or
+ *    bfloat16 (MOE_BF16, raw 16-bit storage).  x, the router weight, all
+ *    expert weights, H, Y and out use ELT; routing weights are float32;
+ *    indices and counts are int32.
+ *  - Weight layout is the [out, in] convention:
+ *      w_router [E][d], w_gate [E][I][d], w_up [E][I][d], w_down [E][d][I],
+ *      ws_gate [Is][d], ws_up [Is][d], ws_down [d][Is]  (Is = I_shared).
+ *  - A = sum_t k_t is the number of (token, expert) assignments.  Arrays
+ *    indexed by assignment have capacity T * k_max entries; only the first A
+ *    are written.
+ *  - Return value: MOE_OK, or an error from host-side validation (nothing is
+ *    launched then), or MOE_ERR_LAUNCH when a kernel launch failed.
+ *  - Routing is bit-reproducible: logits are the float64 sum of the exact
+ *    products, rounded once to float32; selection and order use the key
+ *    (logit descending, expert index ascending).  -0.0 and +0.0 compare equal.
+ *  - Calls on one stream are ordered; calls that share a workspace must not
+ *    overlap in time.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* descriptor values outside the supported range */
+  MOE_ERR_UNSUPPORTED = 3, /* unknown dtype / path / op */
+  MOE_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+  MOE_ERR_ALIGN = 5,       /* a buffer is not 16-byte aligned (workspace: 256) */
+  MOE_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch */
+} moe_status;
+
+/* FFN execution path.  Both compute the same function. */
+typedef enum {
+  MOE_PATH_AUTO = 0,    /* weight streaming when rows per expert are few, else grouped GEMM */
+  MOE_PATH_STREAM = 1,  /* weight-streaming MFMA kernels (memory-bound decode) */
+  MOE_PATH_GEMM = 2     /* LDS-tiled grouped GEMM on MFMA (compute-bound prefill) */
+} moe_path;
+
+/* Workspace owners, for moe_workspace_size. */
+typedef enum {
+  MOE_OP_ROUTE = 0,
+  MOE_OP_PERMUTE = 1,
+  MOE_OP_FFN = 2,
+  MOE_OP_COMBINE = 3,
+  MOE_OP_FORWARD = 4
+} moe_op;
+
+/* Device status bits written by moe_route / moe_forward. */
+#define MOE_DEV_BAD_K 1  /* some k_t was outside [0, k_max]; it was run as k_t = 0 */
+
+/*
+ * Layer descriptor.  Supported ranges:
+ *   0 <= T, T * k_max < 2^31
+ *   d, I: multiples of 128, 128 <= d, I <= 65536
+ *   1 <= E <= 1024, 1 <= k_max <= E
+ *   I_shared: 0 (no shared expert) or a multiple of 128 up to 65536
+ *   dtype: MOE_F32 or MOE_BF16; path: a moe_path value
+ *   routed_scale: finite (1.0 for the plain renormalised softmax)
+ */
+typedef struct moe_desc {
+  int32_t T;            /* tokens in the batch */
+  int32_t d;            /* hidden size */
+  int32_t E;            /* routed experts */
+  int32_t I;            /* intermediate size of one routed expert */
+  int32_t k_max;        /* upper bound on every k_t */
+  int32_t I_shared;     /* intermediate size of the always-on shared expert, 0 = none */
+  int32_t dtype;        /* moe_dtype */
+  int32_t path;         /* moe_path */
+  float routed_scale;   /* factor applied to the renormalised routing weights */
+} moe_desc;
+
+/* Stream handle: a hipStream_t, or NULL for the null stream. */
+typedef void* moe_stream_t;
+
+/*
+ * Bytes of scratch that entry point `op` needs for `desc` (a multiple of
+ * 256; workspaces must be 256-byte aligned).  MOE_OP_FORWARD covers every
+ * other op as well.  A size of 0 means the op takes no workspace (ws may be
+ * NULL).  Host only.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED.
+ */
+moe_status moe_workspace_size(const moe_desc* desc, int32_t op, size_t* bytes);
+
+/*
+ * Router and per-token top-k (MoE-Prism §III-B2, normalised and scaled router
+ * weights of the selected experts ordered by router probability; §III-C1,
+ * per-request budget).
+ *   x           ELT [T][d]
+ *   w_router    ELT [E][d]
+ *   router_bias float [E], or NULL for none (added to the logits before selection)
+ *   k           int32 [T], per-token budgets
+ *   tok_off     int32 [T+1] out: exclusive prefix sum of the validated k; tok_off[T] = A
+ *   topk_ids    int32 [T*k_max] out: ids of token t at tok_off[t] .. tok_off[t+1]-1,
+ *               best first
+ *   topk_w      float [T*k_max] out: w_j = routed_scale * exp(l_j - l_0) / sum_j' exp(l_j' - l_0)
+ *   dev_status  int32 [1] out, or NULL: MOE_DEV_BAD_K if some k_t < 0 or > k_max
+ *               (such a token is routed to no expert); 0 otherwise
+ *   ws          scratch of moe_workspace_size(MOE_OP_ROUTE) bytes
+ */
+moe_status moe_route(const moe_desc* desc, const void* x, const void* w_router,
+                     const float* router_bias, const int32_t* k, int32_t* tok_off,
+                     int32_t* topk_ids, float* topk_w, int32_t* dev_status,
+                     void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Dispatch metadata: a stable counting sort of the A assignments by
+ * (expert ascending, token ascending).  Deterministic and bit-exact.
+ *   tok_off, topk_ids  from moe_route
+ *   expert_counts int32 [E] out: assignments per expert
+ *   expert_off    int32 [E+1] out: exclusive scan of expert_counts
+ *   perm_tok      int32 [T*k_max] out: token of sorted row p
+ *   perm_src      int32 [T*k_max] out: assignment index tok_off[t]+j of sorted row p
+ *   inv_perm      int32 [T*k_max] out: sorted row of assignment a
+ *   n_active      int32 [1] out: experts with at least one assignment
+ *                 (the activated experts whose weights a batch loads; METRO
+ *                 reading notes, arXiv 2512.09277, Q1)
+ *   ws            scratch of moe_workspace_size(MOE_OP_PERMUTE) bytes
+ */
+moe_status moe_permute(const moe_desc* desc, const int32_t* tok_off, const int32_t* topk_ids,
+                       int32_t* expert_counts, int32_t* expert_off, int32_t* perm_tok,
+                       int32_t* perm_src, int32_t* inv_perm, int32_t* n_active,
+                       void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Grouped SwiGLU expert FFN over the permuted rows (MoE-Prism §III-B1,
+ * Eq. (1)): for expert e and sorted row p in [expert_off[e], expert_off[e+1]),
+ *   H[p] = SiLU(x[perm_tok[p]] . w_gate[e]^T) * (x[perm_tok[p]] . w_up[e]^T)
+ *   y_perm[p] = H[p] . w_down[e]^T
+ * with float32 accumulation; H is kept in ELT.  With a shared expert
+ * (I_shared > 0) the same FFN runs on every token with ws_* into y_shared.
+ *   y_perm    ELT [T*k_max][d] out (rows >= A untouched)
+ *   y_shared  ELT [T][d] out; ignored (may be NULL) when I_shared == 0
+ *   ws        scratch of moe_workspace_size(MOE_OP_FFN) bytes (holds H)
+ * The per-expert row counts are read on the device.
+ */
+moe_status moe_ffn(const moe_desc* desc, const void* x, const void* w_gate, const void* w_up,
+                   const void* w_down, const void* ws_gate, const void* ws_up,
+                   const void* ws_down, const int32_t* expert_off, const int32_t* perm_tok,
+                   void* y_perm, void* y_shared, void* ws, size_t ws_bytes,
+                   moe_stream_t stream);
+
+/*
+ * The two halves of moe_ffn's routed part, one kernel launch each, so that a
+ * caller can place or time them separately.
+ *   moe_ffn_gateup: h ELT [T*k_max][I] out, H of the rows above.
+ *   moe_ffn_down:   y_perm ELT [T*k_max][d] out from h.
+ * `ws`: scratch of moe_workspace_size(MOE_OP_FFN) bytes (may be shared with
+ * moe_ffn's; h must not alias it).
+ */
+moe_status moe_ffn_gateup(const moe_desc* desc, const void* x, const void* w_gate,
+                          const void* w_up, const int32_t* expert_off, const int32_t* perm_tok,
+                          void* h, void* ws, size_t ws_bytes, moe_stream_t stream);
+moe_status moe_ffn_down(const moe_desc* desc, const void* h, const void* w_down,
+                        const int32_t* expert_off, void* y_perm, void* ws, size_t ws_bytes,
+                        moe_stream_t stream);
+
+/*
+ * Weighted combine back to token order:
+ *   out[t] = sum_{j < k_t} topk_w[tok_off[t]+j] * y_perm[inv_perm[tok_off[t]+j]]
+ *            (+ y_shared[t] when y_shared != NULL)
+ * summed in float32 in ascending j, rounded once to ELT.  A token with
+ * k_t = 0 gets y_shared[t] (or 0).
+ *   out  ELT [T][d] out
+ */
+moe_status moe_combine(const moe_desc* desc, const void* y_perm, const void* y_shared,
+                       const int32_t* tok_off, const float* topk_w, const int32_t* inv_perm,
+                       void* out, moe_stream_t stream);
+
+/*
+ * The whole layer: route, permute, FFN (+ shared expert) and combine.
+ *   out        ELT [T][d] out
+ *   stats      int32 [E+2] out, or NULL: expert_counts[E], n_active, A
+ *   dev_status int32 [1] out, or NULL: as in moe_route
+ *   ws         scratch of moe_workspace_size(MOE_OP_FORWARD) bytes; it also
+ *              holds the routing and permutation arrays of the call
+ */
+moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router,
+                       const float* router_bias, const int32_t* k, const void* w_gate,
+                       const void* w_up, const void* w_down, const void* ws_gate,
+                       const void* ws_up, const void* ws_down, void* out, int32_t* stats,
+                       int32_t* dev_status, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Static description of a status code.  Never NULL. */
+const char* moe_status_str(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,145 @@
+"""MI355X-native MoE layer forward with a per-token routing top-k.
+
+Thin Python binding over the C ABI of libmoe_mi355x.so (include/moe.h).  The
+functions below only marshal arguments: torch tensors supply device memory and
+the current HIP stream; every step of the layer runs in the HIP kernels.  If
+the library has not been built, importing works but every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import (MOE_BF16, MOE_DEV_BAD_K, MOE_F32, MOE_OP_COMBINE, MOE_OP_FFN,  # noqa: F401
+                   MOE_OP_FORWARD, MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_PATH_AUTO, MOE_PATH_GEMM,
+                   MOE_PATH_STREAM, moe_desc)
+
+__all__ = [
+    "MoeError", "make_desc", "workspace_size", "alloc_workspace", "moe_route", "moe_permute",
+    "moe_ffn", "moe_ffn_gateup", "moe_ffn_down", "moe_combine", "moe_forward", "forward",
+    "library_path",
+]
+
+_DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+_PATHS = {"auto": MOE_PATH_AUTO, "stream": MOE_PATH_STREAM, "gemm": MOE_PATH_GEMM}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        lib = _lib.load()
+        msg = lib.moe_status_str(status).decode()
+        super().__init__(f"{fn}: {_lib.STATUS_NAMES.get(status, status)} ({msg})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def make_desc(T: int, d: int, E: int, I: int, k_max: int, *, I_shared: int = 0,
+              dtype=torch.bfloat16, path: str = "auto", routed_scale: float = 1.0) -> moe_desc:
+    return moe_desc(T, d, E, I, k_max, I_shared, _DTYPES[dtype], _PATHS[path], routed_scale)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoeError(fn, status)
+
+
+def workspace_size(desc: moe_desc, op: int = MOE_OP_FORWARD) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_workspace_size", _lib.load().moe_workspace_size(ctypes.byref(desc), op, ctypes.byref(n)))
+    return n.value
+
+
+def alloc_workspace(desc: moe_desc, op: int = MOE_OP_FORWARD, device="cuda") -> Optional[torch.Tensor]:
+    n = workspace_size(desc, op)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def moe_route(desc, x, w_router, router_bias, k, tok_off, topk_ids, topk_w, dev_status, ws,
+              stream=None) -> None:
+    _check("moe_route", _lib.load().moe_route(
+        ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(k), _ptr(tok_off),
+        _ptr(topk_ids), _ptr(topk_w), _ptr(dev_status), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_permute(desc, tok_off, topk_ids, expert_counts, expert_off, perm_tok, perm_src, inv_perm,
+                n_active, ws, stream=None) -> None:
+    _check("moe_permute", _lib.load().moe_permute(
+        ctypes.byref(desc), _ptr(tok_off), _ptr(topk_ids), _ptr(expert_counts), _ptr(expert_off),
+        _ptr(perm_tok), _ptr(perm_src), _ptr(inv_perm), _ptr(n_active), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
+
+
+def moe_ffn(desc, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, expert_off, perm_tok, y_perm,
+            y_shared, ws, stream=None) -> None:
+    _check("moe_ffn", _lib.load().moe_ffn(
+        ctypes.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(ws_gate),
+        _ptr(ws_up), _ptr(ws_down), _ptr(expert_off), _ptr(perm_tok), _ptr(y_perm), _ptr(y_shared),
+        _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_ffn_gateup(desc, x, w_gate, w_up, expert_off, perm_tok, h, ws=None, stream=None) -> None:
+    _check("moe_ffn_gateup", _lib.load().moe_ffn_gateup(
+        ctypes.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(expert_off), _ptr(perm_tok),
+        _ptr(h), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_ffn_down(desc, h, w_down, expert_off, y_perm, ws=None, stream=None) -> None:
+    _check("moe_ffn_down", _lib.load().moe_ffn_down(
+        ctypes.byref(desc), _ptr(h), _ptr(w_down), _ptr(expert_off), _ptr(y_perm), _ptr(ws),
+        _nbytes(ws), _stream(stream)))
+
+
+def moe_combine(desc, y_perm, y_shared, tok_off, topk_w, inv_perm, out, stream=None) -> None:
+    _check("moe_combine", _lib.load().moe_combine(
+        ctypes.byref(desc), _ptr(y_perm), _ptr(y_shared), _ptr(tok_off), _ptr(topk_w),
+        _ptr(inv_perm), _ptr(out), _stream(stream)))
+
+
+def moe_forward(desc, x, w_router, router_bias, k, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                out, stats, dev_status, ws, stream=None) -> None:
+    _check("moe_forward", _lib.load().moe_forward(
+        ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(k), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(out), _ptr(stats),
+        _ptr(dev_status), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: Optional[torch.Tensor],
+            k: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+            shared: Optional[Sequence[torch.Tensor]] = None, *, k_max: int, routed_scale: float = 1.0,
+            path: str = "auto", ws: Optional[torch.Tensor] = None, stream=None):
+    """Allocate the outputs (and a workspace unless given) and run moe_forward.
+    Returns (out [T, d], stats int32 [E+2] = counts, n_active, A, dev_status int32 [1])."""
+    T, d = x.shape
+    E, I, _ = w_gate.shape
+    Is = shared[0].shape[0] if shared is not None else 0
+    desc = make_desc(T, d, E, I, k_max, I_shared=Is, dtype=x.dtype, path=path,
+                     routed_scale=routed_scale)
+    if ws is None:
+        ws = alloc_workspace(desc, MOE_OP_FORWARD, x.device)
+    out = torch.empty((T, d), dtype=x.dtype, device=x.device)
+    stats = torch.empty(E + 2, dtype=torch.int32, device=x.device)
+    status = torch.empty(1, dtype=torch.int32, device=x.device)
+    sg, su, sd = shared if shared is not None else (None, None, None)
+    moe_forward(desc, x, w_router, router_bias, k, w_gate, w_up, w_down, sg, su, sd, out, stats,
+                status, ws, stream)
+    return out, stats, status

@@ -1,0 +1,67 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// bfloat16 is carried as raw 16-bit storage everywhere outside MFMA operands.
+typedef uint16_t bf16_t;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// float32 -> bfloat16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  __device__ __forceinline__ static float to_f32(float v) { return v; }
+  __device__ __forceinline__ static float from_f32(float v) { return v; }
+};
+template <> struct Elt<bf16_t> {
+  __device__ __forceinline__ static float to_f32(bf16_t v) { return bf16_to_f32(v); }
+  __device__ __forceinline__ static bf16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+// One 16x16 MFMA tile step.  EPV = elements of K each lane supplies per
+// instruction; a 16-byte load holds LOAD_ELEMS elements.
+//  bf16: v_mfma_f32_16x16x32_bf16 (8 K-elements per lane, 32 per instruction)
+//  fp32: v_mfma_f32_16x16x4_f32   (1 K-element per lane, 4 per instruction)
+// A operand: lane l supplies row (l % 16); B operand: column (l % 16); both
+// supply the same K indices, chosen by lane group (l / 16).  The 16x16 f32
+// result holds D[4 * (l / 16) + r][l % 16] in element r of lane l.
+template <typename T> struct Mfma;
+template <> struct Mfma<bf16_t> {
+  static constexpr int EPV = 8;
+  static constexpr int LOAD_ELEMS = 8;
+  __device__ __forceinline__ static f32x4_t step(const uint4& a, const uint4& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<float> {
+  static constexpr int EPV = 1;
+  static constexpr int LOAD_ELEMS = 4;
+};
+
+__device__ __forceinline__ f32x4_t mfma_f32_4(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// SiLU(z) = z * sigmoid(z) = z / (1 + e^-z).
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+}  // namespace moe

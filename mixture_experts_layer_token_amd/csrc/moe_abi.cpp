@@ -1,0 +1,321 @@
+// Exported C ABI of the MoE layer library (declared in include/moe.h).
+// Host-side validation, workspace planning and launch sequencing only; all
+// arithmetic runs in the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr int kDimQuantum = 128;  // d, I and I_shared must be multiples of this
+
+size_t elt_size(const moe_desc& d) { return d.dtype == MOE_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_desc(const moe_desc* d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_GEMM) return MOE_ERR_UNSUPPORTED;
+  if (d->T < 0 || d->E < 1 || d->E > 1024 || d->k_max < 1 || d->k_max > d->E) return MOE_ERR_SHAPE;
+  if (d->d < kDimQuantum || d->d > 65536 || d->d % kDimQuantum) return MOE_ERR_SHAPE;
+  if (d->I < kDimQuantum || d->I > 65536 || d->I % kDimQuantum) return MOE_ERR_SHAPE;
+  if (d->I_shared < 0 || d->I_shared > 65536 || d->I_shared % kDimQuantum) return MOE_ERR_SHAPE;
+  if ((int64_t)d->T * d->k_max >= (int64_t)1 << 31) return MOE_ERR_SHAPE;
+  if (!std::isfinite(d->routed_scale)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// Carves 256-byte-aligned regions out of a workspace (or only sizes them when
+// base == nullptr).
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t n) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+  void* take_bytes(size_t n) { return take<char>(n); }
+  size_t total() const { return (off + 255) & ~size_t(255); }
+};
+
+size_t a_cap(const moe_desc& d) { return (size_t)d.T * d.k_max; }
+int n_blocks(const moe_desc& d) { return (d.T + PERM_BLOCK - 1) / PERM_BLOCK; }
+
+struct RouteWs { float* logits; };
+struct PermWs { int32_t* block_counts; int32_t* block_base; };
+struct FfnWs { void* h; void* h_sh; };
+
+void plan_route(const moe_desc& d, Carver& c, RouteWs& w) { w.logits = c.take<float>((size_t)d.T * d.E); }
+void plan_permute(const moe_desc& d, Carver& c, PermWs& w) {
+  const size_t n = (size_t)n_blocks(d) * d.E;
+  w.block_counts = c.take<int32_t>(n);
+  w.block_base = c.take<int32_t>(n);
+}
+void plan_ffn(const moe_desc& d, Carver& c, FfnWs& w) {
+  w.h = c.take_bytes(a_cap(d) * d.I * elt_size(d));
+  w.h_sh = d.I_shared ? c.take_bytes((size_t)d.T * d.I_shared * elt_size(d)) : nullptr;
+}
+
+struct FwdWs {
+  RouteWs r;
+  PermWs p;
+  FfnWs f;
+  int32_t *tok_off, *ids, *counts, *expert_off, *perm_tok, *perm_src, *inv_perm, *n_active, *status;
+  float* w;
+  void *y, *y_sh;
+};
+
+void plan_forward(const moe_desc& d, Carver& c, FwdWs& w) {
+  plan_route(d, c, w.r);
+  plan_permute(d, c, w.p);
+  plan_ffn(d, c, w.f);
+  const size_t A = a_cap(d);
+  w.tok_off = c.take<int32_t>((size_t)d.T + 1);
+  w.ids = c.take<int32_t>(A);
+  w.w = c.take<float>(A);
+  w.counts = c.take<int32_t>(d.E);
+  w.expert_off = c.take<int32_t>((size_t)d.E + 1);
+  w.perm_tok = c.take<int32_t>(A);
+  w.perm_src = c.take<int32_t>(A);
+  w.inv_perm = c.take<int32_t>(A);
+  w.n_active = c.take<int32_t>(1);
+  w.status = c.take<int32_t>(1);
+  w.y = c.take_bytes(A * d.d * elt_size(d));
+  w.y_sh = d.I_shared ? c.take_bytes((size_t)d.T * d.d * elt_size(d)) : nullptr;
+}
+
+size_t ws_size(const moe_desc& d, int op) {
+  Carver c(nullptr);
+  switch (op) {
+    case MOE_OP_ROUTE: { RouteWs w; plan_route(d, c, w); break; }
+    case MOE_OP_PERMUTE: { PermWs w; plan_permute(d, c, w); break; }
+    case MOE_OP_FFN: { FfnWs w; plan_ffn(d, c, w); break; }
+    case MOE_OP_COMBINE: break;
+    default: { FwdWs w; plan_forward(d, c, w); break; }
+  }
+  return c.total();
+}
+
+// Token-indexed buffers may be NULL when there are no tokens (empty tensors).
+bool tok_ptr(const moe_desc& d, const void* p) { return p != nullptr || d.T == 0; }
+
+moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+#define MOE_TRY(expr)                              \
+  do {                                             \
+    moe_status s_ = (expr);                        \
+    if (s_ != MOE_OK) return s_;                   \
+  } while (0)
+
+moe_status check_ws(const moe_desc& d, int op, const void* ws, size_t ws_bytes) {
+  const size_t need = ws_size(d, op);
+  if (need == 0) return MOE_OK;
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+moe_status path_ok(const moe_desc& d) {
+  // Only the weight-streaming kernels exist so far; AUTO resolves to them.
+  return d.path == MOE_PATH_GEMM ? MOE_ERR_UNSUPPORTED : MOE_OK;
+}
+
+// ---- stage bodies (arguments already validated) ----
+
+moe_status do_route(const moe_desc& d, const void* x, const void* wr, const float* bias, const int32_t* k,
+                    int32_t* tok_off, int32_t* ids, float* w, int32_t* status, const RouteWs& ws, hipStream_t st) {
+  hipError_t e = launch_tok_offsets(k, d.T, d.k_max, tok_off, status, st);
+  if (e == hipSuccess) e = launch_router_logits(d.dtype, x, wr, bias, d.T, d.d, d.E, ws.logits, st);
+  if (e == hipSuccess) e = launch_topk(ws.logits, tok_off, d.T, d.E, d.routed_scale, ids, w, st);
+  return launched(e);
+}
+
+moe_status do_permute(const moe_desc& d, const int32_t* tok_off, const int32_t* ids, int32_t* counts,
+                      int32_t* expert_off, int32_t* perm_tok, int32_t* perm_src, int32_t* inv_perm,
+                      int32_t* n_active, int32_t* stats, const PermWs& ws, hipStream_t st) {
+  return launched(launch_permute(tok_off, ids, d.T, d.E, ws.block_counts, ws.block_base, counts, expert_off,
+                                 perm_tok, perm_src, inv_perm, n_active, stats, st));
+}
+
+moe_status do_gateup(const moe_desc& d, const void* x, const void* wg, const void* wu, const int32_t* expert_off,
+                     const int32_t* perm_tok, void* h, hipStream_t st) {
+  return launched(launch_ffn_gateup_stream(d.dtype, x, perm_tok, wg, wu, expert_off, d.E, 0, h, d.I, d.d, st));
+}
+
+moe_status do_down(const moe_desc& d, const void* h, const void* wd, const int32_t* expert_off, void* y,
+                   hipStream_t st) {
+  return launched(launch_ffn_down_stream(d.dtype, h, wd, expert_off, d.E, 0, y, d.d, d.I, st));
+}
+
+moe_status do_shared(const moe_desc& d, const void* x, const void* sg, const void* su, const void* sd, void* h_sh,
+                     void* y_sh, hipStream_t st) {
+  hipError_t e = launch_ffn_gateup_stream(d.dtype, x, nullptr, sg, su, nullptr, 1, d.T, h_sh, d.I_shared, d.d, st);
+  if (e == hipSuccess) e = launch_ffn_down_stream(d.dtype, h_sh, sd, nullptr, 1, d.T, y_sh, d.d, d.I_shared, st);
+  return launched(e);
+}
+
+moe_status do_combine(const moe_desc& d, const void* y, const void* y_sh, const int32_t* tok_off, const float* w,
+                      const int32_t* inv_perm, void* out, hipStream_t st) {
+  return launched(launch_combine(d.dtype, y, y_sh, tok_off, w, inv_perm, out, d.T, d.d, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_workspace_size(const moe_desc* desc, int32_t op, size_t* bytes) {
+  MOE_TRY(check_desc(desc));
+  if (!bytes) return MOE_ERR_NULL;
+  if (op < MOE_OP_ROUTE || op > MOE_OP_FORWARD) return MOE_ERR_UNSUPPORTED;
+  *bytes = ws_size(*desc, op);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_desc* desc, const void* x, const void* w_router, const float* router_bias,
+                     const int32_t* k, int32_t* tok_off, int32_t* topk_ids, float* topk_w, int32_t* dev_status,
+                     void* ws, size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  if (!tok_ptr(d, x) || !w_router || !tok_ptr(d, k) || !tok_off || !tok_ptr(d, topk_ids) || !tok_ptr(d, topk_w))
+    return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_ALIGN;
+  MOE_TRY(check_ws(d, MOE_OP_ROUTE, ws, ws_bytes));
+  Carver c(ws);
+  RouteWs rw;
+  plan_route(d, c, rw);
+  return do_route(d, x, w_router, router_bias, k, tok_off, topk_ids, topk_w, dev_status, rw,
+                  static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_permute(const moe_desc* desc, const int32_t* tok_off, const int32_t* topk_ids,
+                       int32_t* expert_counts, int32_t* expert_off, int32_t* perm_tok, int32_t* perm_src,
+                       int32_t* inv_perm, int32_t* n_active, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  if (!tok_off || !tok_ptr(d, topk_ids) || !expert_counts || !expert_off || !tok_ptr(d, perm_tok) ||
+      !tok_ptr(d, perm_src) || !tok_ptr(d, inv_perm) || !n_active)
+    return MOE_ERR_NULL;
+  MOE_TRY(check_ws(d, MOE_OP_PERMUTE, ws, ws_bytes));
+  Carver c(ws);
+  PermWs pw;
+  plan_permute(d, c, pw);
+  return do_permute(d, tok_off, topk_ids, expert_counts, expert_off, perm_tok, perm_src, inv_perm, n_active,
+                    nullptr, pw, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_ffn_gateup(const moe_desc* desc, const void* x, const void* w_gate, const void* w_up,
+                          const int32_t* expert_off, const int32_t* perm_tok, void* h, void* ws, size_t ws_bytes,
+                          moe_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  MOE_TRY(path_ok(d));
+  if (!tok_ptr(d, x) || !w_gate || !w_up || !expert_off || !tok_ptr(d, perm_tok) || !tok_ptr(d, h))
+    return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(h)) return MOE_ERR_ALIGN;
+  return do_gateup(d, x, w_gate, w_up, expert_off, perm_tok, h, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_ffn_down(const moe_desc* desc, const void* h, const void* w_down, const int32_t* expert_off,
+                        void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  MOE_TRY(path_ok(d));
+  if (!tok_ptr(d, h) || !w_down || !expert_off || !tok_ptr(d, y_perm)) return MOE_ERR_NULL;
+  if (!aligned16(h) || !aligned16(w_down) || !aligned16(y_perm)) return MOE_ERR_ALIGN;
+  return do_down(d, h, w_down, expert_off, y_perm, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_ffn(const moe_desc* desc, const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                   const void* ws_gate, const void* ws_up, const void* ws_down, const int32_t* expert_off,
+                   const int32_t* perm_tok, void* y_perm, void* y_shared, void* ws, size_t ws_bytes,
+                   moe_stream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  MOE_TRY(path_ok(d));
+  if (!tok_ptr(d, x) || !w_gate || !w_up || !w_down || !expert_off || !tok_ptr(d, perm_tok) ||
+      !tok_ptr(d, y_perm))
+    return MOE_ERR_NULL;
+  if (d.I_shared && (!ws_gate || !ws_up || !ws_down || !tok_ptr(d, y_shared))) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(y_perm))
+    return MOE_ERR_ALIGN;
+  if (d.I_shared && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(ws_down) || !aligned16(y_shared)))
+    return MOE_ERR_ALIGN;
+  MOE_TRY(check_ws(d, MOE_OP_FFN, ws, ws_bytes));
+  Carver c(ws);
+  FfnWs fw;
+  plan_ffn(d, c, fw);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MOE_TRY(do_gateup(d, x, w_gate, w_up, expert_off, perm_tok, fw.h, st));
+  MOE_TRY(do_down(d, fw.h, w_down, expert_off, y_perm, st));
+  if (d.I_shared) MOE_TRY(do_shared(d, x, ws_gate, ws_up, ws_down, fw.h_sh, y_shared, st));
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_desc* desc, const void* y_perm, const void* y_shared, const int32_t* tok_off,
+                       const float* topk_w, const int32_t* inv_perm, void* out, moe_stream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  if (!tok_ptr(d, y_perm) || !tok_off || !tok_ptr(d, topk_w) || !tok_ptr(d, inv_perm) || !tok_ptr(d, out))
+    return MOE_ERR_NULL;
+  if (!aligned16(y_perm) || !aligned16(out) || (y_shared && !aligned16(y_shared))) return MOE_ERR_ALIGN;
+  return do_combine(d, y_perm, y_shared, tok_off, topk_w, inv_perm, out, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router, const float* router_bias,
+                       const int32_t* k, const void* w_gate, const void* w_up, const void* w_down,
+                       const void* ws_gate, const void* ws_up, const void* ws_down, void* out, int32_t* stats,
+                       int32_t* dev_status, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  MOE_TRY(path_ok(d));
+  if (!tok_ptr(d, x) || !w_router || !tok_ptr(d, k) || !w_gate || !w_up || !w_down || !tok_ptr(d, out))
+    return MOE_ERR_NULL;
+  if (d.I_shared && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(out))
+    return MOE_ERR_ALIGN;
+  if (d.I_shared && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(ws_down))) return MOE_ERR_ALIGN;
+  MOE_TRY(check_ws(d, MOE_OP_FORWARD, ws, ws_bytes));
+  Carver c(ws);
+  FwdWs fw;
+  plan_forward(d, c, fw);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* status = dev_status ? dev_status : fw.status;
+  MOE_TRY(do_route(d, x, w_router, router_bias, k, fw.tok_off, fw.ids, fw.w, status, fw.r, st));
+  MOE_TRY(do_permute(d, fw.tok_off, fw.ids, fw.counts, fw.expert_off, fw.perm_tok, fw.perm_src, fw.inv_perm,
+                     fw.n_active, stats, fw.p, st));
+  MOE_TRY(do_gateup(d, x, w_gate, w_up, fw.expert_off, fw.perm_tok, fw.f.h, st));
+  MOE_TRY(do_down(d, fw.f.h, w_down, fw.expert_off, fw.y, st));
+  if (d.I_shared) MOE_TRY(do_shared(d, x, ws_gate, ws_up, ws_down, fw.f.h_sh, fw.y_sh, st));
+  return do_combine(d, fw.y, fw.y_sh, fw.tok_off, fw.w, fw.inv_perm, out, st);
+}
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "descriptor values outside the supported range";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dtype, path or op";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_ALIGN: return "buffer not aligned (16 bytes; workspace 256 bytes)";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

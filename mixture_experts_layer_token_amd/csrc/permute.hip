@@ -1,0 +1,136 @@
+// Dispatch metadata of the grouped expert FFN: per-expert histogram, exclusive
+// scan and a stable counting-sort permutation of the assignments by
+// (expert, token).  Integer work only; bit-exact and run-to-run deterministic
+// (LDS atomics are used only for order-free OR).
+//
+// Tokens are cut into blocks of 256.  In each block every expert owns a
+// 256-bit mask of the tokens that selected it (a token selects an expert at
+// most once).  The rank of (t, e) inside its block is the popcount of e's mask
+// below t, so the global row is
+//   expert_off[e] + block_base[blk][e] + popcount(mask_e & below(t)).
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int MASK_WORDS = PERM_BLOCK / 32;
+
+__device__ __forceinline__ void build_masks(uint32_t* masks, const int32_t* __restrict__ tok_off,
+                                            const int32_t* __restrict__ ids, int T, int E) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * MASK_WORDS; i += PERM_BLOCK) masks[i] = 0u;
+  __syncthreads();
+  const int t = blockIdx.x * PERM_BLOCK + tid;
+  if (t < T) {
+    const int a0 = tok_off[t], a1 = tok_off[t + 1];
+    const uint32_t bit = 1u << (tid & 31);
+    for (int a = a0; a < a1; ++a) {
+      const int e = ids[a];
+      if ((unsigned)e < (unsigned)E) atomicOr(&masks[e * MASK_WORDS + (tid >> 5)], bit);
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(PERM_BLOCK) void expert_hist_kernel(const int32_t* __restrict__ tok_off,
+                                                                 const int32_t* __restrict__ ids, int T, int E,
+                                                                 int32_t* __restrict__ block_counts) {
+  extern __shared__ uint32_t masks[];
+  build_masks(masks, tok_off, ids, T, E);
+  for (int e = threadIdx.x; e < E; e += PERM_BLOCK) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < MASK_WORDS; ++w) c += __popc(masks[e * MASK_WORDS + w]);
+    block_counts[(size_t)blockIdx.x * E + e] = c;
+  }
+}
+
+// One workgroup: per-expert running sums over blocks, then the exclusive scan
+// over experts (E <= 1024: one expert per thread).
+__global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __restrict__ block_counts, int nblk,
+                                                           int E, int32_t* __restrict__ block_base,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ expert_off,
+                                                           int32_t* __restrict__ n_active,
+                                                           int32_t* __restrict__ stats) {
+  __shared__ int32_t sc[1024];
+  __shared__ int32_t nact;
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int b = 0; b < nblk; ++b) {
+      const int v = block_counts[(size_t)b * E + e];
+      block_base[(size_t)b * E + e] = run;
+      run += v;
+    }
+    counts[e] = run;
+    if (stats) stats[e] = run;
+  }
+  if (e == 0) nact = 0;
+  sc[e] = run;
+  __syncthreads();
+  if (run > 0) atomicAdd(&nact, 1);
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = e >= off ? sc[e - off] : 0;
+    __syncthreads();
+    sc[e] += v;
+    __syncthreads();
+  }
+  if (e < E) expert_off[e] = sc[e] - run;
+  if (e == 1023) {
+    expert_off[E] = sc[1023];
+    n_active[0] = nact;
+    if (stats) {
+      stats[E] = nact;
+      stats[E + 1] = sc[1023];
+    }
+  }
+}
+
+__global__ __launch_bounds__(PERM_BLOCK) void expert_scatter_kernel(
+    const int32_t* __restrict__ tok_off, const int32_t* __restrict__ ids, int T, int E,
+    const int32_t* __restrict__ block_base, const int32_t* __restrict__ expert_off,
+    int32_t* __restrict__ perm_tok, int32_t* __restrict__ perm_src, int32_t* __restrict__ inv_perm) {
+  extern __shared__ uint32_t masks[];
+  build_masks(masks, tok_off, ids, T, E);
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x * PERM_BLOCK + tid;
+  if (t >= T) return;
+  const int a0 = tok_off[t], a1 = tok_off[t + 1];
+  const int wi = tid >> 5;
+  const uint32_t below = (1u << (tid & 31)) - 1u;
+  for (int a = a0; a < a1; ++a) {
+    const int e = ids[a];
+    if ((unsigned)e >= (unsigned)E) continue;  // not produced by moe_route; ignored
+    const uint32_t* m = masks + e * MASK_WORDS;
+    int rank = __popc(m[wi] & below);
+    for (int w = 0; w < wi; ++w) rank += __popc(m[w]);
+    const int pos = expert_off[e] + block_base[(size_t)blockIdx.x * E + e] + rank;
+    perm_tok[pos] = t;
+    perm_src[pos] = a;
+    inv_perm[a] = pos;
+  }
+}
+
+hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int E, int32_t* block_counts,
+                          int32_t* block_base, int32_t* counts, int32_t* expert_off, int32_t* perm_tok,
+                          int32_t* perm_src, int32_t* inv_perm, int32_t* n_active, int32_t* stats,
+                          hipStream_t st) {
+  const int nblk = (T + PERM_BLOCK - 1) / PERM_BLOCK;
+  const size_t lds = (size_t)E * MASK_WORDS * sizeof(uint32_t);
+  if (nblk > 0) {
+    hipLaunchKernelGGL(expert_hist_kernel, dim3(nblk), dim3(PERM_BLOCK), lds, st, tok_off, ids, T, E,
+                       block_counts);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, st, block_counts, nblk, E, block_base, counts,
+                     expert_off, n_active, stats);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || nblk == 0) return err;
+  hipLaunchKernelGGL(expert_scatter_kernel, dim3(nblk), dim3(PERM_BLOCK), lds, st, tok_off, ids, T, E,
+                     block_base, expert_off, perm_tok, perm_src, inv_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,86 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/moe.h declares, sizes workspaces and rejects bad
+arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_token_amd as moe
+from mixture_experts_layer_token_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char\*)\s+(moe_\w+)\s*\(", hdr, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = _declared()
+    assert "moe_forward" in names and len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def _desc(**kw):
+    base = dict(T=64, d=4096, E=8, I=14336, k_max=2, I_shared=0, dtype=moe.MOE_BF16, path=0,
+                routed_scale=1.0)
+    base.update(kw)
+    return _lib.moe_desc(**base)
+
+
+def _ws(desc, op):
+    n = ctypes.c_size_t(0)
+    st = _lib.load().moe_workspace_size(ctypes.byref(desc), op, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes():
+    d = _desc()
+    st, fwd = _ws(d, moe.MOE_OP_FORWARD)
+    assert st == 0 and fwd % 256 == 0
+    A = 64 * 2
+    # forward holds at least H [A, I] and Y [A, d] in bf16
+    assert fwd >= A * 14336 * 2 + A * 4096 * 2
+    for op in (moe.MOE_OP_ROUTE, moe.MOE_OP_PERMUTE, moe.MOE_OP_FFN):
+        st, n = _ws(d, op)
+        assert st == 0 and 0 < n <= fwd
+    assert _ws(d, moe.MOE_OP_COMBINE) == (0, 0)
+    assert _ws(_desc(T=0), moe.MOE_OP_FORWARD)[0] == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=100), 2), (dict(I=64), 2), (dict(E=0), 2), (dict(E=1025, k_max=1), 2),
+    (dict(k_max=9), 2), (dict(k_max=0), 2), (dict(T=-1), 2), (dict(I_shared=100), 2),
+    (dict(T=1 << 28, k_max=8), 2), (dict(dtype=7), 3), (dict(path=5), 3),
+    (dict(routed_scale=float("inf")), 2),
+])
+def test_bad_descriptors_rejected(kw, code):
+    assert _ws(_desc(**kw), moe.MOE_OP_FORWARD)[0] == code
+
+
+def test_entry_points_validate_before_launch():
+    lib = _lib.load()
+    d = _desc(T=4, d=128, E=4, I=128, k_max=2)
+    P = lambda v: ctypes.c_void_p(v)
+    # NULL pointers
+    assert lib.moe_route(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None) == 1
+    assert lib.moe_forward(ctypes.byref(d), *([None] * 14), 0, None) == 1
+    assert lib.moe_combine(ctypes.byref(d), None, None, None, None, None, None, None) == 1
+    # workspace too small (all other pointers plausible, never dereferenced)
+    fake = [P(4096 * (i + 1)) for i in range(8)]
+    assert lib.moe_route(ctypes.byref(d), *fake[:7], None, P(1 << 20), 16, None) == 4
+    # misaligned activation
+    assert lib.moe_route(ctypes.byref(d), P(4098), *fake[1:7], None, P(1 << 20), 1 << 30, None) == 5
+    # unsupported path on the FFN
+    dg = _desc(T=4, d=128, E=4, I=128, k_max=2, path=moe.MOE_PATH_GEMM)
+    status = lib.moe_ffn_gateup(ctypes.byref(dg), *fake[:6], None, 0, None)
+    assert status in (0, 3) and (status == 3 or os.environ.get("MOE_HAS_GEMM"))
+    assert lib.moe_status_str(4) == b"workspace missing or too small"
+    with pytest.raises(moe.MoeError):
+        moe._check("x", 2)

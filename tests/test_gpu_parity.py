@@ -1,0 +1,167 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the GPU.
+
+Routing ids, token offsets, per-expert counts, the permutation and the
+activated-expert count must match bit for bit; outputs must be within
+relative L2 <= 1e-2 and max |err| <= 5e-2 (bf16) or relative L2 <= 1e-5
+(fp32).  Full-size workloads are checked on every token's routing and on a
+spread sample of output rows (the oracle computes them one by one).
+"""
+import gc
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_token_amd as moe
+from tests.gpu_util import (check_routing, compare_out, oracle_out, oracle_routing, run_forward,
+                            run_stages, sample_tokens)
+from workloads import CONFIGS, make_custom_layer, make_layer
+
+pytestmark = pytest.mark.gpu
+
+# output rows checked against the oracle per workload (all rows when fewer)
+SAMPLE = {"tiny_fp32": 16, "mixtral_decode": 64, "qwen3_30b_a3b_decode": 64,
+          "subexpert_prefill": 24, "dsv3_decode": 10, "dsv3_prefill": 8}
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe._lib.load()
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_workload_parity(name):
+    cfg = CONFIGS[name]
+    _say(f"[parity] {name}: drawing layer")
+    layer = make_layer(cfg, "cuda")
+    got = run_stages(layer)
+    r, p = oracle_routing(layer)
+    check_routing(got, r, p)
+    fout, stats, status = run_forward(layer)
+    assert status == 0
+    torch.testing.assert_close(fout, got["out"], rtol=0, atol=0)   # fused == staged, bit for bit
+    np.testing.assert_array_equal(stats[:cfg.E], p["counts"])
+    assert stats[cfg.E] == p["n_active"] and stats[cfg.E + 1] == got["A"]
+    tokens = sample_tokens(cfg.T, SAMPLE[name])
+    err = compare_out(fout, oracle_out(layer, tokens), cfg.dtype, tokens)
+    _say(f"[parity] {name}: A={got['A']} n_active={p['n_active']} {err}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,E,d,I,kmax,Is", [
+    (300, 8, 128, 256, 8, 0),      # ragged: two permutation blocks, k up to E (dense limit)
+    (70, 257, 256, 128, 12, 128),  # E just above 256 (8 keys per lane), shared expert
+    (33, 1024, 128, 128, 20, 0),   # largest E
+    (1, 4, 128, 128, 4, 0),        # single token
+    (129, 64, 384, 384, 64, 0),    # k_t up to E = 64
+])
+def test_shapes_and_ragged(dtype, T, E, d, I, kmax, Is):
+    rng = np.random.default_rng(T + E)
+    k = rng.integers(0, kmax + 1, size=T)
+    k[0] = kmax
+    layer = make_custom_layer(T=T, d=d, E=E, I=I, k=k, dtype=dtype, k_max=kmax, I_shared=Is,
+                              zipf=0.7, seed=T, device="cuda")
+    got = run_stages(layer)
+    r, p = oracle_routing(layer)
+    check_routing(got, r, p)
+    tokens = sample_tokens(T, 40)
+    compare_out(got["out"], oracle_out(layer, tokens), dtype, tokens)
+
+
+def test_zero_tokens():
+    layer = make_custom_layer(T=0, d=128, E=4, I=128, k=[], dtype="bf16", k_max=2, device="cuda")
+    out, stats, status = run_forward(layer)
+    assert out.shape == (0, 128) and status == 0
+    assert stats[:4].tolist() == [0] * 4 and stats[4] == 0 and stats[5] == 0
+
+
+def test_all_k_zero_gives_shared_only():
+    T = 9
+    layer = make_custom_layer(T=T, d=128, E=6, I=128, k=[0] * T, dtype="f32", k_max=3, I_shared=256,
+                              device="cuda")
+    out, stats, status = run_forward(layer)
+    assert stats[7] == 0 and stats[6] == 0
+    compare_out(out, oracle_out(layer, np.arange(T)), "f32", np.arange(T))
+
+
+def test_invalid_k_flagged_and_dropped():
+    k = [2, -1, 3, 9, 1]
+    layer = make_custom_layer(T=5, d=128, E=8, I=128, k=k, dtype="bf16", k_max=3, device="cuda")
+    got = run_stages(layer)
+    r, p = oracle_routing(layer)
+    assert r["status"] == moe.MOE_DEV_BAD_K
+    check_routing(got, r, p)
+    assert not got["out"][1].any() and not got["out"][3].any()
+
+
+def test_exact_ties_break_to_lower_index():
+    """Zero hidden states make every logit equal its bias; duplicated router
+    rows make exactly tied logits for any x."""
+    T, E = 40, 16
+    layer = make_custom_layer(T=T, d=128, E=E, I=128, k=[5] * T, dtype="bf16", k_max=8, device="cuda")
+    layer.x[: T // 2].zero_()
+    layer.w_router[1::2].copy_(layer.w_router[0::2])           # experts 2j and 2j+1 tie
+    got = run_stages(layer)
+    r, p = oracle_routing(layer)
+    check_routing(got, r, p)
+    assert got["ids"][:5].tolist() == [0, 1, 2, 3, 4]
+    for t in range(T):
+        sel = got["ids"][5 * t:5 * t + 5]
+        for e in sel:
+            if e % 2 == 1:
+                assert e - 1 in sel          # an odd copy is only taken after its even twin
+
+
+def test_deterministic_bits():
+    layer = make_layer(CONFIGS["qwen3_30b_a3b_decode"], "cuda")
+    a, _, _ = run_forward(layer)
+    b, _, _ = run_forward(layer)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_graph_capture_replays_any_k():
+    """One captured graph of moe_forward serves every k mix."""
+    cfg = CONFIGS["qwen3_30b_a3b_decode"]
+    layer = make_layer(cfg, "cuda")
+    desc = moe.make_desc(cfg.T, cfg.d, cfg.E, cfg.I, cfg.k_max, dtype=layer.x.dtype)
+    ws = moe.alloc_workspace(desc)
+    k_static = layer.k.clone()
+    out = torch.empty_like(layer.x)
+    stats = torch.empty(cfg.E + 2, dtype=torch.int32, device="cuda")
+    status = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def call():
+        moe.moe_forward(desc, layer.x, layer.w_router, layer.router_bias, k_static, layer.w_gate,
+                        layer.w_up, layer.w_down, None, None, None, out, stats, status, ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    rng = np.random.default_rng(1)
+    for rep in range(4):
+        kv = torch.as_tensor(rng.choice([0, 1, 2, 4, 8], size=cfg.T).astype(np.int32), device="cuda")
+        k_static.copy_(kv)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        st = stats.clone()
+        layer.k = kv
+        ref, ref_stats, _ = run_forward(layer)
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(st.cpu(), torch.as_tensor(ref_stats, dtype=torch.int32))

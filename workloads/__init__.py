@@ -58,6 +58,7 @@ __all__ = [
     "make_custom_layer",
     "to_f64",
     "torch_dtype",
+    "ExpertView",
 ]
 
 
@@ -261,3 +262,18 @@ def to_f64(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
     if t.dtype in (torch.int32, torch.int64):
         return t.numpy().astype(np.int64)
     return t.float().numpy().astype(np.float64)
+
+
+class ExpertView:
+    """``view[e]`` is expert e of a stacked weight tensor (any device) as a
+    float64 numpy array, copied on demand, so a CPU check can read a few
+    experts of a layer that only fits in device memory."""
+
+    def __init__(self, stacked: torch.Tensor):
+        self.stacked = stacked
+
+    def __getitem__(self, e: int) -> np.ndarray:
+        return to_f64(self.stacked[e])
+
+    def __len__(self) -> int:
+        return self.stacked.shape[0]
