@@ -6,8 +6,8 @@
 // weight byte is read exactly once, with 16-byte loads, by one wave, while the
 // few rows routed to that expert ride along on the narrow side of a 16x16 MFMA.
 //
-// Work split.  Grid = (column tiles, groups).  A workgroup is 4 waves = WN
-// waves along the output columns x WK waves along K.  A wave owns two 16-row
+// Work split.  Grid = (column tiles, groups).  A workgroup is WN x WK waves:
+// WN waves along the output columns, WK waves along K.  A wave owns two 16-row
 // weight tiles:
 //   gate/up: rows c..c+15 of W_gate and of W_up (same 16 output columns)
 //   down:    rows c..c+31 of W_down (two 16-column tiles)
@@ -15,8 +15,12 @@
 // row per tile (lane l: row l%16, K offset (l/16)*KC).  The activation rows use
 // the same K indices on the other MFMA side, so the instruction sums exactly
 // the K values the lanes supplied (any consistent K order gives the dot
-// product).  Rows are processed 64 at a time (4 MFMA column tiles); waves along
-// K add their partial sums through LDS in a fixed order.
+// product).  Rows are processed 16*SMT at a time; waves along K add their
+// partial sums through LDS in a fixed order (deterministic).
+//
+// Memory pipeline: the weights of step i+1 are requested before the MFMAs of
+// step i, right after the activation rows of step i, so the in-order wait for
+// the activations leaves the next weights in flight.
 //
 // The gate/up epilogue applies SwiGLU (MoE-Prism, arXiv 2510.19366, §III-B1,
 // Eq. (1)): H = SiLU(g) * u, stored in the element type.
@@ -25,7 +29,16 @@
 
 namespace moe {
 
-constexpr int SMT = 4;  // MFMA column tiles (16 rows each) per row group
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename T, bool NT>
+__device__ __forceinline__ uint4 ldw(const T* p) {
+  if (NT) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  return *reinterpret_cast<const uint4*>(p);
+}
 
 template <typename T>
 __device__ __forceinline__ uint4 ld16(const T* p) {
@@ -64,19 +77,39 @@ __device__ __forceinline__ void store4<float>(float* p, float a, float b, float 
 }
 
 // MODE 0: gate/up + SwiGLU.  MODE 1: down projection.
-template <typename T, int MODE, int KC, int WK>
-__global__ __launch_bounds__(256) void ffn_stream_kernel(const T* __restrict__ in,
-                                                         const int32_t* __restrict__ row_map,
-                                                         const T* __restrict__ w0, const T* __restrict__ w1,
-                                                         const int32_t* __restrict__ grp_off, int dense_rows,
-                                                         T* __restrict__ out, int N, int K) {
-  constexpr int WN = 4 / WK;
-  constexpr int CPW = (MODE == 0) ? 16 : 32;  // output columns per wave
-  constexpr int NB = WN * CPW;                // output columns per workgroup
-  constexpr int LE = 16 / sizeof(T);          // elements per 16-byte load
-  constexpr int LPS = KC / LE;                // loads per tile row per K step
+// TPW: 16-row weight tiles per wave.  MODE 0: TPW/2 column tiles of W_gate and
+// the same columns of W_up; MODE 1: TPW column tiles of W_down.  More tiles
+// per wave put more weight bytes in flight per activation row loaded.
+// IL: K layout of a lane's LPS 16-byte loads within a step.  IL = 0: load i of
+// lane group g covers [g*KC + i*LE, +LE) (each lane reads KC contiguous
+// elements); IL = 1: [i*4*LE + g*LE, +LE) (the four lane groups of one load
+// read 64 contiguous bytes of the row).
+// PD: software-pipeline depth.  The weights and activation rows of step s+PD
+// are requested together before the MFMAs of step s, always with the same
+// number of loads per step (rows past the group's end re-read row tile 0), so
+// the in-order wait for step s leaves PD steps in flight.
+// Rows of a group are cut into blocks of 16*SMT.  grid.x = mgroups x column
+// tiles with the tile index varying fastest: workgroups are dealt to the
+// XCDs round-robin by linear id, so consecutive ids must carry real work, and
+// the row blocks of one tile (id stride = tiles) share an XCD, hence its L2,
+// when the tile count is a multiple of 8.  Row-block slot m takes row blocks
+// m, m + mgroups, ...
+template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL>
+__global__ __launch_bounds__(64 * WN * WK) void ffn_stream_kernel(
+    const T* __restrict__ in, const int32_t* __restrict__ row_map, const T* __restrict__ w0,
+    const T* __restrict__ w1, const int32_t* __restrict__ grp_off, int dense_rows, T* __restrict__ out, int N,
+    int K, int mgroups) {
+  static_assert(MODE == 1 || TPW % 2 == 0, "gate/up tiles come in pairs");
+  constexpr int CPW = (MODE == 0) ? 8 * TPW : 16 * TPW;  // output columns per wave
+  constexpr int NB = WN * CPW;                           // output columns per workgroup
+  constexpr int LE = 16 / sizeof(T);                     // elements per 16-byte load
+  constexpr int LPS = KC / LE;                           // loads per tile row per K step
+  constexpr int STEP = 4 * KC;                           // K elements per wave step
+  constexpr int NS = PD + 1;                             // register stages
+  constexpr int LSTR = IL ? 4 * LE : LE;                 // distance between a lane's loads
+  constexpr int HALF = TPW / 2;
   static_assert(KC % LE == 0, "K step must be whole 16-byte loads");
-  __shared__ f32x4_t red[(WK > 1) ? (WK - 1) * WN * SMT * 2 * 64 : 1];
+  __shared__ f32x4_t red[(WK > 1) ? (WK - 1) * WN * SMT * TPW * 64 : 1];
 
   const int g = blockIdx.y;
   int row0, rows;
@@ -88,26 +121,31 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(const T* __restrict__ i
     rows = dense_rows;
   }
   if (rows <= 0) return;
+  const int tiles = gridDim.x / mgroups;
+  const int mslot = blockIdx.x / tiles, tile = blockIdx.x - mslot * tiles;
+  if (mslot * 16 * SMT >= rows) return;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wn = wave % WN, wk = wave / WN;
   const int lr = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * NB + wn * CPW;
+  const int n0 = tile * NB + wn * CPW;
+  const int lofs = IL ? lg * LE : lg * KC;   // lane's first element within a step
   const int Kw = K / WK;
-  const int kbeg = wk * Kw, kend = kbeg + Kw;
+  const int kbeg = wk * Kw;
+  const int nsteps = Kw / STEP;
   const size_t gstride = (size_t)N * K;
-  const T* wa;
-  const T* wb;
-  if (MODE == 0) {
-    wa = w0 + g * gstride + (size_t)(n0 + lr) * K;
-    wb = w1 + g * gstride + (size_t)(n0 + lr) * K;
-  } else {
-    wa = w0 + g * gstride + (size_t)(n0 + lr) * K;
-    wb = w0 + g * gstride + (size_t)(n0 + 16 + lr) * K;
-  }
+  const int tstride = 16 * K;                // elements between consecutive 16-row tiles
+  // tile j's row pointer is wbase(j) + (j % half) * tstride
+  const T* wa = w0 + g * gstride + (size_t)(n0 + lr) * K + kbeg + lofs;
+  const T* wb = (MODE == 0 ? w1 : w0) + g * gstride + (size_t)(n0 + lr) * K + kbeg + lofs;
+  auto wrow = [&](int j) -> const T* {
+    if (MODE == 0) return (j < HALF ? wa : wb) + (j % HALF) * tstride;
+    return wa + j * tstride;
+  };
+  (void)wb;
 
-  for (int mg = 0; mg < rows; mg += 16 * SMT) {
-    const int mts = min(SMT, (rows - mg + 15) >> 4);  // live column tiles (wave-uniform)
+  for (int mg = mslot * 16 * SMT; mg < rows; mg += mgroups * 16 * SMT) {
+    const int mts = min(SMT, (rows - mg + 15) >> 4);  // live row tiles (wave-uniform)
     const T* xr[SMT];
     bool valid[SMT];
 #pragma unroll
@@ -115,34 +153,50 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(const T* __restrict__ i
       const int r = mg + mt * 16 + lr;
       valid[mt] = r < rows;
       const int src = valid[mt] ? (row_map ? row_map[row0 + r] : row0 + r) : 0;
-      xr[mt] = in + (size_t)src * K;
+      xr[mt] = in + (size_t)src * K + kbeg + lofs;
     }
-    f32x4_t acc[SMT][2];
 #pragma unroll
-    for (int mt = 0; mt < SMT; ++mt) {
-      acc[mt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int mt = 1; mt < SMT; ++mt)
+      if (mt >= mts) xr[mt] = xr[0];  // dead row tile: same loads as tile 0, result unused
+    f32x4_t acc[SMT][TPW];
+#pragma unroll
+    for (int mt = 0; mt < SMT; ++mt)
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) acc[mt][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int kc = kbeg; kc < kend; kc += 4 * KC) {
-      const int ko = kc + lg * KC;
-      uint4 A0[LPS], A1[LPS];
+    uint4 Wr[NS][TPW][LPS];
+    uint4 Xr[NS][SMT][LPS];
+    auto issue = [&](uint4 (&w)[TPW][LPS], uint4 (&x)[SMT][LPS], int step) {
+      const int ko = step * STEP;
 #pragma unroll
-      for (int i = 0; i < LPS; ++i) {
-        A0[i] = ld16(wa + ko + i * LE);
-        A1[i] = ld16(wb + ko + i * LE);
-      }
+      for (int j = 0; j < TPW; ++j)
 #pragma unroll
-      for (int mt = 0; mt < SMT; ++mt) {
-        if (mt < mts) {
-          uint4 B[LPS];
+        for (int i = 0; i < LPS; ++i) w[j][i] = ldw<T, false>(wrow(j) + ko + i * LSTR);
 #pragma unroll
-          for (int i = 0; i < LPS; ++i) B[i] = valid[mt] ? ld16(xr[mt] + ko + i * LE) : zero_u4();
+      for (int mt = 0; mt < SMT; ++mt)
 #pragma unroll
-          for (int i = 0; i < LPS; ++i) {
-            mma_tile<T>(acc[mt][0], A0[i], B[i]);
-            mma_tile<T>(acc[mt][1], A1[i], B[i]);
-          }
+        for (int i = 0; i < LPS; ++i) x[mt][i] = ld16(xr[mt] + ko + i * LSTR);
+    };
+#pragma unroll
+    for (int p = 0; p < PD; ++p) issue(Wr[p], Xr[p], min(p, nsteps - 1));
+
+    for (int s0 = 0; s0 < nsteps; s0 += NS) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const int s = s0 + st;
+        if (s < nsteps) {
+          // requests for step s + PD (the last step repeats: cached, in bounds)
+          issue(Wr[(st + PD) % NS], Xr[(st + PD) % NS], min(s + PD, nsteps - 1));
+#pragma unroll
+          for (int mt = 0; mt < SMT; ++mt)
+            if (mt < mts) {
+#pragma unroll
+              for (int i = 0; i < LPS; ++i) {
+                const uint4 b = valid[mt] ? Xr[st][mt][i] : zero_u4();
+#pragma unroll
+                for (int j = 0; j < TPW; ++j) mma_tile<T>(acc[mt][j], Wr[st][j][i], b);
+              }
+            }
         }
       }
     }
@@ -152,8 +206,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(const T* __restrict__ i
 #pragma unroll
         for (int mt = 0; mt < SMT; ++mt)
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-            red[((((wk - 1) * WN + wn) * SMT + mt) * 2 + tt) * 64 + lane] = acc[mt][tt];
+          for (int j = 0; j < TPW; ++j) red[((((wk - 1) * WN + wn) * SMT + mt) * TPW + j) * 64 + lane] = acc[mt][j];
       }
       __syncthreads();
       if (wk == 0) {
@@ -161,7 +214,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(const T* __restrict__ i
 #pragma unroll
           for (int mt = 0; mt < SMT; ++mt)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) acc[mt][tt] += red[((((q - 1) * WN + wn) * SMT + mt) * 2 + tt) * 64 + lane];
+            for (int j = 0; j < TPW; ++j) acc[mt][j] += red[((((q - 1) * WN + wn) * SMT + mt) * TPW + j) * 64 + lane];
         }
       }
     }
@@ -171,15 +224,20 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(const T* __restrict__ i
       for (int mt = 0; mt < SMT; ++mt) {
         const int m = mg + mt * 16 + lr;
         if (mt < mts && m < rows) {
-          T* orow = out + (size_t)(row0 + m) * N;
+          T* orow = out + (size_t)(row0 + m) * N + n0 + 4 * lg;
           if (MODE == 0) {
-            const f32x4_t gt = acc[mt][0], up = acc[mt][1];
-            store4<T>(orow + n0 + 4 * lg, silu(gt[0]) * up[0], silu(gt[1]) * up[1], silu(gt[2]) * up[2],
-                      silu(gt[3]) * up[3]);
+#pragma unroll
+            for (int j = 0; j < HALF; ++j) {
+              const f32x4_t gt = acc[mt][j], up = acc[mt][j + HALF];
+              store4<T>(orow + 16 * j, silu(gt[0]) * up[0], silu(gt[1]) * up[1], silu(gt[2]) * up[2],
+                        silu(gt[3]) * up[3]);
+            }
           } else {
-            const f32x4_t y0 = acc[mt][0], y1 = acc[mt][1];
-            store4<T>(orow + n0 + 4 * lg, y0[0], y0[1], y0[2], y0[3]);
-            store4<T>(orow + n0 + 16 + 4 * lg, y1[0], y1[1], y1[2], y1[3]);
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+              const f32x4_t y = acc[mt][j];
+              store4<T>(orow + 16 * j, y[0], y[1], y[2], y[3]);
+            }
           }
         }
       }
@@ -188,56 +246,62 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(const T* __restrict__ i
   }
 }
 
-template <typename T, int MODE, int KC, int WK>
-static hipError_t launch_one(const T* in, const int32_t* row_map, const T* w0, const T* w1, const int32_t* grp_off,
-                             int G, int dense_rows, T* out, int N, int K, hipStream_t st) {
-  constexpr int NB = (4 / WK) * ((MODE == 0) ? 16 : 32);
-  dim3 grid(N / NB, G);
-  hipLaunchKernelGGL((ffn_stream_kernel<T, MODE, KC, WK>), grid, dim3(256), 0, st, in, row_map, w0, w1, grp_off,
-                     dense_rows, out, N, K);
+// Shape rules a launch must satisfy (checked by the callers): N % NB == 0,
+// K % WK == 0, (K / WK) % (4 * KC) == 0.
+template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL = true>
+constexpr int stream_nb() { return WN * ((MODE == 0) ? 8 * TPW : 16 * TPW); }
+
+template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL = true>
+hipError_t launch_stream_variant(const T* in, const int32_t* row_map, const T* w0, const T* w1,
+                                 const int32_t* grp_off, int G, int dense_rows, T* out, int N, int K,
+                                 int mgroups, hipStream_t st) {
+  constexpr int NB = stream_nb<T, MODE, KC, WN, WK, SMT, TPW, PD, IL>();
+  dim3 grid((N / NB) * mgroups, G);
+  hipLaunchKernelGGL((ffn_stream_kernel<T, MODE, KC, WN, WK, SMT, TPW, PD, IL>), grid, dim3(64 * WN * WK), 0, st,
+                     in, row_map, w0, w1, grp_off, dense_rows, out, N, K, mgroups);
   return hipGetLastError();
 }
 
-// K split across the workgroup's waves for the down projection: long K and few
-// output columns per expert want more waves along K.
-static int pick_wk(int K, int step) {
-  if (K >= 4096 && K % (4 * step) == 0) return 4;
-  if (K >= 512 && K % (2 * step) == 0) return 2;
-  return 1;
+// Production shape of the streaming kernels (chosen by a sweep over tile
+// shapes on the decode workloads): 16-element K chunks per lane (a 64-element
+// step per wave), four 16-row weight tiles per wave, 32 rows per pass, one
+// step of software pipelining, and the four waves of a workgroup splitting K.
+// When K/4 is not a whole number of steps the workgroup is 2 x 2 waves.
+constexpr int S_SMT = 2, S_TPW = 4, S_PD = 1;
+constexpr int S_ROWS = 16 * S_SMT;   // rows per pass
+constexpr int S_MGROUP_CAP = 16;     // row-block slots per column tile
+
+static int stream_mgroups(int rows_max) {
+  return max(1, min(S_MGROUP_CAP, (rows_max + S_ROWS - 1) / S_ROWS));
 }
 
-template <typename T>
-static hipError_t gateup_t(const void* in, const int32_t* row_map, const void* wg, const void* wu,
-                           const int32_t* grp_off, int G, int dense_rows, void* h, int N, int K, hipStream_t st) {
-  constexpr int KC = (sizeof(T) == 2) ? 32 : 8;
-  return launch_one<T, 0, KC, 1>((const T*)in, row_map, (const T*)wg, (const T*)wu, grp_off, G, dense_rows, (T*)h,
-                                 N, K, st);
-}
-
-template <typename T>
-static hipError_t down_t(const void* h, const void* wd, const int32_t* grp_off, int G, int dense_rows, void* y,
-                         int N, int K, hipStream_t st) {
-  constexpr int KC = (sizeof(T) == 2) ? 32 : 8;
-  const int wk = pick_wk(K, 4 * KC);
-  const T* in = (const T*)h;
-  const T* w = (const T*)wd;
-  T* out = (T*)y;
-  if (wk == 4) return launch_one<T, 1, KC, 4>(in, nullptr, w, w, grp_off, G, dense_rows, out, N, K, st);
-  if (wk == 2) return launch_one<T, 1, KC, 2>(in, nullptr, w, w, grp_off, G, dense_rows, out, N, K, st);
-  return launch_one<T, 1, KC, 1>(in, nullptr, w, w, grp_off, G, dense_rows, out, N, K, st);
+template <typename T, int MODE>
+static hipError_t stream_t(const void* in, const int32_t* row_map, const void* w0, const void* w1,
+                           const int32_t* grp_off, int G, int dense_rows, int rows_max, void* out, int N, int K,
+                           hipStream_t st) {
+  constexpr int KC = (sizeof(T) == 2) ? 16 : 8;
+  constexpr int STEP = 4 * KC;
+  const int mg = stream_mgroups(rows_max);
+  const T* x = (const T*)in;
+  if (K % (4 * STEP) == 0)
+    return launch_stream_variant<T, MODE, KC, 1, 4, S_SMT, S_TPW, S_PD>(x, row_map, (const T*)w0, (const T*)w1, grp_off,
+                                                                        G, dense_rows, (T*)out, N, K, mg, st);
+  return launch_stream_variant<T, MODE, KC, 2, 2, S_SMT, S_TPW, S_PD>(x, row_map, (const T*)w0, (const T*)w1, grp_off, G,
+                                                                      dense_rows, (T*)out, N, K, mg, st);
 }
 
 hipError_t launch_ffn_gateup_stream(int dtype, const void* in, const int32_t* row_map, const void* wg,
-                                    const void* wu, const int32_t* grp_off, int G, int dense_rows, void* h,
-                                    int N, int K, hipStream_t st) {
-  if (dtype == DT_BF16) return gateup_t<bf16_t>(in, row_map, wg, wu, grp_off, G, dense_rows, h, N, K, st);
-  return gateup_t<float>(in, row_map, wg, wu, grp_off, G, dense_rows, h, N, K, st);
+                                    const void* wu, const int32_t* grp_off, int G, int dense_rows, int rows_max,
+                                    void* h, int N, int K, hipStream_t st) {
+  if (dtype == DT_BF16)
+    return stream_t<bf16_t, 0>(in, row_map, wg, wu, grp_off, G, dense_rows, rows_max, h, N, K, st);
+  return stream_t<float, 0>(in, row_map, wg, wu, grp_off, G, dense_rows, rows_max, h, N, K, st);
 }
 
 hipError_t launch_ffn_down_stream(int dtype, const void* h, const void* wd, const int32_t* grp_off, int G,
-                                  int dense_rows, void* y, int N, int K, hipStream_t st) {
-  if (dtype == DT_BF16) return down_t<bf16_t>(h, wd, grp_off, G, dense_rows, y, N, K, st);
-  return down_t<float>(h, wd, grp_off, G, dense_rows, y, N, K, st);
+                                  int dense_rows, int rows_max, void* y, int N, int K, hipStream_t st) {
+  if (dtype == DT_BF16) return stream_t<bf16_t, 1>(h, nullptr, wd, wd, grp_off, G, dense_rows, rows_max, y, N, K, st);
+  return stream_t<float, 1>(h, nullptr, wd, wd, grp_off, G, dense_rows, rows_max, y, N, K, st);
 }
 
 }  // namespace moe

@@ -11,12 +11,14 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 constexpr int32_t MOE_DEV_BAD_K_BIT = 1;
 
 // route.hip
-hipError_t launch_tok_offsets(const int32_t* k, int T, int k_max, int32_t* tok_off, int32_t* status,
-                              hipStream_t st);
-hipError_t launch_router_logits(int dtype, const void* x, const void* w, const float* bias, int T, int d,
-                                int E, float* logits, hipStream_t st);
-hipError_t launch_topk(const float* logits, const int32_t* tok_off, int T, int E, float scale, int32_t* ids,
-                       float* wts, hipStream_t st);
+// K slices of the router (float64 partial sums part[S][T][E]); depends on the shape only.
+int router_splits(int T, int d, int E);
+// Router partial logits; also writes tok_off and status (token-offset scan).
+hipError_t launch_router(int dtype, const void* x, const void* w, const int32_t* k, int T, int d, int E, int k_max,
+                         int S, double* part, int32_t* tok_off, int32_t* status, hipStream_t st);
+// Sums the S slices in order, adds the bias, rounds to float32, selects top-k_t.
+hipError_t launch_topk(const double* part, int S, const float* bias, const int32_t* tok_off, int T, int E,
+                       float scale, int32_t* ids, float* wts, hipStream_t st);
 
 // permute.hip
 constexpr int PERM_BLOCK = 256;  // tokens per histogram block
@@ -25,17 +27,18 @@ hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int
                           int32_t* perm_src, int32_t* inv_perm, int32_t* n_active, int32_t* stats,
                           hipStream_t st);
 
-// ffn.hip -- weight-streaming grouped FFN.
+// ffn_stream.hip -- weight-streaming grouped FFN.
 //  gate/up: H[row0+m] = SiLU(in[src(m)] . wg[g]^T) * (in[src(m)] . wu[g]^T), N = I, K = d
 //  down:    Y[row0+m] = H[row0+m] . wd[g]^T,                                 N = d, K = I
 // Groups: G experts with rows [grp_off[g], grp_off[g+1]); grp_off == nullptr
 // means one group of `dense_rows` rows starting at 0.  src(m) = row_map[row0+m]
-// when row_map != nullptr, else row0 + m.
+// when row_map != nullptr, else row0 + m.  rows_max bounds the rows of any
+// group (it sizes the grid; it must not depend on the routing).
 hipError_t launch_ffn_gateup_stream(int dtype, const void* in, const int32_t* row_map, const void* wg,
-                                    const void* wu, const int32_t* grp_off, int G, int dense_rows, void* h,
-                                    int N, int K, hipStream_t st);
+                                    const void* wu, const int32_t* grp_off, int G, int dense_rows, int rows_max,
+                                    void* h, int N, int K, hipStream_t st);
 hipError_t launch_ffn_down_stream(int dtype, const void* h, const void* wd, const int32_t* grp_off, int G,
-                                  int dense_rows, void* y, int N, int K, hipStream_t st);
+                                  int dense_rows, int rows_max, void* y, int N, int K, hipStream_t st);
 
 // combine.hip
 hipError_t launch_combine(int dtype, const void* y, const void* y_shared, const int32_t* tok_off,

@@ -52,11 +52,14 @@ struct Carver {
 size_t a_cap(const moe_desc& d) { return (size_t)d.T * d.k_max; }
 int n_blocks(const moe_desc& d) { return (d.T + PERM_BLOCK - 1) / PERM_BLOCK; }
 
-struct RouteWs { float* logits; };
+struct RouteWs { double* part; int splits; };
 struct PermWs { int32_t* block_counts; int32_t* block_base; };
 struct FfnWs { void* h; void* h_sh; };
 
-void plan_route(const moe_desc& d, Carver& c, RouteWs& w) { w.logits = c.take<float>((size_t)d.T * d.E); }
+void plan_route(const moe_desc& d, Carver& c, RouteWs& w) {
+  w.splits = router_splits(d.T, d.d, d.E);
+  w.part = c.take<double>((size_t)w.splits * d.T * d.E);
+}
 void plan_permute(const moe_desc& d, Carver& c, PermWs& w) {
   const size_t n = (size_t)n_blocks(d) * d.E;
   w.block_counts = c.take<int32_t>(n);
@@ -135,9 +138,8 @@ moe_status path_ok(const moe_desc& d) {
 
 moe_status do_route(const moe_desc& d, const void* x, const void* wr, const float* bias, const int32_t* k,
                     int32_t* tok_off, int32_t* ids, float* w, int32_t* status, const RouteWs& ws, hipStream_t st) {
-  hipError_t e = launch_tok_offsets(k, d.T, d.k_max, tok_off, status, st);
-  if (e == hipSuccess) e = launch_router_logits(d.dtype, x, wr, bias, d.T, d.d, d.E, ws.logits, st);
-  if (e == hipSuccess) e = launch_topk(ws.logits, tok_off, d.T, d.E, d.routed_scale, ids, w, st);
+  hipError_t e = launch_router(d.dtype, x, wr, k, d.T, d.d, d.E, d.k_max, ws.splits, ws.part, tok_off, status, st);
+  if (e == hipSuccess) e = launch_topk(ws.part, ws.splits, bias, tok_off, d.T, d.E, d.routed_scale, ids, w, st);
   return launched(e);
 }
 
@@ -150,18 +152,20 @@ moe_status do_permute(const moe_desc& d, const int32_t* tok_off, const int32_t* 
 
 moe_status do_gateup(const moe_desc& d, const void* x, const void* wg, const void* wu, const int32_t* expert_off,
                      const int32_t* perm_tok, void* h, hipStream_t st) {
-  return launched(launch_ffn_gateup_stream(d.dtype, x, perm_tok, wg, wu, expert_off, d.E, 0, h, d.I, d.d, st));
+  // a token selects an expert at most once: at most T rows per expert
+  return launched(launch_ffn_gateup_stream(d.dtype, x, perm_tok, wg, wu, expert_off, d.E, 0, d.T, h, d.I, d.d, st));
 }
 
 moe_status do_down(const moe_desc& d, const void* h, const void* wd, const int32_t* expert_off, void* y,
                    hipStream_t st) {
-  return launched(launch_ffn_down_stream(d.dtype, h, wd, expert_off, d.E, 0, y, d.d, d.I, st));
+  return launched(launch_ffn_down_stream(d.dtype, h, wd, expert_off, d.E, 0, d.T, y, d.d, d.I, st));
 }
 
 moe_status do_shared(const moe_desc& d, const void* x, const void* sg, const void* su, const void* sd, void* h_sh,
                      void* y_sh, hipStream_t st) {
-  hipError_t e = launch_ffn_gateup_stream(d.dtype, x, nullptr, sg, su, nullptr, 1, d.T, h_sh, d.I_shared, d.d, st);
-  if (e == hipSuccess) e = launch_ffn_down_stream(d.dtype, h_sh, sd, nullptr, 1, d.T, y_sh, d.d, d.I_shared, st);
+  hipError_t e =
+      launch_ffn_gateup_stream(d.dtype, x, nullptr, sg, su, nullptr, 1, d.T, d.T, h_sh, d.I_shared, d.d, st);
+  if (e == hipSuccess) e = launch_ffn_down_stream(d.dtype, h_sh, sd, nullptr, 1, d.T, d.T, y_sh, d.d, d.I_shared, st);
   return launched(e);
 }
 

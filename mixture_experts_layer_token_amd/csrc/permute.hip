@@ -112,12 +112,86 @@ __global__ __launch_bounds__(PERM_BLOCK) void expert_scatter_kernel(
   }
 }
 
+// Whole permutation in one workgroup when all tokens fit in one block
+// (T <= 256, the decode batches): masks, counts, scan over experts and
+// scatter without leaving LDS.
+__global__ __launch_bounds__(PERM_BLOCK) void permute_one_block_kernel(
+    const int32_t* __restrict__ tok_off, const int32_t* __restrict__ ids, int T, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ expert_off, int32_t* __restrict__ perm_tok, int32_t* __restrict__ perm_src,
+    int32_t* __restrict__ inv_perm, int32_t* __restrict__ n_active, int32_t* __restrict__ stats) {
+  extern __shared__ uint32_t masks[];
+  int32_t* eoff = reinterpret_cast<int32_t*>(masks + E * MASK_WORDS);  // [E + 1]
+  __shared__ int32_t part[PERM_BLOCK];
+  __shared__ int32_t nact;
+  build_masks(masks, tok_off, ids, T, E);
+  const int tid = threadIdx.x;
+  const int per = (E + PERM_BLOCK - 1) / PERM_BLOCK;
+  const int beg = min(tid * per, E), end = min(beg + per, E);
+  int s = 0, act = 0;
+  for (int e = beg; e < end; ++e) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < MASK_WORDS; ++w) c += __popc(masks[e * MASK_WORDS + w]);
+    eoff[e] = c;
+    s += c;
+    act += c > 0;
+  }
+  if (tid == 0) nact = 0;
+  part[tid] = s;
+  __syncthreads();
+  if (act) atomicAdd(&nact, act);
+  for (int off = 1; off < PERM_BLOCK; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - s;
+  for (int e = beg; e < end; ++e) {
+    const int c = eoff[e];
+    counts[e] = c;
+    if (stats) stats[e] = c;
+    eoff[e] = run;
+    expert_off[e] = run;
+    run += c;
+  }
+  if (tid == PERM_BLOCK - 1) {
+    expert_off[E] = part[PERM_BLOCK - 1];
+    n_active[0] = nact;
+    if (stats) {
+      stats[E] = nact;
+      stats[E + 1] = part[PERM_BLOCK - 1];
+    }
+  }
+  __syncthreads();
+  if (tid >= T) return;
+  const int a0 = tok_off[tid], a1 = tok_off[tid + 1];
+  const int wi = tid >> 5;
+  const uint32_t below = (1u << (tid & 31)) - 1u;
+  for (int a = a0; a < a1; ++a) {
+    const int e = ids[a];
+    if ((unsigned)e >= (unsigned)E) continue;  // not produced by moe_route; ignored
+    const uint32_t* m = masks + e * MASK_WORDS;
+    int rank = __popc(m[wi] & below);
+    for (int w = 0; w < wi; ++w) rank += __popc(m[w]);
+    const int pos = eoff[e] + rank;
+    perm_tok[pos] = tid;
+    perm_src[pos] = a;
+    inv_perm[a] = pos;
+  }
+}
+
 hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int E, int32_t* block_counts,
                           int32_t* block_base, int32_t* counts, int32_t* expert_off, int32_t* perm_tok,
                           int32_t* perm_src, int32_t* inv_perm, int32_t* n_active, int32_t* stats,
                           hipStream_t st) {
   const int nblk = (T + PERM_BLOCK - 1) / PERM_BLOCK;
   const size_t lds = (size_t)E * MASK_WORDS * sizeof(uint32_t);
+  if (nblk == 1) {
+    hipLaunchKernelGGL(permute_one_block_kernel, dim3(1), dim3(PERM_BLOCK), lds + (E + 1) * sizeof(int32_t), st,
+                       tok_off, ids, T, E, counts, expert_off, perm_tok, perm_src, inv_perm, n_active, stats);
+    return hipGetLastError();
+  }
   if (nblk > 0) {
     hipLaunchKernelGGL(expert_hist_kernel, dim3(nblk), dim3(PERM_BLOCK), lds, st, tok_off, ids, T, E,
                        block_counts);

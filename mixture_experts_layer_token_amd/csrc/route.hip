@@ -10,15 +10,12 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// tok_off = exclusive prefix sum of the validated budgets; one workgroup.
-// A k_t outside [0, k_max] counts as 0 and raises MOE_DEV_BAD_K.
-__global__ __launch_bounds__(1024) void tok_offsets_kernel(const int32_t* __restrict__ k, int T,
-                                                           int k_max, int32_t* __restrict__ tok_off,
-                                                           int32_t* __restrict__ status) {
-  __shared__ int32_t part[1024];
-  __shared__ int32_t bad_any;
+// tok_off = exclusive prefix sum of the validated budgets, by one workgroup of
+// 256 threads.  A k_t outside [0, k_max] counts as 0 and raises MOE_DEV_BAD_K.
+__device__ void token_offsets_block(const int32_t* __restrict__ k, int T, int k_max, int32_t* __restrict__ tok_off,
+                                    int32_t* __restrict__ status, int32_t* part, int32_t* bad_any) {
   const int tid = threadIdx.x;
-  const int per = (T + 1023) / 1024;
+  const int per = (T + 255) / 256;
   const int beg = min(tid * per, T), end = min(beg + per, T);
   int s = 0, bad = 0;
   for (int i = beg; i < end; ++i) {
@@ -26,11 +23,11 @@ __global__ __launch_bounds__(1024) void tok_offsets_kernel(const int32_t* __rest
     if (v < 0 || v > k_max) { v = 0; bad = 1; }
     s += v;
   }
-  if (tid == 0) bad_any = 0;
+  if (tid == 0) *bad_any = 0;
   part[tid] = s;
   __syncthreads();
-  if (bad) atomicOr(&bad_any, 1);
-  for (int off = 1; off < 1024; off <<= 1) {
+  if (bad) atomicOr(bad_any, 1);
+  for (int off = 1; off < 256; off <<= 1) {
     int v = tid >= off ? part[tid - off] : 0;
     __syncthreads();
     part[tid] += v;
@@ -43,15 +40,20 @@ __global__ __launch_bounds__(1024) void tok_offsets_kernel(const int32_t* __rest
     if (v < 0 || v > k_max) v = 0;
     run += v;
   }
-  if (tid == 1023) tok_off[T] = part[1023];
-  if (tid == 0 && status) status[0] = bad_any ? MOE_DEV_BAD_K_BIT : 0;
+  if (tid == 255) tok_off[T] = part[255];
+  if (tid == 0 && status) status[0] = *bad_any ? MOE_DEV_BAD_K_BIT : 0;
 }
 
 // ---------------------------------------------------------------------------
 // Router logits l[t][e] = fp32(sum_i x[t][i] * w[e][i] + b[e]), the sum taken in
 // float64 (exact products; only the accumulation rounds) and rounded once.
 // Tile: 64 tokens x 64 experts per workgroup, 4x4 outputs per thread, K staged
-// through LDS 32 elements at a time, already widened to float64.
+// through LDS 32 elements at a time, already widened to float64.  K is split
+// over gridDim.z slices so that small batches still fill the chip; slice s
+// writes its float64 partial sums to part[s][t][e], and the top-k kernel adds
+// the slices in ascending order (any float64 summation order keeps the
+// routing contract: exact products, float64 accumulation, one rounding).
+// Workgroup (0, 0, 0) also computes the token offsets.
 constexpr int RT = 64, RE = 64, RK = 32, RPAD = 65;
 
 template <typename T>
@@ -91,13 +93,23 @@ __device__ __forceinline__ void stage_rows_f64<float>(double (*dst)[RPAD], const
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void router_logits_kernel(const T* __restrict__ x, const T* __restrict__ w,
-                                                            const float* __restrict__ bias, int T_, int d, int E,
-                                                            float* __restrict__ logits) {
+__global__ __launch_bounds__(256) void router_partial_kernel(const T* __restrict__ x, const T* __restrict__ w,
+                                                             int T_, int d, int E, double* __restrict__ part,
+                                                             const int32_t* __restrict__ k, int k_max,
+                                                             int32_t* __restrict__ tok_off,
+                                                             int32_t* __restrict__ status) {
   __shared__ double xs[RK][RPAD];
   __shared__ double ws[RK][RPAD];
   const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
+    int32_t* scan_part = reinterpret_cast<int32_t*>(&xs[0][0]);
+    token_offsets_block(k, T_, k_max, tok_off, status, scan_part, scan_part + 256);
+    __syncthreads();
+  }
   const int t0 = blockIdx.x * RT, e0 = blockIdx.y * RE;
+  const int S = gridDim.z, chunks = d / RK;
+  const int c_beg = (int)(((long long)blockIdx.z * chunks) / S);
+  const int c_end = (int)(((long long)(blockIdx.z + 1) * chunks) / S);
   const int ty = tid >> 4, tx = tid & 15;
   double acc[4][4];
 #pragma unroll
@@ -105,7 +117,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const T* __restrict_
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
 
-  for (int k0 = 0; k0 < d; k0 += RK) {
+  for (int c = c_beg; c < c_end; ++c) {
+    const int k0 = c * RK;
     stage_rows_f64<T>(xs, x, t0, T_, d, k0, tid);
     stage_rows_f64<T>(ws, w, e0, E, d, k0, tid);
     __syncthreads();
@@ -123,6 +136,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const T* __restrict_
     }
     __syncthreads();
   }
+  double* out = part + (size_t)blockIdx.z * T_ * E;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = t0 + ty + 16 * i;
@@ -130,10 +144,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const T* __restrict_
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = e0 + tx + 16 * j;
-      if (e >= E) continue;
-      double v = acc[i][j];
-      if (bias) v += (double)bias[e];
-      logits[(size_t)t * E + e] = (float)v;
+      if (e < E) out[(size_t)t * E + e] = acc[i][j];
     }
   }
 }
@@ -156,7 +167,8 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 }
 
 template <int KPL>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ part, int S,
+                                                   const float* __restrict__ bias,
                                                    const int32_t* __restrict__ tok_off, int T_, int E,
                                                    float scale, int32_t* __restrict__ ids,
                                                    float* __restrict__ wts) {
@@ -171,7 +183,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     const int e = lane + 64 * s;
     key[s] = 0;
     if (e < E) {
-      float l = logits[(size_t)t * E + e];
+      double acc = 0.0;
+      for (int q = 0; q < S; ++q) acc += part[((size_t)q * T_ + t) * E + e];
+      if (bias) acc += (double)bias[e];
+      float l = (float)acc;
       if (l == 0.0f) l = 0.0f;
       uint32_t u = __float_as_uint(l);
       u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -213,39 +228,37 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_tok_offsets(const int32_t* k, int T, int k_max, int32_t* tok_off, int32_t* status,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(tok_offsets_kernel, dim3(1), dim3(1024), 0, st, k, T, k_max, tok_off, status);
-  return hipGetLastError();
+int router_splits(int T, int d, int E) {
+  if (T == 0) return 1;
+  const int tiles = ((T + RT - 1) / RT) * ((E + RE - 1) / RE);
+  const int want = (256 + tiles - 1) / tiles;
+  return max(1, min(want, d / RK));
 }
 
-hipError_t launch_router_logits(int dtype, const void* x, const void* w, const float* bias, int T, int d,
-                                int E, float* logits, hipStream_t st) {
-  if (T == 0) return hipSuccess;
-  dim3 grid((T + RT - 1) / RT, (E + RE - 1) / RE);
+hipError_t launch_router(int dtype, const void* x, const void* w, const int32_t* k, int T, int d, int E, int k_max,
+                         int S, double* part, int32_t* tok_off, int32_t* status, hipStream_t st) {
+  dim3 grid(max(1, (T + RT - 1) / RT), (E + RE - 1) / RE, S);
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL(router_logits_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)x,
-                       (const bf16_t*)w, bias, T, d, E, logits);
+    hipLaunchKernelGGL(router_partial_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)x, (const bf16_t*)w,
+                       T, d, E, part, k, k_max, tok_off, status);
   else
-    hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, st, (const float*)x,
-                       (const float*)w, bias, T, d, E, logits);
+    hipLaunchKernelGGL(router_partial_kernel<float>, grid, dim3(256), 0, st, (const float*)x, (const float*)w, T,
+                       d, E, part, k, k_max, tok_off, status);
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, const int32_t* tok_off, int T, int E, float scale, int32_t* ids,
-                       float* wts, hipStream_t st) {
+hipError_t launch_topk(const double* part, int S, const float* bias, const int32_t* tok_off, int T, int E,
+                       float scale, int32_t* ids, float* wts, hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((T + 3) / 4);
-  if (E <= 64)
-    hipLaunchKernelGGL(topk_kernel<1>, grid, dim3(256), 0, st, logits, tok_off, T, E, scale, ids, wts);
-  else if (E <= 128)
-    hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(256), 0, st, logits, tok_off, T, E, scale, ids, wts);
-  else if (E <= 256)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(256), 0, st, logits, tok_off, T, E, scale, ids, wts);
-  else if (E <= 512)
-    hipLaunchKernelGGL(topk_kernel<8>, grid, dim3(256), 0, st, logits, tok_off, T, E, scale, ids, wts);
-  else
-    hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, st, logits, tok_off, T, E, scale, ids, wts);
+#define MOE_TOPK(KPL) \
+  hipLaunchKernelGGL(topk_kernel<KPL>, grid, dim3(256), 0, st, part, S, bias, tok_off, T, E, scale, ids, wts)
+  if (E <= 64) MOE_TOPK(1);
+  else if (E <= 128) MOE_TOPK(2);
+  else if (E <= 256) MOE_TOPK(4);
+  else if (E <= 512) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
   return hipGetLastError();
 }
 
