@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens in the CPU-oracle sample (0 = workload default)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="before timing, run a plain elementwise copy (torch.neg) of 512 MiB fp32 three "
+                         "times: the known-size kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -142,6 +145,14 @@ def main():
     def step():
         moe.moe_forward(desc, layer.x, layer.w_router, layer.router_bias, layer.k, layer.w_gate,
                         layer.w_up, layer.w_down, *sh, out, stats, status, ws)
+
+    if args.calib_copy:
+        src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):

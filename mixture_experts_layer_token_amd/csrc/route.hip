@@ -183,8 +183,16 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ pa
     const int e = lane + 64 * s;
     key[s] = 0;
     if (e < E) {
+      // slices summed in groups of 8 (independent loads, fixed tree), groups in order
+      const double* pe = part + (size_t)t * E + e;
+      const size_t qstride = (size_t)T_ * E;
       double acc = 0.0;
-      for (int q = 0; q < S; ++q) acc += part[((size_t)q * T_ + t) * E + e];
+      for (int q0 = 0; q0 < S; q0 += 8) {
+        double v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (q0 + i < S) ? pe[(size_t)(q0 + i) * qstride] : 0.0;
+        acc += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+      }
       if (bias) acc += (double)bias[e];
       float l = (float)acc;
       if (l == 0.0f) l = 0.0f;
@@ -232,7 +240,7 @@ int router_splits(int T, int d, int E) {
   if (T == 0) return 1;
   const int tiles = ((T + RT - 1) / RT) * ((E + RE - 1) / RE);
   const int want = (256 + tiles - 1) / tiles;
-  return max(1, min(want, d / RK));
+  return max(1, min(min(want, 32), d / RK));
 }
 
 hipError_t launch_router(int dtype, const void* x, const void* w, const int32_t* k, int T, int d, int E, int k_max,
