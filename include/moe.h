@@ -73,6 +73,15 @@ typedef enum {
   MOE_PATH_GEMM = 2     /* LDS-tiled grouped GEMM on MFMA (compute-bound prefill) */
 } moe_path;
 
+/* Router algorithm.  Both produce identical ids, order and weights (the
+ * routing contract below); they differ only in cost. */
+typedef enum {
+  MOE_ROUTER_AUTO = 0,      /* screened for bf16 when T * E * d >= 2^30, else float64 */
+  MOE_ROUTER_FLOAT64 = 1,   /* every logit summed in float64 (split-K tiles) */
+  MOE_ROUTER_SCREENED = 2   /* bf16 only: MFMA logits with a proven error bound pick the
+                               candidates; only candidates get the float64 sum */
+} moe_router;
+
 /* Workspace owners, for moe_workspace_size. */
 typedef enum {
   MOE_OP_ROUTE = 0,
@@ -91,7 +100,8 @@ typedef enum {
  *   d, I: multiples of 128, 128 <= d, I <= 65536
  *   1 <= E <= 1024, 1 <= k_max <= E
  *   I_shared: 0 (no shared expert) or a multiple of 128 up to 65536
- *   dtype: MOE_F32 or MOE_BF16; path: a moe_path value
+ *   dtype: MOE_F32 or MOE_BF16; path: a moe_path value; router: a moe_router
+ *   value (MOE_ROUTER_SCREENED needs bf16)
  *   routed_scale: finite (1.0 for the plain renormalised softmax)
  */
 typedef struct moe_desc {
@@ -103,6 +113,7 @@ typedef struct moe_desc {
   int32_t I_shared;     /* intermediate size of the always-on shared expert, 0 = none */
   int32_t dtype;        /* moe_dtype */
   int32_t path;         /* moe_path */
+  int32_t router;       /* moe_router */
   float routed_scale;   /* factor applied to the renormalised routing weights */
 } moe_desc;
 
@@ -117,6 +128,15 @@ typedef void* moe_stream_t;
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED.
  */
 moe_status moe_workspace_size(const moe_desc* desc, int32_t op, size_t* bytes);
+
+/*
+ * The FFN path `desc->path` resolves to, for the routed experts and for the
+ * shared expert (MOE_PATH_STREAM or MOE_PATH_GEMM).  AUTO picks the grouped
+ * GEMM for bf16 when T * k_max >= 64 * E (routed) or T >= 256 (shared), i.e.
+ * from the shape alone; fp32 always streams.  Host only.
+ * Errors: as moe_workspace_size; MOE_ERR_UNSUPPORTED for MOE_PATH_GEMM in fp32.
+ */
+moe_status moe_resolve_path(const moe_desc* desc, int32_t* routed_path, int32_t* shared_path);
 
 /*
  * Router and per-token top-k (MoE-Prism §III-B2, normalised and scaled router
@@ -177,8 +197,9 @@ moe_status moe_ffn(const moe_desc* desc, const void* x, const void* w_gate, cons
                    moe_stream_t stream);
 
 /*
- * The two halves of moe_ffn's routed part, one kernel launch each, so that a
- * caller can place or time them separately.
+ * The two halves of moe_ffn's routed part, so that a caller can place or time
+ * them separately: one kernel launch each on the streaming path; on the GEMM
+ * path each first rebuilds the GEMM's row-block table (a one-workgroup kernel).
  *   moe_ffn_gateup: h ELT [T*k_max][I] out, H of the rows above.
  *   moe_ffn_down:   y_perm ELT [T*k_max][d] out from h.
  * `ws`: scratch of moe_workspace_size(MOE_OP_FFN) bytes (may be shared with

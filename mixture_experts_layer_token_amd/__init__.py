@@ -15,16 +15,17 @@ import torch
 from . import _lib
 from ._lib import (MOE_BF16, MOE_DEV_BAD_K, MOE_F32, MOE_OP_COMBINE, MOE_OP_FFN,  # noqa: F401
                    MOE_OP_FORWARD, MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_PATH_AUTO, MOE_PATH_GEMM,
-                   MOE_PATH_STREAM, moe_desc)
+                   MOE_PATH_STREAM, MOE_ROUTER_AUTO, MOE_ROUTER_FLOAT64, MOE_ROUTER_SCREENED, moe_desc)
 
 __all__ = [
-    "MoeError", "make_desc", "workspace_size", "alloc_workspace", "moe_route", "moe_permute",
+    "MoeError", "make_desc", "workspace_size", "resolve_path", "alloc_workspace", "moe_route", "moe_permute",
     "moe_ffn", "moe_ffn_gateup", "moe_ffn_down", "moe_combine", "moe_forward", "forward",
     "library_path",
 ]
 
 _DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 _PATHS = {"auto": MOE_PATH_AUTO, "stream": MOE_PATH_STREAM, "gemm": MOE_PATH_GEMM}
+_ROUTERS = {"auto": MOE_ROUTER_AUTO, "float64": MOE_ROUTER_FLOAT64, "screened": MOE_ROUTER_SCREENED}
 
 
 class MoeError(RuntimeError):
@@ -40,8 +41,10 @@ def library_path() -> str:
 
 
 def make_desc(T: int, d: int, E: int, I: int, k_max: int, *, I_shared: int = 0,
-              dtype=torch.bfloat16, path: str = "auto", routed_scale: float = 1.0) -> moe_desc:
-    return moe_desc(T, d, E, I, k_max, I_shared, _DTYPES[dtype], _PATHS[path], routed_scale)
+              dtype=torch.bfloat16, path: str = "auto", router: str = "auto",
+              routed_scale: float = 1.0) -> moe_desc:
+    return moe_desc(T, d, E, I, k_max, I_shared, _DTYPES[dtype], _PATHS[path], _ROUTERS[router],
+                    routed_scale)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -63,6 +66,14 @@ def workspace_size(desc: moe_desc, op: int = MOE_OP_FORWARD) -> int:
     n = ctypes.c_size_t(0)
     _check("moe_workspace_size", _lib.load().moe_workspace_size(ctypes.byref(desc), op, ctypes.byref(n)))
     return n.value
+
+
+def resolve_path(desc: moe_desc):
+    """(routed, shared) FFN path names that desc.path resolves to."""
+    r, sh = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("moe_resolve_path", _lib.load().moe_resolve_path(ctypes.byref(desc), ctypes.byref(r), ctypes.byref(sh)))
+    names = {MOE_PATH_STREAM: "stream", MOE_PATH_GEMM: "gemm"}
+    return names[r.value], names[sh.value]
 
 
 def alloc_workspace(desc: moe_desc, op: int = MOE_OP_FORWARD, device="cuda") -> Optional[torch.Tensor]:
@@ -126,13 +137,13 @@ def moe_forward(desc, x, w_router, router_bias, k, w_gate, w_up, w_down, ws_gate
 def forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: Optional[torch.Tensor],
             k: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
             shared: Optional[Sequence[torch.Tensor]] = None, *, k_max: int, routed_scale: float = 1.0,
-            path: str = "auto", ws: Optional[torch.Tensor] = None, stream=None):
+            path: str = "auto", router: str = "auto", ws: Optional[torch.Tensor] = None, stream=None):
     """Allocate the outputs (and a workspace unless given) and run moe_forward.
     Returns (out [T, d], stats int32 [E+2] = counts, n_active, A, dev_status int32 [1])."""
     T, d = x.shape
     E, I, _ = w_gate.shape
     Is = shared[0].shape[0] if shared is not None else 0
-    desc = make_desc(T, d, E, I, k_max, I_shared=Is, dtype=x.dtype, path=path,
+    desc = make_desc(T, d, E, I, k_max, I_shared=Is, dtype=x.dtype, path=path, router=router,
                      routed_scale=routed_scale)
     if ws is None:
         ws = alloc_workspace(desc, MOE_OP_FORWARD, x.device)

@@ -29,8 +29,6 @@
 
 namespace moe {
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
 template <typename T, bool NT>
 __device__ __forceinline__ uint4 ldw(const T* p) {
   if (NT) {

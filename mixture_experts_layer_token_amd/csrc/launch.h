@@ -19,6 +19,15 @@ hipError_t launch_router(int dtype, const void* x, const void* w, const int32_t*
 // Sums the S slices in order, adds the bias, rounds to float32, selects top-k_t.
 hipError_t launch_topk(const double* part, int S, const float* bias, const int32_t* tok_off, int T, int E,
                        float scale, int32_t* ids, float* wts, hipStream_t st);
+// Token offsets alone (one workgroup).
+hipError_t launch_tok_offsets(const int32_t* k, int T, int k_max, int32_t* tok_off, int32_t* status, hipStream_t st);
+
+// route_screen.hip -- bf16 only: MFMA logits with an error bound screen the
+// candidates; exact fp64 logits for candidates; same selection and weights.
+// approx, absum: float [T][E] scratch.  tok_off must be ready.
+hipError_t launch_router_screen(const void* x, const void* w, const float* bias, const int32_t* tok_off, int T,
+                                int d, int E, float scale, float* approx, float* absum, int32_t* ids, float* wts,
+                                hipStream_t st);
 
 // permute.hip
 constexpr int PERM_BLOCK = 256;  // tokens per histogram block
@@ -39,6 +48,17 @@ hipError_t launch_ffn_gateup_stream(int dtype, const void* in, const int32_t* ro
                                     void* h, int N, int K, hipStream_t st);
 hipError_t launch_ffn_down_stream(int dtype, const void* h, const void* wd, const int32_t* grp_off, int G,
                                   int dense_rows, int rows_max, void* y, int N, int K, hipStream_t st);
+
+// ffn_gemm.hip -- grouped-GEMM FFN (bf16): same semantics as the streaming
+// kernels.  tile_off [G+1] (row blocks of 128 per group) is built on the device
+// by launch_gemm_tiles; rb_bound >= tile_off[G] sizes the grid (shape only).
+int gemm_tile_bound(int A_cap, int G);
+hipError_t launch_gemm_tiles(const int32_t* grp_off, int G, int32_t* tile_off, hipStream_t st);
+hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
+                                  const int32_t* grp_off, const int32_t* tile_off, int G, int dense_rows,
+                                  int rb_bound, void* h, int N, int K, hipStream_t st);
+hipError_t launch_ffn_down_gemm(const void* h, const void* wd, const int32_t* grp_off, const int32_t* tile_off,
+                                int G, int dense_rows, int rb_bound, void* y, int N, int K, hipStream_t st);
 
 // combine.hip
 hipError_t launch_combine(int dtype, const void* y, const void* y_shared, const int32_t* tok_off,

@@ -23,6 +23,8 @@ moe_status check_desc(const moe_desc* d) {
   if (!d) return MOE_ERR_NULL;
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_GEMM) return MOE_ERR_UNSUPPORTED;
+  if (d->router < MOE_ROUTER_AUTO || d->router > MOE_ROUTER_SCREENED) return MOE_ERR_UNSUPPORTED;
+  if (d->router == MOE_ROUTER_SCREENED && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->T < 0 || d->E < 1 || d->E > 1024 || d->k_max < 1 || d->k_max > d->E) return MOE_ERR_SHAPE;
   if (d->d < kDimQuantum || d->d > 65536 || d->d % kDimQuantum) return MOE_ERR_SHAPE;
   if (d->I < kDimQuantum || d->I > 65536 || d->I % kDimQuantum) return MOE_ERR_SHAPE;
@@ -52,13 +54,27 @@ struct Carver {
 size_t a_cap(const moe_desc& d) { return (size_t)d.T * d.k_max; }
 int n_blocks(const moe_desc& d) { return (d.T + PERM_BLOCK - 1) / PERM_BLOCK; }
 
-struct RouteWs { double* part; int splits; };
+struct RouteWs { double* part; int splits; float* approx; float* absum; bool screened; };
 struct PermWs { int32_t* block_counts; int32_t* block_base; };
-struct FfnWs { void* h; void* h_sh; };
+struct FfnWs { int32_t* tile_off; void* h; void* h_sh; };
+
+// Large bf16 batches route through the MFMA screen (exact on the candidates);
+// smaller ones sum every logit in float64 directly.
+bool screened_router(const moe_desc& d) {
+  if (d.router == MOE_ROUTER_SCREENED) return true;
+  if (d.router == MOE_ROUTER_FLOAT64) return false;
+  return d.dtype == MOE_BF16 && (double)d.T * d.E * d.d >= 1073741824.0;
+}
 
 void plan_route(const moe_desc& d, Carver& c, RouteWs& w) {
+  w.screened = screened_router(d);
   w.splits = router_splits(d.T, d.d, d.E);
-  w.part = c.take<double>((size_t)w.splits * d.T * d.E);
+  const size_t te = (size_t)d.T * d.E;
+  const size_t bytes = w.screened ? 2 * te * sizeof(float) : (size_t)w.splits * te * sizeof(double);
+  char* p = static_cast<char*>(c.take_bytes(bytes));
+  w.part = reinterpret_cast<double*>(p);
+  w.approx = reinterpret_cast<float*>(p);
+  w.absum = p ? reinterpret_cast<float*>(p + te * sizeof(float)) : nullptr;
 }
 void plan_permute(const moe_desc& d, Carver& c, PermWs& w) {
   const size_t n = (size_t)n_blocks(d) * d.E;
@@ -66,6 +82,7 @@ void plan_permute(const moe_desc& d, Carver& c, PermWs& w) {
   w.block_base = c.take<int32_t>(n);
 }
 void plan_ffn(const moe_desc& d, Carver& c, FfnWs& w) {
+  w.tile_off = c.take<int32_t>((size_t)d.E + 1);
   w.h = c.take_bytes(a_cap(d) * d.I * elt_size(d));
   w.h_sh = d.I_shared ? c.take_bytes((size_t)d.T * d.I_shared * elt_size(d)) : nullptr;
 }
@@ -130,14 +147,34 @@ moe_status check_ws(const moe_desc& d, int op, const void* ws, size_t ws_bytes) 
 }
 
 moe_status path_ok(const moe_desc& d) {
-  // Only the weight-streaming kernels exist so far; AUTO resolves to them.
-  return d.path == MOE_PATH_GEMM ? MOE_ERR_UNSUPPORTED : MOE_OK;
+  // The grouped GEMM is a bf16 kernel.
+  return (d.path == MOE_PATH_GEMM && d.dtype != MOE_BF16) ? MOE_ERR_UNSUPPORTED : MOE_OK;
+}
+
+// Path choice.  Rows per expert set the roofline: a few rows per expert make the
+// FFN a weight stream (HBM-bound), hundreds make it a dense contraction.  AUTO
+// takes the grouped GEMM when the bound on assignments per expert,
+// T * k_max / E, reaches 64 (shape only, so the choice never depends on routing).
+bool routed_gemm(const moe_desc& d) {
+  if (d.dtype != MOE_BF16 || d.path == MOE_PATH_STREAM) return false;
+  if (d.path == MOE_PATH_GEMM) return true;
+  return (int64_t)d.T * d.k_max >= (int64_t)64 * d.E;
+}
+bool shared_gemm(const moe_desc& d) {
+  if (d.dtype != MOE_BF16 || d.path == MOE_PATH_STREAM) return false;
+  return d.path == MOE_PATH_GEMM || d.T >= 256;
 }
 
 // ---- stage bodies (arguments already validated) ----
 
 moe_status do_route(const moe_desc& d, const void* x, const void* wr, const float* bias, const int32_t* k,
                     int32_t* tok_off, int32_t* ids, float* w, int32_t* status, const RouteWs& ws, hipStream_t st) {
+  if (ws.screened) {
+    hipError_t e = launch_tok_offsets(k, d.T, d.k_max, tok_off, status, st);
+    if (e == hipSuccess)
+      e = launch_router_screen(x, wr, bias, tok_off, d.T, d.d, d.E, d.routed_scale, ws.approx, ws.absum, ids, w, st);
+    return launched(e);
+  }
   hipError_t e = launch_router(d.dtype, x, wr, k, d.T, d.d, d.E, d.k_max, ws.splits, ws.part, tok_off, status, st);
   if (e == hipSuccess) e = launch_topk(ws.part, ws.splits, bias, tok_off, d.T, d.E, d.routed_scale, ids, w, st);
   return launched(e);
@@ -150,21 +187,42 @@ moe_status do_permute(const moe_desc& d, const int32_t* tok_off, const int32_t* 
                                  perm_tok, perm_src, inv_perm, n_active, stats, st));
 }
 
+// tile_off: row-block table of the grouped GEMM (built when `build_tiles`).
 moe_status do_gateup(const moe_desc& d, const void* x, const void* wg, const void* wu, const int32_t* expert_off,
-                     const int32_t* perm_tok, void* h, hipStream_t st) {
+                     const int32_t* perm_tok, void* h, int32_t* tile_off, bool build_tiles, hipStream_t st) {
+  if (routed_gemm(d)) {
+    hipError_t e = build_tiles ? launch_gemm_tiles(expert_off, d.E, tile_off, st) : hipSuccess;
+    if (e == hipSuccess)
+      e = launch_ffn_gateup_gemm(x, perm_tok, wg, wu, expert_off, tile_off, d.E, 0, gemm_tile_bound((int)a_cap(d), d.E),
+                                 h, d.I, d.d, st);
+    return launched(e);
+  }
   // a token selects an expert at most once: at most T rows per expert
   return launched(launch_ffn_gateup_stream(d.dtype, x, perm_tok, wg, wu, expert_off, d.E, 0, d.T, h, d.I, d.d, st));
 }
 
 moe_status do_down(const moe_desc& d, const void* h, const void* wd, const int32_t* expert_off, void* y,
-                   hipStream_t st) {
+                   int32_t* tile_off, bool build_tiles, hipStream_t st) {
+  if (routed_gemm(d)) {
+    hipError_t e = build_tiles ? launch_gemm_tiles(expert_off, d.E, tile_off, st) : hipSuccess;
+    if (e == hipSuccess)
+      e = launch_ffn_down_gemm(h, wd, expert_off, tile_off, d.E, 0, gemm_tile_bound((int)a_cap(d), d.E), y, d.d, d.I,
+                               st);
+    return launched(e);
+  }
   return launched(launch_ffn_down_stream(d.dtype, h, wd, expert_off, d.E, 0, d.T, y, d.d, d.I, st));
 }
 
 moe_status do_shared(const moe_desc& d, const void* x, const void* sg, const void* su, const void* sd, void* h_sh,
                      void* y_sh, hipStream_t st) {
-  hipError_t e =
-      launch_ffn_gateup_stream(d.dtype, x, nullptr, sg, su, nullptr, 1, d.T, d.T, h_sh, d.I_shared, d.d, st);
+  hipError_t e;
+  if (shared_gemm(d)) {
+    const int rb = gemm_tile_bound(d.T, 0);  // row blocks of the dense shared expert
+    e = launch_ffn_gateup_gemm(x, nullptr, sg, su, nullptr, nullptr, 1, d.T, rb, h_sh, d.I_shared, d.d, st);
+    if (e == hipSuccess) e = launch_ffn_down_gemm(h_sh, sd, nullptr, nullptr, 1, d.T, rb, y_sh, d.d, d.I_shared, st);
+    return launched(e);
+  }
+  e = launch_ffn_gateup_stream(d.dtype, x, nullptr, sg, su, nullptr, 1, d.T, d.T, h_sh, d.I_shared, d.d, st);
   if (e == hipSuccess) e = launch_ffn_down_stream(d.dtype, h_sh, sd, nullptr, 1, d.T, d.T, y_sh, d.d, d.I_shared, st);
   return launched(e);
 }
@@ -183,6 +241,15 @@ moe_status moe_workspace_size(const moe_desc* desc, int32_t op, size_t* bytes) {
   if (!bytes) return MOE_ERR_NULL;
   if (op < MOE_OP_ROUTE || op > MOE_OP_FORWARD) return MOE_ERR_UNSUPPORTED;
   *bytes = ws_size(*desc, op);
+  return MOE_OK;
+}
+
+moe_status moe_resolve_path(const moe_desc* desc, int32_t* routed_path, int32_t* shared_path) {
+  MOE_TRY(check_desc(desc));
+  if (!routed_path || !shared_path) return MOE_ERR_NULL;
+  MOE_TRY(path_ok(*desc));
+  *routed_path = routed_gemm(*desc) ? MOE_PATH_GEMM : MOE_PATH_STREAM;
+  *shared_path = shared_gemm(*desc) ? MOE_PATH_GEMM : MOE_PATH_STREAM;
   return MOE_OK;
 }
 
@@ -221,27 +288,35 @@ moe_status moe_permute(const moe_desc* desc, const int32_t* tok_off, const int32
 moe_status moe_ffn_gateup(const moe_desc* desc, const void* x, const void* w_gate, const void* w_up,
                           const int32_t* expert_off, const int32_t* perm_tok, void* h, void* ws, size_t ws_bytes,
                           moe_stream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   MOE_TRY(check_desc(desc));
   const moe_desc& d = *desc;
   MOE_TRY(path_ok(d));
+  FfnWs fw{};
+  if (routed_gemm(d)) {
+    MOE_TRY(check_ws(d, MOE_OP_FFN, ws, ws_bytes));
+    Carver c(ws);
+    plan_ffn(d, c, fw);
+  }
   if (!tok_ptr(d, x) || !w_gate || !w_up || !expert_off || !tok_ptr(d, perm_tok) || !tok_ptr(d, h))
     return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(h)) return MOE_ERR_ALIGN;
-  return do_gateup(d, x, w_gate, w_up, expert_off, perm_tok, h, static_cast<hipStream_t>(stream));
+  return do_gateup(d, x, w_gate, w_up, expert_off, perm_tok, h, fw.tile_off, true, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_ffn_down(const moe_desc* desc, const void* h, const void* w_down, const int32_t* expert_off,
                         void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   MOE_TRY(check_desc(desc));
   const moe_desc& d = *desc;
   MOE_TRY(path_ok(d));
+  FfnWs fw{};
+  if (routed_gemm(d)) {
+    MOE_TRY(check_ws(d, MOE_OP_FFN, ws, ws_bytes));
+    Carver c(ws);
+    plan_ffn(d, c, fw);
+  }
   if (!tok_ptr(d, h) || !w_down || !expert_off || !tok_ptr(d, y_perm)) return MOE_ERR_NULL;
   if (!aligned16(h) || !aligned16(w_down) || !aligned16(y_perm)) return MOE_ERR_ALIGN;
-  return do_down(d, h, w_down, expert_off, y_perm, static_cast<hipStream_t>(stream));
+  return do_down(d, h, w_down, expert_off, y_perm, fw.tile_off, true, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_ffn(const moe_desc* desc, const void* x, const void* w_gate, const void* w_up, const void* w_down,
@@ -264,8 +339,8 @@ moe_status moe_ffn(const moe_desc* desc, const void* x, const void* w_gate, cons
   FfnWs fw;
   plan_ffn(d, c, fw);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  MOE_TRY(do_gateup(d, x, w_gate, w_up, expert_off, perm_tok, fw.h, st));
-  MOE_TRY(do_down(d, fw.h, w_down, expert_off, y_perm, st));
+  MOE_TRY(do_gateup(d, x, w_gate, w_up, expert_off, perm_tok, fw.h, fw.tile_off, true, st));
+  MOE_TRY(do_down(d, fw.h, w_down, expert_off, y_perm, fw.tile_off, false, st));
   if (d.I_shared) MOE_TRY(do_shared(d, x, ws_gate, ws_up, ws_down, fw.h_sh, y_shared, st));
   return MOE_OK;
 }
@@ -303,8 +378,8 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router
   MOE_TRY(do_route(d, x, w_router, router_bias, k, fw.tok_off, fw.ids, fw.w, status, fw.r, st));
   MOE_TRY(do_permute(d, fw.tok_off, fw.ids, fw.counts, fw.expert_off, fw.perm_tok, fw.perm_src, fw.inv_perm,
                      fw.n_active, stats, fw.p, st));
-  MOE_TRY(do_gateup(d, x, w_gate, w_up, fw.expert_off, fw.perm_tok, fw.f.h, st));
-  MOE_TRY(do_down(d, fw.f.h, w_down, fw.expert_off, fw.y, st));
+  MOE_TRY(do_gateup(d, x, w_gate, w_up, fw.expert_off, fw.perm_tok, fw.f.h, fw.f.tile_off, true, st));
+  MOE_TRY(do_down(d, fw.f.h, w_down, fw.expert_off, fw.y, fw.f.tile_off, false, st));
   if (d.I_shared) MOE_TRY(do_shared(d, x, ws_gate, ws_up, ws_down, fw.f.h_sh, fw.y_sh, st));
   return do_combine(d, fw.y, fw.y_sh, fw.tok_off, fw.w, fw.inv_perm, out, st);
 }

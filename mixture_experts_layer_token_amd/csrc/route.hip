@@ -236,6 +236,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ pa
 }
 
 // ---------------------------------------------------------------------------
+// Standalone token-offset scan (the screened router has no partial-logit pass).
+__global__ __launch_bounds__(256) void tok_offsets_kernel(const int32_t* __restrict__ k, int T, int k_max,
+                                                          int32_t* __restrict__ tok_off, int32_t* __restrict__ status) {
+  __shared__ int32_t part[257];
+  token_offsets_block(k, T, k_max, tok_off, status, part, part + 256);
+}
+
+hipError_t launch_tok_offsets(const int32_t* k, int T, int k_max, int32_t* tok_off, int32_t* status, hipStream_t st) {
+  hipLaunchKernelGGL(tok_offsets_kernel, dim3(1), dim3(256), 0, st, k, T, k_max, tok_off, status);
+  return hipGetLastError();
+}
+
 int router_splits(int T, int d, int E) {
   if (T == 0) return 1;
   const int tiles = ((T + RT - 1) / RT) * ((E + RE - 1) / RE);

@@ -12,22 +12,22 @@ from workloads import ExpertView, Layer, to_f64
 TOL = {"bf16": dict(rel_l2=1e-2, max_abs=5e-2), "f32": dict(rel_l2=1e-5, max_abs=None)}
 
 
-def desc_of(layer: Layer, path: str = "auto") -> moe.moe_desc:
+def desc_of(layer: Layer, path: str = "auto", router: str = "auto") -> moe.moe_desc:
     c = layer.cfg
     E, I, d = layer.w_gate.shape
     Is = layer.ws_gate.shape[0] if layer.ws_gate is not None else 0
     return moe.make_desc(layer.x.shape[0], d, E, I, c.k_max, I_shared=Is, dtype=layer.x.dtype,
-                         path=path, routed_scale=c.routed_scale)
+                         path=path, router=router, routed_scale=c.routed_scale)
 
 
 def shared_of(layer: Layer):
     return None if layer.ws_gate is None else (layer.ws_gate, layer.ws_up, layer.ws_down)
 
 
-def run_stages(layer: Layer, path: str = "auto") -> dict:
+def run_stages(layer: Layer, path: str = "auto", router: str = "auto") -> dict:
     """moe_route -> moe_permute -> moe_ffn -> moe_combine; returns host copies."""
     dev = layer.device
-    desc = desc_of(layer, path)
+    desc = desc_of(layer, path, router)
     T, d, E, km = desc.T, desc.d, desc.E, desc.k_max
     i32 = dict(dtype=torch.int32, device=dev)
     tok_off = torch.full((T + 1,), -7, **i32)
@@ -60,10 +60,10 @@ def run_stages(layer: Layer, path: str = "auto") -> dict:
                 out=out, A=A)
 
 
-def run_forward(layer: Layer, path: str = "auto"):
+def run_forward(layer: Layer, path: str = "auto", router: str = "auto"):
     out, stats, status = moe.forward(layer.x, layer.w_router, layer.router_bias, layer.k, layer.w_gate,
                                      layer.w_up, layer.w_down, shared_of(layer), k_max=layer.cfg.k_max,
-                                     routed_scale=layer.cfg.routed_scale, path=path)
+                                     routed_scale=layer.cfg.routed_scale, path=path, router=router)
     torch.cuda.synchronize()
     return out, stats.cpu().numpy().astype(np.int64), int(status.item())
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def _desc(**kw):
     base = dict(T=64, d=4096, E=8, I=14336, k_max=2, I_shared=0, dtype=moe.MOE_BF16, path=0,
-                routed_scale=1.0)
+                router=0, routed_scale=1.0)
     base.update(kw)
     return _lib.moe_desc(**base)
 
@@ -57,7 +57,8 @@ def test_workspace_sizes():
 @pytest.mark.parametrize("kw,code", [
     (dict(d=100), 2), (dict(I=64), 2), (dict(E=0), 2), (dict(E=1025, k_max=1), 2),
     (dict(k_max=9), 2), (dict(k_max=0), 2), (dict(T=-1), 2), (dict(I_shared=100), 2),
-    (dict(T=1 << 28, k_max=8), 2), (dict(dtype=7), 3), (dict(path=5), 3),
+    (dict(T=1 << 28, k_max=8), 2), (dict(dtype=7), 3), (dict(path=5), 3), (dict(router=3), 3),
+    (dict(router=2, dtype=0), 3),
     (dict(routed_scale=float("inf")), 2),
 ])
 def test_bad_descriptors_rejected(kw, code):
@@ -77,10 +78,29 @@ def test_entry_points_validate_before_launch():
     assert lib.moe_route(ctypes.byref(d), *fake[:7], None, P(1 << 20), 16, None) == 4
     # misaligned activation
     assert lib.moe_route(ctypes.byref(d), P(4098), *fake[1:7], None, P(1 << 20), 1 << 30, None) == 5
-    # unsupported path on the FFN
+    # the grouped-GEMM FFN needs its workspace (tile table) and is bf16 only
     dg = _desc(T=4, d=128, E=4, I=128, k_max=2, path=moe.MOE_PATH_GEMM)
-    status = lib.moe_ffn_gateup(ctypes.byref(dg), *fake[:6], None, 0, None)
-    assert status in (0, 3) and (status == 3 or os.environ.get("MOE_HAS_GEMM"))
+    assert lib.moe_ffn_gateup(ctypes.byref(dg), *fake[:6], None, 0, None) == 4
+    assert lib.moe_ffn_down(ctypes.byref(dg), *fake[:4], None, 0, None) == 4
+    df = _desc(T=4, d=128, E=4, I=128, k_max=2, path=moe.MOE_PATH_GEMM, dtype=moe.MOE_F32)
+    assert lib.moe_ffn_gateup(ctypes.byref(df), *fake[:6], None, 0, None) == 3
     assert lib.moe_status_str(4) == b"workspace missing or too small"
     with pytest.raises(moe.MoeError):
         moe._check("x", 2)
+
+
+def test_resolve_path_rule():
+    """AUTO: grouped GEMM for bf16 when T*k_max >= 64*E (routed) / T >= 256 (shared)."""
+    import mixture_experts_layer_token_amd as m
+    cases = [((64, 4096, 8, 14336, 2), "stream"), ((8192, 2048, 256, 384, 32), "gemm"),
+             ((4096, 7168, 256, 2048, 8), "gemm"), ((128, 7168, 256, 2048, 8), "stream"),
+             ((256, 2048, 128, 768, 8), "stream"), ((512, 128, 8, 128, 1), "gemm")]
+    for (T, d, E, I, km), want in cases:
+        assert m.resolve_path(m.make_desc(T, d, E, I, km))[0] == want
+    assert m.resolve_path(m.make_desc(4096, 128, 8, 128, 2, I_shared=128))[1] == "gemm"
+    assert m.resolve_path(m.make_desc(128, 128, 8, 128, 2, I_shared=128))[1] == "stream"
+    assert m.resolve_path(m.make_desc(8192, 2048, 256, 384, 32, path="stream")) == ("stream", "stream")
+    import torch
+    assert m.resolve_path(m.make_desc(8192, 256, 8, 128, 8, dtype=torch.float32)) == ("stream", "stream")
+    with pytest.raises(m.MoeError):
+        m.resolve_path(m.make_desc(64, 256, 8, 128, 2, dtype=torch.float32, path="gemm"))

@@ -103,14 +103,15 @@ def test_invalid_k_flagged_and_dropped():
     assert not got["out"][1].any() and not got["out"][3].any()
 
 
-def test_exact_ties_break_to_lower_index():
+@pytest.mark.parametrize("router", ["float64", "screened"])
+def test_exact_ties_break_to_lower_index(router):
     """Zero hidden states make every logit equal its bias; duplicated router
     rows make exactly tied logits for any x."""
     T, E = 40, 16
     layer = make_custom_layer(T=T, d=128, E=E, I=128, k=[5] * T, dtype="bf16", k_max=8, device="cuda")
     layer.x[: T // 2].zero_()
     layer.w_router[1::2].copy_(layer.w_router[0::2])           # experts 2j and 2j+1 tie
-    got = run_stages(layer)
+    got = run_stages(layer, router=router)
     r, p = oracle_routing(layer)
     check_routing(got, r, p)
     assert got["ids"][:5].tolist() == [0, 1, 2, 3, 4]
@@ -165,3 +166,59 @@ def test_graph_capture_replays_any_k():
         ref, ref_stats, _ = run_forward(layer)
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
         assert torch.equal(st.cpu(), torch.as_tensor(ref_stats, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("path", ["stream", "gemm"])
+@pytest.mark.parametrize("T,E,d,I,kmax,Is", [
+    (700, 16, 256, 384, 8, 256),     # ragged row blocks, shared expert over 700 tokens
+    (300, 8, 128, 128, 8, 0),        # every expert has 100-300 rows
+    (1500, 64, 512, 256, 16, 128),   # many experts, uneven rows
+    (40, 32, 384, 128, 4, 0),        # few rows per expert (GEMM tail-only tiles)
+])
+def test_ffn_paths_bf16(path, T, E, d, I, kmax, Is):
+    """Both FFN paths compute the same function on the same routing."""
+    rng = np.random.default_rng(T * E)
+    k = rng.integers(1, kmax + 1, size=T)
+    layer = make_custom_layer(T=T, d=d, E=E, I=I, k=k, dtype="bf16", k_max=kmax, I_shared=Is, zipf=1.0,
+                              seed=E, device="cuda")
+    got = run_stages(layer, path=path)
+    r, p = oracle_routing(layer)
+    check_routing(got, r, p)
+    tokens = sample_tokens(T, 48)
+    err = compare_out(got["out"], oracle_out(layer, tokens), "bf16", tokens)
+    fout, _, _ = run_forward(layer, path=path)
+    torch.testing.assert_close(fout, got["out"], rtol=0, atol=0)
+    _say(f"[paths] {path} T={T} E={E}: {err}")
+
+
+@pytest.mark.parametrize("name,path", [("qwen3_30b_a3b_decode", "gemm"), ("subexpert_prefill", "stream")])
+def test_workload_other_path(name, path):
+    """A workload on the path AUTO does not pick for it."""
+    cfg = CONFIGS[name]
+    layer = make_layer(cfg, "cuda")
+    fout, stats, status = run_forward(layer, path=path)
+    assert status == 0
+    tokens = sample_tokens(cfg.T, 16)
+    compare_out(fout, oracle_out(layer, tokens), cfg.dtype, tokens)
+
+
+@pytest.mark.parametrize("T,E,d,kmax,zipf", [
+    (1000, 256, 2048, 32, 0.0),   # sub-expert-like: many candidates near the cut
+    (777, 64, 1024, 8, 1.1),      # biased router, ragged T
+    (300, 1024, 256, 20, 0.5),    # largest E
+    (129, 8, 4096, 8, 0.0),       # k_t up to E
+])
+def test_screened_router_bit_exact(T, E, d, kmax, zipf):
+    """The MFMA-screened router selects, orders and weights exactly like the
+    float64 router and the oracle (only the cost differs)."""
+    rng = np.random.default_rng(T + E)
+    k = rng.integers(0, kmax + 1, size=T)
+    layer = make_custom_layer(T=T, d=d, E=E, I=128, k=k, dtype="bf16", k_max=kmax, zipf=zipf, seed=E,
+                              device="cuda")
+    layer.x[T // 3].zero_()                                    # a token with all logits = bias
+    got = run_stages(layer, router="screened")
+    ref64 = run_stages(layer, router="float64")
+    r, p = oracle_routing(layer)
+    check_routing(got, r, p)
+    np.testing.assert_array_equal(got["ids"], ref64["ids"])
+    np.testing.assert_array_equal(got["w"], ref64["w"])        # same fp32 logits -> same weights
