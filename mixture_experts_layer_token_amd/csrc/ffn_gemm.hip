@@ -123,67 +123,73 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < NMAT * TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Stage pipeline: LDS is double-buffered and the global loads run PD stages
-  // ahead in a queue of register sets (set 0 = the next stage to store), so a
-  // stage's loads have PD stages of MFMA work to arrive.  Every iteration is
-  // the same straight-line code (a branch around the loads made the compiler
-  // keep the registers in scratch): steps past the end re-read the last stage
-  // (cached) and the final store goes to the idle buffer, which nobody reads.
-  u32x4_t ra[PD][ACH], rbv[PD][BCH];
+  // Stage pipeline: LDS is double-buffered; the global loads of stage s + 1
+  // are issued one stage ahead into one of two register sets used in turn
+  // (the K loop is unrolled by two, so no set is ever copied).  K / BK is
+  // even (K is a multiple of 128), and every iteration is the same
+  // straight-line code -- a branch around the loads made the compiler keep the
+  // registers in scratch: steps past the end re-read the last stage (cached)
+  // and the final store goes to the idle buffer, which nobody reads.
+  static_assert(PD == 1, "one stage of register prefetch");
+  u32x4_t ra0[ACH], rb0[BCH], ra1[ACH], rb1[BCH];
   const int nk = K / BK;
 #pragma unroll
   for (int i = 0; i < ACH; ++i) st_lds16(&As[0][adst[i]], ld_g16(asrc[i]));
 #pragma unroll
   for (int i = 0; i < BCH; ++i) st_lds16(&Bs[0][bdst[i]], ld_g16(bsrc[i]));
+  {
+    const int k1 = min(1, nk - 1) * BK;
 #pragma unroll
-  for (int p = 0; p < PD; ++p) {
-    const int kp = min(p + 1, nk - 1) * BK;
+    for (int i = 0; i < ACH; ++i) ra0[i] = ld_g16(asrc[i] + k1);
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) ra[p][i] = ld_g16(asrc[i] + kp);
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) rbv[p][i] = ld_g16(bsrc[i] + kp);
+    for (int i = 0; i < BCH; ++i) rb0[i] = ld_g16(bsrc[i] + k1);
   }
   __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    // stage kt + 1 + PD into a fresh set
-    u32x4_t na[ACH], nb[BCH];
-    const int kn = min(kt + 1 + PD, nk - 1) * BK;
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) na[i] = ld_g16(asrc[i] + kn);
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) nb[i] = ld_g16(bsrc[i] + kn);
+  auto mma_stage = [&](const bf16_t* as, const bf16_t* bs) {
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
       u32x4_t bfr[TM];   // activation rows: B operand
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        bfr[i] = ld_lds16(&As[st][(wm * (BM / WGM) + i * 16 + lr) * LD + kk + lg * 8]);
+      for (int i = 0; i < TM; ++i) bfr[i] = ld_lds16(&as[(wm * (BM / WGM) + i * 16 + lr) * LD + kk + lg * 8]);
 #pragma unroll
       for (int q = 0; q < NMAT * TN; ++q) {
         const int mat = q / TN, tj = q % TN;
-        const u32x4_t afr = ld_lds16(&Bs[st][(mat * BN + wn * (BN / WGN) + tj * 16 + lr) * LD + kk + lg * 8]);
+        const u32x4_t afr = ld_lds16(&bs[(mat * BN + wn * (BN / WGN) + tj * 16 + lr) * LD + kk + lg * 8]);
 #pragma unroll
         for (int i = 0; i < TM; ++i) acc[i][q] = Mfma<bf16_t>::step(afr, bfr[i], acc[i][q]);
       }
     }
-    // set 0 holds stage kt + 1
+  };
+
+  for (int kt = 0; kt < nk; kt += 2) {
+    // even stage kt: LDS buffer 0; set 0 holds stage kt+1, set 1 receives kt+2
+    {
+      const int kn = min(kt + 2, nk - 1) * BK;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) st_lds16(&As[st ^ 1][adst[i]], ra[0][i]);
+      for (int i = 0; i < ACH; ++i) ra1[i] = ld_g16(asrc[i] + kn);
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) st_lds16(&Bs[st ^ 1][bdst[i]], rbv[0][i]);
-#pragma unroll
-    for (int p = 0; p + 1 < PD; ++p) {
-#pragma unroll
-      for (int i = 0; i < ACH; ++i) ra[p][i] = ra[p + 1][i];
-#pragma unroll
-      for (int i = 0; i < BCH; ++i) rbv[p][i] = rbv[p + 1][i];
+      for (int i = 0; i < BCH; ++i) rb1[i] = ld_g16(bsrc[i] + kn);
     }
+    mma_stage(As[0], Bs[0]);
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) ra[PD - 1][i] = na[i];
+    for (int i = 0; i < ACH; ++i) st_lds16(&As[1][adst[i]], ra0[i]);
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) rbv[PD - 1][i] = nb[i];
+    for (int i = 0; i < BCH; ++i) st_lds16(&Bs[1][bdst[i]], rb0[i]);
+    __syncthreads();
+    // odd stage kt+1: LDS buffer 1; set 1 holds kt+2, set 0 receives kt+3
+    {
+      const int kn = min(kt + 3, nk - 1) * BK;
+#pragma unroll
+      for (int i = 0; i < ACH; ++i) ra0[i] = ld_g16(asrc[i] + kn);
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) rb0[i] = ld_g16(bsrc[i] + kn);
+    }
+    mma_stage(As[1], Bs[1]);
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) st_lds16(&As[0][adst[i]], ra1[i]);
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) st_lds16(&Bs[0][bdst[i]], rb1[i]);
     __syncthreads();
   }
 
