@@ -10,58 +10,95 @@
 //            (MoE-Prism §III-B1, Eq. (1)), input rows gathered through perm_tok;
 //   down:    [rows_e, I] x W_down[e]^T.
 //
-// Tiling: a workgroup (4 waves, 2 x 2) owns BM rows x BN columns of each of
+// Tiling.  A workgroup of WM x WN waves owns BM rows x BNW columns of each of
 // NMAT weight matrices (NMAT = 2 for the gate/up pair, 1 for down).  K advances
-// BK = 64 at a time through double-buffered LDS (one barrier per step; the next
-// step's global loads are in flight during the MFMAs).  A wave holds
-// (BM/2) x (BN/2) outputs per matrix as 16x16 tiles of v_mfma_f32_16x16x32_bf16
-// with the weights as the A operand, so a lane ends with 4 consecutive output
-// columns of one row (8-byte stores).  LDS rows are padded by 16 bytes so the
-// 16 rows a fragment read touches fall in distinct banks.
+// 64 at a time through a ring of STAGES LDS buffers filled by global->LDS DMA
+// loads (global_load_lds_dwordx4): no VGPR staging, so the registers hold only
+// accumulators and fragments, and the loads of the next stages are in flight
+// while the current one is multiplied.  A wave holds (BM/WM) x (BNW/WN)
+// outputs per matrix as 32x32 tiles of v_mfma_f32_32x32x16_bf16 with the
+// weights as the A operand (a lane ends with 4 consecutive output columns of a
+// row: 8-byte stores).
 //
-// Scheduling: the tiles of expert e are the row blocks [tile_off[e],
+// LDS layout.  A stage holds each tile row as 128 bytes (64 bf16 of K) with no
+// padding; the eight 16-byte chunks of row r are XOR-permuted by (r >> 1) & 7.
+// A DMA instruction writes 1 KB (64 lanes x 16 bytes) to consecutive LDS
+// addresses, so the permutation is applied by choosing which global chunk each
+// lane fetches.  With it, the fragment reads of the 32x32x16 MFMA (32 rows x
+// two adjacent chunks per instruction) are free of bank conflicts on gfx950.
+//
+// Schedule.  Within a stage, the fragment reads of k16 step s+1 alternate with
+// the MFMAs of step s (sched_group_barrier), so both fragment sets are live.
+// The barrier that hands over stage kt+1 sits before the last k16 step of stage
+// kt; after it the buffer of stage kt is refilled (stage kt+STAGES) and the
+// first fragments of stage kt+1 are read during the last MFMAs of stage kt.
+// One barrier per stage; the DMA waits are explicit vmcnt counts.
+//
+// Scheduling of tiles.  The tiles of expert e are the row blocks [tile_off[e],
 // tile_off[e+1]) (tile_off is built on the device from the per-expert counts),
 // times the N tiles.  The grid is sized by an upper bound that depends only on
 // the layer shape; each workgroup reads the real tile count and maps its id so
-// that XCD x (ids x, x+8, ...) takes one contiguous range of (row block, N tile)
-// pairs: the N tiles of a row block, then the next row block of the same
-// expert, which keeps an expert's weights in that XCD's L2.
+// that XCD x (ids x, x+8, ...) takes one contiguous range of (row tile, N tile)
+// pairs: the N tiles of a row tile, then the next row tile of the same expert,
+// which keeps an expert's weights and gathered rows in that XCD's L2.
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
 
-constexpr int GBM = 256;  // rows per row block of the tile table (a multiple of every BM used)
-constexpr int GPAD = 8;   // LDS row padding (elements)
+namespace {
 
-__device__ __forceinline__ void st_lds16(bf16_t* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
-__device__ __forceinline__ u32x4_t ld_lds16(const bf16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
-__device__ __forceinline__ u32x4_t ld_g16(const bf16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+constexpr int GBM = 256;  // rows per row block of the tile table (a multiple of every BM used)
+constexpr int BK = 64;    // K elements per stage: one 128-byte LDS row per tile row
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N> __device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+// vm_wait<n> for a wave-uniform n in [0, NMAX] (the count must be an immediate).
+template <int NMAX> __device__ __forceinline__ void vm_wait_dyn(int n) {
+  if constexpr (NMAX <= 0) {
+    vm_wait<0>();
+  } else {
+    if (n >= NMAX) vm_wait<NMAX>();
+    else vm_wait_dyn<NMAX - 1>(n);
+  }
+}
+__device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// byte offset of 16-byte chunk c of tile row r within a stage operand
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) * 16); }
+
+}  // namespace
 
 // MODE 0: gate/up pair + SwiGLU epilogue.  MODE 1: down projection.
-// BM x BN (per weight matrix) output tile, BK K-elements per LDS stage,
-// WGM x WGN waves.  BM must divide GBM (row blocks of the tile table).
-template <int MODE, int BM, int BN, int BK, int WGM, int WGN, int PD>
-__global__ __launch_bounds__(64 * WGM * WGN) void ffn_gemm_kernel(
+template <int MODE, int BM, int BNW, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     const bf16_t* __restrict__ in, const int32_t* __restrict__ row_map, const bf16_t* __restrict__ w0,
     const bf16_t* __restrict__ w1, const int32_t* __restrict__ grp_off, const int32_t* __restrict__ tile_off, int G,
     int dense_rows, bf16_t* __restrict__ out, int N, int K) {
-  constexpr int NT = 64 * WGM * WGN;       // threads
+  constexpr int NW = WM * WN;
   constexpr int NMAT = (MODE == 0) ? 2 : 1;
-  constexpr int BROWS = NMAT * BN;         // weight rows staged per stage
-  constexpr int LD = BK + GPAD;            // LDS row pitch (elements)
-  constexpr int TM = BM / WGM / 16;        // 16-row tiles per wave
-  constexpr int TN = BN / WGN / 16;        // 16-column tiles per wave per matrix
-  constexpr int ACH = BM * BK / 8 / NT;    // 16-byte chunks of the row tile per thread
-  constexpr int BCH = BROWS * BK / 8 / NT; // ... of the weight tile
-  constexpr int SUB = GBM / BM;            // tiles per table row block
-  static_assert(ACH >= 1 && BCH >= 1 && ACH * NT * 8 == BM * BK && BCH * NT * 8 == BROWS * BK, "chunking");
-  static_assert(TM >= 1 && TN >= 1 && GBM % BM == 0, "tiling");
-  __shared__ bf16_t As[2][BM * LD];
-  __shared__ bf16_t Bs[2][BROWS * LD];
+  constexpr int WROWS = NMAT * BNW;                          // weight rows per stage
+  constexpr int XBYTES = BM * 128, SBYTES = XBYTES + WROWS * 128;
+  constexpr int XI = BM / 8 / NW, WI = WROWS / 8 / NW;        // DMA instructions per wave per stage
+  constexpr int TMW = BM / WM / 32, TNW = BNW / WN / 32;      // 32x32 tiles per wave
+  constexpr int SUB = GBM / BM;
+  constexpr int KS = BK / 16;                                 // k16 steps per stage
+  static_assert(XI * 8 * NW == BM && WI * 8 * NW == WROWS, "DMA split");
+  static_assert(TMW >= 1 && TNW >= 1 && GBM % BM == 0, "tiling");
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  __shared__ __attribute__((aligned(1024))) char lds[STAGES * SBYTES];
 
   // ---- which (group, row tile, N tile) this workgroup owns ----
-  const int nN = N / BN;
+  const int nN = N / BNW;
   const int total_rb = grp_off ? tile_off[G] : (dense_rows + GBM - 1) / GBM;
   const int total = total_rb * SUB * nN;
   const int per = (total + 7) >> 3;
@@ -85,134 +122,163 @@ __global__ __launch_bounds__(64 * WGM * WGN) void ffn_gemm_kernel(
   }
   const int m0 = mb * GBM + (mtile % SUB) * BM;  // first row of the tile within the group
   if (m0 >= rows) return;                        // the row block's rows end in an earlier sub-tile
-  const int n0 = nt * BN;                        // first output column
+  const int n0 = nt * BNW;                       // first output column
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave / WGN, wn = wave % WGN;
-  const int lr = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
 
-  // ---- global source pointers of this thread's 16-byte chunks ----
-  const bf16_t* asrc[ACH];
-  int adst[ACH];
+  // ---- DMA sources.  Instruction j of this wave fills tile rows 8q .. 8q+7
+  // (q = j*NW + wave); lane i covers row 8q + i/8, LDS chunk i%8, which holds
+  // K chunk (i%8) ^ swz(row).  Rows past the group's end are not fetched
+  // (their columns are never stored); the decision is made per instruction and
+  // wave, so a wave issues the same count of DMA loads in every stage. ----
+  const bf16_t* xsrc[XI];
+  bool xon[XI], xany[XI];
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int c = tid + NT * i;
-    const int r = c / (BK / 8), kc = c % (BK / 8);
+  for (int j = 0; j < XI; ++j) {
+    const int r = 8 * (j * NW + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
     int m = m0 + r;
-    if (m >= rows) m = rows - 1;                       // tail rows: any valid row, results unused
+    xon[j] = m < rows;
+    xany[j] = __builtin_amdgcn_ballot_w64(xon[j]) != 0;
+    if (m >= rows) m = rows - 1;
     const int src = row_map ? row_map[row0 + m] : row0 + m;
-    asrc[i] = in + (size_t)src * K + kc * 8;
-    adst[i] = r * LD + kc * 8;
+    xsrc[j] = in + (size_t)src * K + c * 8;
   }
   const size_t gstride = (size_t)N * K;
-  const bf16_t* bsrc[BCH];
-  int bdst[BCH];
+  const bf16_t* wsrc[WI];
 #pragma unroll
-  for (int i = 0; i < BCH; ++i) {
-    const int c = tid + NT * i;
-    const int r = c / (BK / 8), kc = c % (BK / 8);
-    const bf16_t* wbase = (MODE == 0 && r >= BN) ? w1 : w0;
-    const int wr = (MODE == 0 && r >= BN) ? r - BN : r;
-    bsrc[i] = wbase + g * gstride + (size_t)(n0 + wr) * K + kc * 8;
-    bdst[i] = r * LD + kc * 8;
+  for (int j = 0; j < WI; ++j) {
+    const int r = 8 * (j * NW + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    const bf16_t* wb = (MODE == 0 && r >= BNW) ? w1 : w0;
+    const int wr = (MODE == 0 && r >= BNW) ? r - BNW : r;
+    wsrc[j] = wb + g * gstride + (size_t)(n0 + wr) * K + c * 8;
   }
-
-  f32x4_t acc[TM][NMAT * TN];
+  int per_stage = WI;  // DMA instructions this wave issues per stage
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int j = 0; j < XI; ++j) per_stage += xany[j] ? 1 : 0;
+  auto issue = [&](int kt, int buf) {
+    char* sb = lds + buf * SBYTES;
+    const int ko = kt * BK;
 #pragma unroll
-    for (int j = 0; j < NMAT * TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Stage pipeline: LDS is double-buffered; the global loads of stage s + 1
-  // are issued one stage ahead into one of two register sets used in turn
-  // (the K loop is unrolled by two, so no set is ever copied).  K / BK is
-  // even (K is a multiple of 128), and every iteration is the same
-  // straight-line code -- a branch around the loads made the compiler keep the
-  // registers in scratch: steps past the end re-read the last stage (cached)
-  // and the final store goes to the idle buffer, which nobody reads.
-  static_assert(PD == 1, "one stage of register prefetch");
-  u32x4_t ra0[ACH], rb0[BCH], ra1[ACH], rb1[BCH];
-  const int nk = K / BK;
+    for (int j = 0; j < XI; ++j)
+      if (xany[j] && xon[j])
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(xsrc[j] + ko), (lds_ptr_t)(sb + (j * NW + wave) * 1024), 16, 0, 0);
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) st_lds16(&As[0][adst[i]], ld_g16(asrc[i]));
-#pragma unroll
-  for (int i = 0; i < BCH; ++i) st_lds16(&Bs[0][bdst[i]], ld_g16(bsrc[i]));
-  {
-    const int k1 = min(1, nk - 1) * BK;
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) ra0[i] = ld_g16(asrc[i] + k1);
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) rb0[i] = ld_g16(bsrc[i] + k1);
-  }
-  __syncthreads();
-
-  auto mma_stage = [&](const bf16_t* as, const bf16_t* bs) {
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      u32x4_t bfr[TM];   // activation rows: B operand
-#pragma unroll
-      for (int i = 0; i < TM; ++i) bfr[i] = ld_lds16(&as[(wm * (BM / WGM) + i * 16 + lr) * LD + kk + lg * 8]);
-#pragma unroll
-      for (int q = 0; q < NMAT * TN; ++q) {
-        const int mat = q / TN, tj = q % TN;
-        const u32x4_t afr = ld_lds16(&bs[(mat * BN + wn * (BN / WGN) + tj * 16 + lr) * LD + kk + lg * 8]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) acc[i][q] = Mfma<bf16_t>::step(afr, bfr[i], acc[i][q]);
-      }
-    }
+    for (int j = 0; j < WI; ++j)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[j] + ko), (lds_ptr_t)(sb + XBYTES + (j * NW + wave) * 1024),
+                                       16, 0, 0);
   };
 
-  for (int kt = 0; kt < nk; kt += 2) {
-    // even stage kt: LDS buffer 0; set 0 holds stage kt+1, set 1 receives kt+2
-    {
-      const int kn = min(kt + 2, nk - 1) * BK;
+  f32x16_t acc[NMAT * TNW][TMW];
 #pragma unroll
-      for (int i = 0; i < ACH; ++i) ra1[i] = ld_g16(asrc[i] + kn);
+  for (int q = 0; q < NMAT * TNW; ++q)
 #pragma unroll
-      for (int i = 0; i < BCH; ++i) rb1[i] = ld_g16(bsrc[i] + kn);
+    for (int i = 0; i < TMW; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[q][i][e] = 0.f;
+
+  // ---- fragments: lane l supplies tile row (l % 32) and K chunk 2s + l/32 of
+  // k16 step s (A = weights, B = activations) ----
+  const int l32 = lane & 31, lh = lane >> 5;
+  u32x4_t fw[2][NMAT * TNW], fx[2][TMW];
+  auto load_frags = [&](int buf, int s, int slot) {
+    const char* xs = lds + buf * SBYTES;
+    const char* ws = xs + XBYTES;
+#pragma unroll
+    for (int i = 0; i < TMW; ++i)
+      fx[slot][i] = *reinterpret_cast<const u32x4_t*>(xs + lds_off(wm * (BM / WM) + i * 32 + l32, 2 * s + lh));
+#pragma unroll
+    for (int q = 0; q < NMAT * TNW; ++q) {
+      const int mat = q / TNW, tj = q % TNW;
+      fw[slot][q] = *reinterpret_cast<const u32x4_t*>(
+          ws + lds_off(mat * BNW + wn * (BNW / WN) + tj * 32 + l32, 2 * s + lh));
     }
-    mma_stage(As[0], Bs[0]);
+  };
+  auto mma = [&](int slot) {
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) st_lds16(&As[1][adst[i]], ra0[i]);
+    for (int q = 0; q < NMAT * TNW; ++q)
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) st_lds16(&Bs[1][bdst[i]], rb0[i]);
-    __syncthreads();
-    // odd stage kt+1: LDS buffer 1; set 1 holds kt+2, set 0 receives kt+3
-    {
-      const int kn = min(kt + 3, nk - 1) * BK;
+      for (int i = 0; i < TMW; ++i)
+        acc[q][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fw[slot][q]),
+                                                            __builtin_bit_cast(bf16x8_t, fx[slot][i]), acc[q][i], 0, 0, 0);
+  };
+  // one k16 step: the next step's fragment reads alternate with this step's MFMAs
+  constexpr int NFRAG = NMAT * TNW + TMW, NMMA = NMAT * TNW * TMW;
+  static_assert(NMMA >= NFRAG, "fewer MFMAs than fragment reads per step");
+  auto interleave = [&]() {
 #pragma unroll
-      for (int i = 0; i < ACH; ++i) ra0[i] = ld_g16(asrc[i] + kn);
-#pragma unroll
-      for (int i = 0; i < BCH; ++i) rb0[i] = ld_g16(bsrc[i] + kn);
+    for (int i = 0; i < NFRAG; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
-    mma_stage(As[1], Bs[1]);
+    if constexpr (NMMA > NFRAG) __builtin_amdgcn_sched_group_barrier(0x008, NMMA - NFRAG, 0);
+  };
+
+  const int nk = K / BK;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) st_lds16(&As[0][adst[i]], ra1[i]);
+  for (int s = 0; s < STAGES; ++s)
+    if (s < nk) issue(s, s);
+  // stage 0 landed: the stages issued after it may still be in flight
+  vm_wait_dyn<(STAGES - 1) * (XI + WI)>((min(nk, STAGES) - 1) * per_stage);
+  compiler_fence();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+  load_frags(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt % STAGES;
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) st_lds16(&Bs[0][bdst[i]], rb1[i]);
-    __syncthreads();
+    for (int s = 0; s < KS; ++s) {
+      if (s + 1 < KS) {
+        load_frags(buf, s + 1, (s + 1) & 1);
+      } else {
+        // Stage kt+1 landed (later stages may still be in flight) and this
+        // wave's reads of buffer kt are complete: after the barrier the buffer
+        // is refilled.  On the last stage nothing is waited for and the reads
+        // below touch a buffer whose values are never used, which keeps the
+        // step branch-free so its reads interleave with its MFMAs.
+        const int later = max(0, min(nk - 1, kt + STAGES - 1) - (kt + 1));
+        vm_wait_dyn<(STAGES - 2) * (XI + WI)>(later * per_stage);
+        lgkm_wait0();
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        if (kt + STAGES < nk) issue(kt + STAGES, buf);
+        load_frags((kt + 1) % STAGES, 0, 0);
+      }
+      mma(s & 1);
+      interleave();
+    }
   }
 
-  // ---- epilogue: lane holds D[n = 4*lg + r][m = lr] of each 16x16 tile ----
+  // ---- epilogue: element e of acc[q][i] is D[n = 8*(e/4) + 4*lh + e%4][m = l32]
+  // of the 32x32 tile (n: weight row, m: tile row) ----
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm * (BM / WGM) + i * 16 + lr;
+  for (int i = 0; i < TMW; ++i) {
+    const int m = m0 + wm * (BM / WM) + i * 32 + l32;
     if (m >= rows) continue;
-    bf16_t* orow = out + (size_t)(row0 + m) * N + n0 + wn * (BN / WGN) + 4 * lg;
+    bf16_t* orow = out + (size_t)(row0 + m) * N + n0 + wn * (BNW / WN) + 4 * lh;
 #pragma unroll
-    for (int tj = 0; tj < TN; ++tj) {
-      uint32_t o0, o1;
-      if (MODE == 0) {
-        const f32x4_t gt = acc[i][tj], up = acc[i][TN + tj];
-        o0 = (uint32_t)f32_to_bf16(silu(gt[0]) * up[0]) | ((uint32_t)f32_to_bf16(silu(gt[1]) * up[1]) << 16);
-        o1 = (uint32_t)f32_to_bf16(silu(gt[2]) * up[2]) | ((uint32_t)f32_to_bf16(silu(gt[3]) * up[3]) << 16);
-      } else {
-        const f32x4_t y = acc[i][tj];
-        o0 = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
-        o1 = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+    for (int tj = 0; tj < TNW; ++tj)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        uint32_t o0, o1;
+        if (MODE == 0) {
+          const f32x16_t& gt = acc[tj][i];
+          const f32x16_t& up = acc[TNW + tj][i];
+          o0 = (uint32_t)f32_to_bf16(silu(gt[4 * e4 + 0]) * up[4 * e4 + 0]) |
+               ((uint32_t)f32_to_bf16(silu(gt[4 * e4 + 1]) * up[4 * e4 + 1]) << 16);
+          o1 = (uint32_t)f32_to_bf16(silu(gt[4 * e4 + 2]) * up[4 * e4 + 2]) |
+               ((uint32_t)f32_to_bf16(silu(gt[4 * e4 + 3]) * up[4 * e4 + 3]) << 16);
+        } else {
+          const f32x16_t& y = acc[tj][i];
+          o0 = (uint32_t)f32_to_bf16(y[4 * e4 + 0]) | ((uint32_t)f32_to_bf16(y[4 * e4 + 1]) << 16);
+          o1 = (uint32_t)f32_to_bf16(y[4 * e4 + 2]) | ((uint32_t)f32_to_bf16(y[4 * e4 + 3]) << 16);
+        }
+        *reinterpret_cast<uint2*>(orow + tj * 32 + 8 * e4) = make_uint2(o0, o1);
       }
-      *reinterpret_cast<uint2*>(orow + tj * 16) = make_uint2(o0, o1);
-    }
   }
 }
 
@@ -237,14 +303,15 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
 
 int gemm_tile_bound(int A_cap, int G) { return (A_cap + GBM - 1) / GBM + G; }
 
-template <int MODE, int BM, int BN, int BK, int WGM, int WGN, int PD>
-hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, const void* w0, const void* w1,
-                               const int32_t* grp_off, const int32_t* tile_off, int G, int dense_rows, int rb_bound,
-                               void* out, int N, int K, hipStream_t st) {
-  const long long total = (long long)rb_bound * (GBM / BM) * (N / BN);
+template <int MODE, int BM, int BNW, int WM, int WN, int STAGES>
+static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, const void* w0, const void* w1,
+                                      const int32_t* grp_off, const int32_t* tile_off, int G, int dense_rows,
+                                      int rb_bound, void* out, int N, int K, hipStream_t st) {
+  if (N % BNW != 0 || K % BK != 0) return hipErrorInvalidValue;
+  const long long total = (long long)rb_bound * (GBM / BM) * (N / BNW);
   if (total == 0) return hipSuccess;
   const long long blocks = ((total + 7) / 8) * 8;
-  hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BN, BK, WGM, WGN, PD>), dim3((unsigned)blocks), dim3(64 * WGM * WGN), 0,
+  hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, STAGES>), dim3((unsigned)blocks), dim3(64 * WM * WN), 0,
                      st, (const bf16_t*)in, row_map, (const bf16_t*)w0, (const bf16_t*)w1, grp_off, tile_off, G,
                      dense_rows, (bf16_t*)out, N, K);
   return hipGetLastError();
@@ -255,17 +322,35 @@ hipError_t launch_gemm_tiles(const int32_t* grp_off, int G, int32_t* tile_off, h
   return hipGetLastError();
 }
 
+// Tile height: 256-row tiles when groups hold hundreds of rows (fewer weight
+// re-reads per flop); 128-row tiles when they hold about a hundred, where a
+// 256-row tile would be mostly empty (there the layer streams weights, and the
+// 3-stage ring keeps more of them in flight).
 hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
                                   const int32_t* grp_off, const int32_t* tile_off, int G, int dense_rows,
-                                  int rb_bound, void* h, int N, int K, hipStream_t st) {
-  return launch_gemm_variant<0, 128, 64, 64, 2, 2, 1>(in, row_map, wg, wu, grp_off, tile_off, G, dense_rows, rb_bound,
-                                                   h, N, K, st);
+                                  int rb_bound, int rows_hint, void* h, int N, int K, hipStream_t st) {
+  if (rows_hint >= GBM)
+    return launch_gemm_variant<0, 256, 128, 4, 2, 2>(in, row_map, wg, wu, grp_off, tile_off, G, dense_rows, rb_bound,
+                                                    h, N, K, st);
+  return launch_gemm_variant<0, 128, 128, 2, 4, 3>(in, row_map, wg, wu, grp_off, tile_off, G, dense_rows, rb_bound, h,
+                                                  N, K, st);
 }
 
 hipError_t launch_ffn_down_gemm(const void* h, const void* wd, const int32_t* grp_off, const int32_t* tile_off,
-                                int G, int dense_rows, int rb_bound, void* y, int N, int K, hipStream_t st) {
-  return launch_gemm_variant<1, 128, 128, 64, 2, 2, 1>(h, nullptr, wd, wd, grp_off, tile_off, G, dense_rows, rb_bound,
-                                                    y, N, K, st);
+                                int G, int dense_rows, int rb_bound, int rows_hint, void* y, int N, int K,
+                                hipStream_t st) {
+  if (rows_hint >= GBM) {
+    if (N % 256 == 0)
+      return launch_gemm_variant<1, 256, 256, 4, 2, 2>(h, nullptr, wd, wd, grp_off, tile_off, G, dense_rows, rb_bound,
+                                                      y, N, K, st);
+    return launch_gemm_variant<1, 256, 128, 4, 2, 2>(h, nullptr, wd, wd, grp_off, tile_off, G, dense_rows, rb_bound, y,
+                                                    N, K, st);
+  }
+  if (N % 256 == 0)
+    return launch_gemm_variant<1, 128, 256, 2, 2, 3>(h, nullptr, wd, wd, grp_off, tile_off, G, dense_rows, rb_bound, y,
+                                                    N, K, st);
+  return launch_gemm_variant<1, 128, 128, 2, 2, 3>(h, nullptr, wd, wd, grp_off, tile_off, G, dense_rows, rb_bound, y,
+                                                  N, K, st);
 }
 
 }  // namespace moe

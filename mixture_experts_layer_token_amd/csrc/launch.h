@@ -50,15 +50,18 @@ hipError_t launch_ffn_down_stream(int dtype, const void* h, const void* wd, cons
                                   int dense_rows, int rows_max, void* y, int N, int K, hipStream_t st);
 
 // ffn_gemm.hip -- grouped-GEMM FFN (bf16): same semantics as the streaming
-// kernels.  tile_off [G+1] (row blocks of 128 per group) is built on the device
-// by launch_gemm_tiles; rb_bound >= tile_off[G] sizes the grid (shape only).
+// kernels.  tile_off [G+1] (row blocks of 256 per group) is built on the device
+// by launch_gemm_tiles; rb_bound >= tile_off[G] sizes the grid and rows_hint
+// (an estimate of rows per group) picks the tile height -- both from the shape
+// only.  N must be a multiple of 128 and K of 64.
 int gemm_tile_bound(int A_cap, int G);
 hipError_t launch_gemm_tiles(const int32_t* grp_off, int G, int32_t* tile_off, hipStream_t st);
 hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
                                   const int32_t* grp_off, const int32_t* tile_off, int G, int dense_rows,
-                                  int rb_bound, void* h, int N, int K, hipStream_t st);
+                                  int rb_bound, int rows_hint, void* h, int N, int K, hipStream_t st);
 hipError_t launch_ffn_down_gemm(const void* h, const void* wd, const int32_t* grp_off, const int32_t* tile_off,
-                                int G, int dense_rows, int rb_bound, void* y, int N, int K, hipStream_t st);
+                                int G, int dense_rows, int rb_bound, int rows_hint, void* y, int N, int K,
+                                hipStream_t st);
 
 // combine.hip
 hipError_t launch_combine(int dtype, const void* y, const void* y_shared, const int32_t* tok_off,

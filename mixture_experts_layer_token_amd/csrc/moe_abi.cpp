@@ -160,6 +160,9 @@ bool routed_gemm(const moe_desc& d) {
   if (d.path == MOE_PATH_GEMM) return true;
   return (int64_t)d.T * d.k_max >= (int64_t)64 * d.E;
 }
+// Rows-per-expert estimate for the GEMM tile choice: the bound T * k_max / E
+// (shape only).
+int rows_hint(const moe_desc& d) { return (int)std::min<int64_t>((int64_t)d.T * d.k_max / d.E, d.T); }
 bool shared_gemm(const moe_desc& d) {
   if (d.dtype != MOE_BF16 || d.path == MOE_PATH_STREAM) return false;
   return d.path == MOE_PATH_GEMM || d.T >= 256;
@@ -194,7 +197,7 @@ moe_status do_gateup(const moe_desc& d, const void* x, const void* wg, const voi
     hipError_t e = build_tiles ? launch_gemm_tiles(expert_off, d.E, tile_off, st) : hipSuccess;
     if (e == hipSuccess)
       e = launch_ffn_gateup_gemm(x, perm_tok, wg, wu, expert_off, tile_off, d.E, 0, gemm_tile_bound((int)a_cap(d), d.E),
-                                 h, d.I, d.d, st);
+                                 rows_hint(d), h, d.I, d.d, st);
     return launched(e);
   }
   // a token selects an expert at most once: at most T rows per expert
@@ -206,8 +209,8 @@ moe_status do_down(const moe_desc& d, const void* h, const void* wd, const int32
   if (routed_gemm(d)) {
     hipError_t e = build_tiles ? launch_gemm_tiles(expert_off, d.E, tile_off, st) : hipSuccess;
     if (e == hipSuccess)
-      e = launch_ffn_down_gemm(h, wd, expert_off, tile_off, d.E, 0, gemm_tile_bound((int)a_cap(d), d.E), y, d.d, d.I,
-                               st);
+      e = launch_ffn_down_gemm(h, wd, expert_off, tile_off, d.E, 0, gemm_tile_bound((int)a_cap(d), d.E), rows_hint(d),
+                               y, d.d, d.I, st);
     return launched(e);
   }
   return launched(launch_ffn_down_stream(d.dtype, h, wd, expert_off, d.E, 0, d.T, y, d.d, d.I, st));
@@ -218,8 +221,9 @@ moe_status do_shared(const moe_desc& d, const void* x, const void* sg, const voi
   hipError_t e;
   if (shared_gemm(d)) {
     const int rb = gemm_tile_bound(d.T, 0);  // row blocks of the dense shared expert
-    e = launch_ffn_gateup_gemm(x, nullptr, sg, su, nullptr, nullptr, 1, d.T, rb, h_sh, d.I_shared, d.d, st);
-    if (e == hipSuccess) e = launch_ffn_down_gemm(h_sh, sd, nullptr, nullptr, 1, d.T, rb, y_sh, d.d, d.I_shared, st);
+    e = launch_ffn_gateup_gemm(x, nullptr, sg, su, nullptr, nullptr, 1, d.T, rb, d.T, h_sh, d.I_shared, d.d, st);
+    if (e == hipSuccess)
+      e = launch_ffn_down_gemm(h_sh, sd, nullptr, nullptr, 1, d.T, rb, d.T, y_sh, d.d, d.I_shared, st);
     return launched(e);
   }
   e = launch_ffn_gateup_stream(d.dtype, x, nullptr, sg, su, nullptr, 1, d.T, d.T, h_sh, d.I_shared, d.d, st);
