@@ -197,14 +197,22 @@ moe_status moe_ffn(const moe_desc* desc, const void* x, const void* w_gate, cons
                    moe_stream_t stream);
 
 /*
- * The two halves of moe_ffn's routed part, so that a caller can place or time
- * them separately: one kernel launch each on the streaming path; on the GEMM
- * path each first rebuilds the GEMM's row-block table (a one-workgroup kernel).
+ * The routed part of moe_ffn as three calls, so that a caller can place or
+ * time the two FFN halves separately (one kernel launch each):
+ *   moe_ffn_plan:   writes the row-block work table of the FFN kernels into
+ *                   `ws` from expert_off (one one-workgroup kernel).  Each
+ *                   expert's rows are cut into fixed-size blocks and listed;
+ *                   the list's length bound depends on the shape only, so the
+ *                   FFN launch grids do too.  Must precede moe_ffn_gateup /
+ *                   moe_ffn_down on the same `ws` and stream, and be repeated
+ *                   whenever expert_off changes.
  *   moe_ffn_gateup: h ELT [T*k_max][I] out, H of the rows above.
  *   moe_ffn_down:   y_perm ELT [T*k_max][d] out from h.
  * `ws`: scratch of moe_workspace_size(MOE_OP_FFN) bytes (may be shared with
- * moe_ffn's; h must not alias it).
+ * moe_ffn's; h must not alias it).  Errors: as moe_ffn.
  */
+moe_status moe_ffn_plan(const moe_desc* desc, const int32_t* expert_off, void* ws, size_t ws_bytes,
+                        moe_stream_t stream);
 moe_status moe_ffn_gateup(const moe_desc* desc, const void* x, const void* w_gate,
                           const void* w_up, const int32_t* expert_off, const int32_t* perm_tok,
                           void* h, void* ws, size_t ws_bytes, moe_stream_t stream);

@@ -19,7 +19,7 @@ from ._lib import (MOE_BF16, MOE_DEV_BAD_K, MOE_F32, MOE_OP_COMBINE, MOE_OP_FFN,
 
 __all__ = [
     "MoeError", "make_desc", "workspace_size", "resolve_path", "alloc_workspace", "moe_route", "moe_permute",
-    "moe_ffn", "moe_ffn_gateup", "moe_ffn_down", "moe_combine", "moe_forward", "forward",
+    "moe_ffn", "moe_ffn_plan", "moe_ffn_gateup", "moe_ffn_down", "moe_combine", "moe_forward", "forward",
     "library_path",
 ]
 
@@ -106,6 +106,11 @@ def moe_ffn(desc, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, expert_off, 
         ctypes.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(ws_gate),
         _ptr(ws_up), _ptr(ws_down), _ptr(expert_off), _ptr(perm_tok), _ptr(y_perm), _ptr(y_shared),
         _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_ffn_plan(desc, expert_off, ws, stream=None) -> None:
+    _check("moe_ffn_plan", _lib.load().moe_ffn_plan(
+        ctypes.byref(desc), _ptr(expert_off), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_ffn_gateup(desc, x, w_gate, w_up, expert_off, perm_tok, h, ws=None, stream=None) -> None:

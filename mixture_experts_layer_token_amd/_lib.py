@@ -36,6 +36,7 @@ SIGNATURES = {
     "moe_permute": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
     "moe_ffn": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
                 c_ptr, c_size, c_ptr],
+    "moe_ffn_plan": [_P, c_ptr, c_ptr, c_size, c_ptr],
     "moe_ffn_gateup": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
     "moe_ffn_down": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
     "moe_combine": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr],

@@ -34,13 +34,14 @@
 // first fragments of stage kt+1 are read during the last MFMAs of stage kt.
 // One barrier per stage; the DMA waits are explicit vmcnt counts.
 //
-// Scheduling of tiles.  The tiles of expert e are the row blocks [tile_off[e],
-// tile_off[e+1]) (tile_off is built on the device from the per-expert counts),
-// times the N tiles.  The grid is sized by an upper bound that depends only on
-// the layer shape; each workgroup reads the real tile count and maps its id so
-// that XCD x (ids x, x+8, ...) takes one contiguous range of (row tile, N tile)
-// pairs: the N tiles of a row tile, then the next row tile of the same expert,
-// which keeps an expert's weights and gathered rows in that XCD's L2.
+// Scheduling of tiles.  The rows of each expert are cut into row blocks of 256
+// listed in a row-block table built on the device from the per-expert counts;
+// a row block is GBM/BM row tiles, each times the N tiles.  The grid is sized
+// by the table's bound, which depends only on the layer shape; each workgroup
+// reads the real block count and maps its id so that XCD x (ids x, x+8, ...)
+// takes one contiguous range of (row tile, N tile) pairs: the N tiles of a row
+// tile, then the next row tile of the same expert, which keeps an expert's
+// weights and gathered rows in that XCD's L2.
 #include "common.h"
 #include "launch.h"
 
@@ -82,8 +83,8 @@ __device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ sw
 template <int MODE, int BM, int BNW, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     const bf16_t* __restrict__ in, const int32_t* __restrict__ row_map, const bf16_t* __restrict__ w0,
-    const bf16_t* __restrict__ w1, const int32_t* __restrict__ grp_off, const int32_t* __restrict__ tile_off, int G,
-    int dense_rows, bf16_t* __restrict__ out, int N, int K) {
+    const bf16_t* __restrict__ w1, const int4* __restrict__ blocks, int bound, int dense_rows,
+    bf16_t* __restrict__ out, int N, int K) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = (MODE == 0) ? 2 : 1;
   constexpr int WROWS = NMAT * BNW;                          // weight rows per stage
@@ -97,9 +98,9 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
   __shared__ __attribute__((aligned(1024))) char lds[STAGES * SBYTES];
 
-  // ---- which (group, row tile, N tile) this workgroup owns ----
+  // ---- which (row block, row tile, N tile) this workgroup owns ----
   const int nN = N / BNW;
-  const int total_rb = grp_off ? tile_off[G] : (dense_rows + GBM - 1) / GBM;
+  const int total_rb = blocks ? blocks[bound].x : (dense_rows + GBM - 1) / GBM;
   const int total = total_rb * SUB * nN;
   const int per = (total + 7) >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -108,21 +109,20 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   if (logical >= total) return;
   const int mtile = logical / nN, nt = logical - mtile * nN;
   const int rb = mtile / SUB;
-  int g = 0, row0 = 0, rows = dense_rows, mb = rb;
-  if (grp_off) {
-    int lo = 0, hi = G - 1;  // last g with tile_off[g] <= rb
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (tile_off[mid] <= rb) lo = mid; else hi = mid - 1;
-    }
-    g = lo;
-    row0 = grp_off[g];
-    rows = grp_off[g + 1] - row0;
-    mb = rb - tile_off[g];
+  int g, row0, rows;  // group, first row and rows of the row block
+  if (blocks) {
+    const int4 b = blocks[rb];
+    g = b.x;
+    row0 = b.y;
+    rows = b.z;
+  } else {
+    g = 0;
+    row0 = rb * GBM;
+    rows = min(GBM, dense_rows - row0);
   }
-  const int m0 = mb * GBM + (mtile % SUB) * BM;  // first row of the tile within the group
-  if (m0 >= rows) return;                        // the row block's rows end in an earlier sub-tile
-  const int n0 = nt * BNW;                       // first output column
+  const int m0 = (mtile % SUB) * BM;  // first row of the tile within the row block
+  if (m0 >= rows) return;             // the block's rows end in an earlier sub-tile
+  const int n0 = nt * BNW;            // first output column
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -282,43 +282,21 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   }
 }
 
-// tile_off[g] = sum over g' < g of ceil(rows_g' / GBM); one workgroup.
-__global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restrict__ grp_off, int G,
-                                                          int32_t* __restrict__ tile_off) {
-  __shared__ int32_t sc[1024];
-  const int g = threadIdx.x;
-  int v = 0;
-  if (g < G) v = (grp_off[g + 1] - grp_off[g] + GBM - 1) / GBM;
-  sc[g] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int u = g >= off ? sc[g - off] : 0;
-    __syncthreads();
-    sc[g] += u;
-    __syncthreads();
-  }
-  if (g < G) tile_off[g] = sc[g] - v;
-  if (g == 1023) tile_off[G] = sc[1023];
-}
-
-int gemm_tile_bound(int A_cap, int G) { return (A_cap + GBM - 1) / GBM + G; }
+int gemm_row_block() { return GBM; }
 
 template <int MODE, int BM, int BNW, int WM, int WN, int STAGES>
 static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, const void* w0, const void* w1,
-                                      const int32_t* grp_off, const int32_t* tile_off, int G, int dense_rows,
-                                      int rb_bound, void* out, int N, int K, hipStream_t st) {
+                                      const int4* blocks, int bound, int dense_rows, void* out, int N, int K,
+                                      hipStream_t st) {
   if (N % BNW != 0 || K % BK != 0) return hipErrorInvalidValue;
+  const int rb_bound = blocks ? bound : (dense_rows + GBM - 1) / GBM;
   const long long total = (long long)rb_bound * (GBM / BM) * (N / BNW);
   if (total == 0) return hipSuccess;
-  const long long blocks = ((total + 7) / 8) * 8;
-  hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, STAGES>), dim3((unsigned)blocks), dim3(64 * WM * WN), 0,
-                     st, (const bf16_t*)in, row_map, (const bf16_t*)w0, (const bf16_t*)w1, grp_off, tile_off, G,
-                     dense_rows, (bf16_t*)out, N, K);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_tiles(const int32_t* grp_off, int G, int32_t* tile_off, hipStream_t st) {
-  hipLaunchKernelGGL(gemm_tiles_kernel, dim3(1), dim3(1024), 0, st, grp_off, G, tile_off);
+  const long long nwg = ((total + 7) / 8) * 8;
+  if (nwg > 0x7fffffffLL / (64 * WM * WN)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, STAGES>), dim3((unsigned)nwg), dim3(64 * WM * WN), 0,
+                     st, (const bf16_t*)in, row_map, (const bf16_t*)w0, (const bf16_t*)w1, blocks, bound, dense_rows,
+                     (bf16_t*)out, N, K);
   return hipGetLastError();
 }
 
@@ -327,30 +305,23 @@ hipError_t launch_gemm_tiles(const int32_t* grp_off, int G, int32_t* tile_off, h
 // 256-row tile would be mostly empty (there the layer streams weights, and the
 // 3-stage ring keeps more of them in flight).
 hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
-                                  const int32_t* grp_off, const int32_t* tile_off, int G, int dense_rows,
-                                  int rb_bound, int rows_hint, void* h, int N, int K, hipStream_t st) {
+                                  const int4* blocks, int bound, int dense_rows, int rows_hint, void* h, int N,
+                                  int K, hipStream_t st) {
   if (rows_hint >= GBM)
-    return launch_gemm_variant<0, 256, 128, 4, 2, 2>(in, row_map, wg, wu, grp_off, tile_off, G, dense_rows, rb_bound,
-                                                    h, N, K, st);
-  return launch_gemm_variant<0, 128, 128, 2, 4, 3>(in, row_map, wg, wu, grp_off, tile_off, G, dense_rows, rb_bound, h,
-                                                  N, K, st);
+    return launch_gemm_variant<0, 256, 128, 4, 2, 2>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st);
+  return launch_gemm_variant<0, 128, 128, 2, 4, 3>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st);
 }
 
-hipError_t launch_ffn_down_gemm(const void* h, const void* wd, const int32_t* grp_off, const int32_t* tile_off,
-                                int G, int dense_rows, int rb_bound, int rows_hint, void* y, int N, int K,
-                                hipStream_t st) {
+hipError_t launch_ffn_down_gemm(const void* h, const void* wd, const int4* blocks, int bound, int dense_rows,
+                                int rows_hint, void* y, int N, int K, hipStream_t st) {
   if (rows_hint >= GBM) {
     if (N % 256 == 0)
-      return launch_gemm_variant<1, 256, 256, 4, 2, 2>(h, nullptr, wd, wd, grp_off, tile_off, G, dense_rows, rb_bound,
-                                                      y, N, K, st);
-    return launch_gemm_variant<1, 256, 128, 4, 2, 2>(h, nullptr, wd, wd, grp_off, tile_off, G, dense_rows, rb_bound, y,
-                                                    N, K, st);
+      return launch_gemm_variant<1, 256, 256, 4, 2, 2>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st);
+    return launch_gemm_variant<1, 256, 128, 4, 2, 2>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st);
   }
   if (N % 256 == 0)
-    return launch_gemm_variant<1, 128, 256, 2, 2, 3>(h, nullptr, wd, wd, grp_off, tile_off, G, dense_rows, rb_bound, y,
-                                                    N, K, st);
-  return launch_gemm_variant<1, 128, 128, 2, 2, 3>(h, nullptr, wd, wd, grp_off, tile_off, G, dense_rows, rb_bound, y,
-                                                  N, K, st);
+    return launch_gemm_variant<1, 128, 256, 2, 2, 3>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st);
+  return launch_gemm_variant<1, 128, 128, 2, 2, 3>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st);
 }
 
 }  // namespace moe

@@ -6,17 +6,21 @@
 // weight byte is read exactly once, with 16-byte loads, by one wave, while the
 // few rows routed to that expert ride along on the narrow side of a 16x16 MFMA.
 //
-// Work split.  Grid = (column tiles, groups).  A workgroup is WN x WK waves:
-// WN waves along the output columns, WK waves along K.  A wave owns two 16-row
-// weight tiles:
-//   gate/up: rows c..c+15 of W_gate and of W_up (same 16 output columns)
-//   down:    rows c..c+31 of W_down (two 16-column tiles)
+// Work split.  The rows of each expert group are cut into blocks of 16*SMT
+// rows, listed in a row-block table built on the device (entries past the
+// real count are sentinels), so the grid -- column tiles x table bound --
+// depends only on the layer shape and carries no per-expert slack: a
+// workgroup takes one (row block, column tile) pair.  A workgroup is WN x WK
+// waves: WN waves along the output columns, WK waves along K.  A wave owns TPW
+// 16-row weight tiles:
+//   gate/up: TPW/2 tiles of W_gate rows and the same rows of W_up
+//   down:    TPW tiles of W_down rows
 // and for each K step loads, per lane, KC contiguous elements of one weight
 // row per tile (lane l: row l%16, K offset (l/16)*KC).  The activation rows use
 // the same K indices on the other MFMA side, so the instruction sums exactly
 // the K values the lanes supplied (any consistent K order gives the dot
-// product).  Rows are processed 16*SMT at a time; waves along K add their
-// partial sums through LDS in a fixed order (deterministic).
+// product).  Waves along K add their partial sums through LDS in a fixed
+// order (deterministic).
 //
 // Memory pipeline: the weights of step i+1 are requested before the MFMAs of
 // step i, right after the activation rows of step i, so the in-order wait for
@@ -84,44 +88,163 @@ __device__ __forceinline__ void store4<float>(float* p, float a, float b, float 
 // read 64 contiguous bytes of the row).
 // PD: software-pipeline depth.  The weights and activation rows of step s+PD
 // are requested together before the MFMAs of step s, always with the same
-// number of loads per step (rows past the group's end re-read row tile 0), so
-// the in-order wait for step s leaves PD steps in flight.
-// Rows of a group are cut into blocks of 16*SMT.  grid.x = mgroups x column
-// tiles with the tile index varying fastest: workgroups are dealt to the
-// XCDs round-robin by linear id, so consecutive ids must carry real work, and
-// the row blocks of one tile (id stride = tiles) share an XCD, hence its L2,
-// when the tile count is a multiple of 8.  Row-block slot m takes row blocks
-// m, m + mgroups, ...
-template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL>
-__global__ __launch_bounds__(64 * WN * WK) void ffn_stream_kernel(
-    const T* __restrict__ in, const int32_t* __restrict__ row_map, const T* __restrict__ w0,
-    const T* __restrict__ w1, const int32_t* __restrict__ grp_off, int dense_rows, T* __restrict__ out, int N,
-    int K, int mgroups) {
-  static_assert(MODE == 1 || TPW % 2 == 0, "gate/up tiles come in pairs");
-  constexpr int CPW = (MODE == 0) ? 8 * TPW : 16 * TPW;  // output columns per wave
-  constexpr int NB = WN * CPW;                           // output columns per workgroup
+// number of loads per step, so the in-order wait for step s leaves PD steps in
+// flight.
+// SM: 16-row activation tiles per pass (the block's rows; a block of at most
+// 16 rows runs the SM = 1 body, which loads half the activation bytes).
+template <typename T, int MODE, int KC, int WN, int WK, int SM, int TPW, int PD, bool IL>
+__device__ __forceinline__ void stream_block(const T* __restrict__ in, const int32_t* __restrict__ row_map,
+                                             const T* wa, const T* wb, int K, int kbeg, int lofs, int nsteps,
+                                             int mg, int rows, T* __restrict__ out, int N, int n0, f32x4_t* red) {
   constexpr int LE = 16 / sizeof(T);                     // elements per 16-byte load
   constexpr int LPS = KC / LE;                           // loads per tile row per K step
   constexpr int STEP = 4 * KC;                           // K elements per wave step
   constexpr int NS = PD + 1;                             // register stages
   constexpr int LSTR = IL ? 4 * LE : LE;                 // distance between a lane's loads
   constexpr int HALF = TPW / 2;
-  static_assert(KC % LE == 0, "K step must be whole 16-byte loads");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wn = wave % WN, wk = wave / WN;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int tstride = 16 * K;                // elements between consecutive 16-row tiles
+  // tile j's row pointer is wbase(j) + (j % half) * tstride
+  auto wrow = [&](int j) -> const T* {
+    if (MODE == 0) return (j < HALF ? wa : wb) + (j % HALF) * tstride;
+    return wa + j * tstride;
+  };
+  (void)wb;
+
+  const int mts = (rows + 15) >> 4;  // live row tiles (wave-uniform)
+  const T* xr[SM];
+  bool valid[SM];
+#pragma unroll
+  for (int mt = 0; mt < SM; ++mt) {
+    const int r = mt * 16 + lr;
+    valid[mt] = r < rows;
+    const int src = valid[mt] ? (row_map ? row_map[mg + r] : mg + r) : 0;
+    xr[mt] = in + (size_t)src * K + kbeg + lofs;
+  }
+#pragma unroll
+  for (int mt = 1; mt < SM; ++mt)
+    if (mt >= mts) xr[mt] = xr[0];  // dead row tile: same loads as tile 0, result unused
+  f32x4_t acc[SM][TPW];
+#pragma unroll
+  for (int mt = 0; mt < SM; ++mt)
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) acc[mt][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 Wr[NS][TPW][LPS];
+  uint4 Xr[NS][SM][LPS];
+  auto issue = [&](uint4 (&w)[TPW][LPS], uint4 (&x)[SM][LPS], int step) {
+    const int ko = step * STEP;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int i = 0; i < LPS; ++i) w[j][i] = ldw<T, false>(wrow(j) + ko + i * LSTR);
+#pragma unroll
+    for (int mt = 0; mt < SM; ++mt)
+#pragma unroll
+      for (int i = 0; i < LPS; ++i) x[mt][i] = ld16(xr[mt] + ko + i * LSTR);
+  };
+#pragma unroll
+  for (int p = 0; p < PD; ++p) issue(Wr[p], Xr[p], min(p, nsteps - 1));
+
+  for (int s0 = 0; s0 < nsteps; s0 += NS) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int s = s0 + st;
+      if (s < nsteps) {
+        // requests for step s + PD (the last step repeats: cached, in bounds)
+        issue(Wr[(st + PD) % NS], Xr[(st + PD) % NS], min(s + PD, nsteps - 1));
+#pragma unroll
+        for (int mt = 0; mt < SM; ++mt)
+          if (mt < mts) {
+#pragma unroll
+            for (int i = 0; i < LPS; ++i) {
+              const uint4 b = valid[mt] ? Xr[st][mt][i] : zero_u4();
+#pragma unroll
+              for (int j = 0; j < TPW; ++j) mma_tile<T>(acc[mt][j], Wr[st][j][i], b);
+            }
+          }
+      }
+    }
+  }
+
+  if (WK > 1) {
+    if (wk > 0) {
+#pragma unroll
+      for (int mt = 0; mt < SM; ++mt)
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) red[((((wk - 1) * WN + wn) * SM + mt) * TPW + j) * 64 + lane] = acc[mt][j];
+    }
+    __syncthreads();
+    if (wk == 0) {
+      for (int q = 1; q < WK; ++q) {
+#pragma unroll
+        for (int mt = 0; mt < SM; ++mt)
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) acc[mt][j] += red[((((q - 1) * WN + wn) * SM + mt) * TPW + j) * 64 + lane];
+      }
+    }
+  }
+
+  if (wk == 0) {
+#pragma unroll
+    for (int mt = 0; mt < SM; ++mt) {
+      const int m = mt * 16 + lr;
+      if (mt < mts && m < rows) {
+        T* orow = out + (size_t)(mg + m) * N + n0 + 4 * lg;
+        if (MODE == 0) {
+#pragma unroll
+          for (int j = 0; j < HALF; ++j) {
+            const f32x4_t gt = acc[mt][j], up = acc[mt][j + HALF];
+            store4<T>(orow + 16 * j, silu(gt[0]) * up[0], silu(gt[1]) * up[1], silu(gt[2]) * up[2],
+                      silu(gt[3]) * up[3]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) {
+            const f32x4_t y = acc[mt][j];
+            store4<T>(orow + 16 * j, y[0], y[1], y[2], y[3]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Linear workgroup id = block * tiles + tile.  Workgroups are dealt to the
+// XCDs round-robin by linear id, so when the tile count is a multiple of 8 all
+// row blocks of one column tile (an expert with many rows has several) run
+// on the same XCD and share its L2 copy of the weight tile.  Blocks hold up to
+// 16*SMT rows.  OCC: waves per SIMD the register allocation must allow (1: no
+// constraint).
+template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL, int OCC>
+__global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void ffn_stream_kernel(
+    const T* __restrict__ in, const int32_t* __restrict__ row_map, const T* __restrict__ w0,
+    const T* __restrict__ w1, const int4* __restrict__ blocks, int dense_rows, T* __restrict__ out, int N, int K,
+    int tiles) {
+  static_assert(MODE == 1 || TPW % 2 == 0, "gate/up tiles come in pairs");
+  static_assert(KC % (16 / sizeof(T)) == 0, "K step must be whole 16-byte loads");
+  constexpr int CPW = (MODE == 0) ? 8 * TPW : 16 * TPW;  // output columns per wave
+  constexpr int NB = WN * CPW;                           // output columns per workgroup
+  constexpr int LE = 16 / sizeof(T);
+  constexpr int STEP = 4 * KC;                           // K elements per wave step
   __shared__ f32x4_t red[(WK > 1) ? (WK - 1) * WN * SMT * TPW * 64 : 1];
 
-  const int g = blockIdx.y;
-  int row0, rows;
-  if (grp_off) {
-    row0 = grp_off[g];
-    rows = grp_off[g + 1] - row0;
+  const int blk = blockIdx.x / tiles, tile = blockIdx.x - blk * tiles;
+  int g, mg, rows;  // group, first row of the block, rows in the block
+  if (blocks) {
+    const int4 b = blocks[blk];
+    g = b.x;
+    mg = b.y;
+    rows = b.z;
+    if (g < 0) return;
   } else {
-    row0 = 0;
-    rows = dense_rows;
+    g = 0;
+    mg = blk * 16 * SMT;
+    rows = min(16 * SMT, dense_rows - mg);
+    if (rows <= 0) return;
   }
-  if (rows <= 0) return;
-  const int tiles = gridDim.x / mgroups;
-  const int mslot = blockIdx.x / tiles, tile = blockIdx.x - mslot * tiles;
-  if (mslot * 16 * SMT >= rows) return;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wn = wave % WN, wk = wave / WN;
@@ -132,174 +255,70 @@ __global__ __launch_bounds__(64 * WN * WK) void ffn_stream_kernel(
   const int kbeg = wk * Kw;
   const int nsteps = Kw / STEP;
   const size_t gstride = (size_t)N * K;
-  const int tstride = 16 * K;                // elements between consecutive 16-row tiles
-  // tile j's row pointer is wbase(j) + (j % half) * tstride
   const T* wa = w0 + g * gstride + (size_t)(n0 + lr) * K + kbeg + lofs;
   const T* wb = (MODE == 0 ? w1 : w0) + g * gstride + (size_t)(n0 + lr) * K + kbeg + lofs;
-  auto wrow = [&](int j) -> const T* {
-    if (MODE == 0) return (j < HALF ? wa : wb) + (j % HALF) * tstride;
-    return wa + j * tstride;
-  };
-  (void)wb;
-
-  for (int mg = mslot * 16 * SMT; mg < rows; mg += mgroups * 16 * SMT) {
-    const int mts = min(SMT, (rows - mg + 15) >> 4);  // live row tiles (wave-uniform)
-    const T* xr[SMT];
-    bool valid[SMT];
-#pragma unroll
-    for (int mt = 0; mt < SMT; ++mt) {
-      const int r = mg + mt * 16 + lr;
-      valid[mt] = r < rows;
-      const int src = valid[mt] ? (row_map ? row_map[row0 + r] : row0 + r) : 0;
-      xr[mt] = in + (size_t)src * K + kbeg + lofs;
-    }
-#pragma unroll
-    for (int mt = 1; mt < SMT; ++mt)
-      if (mt >= mts) xr[mt] = xr[0];  // dead row tile: same loads as tile 0, result unused
-    f32x4_t acc[SMT][TPW];
-#pragma unroll
-    for (int mt = 0; mt < SMT; ++mt)
-#pragma unroll
-      for (int j = 0; j < TPW; ++j) acc[mt][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    uint4 Wr[NS][TPW][LPS];
-    uint4 Xr[NS][SMT][LPS];
-    auto issue = [&](uint4 (&w)[TPW][LPS], uint4 (&x)[SMT][LPS], int step) {
-      const int ko = step * STEP;
-#pragma unroll
-      for (int j = 0; j < TPW; ++j)
-#pragma unroll
-        for (int i = 0; i < LPS; ++i) w[j][i] = ldw<T, false>(wrow(j) + ko + i * LSTR);
-#pragma unroll
-      for (int mt = 0; mt < SMT; ++mt)
-#pragma unroll
-        for (int i = 0; i < LPS; ++i) x[mt][i] = ld16(xr[mt] + ko + i * LSTR);
-    };
-#pragma unroll
-    for (int p = 0; p < PD; ++p) issue(Wr[p], Xr[p], min(p, nsteps - 1));
-
-    for (int s0 = 0; s0 < nsteps; s0 += NS) {
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const int s = s0 + st;
-        if (s < nsteps) {
-          // requests for step s + PD (the last step repeats: cached, in bounds)
-          issue(Wr[(st + PD) % NS], Xr[(st + PD) % NS], min(s + PD, nsteps - 1));
-#pragma unroll
-          for (int mt = 0; mt < SMT; ++mt)
-            if (mt < mts) {
-#pragma unroll
-              for (int i = 0; i < LPS; ++i) {
-                const uint4 b = valid[mt] ? Xr[st][mt][i] : zero_u4();
-#pragma unroll
-                for (int j = 0; j < TPW; ++j) mma_tile<T>(acc[mt][j], Wr[st][j][i], b);
-              }
-            }
-        }
-      }
-    }
-
-    if (WK > 1) {
-      if (wk > 0) {
-#pragma unroll
-        for (int mt = 0; mt < SMT; ++mt)
-#pragma unroll
-          for (int j = 0; j < TPW; ++j) red[((((wk - 1) * WN + wn) * SMT + mt) * TPW + j) * 64 + lane] = acc[mt][j];
-      }
-      __syncthreads();
-      if (wk == 0) {
-        for (int q = 1; q < WK; ++q) {
-#pragma unroll
-          for (int mt = 0; mt < SMT; ++mt)
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) acc[mt][j] += red[((((q - 1) * WN + wn) * SMT + mt) * TPW + j) * 64 + lane];
-        }
-      }
-    }
-
-    if (wk == 0) {
-#pragma unroll
-      for (int mt = 0; mt < SMT; ++mt) {
-        const int m = mg + mt * 16 + lr;
-        if (mt < mts && m < rows) {
-          T* orow = out + (size_t)(row0 + m) * N + n0 + 4 * lg;
-          if (MODE == 0) {
-#pragma unroll
-            for (int j = 0; j < HALF; ++j) {
-              const f32x4_t gt = acc[mt][j], up = acc[mt][j + HALF];
-              store4<T>(orow + 16 * j, silu(gt[0]) * up[0], silu(gt[1]) * up[1], silu(gt[2]) * up[2],
-                        silu(gt[3]) * up[3]);
-            }
-          } else {
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-              const f32x4_t y = acc[mt][j];
-              store4<T>(orow + 16 * j, y[0], y[1], y[2], y[3]);
-            }
-          }
-        }
-      }
-    }
-    if (WK > 1) __syncthreads();
-  }
+  if (SMT > 1 && rows <= 16)
+    stream_block<T, MODE, KC, WN, WK, 1, TPW, PD, IL>(in, row_map, wa, wb, K, kbeg, lofs, nsteps, mg, rows, out, N,
+                                                      n0, red);
+  else
+    stream_block<T, MODE, KC, WN, WK, SMT, TPW, PD, IL>(in, row_map, wa, wb, K, kbeg, lofs, nsteps, mg, rows, out,
+                                                        N, n0, red);
 }
 
 // Shape rules a launch must satisfy (checked by the callers): N % NB == 0,
 // K % WK == 0, (K / WK) % (4 * KC) == 0.
-template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL = true>
+template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL = true, int OCC = 1>
 constexpr int stream_nb() { return WN * ((MODE == 0) ? 8 * TPW : 16 * TPW); }
 
-template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL = true>
-hipError_t launch_stream_variant(const T* in, const int32_t* row_map, const T* w0, const T* w1,
-                                 const int32_t* grp_off, int G, int dense_rows, T* out, int N, int K,
-                                 int mgroups, hipStream_t st) {
-  constexpr int NB = stream_nb<T, MODE, KC, WN, WK, SMT, TPW, PD, IL>();
-  dim3 grid((N / NB) * mgroups, G);
-  hipLaunchKernelGGL((ffn_stream_kernel<T, MODE, KC, WN, WK, SMT, TPW, PD, IL>), grid, dim3(64 * WN * WK), 0, st,
-                     in, row_map, w0, w1, grp_off, dense_rows, out, N, K, mgroups);
+template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL = true, int OCC = 1>
+hipError_t launch_stream_variant(const T* in, const int32_t* row_map, const T* w0, const T* w1, const int4* blocks,
+                                 int nblk, int dense_rows, T* out, int N, int K, hipStream_t st) {
+  constexpr int NB = stream_nb<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, OCC>();
+  const int tiles = N / NB;
+  const long long total = (long long)tiles * nblk;
+  if (total == 0) return hipSuccess;
+  if (total > 0x7fffffffLL / (64 * WN * WK)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((ffn_stream_kernel<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, OCC>), dim3((unsigned)total),
+                     dim3(64 * WN * WK), 0, st, in, row_map, w0, w1, blocks, dense_rows, out, N, K, tiles);
   return hipGetLastError();
 }
 
 // Production shape of the streaming kernels (chosen by a sweep over tile
 // shapes on the decode workloads): 16-element K chunks per lane (a 64-element
-// step per wave), four 16-row weight tiles per wave, 32 rows per pass, one
+// step per wave), four 16-row weight tiles per wave, 32 rows per block, one
 // step of software pipelining, and the four waves of a workgroup splitting K.
 // When K/4 is not a whole number of steps the workgroup is 2 x 2 waves.
 constexpr int S_SMT = 2, S_TPW = 4, S_PD = 1;
-constexpr int S_ROWS = 16 * S_SMT;   // rows per pass
-constexpr int S_MGROUP_CAP = 16;     // row-block slots per column tile
+constexpr int S_ROWS = 16 * S_SMT;   // rows per block
 
-static int stream_mgroups(int rows_max) {
-  return max(1, min(S_MGROUP_CAP, (rows_max + S_ROWS - 1) / S_ROWS));
-}
+int stream_row_block() { return S_ROWS; }
 
 template <typename T, int MODE>
-static hipError_t stream_t(const void* in, const int32_t* row_map, const void* w0, const void* w1,
-                           const int32_t* grp_off, int G, int dense_rows, int rows_max, void* out, int N, int K,
-                           hipStream_t st) {
+static hipError_t stream_t(const void* in, const int32_t* row_map, const void* w0, const void* w1, const int4* blocks,
+                           int bound, int dense_rows, void* out, int N, int K, hipStream_t st) {
   constexpr int KC = (sizeof(T) == 2) ? 16 : 8;
   constexpr int STEP = 4 * KC;
-  const int mg = stream_mgroups(rows_max);
+  const int nblk = blocks ? bound : (dense_rows + S_ROWS - 1) / S_ROWS;
   const T* x = (const T*)in;
   if (K % (4 * STEP) == 0)
-    return launch_stream_variant<T, MODE, KC, 1, 4, S_SMT, S_TPW, S_PD>(x, row_map, (const T*)w0, (const T*)w1, grp_off,
-                                                                        G, dense_rows, (T*)out, N, K, mg, st);
-  return launch_stream_variant<T, MODE, KC, 2, 2, S_SMT, S_TPW, S_PD>(x, row_map, (const T*)w0, (const T*)w1, grp_off, G,
-                                                                      dense_rows, (T*)out, N, K, mg, st);
+    return launch_stream_variant<T, MODE, KC, 1, 4, S_SMT, S_TPW, S_PD>(x, row_map, (const T*)w0, (const T*)w1, blocks,
+                                                                        nblk, dense_rows, (T*)out, N, K, st);
+  return launch_stream_variant<T, MODE, KC, 2, 2, S_SMT, S_TPW, S_PD>(x, row_map, (const T*)w0, (const T*)w1, blocks,
+                                                                      nblk, dense_rows, (T*)out, N, K, st);
 }
 
 hipError_t launch_ffn_gateup_stream(int dtype, const void* in, const int32_t* row_map, const void* wg,
-                                    const void* wu, const int32_t* grp_off, int G, int dense_rows, int rows_max,
-                                    void* h, int N, int K, hipStream_t st) {
+                                    const void* wu, const int4* blocks, int bound, int dense_rows, void* h, int N,
+                                    int K, hipStream_t st) {
   if (dtype == DT_BF16)
-    return stream_t<bf16_t, 0>(in, row_map, wg, wu, grp_off, G, dense_rows, rows_max, h, N, K, st);
-  return stream_t<float, 0>(in, row_map, wg, wu, grp_off, G, dense_rows, rows_max, h, N, K, st);
+    return stream_t<bf16_t, 0>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st);
+  return stream_t<float, 0>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st);
 }
 
-hipError_t launch_ffn_down_stream(int dtype, const void* h, const void* wd, const int32_t* grp_off, int G,
-                                  int dense_rows, int rows_max, void* y, int N, int K, hipStream_t st) {
-  if (dtype == DT_BF16) return stream_t<bf16_t, 1>(h, nullptr, wd, wd, grp_off, G, dense_rows, rows_max, y, N, K, st);
-  return stream_t<float, 1>(h, nullptr, wd, wd, grp_off, G, dense_rows, rows_max, y, N, K, st);
+hipError_t launch_ffn_down_stream(int dtype, const void* h, const void* wd, const int4* blocks, int bound,
+                                  int dense_rows, void* y, int N, int K, hipStream_t st) {
+  if (dtype == DT_BF16) return stream_t<bf16_t, 1>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st);
+  return stream_t<float, 1>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st);
 }
 
 }  // namespace moe

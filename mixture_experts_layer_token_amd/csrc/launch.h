@@ -29,39 +29,50 @@ hipError_t launch_router_screen(const void* x, const void* w, const float* bias,
                                 int d, int E, float scale, float* approx, float* absum, int32_t* ids, float* wts,
                                 hipStream_t st);
 
+// Row-block table of the grouped FFN kernels.  The rows of group g,
+// [grp_off[g], grp_off[g+1]), are cut into blocks of RB rows; entry i is
+// {g, first row, rows in the block, 0} for i < count, {-1, 0, 0, 0} for
+// count <= i < bound, and entry `bound` is {count, 0, 0, 0}.  `bound` comes
+// from the shape only (it sizes launch grids): sum_g ceil(rows_g / RB) <=
+// A_cap / RB + min(G, A_cap) when sum_g rows_g <= A_cap.
+int row_block_bound(int A_cap, int G, int RB);
+// One workgroup (G <= 1024) builds the table from grp_off.
+hipError_t launch_row_blocks(const int32_t* grp_off, int G, int RB, int bound, int4* blocks, hipStream_t st);
+
 // permute.hip
 constexpr int PERM_BLOCK = 256;  // tokens per histogram block
+// blocks (nullable): also writes the row-block table of the expert groups
+// (RB rows per block, `bound` entries + the count), as launch_row_blocks would.
 hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int E, int32_t* block_counts,
                           int32_t* block_base, int32_t* counts, int32_t* expert_off, int32_t* perm_tok,
-                          int32_t* perm_src, int32_t* inv_perm, int32_t* n_active, int32_t* stats,
-                          hipStream_t st);
+                          int32_t* perm_src, int32_t* inv_perm, int32_t* n_active, int32_t* stats, int RB,
+                          int bound, int4* blocks, hipStream_t st);
 
 // ffn_stream.hip -- weight-streaming grouped FFN.
-//  gate/up: H[row0+m] = SiLU(in[src(m)] . wg[g]^T) * (in[src(m)] . wu[g]^T), N = I, K = d
-//  down:    Y[row0+m] = H[row0+m] . wd[g]^T,                                 N = d, K = I
-// Groups: G experts with rows [grp_off[g], grp_off[g+1]); grp_off == nullptr
-// means one group of `dense_rows` rows starting at 0.  src(m) = row_map[row0+m]
-// when row_map != nullptr, else row0 + m.  rows_max bounds the rows of any
-// group (it sizes the grid; it must not depend on the routing).
+//  gate/up: H[r] = SiLU(in[src(r)] . wg[g]^T) * (in[src(r)] . wu[g]^T), N = I, K = d
+//  down:    Y[r] = H[r] . wd[g]^T,                                     N = d, K = I
+// Work: the row-block table `blocks` (RB = stream_row_block(), `bound` entries)
+// of the expert groups; blocks == nullptr means one dense group of
+// `dense_rows` rows starting at 0 (weights of group 0).  src(r) = row_map[r]
+// when row_map != nullptr, else r.
+int stream_row_block();
 hipError_t launch_ffn_gateup_stream(int dtype, const void* in, const int32_t* row_map, const void* wg,
-                                    const void* wu, const int32_t* grp_off, int G, int dense_rows, int rows_max,
-                                    void* h, int N, int K, hipStream_t st);
-hipError_t launch_ffn_down_stream(int dtype, const void* h, const void* wd, const int32_t* grp_off, int G,
-                                  int dense_rows, int rows_max, void* y, int N, int K, hipStream_t st);
+                                    const void* wu, const int4* blocks, int bound, int dense_rows, void* h, int N,
+                                    int K, hipStream_t st);
+hipError_t launch_ffn_down_stream(int dtype, const void* h, const void* wd, const int4* blocks, int bound,
+                                  int dense_rows, void* y, int N, int K, hipStream_t st);
 
 // ffn_gemm.hip -- grouped-GEMM FFN (bf16): same semantics as the streaming
-// kernels.  tile_off [G+1] (row blocks of 256 per group) is built on the device
-// by launch_gemm_tiles; rb_bound >= tile_off[G] sizes the grid and rows_hint
-// (an estimate of rows per group) picks the tile height -- both from the shape
-// only.  N must be a multiple of 128 and K of 64.
-int gemm_tile_bound(int A_cap, int G);
-hipError_t launch_gemm_tiles(const int32_t* grp_off, int G, int32_t* tile_off, hipStream_t st);
+// kernels, over the row-block table with RB = gemm_row_block() (`bound`
+// entries + count; blocks == nullptr: one dense group of dense_rows rows).
+// rows_hint (an estimate of rows per group, from the shape only) picks the
+// tile height.  N must be a multiple of 128 and K of 64.
+int gemm_row_block();
 hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
-                                  const int32_t* grp_off, const int32_t* tile_off, int G, int dense_rows,
-                                  int rb_bound, int rows_hint, void* h, int N, int K, hipStream_t st);
-hipError_t launch_ffn_down_gemm(const void* h, const void* wd, const int32_t* grp_off, const int32_t* tile_off,
-                                int G, int dense_rows, int rb_bound, int rows_hint, void* y, int N, int K,
-                                hipStream_t st);
+                                  const int4* blocks, int bound, int dense_rows, int rows_hint, void* h, int N,
+                                  int K, hipStream_t st);
+hipError_t launch_ffn_down_gemm(const void* h, const void* wd, const int4* blocks, int bound, int dense_rows,
+                                int rows_hint, void* y, int N, int K, hipStream_t st);
 
 // combine.hip
 hipError_t launch_combine(int dtype, const void* y, const void* y_shared, const int32_t* tok_off,

@@ -56,7 +56,7 @@ int n_blocks(const moe_desc& d) { return (d.T + PERM_BLOCK - 1) / PERM_BLOCK; }
 
 struct RouteWs { double* part; int splits; float* approx; float* absum; bool screened; };
 struct PermWs { int32_t* block_counts; int32_t* block_base; };
-struct FfnWs { int32_t* tile_off; void* h; void* h_sh; };
+struct FfnWs { int4* blocks; int bound; int rb; void* h; void* h_sh; };
 
 // Large bf16 batches route through the MFMA screen (exact on the candidates);
 // smaller ones sum every logit in float64 directly.
@@ -81,8 +81,15 @@ void plan_permute(const moe_desc& d, Carver& c, PermWs& w) {
   w.block_counts = c.take<int32_t>(n);
   w.block_base = c.take<int32_t>(n);
 }
+// Rows per entry of the routed FFN's row-block table: the GEMM's row block,
+// or the streaming kernel's rows per workgroup.
+bool routed_gemm(const moe_desc& d);
+int ffn_rb(const moe_desc& d) { return routed_gemm(d) ? gemm_row_block() : stream_row_block(); }
+
 void plan_ffn(const moe_desc& d, Carver& c, FfnWs& w) {
-  w.tile_off = c.take<int32_t>((size_t)d.E + 1);
+  w.rb = ffn_rb(d);
+  w.bound = row_block_bound((int)a_cap(d), d.E, w.rb);
+  w.blocks = c.take<int4>((size_t)w.bound + 1);
   w.h = c.take_bytes(a_cap(d) * d.I * elt_size(d));
   w.h_sh = d.I_shared ? c.take_bytes((size_t)d.T * d.I_shared * elt_size(d)) : nullptr;
 }
@@ -185,49 +192,42 @@ moe_status do_route(const moe_desc& d, const void* x, const void* wr, const floa
 
 moe_status do_permute(const moe_desc& d, const int32_t* tok_off, const int32_t* ids, int32_t* counts,
                       int32_t* expert_off, int32_t* perm_tok, int32_t* perm_src, int32_t* inv_perm,
-                      int32_t* n_active, int32_t* stats, const PermWs& ws, hipStream_t st) {
+                      int32_t* n_active, int32_t* stats, const PermWs& ws, const FfnWs* fw, hipStream_t st) {
   return launched(launch_permute(tok_off, ids, d.T, d.E, ws.block_counts, ws.block_base, counts, expert_off,
-                                 perm_tok, perm_src, inv_perm, n_active, stats, st));
+                                 perm_tok, perm_src, inv_perm, n_active, stats, fw ? fw->rb : 1, fw ? fw->bound : 0,
+                                 fw ? fw->blocks : nullptr, st));
 }
 
-// tile_off: row-block table of the grouped GEMM (built when `build_tiles`).
+// The row-block table fw.blocks is built here when `build_blocks` (otherwise
+// the permutation wrote it).
 moe_status do_gateup(const moe_desc& d, const void* x, const void* wg, const void* wu, const int32_t* expert_off,
-                     const int32_t* perm_tok, void* h, int32_t* tile_off, bool build_tiles, hipStream_t st) {
-  if (routed_gemm(d)) {
-    hipError_t e = build_tiles ? launch_gemm_tiles(expert_off, d.E, tile_off, st) : hipSuccess;
-    if (e == hipSuccess)
-      e = launch_ffn_gateup_gemm(x, perm_tok, wg, wu, expert_off, tile_off, d.E, 0, gemm_tile_bound((int)a_cap(d), d.E),
-                                 rows_hint(d), h, d.I, d.d, st);
-    return launched(e);
-  }
-  // a token selects an expert at most once: at most T rows per expert
-  return launched(launch_ffn_gateup_stream(d.dtype, x, perm_tok, wg, wu, expert_off, d.E, 0, d.T, h, d.I, d.d, st));
+                     const int32_t* perm_tok, void* h, const FfnWs& fw, bool build_blocks, hipStream_t st) {
+  hipError_t e = build_blocks ? launch_row_blocks(expert_off, d.E, fw.rb, fw.bound, fw.blocks, st) : hipSuccess;
+  if (e != hipSuccess) return launched(e);
+  if (routed_gemm(d))
+    return launched(launch_ffn_gateup_gemm(x, perm_tok, wg, wu, fw.blocks, fw.bound, 0, rows_hint(d), h, d.I, d.d, st));
+  return launched(launch_ffn_gateup_stream(d.dtype, x, perm_tok, wg, wu, fw.blocks, fw.bound, 0, h, d.I, d.d, st));
 }
 
 moe_status do_down(const moe_desc& d, const void* h, const void* wd, const int32_t* expert_off, void* y,
-                   int32_t* tile_off, bool build_tiles, hipStream_t st) {
-  if (routed_gemm(d)) {
-    hipError_t e = build_tiles ? launch_gemm_tiles(expert_off, d.E, tile_off, st) : hipSuccess;
-    if (e == hipSuccess)
-      e = launch_ffn_down_gemm(h, wd, expert_off, tile_off, d.E, 0, gemm_tile_bound((int)a_cap(d), d.E), rows_hint(d),
-                               y, d.d, d.I, st);
-    return launched(e);
-  }
-  return launched(launch_ffn_down_stream(d.dtype, h, wd, expert_off, d.E, 0, d.T, y, d.d, d.I, st));
+                   const FfnWs& fw, bool build_blocks, hipStream_t st) {
+  hipError_t e = build_blocks ? launch_row_blocks(expert_off, d.E, fw.rb, fw.bound, fw.blocks, st) : hipSuccess;
+  if (e != hipSuccess) return launched(e);
+  if (routed_gemm(d))
+    return launched(launch_ffn_down_gemm(h, wd, fw.blocks, fw.bound, 0, rows_hint(d), y, d.d, d.I, st));
+  return launched(launch_ffn_down_stream(d.dtype, h, wd, fw.blocks, fw.bound, 0, y, d.d, d.I, st));
 }
 
 moe_status do_shared(const moe_desc& d, const void* x, const void* sg, const void* su, const void* sd, void* h_sh,
                      void* y_sh, hipStream_t st) {
   hipError_t e;
   if (shared_gemm(d)) {
-    const int rb = gemm_tile_bound(d.T, 0);  // row blocks of the dense shared expert
-    e = launch_ffn_gateup_gemm(x, nullptr, sg, su, nullptr, nullptr, 1, d.T, rb, d.T, h_sh, d.I_shared, d.d, st);
-    if (e == hipSuccess)
-      e = launch_ffn_down_gemm(h_sh, sd, nullptr, nullptr, 1, d.T, rb, d.T, y_sh, d.d, d.I_shared, st);
+    e = launch_ffn_gateup_gemm(x, nullptr, sg, su, nullptr, 0, d.T, d.T, h_sh, d.I_shared, d.d, st);
+    if (e == hipSuccess) e = launch_ffn_down_gemm(h_sh, sd, nullptr, 0, d.T, d.T, y_sh, d.d, d.I_shared, st);
     return launched(e);
   }
-  e = launch_ffn_gateup_stream(d.dtype, x, nullptr, sg, su, nullptr, 1, d.T, d.T, h_sh, d.I_shared, d.d, st);
-  if (e == hipSuccess) e = launch_ffn_down_stream(d.dtype, h_sh, sd, nullptr, 1, d.T, d.T, y_sh, d.d, d.I_shared, st);
+  e = launch_ffn_gateup_stream(d.dtype, x, nullptr, sg, su, nullptr, 0, d.T, h_sh, d.I_shared, d.d, st);
+  if (e == hipSuccess) e = launch_ffn_down_stream(d.dtype, h_sh, sd, nullptr, 0, d.T, y_sh, d.d, d.I_shared, st);
   return launched(e);
 }
 
@@ -286,7 +286,20 @@ moe_status moe_permute(const moe_desc* desc, const int32_t* tok_off, const int32
   PermWs pw;
   plan_permute(d, c, pw);
   return do_permute(d, tok_off, topk_ids, expert_counts, expert_off, perm_tok, perm_src, inv_perm, n_active,
-                    nullptr, pw, static_cast<hipStream_t>(stream));
+                    nullptr, pw, nullptr, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_ffn_plan(const moe_desc* desc, const int32_t* expert_off, void* ws, size_t ws_bytes,
+                        moe_stream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  MOE_TRY(path_ok(d));
+  MOE_TRY(check_ws(d, MOE_OP_FFN, ws, ws_bytes));
+  if (!expert_off) return MOE_ERR_NULL;
+  Carver c(ws);
+  FfnWs fw;
+  plan_ffn(d, c, fw);
+  return launched(launch_row_blocks(expert_off, d.E, fw.rb, fw.bound, fw.blocks, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_ffn_gateup(const moe_desc* desc, const void* x, const void* w_gate, const void* w_up,
@@ -295,16 +308,14 @@ moe_status moe_ffn_gateup(const moe_desc* desc, const void* x, const void* w_gat
   MOE_TRY(check_desc(desc));
   const moe_desc& d = *desc;
   MOE_TRY(path_ok(d));
-  FfnWs fw{};
-  if (routed_gemm(d)) {
-    MOE_TRY(check_ws(d, MOE_OP_FFN, ws, ws_bytes));
-    Carver c(ws);
-    plan_ffn(d, c, fw);
-  }
+  MOE_TRY(check_ws(d, MOE_OP_FFN, ws, ws_bytes));
   if (!tok_ptr(d, x) || !w_gate || !w_up || !expert_off || !tok_ptr(d, perm_tok) || !tok_ptr(d, h))
     return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(h)) return MOE_ERR_ALIGN;
-  return do_gateup(d, x, w_gate, w_up, expert_off, perm_tok, h, fw.tile_off, true, static_cast<hipStream_t>(stream));
+  Carver c(ws);
+  FfnWs fw;
+  plan_ffn(d, c, fw);
+  return do_gateup(d, x, w_gate, w_up, expert_off, perm_tok, h, fw, false, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_ffn_down(const moe_desc* desc, const void* h, const void* w_down, const int32_t* expert_off,
@@ -312,15 +323,13 @@ moe_status moe_ffn_down(const moe_desc* desc, const void* h, const void* w_down,
   MOE_TRY(check_desc(desc));
   const moe_desc& d = *desc;
   MOE_TRY(path_ok(d));
-  FfnWs fw{};
-  if (routed_gemm(d)) {
-    MOE_TRY(check_ws(d, MOE_OP_FFN, ws, ws_bytes));
-    Carver c(ws);
-    plan_ffn(d, c, fw);
-  }
+  MOE_TRY(check_ws(d, MOE_OP_FFN, ws, ws_bytes));
   if (!tok_ptr(d, h) || !w_down || !expert_off || !tok_ptr(d, y_perm)) return MOE_ERR_NULL;
   if (!aligned16(h) || !aligned16(w_down) || !aligned16(y_perm)) return MOE_ERR_ALIGN;
-  return do_down(d, h, w_down, expert_off, y_perm, fw.tile_off, true, static_cast<hipStream_t>(stream));
+  Carver c(ws);
+  FfnWs fw;
+  plan_ffn(d, c, fw);
+  return do_down(d, h, w_down, expert_off, y_perm, fw, false, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_ffn(const moe_desc* desc, const void* x, const void* w_gate, const void* w_up, const void* w_down,
@@ -343,8 +352,8 @@ moe_status moe_ffn(const moe_desc* desc, const void* x, const void* w_gate, cons
   FfnWs fw;
   plan_ffn(d, c, fw);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  MOE_TRY(do_gateup(d, x, w_gate, w_up, expert_off, perm_tok, fw.h, fw.tile_off, true, st));
-  MOE_TRY(do_down(d, fw.h, w_down, expert_off, y_perm, fw.tile_off, false, st));
+  MOE_TRY(do_gateup(d, x, w_gate, w_up, expert_off, perm_tok, fw.h, fw, true, st));
+  MOE_TRY(do_down(d, fw.h, w_down, expert_off, y_perm, fw, false, st));
   if (d.I_shared) MOE_TRY(do_shared(d, x, ws_gate, ws_up, ws_down, fw.h_sh, y_shared, st));
   return MOE_OK;
 }
@@ -381,9 +390,9 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router
   int32_t* status = dev_status ? dev_status : fw.status;
   MOE_TRY(do_route(d, x, w_router, router_bias, k, fw.tok_off, fw.ids, fw.w, status, fw.r, st));
   MOE_TRY(do_permute(d, fw.tok_off, fw.ids, fw.counts, fw.expert_off, fw.perm_tok, fw.perm_src, fw.inv_perm,
-                     fw.n_active, stats, fw.p, st));
-  MOE_TRY(do_gateup(d, x, w_gate, w_up, fw.expert_off, fw.perm_tok, fw.f.h, fw.f.tile_off, true, st));
-  MOE_TRY(do_down(d, fw.f.h, w_down, fw.expert_off, fw.y, fw.f.tile_off, false, st));
+                     fw.n_active, stats, fw.p, &fw.f, st));
+  MOE_TRY(do_gateup(d, x, w_gate, w_up, fw.expert_off, fw.perm_tok, fw.f.h, fw.f, false, st));
+  MOE_TRY(do_down(d, fw.f.h, w_down, fw.expert_off, fw.y, fw.f, false, st));
   if (d.I_shared) MOE_TRY(do_shared(d, x, ws_gate, ws_up, ws_down, fw.f.h_sh, fw.y_sh, st));
   return do_combine(d, fw.y, fw.y_sh, fw.tok_off, fw.w, fw.inv_perm, out, st);
 }

@@ -15,6 +15,63 @@ namespace moe {
 
 constexpr int MASK_WORDS = PERM_BLOCK / 32;
 
+// ---------------------------------------------------------------------------
+// Row-block table of the grouped FFN (declared in launch.h).
+int row_block_bound(int A_cap, int G, int RB) { return A_cap / RB + min(G, A_cap); }
+
+// Group g's entries (rows [r0, r0 + n)) from table index `start` on.
+__device__ __forceinline__ void put_row_blocks(int4* __restrict__ blocks, int g, int r0, int n, int RB, int start,
+                                               int bound) {
+  for (int b = 0, i = start; b * RB < n && i < bound; ++b, ++i) blocks[i] = make_int4(g, r0 + b * RB, min(RB, n - b * RB), 0);
+}
+// Sentinels after the `count` real entries and the count itself at `bound`.
+__device__ __forceinline__ void close_row_blocks(int4* __restrict__ blocks, int count, int bound, int tid,
+                                                 int nthreads) {
+  count = min(count, bound);
+  for (int i = count + tid; i < bound; i += nthreads) blocks[i] = make_int4(-1, 0, 0, 0);
+  if (tid == 0) blocks[bound] = make_int4(count, 0, 0, 0);
+}
+
+// Inclusive scan of one value per thread over a workgroup of NT threads.
+template <int NT>
+__device__ __forceinline__ int block_inclusive_scan(int v, int32_t* sc) {
+  const int tid = threadIdx.x;
+  sc[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    const int u = tid >= off ? sc[tid - off] : 0;
+    __syncthreads();
+    sc[tid] += u;
+    __syncthreads();
+  }
+  const int r = sc[tid];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void row_blocks_kernel(const int32_t* __restrict__ grp_off, int G, int RB,
+                                                          int bound, int4* __restrict__ blocks) {
+  __shared__ int32_t sc[1024];
+  __shared__ int32_t total;
+  const int g = threadIdx.x;
+  int r0 = 0, n = 0;
+  if (g < G) {
+    r0 = grp_off[g];
+    n = max(0, grp_off[g + 1] - r0);
+  }
+  const int nb = (n + RB - 1) / RB;
+  const int incl = block_inclusive_scan<1024>(nb, sc);
+  if (g == 1023) total = incl;
+  __syncthreads();
+  put_row_blocks(blocks, g, r0, n, RB, incl - nb, bound);
+  close_row_blocks(blocks, total, bound, g, 1024);
+}
+
+hipError_t launch_row_blocks(const int32_t* grp_off, int G, int RB, int bound, int4* blocks, hipStream_t st) {
+  hipLaunchKernelGGL(row_blocks_kernel, dim3(1), dim3(1024), 0, st, grp_off, G, RB, bound, blocks);
+  return hipGetLastError();
+}
+
 __device__ __forceinline__ void build_masks(uint32_t* masks, const int32_t* __restrict__ tok_off,
                                             const int32_t* __restrict__ ids, int T, int E) {
   const int tid = threadIdx.x;
@@ -52,9 +109,10 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ expert_off,
                                                            int32_t* __restrict__ n_active,
-                                                           int32_t* __restrict__ stats) {
+                                                           int32_t* __restrict__ stats, int RB, int bound,
+                                                           int4* __restrict__ blocks) {
   __shared__ int32_t sc[1024];
-  __shared__ int32_t nact;
+  __shared__ int32_t nact, nblocks;
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
@@ -76,7 +134,8 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __rest
     sc[e] += v;
     __syncthreads();
   }
-  if (e < E) expert_off[e] = sc[e] - run;
+  const int first = sc[e] - run;
+  if (e < E) expert_off[e] = first;
   if (e == 1023) {
     expert_off[E] = sc[1023];
     n_active[0] = nact;
@@ -84,6 +143,15 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __rest
       stats[E] = nact;
       stats[E + 1] = sc[1023];
     }
+  }
+  if (blocks) {
+    __syncthreads();
+    const int nb = (run + RB - 1) / RB;
+    const int incl = block_inclusive_scan<1024>(nb, sc);
+    if (e == 1023) nblocks = incl;
+    __syncthreads();
+    put_row_blocks(blocks, e, first, run, RB, incl - nb, bound);
+    close_row_blocks(blocks, nblocks, bound, e, 1024);
   }
 }
 
@@ -118,11 +186,12 @@ __global__ __launch_bounds__(PERM_BLOCK) void expert_scatter_kernel(
 __global__ __launch_bounds__(PERM_BLOCK) void permute_one_block_kernel(
     const int32_t* __restrict__ tok_off, const int32_t* __restrict__ ids, int T, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ expert_off, int32_t* __restrict__ perm_tok, int32_t* __restrict__ perm_src,
-    int32_t* __restrict__ inv_perm, int32_t* __restrict__ n_active, int32_t* __restrict__ stats) {
+    int32_t* __restrict__ inv_perm, int32_t* __restrict__ n_active, int32_t* __restrict__ stats, int RB, int bound,
+    int4* __restrict__ blocks) {
   extern __shared__ uint32_t masks[];
   int32_t* eoff = reinterpret_cast<int32_t*>(masks + E * MASK_WORDS);  // [E + 1]
   __shared__ int32_t part[PERM_BLOCK];
-  __shared__ int32_t nact;
+  __shared__ int32_t nact, nblocks;
   build_masks(masks, tok_off, ids, T, E);
   const int tid = threadIdx.x;
   const int per = (E + PERM_BLOCK - 1) / PERM_BLOCK;
@@ -156,6 +225,7 @@ __global__ __launch_bounds__(PERM_BLOCK) void permute_one_block_kernel(
     run += c;
   }
   if (tid == PERM_BLOCK - 1) {
+    eoff[E] = part[PERM_BLOCK - 1];
     expert_off[E] = part[PERM_BLOCK - 1];
     n_active[0] = nact;
     if (stats) {
@@ -164,6 +234,21 @@ __global__ __launch_bounds__(PERM_BLOCK) void permute_one_block_kernel(
     }
   }
   __syncthreads();
+  if (blocks) {
+    // row-block table: this thread's experts, after the blocks of lower threads
+    int nb = 0;
+    for (int e = beg; e < end; ++e) nb += (eoff[e + 1] - eoff[e] + RB - 1) / RB;
+    const int incl = block_inclusive_scan<PERM_BLOCK>(nb, part);
+    if (tid == PERM_BLOCK - 1) nblocks = incl;
+    __syncthreads();
+    int start = incl - nb;
+    for (int e = beg; e < end; ++e) {
+      const int c = eoff[e + 1] - eoff[e];
+      put_row_blocks(blocks, e, eoff[e], c, RB, start, bound);
+      start += (c + RB - 1) / RB;
+    }
+    close_row_blocks(blocks, nblocks, bound, tid, PERM_BLOCK);
+  }
   if (tid >= T) return;
   const int a0 = tok_off[tid], a1 = tok_off[tid + 1];
   const int wi = tid >> 5;
@@ -183,13 +268,14 @@ __global__ __launch_bounds__(PERM_BLOCK) void permute_one_block_kernel(
 
 hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int E, int32_t* block_counts,
                           int32_t* block_base, int32_t* counts, int32_t* expert_off, int32_t* perm_tok,
-                          int32_t* perm_src, int32_t* inv_perm, int32_t* n_active, int32_t* stats,
-                          hipStream_t st) {
+                          int32_t* perm_src, int32_t* inv_perm, int32_t* n_active, int32_t* stats, int RB,
+                          int bound, int4* blocks, hipStream_t st) {
   const int nblk = (T + PERM_BLOCK - 1) / PERM_BLOCK;
   const size_t lds = (size_t)E * MASK_WORDS * sizeof(uint32_t);
   if (nblk == 1) {
     hipLaunchKernelGGL(permute_one_block_kernel, dim3(1), dim3(PERM_BLOCK), lds + (E + 1) * sizeof(int32_t), st,
-                       tok_off, ids, T, E, counts, expert_off, perm_tok, perm_src, inv_perm, n_active, stats);
+                       tok_off, ids, T, E, counts, expert_off, perm_tok, perm_src, inv_perm, n_active, stats, RB,
+                       bound, blocks);
     return hipGetLastError();
   }
   if (nblk > 0) {
@@ -199,7 +285,7 @@ hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, st, block_counts, nblk, E, block_base, counts,
-                     expert_off, n_active, stats);
+                     expert_off, n_active, stats, RB, bound, blocks);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nblk == 0) return err;
   hipLaunchKernelGGL(expert_scatter_kernel, dim3(nblk), dim3(PERM_BLOCK), lds, st, tok_off, ids, T, E,

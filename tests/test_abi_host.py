@@ -84,6 +84,8 @@ def test_entry_points_validate_before_launch():
     assert lib.moe_ffn_down(ctypes.byref(dg), *fake[:4], None, 0, None) == 4
     df = _desc(T=4, d=128, E=4, I=128, k_max=2, path=moe.MOE_PATH_GEMM, dtype=moe.MOE_F32)
     assert lib.moe_ffn_gateup(ctypes.byref(df), *fake[:6], None, 0, None) == 3
+    assert lib.moe_ffn_plan(ctypes.byref(dg), fake[0], None, 0, None) == 4
+    assert lib.moe_ffn_plan(ctypes.byref(dg), None, None, 0, None) in (1, 4)
     assert lib.moe_status_str(4) == b"workspace missing or too small"
     with pytest.raises(moe.MoeError):
         moe._check("x", 2)

@@ -222,3 +222,33 @@ def test_screened_router_bit_exact(T, E, d, kmax, zipf):
     check_routing(got, r, p)
     np.testing.assert_array_equal(got["ids"], ref64["ids"])
     np.testing.assert_array_equal(got["w"], ref64["w"])        # same fp32 logits -> same weights
+
+
+@pytest.mark.parametrize("name,path", [("qwen3_30b_a3b_decode", "stream"), ("qwen3_30b_a3b_decode", "gemm"),
+                                       ("tiny_fp32", "stream")])
+def test_split_ffn_calls_match_moe_ffn(name, path):
+    """moe_ffn_plan + moe_ffn_gateup + moe_ffn_down give moe_ffn's routed output
+    bit for bit (the Zipf-skewed batch has experts spanning several row blocks)."""
+    cfg = CONFIGS[name]
+    layer = make_layer(cfg, "cuda")
+    got = run_stages(layer, path=path)
+    dev = layer.device
+    desc = moe.make_desc(cfg.T, cfg.d, cfg.E, cfg.I, cfg.k_max, dtype=layer.x.dtype, path=path)
+    i32 = dict(dtype=torch.int32, device=dev)
+    eoff = torch.as_tensor(got["expert_off"], **i32)
+    ptok = torch.zeros(cfg.T * cfg.k_max, **i32)
+    ptok[:got["A"]] = torch.as_tensor(got["perm_tok"], **i32)
+    ws = moe.alloc_workspace(desc, moe.MOE_OP_FFN, dev)
+    y_ref = torch.empty((cfg.T * cfg.k_max, cfg.d), dtype=layer.x.dtype, device=dev)
+    moe.moe_ffn(desc, layer.x, layer.w_gate, layer.w_up, layer.w_down, None, None, None, eoff, ptok, y_ref,
+                None, ws)
+    h = torch.empty((cfg.T * cfg.k_max, cfg.I), dtype=layer.x.dtype, device=dev)
+    y = torch.empty_like(y_ref)
+    ws2 = moe.alloc_workspace(desc, moe.MOE_OP_FFN, dev)
+    moe.moe_ffn_plan(desc, eoff, ws2)
+    moe.moe_ffn_gateup(desc, layer.x, layer.w_gate, layer.w_up, eoff, ptok, h, ws2)
+    moe.moe_ffn_down(desc, h, layer.w_down, eoff, y, ws2)
+    torch.cuda.synchronize()
+    A = got["A"]
+    assert torch.equal(y[:A].view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32),
+                       y_ref[:A].view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32))
