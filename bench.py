@@ -47,6 +47,9 @@ def parse():
                          "GPU clocks have settled before timing")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--eager", action="store_true", help="time plain launches instead of a HIP graph")
+    ap.add_argument("--router", default="auto", choices=["auto", "float64", "screened"],
+                    help="router algorithm (both give identical routing; they differ in cost)")
+    ap.add_argument("--path", default="auto", choices=["auto", "stream", "gemm"], help="FFN path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens in the CPU-oracle sample (0 = workload default)")
@@ -138,7 +141,7 @@ def main():
     T, d, E, I = cfg.T, cfg.d, cfg.E, cfg.I
     Is = cfg.I_shared
     desc = moe.make_desc(T, d, E, I, cfg.k_max, I_shared=Is, dtype=layer.x.dtype,
-                         routed_scale=cfg.routed_scale)
+                         routed_scale=cfg.routed_scale, path=args.path, router=args.router)
     ws = moe.alloc_workspace(desc, moe.MOE_OP_FORWARD, dev)
     out = torch.empty((T, d), dtype=layer.x.dtype, device=dev)
     stats = torch.empty(E + 2, dtype=torch.int32, device=dev)
@@ -177,6 +180,7 @@ def main():
             if n % 8 == 0:
                 stream.synchronize()
         stream.synchronize()
+        n_warm = n
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -265,7 +269,7 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": n_warm,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -275,6 +279,7 @@ def main():
         "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "I": I, "I_shared": Is,
                    "k_values": k_desc, "k_max": cfg.k_max, "A": A, "n_active": n_act,
                    "execution": "eager" if args.eager else "hip_graph", "ffn_path": routed_path,
+                   "router": args.router,
                    "wall_s": round(wall, 3)},
         "layer": layer_info,
         "roofline": roof,

@@ -1,7 +1,6 @@
 // Weighted combine back to token order:
 //   out[t] = sum_{j < k_t} w[t, j] * Y[inv_perm[tok_off[t] + j]]  (+ Y_shared[t])
 // in float32, j ascending (deterministic), rounded once to the element type.
-// One workgroup per token; each thread owns 16-byte column chunks.
 #include "common.h"
 #include "launch.h"
 
@@ -16,66 +15,98 @@ __device__ __forceinline__ void unpack(const uint4& v, float (&f)[8]) {
   }
 }
 
-__global__ __launch_bounds__(256) void combine_bf16_kernel(const bf16_t* __restrict__ y,
-                                                           const bf16_t* __restrict__ ysh,
-                                                           const int32_t* __restrict__ tok_off,
-                                                           const float* __restrict__ wts,
-                                                           const int32_t* __restrict__ inv_perm,
-                                                           bf16_t* __restrict__ out, int d) {
-  const int t = blockIdx.x;
-  const int a0 = tok_off[t], a1 = tok_off[t + 1];
-  for (int c = threadIdx.x; c < d / 8; c += 256) {
-    float acc[8];
+// The token's (row, weight) pairs are staged in LDS, CB at a time; each thread
+// then requests the CB rows' 16-byte chunks together before summing them in
+// ascending j (the loads overlap, the arithmetic order does not change).
+constexpr int CB = 8;      // rows in flight per thread
+constexpr int CSTAGE = 256;  // assignments staged in LDS per round
+
+template <typename T>
+__device__ __forceinline__ void load_chunk(const T* p, float (&f)[16 / sizeof(T)]);
+template <>
+__device__ __forceinline__ void load_chunk<bf16_t>(const bf16_t* p, float (&f)[8]) {
+  unpack(*reinterpret_cast<const uint4*>(p), f);
+}
+template <>
+__device__ __forceinline__ void load_chunk<float>(const float* p, float (&f)[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+}
+template <typename T>
+__device__ __forceinline__ void store_chunk(T* p, const float* f);
+template <>
+__device__ __forceinline__ void store_chunk<bf16_t>(bf16_t* p, const float* f) {
+  uint32_t o[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int a = a0; a < a1; ++a) {
-      const float w = wts[a];
-      const uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)inv_perm[a] * d + c * 8);
-      float f[8];
-      unpack(v, f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, f[i], acc[i]);
-    }
-    if (ysh) {
-      const uint4 v = *reinterpret_cast<const uint4*>(ysh + (size_t)t * d + c * 8);
-      float f[8];
-      unpack(v, f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += f[i];
-    }
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
-    *reinterpret_cast<uint4*>(out + (size_t)t * d + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-  }
+  for (int i = 0; i < 4; ++i) o[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+template <>
+__device__ __forceinline__ void store_chunk<float>(float* p, const float* f) {
+  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
 }
 
-__global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restrict__ y, const float* __restrict__ ysh,
-                                                          const int32_t* __restrict__ tok_off,
-                                                          const float* __restrict__ wts,
-                                                          const int32_t* __restrict__ inv_perm,
-                                                          float* __restrict__ out, int d) {
-  const int t = blockIdx.x;
+// One workgroup per token; a thread owns 16-byte column chunks c, c+256, ...
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const T* __restrict__ ysh,
+                                                      const int32_t* __restrict__ tok_off,
+                                                      const float* __restrict__ wts,
+                                                      const int32_t* __restrict__ inv_perm, T* __restrict__ out,
+                                                      int d) {
+  constexpr int LE = 16 / sizeof(T);
+  __shared__ int32_t srow[CSTAGE];
+  __shared__ float sw[CSTAGE];
+  const int t = blockIdx.x, tid = threadIdx.x;
   const int a0 = tok_off[t], a1 = tok_off[t + 1];
-  for (int c = threadIdx.x; c < d / 4; c += 256) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int a = a0; a < a1; ++a) {
-      const float w = wts[a];
-      const float4 v = *reinterpret_cast<const float4*>(y + (size_t)inv_perm[a] * d + c * 4);
-      acc.x = fmaf(w, v.x, acc.x);
-      acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z);
-      acc.w = fmaf(w, v.w, acc.w);
+  const int nch = d / LE;
+  const int per = (nch + 255) / 256;  // chunks per thread (uniform loop bound)
+  float acc[4][LE];                   // up to four chunks per thread kept live (d <= 8192 for bf16)
+  for (int c0 = 0; c0 < per; c0 += 4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < LE; ++i) acc[q][i] = 0.f;
+    for (int s0 = a0; s0 < a1; s0 += CSTAGE) {
+      const int n = min(CSTAGE, a1 - s0);
+      __syncthreads();
+      if (tid < n) {
+        srow[tid] = inv_perm[s0 + tid];
+        sw[tid] = wts[s0 + tid];
+      }
+      __syncthreads();
+      for (int j0 = 0; j0 < n; j0 += CB) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = tid + 256 * (c0 + q);
+          if (c0 + q < per && c < nch) {
+            float f[CB][LE];
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+              if (j0 + j < n) load_chunk<T>(y + (size_t)srow[j0 + j] * d + c * LE, f[j]);
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+              if (j0 + j < n) {
+                const float w = sw[j0 + j];
+#pragma unroll
+                for (int i = 0; i < LE; ++i) acc[q][i] = fmaf(w, f[j][i], acc[q][i]);
+              }
+          }
+        }
+      }
     }
-    if (ysh) {
-      const float4 v = *reinterpret_cast<const float4*>(ysh + (size_t)t * d + c * 4);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = tid + 256 * (c0 + q);
+      if (c0 + q < per && c < nch) {
+        if (ysh) {
+          float f[LE];
+          load_chunk<T>(ysh + (size_t)t * d + c * LE, f);
+#pragma unroll
+          for (int i = 0; i < LE; ++i) acc[q][i] += f[i];
+        }
+        store_chunk<T>(out + (size_t)t * d + c * LE, acc[q]);
+      }
     }
-    *reinterpret_cast<float4*>(out + (size_t)t * d + c * 4) = acc;
   }
 }
 
@@ -83,10 +114,10 @@ hipError_t launch_combine(int dtype, const void* y, const void* y_shared, const 
                           const float* wts, const int32_t* inv_perm, void* out, int T, int d, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL(combine_bf16_kernel, dim3(T), dim3(256), 0, st, (const bf16_t*)y, (const bf16_t*)y_shared,
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(256), 0, st, (const bf16_t*)y, (const bf16_t*)y_shared,
                        tok_off, wts, inv_perm, (bf16_t*)out, d);
   else
-    hipLaunchKernelGGL(combine_f32_kernel, dim3(T), dim3(256), 0, st, (const float*)y, (const float*)y_shared,
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)y, (const float*)y_shared,
                        tok_off, wts, inv_perm, (float*)out, d);
   return hipGetLastError();
 }

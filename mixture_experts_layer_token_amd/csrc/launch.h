@@ -18,16 +18,18 @@ hipError_t launch_router(int dtype, const void* x, const void* w, const int32_t*
                          int S, double* part, int32_t* tok_off, int32_t* status, hipStream_t st);
 // Sums the S slices in order, adds the bias, rounds to float32, selects top-k_t.
 hipError_t launch_topk(const double* part, int S, const float* bias, const int32_t* tok_off, int T, int E,
-                       float scale, int32_t* ids, float* wts, hipStream_t st);
+                       int k_max, float scale, int32_t* ids, float* wts, hipStream_t st);
 // Token offsets alone (one workgroup).
 hipError_t launch_tok_offsets(const int32_t* k, int T, int k_max, int32_t* tok_off, int32_t* status, hipStream_t st);
 
 // route_screen.hip -- bf16 only: MFMA logits with an error bound screen the
 // candidates; exact fp64 logits for candidates; same selection and weights.
-// approx, absum: float [T][E] scratch.  tok_off must be ready.
-hipError_t launch_router_screen(const void* x, const void* w, const float* bias, const int32_t* tok_off, int T,
-                                int d, int E, float scale, float* approx, float* absum, int32_t* ids, float* wts,
-                                hipStream_t st);
+// K slices of the screening pass (partials approx, absum: float [S][T][E]).
+int router_screen_splits(int T, int d, int E);
+// Token offsets (first workgroup), screening pass, then selection.
+hipError_t launch_router_screen(const void* x, const void* w, const float* bias, const int32_t* k, int T, int d,
+                                int E, int k_max, int S, float scale, float* approx, float* absum, int32_t* tok_off,
+                                int32_t* status, int32_t* ids, float* wts, hipStream_t st);
 
 // Row-block table of the grouped FFN kernels.  The rows of group g,
 // [grp_off[g], grp_off[g+1]), are cut into blocks of RB rows; entry i is

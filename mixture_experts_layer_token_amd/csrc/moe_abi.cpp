@@ -68,13 +68,13 @@ bool screened_router(const moe_desc& d) {
 
 void plan_route(const moe_desc& d, Carver& c, RouteWs& w) {
   w.screened = screened_router(d);
-  w.splits = router_splits(d.T, d.d, d.E);
-  const size_t te = (size_t)d.T * d.E;
-  const size_t bytes = w.screened ? 2 * te * sizeof(float) : (size_t)w.splits * te * sizeof(double);
+  w.splits = w.screened ? router_screen_splits(d.T, d.d, d.E) : router_splits(d.T, d.d, d.E);
+  const size_t ste = (size_t)w.splits * d.T * d.E;
+  const size_t bytes = w.screened ? 2 * ste * sizeof(float) : ste * sizeof(double);
   char* p = static_cast<char*>(c.take_bytes(bytes));
   w.part = reinterpret_cast<double*>(p);
   w.approx = reinterpret_cast<float*>(p);
-  w.absum = p ? reinterpret_cast<float*>(p + te * sizeof(float)) : nullptr;
+  w.absum = p ? reinterpret_cast<float*>(p + ste * sizeof(float)) : nullptr;
 }
 void plan_permute(const moe_desc& d, Carver& c, PermWs& w) {
   const size_t n = (size_t)n_blocks(d) * d.E;
@@ -179,14 +179,11 @@ bool shared_gemm(const moe_desc& d) {
 
 moe_status do_route(const moe_desc& d, const void* x, const void* wr, const float* bias, const int32_t* k,
                     int32_t* tok_off, int32_t* ids, float* w, int32_t* status, const RouteWs& ws, hipStream_t st) {
-  if (ws.screened) {
-    hipError_t e = launch_tok_offsets(k, d.T, d.k_max, tok_off, status, st);
-    if (e == hipSuccess)
-      e = launch_router_screen(x, wr, bias, tok_off, d.T, d.d, d.E, d.routed_scale, ws.approx, ws.absum, ids, w, st);
-    return launched(e);
-  }
+  if (ws.screened)
+    return launched(launch_router_screen(x, wr, bias, k, d.T, d.d, d.E, d.k_max, ws.splits, d.routed_scale, ws.approx,
+                                         ws.absum, tok_off, status, ids, w, st));
   hipError_t e = launch_router(d.dtype, x, wr, k, d.T, d.d, d.E, d.k_max, ws.splits, ws.part, tok_off, status, st);
-  if (e == hipSuccess) e = launch_topk(ws.part, ws.splits, bias, tok_off, d.T, d.E, d.routed_scale, ids, w, st);
+  if (e == hipSuccess) e = launch_topk(ws.part, ws.splits, bias, tok_off, d.T, d.E, d.k_max, d.routed_scale, ids, w, st);
   return launched(e);
 }
 

@@ -6,44 +6,11 @@
 // renormalised over the selected set, times the routed scaling factor.
 #include "common.h"
 #include "launch.h"
+#include "select.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// tok_off = exclusive prefix sum of the validated budgets, by one workgroup of
-// 256 threads.  A k_t outside [0, k_max] counts as 0 and raises MOE_DEV_BAD_K.
-__device__ void token_offsets_block(const int32_t* __restrict__ k, int T, int k_max, int32_t* __restrict__ tok_off,
-                                    int32_t* __restrict__ status, int32_t* part, int32_t* bad_any) {
-  const int tid = threadIdx.x;
-  const int per = (T + 255) / 256;
-  const int beg = min(tid * per, T), end = min(beg + per, T);
-  int s = 0, bad = 0;
-  for (int i = beg; i < end; ++i) {
-    int v = k[i];
-    if (v < 0 || v > k_max) { v = 0; bad = 1; }
-    s += v;
-  }
-  if (tid == 0) *bad_any = 0;
-  part[tid] = s;
-  __syncthreads();
-  if (bad) atomicOr(bad_any, 1);
-  for (int off = 1; off < 256; off <<= 1) {
-    int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = part[tid] - s;
-  for (int i = beg; i < end; ++i) {
-    tok_off[i] = run;
-    int v = k[i];
-    if (v < 0 || v > k_max) v = 0;
-    run += v;
-  }
-  if (tid == 255) tok_off[T] = part[255];
-  if (tid == 0 && status) status[0] = *bad_any ? MOE_DEV_BAD_K_BIT : 0;
-}
-
 // ---------------------------------------------------------------------------
 // Router logits l[t][e] = fp32(sum_i x[t][i] * w[e][i] + b[e]), the sum taken in
 // float64 (exact products; only the accumulation rounds) and rounded once.
@@ -103,7 +70,7 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const T* __restrict
   const int tid = threadIdx.x;
   if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
     int32_t* scan_part = reinterpret_cast<int32_t*>(&xs[0][0]);
-    token_offsets_block(k, T_, k_max, tok_off, status, scan_part, scan_part + 256);
+    token_offsets_block<256>(k, T_, k_max, tok_off, status, scan_part, scan_part + 256);
     __syncthreads();
   }
   const int t0 = blockIdx.x * RT, e0 = blockIdx.y * RE;
@@ -150,40 +117,29 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const T* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Top-k_t per token, one wave64 per token.  Every expert becomes a 64-bit key:
-// high word = order-preserving image of the float32 logit (-0 folded to +0),
-// low word = ~e, so the largest key is the largest logit with the lowest
-// index.  k_t rounds of (lane max, wave max via xor-shuffles, remove winner)
-// emit the experts best first.  The softmax over the selected logits is
-// accumulated on the fly (every lane sees every winner), so each lane keeps
-// only the unnormalised weights of the slots it will write.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
+// Top-k_t per token, one wave64 per token: the S slices of float64 partial
+// sums are added in ascending slice order (eight independent loads at a time,
+// a fixed tree inside each group), the bias is added and the sum is rounded
+// once to float32; the selection and weights follow select.h.
 template <int KPL>
 __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ part, int S,
                                                    const float* __restrict__ bias,
                                                    const int32_t* __restrict__ tok_off, int T_, int E,
                                                    float scale, int32_t* __restrict__ ids,
-                                                   float* __restrict__ wts) {
+                                                   float* __restrict__ wts, int scratch_slots) {
+  extern __shared__ uint64_t topk_scratch[];
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
   const int base = tok_off[t];
   const int kt = tok_off[t + 1] - base;
-  uint64_t key[KPL];
+  if (kt == 0) return;
+  uint32_t key[KPL];
 #pragma unroll
   for (int s = 0; s < KPL; ++s) {
     const int e = lane + 64 * s;
     key[s] = 0;
     if (e < E) {
-      // slices summed in groups of 8 (independent loads, fixed tree), groups in order
       const double* pe = part + (size_t)t * E + e;
       const size_t qstride = (size_t)T_ * E;
       double acc = 0.0;
@@ -194,57 +150,23 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ pa
         acc += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
       }
       if (bias) acc += (double)bias[e];
-      float l = (float)acc;
-      if (l == 0.0f) l = 0.0f;
-      uint32_t u = __float_as_uint(l);
-      u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-      key[s] = (static_cast<uint64_t>(u) << 32) | static_cast<uint64_t>(0xffffffffu - (uint32_t)e);
+      key[s] = logit_key((float)acc);
     }
   }
-  float mine[KPL];
-#pragma unroll
-  for (int s = 0; s < KPL; ++s) mine[s] = 0.f;
-  float l0 = 0.f, sum = 0.f;
-  for (int j = 0; j < kt; ++j) {
-    uint64_t m = key[0];
-#pragma unroll
-    for (int s = 1; s < KPL; ++s) m = key[s] > m ? key[s] : m;
-    m = wave_max_u64(m);
-#pragma unroll
-    for (int s = 0; s < KPL; ++s)
-      if (key[s] == m) key[s] = 0;
-    const int e = (int)(0xffffffffu - (uint32_t)(m & 0xffffffffu));
-    uint32_t u = (uint32_t)(m >> 32);
-    u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
-    const float l = __uint_as_float(u);
-    if (j == 0) l0 = l;
-    const float p = expf(l - l0);
-    sum += p;
-    if (lane == (j & 63)) {
-#pragma unroll
-      for (int s = 0; s < KPL; ++s)
-        if ((j >> 6) == s) mine[s] = p;
-      ids[base + j] = e;
-    }
-  }
-  const float inv = scale / sum;
-#pragma unroll
-  for (int s = 0; s < KPL; ++s) {
-    const int j = lane + 64 * s;
-    if (j < kt) wts[base + j] = mine[s] * inv;
-  }
+  wave_topk_softmax<KPL>(key, kt, scale, ids + base, wts + base,
+                         topk_scratch + (threadIdx.x >> 6) * scratch_slots);
 }
 
 // ---------------------------------------------------------------------------
 // Standalone token-offset scan (the screened router has no partial-logit pass).
-__global__ __launch_bounds__(256) void tok_offsets_kernel(const int32_t* __restrict__ k, int T, int k_max,
-                                                          int32_t* __restrict__ tok_off, int32_t* __restrict__ status) {
-  __shared__ int32_t part[257];
-  token_offsets_block(k, T, k_max, tok_off, status, part, part + 256);
+__global__ __launch_bounds__(1024) void tok_offsets_kernel(const int32_t* __restrict__ k, int T, int k_max,
+                                                           int32_t* __restrict__ tok_off, int32_t* __restrict__ status) {
+  __shared__ int32_t part[1025];
+  token_offsets_block<1024>(k, T, k_max, tok_off, status, part, part + 1024);
 }
 
 hipError_t launch_tok_offsets(const int32_t* k, int T, int k_max, int32_t* tok_off, int32_t* status, hipStream_t st) {
-  hipLaunchKernelGGL(tok_offsets_kernel, dim3(1), dim3(256), 0, st, k, T, k_max, tok_off, status);
+  hipLaunchKernelGGL(tok_offsets_kernel, dim3(1), dim3(1024), 0, st, k, T, k_max, tok_off, status);
   return hipGetLastError();
 }
 
@@ -268,11 +190,13 @@ hipError_t launch_router(int dtype, const void* x, const void* w, const int32_t*
 }
 
 hipError_t launch_topk(const double* part, int S, const float* bias, const int32_t* tok_off, int T, int E,
-                       float scale, int32_t* ids, float* wts, hipStream_t st) {
+                       int k_max, float scale, int32_t* ids, float* wts, hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((T + 3) / 4);
+  const int slots = k_max + 1;
+  const size_t lds = (size_t)4 * slots * sizeof(uint64_t);
 #define MOE_TOPK(KPL) \
-  hipLaunchKernelGGL(topk_kernel<KPL>, grid, dim3(256), 0, st, part, S, bias, tok_off, T, E, scale, ids, wts)
+  hipLaunchKernelGGL(topk_kernel<KPL>, grid, dim3(256), lds, st, part, S, bias, tok_off, T, E, scale, ids, wts, slots)
   if (E <= 64) MOE_TOPK(1);
   else if (E <= 128) MOE_TOPK(2);
   else if (E <= 256) MOE_TOPK(4);

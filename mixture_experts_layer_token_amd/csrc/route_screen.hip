@@ -9,33 +9,47 @@
 // logits that cannot enter the top-k_t.
 //
 // Pass 1 (MFMA): a[t][e] = sum x_i w_i and s[t][e] = sum |x_i||w_i| in fp32 with
-// v_mfma_f32_16x16x32_bf16.  Products of bf16 values are exact in fp32, so in
-// any summation order |a - exact| <= d * u * S with u = 2^-24 (2^-23 if the
-// hardware truncates) and S <= s / (1 - d u).  The radius used is
-// r = d * 2^-22 * s (+ a tiny floor), which covers both.
+// v_mfma_f32_16x16x32_bf16, K split over S slices (partial sums per slice, added
+// in slice order by pass 2).  Products of bf16 values are exact in fp32, so in
+// any summation order of depth n the error is at most n * u * S with
+// u = 2^-24 (2^-23 if the hardware truncates) and S <= s / (1 - n u); the
+// slices make n <= d/S + S <= d.  The radius used is r = d * 2^-22 * s (+ a
+// tiny floor), which covers both roundings with a factor of two to spare.
 //
 // Pass 2 (one wave per token): lower_e = a + b - r, upper_e = a + b + r (fp64).
-// L = k_t-th largest lower bound.  Expert e is a candidate iff
+// L = the k_t-th largest lower bound, each rounded down to fp32 first (a
+// smaller L only adds candidates).  Expert e is a candidate iff
 // upper_e >= L - m, m = 2^-21 |L| + 2^-126 (four fp32 ulps at L).  A
 // non-candidate is beaten by k_t experts whose exact logits exceed its own by
 // more than m, so their fp32 logits are strictly larger: it cannot be selected.
-// Candidates get the exact fp64 dot product; the usual wave top-k runs on their
-// exact fp32 logits (non-candidates are never reached, since the k_t experts
-// defining L are candidates).
+// Candidates get the exact fp64 dot product; the top-k of select.h runs on
+// their exact fp32 logits (non-candidates are never reached, since the k_t
+// experts defining L are candidates).
 #include "common.h"
 #include "launch.h"
+#include "select.h"
 
 namespace moe {
 
-// ---- pass 1: approximate logits and |x||w| sums, 64 tokens x 64 experts per WG
-// 4 waves in 2 x 2, each 32 experts x 32 tokens = 2 x 2 tiles of 16 x 16.
-__global__ __launch_bounds__(256) void router_screen_mfma_kernel(const bf16_t* __restrict__ x,
-                                                                 const bf16_t* __restrict__ w, int T, int d, int E,
-                                                                 float* __restrict__ approx, float* __restrict__ absum) {
+// ---- pass 1: partial approximate logits and |x||w| sums of one K slice,
+// 64 tokens x 64 experts per workgroup; 4 waves in 2 x 2, each 32 experts x 32
+// tokens = 2 x 2 tiles of 16 x 16.  Workgroup (0, 0, 0) first writes the token
+// offsets (pass 2 needs them).
+__global__ __launch_bounds__(256) void router_screen_mfma_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int T, int d, int E, float* __restrict__ approx,
+    float* __restrict__ absum, const int32_t* __restrict__ k, int k_max, int32_t* __restrict__ tok_off,
+    int32_t* __restrict__ status) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
+    __shared__ int32_t scan_part[257];
+    token_offsets_block<256>(k, T, k_max, tok_off, status, scan_part, scan_part + 256);
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
   const int t0 = blockIdx.x * 64 + (wave & 1) * 32;
   const int e0 = blockIdx.y * 64 + (wave >> 1) * 32;
+  const int S = gridDim.z, chunks = d / 32;
+  const int k_beg = (int)(((long long)blockIdx.z * chunks) / S) * 32;
+  const int k_end = (int)(((long long)(blockIdx.z + 1) * chunks) / S) * 32;
   // operand rows (clamped in range; results of clamped rows are not stored)
   const bf16_t* wr[2];
   const bf16_t* xr[2];
@@ -53,34 +67,38 @@ __global__ __launch_bounds__(256) void router_screen_mfma_kernel(const bf16_t* _
       aab[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   const u32x4_t sign_off = {0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
-  u32x4_t a[2], b[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    a[i] = *reinterpret_cast<const u32x4_t*>(wr[i]);
-    b[i] = *reinterpret_cast<const u32x4_t*>(xr[i]);
-  }
-  for (int k = 0; k < d; k += 32) {
-    const int kn = (k + 32 < d) ? k + 32 : k;  // next step (the last re-reads, cached)
-    u32x4_t na[2], nb[2];
+  if (k_beg < k_end) {
+    u32x4_t a[2], b[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      na[i] = *reinterpret_cast<const u32x4_t*>(wr[i] + kn);
-      nb[i] = *reinterpret_cast<const u32x4_t*>(xr[i] + kn);
+      a[i] = *reinterpret_cast<const u32x4_t*>(wr[i] + k_beg);
+      b[i] = *reinterpret_cast<const u32x4_t*>(xr[i] + k_beg);
     }
+    for (int kk = k_beg; kk < k_end; kk += 32) {
+      const int kn = (kk + 32 < k_end) ? kk + 32 : kk;  // next step (the last re-reads, cached)
+      u32x4_t na[2], nb[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        acc[i][j] = Mfma<bf16_t>::step(a[i], b[j], acc[i][j]);
-        aab[i][j] = Mfma<bf16_t>::step(a[i] & sign_off, b[j] & sign_off, aab[i][j]);
+      for (int i = 0; i < 2; ++i) {
+        na[i] = *reinterpret_cast<const u32x4_t*>(wr[i] + kn);
+        nb[i] = *reinterpret_cast<const u32x4_t*>(xr[i] + kn);
       }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      a[i] = na[i];
-      b[i] = nb[i];
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = Mfma<bf16_t>::step(a[i], b[j], acc[i][j]);
+          aab[i][j] = Mfma<bf16_t>::step(a[i] & sign_off, b[j] & sign_off, aab[i][j]);
+        }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = na[i];
+        b[i] = nb[i];
+      }
     }
   }
   // lane holds D[e = 4*lg + r][t = lr] of each tile
+  float* const ap = approx + (size_t)blockIdx.z * T * E;
+  float* const sp = absum + (size_t)blockIdx.z * T * E;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -91,215 +109,205 @@ __global__ __launch_bounds__(256) void router_screen_mfma_kernel(const bf16_t* _
       for (int r = 0; r < 4; ++r) {
         const int e = e0 + i * 16 + 4 * lg + r;
         if (e < E) {
-          approx[(size_t)t * E + e] = acc[i][j][r];
-          absum[(size_t)t * E + e] = aab[i][j][r];
+          ap[(size_t)t * E + e] = acc[i][j][r];
+          sp[(size_t)t * E + e] = aab[i][j][r];
         }
       }
     }
 }
 
-__device__ __forceinline__ uint64_t dkey(double v) {  // order-preserving image of a double
-  uint64_t u = __double_as_longlong(v);
-  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64s(uint64_t v) {
+// Lane share of an exact dot product over one 8-element chunk: the products
+// of bf16 values are exact in float32, each is widened and added in float64.
+// acc[q] takes elements 2q and 2q+1 (four independent chains).
+__device__ __forceinline__ void dot8(const uint4& xv, const uint4& wv, double (&acc)[4]) {
+  const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+  const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
+  for (int q = 0; q < 4; ++q) {
+    const float p0 = __uint_as_float(xs[q] << 16) * __uint_as_float(ws[q] << 16);
+    const float p1 = __uint_as_float(xs[q] & 0xffff0000u) * __uint_as_float(ws[q] & 0xffff0000u);
+    acc[q] += (double)p0;
+    acc[q] += (double)p1;
   }
-  return v;
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
+// ---- pass 2: candidates, exact logits, top-k_t and weights; one wave per token.
+// Exact dot products run in passes of 512 * XC elements (lane l takes
+// elements [8l + 512 i, +8) of chunk i).
+constexpr int SEL_GRP = 8;  // candidates whose cross-lane sums are done together
 
-// exact fp64 dots of one token row with NC expert rows (bf16), the whole wave
-// cooperating: lane l takes elements [8l + 512i, +8); results are wave sums.
-template <int NC>
-__device__ __forceinline__ void exact_dots(const bf16_t* __restrict__ xr, const bf16_t* const (&wr)[NC], int d,
-                                           int lane, double (&out)[NC]) {
-  double acc[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) acc[c] = 0.0;
-  for (int i = lane * 8; i < d; i += 512) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(xr + i);
-    uint4 wv[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) wv[c] = *reinterpret_cast<const uint4*>(wr[c] + i);
-    const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-    double xd[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      xd[2 * q] = (double)__uint_as_float(xs[q] << 16);
-      xd[2 * q + 1] = (double)__uint_as_float(xs[q] & 0xffff0000u);
-    }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint32_t ws[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[c] = fma(xd[2 * q], (double)__uint_as_float(ws[q] << 16), acc[c]);
-        acc[c] = fma(xd[2 * q + 1], (double)__uint_as_float(ws[q] & 0xffff0000u), acc[c]);
-      }
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < NC; ++c) out[c] = wave_sum_f64(acc[c]);
-}
-
-// ---- pass 2: candidates, exact logits, top-k_t and weights; one wave per token
-template <int KPL>
+template <int KPL, int XC>
 __global__ __launch_bounds__(256) void router_screen_select_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const float* __restrict__ bias,
-    const float* __restrict__ approx, const float* __restrict__ absum, const int32_t* __restrict__ tok_off, int T,
-    int d, int E, float scale, int32_t* __restrict__ ids, float* __restrict__ wts) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const float* __restrict__ approx, const float* __restrict__ absum, int S, const int32_t* __restrict__ tok_off,
+    int T, int d, int E, float scale, int32_t* __restrict__ ids, float* __restrict__ wts, int red_words,
+    int lds_words) {
+  extern __shared__ uint64_t sel_lds[];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;
   const int base = tok_off[t];
   const int kt = tok_off[t + 1] - base;
   if (kt == 0) return;
+  // per-wave LDS: [red_words: lane shares of SEL_GRP candidates, later the
+  // top-k scratch][E int32: candidate list][E doubles: exact sums by candidate]
+  uint64_t* const area = sel_lds + (size_t)wv * lds_words;
+  double* const red = reinterpret_cast<double*>(area);
+  int32_t* const clist = reinterpret_cast<int32_t*>(area + red_words);
+  double* const cval = reinterpret_cast<double*>(area + red_words + (E + 1) / 2);
+
+  // bounds from the slice partials (added in slice order); the bias of the
+  // lane's experts stays in registers
   const double rad_scale = (double)d * 0x1p-22;
-  double lower[KPL], upper[KPL];
+  double cen[KPL], rad[KPL];
+  float bs[KPL];
+  uint32_t lkey[KPL];
+  const size_t sstride = (size_t)T * E;
 #pragma unroll
   for (int s = 0; s < KPL; ++s) {
     const int e = lane + 64 * s;
-    lower[s] = -INFINITY;
-    upper[s] = -INFINITY;
+    cen[s] = 0.0;
+    rad[s] = 0.0;
+    lkey[s] = 0;
+    bs[s] = 0.f;
     if (e < E) {
-      const double c = (double)approx[(size_t)t * E + e] + (bias ? (double)bias[e] : 0.0);
-      const double r = rad_scale * (double)absum[(size_t)t * E + e] + 0x1p-126;
-      lower[s] = c - r;
-      upper[s] = c + r;
+      if (bias) bs[s] = bias[e];
+      // slices in ascending order, eight loads in flight at a time
+      float a = 0.f, m = 0.f;
+      const float* pa = approx + (size_t)t * E + e;
+      const float* pm = absum + (size_t)t * E + e;
+      for (int q0 = 0; q0 < S; q0 += 8) {
+        float va[8], vm[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          va[i] = (q0 + i < S) ? pa[(size_t)(q0 + i) * sstride] : 0.f;
+          vm[i] = (q0 + i < S) ? pm[(size_t)(q0 + i) * sstride] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          a += va[i];
+          m += vm[i];
+        }
+      }
+      cen[s] = (double)a + (double)bs[s];
+      rad[s] = rad_scale * (double)m + 0x1p-126;
+      lkey[s] = logit_key(__double2float_rd(cen[s] - rad[s]));
     }
   }
-  // L = kt-th largest lower bound.  Keys: the order-preserving image of the
-  // bound with its low 10 bits replaced by the inverted expert index, so keys
-  // are unique; the truncation only lowers L (more candidates, still exact).
-  uint64_t lk[KPL];
-#pragma unroll
-  for (int s = 0; s < KPL; ++s) {
-    const int e = lane + 64 * s;
-    lk[s] = (e < E) ? ((dkey(lower[s]) & ~0x3ffull) | (uint64_t)(1023 - e)) : 0;
-  }
-  uint64_t kth = 0;
-  for (int j = 0; j < kt; ++j) {
-    uint64_t m = lk[0];
-#pragma unroll
-    for (int s = 1; s < KPL; ++s) m = lk[s] > m ? lk[s] : m;
-    m = wave_max_u64s(m);
-#pragma unroll
-    for (int s = 0; s < KPL; ++s)
-      if (lk[s] == m) lk[s] = 0;
-    kth = m;
-  }
-  uint64_t ku = kth & ~0x3ffull;
-  ku = (ku & 0x8000000000000000ull) ? (ku & 0x7fffffffffffffffull) : ~ku;
-  const double L = __longlong_as_double(ku);
-  const double cut = L - (fabs(L) * 0x1p-21 + 0x1p-126);
+  const float L = key_logit(wave_kth_largest<KPL>(lkey, kt));
+  const double cut = (double)L - (fabs((double)L) * 0x1p-21 + 0x1p-126);
 
-  // candidate list (ascending expert index) in LDS, then exact logits four at a time
-  __shared__ int32_t clist_all[4][1024];
-  int32_t* clist = clist_all[threadIdx.x >> 6];
+  // candidate list, ascending expert index; cidx = a slot's place in it
   int ncand = 0;
+  int cidx[KPL];
+  const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int s = 0; s < KPL; ++s) {
     const int e = lane + 64 * s;
-    const bool cand = (e < E) && (upper[s] >= cut);
+    const bool cand = (e < E) && (cen[s] + rad[s] >= cut);
     const uint64_t mask = __ballot(cand);
-    if (cand) clist[ncand + __popcll(mask & ((1ull << lane) - 1ull))] = e;
+    cidx[s] = cand ? ncand + __popcll(mask & below) : -1;
+    if (cand) clist[cidx[s]] = e;
     ncand += __popcll(mask);
   }
-  __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const bf16_t* xr = x + (size_t)t * d;
-  uint64_t key[KPL];
+
+  // Exact logits.  Work items (candidate c, pass p) in order, p fastest; the
+  // router row and token row chunks of item i+1 are requested before item i
+  // is summed.  Each lane's share of a candidate goes to red[c % SEL_GRP][lane];
+  // every SEL_GRP candidates, lane j adds the 64 shares of candidate j of the
+  // group in lane order and stores the rounded logit's key.
+  const bf16_t* xrow = x + (size_t)t * d;
+  constexpr int PASS = 512 * XC;
+  const int npass = (d + PASS - 1) / PASS;
+  const int items = ncand * npass;
+  auto load_item = [&](uint4 (&xv)[XC], uint4 (&wr)[XC], int it) {
+    const int c = it / npass, p0 = (it - c * npass) * PASS;
+    const bf16_t* row = w + (size_t)clist[c] * d;
 #pragma unroll
-  for (int s = 0; s < KPL; ++s) key[s] = 0;
-  for (int c0 = 0; c0 < ncand; c0 += 4) {
-    int ce[4];
-    const bf16_t* wr[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      ce[c] = clist[min(c0 + c, ncand - 1)];  // past the end: repeat the last candidate (result unused)
-      wr[c] = w + (size_t)ce[c] * d;
+    for (int i = 0; i < XC; ++i) {
+      const int off = p0 + 512 * i + 8 * lane;
+      xv[i] = off < d ? *reinterpret_cast<const uint4*>(xrow + off) : zero_u4();
+      wr[i] = off < d ? *reinterpret_cast<const uint4*>(row + off) : zero_u4();
     }
-    double v[4];
-    exact_dots<4>(xr, wr, d, lane, v);
+  };
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  auto finish_item = [&](int it, const uint4 (&xv)[XC], const uint4 (&wr)[XC]) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (c0 + c >= ncand) continue;
-      double vv = v[c];
-      if (bias) vv += (double)bias[ce[c]];
-      float l = (float)vv;
-      if (l == 0.0f) l = 0.0f;
-      uint32_t u = __float_as_uint(l);
-      u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-      const uint64_t kk = (static_cast<uint64_t>(u) << 32) | static_cast<uint64_t>(0xffffffffu - (uint32_t)ce[c]);
-      if (lane == (ce[c] & 63)) {
-#pragma unroll
-        for (int s = 0; s < KPL; ++s)
-          if ((ce[c] >> 6) == s) key[s] = kk;
+    for (int i = 0; i < XC; ++i) dot8(xv[i], wr[i], acc);
+    const int c = it / npass;
+    if (it - c * npass == npass - 1) {  // candidate complete
+      red[(c % SEL_GRP) * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      acc[0] = acc[1] = acc[2] = acc[3] = 0.0;
+      if (c % SEL_GRP == SEL_GRP - 1 || c == ncand - 1) {
+        const int g0 = c - c % SEL_GRP;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane <= c - g0) {
+          double v = 0.0;
+          for (int l = 0; l < 64; ++l) v += red[lane * 64 + l];
+          cval[g0 + lane] = v;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
+  };
+  uint4 xa[XC], wa[XC], xb[XC], wb[XC];
+  if (items > 0) load_item(xa, wa, 0);
+  for (int it = 0; it < items; it += 2) {
+    if (it + 1 < items) load_item(xb, wb, it + 1);
+    finish_item(it, xa, wa);
+    if (it + 2 < items) load_item(xa, wa, it + 2);
+    if (it + 1 < items) finish_item(it + 1, xb, wb);
   }
-  float mine[KPL];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // keys of the candidates (bias added in float64 before the one rounding)
+  uint32_t key[KPL];
 #pragma unroll
-  for (int s = 0; s < KPL; ++s) mine[s] = 0.f;
-  float l0 = 0.f, sum = 0.f;
-  for (int j = 0; j < kt; ++j) {
-    uint64_t m = key[0];
-#pragma unroll
-    for (int s = 1; s < KPL; ++s) m = key[s] > m ? key[s] : m;
-    m = wave_max_u64s(m);
-#pragma unroll
-    for (int s = 0; s < KPL; ++s)
-      if (key[s] == m) key[s] = 0;
-    const int e = (int)(0xffffffffu - (uint32_t)(m & 0xffffffffu));
-    uint32_t u = (uint32_t)(m >> 32);
-    u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
-    const float l = __uint_as_float(u);
-    if (j == 0) l0 = l;
-    const float p = expf(l - l0);
-    sum += p;
-    if (lane == (j & 63)) {
-#pragma unroll
-      for (int s = 0; s < KPL; ++s)
-        if ((j >> 6) == s) mine[s] = p;
-      ids[base + j] = e;
-    }
-  }
-  const float inv = scale / sum;
-#pragma unroll
-  for (int s = 0; s < KPL; ++s) {
-    const int j = lane + 64 * s;
-    if (j < kt) wts[base + j] = mine[s] * inv;
-  }
+  for (int s = 0; s < KPL; ++s) key[s] = cidx[s] >= 0 ? logit_key((float)(cval[cidx[s]] + (double)bs[s])) : 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  wave_topk_softmax<KPL>(key, kt, scale, ids + base, wts + base, area);
 }
 
-hipError_t launch_router_screen(const void* x, const void* w, const float* bias, const int32_t* tok_off, int T,
-                                int d, int E, float scale, float* approx, float* absum, int32_t* ids, float* wts,
-                                hipStream_t st) {
-  if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(router_screen_mfma_kernel, dim3((T + 63) / 64, (E + 63) / 64), dim3(256), 0, st,
-                     (const bf16_t*)x, (const bf16_t*)w, T, d, E, approx, absum);
+// Slices: enough workgroups to fill the chip when the batch is small, at least
+// two 32-element steps per slice, and at most 2^21 partial entries.
+int router_screen_splits(int T, int d, int E) {
+  const long long tiles = (long long)max(1, (T + 63) / 64) * ((E + 63) / 64);
+  long long S = (256 + tiles - 1) / tiles;
+  S = min(S, (long long)max(1, d / 64));
+  S = min(S, 32LL);
+  S = min(S, max(1LL, (2LL << 20) / max(1LL, (long long)T * E)));
+  return (int)max(1LL, S);
+}
+
+hipError_t launch_router_screen(const void* x, const void* w, const float* bias, const int32_t* k, int T, int d,
+                                int E, int k_max, int S, float scale, float* approx, float* absum, int32_t* tok_off,
+                                int32_t* status, int32_t* ids, float* wts, hipStream_t st) {
+  hipLaunchKernelGGL(router_screen_mfma_kernel, dim3(max(1, (T + 63) / 64), (E + 63) / 64, S), dim3(256), 0, st,
+                     (const bf16_t*)x, (const bf16_t*)w, T, d, E, approx, absum, k, k_max, tok_off, status);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || T == 0) return err;
   dim3 grid((T + 3) / 4);
-#define MOE_SEL(KPL)                                                                                            \
-  hipLaunchKernelGGL(router_screen_select_kernel<KPL>, grid, dim3(256), 0, st, (const bf16_t*)x, (const bf16_t*)w, \
-                     bias, approx, absum, tok_off, T, d, E, scale, ids, wts)
-  if (E <= 64) MOE_SEL(1);
-  else if (E <= 128) MOE_SEL(2);
-  else if (E <= 256) MOE_SEL(4);
-  else if (E <= 512) MOE_SEL(8);
-  else MOE_SEL(16);
+  const int red_words = max(SEL_GRP * 64, k_max + 1);
+  const int words = red_words + (E + 1) / 2 + E;
+  const size_t lds = (size_t)4 * words * sizeof(uint64_t);
+#define MOE_SEL(KPL, XC)                                                                                          \
+  hipLaunchKernelGGL((router_screen_select_kernel<KPL, XC>), grid, dim3(256), lds, st, (const bf16_t*)x,          \
+                     (const bf16_t*)w, bias, approx, absum, S, tok_off, T, d, E, scale, ids, wts, red_words, words)
+  if (E <= 64) MOE_SEL(1, 4);
+  else if (E <= 128) MOE_SEL(2, 4);
+  else if (E <= 256) MOE_SEL(4, 4);
+  else if (E <= 512) MOE_SEL(8, 4);
+  else MOE_SEL(16, 4);
 #undef MOE_SEL
   return hipGetLastError();
 }
