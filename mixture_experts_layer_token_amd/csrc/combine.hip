@@ -15,11 +15,10 @@ __device__ __forceinline__ void unpack(const uint4& v, float (&f)[8]) {
   }
 }
 
-// The token's (row, weight) pairs are staged in LDS, CB at a time; each thread
-// then requests the CB rows' 16-byte chunks together before summing them in
+// One workgroup per token; a thread owns 16-byte column chunks c, c+256, ...
+// The rows of CB assignments are requested together, then summed in
 // ascending j (the loads overlap, the arithmetic order does not change).
-constexpr int CB = 8;      // rows in flight per thread
-constexpr int CSTAGE = 256;  // assignments staged in LDS per round
+constexpr int CB = 4;
 
 template <typename T>
 __device__ __forceinline__ void load_chunk(const T* p, float (&f)[16 / sizeof(T)]);
@@ -46,7 +45,6 @@ __device__ __forceinline__ void store_chunk<float>(float* p, const float* f) {
   *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
 }
 
-// One workgroup per token; a thread owns 16-byte column chunks c, c+256, ...
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const T* __restrict__ ysh,
                                                       const int32_t* __restrict__ tok_off,
@@ -54,59 +52,38 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
                                                       const int32_t* __restrict__ inv_perm, T* __restrict__ out,
                                                       int d) {
   constexpr int LE = 16 / sizeof(T);
-  __shared__ int32_t srow[CSTAGE];
-  __shared__ float sw[CSTAGE];
-  const int t = blockIdx.x, tid = threadIdx.x;
+  const int t = blockIdx.x;
   const int a0 = tok_off[t], a1 = tok_off[t + 1];
-  const int nch = d / LE;
-  const int per = (nch + 255) / 256;  // chunks per thread (uniform loop bound)
-  float acc[4][LE];                   // up to four chunks per thread kept live (d <= 8192 for bf16)
-  for (int c0 = 0; c0 < per; c0 += 4) {
+  for (int c = threadIdx.x; c < d / LE; c += 256) {
+    float acc[LE];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int i = 0; i < LE; ++i) acc[i] = 0.f;
+    int a = a0;
+    for (; a + CB <= a1; a += CB) {
+      float f[CB][LE];
 #pragma unroll
-      for (int i = 0; i < LE; ++i) acc[q][i] = 0.f;
-    for (int s0 = a0; s0 < a1; s0 += CSTAGE) {
-      const int n = min(CSTAGE, a1 - s0);
-      __syncthreads();
-      if (tid < n) {
-        srow[tid] = inv_perm[s0 + tid];
-        sw[tid] = wts[s0 + tid];
-      }
-      __syncthreads();
-      for (int j0 = 0; j0 < n; j0 += CB) {
+      for (int j = 0; j < CB; ++j) load_chunk<T>(y + (size_t)inv_perm[a + j] * d + c * LE, f[j]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = tid + 256 * (c0 + q);
-          if (c0 + q < per && c < nch) {
-            float f[CB][LE];
+      for (int j = 0; j < CB; ++j) {
+        const float w = wts[a + j];
 #pragma unroll
-            for (int j = 0; j < CB; ++j)
-              if (j0 + j < n) load_chunk<T>(y + (size_t)srow[j0 + j] * d + c * LE, f[j]);
-#pragma unroll
-            for (int j = 0; j < CB; ++j)
-              if (j0 + j < n) {
-                const float w = sw[j0 + j];
-#pragma unroll
-                for (int i = 0; i < LE; ++i) acc[q][i] = fmaf(w, f[j][i], acc[q][i]);
-              }
-          }
-        }
+        for (int i = 0; i < LE; ++i) acc[i] = fmaf(w, f[j][i], acc[i]);
       }
     }
+    for (; a < a1; ++a) {
+      float f[LE];
+      load_chunk<T>(y + (size_t)inv_perm[a] * d + c * LE, f);
+      const float w = wts[a];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = tid + 256 * (c0 + q);
-      if (c0 + q < per && c < nch) {
-        if (ysh) {
-          float f[LE];
-          load_chunk<T>(ysh + (size_t)t * d + c * LE, f);
-#pragma unroll
-          for (int i = 0; i < LE; ++i) acc[q][i] += f[i];
-        }
-        store_chunk<T>(out + (size_t)t * d + c * LE, acc[q]);
-      }
+      for (int i = 0; i < LE; ++i) acc[i] = fmaf(w, f[i], acc[i]);
     }
+    if (ysh) {
+      float f[LE];
+      load_chunk<T>(ysh + (size_t)t * d + c * LE, f);
+#pragma unroll
+      for (int i = 0; i < LE; ++i) acc[i] += f[i];
+    }
+    store_chunk<T>(out + (size_t)t * d + c * LE, acc);
   }
 }
 

@@ -84,7 +84,8 @@ template <int MODE, int BM, int BNW, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     const bf16_t* __restrict__ in, const int32_t* __restrict__ row_map, const bf16_t* __restrict__ w0,
     const bf16_t* __restrict__ w1, const int4* __restrict__ blocks, int bound, int dense_rows,
-    bf16_t* __restrict__ out, int N, int K) {
+    bf16_t* __restrict__ out, int N, int K, const bf16_t* __restrict__ in_s, const bf16_t* __restrict__ w0s,
+    const bf16_t* __restrict__ w1s, bf16_t* __restrict__ out_s, int rows_s) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = (MODE == 0) ? 2 : 1;
   constexpr int WROWS = NMAT * BNW;                          // weight rows per stage
@@ -98,19 +99,40 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
   __shared__ __attribute__((aligned(1024))) char lds[STAGES * SBYTES];
 
-  // ---- which (row block, row tile, N tile) this workgroup owns ----
+  // ---- which (row block, row tile, N tile) this workgroup owns.  Row tiles
+  // of the second, dense problem (rows_s > 0: an always-on expert over rows
+  // [0, rows_s) with weights w0s/w1s) are spread evenly through those of the
+  // grouped one, so every XCD interleaves both. ----
   const int nN = N / BNW;
-  const int total_rb = blocks ? blocks[bound].x : (dense_rows + GBM - 1) / GBM;
-  const int total = total_rb * SUB * nN;
+  const int r_mt = (blocks ? blocks[bound].x : (dense_rows + GBM - 1) / GBM) * SUB;
+  const int s_mt = ((rows_s + GBM - 1) / GBM) * SUB;
+  const int mt_all = r_mt + s_mt;
+  const int total = mt_all * nN;
   const int per = (total + 7) >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   if (slot >= per) return;
   const int logical = xcd * per + slot;
   if (logical >= total) return;
   const int mtile = logical / nN, nt = logical - mtile * nN;
-  const int rb = mtile / SUB;
+  bool second = false;
+  int mk = mtile;  // row tile index within its problem
+  if (s_mt > 0) {
+    const int lo = (int)((long long)mtile * s_mt / mt_all), hi = (int)((long long)(mtile + 1) * s_mt / mt_all);
+    second = hi > lo;
+    mk = second ? lo : mtile - hi;
+  }
+  const int rb = mk / SUB;
   int g, row0, rows;  // group, first row and rows of the row block
-  if (blocks) {
+  if (second) {
+    g = 0;
+    row0 = rb * GBM;
+    rows = min(GBM, rows_s - row0);
+    in = in_s;
+    row_map = nullptr;
+    w0 = w0s;
+    w1 = w1s;
+    out = out_s;
+  } else if (blocks) {
     const int4 b = blocks[rb];
     g = b.x;
     row0 = b.y;
@@ -120,9 +142,9 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     row0 = rb * GBM;
     rows = min(GBM, dense_rows - row0);
   }
-  const int m0 = (mtile % SUB) * BM;  // first row of the tile within the row block
-  if (m0 >= rows) return;             // the block's rows end in an earlier sub-tile
-  const int n0 = nt * BNW;            // first output column
+  const int m0 = (mk % SUB) * BM;  // first row of the tile within the row block
+  if (m0 >= rows) return;          // the block's rows end in an earlier sub-tile
+  const int n0 = nt * BNW;         // first output column
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -287,16 +309,17 @@ int gemm_row_block() { return GBM; }
 template <int MODE, int BM, int BNW, int WM, int WN, int STAGES>
 static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, const void* w0, const void* w1,
                                       const int4* blocks, int bound, int dense_rows, void* out, int N, int K,
-                                      hipStream_t st) {
+                                      hipStream_t st, const GemmSecond& sec = GemmSecond{}) {
   if (N % BNW != 0 || K % BK != 0) return hipErrorInvalidValue;
   const int rb_bound = blocks ? bound : (dense_rows + GBM - 1) / GBM;
-  const long long total = (long long)rb_bound * (GBM / BM) * (N / BNW);
+  const long long total = ((long long)rb_bound + (sec.rows + GBM - 1) / GBM) * (GBM / BM) * (N / BNW);
   if (total == 0) return hipSuccess;
   const long long nwg = ((total + 7) / 8) * 8;
   if (nwg > 0x7fffffffLL / (64 * WM * WN)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, STAGES>), dim3((unsigned)nwg), dim3(64 * WM * WN), 0,
                      st, (const bf16_t*)in, row_map, (const bf16_t*)w0, (const bf16_t*)w1, blocks, bound, dense_rows,
-                     (bf16_t*)out, N, K);
+                     (bf16_t*)out, N, K, (const bf16_t*)sec.in, (const bf16_t*)sec.w0, (const bf16_t*)sec.w1,
+                     (bf16_t*)sec.out, sec.rows);
   return hipGetLastError();
 }
 
@@ -306,22 +329,22 @@ static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, co
 // 3-stage ring keeps more of them in flight).
 hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
                                   const int4* blocks, int bound, int dense_rows, int rows_hint, void* h, int N,
-                                  int K, hipStream_t st) {
+                                  int K, hipStream_t st, const GemmSecond& sec) {
   if (rows_hint >= GBM)
-    return launch_gemm_variant<0, 256, 128, 4, 2, 2>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st);
-  return launch_gemm_variant<0, 128, 128, 2, 4, 3>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st);
+    return launch_gemm_variant<0, 256, 128, 4, 2, 2>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st, sec);
+  return launch_gemm_variant<0, 128, 128, 2, 4, 3>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st, sec);
 }
 
 hipError_t launch_ffn_down_gemm(const void* h, const void* wd, const int4* blocks, int bound, int dense_rows,
-                                int rows_hint, void* y, int N, int K, hipStream_t st) {
+                                int rows_hint, void* y, int N, int K, hipStream_t st, const GemmSecond& sec) {
   if (rows_hint >= GBM) {
     if (N % 256 == 0)
-      return launch_gemm_variant<1, 256, 256, 4, 2, 2>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st);
-    return launch_gemm_variant<1, 256, 128, 4, 2, 2>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st);
+      return launch_gemm_variant<1, 256, 256, 4, 2, 2>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
+    return launch_gemm_variant<1, 256, 128, 4, 2, 2>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
   }
   if (N % 256 == 0)
-    return launch_gemm_variant<1, 128, 256, 2, 2, 3>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st);
-  return launch_gemm_variant<1, 128, 128, 2, 2, 3>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st);
+    return launch_gemm_variant<1, 128, 256, 2, 2, 3>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
+  return launch_gemm_variant<1, 128, 128, 2, 2, 3>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
 }
 
 }  // namespace moe

@@ -69,12 +69,24 @@ hipError_t launch_ffn_down_stream(int dtype, const void* h, const void* wd, cons
 // entries + count; blocks == nullptr: one dense group of dense_rows rows).
 // rows_hint (an estimate of rows per group, from the shape only) picks the
 // tile height.  N must be a multiple of 128 and K of 64.
+// `sec` optionally adds a second, dense problem of the same N and K to the
+// launch: rows [0, sec.rows) of sec.in (no row map) against weights
+// sec.w0 / sec.w1 into sec.out -- the always-on shared expert, whose
+// compute-bound tiles then interleave with the grouped, weight-streaming ones.
+struct GemmSecond {
+  const void* in = nullptr;
+  const void* w0 = nullptr;
+  const void* w1 = nullptr;
+  void* out = nullptr;
+  int rows = 0;
+};
 int gemm_row_block();
 hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
                                   const int4* blocks, int bound, int dense_rows, int rows_hint, void* h, int N,
-                                  int K, hipStream_t st);
+                                  int K, hipStream_t st, const GemmSecond& sec = GemmSecond{});
 hipError_t launch_ffn_down_gemm(const void* h, const void* wd, const int4* blocks, int bound, int dense_rows,
-                                int rows_hint, void* y, int N, int K, hipStream_t st);
+                                int rows_hint, void* y, int N, int K, hipStream_t st,
+                                const GemmSecond& sec = GemmSecond{});
 
 // combine.hip
 hipError_t launch_combine(int dtype, const void* y, const void* y_shared, const int32_t* tok_off,

@@ -174,6 +174,12 @@ bool shared_gemm(const moe_desc& d) {
   if (d.dtype != MOE_BF16 || d.path == MOE_PATH_STREAM) return false;
   return d.path == MOE_PATH_GEMM || d.T >= 256;
 }
+// The shared expert runs inside the routed grouped-GEMM launches (its row
+// tiles interleaved with the routed ones) when both take the GEMM path and
+// its intermediate size equals the routed one.
+bool fused_shared(const moe_desc& d) {
+  return d.I_shared > 0 && d.I_shared == d.I && routed_gemm(d) && shared_gemm(d);
+}
 
 // ---- stage bodies (arguments already validated) ----
 
@@ -197,21 +203,24 @@ moe_status do_permute(const moe_desc& d, const int32_t* tok_off, const int32_t* 
 
 // The row-block table fw.blocks is built here when `build_blocks` (otherwise
 // the permutation wrote it).
+// `sec`: the shared expert's part when it is fused into the routed launch.
 moe_status do_gateup(const moe_desc& d, const void* x, const void* wg, const void* wu, const int32_t* expert_off,
-                     const int32_t* perm_tok, void* h, const FfnWs& fw, bool build_blocks, hipStream_t st) {
+                     const int32_t* perm_tok, void* h, const FfnWs& fw, bool build_blocks, hipStream_t st,
+                     const GemmSecond& sec = GemmSecond{}) {
   hipError_t e = build_blocks ? launch_row_blocks(expert_off, d.E, fw.rb, fw.bound, fw.blocks, st) : hipSuccess;
   if (e != hipSuccess) return launched(e);
   if (routed_gemm(d))
-    return launched(launch_ffn_gateup_gemm(x, perm_tok, wg, wu, fw.blocks, fw.bound, 0, rows_hint(d), h, d.I, d.d, st));
+    return launched(
+        launch_ffn_gateup_gemm(x, perm_tok, wg, wu, fw.blocks, fw.bound, 0, rows_hint(d), h, d.I, d.d, st, sec));
   return launched(launch_ffn_gateup_stream(d.dtype, x, perm_tok, wg, wu, fw.blocks, fw.bound, 0, h, d.I, d.d, st));
 }
 
 moe_status do_down(const moe_desc& d, const void* h, const void* wd, const int32_t* expert_off, void* y,
-                   const FfnWs& fw, bool build_blocks, hipStream_t st) {
+                   const FfnWs& fw, bool build_blocks, hipStream_t st, const GemmSecond& sec = GemmSecond{}) {
   hipError_t e = build_blocks ? launch_row_blocks(expert_off, d.E, fw.rb, fw.bound, fw.blocks, st) : hipSuccess;
   if (e != hipSuccess) return launched(e);
   if (routed_gemm(d))
-    return launched(launch_ffn_down_gemm(h, wd, fw.blocks, fw.bound, 0, rows_hint(d), y, d.d, d.I, st));
+    return launched(launch_ffn_down_gemm(h, wd, fw.blocks, fw.bound, 0, rows_hint(d), y, d.d, d.I, st, sec));
   return launched(launch_ffn_down_stream(d.dtype, h, wd, fw.blocks, fw.bound, 0, y, d.d, d.I, st));
 }
 
@@ -349,6 +358,12 @@ moe_status moe_ffn(const moe_desc* desc, const void* x, const void* w_gate, cons
   FfnWs fw;
   plan_ffn(d, c, fw);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fused_shared(d)) {
+    MOE_TRY(do_gateup(d, x, w_gate, w_up, expert_off, perm_tok, fw.h, fw, true, st,
+                      GemmSecond{x, ws_gate, ws_up, fw.h_sh, d.T}));
+    return do_down(d, fw.h, w_down, expert_off, y_perm, fw, false, st,
+                   GemmSecond{fw.h_sh, ws_down, ws_down, y_shared, d.T});
+  }
   MOE_TRY(do_gateup(d, x, w_gate, w_up, expert_off, perm_tok, fw.h, fw, true, st));
   MOE_TRY(do_down(d, fw.h, w_down, expert_off, y_perm, fw, false, st));
   if (d.I_shared) MOE_TRY(do_shared(d, x, ws_gate, ws_up, ws_down, fw.h_sh, y_shared, st));
@@ -388,9 +403,16 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router
   MOE_TRY(do_route(d, x, w_router, router_bias, k, fw.tok_off, fw.ids, fw.w, status, fw.r, st));
   MOE_TRY(do_permute(d, fw.tok_off, fw.ids, fw.counts, fw.expert_off, fw.perm_tok, fw.perm_src, fw.inv_perm,
                      fw.n_active, stats, fw.p, &fw.f, st));
-  MOE_TRY(do_gateup(d, x, w_gate, w_up, fw.expert_off, fw.perm_tok, fw.f.h, fw.f, false, st));
-  MOE_TRY(do_down(d, fw.f.h, w_down, fw.expert_off, fw.y, fw.f, false, st));
-  if (d.I_shared) MOE_TRY(do_shared(d, x, ws_gate, ws_up, ws_down, fw.f.h_sh, fw.y_sh, st));
+  if (fused_shared(d)) {
+    MOE_TRY(do_gateup(d, x, w_gate, w_up, fw.expert_off, fw.perm_tok, fw.f.h, fw.f, false, st,
+                      GemmSecond{x, ws_gate, ws_up, fw.f.h_sh, d.T}));
+    MOE_TRY(do_down(d, fw.f.h, w_down, fw.expert_off, fw.y, fw.f, false, st,
+                    GemmSecond{fw.f.h_sh, ws_down, ws_down, fw.y_sh, d.T}));
+  } else {
+    MOE_TRY(do_gateup(d, x, w_gate, w_up, fw.expert_off, fw.perm_tok, fw.f.h, fw.f, false, st));
+    MOE_TRY(do_down(d, fw.f.h, w_down, fw.expert_off, fw.y, fw.f, false, st));
+    if (d.I_shared) MOE_TRY(do_shared(d, x, ws_gate, ws_up, ws_down, fw.f.h_sh, fw.y_sh, st));
+  }
   return do_combine(d, fw.y, fw.y_sh, fw.tok_off, fw.w, fw.inv_perm, out, st);
 }
 

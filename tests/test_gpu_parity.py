@@ -174,6 +174,7 @@ def test_graph_capture_replays_any_k():
     (300, 8, 128, 128, 8, 0),        # every expert has 100-300 rows
     (1500, 64, 512, 256, 16, 128),   # many experts, uneven rows
     (40, 32, 384, 128, 4, 0),        # few rows per expert (GEMM tail-only tiles)
+    (520, 8, 256, 256, 4, 256),      # shared expert as wide as the routed ones: fused into the GEMM launches
 ])
 def test_ffn_paths_bf16(path, T, E, d, I, kmax, Is):
     """Both FFN paths compute the same function on the same routing."""
