@@ -14,113 +14,107 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // Router logits l[t][e] = fp32(sum_i x[t][i] * w[e][i] + b[e]), the sum taken in
 // float64 (exact products; only the accumulation rounds) and rounded once.
-// Tile: 64 tokens x 64 experts per workgroup, 4x4 outputs per thread, K staged
+// Tile: 64 tokens x RE experts per workgroup (RE = 8, 16 or 64, the smallest
+// that holds E, so small expert counts do not pay for padding), K staged
 // through LDS 32 elements at a time, already widened to float64.  K is split
 // over gridDim.z slices so that small batches still fill the chip; slice s
 // writes its float64 partial sums to part[s][t][e], and the top-k kernel adds
 // the slices in ascending order (any float64 summation order keeps the
 // routing contract: exact products, float64 accumulation, one rounding).
 // Workgroup (0, 0, 0) also computes the token offsets.
-constexpr int RT = 64, RE = 64, RK = 32, RPAD = 65;
+constexpr int RT = 64, RK = 32;
 
-template <typename T>
-__device__ __forceinline__ void stage_rows_f64(double (*dst)[RPAD], const T* __restrict__ src,
-                                               int row0, int nrows, int ld, int k0, int tid);
-
-template <>
-__device__ __forceinline__ void stage_rows_f64<bf16_t>(double (*dst)[RPAD], const bf16_t* __restrict__ src,
-                                                       int row0, int nrows, int ld, int k0, int tid) {
-  // 64 rows x 32 bf16 = 256 chunks of 8 elements; one per thread.
-  const int r = tid & 63, c = tid >> 6;
-  uint4 v = zero_u4();
-  if (row0 + r < nrows) v = *reinterpret_cast<const uint4*>(src + (size_t)(row0 + r) * ld + k0 + c * 8);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// NR rows x RK elements of src (rows past nrows read as zero) into dst[k][row].
+template <int NR, int LD, typename T>
+__device__ __forceinline__ void stage_rows_f64(double (*dst)[LD], const T* __restrict__ src, int row0, int nrows,
+                                               int ld, int k0, int tid) {
+  constexpr int LE = 16 / sizeof(T);       // elements per 16-byte load
+  constexpr int CH = RK / LE;              // loads per row
+  constexpr int PER = (NR * CH + 255) / 256;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    dst[c * 8 + 2 * i][r] = (double)__uint_as_float(w[i] << 16);
-    dst[c * 8 + 2 * i + 1][r] = (double)__uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-
-template <>
-__device__ __forceinline__ void stage_rows_f64<float>(double (*dst)[RPAD], const float* __restrict__ src,
-                                                      int row0, int nrows, int ld, int k0, int tid) {
-  // 64 rows x 32 floats = 512 chunks of 4 elements; two per thread.
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
+  for (int p = 0; p < PER; ++p) {
     const int q = tid + 256 * p;
-    const int r = q & 63, c = q >> 6;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row0 + r < nrows) v = *reinterpret_cast<const float4*>(src + (size_t)(row0 + r) * ld + k0 + c * 4);
-    dst[c * 4 + 0][r] = (double)v.x;
-    dst[c * 4 + 1][r] = (double)v.y;
-    dst[c * 4 + 2][r] = (double)v.z;
-    dst[c * 4 + 3][r] = (double)v.w;
+    if (q < NR * CH) {
+      const int r = q % NR, c = q / NR;
+      uint4 v = zero_u4();
+      if (row0 + r < nrows) v = *reinterpret_cast<const uint4*>(src + (size_t)(row0 + r) * ld + k0 + c * LE);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dst[c * 8 + 2 * i][r] = (double)__uint_as_float(u[i] << 16);
+          dst[c * 8 + 2 * i + 1][r] = (double)__uint_as_float(u[i] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[c * 4 + i][r] = (double)__uint_as_float(u[i]);
+      }
+    }
   }
 }
 
-template <typename T>
+template <typename T, int RE>
 __global__ __launch_bounds__(256) void router_partial_kernel(const T* __restrict__ x, const T* __restrict__ w,
                                                              int T_, int d, int E, double* __restrict__ part,
                                                              const int32_t* __restrict__ k, int k_max,
                                                              int32_t* __restrict__ tok_off,
                                                              int32_t* __restrict__ status) {
-  __shared__ double xs[RK][RPAD];
-  __shared__ double ws[RK][RPAD];
+  constexpr int TX = RE < 16 ? RE : 16, EPT = RE / TX, TY = 256 / TX, TPT = RT / TY;
+  __shared__ double xs[RK][RT + 1];
+  __shared__ double ws[RK][RE + 1];
+  __shared__ int32_t scan_part[257];
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
-    int32_t* scan_part = reinterpret_cast<int32_t*>(&xs[0][0]);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
     token_offsets_block<256>(k, T_, k_max, tok_off, status, scan_part, scan_part + 256);
-    __syncthreads();
-  }
   const int t0 = blockIdx.x * RT, e0 = blockIdx.y * RE;
   const int S = gridDim.z, chunks = d / RK;
   const int c_beg = (int)(((long long)blockIdx.z * chunks) / S);
   const int c_end = (int)(((long long)(blockIdx.z + 1) * chunks) / S);
-  const int ty = tid >> 4, tx = tid & 15;
-  double acc[4][4];
+  const int ty = tid / TX, tx = tid % TX;
+  double acc[TPT][EPT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TPT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int j = 0; j < EPT; ++j) acc[i][j] = 0.0;
 
   for (int c = c_beg; c < c_end; ++c) {
     const int k0 = c * RK;
-    stage_rows_f64<T>(xs, x, t0, T_, d, k0, tid);
-    stage_rows_f64<T>(ws, w, e0, E, d, k0, tid);
+    stage_rows_f64<RT, RT + 1, T>(xs, x, t0, T_, d, k0, tid);
+    stage_rows_f64<RE, RE + 1, T>(ws, w, e0, E, d, k0, tid);
     __syncthreads();
 #pragma unroll 8
     for (int kk = 0; kk < RK; ++kk) {
-      double a[4], b[4];
+      double a[TPT], b[EPT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty + 16 * i];
+      for (int i = 0; i < TPT; ++i) a[i] = xs[kk][ty + TY * i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx + 16 * j];
+      for (int j = 0; j < EPT; ++j) b[j] = ws[kk][tx + TX * j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TPT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < EPT; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
     }
     __syncthreads();
   }
   double* out = part + (size_t)blockIdx.z * T_ * E;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty + 16 * i;
+  for (int i = 0; i < TPT; ++i) {
+    const int t = t0 + ty + TY * i;
     if (t >= T_) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx + 16 * j;
+    for (int j = 0; j < EPT; ++j) {
+      const int e = e0 + tx + TX * j;
       if (e < E) out[(size_t)t * E + e] = acc[i][j];
     }
   }
 }
 
+static int router_tile_e(int E) { return E <= 8 ? 8 : (E <= 16 ? 16 : 64); }
+
 // ---------------------------------------------------------------------------
 // Top-k_t per token, one wave64 per token: the S slices of float64 partial
-// sums are added in ascending slice order (eight independent loads at a time,
-// a fixed tree inside each group), the bias is added and the sum is rounded
-// once to float32; the selection and weights follow select.h.
+// sums are added in ascending slice order, the bias is added and the sum is
+// rounded once to float32; the selection and weights follow select.h.
 template <int KPL>
 __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ part, int S,
                                                    const float* __restrict__ bias,
@@ -142,12 +136,16 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ pa
     if (e < E) {
       const double* pe = part + (size_t)t * E + e;
       const size_t qstride = (size_t)T_ * E;
+      // G loads in flight at a time (all slices at once for one key per lane);
+      // each group is summed in order, groups in order
+      constexpr int G = KPL == 1 ? 32 : (KPL == 2 ? 16 : 8);
       double acc = 0.0;
-      for (int q0 = 0; q0 < S; q0 += 8) {
-        double v[8];
+      for (int q0 = 0; q0 < S; q0 += G) {
+        double v[G];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (q0 + i < S) ? pe[(size_t)(q0 + i) * qstride] : 0.0;
-        acc += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+        for (int i = 0; i < G; ++i) v[i] = (q0 + i < S) ? pe[(size_t)(q0 + i) * qstride] : 0.0;
+#pragma unroll
+        for (int i = 0; i < G; ++i) acc += v[i];
       }
       if (bias) acc += (double)bias[e];
       key[s] = logit_key((float)acc);
@@ -172,20 +170,33 @@ hipError_t launch_tok_offsets(const int32_t* k, int T, int k_max, int32_t* tok_o
 
 int router_splits(int T, int d, int E) {
   if (T == 0) return 1;
-  const int tiles = ((T + RT - 1) / RT) * ((E + RE - 1) / RE);
+  const int tiles = ((T + RT - 1) / RT) * ((E + router_tile_e(E) - 1) / router_tile_e(E));
   const int want = (256 + tiles - 1) / tiles;
   return max(1, min(min(want, 32), d / RK));
 }
 
+template <typename T>
+static void launch_router_t(const T* x, const T* w, const int32_t* k, int T_, int d, int E, int k_max, int S,
+                            double* part, int32_t* tok_off, int32_t* status, hipStream_t st) {
+  const int RE = router_tile_e(E);
+  dim3 grid(max(1, (T_ + RT - 1) / RT), (E + RE - 1) / RE, S);
+  if (RE == 8)
+    hipLaunchKernelGGL((router_partial_kernel<T, 8>), grid, dim3(256), 0, st, x, w, T_, d, E, part, k, k_max, tok_off,
+                       status);
+  else if (RE == 16)
+    hipLaunchKernelGGL((router_partial_kernel<T, 16>), grid, dim3(256), 0, st, x, w, T_, d, E, part, k, k_max,
+                       tok_off, status);
+  else
+    hipLaunchKernelGGL((router_partial_kernel<T, 64>), grid, dim3(256), 0, st, x, w, T_, d, E, part, k, k_max,
+                       tok_off, status);
+}
+
 hipError_t launch_router(int dtype, const void* x, const void* w, const int32_t* k, int T, int d, int E, int k_max,
                          int S, double* part, int32_t* tok_off, int32_t* status, hipStream_t st) {
-  dim3 grid(max(1, (T + RT - 1) / RT), (E + RE - 1) / RE, S);
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL(router_partial_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)x, (const bf16_t*)w,
-                       T, d, E, part, k, k_max, tok_off, status);
+    launch_router_t<bf16_t>((const bf16_t*)x, (const bf16_t*)w, k, T, d, E, k_max, S, part, tok_off, status, st);
   else
-    hipLaunchKernelGGL(router_partial_kernel<float>, grid, dim3(256), 0, st, (const float*)x, (const float*)w, T,
-                       d, E, part, k, k_max, tok_off, status);
+    launch_router_t<float>((const float*)x, (const float*)w, k, T, d, E, k_max, S, part, tok_off, status, st);
   return hipGetLastError();
 }
 
