@@ -59,23 +59,27 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+KERNEL_SOURCES = {"stream": ("ffn_stream.hip", "common.h"), "gemm": ("ffn_gemm.hip", "common.h")}
+
+
+def kernel_source_hash(path: str) -> str:
+    """Hash of the source files of the gate/up kernel of FFN path `path`."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_layer_token_amd", "csrc")
-    for f in ("ffn_stream.hip", "ffn_gemm.hip", "common.h"):
+    for f in KERNEL_SOURCES[path]:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, path: str):
     """Per-launch HBM bytes of the gate/up kernel from the committed rocprofv3
     counter runs, or None when absent or taken on other kernel source."""
     try:
         rec = json.load(open(TRAFFIC_FILE))[workload]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("path") != path or rec.get("source_hash") != kernel_source_hash(path):
         return None
     return rec.get("bytes_per_launch")
 
@@ -248,7 +252,7 @@ def main():
                       else "ffn_stream_kernel (gate/up + SwiGLU)")
     roof["avg_launch_us"] = round(k_ms * 1e3, 2)
     roof["algorithmic_per_launch"] = gu_flops if cfg.name in PREFILL else gu_bytes
-    roof["traffic"] = measured_traffic(cfg.name)
+    roof["traffic"] = measured_traffic(cfg.name, routed_path)
 
     # ---- whole layer against its own roofline ----
     w_bytes = 3 * n_act * d * I * esz

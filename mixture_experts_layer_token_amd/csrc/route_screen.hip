@@ -31,10 +31,12 @@
 
 namespace moe {
 
-// ---- pass 1: partial approximate logits and |x||w| sums of one K slice,
-// 64 tokens x 64 experts per workgroup; 4 waves in 2 x 2, each 32 experts x 32
-// tokens = 2 x 2 tiles of 16 x 16.  Workgroup (0, 0, 0) first writes the token
-// offsets (pass 2 needs them).
+// ---- pass 1: partial approximate logits and |x||w| sums of one K slice.
+// A workgroup covers 64 tokens x 256 experts: wave w takes experts
+// [64w, 64w + 64) of the span as a 4 x 4 grid of 16 x 16 MFMA tiles.  The four
+// waves read the same token rows (hits in the CU's L1 after the first), so the
+// bytes fetched per MFMA are a quarter of a one-tile-per-wave split.
+// Workgroup (0, 0, 0) first writes the token offsets (pass 2 needs them).
 __global__ __launch_bounds__(256) void router_screen_mfma_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int T, int d, int E, float* __restrict__ approx,
     float* __restrict__ absum, const int32_t* __restrict__ k, int k_max, int32_t* __restrict__ tok_off,
@@ -45,52 +47,59 @@ __global__ __launch_bounds__(256) void router_screen_mfma_kernel(
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int t0 = blockIdx.x * 64 + (wave & 1) * 32;
-  const int e0 = blockIdx.y * 64 + (wave >> 1) * 32;
+  const int t0 = blockIdx.x * 64;
+  const int e0 = blockIdx.y * 256 + wave * 64;
+  if (e0 >= E) return;
   const int S = gridDim.z, chunks = d / 32;
   const int k_beg = (int)(((long long)blockIdx.z * chunks) / S) * 32;
   const int k_end = (int)(((long long)(blockIdx.z + 1) * chunks) / S) * 32;
   // operand rows (clamped in range; results of clamped rows are not stored)
-  const bf16_t* wr[2];
-  const bf16_t* xr[2];
+  const bf16_t* wr[4];
+  const bf16_t* xr[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
     wr[i] = w + (size_t)min(e0 + i * 16 + lr, E - 1) * d + lg * 8;
     xr[i] = x + (size_t)min(t0 + i * 16 + lr, T - 1) * d + lg * 8;
   }
-  f32x4_t acc[2][2], aab[2][2];
+  f32x4_t acc[4][4], aab[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 4; ++j) {
       acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       aab[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   const u32x4_t sign_off = {0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
   if (k_beg < k_end) {
-    u32x4_t a[2], b[2];
+    u32x4_t a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
       a[i] = *reinterpret_cast<const u32x4_t*>(wr[i] + k_beg);
       b[i] = *reinterpret_cast<const u32x4_t*>(xr[i] + k_beg);
     }
     for (int kk = k_beg; kk < k_end; kk += 32) {
       const int kn = (kk + 32 < k_end) ? kk + 32 : kk;  // next step (the last re-reads, cached)
-      u32x4_t na[2], nb[2];
+      u32x4_t na[4], nb[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 4; ++i) {
         na[i] = *reinterpret_cast<const u32x4_t*>(wr[i] + kn);
         nb[i] = *reinterpret_cast<const u32x4_t*>(xr[i] + kn);
       }
+      u32x4_t aa[4], ab[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i) {
+        aa[i] = a[i] & sign_off;
+        ab[i] = b[i] & sign_off;
+      }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
           acc[i][j] = Mfma<bf16_t>::step(a[i], b[j], acc[i][j]);
-          aab[i][j] = Mfma<bf16_t>::step(a[i] & sign_off, b[j] & sign_off, aab[i][j]);
+          aab[i][j] = Mfma<bf16_t>::step(aa[i], ab[j], aab[i][j]);
         }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 4; ++i) {
         a[i] = na[i];
         b[i] = nb[i];
       }
@@ -100,20 +109,25 @@ __global__ __launch_bounds__(256) void router_screen_mfma_kernel(
   float* const ap = approx + (size_t)blockIdx.z * T * E;
   float* const sp = absum + (size_t)blockIdx.z * T * E;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + j * 16 + lr;
+    if (t >= T) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int t = t0 + j * 16 + lr;
-      if (t >= T) continue;
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + i * 16 + 4 * lg;
+      if ((E & 3) == 0 && e + 3 < E) {
+        *reinterpret_cast<float4*>(ap + (size_t)t * E + e) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        *reinterpret_cast<float4*>(sp + (size_t)t * E + e) = make_float4(aab[i][j][0], aab[i][j][1], aab[i][j][2], aab[i][j][3]);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = e0 + i * 16 + 4 * lg + r;
-        if (e < E) {
-          ap[(size_t)t * E + e] = acc[i][j][r];
-          sp[(size_t)t * E + e] = aab[i][j][r];
-        }
+        for (int r = 0; r < 4; ++r)
+          if (e + r < E) {
+            ap[(size_t)t * E + e + r] = acc[i][j][r];
+            sp[(size_t)t * E + e + r] = aab[i][j][r];
+          }
       }
     }
+  }
 }
 
 // Lane share of an exact dot product over one 8-element chunk: the products
@@ -278,21 +292,22 @@ __global__ __launch_bounds__(256) void router_screen_select_kernel(
   wave_topk_softmax<KPL>(key, kt, scale, ids + base, wts + base, area);
 }
 
-// Slices: enough workgroups to fill the chip when the batch is small, at least
-// two 32-element steps per slice, and at most 2^21 partial entries.
+// Slices: enough workgroups (64 tokens x 256 experts each) to give every CU
+// one, at least two 32-element steps per slice, and at most 2^22 partial
+// entries per array.
 int router_screen_splits(int T, int d, int E) {
-  const long long tiles = (long long)max(1, (T + 63) / 64) * ((E + 63) / 64);
-  long long S = (256 + tiles - 1) / tiles;
+  const long long wgs = (long long)max(1, (T + 63) / 64) * ((E + 255) / 256);
+  long long S = (256 + wgs - 1) / wgs;
   S = min(S, (long long)max(1, d / 64));
   S = min(S, 32LL);
-  S = min(S, max(1LL, (2LL << 20) / max(1LL, (long long)T * E)));
+  S = min(S, max(1LL, (4LL << 20) / max(1LL, (long long)T * E)));
   return (int)max(1LL, S);
 }
 
 hipError_t launch_router_screen(const void* x, const void* w, const float* bias, const int32_t* k, int T, int d,
                                 int E, int k_max, int S, float scale, float* approx, float* absum, int32_t* tok_off,
                                 int32_t* status, int32_t* ids, float* wts, hipStream_t st) {
-  hipLaunchKernelGGL(router_screen_mfma_kernel, dim3(max(1, (T + 63) / 64), (E + 63) / 64, S), dim3(256), 0, st,
+  hipLaunchKernelGGL(router_screen_mfma_kernel, dim3(max(1, (T + 63) / 64), (E + 255) / 256, S), dim3(256), 0, st,
                      (const bf16_t*)x, (const bf16_t*)w, T, d, E, approx, absum, k, k_max, tok_off, status);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || T == 0) return err;
