@@ -45,7 +45,7 @@ hipError_t launch_row_blocks(const int32_t* grp_off, int G, int RB, int bound, i
 constexpr int PERM_BLOCK = 256;  // tokens per histogram block
 // blocks (nullable): also writes the row-block table of the expert groups
 // (RB rows per block, `bound` entries + the count), as launch_row_blocks would.
-hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int E, int32_t* block_counts,
+hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int E, int k_max, int32_t* block_counts,
                           int32_t* block_base, int32_t* counts, int32_t* expert_off, int32_t* perm_tok,
                           int32_t* perm_src, int32_t* inv_perm, int32_t* n_active, int32_t* stats, int RB,
                           int bound, int4* blocks, hipStream_t st);

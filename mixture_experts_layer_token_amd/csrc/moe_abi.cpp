@@ -196,7 +196,7 @@ moe_status do_route(const moe_desc& d, const void* x, const void* wr, const floa
 moe_status do_permute(const moe_desc& d, const int32_t* tok_off, const int32_t* ids, int32_t* counts,
                       int32_t* expert_off, int32_t* perm_tok, int32_t* perm_src, int32_t* inv_perm,
                       int32_t* n_active, int32_t* stats, const PermWs& ws, const FfnWs* fw, hipStream_t st) {
-  return launched(launch_permute(tok_off, ids, d.T, d.E, ws.block_counts, ws.block_base, counts, expert_off,
+  return launched(launch_permute(tok_off, ids, d.T, d.E, d.k_max, ws.block_counts, ws.block_base, counts, expert_off,
                                  perm_tok, perm_src, inv_perm, n_active, stats, fw ? fw->rb : 1, fw ? fw->bound : 0,
                                  fw ? fw->blocks : nullptr, st));
 }

@@ -103,40 +103,67 @@ __global__ __launch_bounds__(PERM_BLOCK) void expert_hist_kernel(const int32_t* 
 }
 
 // One workgroup: per-expert running sums over blocks, then the exclusive scan
-// over experts (E <= 1024: one expert per thread).
+// over experts.  Q = 1024 / E' threads share an expert (E' = E rounded up to a
+// power of two): thread (e, q) sums a contiguous run of blocks, the runs'
+// sums are scanned per expert, then every thread writes its blocks' bases.
 __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __restrict__ block_counts, int nblk,
-                                                           int E, int32_t* __restrict__ block_base,
+                                                           int E, int Q, int32_t* __restrict__ block_base,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ expert_off,
                                                            int32_t* __restrict__ n_active,
                                                            int32_t* __restrict__ stats, int RB, int bound,
                                                            int4* __restrict__ blocks) {
   __shared__ int32_t sc[1024];
+  __shared__ int32_t qsum[1024];
   __shared__ int32_t nact, nblocks;
-  const int e = threadIdx.x;
-  int run = 0;
+  const int tid = threadIdx.x;
+  const int e = tid / Q, q = tid - (tid / Q) * Q;  // Q is a power of two dividing 1024
+  const int per = (nblk + Q - 1) / Q;
+  const int b0 = min(q * per, nblk), b1 = min(b0 + per, nblk);
+  int part = 0;
   if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      const int v = block_counts[(size_t)b * E + e];
-      block_base[(size_t)b * E + e] = run;
-      run += v;
+#pragma unroll 8
+    for (int bb = b0; bb < b1; ++bb) part += block_counts[(size_t)bb * E + e];
+  }
+  qsum[tid] = part;
+  if (tid == 0) nact = 0;
+  __syncthreads();
+  // exclusive prefix of the runs of expert e, and its total
+  int before = 0, run = 0;
+  for (int j = 0; j < Q; ++j) {
+    const int v = qsum[e * Q + j];
+    if (j < q) before += v;
+    run += v;
+  }
+  if (e < E) {
+    int r = before;
+#pragma unroll 8
+    for (int bb = b0; bb < b1; ++bb) {
+      block_base[(size_t)bb * E + e] = r;
+      r += block_counts[(size_t)bb * E + e];
     }
+  }
+  // one thread per expert continues with the expert scan
+  const bool lead = q == 0 && e < E;
+  if (lead) {
     counts[e] = run;
     if (stats) stats[e] = run;
+    if (run > 0) atomicAdd(&nact, 1);
   }
-  if (e == 0) nact = 0;
-  sc[e] = run;
   __syncthreads();
-  if (run > 0) atomicAdd(&nact, 1);
+  const int ev = (q == 0 && e < E) ? run : 0;  // one contribution per expert, in expert order
+  // scan over experts in the order of e (thread tid = e * Q holds expert e)
+  sc[tid] = ev;
+  __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    const int v = e >= off ? sc[e - off] : 0;
+    const int v = tid >= off ? sc[tid - off] : 0;
     __syncthreads();
-    sc[e] += v;
+    sc[tid] += v;
     __syncthreads();
   }
-  const int first = sc[e] - run;
-  if (e < E) expert_off[e] = first;
-  if (e == 1023) {
+  const int first = sc[tid] - ev;
+  if (lead) expert_off[e] = first;
+  if (tid == 1023) {
     expert_off[E] = sc[1023];
     n_active[0] = nact;
     if (stats) {
@@ -146,37 +173,87 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __rest
   }
   if (blocks) {
     __syncthreads();
-    const int nb = (run + RB - 1) / RB;
+    const int nb = lead ? (run + RB - 1) / RB : 0;
     const int incl = block_inclusive_scan<1024>(nb, sc);
-    if (e == 1023) nblocks = incl;
+    if (tid == 1023) nblocks = incl;
     __syncthreads();
-    put_row_blocks(blocks, e, first, run, RB, incl - nb, bound);
-    close_row_blocks(blocks, nblocks, bound, e, 1024);
+    if (lead) put_row_blocks(blocks, e, first, run, RB, incl - nb, bound);
+    close_row_blocks(blocks, nblocks, bound, tid, 1024);
   }
 }
 
+// Scatter: SPLIT workgroups per 256-token block, each placing the assignments
+// of 256 / SPLIT of its tokens.  Every workgroup rebuilds the block's masks and
+// the per-word popcount prefixes, so a rank is two LDS reads.
+constexpr int SCATTER_SPLIT = 4;
+
 __global__ __launch_bounds__(PERM_BLOCK) void expert_scatter_kernel(
-    const int32_t* __restrict__ tok_off, const int32_t* __restrict__ ids, int T, int E,
+    const int32_t* __restrict__ tok_off, const int32_t* __restrict__ ids, int T, int E, int k_max,
     const int32_t* __restrict__ block_base, const int32_t* __restrict__ expert_off,
     int32_t* __restrict__ perm_tok, int32_t* __restrict__ perm_src, int32_t* __restrict__ inv_perm) {
   extern __shared__ uint32_t masks[];
-  build_masks(masks, tok_off, ids, T, E);
+  int32_t* const wpre = reinterpret_cast<int32_t*>(masks + E * MASK_WORDS);  // [E][MASK_WORDS]
+  const int blk = blockIdx.x / SCATTER_SPLIT, part = blockIdx.x - blk * SCATTER_SPLIT;
   const int tid = threadIdx.x;
-  const int t = blockIdx.x * PERM_BLOCK + tid;
-  if (t >= T) return;
-  const int a0 = tok_off[t], a1 = tok_off[t + 1];
-  const int wi = tid >> 5;
-  const uint32_t below = (1u << (tid & 31)) - 1u;
-  for (int a = a0; a < a1; ++a) {
+  // masks of the whole block
+  for (int i = tid; i < E * MASK_WORDS; i += PERM_BLOCK) masks[i] = 0u;
+  __syncthreads();
+  {
+    const int t = blk * PERM_BLOCK + tid;
+    if (t < T) {
+      const int a0 = tok_off[t], a1 = tok_off[t + 1];
+      const uint32_t bit = 1u << (tid & 31);
+      for (int a = a0; a < a1; ++a) {
+        const int e = ids[a];
+        if ((unsigned)e < (unsigned)E) atomicOr(&masks[e * MASK_WORDS + (tid >> 5)], bit);
+      }
+    }
+  }
+  __syncthreads();
+  // global base of (block, expert) plus the popcounts of the words before w
+  for (int e = tid; e < E; e += PERM_BLOCK) {
+    int r = expert_off[e] + block_base[(size_t)blk * E + e];
+#pragma unroll
+    for (int w = 0; w < MASK_WORDS; ++w) {
+      wpre[e * MASK_WORDS + w] = r;
+      r += __popc(masks[e * MASK_WORDS + w]);
+    }
+  }
+  __syncthreads();
+  // this workgroup's tokens: one thread per (token, assignment slot j < 64)
+  constexpr int TPW = PERM_BLOCK / SCATTER_SPLIT;  // tokens per workgroup
+  const int tl0 = part * TPW;
+  const int slots = min(k_max, 64);
+  for (int i = tid; i < TPW * slots; i += PERM_BLOCK) {
+    const int tl = tl0 + (i & (TPW - 1)), j = i / TPW;  // token within the block, its j-th assignment
+    const int t = blk * PERM_BLOCK + tl;
+    if (t >= T) continue;
+    const int a0 = tok_off[t], a1 = tok_off[t + 1];
+    if (a0 + j >= a1) continue;
+    const int a = a0 + j;
     const int e = ids[a];
     if ((unsigned)e >= (unsigned)E) continue;  // not produced by moe_route; ignored
-    const uint32_t* m = masks + e * MASK_WORDS;
-    int rank = __popc(m[wi] & below);
-    for (int w = 0; w < wi; ++w) rank += __popc(m[w]);
-    const int pos = expert_off[e] + block_base[(size_t)blockIdx.x * E + e] + rank;
+    const int wi = tl >> 5;
+    const int pos = wpre[e * MASK_WORDS + wi] + __popc(masks[e * MASK_WORDS + wi] & ((1u << (tl & 31)) - 1u));
     perm_tok[pos] = t;
     perm_src[pos] = a;
     inv_perm[a] = pos;
+  }
+  // assignment slots past 64 (k_t > 64): the remaining ones, thread per token
+  for (int tl = tl0 + tid; tl < tl0 + TPW; tl += PERM_BLOCK) {
+    const int t = blk * PERM_BLOCK + tl;
+    if (t >= T) continue;
+    const int a0 = tok_off[t], a1 = tok_off[t + 1];
+    const int wi = tl >> 5;
+    const uint32_t below = (1u << (tl & 31)) - 1u;
+    for (int a = a0 + 64; a < a1; ++a) {
+      const int e = ids[a];
+      if ((unsigned)e >= (unsigned)E) continue;
+      const int pos = wpre[e * MASK_WORDS + wi] + __popc(masks[e * MASK_WORDS + wi] & below);
+      perm_tok[pos] = t;
+      perm_src[pos] = a;
+      inv_perm[a] = pos;
+    }
   }
 }
 
@@ -266,7 +343,7 @@ __global__ __launch_bounds__(PERM_BLOCK) void permute_one_block_kernel(
   }
 }
 
-hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int E, int32_t* block_counts,
+hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int E, int k_max, int32_t* block_counts,
                           int32_t* block_base, int32_t* counts, int32_t* expert_off, int32_t* perm_tok,
                           int32_t* perm_src, int32_t* inv_perm, int32_t* n_active, int32_t* stats, int RB,
                           int bound, int4* blocks, hipStream_t st) {
@@ -284,12 +361,14 @@ hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, st, block_counts, nblk, E, block_base, counts,
+  int Q = 1;  // threads per expert in the scan: a power of two with Q * E <= 1024
+  while (Q * 2 * E <= 1024) Q *= 2;
+  hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, st, block_counts, nblk, E, Q, block_base, counts,
                      expert_off, n_active, stats, RB, bound, blocks);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nblk == 0) return err;
-  hipLaunchKernelGGL(expert_scatter_kernel, dim3(nblk), dim3(PERM_BLOCK), lds, st, tok_off, ids, T, E,
-                     block_base, expert_off, perm_tok, perm_src, inv_perm);
+  hipLaunchKernelGGL(expert_scatter_kernel, dim3(nblk * SCATTER_SPLIT), dim3(PERM_BLOCK), 2 * lds, st, tok_off, ids,
+                     T, E, k_max, block_base, expert_off, perm_tok, perm_src, inv_perm);
   return hipGetLastError();
 }
 

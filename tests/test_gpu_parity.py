@@ -63,6 +63,7 @@ def test_workload_parity(name):
     (33, 1024, 128, 128, 20, 0),   # largest E
     (1, 4, 128, 128, 4, 0),        # single token
     (129, 64, 384, 384, 64, 0),    # k_t up to E = 64
+    (300, 128, 128, 128, 100, 0),  # two permutation blocks with k_t > 64 assignments per token
 ])
 def test_shapes_and_ragged(dtype, T, E, d, I, kmax, Is):
     rng = np.random.default_rng(T + E)
