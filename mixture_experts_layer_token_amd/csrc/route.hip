@@ -125,9 +125,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ pa
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
+  // the partial sums do not depend on the budget: read them before it arrives
   const int base = tok_off[t];
   const int kt = tok_off[t + 1] - base;
-  if (kt == 0) return;
   uint32_t key[KPL];
 #pragma unroll
   for (int s = 0; s < KPL; ++s) {
@@ -151,6 +151,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ pa
       key[s] = logit_key((float)acc);
     }
   }
+  if (kt == 0) return;
   wave_topk_softmax<KPL>(key, kt, scale, ids + base, wts + base,
                          topk_scratch + (threadIdx.x >> 6) * scratch_slots);
 }

@@ -160,9 +160,9 @@ __global__ __launch_bounds__(256) void router_screen_select_kernel(
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;
+  // the slice partials do not depend on the budget: read them before it arrives
   const int base = tok_off[t];
   const int kt = tok_off[t + 1] - base;
-  if (kt == 0) return;
   // per-wave LDS: [red_words: lane shares of SEL_GRP candidates, later the
   // top-k scratch][E int32: candidate list][E doubles: exact sums by candidate]
   uint64_t* const area = sel_lds + (size_t)wv * lds_words;
@@ -208,6 +208,7 @@ __global__ __launch_bounds__(256) void router_screen_select_kernel(
       lkey[s] = logit_key(__double2float_rd(cen[s] - rad[s]));
     }
   }
+  if (kt == 0) return;
   const float L = key_logit(wave_kth_largest<KPL>(lkey, kt));
   const double cut = (double)L - (fabs((double)L) * 0x1p-21 + 0x1p-126);
 
