@@ -6,8 +6,8 @@
 // weight byte is read exactly once, with 16-byte loads, by one wave, while the
 // few rows routed to that expert ride along on the narrow side of a 16x16 MFMA.
 //
-// Work split.  The rows of each expert group are cut into blocks of 16*SMT
-// rows, listed in a row-block table built on the device (entries past the
+// Work split.  The rows of each expert group are cut into blocks of up to
+// 64 rows, listed in a row-block table built on the device (entries past the
 // real count are sentinels), so the grid -- column tiles x table bound --
 // depends only on the layer shape and carries no per-expert slack: a
 // workgroup takes one (row block, column tile) pair.  A workgroup is WN x WK
@@ -19,8 +19,13 @@
 // row per tile (lane l: row l%16, K offset (l/16)*KC).  The activation rows use
 // the same K indices on the other MFMA side, so the instruction sums exactly
 // the K values the lanes supplied (any consistent K order gives the dot
-// product).  Waves along K add their partial sums through LDS in a fixed
-// order (deterministic).
+// product).  A block of at most 32 rows is one row group: the WK waves split
+// K.  A block of 33..64 rows is two row groups of up to 32 rows, each with
+// WK/2 waves splitting K: the two groups read the same weight bytes at about
+// the same time, so one of the two requests is served by the CU's L1 instead
+// of the L2, which halves the L2-to-CU weight traffic of heavily used experts
+// (the L2-to-CU path, not HBM, limits those).  Waves along K add their partial
+// sums through LDS in a fixed order (deterministic).
 //
 // Memory pipeline: the weights of step i+1 are requested before the MFMAs of
 // step i, right after the activation rows of step i, so the in-order wait for
@@ -92,18 +97,20 @@ __device__ __forceinline__ void store4<float>(float* p, float a, float b, float 
 // flight.
 // SM: 16-row activation tiles per pass (the block's rows; a block of at most
 // 16 rows runs the SM = 1 body, which loads half the activation bytes).
-template <typename T, int MODE, int KC, int WN, int WK, int SM, int TPW, int PD, bool IL>
+// WKR: waves splitting K within this wave's row group; wk: this wave's index
+// among them; slot0: the group's first LDS reduction slot; SLOT: f32x4 per slot.
+template <typename T, int MODE, int KC, int WN, int WKR, int SM, int TPW, int PD, bool IL, int SLOT>
 __device__ __forceinline__ void stream_block(const T* __restrict__ in, const int32_t* __restrict__ row_map,
                                              const T* wa, const T* wb, int K, int kbeg, int lofs, int nsteps,
-                                             int mg, int rows, T* __restrict__ out, int N, int n0, f32x4_t* red) {
+                                             int mg, int rows, T* __restrict__ out, int N, int n0, f32x4_t* red,
+                                             int wn, int wk, int slot0) {
   constexpr int LE = 16 / sizeof(T);                     // elements per 16-byte load
   constexpr int LPS = KC / LE;                           // loads per tile row per K step
   constexpr int STEP = 4 * KC;                           // K elements per wave step
   constexpr int NS = PD + 1;                             // register stages
   constexpr int LSTR = IL ? 4 * LE : LE;                 // distance between a lane's loads
   constexpr int HALF = TPW / 2;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wn = wave % WN, wk = wave / WN;
+  const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
   const int tstride = 16 * K;                // elements between consecutive 16-row tiles
   // tile j's row pointer is wbase(j) + (j % half) * tstride
@@ -169,20 +176,22 @@ __device__ __forceinline__ void stream_block(const T* __restrict__ in, const int
     }
   }
 
-  if (WK > 1) {
+  if (WKR > 1) {
     if (wk > 0) {
+      f32x4_t* r = red + (size_t)((slot0 + wk - 1) * WN + wn) * SLOT;
 #pragma unroll
       for (int mt = 0; mt < SM; ++mt)
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) red[((((wk - 1) * WN + wn) * SM + mt) * TPW + j) * 64 + lane] = acc[mt][j];
+        for (int j = 0; j < TPW; ++j) r[(mt * TPW + j) * 64 + lane] = acc[mt][j];
     }
     __syncthreads();
     if (wk == 0) {
-      for (int q = 1; q < WK; ++q) {
+      for (int q = 1; q < WKR; ++q) {
+        const f32x4_t* r = red + (size_t)((slot0 + q - 1) * WN + wn) * SLOT;
 #pragma unroll
         for (int mt = 0; mt < SM; ++mt)
 #pragma unroll
-          for (int j = 0; j < TPW; ++j) acc[mt][j] += red[((((q - 1) * WN + wn) * SM + mt) * TPW + j) * 64 + lane];
+          for (int j = 0; j < TPW; ++j) acc[mt][j] += r[(mt * TPW + j) * 64 + lane];
       }
     }
   }
@@ -216,8 +225,8 @@ __device__ __forceinline__ void stream_block(const T* __restrict__ in, const int
 // XCDs round-robin by linear id, so when the tile count is a multiple of 8 all
 // row blocks of one column tile (an expert with many rows has several) run
 // on the same XCD and share its L2 copy of the weight tile.  Blocks hold up to
-// 16*SMT rows.  OCC: waves per SIMD the register allocation must allow (1: no
-// constraint).
+// 32*SMT rows (two row groups of 16*SMT).  OCC: waves per SIMD the register
+// allocation must allow (1: no constraint).
 template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL, int OCC>
 __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void ffn_stream_kernel(
     const T* __restrict__ in, const int32_t* __restrict__ row_map, const T* __restrict__ w0,
@@ -225,11 +234,14 @@ __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OC
     int tiles) {
   static_assert(MODE == 1 || TPW % 2 == 0, "gate/up tiles come in pairs");
   static_assert(KC % (16 / sizeof(T)) == 0, "K step must be whole 16-byte loads");
+  static_assert(WK % 2 == 0, "two row groups split the K waves in halves");
   constexpr int CPW = (MODE == 0) ? 8 * TPW : 16 * TPW;  // output columns per wave
   constexpr int NB = WN * CPW;                           // output columns per workgroup
   constexpr int LE = 16 / sizeof(T);
   constexpr int STEP = 4 * KC;                           // K elements per wave step
-  __shared__ f32x4_t red[(WK > 1) ? (WK - 1) * WN * SMT * TPW * 64 : 1];
+  constexpr int GR = 16 * SMT;                           // rows per row group
+  constexpr int SLOT = SMT * TPW * 64;                   // f32x4 per reduction slot
+  __shared__ f32x4_t red[(WK - 1) * WN * SLOT];
 
   const int blk = blockIdx.x / tiles, tile = blockIdx.x - blk * tiles;
   int g, mg, rows;  // group, first row of the block, rows in the block
@@ -241,28 +253,43 @@ __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OC
     if (g < 0) return;
   } else {
     g = 0;
-    mg = blk * 16 * SMT;
-    rows = min(16 * SMT, dense_rows - mg);
+    mg = blk * 2 * GR;
+    rows = min(2 * GR, dense_rows - mg);
     if (rows <= 0) return;
   }
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wn = wave % WN, wk = wave / WN;
-  const int lr = lane & 15, lg = lane >> 4;
+  const int lg = lane >> 4, lr = lane & 15;
   const int n0 = tile * NB + wn * CPW;
   const int lofs = IL ? lg * LE : lg * KC;   // lane's first element within a step
-  const int Kw = K / WK;
-  const int kbeg = wk * Kw;
-  const int nsteps = Kw / STEP;
   const size_t gstride = (size_t)N * K;
-  const T* wa = w0 + g * gstride + (size_t)(n0 + lr) * K + kbeg + lofs;
-  const T* wb = (MODE == 0 ? w1 : w0) + g * gstride + (size_t)(n0 + lr) * K + kbeg + lofs;
-  if (SMT > 1 && rows <= 16)
-    stream_block<T, MODE, KC, WN, WK, 1, TPW, PD, IL>(in, row_map, wa, wb, K, kbeg, lofs, nsteps, mg, rows, out, N,
-                                                      n0, red);
-  else
-    stream_block<T, MODE, KC, WN, WK, SMT, TPW, PD, IL>(in, row_map, wa, wb, K, kbeg, lofs, nsteps, mg, rows, out,
-                                                        N, n0, red);
+  const T* const wrow_a = w0 + g * gstride + (size_t)(n0 + lr) * K + lofs;
+  const T* const wrow_b = (MODE == 0 ? w1 : w0) + g * gstride + (size_t)(n0 + lr) * K + lofs;
+  if (rows <= GR) {
+    // one row group; the WK waves split K
+    const int Kw = K / WK, kbeg = wk * Kw, nsteps = Kw / STEP;
+    if (SMT > 1 && rows <= 16)
+      stream_block<T, MODE, KC, WN, WK, 1, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kbeg, wrow_b + kbeg, K, kbeg, lofs,
+                                                              nsteps, mg, rows, out, N, n0, red, wn, wk, 0);
+    else
+      stream_block<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kbeg, wrow_b + kbeg, K, kbeg,
+                                                                lofs, nsteps, mg, rows, out, N, n0, red, wn, wk, 0);
+  } else {
+    // two row groups; WK/2 waves split K within each
+    constexpr int WKR = WK / 2;
+    const int grp = wk / WKR, wkr = wk - grp * WKR;
+    const int Kw = K / WKR, kbeg = wkr * Kw, nsteps = Kw / STEP;
+    const int mgg = mg + grp * GR, rg = min(GR, rows - grp * GR);
+    if (SMT > 1 && rg <= 16)
+      stream_block<T, MODE, KC, WN, WKR, 1, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kbeg, wrow_b + kbeg, K, kbeg,
+                                                               lofs, nsteps, mgg, rg, out, N, n0, red, wn, wkr,
+                                                               grp * (WKR - 1));
+    else
+      stream_block<T, MODE, KC, WN, WKR, SMT, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kbeg, wrow_b + kbeg, K, kbeg,
+                                                                 lofs, nsteps, mgg, rg, out, N, n0, red, wn, wkr,
+                                                                 grp * (WKR - 1));
+  }
 }
 
 // Shape rules a launch must satisfy (checked by the callers): N % NB == 0,
@@ -283,15 +310,34 @@ hipError_t launch_stream_variant(const T* in, const int32_t* row_map, const T* w
   return hipGetLastError();
 }
 
-// Production shape of the streaming kernels (chosen by a sweep over tile
+// Production shape of the streaming kernels (chosen by sweeps over tile
 // shapes on the decode workloads): 16-element K chunks per lane (a 64-element
-// step per wave), four 16-row weight tiles per wave, 32 rows per block, one
-// step of software pipelining, and the four waves of a workgroup splitting K.
-// When K/4 is not a whole number of steps the workgroup is 2 x 2 waves.
-constexpr int S_SMT = 2, S_TPW = 4, S_PD = 1;
-constexpr int S_ROWS = 16 * S_SMT;   // rows per block
+// step per wave), four 16-row weight tiles per wave, 64 rows per block, and
+// the four waves of a workgroup splitting K.  When K/4 is not a whole number
+// of steps the workgroup is 2 x 2 waves.  Pipeline depth: one step ahead; two
+// in bf16 when every wave runs at least 16 steps (long K, e.g. the down
+// projection of a 14336-wide expert), where the deeper queue outweighs the
+// lower occupancy its registers cost (3 -> 2 waves per SIMD); with short K
+// the prologue dominates and the deeper pipeline loses.
+constexpr int S_SMT = 2, S_TPW = 4;
+constexpr int S_ROWS = 32 * S_SMT;   // rows per block (two row groups)
+constexpr int S_DEEP_STEPS = 16;     // steps per wave from which bf16 runs two steps ahead
 
 int stream_row_block() { return S_ROWS; }
+
+template <typename T, int MODE, int WN, int WK>
+static hipError_t stream_wk(const T* x, const int32_t* row_map, const T* w0, const T* w1, const int4* blocks,
+                            int nblk, int dense_rows, T* out, int N, int K, hipStream_t st) {
+  constexpr int KC = (sizeof(T) == 2) ? 16 : 8;
+  constexpr int STEP = 4 * KC;
+  if constexpr (sizeof(T) == 2) {
+    if (K / WK / STEP >= S_DEEP_STEPS)
+      return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, 2>(x, row_map, w0, w1, blocks, nblk, dense_rows,
+                                                                         out, N, K, st);
+  }
+  return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, 1>(x, row_map, w0, w1, blocks, nblk, dense_rows, out,
+                                                                     N, K, st);
+}
 
 template <typename T, int MODE>
 static hipError_t stream_t(const void* in, const int32_t* row_map, const void* w0, const void* w1, const int4* blocks,
@@ -301,10 +347,8 @@ static hipError_t stream_t(const void* in, const int32_t* row_map, const void* w
   const int nblk = blocks ? bound : (dense_rows + S_ROWS - 1) / S_ROWS;
   const T* x = (const T*)in;
   if (K % (4 * STEP) == 0)
-    return launch_stream_variant<T, MODE, KC, 1, 4, S_SMT, S_TPW, S_PD>(x, row_map, (const T*)w0, (const T*)w1, blocks,
-                                                                        nblk, dense_rows, (T*)out, N, K, st);
-  return launch_stream_variant<T, MODE, KC, 2, 2, S_SMT, S_TPW, S_PD>(x, row_map, (const T*)w0, (const T*)w1, blocks,
-                                                                      nblk, dense_rows, (T*)out, N, K, st);
+    return stream_wk<T, MODE, 1, 4>(x, row_map, (const T*)w0, (const T*)w1, blocks, nblk, dense_rows, (T*)out, N, K, st);
+  return stream_wk<T, MODE, 2, 2>(x, row_map, (const T*)w0, (const T*)w1, blocks, nblk, dense_rows, (T*)out, N, K, st);
 }
 
 hipError_t launch_ffn_gateup_stream(int dtype, const void* in, const int32_t* row_map, const void* wg,
