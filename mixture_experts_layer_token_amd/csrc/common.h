@@ -69,4 +69,33 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// ---- global->LDS DMA and explicit waits ----
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N> __device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+// vm_wait<n> for a wave-uniform n in [0, NMAX] (the count must be an immediate).
+template <int NMAX> __device__ __forceinline__ void vm_wait_dyn(int n) {
+  if constexpr (NMAX <= 0) {
+    vm_wait<0>();
+  } else {
+    if (n >= NMAX) vm_wait<NMAX>();
+    else vm_wait_dyn<NMAX - 1>(n);
+  }
+}
+__device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// LDS tiles of 128-byte rows: the eight 16-byte chunks of row r are
+// XOR-permuted by (r >> 1) & 7, which keeps both 16-row x 16-byte and
+// 32-row x 32-byte fragment reads free of bank conflicts.
+__device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 7; }
+// byte offset of 16-byte chunk c of tile row r
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ lds_swz(r)) * 16); }
+
 }  // namespace moe

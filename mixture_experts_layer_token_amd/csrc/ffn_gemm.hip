@@ -53,30 +53,6 @@ constexpr int GBM = 256;  // rows per row block of the tile table (a multiple of
 constexpr int BK = 64;    // K elements per stage: one 128-byte LDS row per tile row
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-template <int N> __device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
-}
-// vm_wait<n> for a wave-uniform n in [0, NMAX] (the count must be an immediate).
-template <int NMAX> __device__ __forceinline__ void vm_wait_dyn(int n) {
-  if constexpr (NMAX <= 0) {
-    vm_wait<0>();
-  } else {
-    if (n >= NMAX) vm_wait<NMAX>();
-    else vm_wait_dyn<NMAX - 1>(n);
-  }
-}
-__device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
-// byte offset of 16-byte chunk c of tile row r within a stage operand
-__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) * 16); }
-
 }  // namespace
 
 // MODE 0: gate/up pair + SwiGLU epilogue.  MODE 1: down projection.
@@ -160,7 +136,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
 #pragma unroll
   for (int j = 0; j < XI; ++j) {
     const int r = 8 * (j * NW + wave) + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
+    const int c = (lane & 7) ^ lds_swz(r);
     int m = m0 + r;
     xon[j] = m < rows;
     xany[j] = __builtin_amdgcn_ballot_w64(xon[j]) != 0;
@@ -173,7 +149,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
 #pragma unroll
   for (int j = 0; j < WI; ++j) {
     const int r = 8 * (j * NW + wave) + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
+    const int c = (lane & 7) ^ lds_swz(r);
     const bf16_t* wb = (MODE == 0 && r >= BNW) ? w1 : w0;
     const int wr = (MODE == 0 && r >= BNW) ? r - BNW : r;
     wsrc[j] = wb + g * gstride + (size_t)(n0 + wr) * K + c * 8;

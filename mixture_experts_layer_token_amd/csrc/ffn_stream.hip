@@ -221,6 +221,109 @@ __device__ __forceinline__ void stream_block(const T* __restrict__ in, const int
   }
 }
 
+// Shared-tile body for a block of 33..64 rows in a workgroup of four waves
+// along K (WN = 1).  Each K step of the workgroup -- the TPW = 4 weight tiles
+// (16 rows x 128 bytes each) and the block's 64 activation rows (128 bytes
+// each) -- is copied into LDS by global->LDS DMA loads of whole 128-byte
+// lines (wave w fetches weight tile w and activation rows 16w..16w+15), two
+// steps ahead in a ring of three stages.  Every wave then multiplies all four
+// weight tiles with its own 16 activation rows and runs over the whole K, so
+// there is no reduction.  The weights of such a block leave the L2 once, as
+// full lines, instead of once per 32-row half as 64-byte half lines.  With no
+// register loads in the loop, every wait is an explicit count.
+// `ring` holds 3 stages of 16 KB: [weights 64 x 128 B][activations 64 x 128 B].
+constexpr int SHARED_STAGES = 3, SHARED_STAGE_BYTES = 2 * 64 * 128;
+
+template <typename T, int MODE, int KC, int TPW>
+__device__ __forceinline__ void stream_block_shared(const T* __restrict__ in, const int32_t* __restrict__ row_map,
+                                                    const T* w0, const T* w1, int K, int mg, int rows,
+                                                    T* __restrict__ out, int N, int n0, char* ring) {
+  constexpr int LE = 16 / sizeof(T);
+  constexpr int LPS = KC / LE;
+  constexpr int STEP = 4 * KC;
+  constexpr int HALF = TPW / 2;
+  constexpr int NST = SHARED_STAGES;
+  constexpr int SB = SHARED_STAGE_BYTES, XOFS = SB / 2;
+  static_assert(STEP * sizeof(T) == 128 && LPS == 2, "a step is one 128-byte line per row");
+  static_assert(TPW == 4, "one weight tile and 16 activation rows per wave");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int nsteps = K / STEP;
+
+  // DMA instruction q of wave w fills LDS rows 16w + 8q .. +7 of the weight
+  // and the activation region (1 KB each); lane i writes chunk slot i % 8 of
+  // row R = 16w + 8q + i / 8 and so fetches K chunk (i % 8) ^ swz(R).
+  const T* tb = MODE == 0 ? (wave < HALF ? w0 : w1) + (size_t)(n0 + 16 * (wave % HALF)) * K
+                          : w0 + (size_t)(n0 + 16 * wave) * K;
+  const T* wsrc[2];
+  const T* xsrc[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 8 * q + (lane >> 3), R = 16 * wave + r;
+    const int c = (lane & 7) ^ lds_swz(R);
+    wsrc[q] = tb + (size_t)r * K + c * LE;
+    const int m = R < rows ? R : 0;  // a missing row repeats the block's first row (never stored)
+    const int src = row_map ? row_map[mg + m] : mg + m;
+    xsrc[q] = in + (size_t)src * K + c * LE;
+  }
+  auto issue = [&](int s) {
+    char* sb = ring + (s % NST) * SB + wave * 2048;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[q] + s * STEP), (lds_ptr_t)(sb + q * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(xsrc[q] + s * STEP), (lds_ptr_t)(sb + XOFS + q * 1024), 16, 0, 0);
+    }
+  };
+  f32x4_t acc[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Every step issues the same four loads (past the end, the last step again:
+  // in bounds, into a stage nobody reads any more), so the counts are constant.
+  issue(0);
+  issue(min(1, nsteps - 1));
+  for (int s = 0; s < nsteps; ++s) {
+    // step s landed for this wave (step s + 1's four loads may be in flight);
+    // after the barrier every wave's part has landed and every wave is done
+    // reading the stage that step s + 2 refills
+    vm_wait<4>();
+    lgkm_wait0();
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    issue(min(s + 2, nsteps - 1));
+    const char* sb = ring + (s % NST) * SB;
+    uint4 W[TPW][LPS], X[LPS];
+#pragma unroll
+    for (int i = 0; i < LPS; ++i) {
+      X[i] = *reinterpret_cast<const uint4*>(sb + XOFS + lds_off(16 * wave + lr, lg + 4 * i));
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) W[j][i] = *reinterpret_cast<const uint4*>(sb + lds_off(16 * j + lr, lg + 4 * i));
+    }
+#pragma unroll
+    for (int i = 0; i < LPS; ++i)
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) mma_tile<T>(acc[j], W[j][i], X[i]);
+  }
+  vm_wait<0>();  // no DMA into LDS may outlive the workgroup
+
+  const int m = 16 * wave + lr;
+  if (m < rows) {
+    T* orow = out + (size_t)(mg + m) * N + n0 + 4 * lg;
+    if (MODE == 0) {
+#pragma unroll
+      for (int j = 0; j < HALF; ++j) {
+        const f32x4_t gt = acc[j], up = acc[j + HALF];
+        store4<T>(orow + 16 * j, silu(gt[0]) * up[0], silu(gt[1]) * up[1], silu(gt[2]) * up[2],
+                  silu(gt[3]) * up[3]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) store4<T>(orow + 16 * j, acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+    }
+  }
+}
+
 // Linear workgroup id = block * tiles + tile.  Workgroups are dealt to the
 // XCDs round-robin by linear id, so when the tile count is a multiple of 8 all
 // row blocks of one column tile (an expert with many rows has several) run
@@ -241,7 +344,13 @@ __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OC
   constexpr int STEP = 4 * KC;                           // K elements per wave step
   constexpr int GR = 16 * SMT;                           // rows per row group
   constexpr int SLOT = SMT * TPW * 64;                   // f32x4 per reduction slot
-  __shared__ f32x4_t red[(WK - 1) * WN * SLOT];
+  // shared-tile mode for 33..64-row blocks (see stream_block_shared)
+  constexpr bool SHARED = WN == 1 && WK == 4 && TPW == 4 && IL && KC * sizeof(T) == 32;
+  constexpr int RED_BYTES = (WK - 1) * WN * SLOT * (int)sizeof(f32x4_t);
+  constexpr int LDS_BYTES = SHARED && SHARED_STAGES * SHARED_STAGE_BYTES > RED_BYTES
+                                ? SHARED_STAGES * SHARED_STAGE_BYTES : RED_BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+  f32x4_t* const red = reinterpret_cast<f32x4_t*>(smem);
 
   const int blk = blockIdx.x / tiles, tile = blockIdx.x - blk * tiles;
   int g, mg, rows;  // group, first row of the block, rows in the block
@@ -275,6 +384,9 @@ __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OC
     else
       stream_block<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kbeg, wrow_b + kbeg, K, kbeg,
                                                                 lofs, nsteps, mg, rows, out, N, n0, red, wn, wk, 0);
+  } else if constexpr (SHARED) {
+    stream_block_shared<T, MODE, KC, TPW>(in, row_map, w0 + g * gstride, (MODE == 0 ? w1 : w0) + g * gstride, K, mg,
+                                          rows, out, N, n0, smem);
   } else {
     // two row groups; WK/2 waves split K within each
     constexpr int WKR = WK / 2;
