@@ -20,12 +20,14 @@
 // the same K indices on the other MFMA side, so the instruction sums exactly
 // the K values the lanes supplied (any consistent K order gives the dot
 // product).  A block of at most 32 rows is one row group: the WK waves split
-// K.  A block of 33..64 rows is two row groups of up to 32 rows, each with
-// WK/2 waves splitting K: the two groups read the same weight bytes at about
-// the same time, so one of the two requests is served by the CU's L1 instead
-// of the L2, which halves the L2-to-CU weight traffic of heavily used experts
-// (the L2-to-CU path, not HBM, limits those).  Waves along K add their partial
-// sums through LDS in a fixed order (deterministic).
+// K and add their partial sums through LDS in a fixed order (deterministic).
+// A block of 33..64 rows (and, when K is short, every block) runs the
+// shared-tile body below: its weight tile passes through LDS once for all 64
+// rows.  This matters because the 16-row x 64-byte pattern of the direct
+// loads moves L2-resident data into a CU at well under half the rate of
+// whole-line loads, and heavily used experts are read from the L2 by many row
+// blocks.  (Workgroups of two waves along K per row group stand in where the
+// shared body does not apply.)
 //
 // Memory pipeline: the weights of step i+1 are requested before the MFMAs of
 // step i, right after the activation rows of step i, so the in-order wait for
@@ -255,38 +257,46 @@ __device__ __forceinline__ void stream_block_shared(const T* __restrict__ in, co
   // row R = 16w + 8q + i / 8 and so fetches K chunk (i % 8) ^ swz(R).
   const T* tb = MODE == 0 ? (wave < HALF ? w0 : w1) + (size_t)(n0 + 16 * (wave % HALF)) * K
                           : w0 + (size_t)(n0 + 16 * wave) * K;
+  // Activation rows past the block's end: an instruction whose eight rows
+  // are all missing is not issued (wave-uniform); within a partly filled one
+  // a missing row repeats the block's first row (its outputs are not stored).
   const T* wsrc[2];
   const T* xsrc[2];
+  bool xon[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int r = 8 * q + (lane >> 3), R = 16 * wave + r;
     const int c = (lane & 7) ^ lds_swz(R);
     wsrc[q] = tb + (size_t)r * K + c * LE;
-    const int m = R < rows ? R : 0;  // a missing row repeats the block's first row (never stored)
+    xon[q] = 16 * wave + 8 * q < rows;
+    const int m = R < rows ? R : 0;
     const int src = row_map ? row_map[mg + m] : mg + m;
     xsrc[q] = in + (size_t)src * K + c * LE;
   }
+  const int per_step = 2 + (xon[0] ? 1 : 0) + (xon[1] ? 1 : 0);  // loads this wave issues per step
   auto issue = [&](int s) {
     char* sb = ring + (s % NST) * SB + wave * 2048;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[q] + s * STEP), (lds_ptr_t)(sb + q * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(xsrc[q] + s * STEP), (lds_ptr_t)(sb + XOFS + q * 1024), 16, 0, 0);
+      if (xon[q])
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(xsrc[q] + s * STEP), (lds_ptr_t)(sb + XOFS + q * 1024), 16, 0,
+                                         0);
     }
   };
   f32x4_t acc[TPW];
 #pragma unroll
   for (int j = 0; j < TPW; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Every step issues the same four loads (past the end, the last step again:
-  // in bounds, into a stage nobody reads any more), so the counts are constant.
+  // Every step issues the same loads (past the end, the last step again: in
+  // bounds, into a stage nobody reads any more), so the counts are constant.
   issue(0);
   issue(min(1, nsteps - 1));
   for (int s = 0; s < nsteps; ++s) {
-    // step s landed for this wave (step s + 1's four loads may be in flight);
+    // step s landed for this wave (step s + 1's loads may be in flight);
     // after the barrier every wave's part has landed and every wave is done
     // reading the stage that step s + 2 refills
-    vm_wait<4>();
+    vm_wait_dyn<4>(per_step);
     lgkm_wait0();
     compiler_fence();
     __builtin_amdgcn_s_barrier();
@@ -375,7 +385,10 @@ __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OC
   const size_t gstride = (size_t)N * K;
   const T* const wrow_a = w0 + g * gstride + (size_t)(n0 + lr) * K + lofs;
   const T* const wrow_b = (MODE == 0 ? w1 : w0) + g * gstride + (size_t)(n0 + lr) * K + lofs;
-  if (rows <= GR) {
+  // With a short K (under four steps per wave when split WK ways) every
+  // block takes the shared-tile body, whose waves each run the whole K.
+  const int light_max = (!SHARED || K / WK / STEP >= 4) ? GR : 0;
+  if (rows <= light_max) {
     // one row group; the WK waves split K
     const int Kw = K / WK, kbeg = wk * Kw, nsteps = Kw / STEP;
     if (SMT > 1 && rows <= 16)
