@@ -69,6 +69,28 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// Inclusive prefix sum of one int per thread over a workgroup of NT threads
+// (a multiple of 64): a shuffle scan inside each wave, then the totals of the
+// lower waves.  `wsum` is NT / 64 ints of LDS; the trailing barrier lets the
+// caller reuse it at once.
+template <int NT>
+__device__ __forceinline__ int block_scan_incl(int v, int32_t* wsum) {
+  static_assert(NT % 64 == 0 && NT <= 1024, "whole waves");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  int add = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) add += i < w ? wsum[i] : 0;
+  __syncthreads();
+  return v + add;
+}
+
 // ---- global->LDS DMA and explicit waits ----
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;

@@ -32,21 +32,11 @@ __device__ __forceinline__ void close_row_blocks(int4* __restrict__ blocks, int 
   if (tid == 0) blocks[bound] = make_int4(count, 0, 0, 0);
 }
 
-// Inclusive scan of one value per thread over a workgroup of NT threads.
+// Inclusive scan of one value per thread over a workgroup of NT threads
+// (`sc` provides the NT / 64 wave totals).
 template <int NT>
 __device__ __forceinline__ int block_inclusive_scan(int v, int32_t* sc) {
-  const int tid = threadIdx.x;
-  sc[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const int u = tid >= off ? sc[tid - off] : 0;
-    __syncthreads();
-    sc[tid] += u;
-    __syncthreads();
-  }
-  const int r = sc[tid];
-  __syncthreads();
-  return r;
+  return block_scan_incl<NT>(v, sc);
 }
 
 __global__ __launch_bounds__(1024) void row_blocks_kernel(const int32_t* __restrict__ grp_off, int G, int RB,
@@ -153,22 +143,15 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __rest
   __syncthreads();
   const int ev = (q == 0 && e < E) ? run : 0;  // one contribution per expert, in expert order
   // scan over experts in the order of e (thread tid = e * Q holds expert e)
-  sc[tid] = ev;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? sc[tid - off] : 0;
-    __syncthreads();
-    sc[tid] += v;
-    __syncthreads();
-  }
-  const int first = sc[tid] - ev;
+  const int incl = block_scan_incl<1024>(ev, sc);
+  const int first = incl - ev;
   if (lead) expert_off[e] = first;
   if (tid == 1023) {
-    expert_off[E] = sc[1023];
+    expert_off[E] = incl;
     n_active[0] = nact;
     if (stats) {
       stats[E] = nact;
-      stats[E + 1] = sc[1023];
+      stats[E + 1] = incl;
     }
   }
   if (blocks) {
@@ -283,16 +266,10 @@ __global__ __launch_bounds__(PERM_BLOCK) void permute_one_block_kernel(
     act += c > 0;
   }
   if (tid == 0) nact = 0;
-  part[tid] = s;
   __syncthreads();
   if (act) atomicAdd(&nact, act);
-  for (int off = 1; off < PERM_BLOCK; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = part[tid] - s;
+  const int incl_s = block_scan_incl<PERM_BLOCK>(s, part);
+  int run = incl_s - s;
   for (int e = beg; e < end; ++e) {
     const int c = eoff[e];
     counts[e] = c;
@@ -302,12 +279,12 @@ __global__ __launch_bounds__(PERM_BLOCK) void permute_one_block_kernel(
     run += c;
   }
   if (tid == PERM_BLOCK - 1) {
-    eoff[E] = part[PERM_BLOCK - 1];
-    expert_off[E] = part[PERM_BLOCK - 1];
+    eoff[E] = incl_s;
+    expert_off[E] = incl_s;
     n_active[0] = nact;
     if (stats) {
       stats[E] = nact;
-      stats[E + 1] = part[PERM_BLOCK - 1];
+      stats[E + 1] = incl_s;
     }
   }
   __syncthreads();

@@ -21,7 +21,8 @@ namespace moe {
 // writes its float64 partial sums to part[s][t][e], and the top-k kernel adds
 // the slices in ascending order (any float64 summation order keeps the
 // routing contract: exact products, float64 accumulation, one rounding).
-// Workgroup (0, 0, 0) also computes the token offsets.
+// One more slice index (z = S) holds the token-offset scan in its first
+// workgroup, so the scan runs beside the tiles instead of before one of them.
 constexpr int RT = 64, RK = 32;
 
 // NR rows x RK elements of src (rows past nrows read as zero) into dst[k][row].
@@ -64,10 +65,13 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const T* __restrict
   __shared__ double ws[RK][RE + 1];
   __shared__ int32_t scan_part[257];
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
-    token_offsets_block<256>(k, T_, k_max, tok_off, status, scan_part, scan_part + 256);
+  const int S = gridDim.z - 1, chunks = d / RK;
+  if (blockIdx.z == S) {
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+      token_offsets_block<256>(k, T_, k_max, tok_off, status, scan_part, scan_part + 256);
+    return;
+  }
   const int t0 = blockIdx.x * RT, e0 = blockIdx.y * RE;
-  const int S = gridDim.z, chunks = d / RK;
   const int c_beg = (int)(((long long)blockIdx.z * chunks) / S);
   const int c_end = (int)(((long long)(blockIdx.z + 1) * chunks) / S);
   const int ty = tid / TX, tx = tid % TX;
@@ -128,27 +132,36 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ pa
   // the partial sums do not depend on the budget: read them before it arrives
   const int base = tok_off[t];
   const int kt = tok_off[t + 1] - base;
+  // G slices of every slot in flight at a time (G * KPL <= 32 loads); each
+  // slot's slices are added in ascending order
+  constexpr int G = 32 / KPL;
+  const size_t qstride = (size_t)T_ * E;
+  double acc[KPL];
+#pragma unroll
+  for (int s = 0; s < KPL; ++s) acc[s] = 0.0;
+  for (int q0 = 0; q0 < S; q0 += G) {
+    double v[KPL][G];
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) {
+      const int e = lane + 64 * s;
+      const double* pe = part + (size_t)t * E + (e < E ? e : 0);
+#pragma unroll
+      for (int i = 0; i < G; ++i) v[s][i] = (q0 + i < S) ? pe[(size_t)(q0 + i) * qstride] : 0.0;
+    }
+#pragma unroll
+    for (int s = 0; s < KPL; ++s)
+#pragma unroll
+      for (int i = 0; i < G; ++i) acc[s] += v[s][i];
+  }
   uint32_t key[KPL];
 #pragma unroll
   for (int s = 0; s < KPL; ++s) {
     const int e = lane + 64 * s;
     key[s] = 0;
     if (e < E) {
-      const double* pe = part + (size_t)t * E + e;
-      const size_t qstride = (size_t)T_ * E;
-      // G loads in flight at a time (all slices at once for one key per lane);
-      // each group is summed in order, groups in order
-      constexpr int G = KPL == 1 ? 32 : (KPL == 2 ? 16 : 8);
-      double acc = 0.0;
-      for (int q0 = 0; q0 < S; q0 += G) {
-        double v[G];
-#pragma unroll
-        for (int i = 0; i < G; ++i) v[i] = (q0 + i < S) ? pe[(size_t)(q0 + i) * qstride] : 0.0;
-#pragma unroll
-        for (int i = 0; i < G; ++i) acc += v[i];
-      }
-      if (bias) acc += (double)bias[e];
-      key[s] = logit_key((float)acc);
+      double l = acc[s];
+      if (bias) l += (double)bias[e];
+      key[s] = logit_key((float)l);
     }
   }
   if (kt == 0) return;
@@ -180,7 +193,7 @@ template <typename T>
 static void launch_router_t(const T* x, const T* w, const int32_t* k, int T_, int d, int E, int k_max, int S,
                             double* part, int32_t* tok_off, int32_t* status, hipStream_t st) {
   const int RE = router_tile_e(E);
-  dim3 grid(max(1, (T_ + RT - 1) / RT), (E + RE - 1) / RE, S);
+  dim3 grid(max(1, (T_ + RT - 1) / RT), (E + RE - 1) / RE, S + 1);  // slice S: the token scan
   if (RE == 8)
     hipLaunchKernelGGL((router_partial_kernel<T, 8>), grid, dim3(256), 0, st, x, w, T_, d, E, part, k, k_max, tok_off,
                        status);

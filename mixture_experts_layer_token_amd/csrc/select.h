@@ -26,7 +26,7 @@ namespace moe {
 
 // tok_off = exclusive prefix sum of the validated budgets, by one workgroup of
 // NT threads (each a contiguous run of tokens).  A k_t outside [0, k_max]
-// counts as 0 and raises MOE_DEV_BAD_K.  `part` holds NT ints, `bad_any` one.
+// counts as 0 and raises MOE_DEV_BAD_K.  `part` holds NT / 64 ints, `bad_any` one.
 template <int NT>
 __device__ void token_offsets_block(const int32_t* __restrict__ k, int T, int k_max, int32_t* __restrict__ tok_off,
                                     int32_t* __restrict__ status, int32_t* part, int32_t* bad_any) {
@@ -42,23 +42,17 @@ __device__ void token_offsets_block(const int32_t* __restrict__ k, int T, int k_
     s += ok ? v : 0;
   }
   if (tid == 0) *bad_any = 0;
-  part[tid] = s;
   __syncthreads();
   if (bad) atomicOr(bad_any, 1);
-  for (int off = 1; off < NT; off <<= 1) {
-    int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = part[tid] - s;
+  const int incl = block_scan_incl<NT>(s, part);  // its barriers also publish bad_any
+  int run = incl - s;
 #pragma unroll 8
   for (int i = beg; i < end; ++i) {
     tok_off[i] = run;
     const int v = k[i];
     run += (v >= 0 && v <= k_max) ? v : 0;
   }
-  if (tid == NT - 1) tok_off[T] = part[NT - 1];
+  if (tid == NT - 1) tok_off[T] = incl;
   if (tid == 0 && status) status[0] = *bad_any ? MOE_DEV_BAD_K_BIT : 0;
 }
 
