@@ -33,7 +33,6 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 (matrix and vector)
 DEFAULT_WORKLOAD = "mixtral_decode"
-PREFILL = {"subexpert_prefill", "dsv3_prefill"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -269,11 +268,16 @@ def main():
     alone_ms = k_start.elapsed_time(k_end) / n_in
     gu_bytes = 2 * n_act * I * d * esz + T * d * esz + A * I * esz   # weights + x rows + H
     gu_flops = 4.0 * d * I * A
-    if cfg.name in PREFILL:
-        peak = PEAK_BF16_TFLOPS if esz == 2 else PEAK_FP32_TFLOPS
+    # The bound is the roofline's: arithmetic intensity (algorithmic FLOPs per
+    # algorithmic byte) against the ridge point peak FLOP/s / peak HBM bytes/s.
+    peak_f = PEAK_BF16_TFLOPS if esz == 2 else PEAK_FP32_TFLOPS
+    intensity = gu_flops / gu_bytes
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    mfma_bound = intensity >= ridge
+    if mfma_bound:
         ach = gu_flops / (k_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4)}
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_f, "unit": "TFLOP/s",
+                "frac": round(ach / peak_f, 4)}
     else:
         ach = gu_bytes / (k_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -283,7 +287,9 @@ def main():
     roof["avg_launch_us"] = round(k_ms * 1e3, 2)
     roof["timing"] = "in the layer (separate calls, events around each launch)"
     roof["back_to_back_us"] = round(alone_ms * 1e3, 2)
-    roof["algorithmic_per_launch"] = gu_flops if cfg.name in PREFILL else gu_bytes
+    roof["algorithmic_per_launch"] = gu_flops if mfma_bound else gu_bytes
+    roof["intensity_flop_per_byte"] = round(intensity, 1)
+    roof["ridge_flop_per_byte"] = round(ridge, 1)
     roof["traffic"] = measured_traffic(cfg.name, routed_path)
 
     # ---- whole layer against its own roofline ----

@@ -42,6 +42,8 @@
 // takes one contiguous range of (row tile, N tile) pairs: the N tiles of a row
 // tile, then the next row tile of the same expert, which keeps an expert's
 // weights and gathered rows in that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -181,75 +183,98 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   // ---- fragments: lane l supplies tile row (l % 32) and K chunk 2s + l/32 of
   // k16 step s (A = weights, B = activations) ----
   const int l32 = lane & 31, lh = lane >> 5;
-  u32x4_t fw[2][NMAT * TNW], fx[2][TMW];
-  auto load_frags = [&](int buf, int s, int slot) {
-    const char* xs = lds + buf * SBYTES;
-    const char* ws = xs + XBYTES;
-#pragma unroll
-    for (int i = 0; i < TMW; ++i)
-      fx[slot][i] = *reinterpret_cast<const u32x4_t*>(xs + lds_off(wm * (BM / WM) + i * 32 + l32, 2 * s + lh));
-#pragma unroll
-    for (int q = 0; q < NMAT * TNW; ++q) {
-      const int mat = q / TNW, tj = q % TNW;
-      fw[slot][q] = *reinterpret_cast<const u32x4_t*>(
-          ws + lds_off(mat * BNW + wn * (BNW / WN) + tj * 32 + l32, 2 * s + lh));
-    }
-  };
-  auto mma = [&](int slot) {
-#pragma unroll
-    for (int q = 0; q < NMAT * TNW; ++q)
-#pragma unroll
-      for (int i = 0; i < TMW; ++i)
-        acc[q][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fw[slot][q]),
-                                                            __builtin_bit_cast(bf16x8_t, fx[slot][i]), acc[q][i], 0, 0, 0);
-  };
-  // one k16 step: the next step's fragment reads alternate with this step's MFMAs
-  constexpr int NFRAG = NMAT * TNW + TMW, NMMA = NMAT * TNW * TMW;
-  static_assert(NMMA >= NFRAG, "fewer MFMAs than fragment reads per step");
-  auto interleave = [&]() {
-#pragma unroll
-    for (int i = 0; i < NFRAG; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    }
-    if constexpr (NMMA > NFRAG) __builtin_amdgcn_sched_group_barrier(0x008, NMMA - NFRAG, 0);
-  };
-
   const int nk = K / BK;
+  // Row tiles of this wave that hold rows of the block (wave-uniform): the
+  // MFMAs and fragment reads of the empty 32-row tiles of a partly filled
+  // block are skipped (LIVE = 0: the wave only loads and synchronises).
+  const int wrows = rows - m0 - wm * (BM / WM);
+  const int live = wrows <= 0 ? 0 : min(TMW, (wrows + 31) / 32);
+
+  auto main_loop = [&](auto live_c) {
+    constexpr int LIVE = decltype(live_c)::value;
+    u32x4_t fw[2][NMAT * TNW], fx[2][TMW > 0 ? TMW : 1];
+    auto load_frags = [&](int buf, int s, int slot) {
+      if constexpr (LIVE > 0) {
+        const char* xs = lds + buf * SBYTES;
+        const char* ws = xs + XBYTES;
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s)
-    if (s < nk) issue(s, s);
-  // stage 0 landed: the stages issued after it may still be in flight
-  vm_wait_dyn<(STAGES - 1) * (XI + WI)>((min(nk, STAGES) - 1) * per_stage);
-  compiler_fence();
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
-  load_frags(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt % STAGES;
+        for (int i = 0; i < LIVE; ++i)
+          fx[slot][i] = *reinterpret_cast<const u32x4_t*>(xs + lds_off(wm * (BM / WM) + i * 32 + l32, 2 * s + lh));
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (s + 1 < KS) {
-        load_frags(buf, s + 1, (s + 1) & 1);
-      } else {
-        // Stage kt+1 landed (later stages may still be in flight) and this
-        // wave's reads of buffer kt are complete: after the barrier the buffer
-        // is refilled.  On the last stage nothing is waited for and the reads
-        // below touch a buffer whose values are never used, which keeps the
-        // step branch-free so its reads interleave with its MFMAs.
-        const int later = max(0, min(nk - 1, kt + STAGES - 1) - (kt + 1));
-        vm_wait_dyn<(STAGES - 2) * (XI + WI)>(later * per_stage);
-        lgkm_wait0();
-        compiler_fence();
-        __builtin_amdgcn_s_barrier();
-        compiler_fence();
-        if (kt + STAGES < nk) issue(kt + STAGES, buf);
-        load_frags((kt + 1) % STAGES, 0, 0);
+        for (int q = 0; q < NMAT * TNW; ++q) {
+          const int mat = q / TNW, tj = q % TNW;
+          fw[slot][q] = *reinterpret_cast<const u32x4_t*>(
+              ws + lds_off(mat * BNW + wn * (BNW / WN) + tj * 32 + l32, 2 * s + lh));
+        }
       }
-      mma(s & 1);
-      interleave();
+    };
+    auto mma = [&](int slot) {
+#pragma unroll
+      for (int q = 0; q < NMAT * TNW; ++q)
+#pragma unroll
+        for (int i = 0; i < LIVE; ++i)
+          acc[q][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fw[slot][q]),
+                                                              __builtin_bit_cast(bf16x8_t, fx[slot][i]), acc[q][i], 0,
+                                                              0, 0);
+    };
+    // one k16 step: the next step's fragment reads alternate with this step's MFMAs
+    constexpr int NFRAG = LIVE > 0 ? NMAT * TNW + LIVE : 0, NMMA = NMAT * TNW * LIVE;
+    constexpr int NPAIR = NFRAG < NMMA ? NFRAG : NMMA;
+    auto interleave = [&]() {
+#pragma unroll
+      for (int i = 0; i < NPAIR; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+      if constexpr (NMMA > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, NMMA - NPAIR, 0);
+      if constexpr (NFRAG > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NFRAG - NPAIR, 0);
+    };
+
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < nk) issue(s, s);
+    // stage 0 landed: the stages issued after it may still be in flight
+    vm_wait_dyn<(STAGES - 1) * (XI + WI)>((min(nk, STAGES) - 1) * per_stage);
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    load_frags(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt % STAGES;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) {
+          load_frags(buf, s + 1, (s + 1) & 1);
+        } else {
+          // Stage kt+1 landed (later stages may still be in flight) and this
+          // wave's reads of buffer kt are complete: after the barrier the buffer
+          // is refilled.  On the last stage nothing is waited for and the reads
+          // below touch a buffer whose values are never used, which keeps the
+          // step branch-free so its reads interleave with its MFMAs.
+          const int later = max(0, min(nk - 1, kt + STAGES - 1) - (kt + 1));
+          vm_wait_dyn<(STAGES - 2) * (XI + WI)>(later * per_stage);
+          lgkm_wait0();
+          compiler_fence();
+          __builtin_amdgcn_s_barrier();
+          compiler_fence();
+          if (kt + STAGES < nk) issue(kt + STAGES, buf);
+          load_frags((kt + 1) % STAGES, 0, 0);
+        }
+        mma(s & 1);
+        interleave();
+      }
     }
-  }
+  };
+  auto dispatch = [&](auto self, auto c) {
+    constexpr int L = decltype(c)::value;
+    if constexpr (L == 0) {
+      main_loop(c);
+    } else {
+      if (live >= L) main_loop(c);
+      else self(self, std::integral_constant<int, L - 1>{});
+    }
+  };
+  dispatch(dispatch, std::integral_constant<int, TMW>{});
 
   // ---- epilogue: element e of acc[q][i] is D[n = 8*(e/4) + 4*lh + e%4][m = l32]
   // of the 32x32 tile (n: weight row, m: tile row) ----
