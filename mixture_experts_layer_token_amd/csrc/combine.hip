@@ -16,8 +16,9 @@ __device__ __forceinline__ void unpack(const uint4& v, float (&f)[8]) {
 }
 
 // One workgroup per token; a thread owns 16-byte column chunks c, c+256, ...
-// The rows of CB assignments are requested together, then summed in
-// ascending j (the loads overlap, the arithmetic order does not change).
+// The rows of CB assignments are requested together, one batch ahead of the
+// batch being summed; the sum runs in ascending j (the loads overlap, the
+// arithmetic order does not change).
 constexpr int CB = 4;
 
 template <typename T>
@@ -30,6 +31,16 @@ template <>
 __device__ __forceinline__ void load_chunk<float>(const float* p, float (&f)[4]) {
   const float4 v = *reinterpret_cast<const float4*>(p);
   f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+}
+template <typename T>
+__device__ __forceinline__ void unpack_chunk(const uint4& v, float (&f)[16 / sizeof(T)]);
+template <>
+__device__ __forceinline__ void unpack_chunk<bf16_t>(const uint4& v, float (&f)[8]) {
+  unpack(v, f);
+}
+template <>
+__device__ __forceinline__ void unpack_chunk<float>(const uint4& v, float (&f)[4]) {
+  f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y); f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
 }
 template <typename T>
 __device__ __forceinline__ void store_chunk(T* p, const float* f);
@@ -54,28 +65,38 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
   constexpr int LE = 16 / sizeof(T);
   const int t = blockIdx.x;
   const int a0 = tok_off[t], a1 = tok_off[t + 1];
+  const int nb = (a1 - a0 + CB - 1) / CB;
   for (int c = threadIdx.x; c < d / LE; c += 256) {
     float acc[LE];
 #pragma unroll
     for (int i = 0; i < LE; ++i) acc[i] = 0.f;
-    int a = a0;
-    for (; a + CB <= a1; a += CB) {
-      float f[CB][LE];
-#pragma unroll
-      for (int j = 0; j < CB; ++j) load_chunk<T>(y + (size_t)inv_perm[a + j] * d + c * LE, f[j]);
+    uint4 rb[2][CB];
+    auto issue = [&](uint4 (&r)[CB], int b) {
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
-        const float w = wts[a + j];
-#pragma unroll
-        for (int i = 0; i < LE; ++i) acc[i] = fmaf(w, f[j][i], acc[i]);
+        const int a = a0 + b * CB + j;
+        r[j] = a < a1 ? *reinterpret_cast<const uint4*>(y + (size_t)inv_perm[a] * d + c * LE) : zero_u4();
       }
-    }
-    for (; a < a1; ++a) {
-      float f[LE];
-      load_chunk<T>(y + (size_t)inv_perm[a] * d + c * LE, f);
-      const float w = wts[a];
+    };
+    auto consume = [&](const uint4 (&r)[CB], int b) {
 #pragma unroll
-      for (int i = 0; i < LE; ++i) acc[i] = fmaf(w, f[i], acc[i]);
+      for (int j = 0; j < CB; ++j) {
+        const int a = a0 + b * CB + j;
+        if (a < a1) {
+          float f[LE];
+          unpack_chunk<T>(r[j], f);
+          const float w = wts[a];
+#pragma unroll
+          for (int i = 0; i < LE; ++i) acc[i] = fmaf(w, f[i], acc[i]);
+        }
+      }
+    };
+    if (nb > 0) issue(rb[0], 0);
+    for (int b = 0; b < nb; b += 2) {
+      if (b + 1 < nb) issue(rb[1], b + 1);
+      consume(rb[0], b);
+      if (b + 2 < nb) issue(rb[0], b + 2);
+      if (b + 1 < nb) consume(rb[1], b + 1);
     }
     if (ysh) {
       float f[LE];

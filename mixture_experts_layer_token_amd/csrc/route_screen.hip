@@ -150,7 +150,9 @@ __device__ __forceinline__ void dot8(const uint4& xv, const uint4& wv, double (&
 // elements [8l + 512 i, +8) of chunk i).
 constexpr int SEL_GRP = 8;  // candidates whose cross-lane sums are done together
 
-template <int KPL, int XC>
+// XR: the token row fits one pass (d <= 512 * XC) and is loaded once, before
+// the candidates, instead of once per candidate.
+template <int KPL, int XC, bool XR>
 __global__ __launch_bounds__(256) void router_screen_select_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const float* __restrict__ bias,
     const float* __restrict__ approx, const float* __restrict__ absum, int S, const int32_t* __restrict__ tok_off,
@@ -238,20 +240,28 @@ __global__ __launch_bounds__(256) void router_screen_select_kernel(
   constexpr int PASS = 512 * XC;
   const int npass = (d + PASS - 1) / PASS;
   const int items = ncand * npass;
+  uint4 xres[XR ? XC : 1];
+  if constexpr (XR) {
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int off = 512 * i + 8 * lane;
+      xres[i] = off < d ? *reinterpret_cast<const uint4*>(xrow + off) : zero_u4();
+    }
+  }
   auto load_item = [&](uint4 (&xv)[XC], uint4 (&wr)[XC], int it) {
     const int c = it / npass, p0 = (it - c * npass) * PASS;
     const bf16_t* row = w + (size_t)clist[c] * d;
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
       const int off = p0 + 512 * i + 8 * lane;
-      xv[i] = off < d ? *reinterpret_cast<const uint4*>(xrow + off) : zero_u4();
+      if constexpr (!XR) xv[i] = off < d ? *reinterpret_cast<const uint4*>(xrow + off) : zero_u4();
       wr[i] = off < d ? *reinterpret_cast<const uint4*>(row + off) : zero_u4();
     }
   };
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
   auto finish_item = [&](int it, const uint4 (&xv)[XC], const uint4 (&wr)[XC]) {
 #pragma unroll
-    for (int i = 0; i < XC; ++i) dot8(xv[i], wr[i], acc);
+    for (int i = 0; i < XC; ++i) dot8(XR ? xres[i] : xv[i], wr[i], acc);
     const int c = it / npass;
     if (it - c * npass == npass - 1) {  // candidate complete
       red[(c % SEL_GRP) * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
@@ -305,6 +315,18 @@ int router_screen_splits(int T, int d, int E) {
   return (int)max(1LL, S);
 }
 
+template <int KPL, int XC>
+static void launch_select(dim3 grid, size_t lds, hipStream_t st, const bf16_t* x, const bf16_t* w, const float* bias,
+                          const float* approx, const float* absum, int S, const int32_t* tok_off, int T, int d, int E,
+                          float scale, int32_t* ids, float* wts, int red_words, int words) {
+  if (d <= 512 * XC)
+    hipLaunchKernelGGL((router_screen_select_kernel<KPL, XC, true>), grid, dim3(256), lds, st, x, w, bias, approx,
+                       absum, S, tok_off, T, d, E, scale, ids, wts, red_words, words);
+  else
+    hipLaunchKernelGGL((router_screen_select_kernel<KPL, XC, false>), grid, dim3(256), lds, st, x, w, bias, approx,
+                       absum, S, tok_off, T, d, E, scale, ids, wts, red_words, words);
+}
+
 hipError_t launch_router_screen(const void* x, const void* w, const float* bias, const int32_t* k, int T, int d,
                                 int E, int k_max, int S, float scale, float* approx, float* absum, int32_t* tok_off,
                                 int32_t* status, int32_t* ids, float* wts, hipStream_t st) {
@@ -317,8 +339,8 @@ hipError_t launch_router_screen(const void* x, const void* w, const float* bias,
   const int words = red_words + (E + 1) / 2 + E;
   const size_t lds = (size_t)4 * words * sizeof(uint64_t);
 #define MOE_SEL(KPL, XC)                                                                                          \
-  hipLaunchKernelGGL((router_screen_select_kernel<KPL, XC>), grid, dim3(256), lds, st, (const bf16_t*)x,          \
-                     (const bf16_t*)w, bias, approx, absum, S, tok_off, T, d, E, scale, ids, wts, red_words, words)
+  launch_select<KPL, XC>(grid, lds, st, (const bf16_t*)x, (const bf16_t*)w, bias, approx, absum, S, tok_off, T, d, E, \
+                         scale, ids, wts, red_words, words)
   if (E <= 64) MOE_SEL(1, 4);
   else if (E <= 128) MOE_SEL(2, 4);
   else if (E <= 256) MOE_SEL(4, 4);
