@@ -49,6 +49,13 @@ def parse():
     ap.add_argument("--router", default="auto", choices=["auto", "float64", "screened"],
                     help="router algorithm (both give identical routing; they differ in cost)")
     ap.add_argument("--path", default="auto", choices=["auto", "stream", "gemm"], help="FFN path")
+    ap.add_argument("--k-dist", default="",
+                    help="eq7:MU,SIGMA draws the budgets k = clip(round(N(MU, SIGMA^2)), 1, k_max) "
+                         "instead of the workload's own law")
+    ap.add_argument("--k-policy", default="exact",
+                    help="budget each token executes: exact (its own k_t; the headline), batch_max "
+                         "(every token runs the batch maximum) or round_up:N (k_t rounded up to a "
+                         "multiple of N) -- the over-serving comparators")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens in the CPU-oracle sample (0 = workload default)")
@@ -146,12 +153,22 @@ def main():
     torch.cuda.set_device(dev)
     print(f"[bench] drawing {cfg.name}", file=sys.stderr, flush=True)
     layer = make_layer(cfg, dev)
+    if args.k_dist:
+        kind, _, params = args.k_dist.partition(":")
+        if kind != "eq7":
+            raise SystemExit(f"unknown --k-dist {args.k_dist!r}")
+        mu, sigma = (float(v) for v in params.split(","))
+        from workloads import draw_k_eq7
+        layer.k = draw_k_eq7(cfg.T, mu, sigma, cfg.k_max, cfg.seed).to(dev)
     torch.cuda.synchronize()
 
     T, d, E, I = cfg.T, cfg.d, cfg.E, cfg.I
     Is = cfg.I_shared
+    kpol, _, kgran = args.k_policy.partition(":")
+    kgran = int(kgran) if kgran else 1
+    kp = dict(k_policy=kpol, k_granule=kgran)
     desc = moe.make_desc(T, d, E, I, cfg.k_max, I_shared=Is, dtype=layer.x.dtype,
-                         routed_scale=cfg.routed_scale, path=args.path, router=args.router)
+                         routed_scale=cfg.routed_scale, path=args.path, router=args.router, **kp)
     ws = moe.alloc_workspace(desc, moe.MOE_OP_FORWARD, dev)
     out = torch.empty((T, d), dtype=layer.x.dtype, device=dev)
     stats = torch.empty(E + 2, dtype=torch.int32, device=dev)
@@ -213,7 +230,7 @@ def main():
     # gate/up launch, so the kernel sees the caches, clocks and power state it
     # has in the layer.  It is also timed back to back on its own. ----
     desc_r = moe.make_desc(T, d, E, I, cfg.k_max, dtype=layer.x.dtype, routed_scale=cfg.routed_scale,
-                           path=args.path, router=args.router)
+                           path=args.path, router=args.router, **kp)
     tok_off = torch.empty(T + 1, dtype=torch.int32, device=dev)
     ids = torch.empty(T * cfg.k_max, dtype=torch.int32, device=dev)
     wts = torch.empty(T * cfg.k_max, dtype=torch.float32, device=dev)
@@ -290,7 +307,8 @@ def main():
     roof["algorithmic_per_launch"] = gu_flops if mfma_bound else gu_bytes
     roof["intensity_flop_per_byte"] = round(intensity, 1)
     roof["ridge_flop_per_byte"] = round(ridge, 1)
-    roof["traffic"] = measured_traffic(cfg.name, routed_path)
+    roof["traffic"] = (measured_traffic(cfg.name, routed_path)
+                       if args.k_policy == "exact" and not args.k_dist else None)
 
     # ---- whole layer against its own roofline ----
     w_bytes = 3 * n_act * d * I * esz
@@ -305,13 +323,13 @@ def main():
                                          (PEAK_BF16_TFLOPS if esz == 2 else PEAK_FP32_TFLOPS), 4)}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.k_policy == "exact":
         n = args.cpu_sample or {"mixtral_decode": 64, "qwen3_30b_a3b_decode": 256, "tiny_fp32": 16,
                                 "subexpert_prefill": 64, "dsv3_decode": 16, "dsv3_prefill": 16}[cfg.name]
         print(f"[bench] timing the CPU oracle on {n} tokens", file=sys.stderr, flush=True)
         cpu = cpu_baseline(layer, n)
 
-    k_desc = "/".join(str(v) for v in cfg.k_values)
+    k_desc = args.k_dist if args.k_dist else "/".join(str(v) for v in cfg.k_values)
     rec = {
         "metric": METRIC,
         "value": round(T / layer_s, 1),
@@ -328,7 +346,7 @@ def main():
         "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "I": I, "I_shared": Is,
                    "k_values": k_desc, "k_max": cfg.k_max, "A": A, "n_active": n_act,
                    "execution": "eager" if args.eager else "hip_graph", "ffn_path": routed_path,
-                   "router": args.router,
+                   "router": args.router, "k_policy": args.k_policy, "k_dist": args.k_dist or "workload",
                    "wall_s": round(wall, 3)},
         "layer": layer_info,
         "roofline": roof,

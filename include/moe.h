@@ -82,6 +82,20 @@ typedef enum {
                                candidates; only candidates get the float64 sum */
 } moe_router;
 
+/* Budget each token executes, from its requested k_t (validated first: a
+ * k_t outside [0, k_max] is flagged and runs as 0 under every policy).
+ * EXACT runs k_t.  The other two are the over-serving comparators of
+ * MoE-Prism: BATCH_MAX runs the batch-level maximum budget for every token
+ * with a valid budget (§III-C1: a dispatch that mixes budgets uses the
+ * largest one so that every request gets at least its own); ROUND_UP runs
+ * N * ceil(k_t / N), N = k_granule (§V-D1: a whole-expert layout with N
+ * sub-experts per expert can only execute multiples of N). */
+typedef enum {
+  MOE_K_EXACT = 0,
+  MOE_K_BATCH_MAX = 1,
+  MOE_K_ROUND_UP = 2
+} moe_k_policy;
+
 /* Workspace owners, for moe_workspace_size. */
 typedef enum {
   MOE_OP_ROUTE = 0,
@@ -103,6 +117,8 @@ typedef enum {
  *   dtype: MOE_F32 or MOE_BF16; path: a moe_path value; router: a moe_router
  *   value (MOE_ROUTER_SCREENED needs bf16)
  *   routed_scale: finite (1.0 for the plain renormalised softmax)
+ *   k_policy: a moe_k_policy value; k_granule: N >= 1 for MOE_K_ROUND_UP,
+ *   with k_max a multiple of N (ignored by the other policies)
  */
 typedef struct moe_desc {
   int32_t T;            /* tokens in the batch */
@@ -115,6 +131,8 @@ typedef struct moe_desc {
   int32_t path;         /* moe_path */
   int32_t router;       /* moe_router */
   float routed_scale;   /* factor applied to the renormalised routing weights */
+  int32_t k_policy;     /* moe_k_policy: budget each token executes */
+  int32_t k_granule;    /* N of MOE_K_ROUND_UP */
 } moe_desc;
 
 /* Stream handle: a hipStream_t, or NULL for the null stream. */
@@ -146,7 +164,8 @@ moe_status moe_resolve_path(const moe_desc* desc, int32_t* routed_path, int32_t*
  *   w_router    ELT [E][d]
  *   router_bias float [E], or NULL for none (added to the logits before selection)
  *   k           int32 [T], per-token budgets
- *   tok_off     int32 [T+1] out: exclusive prefix sum of the validated k; tok_off[T] = A
+ *   tok_off     int32 [T+1] out: exclusive prefix sum of the executed budgets (the
+ *               validated k_t under desc->k_policy); tok_off[T] = A
  *   topk_ids    int32 [T*k_max] out: ids of token t at tok_off[t] .. tok_off[t+1]-1,
  *               best first
  *   topk_w      float [T*k_max] out: w_j = routed_scale * exp(l_j - l_0) / sum_j' exp(l_j' - l_0)

@@ -15,7 +15,8 @@ import torch
 from . import _lib
 from ._lib import (MOE_BF16, MOE_DEV_BAD_K, MOE_F32, MOE_OP_COMBINE, MOE_OP_FFN,  # noqa: F401
                    MOE_OP_FORWARD, MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_PATH_AUTO, MOE_PATH_GEMM,
-                   MOE_PATH_STREAM, MOE_ROUTER_AUTO, MOE_ROUTER_FLOAT64, MOE_ROUTER_SCREENED, moe_desc)
+                   MOE_PATH_STREAM, MOE_ROUTER_AUTO, MOE_ROUTER_FLOAT64, MOE_ROUTER_SCREENED, MOE_K_EXACT,
+                   MOE_K_BATCH_MAX, MOE_K_ROUND_UP, moe_desc)
 
 __all__ = [
     "MoeError", "make_desc", "workspace_size", "resolve_path", "alloc_workspace", "moe_route", "moe_permute",
@@ -26,6 +27,7 @@ __all__ = [
 _DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 _PATHS = {"auto": MOE_PATH_AUTO, "stream": MOE_PATH_STREAM, "gemm": MOE_PATH_GEMM}
 _ROUTERS = {"auto": MOE_ROUTER_AUTO, "float64": MOE_ROUTER_FLOAT64, "screened": MOE_ROUTER_SCREENED}
+_K_POLICIES = {"exact": MOE_K_EXACT, "batch_max": MOE_K_BATCH_MAX, "round_up": MOE_K_ROUND_UP}
 
 
 class MoeError(RuntimeError):
@@ -42,9 +44,12 @@ def library_path() -> str:
 
 def make_desc(T: int, d: int, E: int, I: int, k_max: int, *, I_shared: int = 0,
               dtype=torch.bfloat16, path: str = "auto", router: str = "auto",
-              routed_scale: float = 1.0) -> moe_desc:
+              routed_scale: float = 1.0, k_policy: str = "exact", k_granule: int = 1) -> moe_desc:
+    """Layer descriptor.  k_policy: "exact" (each token runs its own k_t),
+    "batch_max" (every valid token runs the batch's largest budget) or
+    "round_up" (k_t rounded up to a multiple of k_granule)."""
     return moe_desc(T, d, E, I, k_max, I_shared, _DTYPES[dtype], _PATHS[path], _ROUTERS[router],
-                    routed_scale)
+                    routed_scale, _K_POLICIES[k_policy], k_granule)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -142,14 +147,15 @@ def moe_forward(desc, x, w_router, router_bias, k, w_gate, w_up, w_down, ws_gate
 def forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: Optional[torch.Tensor],
             k: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
             shared: Optional[Sequence[torch.Tensor]] = None, *, k_max: int, routed_scale: float = 1.0,
-            path: str = "auto", router: str = "auto", ws: Optional[torch.Tensor] = None, stream=None):
+            path: str = "auto", router: str = "auto", k_policy: str = "exact", k_granule: int = 1,
+            ws: Optional[torch.Tensor] = None, stream=None):
     """Allocate the outputs (and a workspace unless given) and run moe_forward.
     Returns (out [T, d], stats int32 [E+2] = counts, n_active, A, dev_status int32 [1])."""
     T, d = x.shape
     E, I, _ = w_gate.shape
     Is = shared[0].shape[0] if shared is not None else 0
     desc = make_desc(T, d, E, I, k_max, I_shared=Is, dtype=x.dtype, path=path, router=router,
-                     routed_scale=routed_scale)
+                     routed_scale=routed_scale, k_policy=k_policy, k_granule=k_granule)
     if ws is None:
         ws = alloc_workspace(desc, MOE_OP_FORWARD, x.device)
     out = torch.empty((T, d), dtype=x.dtype, device=x.device)

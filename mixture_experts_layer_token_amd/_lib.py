@@ -13,6 +13,7 @@ c_size = ctypes.c_size_t
 MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_GEMM = 0, 1, 2
 MOE_ROUTER_AUTO, MOE_ROUTER_FLOAT64, MOE_ROUTER_SCREENED = 0, 1, 2
+MOE_K_EXACT, MOE_K_BATCH_MAX, MOE_K_ROUND_UP = 0, 1, 2
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_FORWARD = 0, 1, 2, 3, 4
 MOE_DEV_BAD_K = 1
 
@@ -23,7 +24,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
 class moe_desc(ctypes.Structure):
     _fields_ = [("T", c_i32), ("d", c_i32), ("E", c_i32), ("I", c_i32), ("k_max", c_i32),
                 ("I_shared", c_i32), ("dtype", c_i32), ("path", c_i32), ("router", c_i32),
-                ("routed_scale", ctypes.c_float)]
+                ("routed_scale", ctypes.c_float), ("k_policy", c_i32), ("k_granule", c_i32)]
 
 
 _P = ctypes.POINTER(moe_desc)

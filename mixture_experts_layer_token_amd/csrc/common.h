@@ -91,6 +91,23 @@ __device__ __forceinline__ int block_scan_incl(int v, int32_t* wsum) {
   return v + add;
 }
 
+// Maximum of one int per thread over a workgroup of NT threads (a multiple of
+// 64); `wsum` is NT / 64 ints of LDS; every thread gets the result.
+template <int NT>
+__device__ __forceinline__ int block_max(int v, int32_t* wsum) {
+  static_assert(NT % 64 == 0 && NT <= 1024, "whole waves");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  if (lane == 0) wsum[w] = v;
+  __syncthreads();
+  int m = wsum[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) m = max(m, wsum[i]);
+  __syncthreads();
+  return m;
+}
+
 // ---- global->LDS DMA and explicit waits ----
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;

@@ -10,17 +10,24 @@ namespace moe {
 enum { DT_F32 = 0, DT_BF16 = 1 };
 constexpr int32_t MOE_DEV_BAD_K_BIT = 1;
 
+// Budget each token executes (values of moe_k_policy): the validated k_t
+// (EXACT), the batch maximum of the validated budgets for every valid token
+// (BATCH_MAX), or k_t rounded up to a multiple of `granule` (ROUND_UP).
+enum { K_EXACT = 0, K_BATCH_MAX = 1, K_ROUND_UP = 2 };
+struct BudgetPolicy {
+  int policy;
+  int granule;
+};
+
 // route.hip
 // K slices of the router (float64 partial sums part[S][T][E]); depends on the shape only.
 int router_splits(int T, int d, int E);
 // Router partial logits; also writes tok_off and status (token-offset scan).
 hipError_t launch_router(int dtype, const void* x, const void* w, const int32_t* k, int T, int d, int E, int k_max,
-                         int S, double* part, int32_t* tok_off, int32_t* status, hipStream_t st);
+                         BudgetPolicy pol, int S, double* part, int32_t* tok_off, int32_t* status, hipStream_t st);
 // Sums the S slices in order, adds the bias, rounds to float32, selects top-k_t.
 hipError_t launch_topk(const double* part, int S, const float* bias, const int32_t* tok_off, int T, int E,
                        int k_max, float scale, int32_t* ids, float* wts, hipStream_t st);
-// Token offsets alone (one workgroup).
-hipError_t launch_tok_offsets(const int32_t* k, int T, int k_max, int32_t* tok_off, int32_t* status, hipStream_t st);
 
 // route_screen.hip -- bf16 only: MFMA logits with an error bound screen the
 // candidates; exact fp64 logits for candidates; same selection and weights.
@@ -28,8 +35,8 @@ hipError_t launch_tok_offsets(const int32_t* k, int T, int k_max, int32_t* tok_o
 int router_screen_splits(int T, int d, int E);
 // Token offsets (first workgroup), screening pass, then selection.
 hipError_t launch_router_screen(const void* x, const void* w, const float* bias, const int32_t* k, int T, int d,
-                                int E, int k_max, int S, float scale, float* approx, float* absum, int32_t* tok_off,
-                                int32_t* status, int32_t* ids, float* wts, hipStream_t st);
+                                int E, int k_max, BudgetPolicy pol, int S, float scale, float* approx, float* absum,
+                                int32_t* tok_off, int32_t* status, int32_t* ids, float* wts, hipStream_t st);
 
 // Row-block table of the grouped FFN kernels.  The rows of group g,
 // [grp_off[g], grp_off[g+1]), are cut into blocks of RB rows; entry i is

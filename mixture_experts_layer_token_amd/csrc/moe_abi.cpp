@@ -31,6 +31,8 @@ moe_status check_desc(const moe_desc* d) {
   if (d->I_shared < 0 || d->I_shared > 65536 || d->I_shared % kDimQuantum) return MOE_ERR_SHAPE;
   if ((int64_t)d->T * d->k_max >= (int64_t)1 << 31) return MOE_ERR_SHAPE;
   if (!std::isfinite(d->routed_scale)) return MOE_ERR_SHAPE;
+  if (d->k_policy < MOE_K_EXACT || d->k_policy > MOE_K_ROUND_UP) return MOE_ERR_UNSUPPORTED;
+  if (d->k_policy == MOE_K_ROUND_UP && (d->k_granule < 1 || d->k_max % d->k_granule)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -52,6 +54,9 @@ struct Carver {
 };
 
 size_t a_cap(const moe_desc& d) { return (size_t)d.T * d.k_max; }
+BudgetPolicy budget(const moe_desc& d) {
+  return BudgetPolicy{d.k_policy, d.k_policy == MOE_K_ROUND_UP ? d.k_granule : 1};
+}
 int n_blocks(const moe_desc& d) { return (d.T + PERM_BLOCK - 1) / PERM_BLOCK; }
 
 struct RouteWs { double* part; int splits; float* approx; float* absum; bool screened; };
@@ -186,9 +191,11 @@ bool fused_shared(const moe_desc& d) {
 moe_status do_route(const moe_desc& d, const void* x, const void* wr, const float* bias, const int32_t* k,
                     int32_t* tok_off, int32_t* ids, float* w, int32_t* status, const RouteWs& ws, hipStream_t st) {
   if (ws.screened)
-    return launched(launch_router_screen(x, wr, bias, k, d.T, d.d, d.E, d.k_max, ws.splits, d.routed_scale, ws.approx,
+    return launched(launch_router_screen(x, wr, bias, k, d.T, d.d, d.E, d.k_max, budget(d), ws.splits, d.routed_scale,
+                                         ws.approx,
                                          ws.absum, tok_off, status, ids, w, st));
-  hipError_t e = launch_router(d.dtype, x, wr, k, d.T, d.d, d.E, d.k_max, ws.splits, ws.part, tok_off, status, st);
+  hipError_t e =
+      launch_router(d.dtype, x, wr, k, d.T, d.d, d.E, d.k_max, budget(d), ws.splits, ws.part, tok_off, status, st);
   if (e == hipSuccess) e = launch_topk(ws.part, ws.splits, bias, tok_off, d.T, d.E, d.k_max, d.routed_scale, ids, w, st);
   return launched(e);
 }

@@ -58,7 +58,7 @@ template <typename T, int RE>
 __global__ __launch_bounds__(256) void router_partial_kernel(const T* __restrict__ x, const T* __restrict__ w,
                                                              int T_, int d, int E, double* __restrict__ part,
                                                              const int32_t* __restrict__ k, int k_max,
-                                                             int32_t* __restrict__ tok_off,
+                                                             BudgetPolicy pol, int32_t* __restrict__ tok_off,
                                                              int32_t* __restrict__ status) {
   constexpr int TX = RE < 16 ? RE : 16, EPT = RE / TX, TY = 256 / TX, TPT = RT / TY;
   __shared__ double xs[RK][RT + 1];
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const T* __restrict
   const int S = gridDim.z - 1, chunks = d / RK;
   if (blockIdx.z == S) {
     if (blockIdx.x == 0 && blockIdx.y == 0)
-      token_offsets_block<256>(k, T_, k_max, tok_off, status, scan_part, scan_part + 256);
+      token_offsets_block<256>(k, T_, k_max, pol, tok_off, status, scan_part, scan_part + 256);
     return;
   }
   const int t0 = blockIdx.x * RT, e0 = blockIdx.y * RE;
@@ -169,19 +169,6 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ pa
                          topk_scratch + (threadIdx.x >> 6) * scratch_slots);
 }
 
-// ---------------------------------------------------------------------------
-// Standalone token-offset scan (the screened router has no partial-logit pass).
-__global__ __launch_bounds__(1024) void tok_offsets_kernel(const int32_t* __restrict__ k, int T, int k_max,
-                                                           int32_t* __restrict__ tok_off, int32_t* __restrict__ status) {
-  __shared__ int32_t part[1025];
-  token_offsets_block<1024>(k, T, k_max, tok_off, status, part, part + 1024);
-}
-
-hipError_t launch_tok_offsets(const int32_t* k, int T, int k_max, int32_t* tok_off, int32_t* status, hipStream_t st) {
-  hipLaunchKernelGGL(tok_offsets_kernel, dim3(1), dim3(1024), 0, st, k, T, k_max, tok_off, status);
-  return hipGetLastError();
-}
-
 int router_splits(int T, int d, int E) {
   if (T == 0) return 1;
   const int tiles = ((T + RT - 1) / RT) * ((E + router_tile_e(E) - 1) / router_tile_e(E));
@@ -190,27 +177,28 @@ int router_splits(int T, int d, int E) {
 }
 
 template <typename T>
-static void launch_router_t(const T* x, const T* w, const int32_t* k, int T_, int d, int E, int k_max, int S,
-                            double* part, int32_t* tok_off, int32_t* status, hipStream_t st) {
+static void launch_router_t(const T* x, const T* w, const int32_t* k, int T_, int d, int E, int k_max,
+                            BudgetPolicy pol, int S, double* part, int32_t* tok_off, int32_t* status,
+                            hipStream_t st) {
   const int RE = router_tile_e(E);
   dim3 grid(max(1, (T_ + RT - 1) / RT), (E + RE - 1) / RE, S + 1);  // slice S: the token scan
   if (RE == 8)
-    hipLaunchKernelGGL((router_partial_kernel<T, 8>), grid, dim3(256), 0, st, x, w, T_, d, E, part, k, k_max, tok_off,
-                       status);
+    hipLaunchKernelGGL((router_partial_kernel<T, 8>), grid, dim3(256), 0, st, x, w, T_, d, E, part, k, k_max, pol,
+                       tok_off, status);
   else if (RE == 16)
-    hipLaunchKernelGGL((router_partial_kernel<T, 16>), grid, dim3(256), 0, st, x, w, T_, d, E, part, k, k_max,
+    hipLaunchKernelGGL((router_partial_kernel<T, 16>), grid, dim3(256), 0, st, x, w, T_, d, E, part, k, k_max, pol,
                        tok_off, status);
   else
-    hipLaunchKernelGGL((router_partial_kernel<T, 64>), grid, dim3(256), 0, st, x, w, T_, d, E, part, k, k_max,
+    hipLaunchKernelGGL((router_partial_kernel<T, 64>), grid, dim3(256), 0, st, x, w, T_, d, E, part, k, k_max, pol,
                        tok_off, status);
 }
 
 hipError_t launch_router(int dtype, const void* x, const void* w, const int32_t* k, int T, int d, int E, int k_max,
-                         int S, double* part, int32_t* tok_off, int32_t* status, hipStream_t st) {
+                         BudgetPolicy pol, int S, double* part, int32_t* tok_off, int32_t* status, hipStream_t st) {
   if (dtype == DT_BF16)
-    launch_router_t<bf16_t>((const bf16_t*)x, (const bf16_t*)w, k, T, d, E, k_max, S, part, tok_off, status, st);
+    launch_router_t<bf16_t>((const bf16_t*)x, (const bf16_t*)w, k, T, d, E, k_max, pol, S, part, tok_off, status, st);
   else
-    launch_router_t<float>((const float*)x, (const float*)w, k, T, d, E, k_max, S, part, tok_off, status, st);
+    launch_router_t<float>((const float*)x, (const float*)w, k, T, d, E, k_max, pol, S, part, tok_off, status, st);
   return hipGetLastError();
 }
 

@@ -39,11 +39,11 @@ namespace moe {
 // Workgroup (0, 0, 0) first writes the token offsets (pass 2 needs them).
 __global__ __launch_bounds__(256) void router_screen_mfma_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int T, int d, int E, float* __restrict__ approx,
-    float* __restrict__ absum, const int32_t* __restrict__ k, int k_max, int32_t* __restrict__ tok_off,
-    int32_t* __restrict__ status) {
+    float* __restrict__ absum, const int32_t* __restrict__ k, int k_max, BudgetPolicy pol,
+    int32_t* __restrict__ tok_off, int32_t* __restrict__ status) {
   if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
     __shared__ int32_t scan_part[257];
-    token_offsets_block<256>(k, T, k_max, tok_off, status, scan_part, scan_part + 256);
+    token_offsets_block<256>(k, T, k_max, pol, tok_off, status, scan_part, scan_part + 256);
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
@@ -328,10 +328,10 @@ static void launch_select(dim3 grid, size_t lds, hipStream_t st, const bf16_t* x
 }
 
 hipError_t launch_router_screen(const void* x, const void* w, const float* bias, const int32_t* k, int T, int d,
-                                int E, int k_max, int S, float scale, float* approx, float* absum, int32_t* tok_off,
-                                int32_t* status, int32_t* ids, float* wts, hipStream_t st) {
+                                int E, int k_max, BudgetPolicy pol, int S, float scale, float* approx, float* absum,
+                                int32_t* tok_off, int32_t* status, int32_t* ids, float* wts, hipStream_t st) {
   hipLaunchKernelGGL(router_screen_mfma_kernel, dim3(max(1, (T + 63) / 64), (E + 255) / 256, S), dim3(256), 0, st,
-                     (const bf16_t*)x, (const bf16_t*)w, T, d, E, approx, absum, k, k_max, tok_off, status);
+                     (const bf16_t*)x, (const bf16_t*)w, T, d, E, approx, absum, k, k_max, pol, tok_off, status);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || T == 0) return err;
   dim3 grid((T + 3) / 4);

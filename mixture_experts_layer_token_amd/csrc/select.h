@@ -24,23 +24,40 @@
 
 namespace moe {
 
-// tok_off = exclusive prefix sum of the validated budgets, by one workgroup of
+// tok_off = exclusive prefix sum of the executed budgets, by one workgroup of
 // NT threads (each a contiguous run of tokens).  A k_t outside [0, k_max]
-// counts as 0 and raises MOE_DEV_BAD_K.  `part` holds NT / 64 ints, `bad_any` one.
+// counts as 0 and raises MOE_DEV_BAD_K; the policy then maps each valid
+// budget to the one executed (BATCH_MAX: the largest valid budget of the
+// batch; ROUND_UP: the next multiple of the granule, at most k_max when k_max
+// is a multiple of it).  `part` holds NT / 64 ints, `bad_any` one.
+__device__ __forceinline__ int budget_valid(int v, int k_max) { return v >= 0 && v <= k_max; }
+__device__ __forceinline__ int budget_exec(int v, int k_max, BudgetPolicy pol, int kb) {
+  if (!budget_valid(v, k_max)) return 0;
+  if (pol.policy == K_BATCH_MAX) return kb;
+  if (pol.policy == K_ROUND_UP) return (v + pol.granule - 1) / pol.granule * pol.granule;
+  return v;
+}
+
 template <int NT>
-__device__ void token_offsets_block(const int32_t* __restrict__ k, int T, int k_max, int32_t* __restrict__ tok_off,
-                                    int32_t* __restrict__ status, int32_t* part, int32_t* bad_any) {
+__device__ void token_offsets_block(const int32_t* __restrict__ k, int T, int k_max, BudgetPolicy pol,
+                                    int32_t* __restrict__ tok_off, int32_t* __restrict__ status, int32_t* part,
+                                    int32_t* bad_any) {
   const int tid = threadIdx.x;
   const int per = (T + NT - 1) / NT;
   const int beg = min(tid * per, T), end = min(beg + per, T);
-  int s = 0, bad = 0;
+  int bad = 0, kmx = 0;
 #pragma unroll 8
   for (int i = beg; i < end; ++i) {
-    int v = k[i];
-    const bool ok = v >= 0 && v <= k_max;
+    const int v = k[i];
+    const bool ok = budget_valid(v, k_max);
     bad |= !ok;
-    s += ok ? v : 0;
+    kmx = max(kmx, ok ? v : 0);
   }
+  // batch maximum of the valid budgets (only BATCH_MAX uses it)
+  const int kb = pol.policy == K_BATCH_MAX ? block_max<NT>(kmx, part) : 0;
+  int s = 0;
+#pragma unroll 8
+  for (int i = beg; i < end; ++i) s += budget_exec(k[i], k_max, pol, kb);
   if (tid == 0) *bad_any = 0;
   __syncthreads();
   if (bad) atomicOr(bad_any, 1);
@@ -49,8 +66,7 @@ __device__ void token_offsets_block(const int32_t* __restrict__ k, int T, int k_
 #pragma unroll 8
   for (int i = beg; i < end; ++i) {
     tok_off[i] = run;
-    const int v = k[i];
-    run += (v >= 0 && v <= k_max) ? v : 0;
+    run += budget_exec(k[i], k_max, pol, kb);
   }
   if (tid == NT - 1) tok_off[T] = incl;
   if (tid == 0 && status) status[0] = *bad_any ? MOE_DEV_BAD_K_BIT : 0;

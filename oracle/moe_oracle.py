@@ -19,9 +19,12 @@ precision):
   gating paragraph: the router orders the selected experts by probability);
   equal float32 logits are ordered by the lower expert index.
 * Weights: softmax over the selected logits, i.e. the softmax over all E
-  renormalised to the selected set, times the routed scaling factor (§III-B2,
-  "normalized and scaled" router weights; the expanded linear gate keeps the
-  model's routing normalisation and an N-adjusted routed scaling).
+  renormalised to the selected set, times the routed scaling factor (§III-B2:
+  the router weights are normalised, then scaled; the expanded linear gate
+  keeps the model's routing normalisation and an N-adjusted routed scaling).
+* Executed budgets: a token runs its own k_t, or under the over-serving
+  comparators the batch's largest budget (§III-C1) or k_t rounded up to a
+  multiple of N (§V-D1).
 * Expert FFN: SwiGLU, §III-B1 Eq. (1): A = SiLU(X W_gate) * (X W_up) and
   X' = A W_down, with SiLU(z) = z * sigmoid(z).  Weights are stored in the
   [out, in] layout, so X W_gate of the page is x @ w_gate[e].T here.
@@ -45,6 +48,7 @@ from typing import Any, Optional, Sequence
 import numpy as np
 
 __all__ = [
+    "execution_budgets",
     "router_logits",
     "select_experts",
     "route",
@@ -79,6 +83,38 @@ def select_experts(logits_row: np.ndarray, k: int) -> np.ndarray:
     that order (equal logits keep ascending index order; -0.0 == +0.0)."""
     order = np.argsort(-np.asarray(logits_row, dtype=np.float32), kind="stable")
     return order[:k].astype(np.int64)
+
+
+def execution_budgets(k, k_max: int, policy: str = "exact", granule: int = 1):
+    """Budgets the layer executes, and the invalid-budget status.
+
+    A k_t outside [0, k_max] is invalid: it sets the status to 1 and the token
+    runs no routed expert under every policy.  For the valid ones:
+      exact      k_t itself (MoE-Prism §III-C1: the request's own budget);
+      batch_max  the largest valid budget of the whole batch, for every valid
+                 token (§III-C1: one dispatch mixing budgets runs the batch
+                 maximum, over-serving the smaller requests);
+      round_up   N * ceil(k_t / N) with N = granule (§V-D1: a layout of whole
+                 experts, each N sub-experts wide, executes only multiples of
+                 N); k_max must be a multiple of N.
+    Returns (int64 [T] executed budgets, status 0 or 1).
+    """
+    k = np.asarray(k, dtype=np.int64)
+    valid = (k >= 0) & (k <= k_max)
+    status = int((~valid).any())
+    kv = np.where(valid, k, 0)
+    if policy == "exact":
+        ke = kv
+    elif policy == "batch_max":
+        kb = int(kv.max()) if kv.size else 0
+        ke = np.where(valid, kb, 0)
+    elif policy == "round_up":
+        if granule < 1 or k_max % granule:
+            raise ValueError("round_up needs granule >= 1 dividing k_max")
+        ke = -(-kv // granule) * granule
+    else:
+        raise ValueError(f"unknown budget policy {policy!r}")
+    return ke.astype(np.int64), status
 
 
 def route(x, w_router, bias, k, k_max: int, routed_scale: float = 1.0,

@@ -12,22 +12,25 @@ from workloads import ExpertView, Layer, to_f64
 TOL = {"bf16": dict(rel_l2=1e-2, max_abs=5e-2), "f32": dict(rel_l2=1e-5, max_abs=None)}
 
 
-def desc_of(layer: Layer, path: str = "auto", router: str = "auto") -> moe.moe_desc:
+def desc_of(layer: Layer, path: str = "auto", router: str = "auto", k_policy: str = "exact",
+            k_granule: int = 1) -> moe.moe_desc:
     c = layer.cfg
     E, I, d = layer.w_gate.shape
     Is = layer.ws_gate.shape[0] if layer.ws_gate is not None else 0
     return moe.make_desc(layer.x.shape[0], d, E, I, c.k_max, I_shared=Is, dtype=layer.x.dtype,
-                         path=path, router=router, routed_scale=c.routed_scale)
+                         path=path, router=router, routed_scale=c.routed_scale, k_policy=k_policy,
+                         k_granule=k_granule)
 
 
 def shared_of(layer: Layer):
     return None if layer.ws_gate is None else (layer.ws_gate, layer.ws_up, layer.ws_down)
 
 
-def run_stages(layer: Layer, path: str = "auto", router: str = "auto") -> dict:
+def run_stages(layer: Layer, path: str = "auto", router: str = "auto", k_policy: str = "exact",
+               k_granule: int = 1) -> dict:
     """moe_route -> moe_permute -> moe_ffn -> moe_combine; returns host copies."""
     dev = layer.device
-    desc = desc_of(layer, path, router)
+    desc = desc_of(layer, path, router, k_policy, k_granule)
     T, d, E, km = desc.T, desc.d, desc.E, desc.k_max
     i32 = dict(dtype=torch.int32, device=dev)
     tok_off = torch.full((T + 1,), -7, **i32)
@@ -60,18 +63,22 @@ def run_stages(layer: Layer, path: str = "auto", router: str = "auto") -> dict:
                 out=out, A=A)
 
 
-def run_forward(layer: Layer, path: str = "auto", router: str = "auto"):
+def run_forward(layer: Layer, path: str = "auto", router: str = "auto", k_policy: str = "exact",
+                k_granule: int = 1):
     out, stats, status = moe.forward(layer.x, layer.w_router, layer.router_bias, layer.k, layer.w_gate,
                                      layer.w_up, layer.w_down, shared_of(layer), k_max=layer.cfg.k_max,
-                                     routed_scale=layer.cfg.routed_scale, path=path, router=router)
+                                     routed_scale=layer.cfg.routed_scale, path=path, router=router,
+                                     k_policy=k_policy, k_granule=k_granule)
     torch.cuda.synchronize()
     return out, stats.cpu().numpy().astype(np.int64), int(status.item())
 
 
-def oracle_routing(layer: Layer):
+def oracle_routing(layer: Layer, k_policy: str = "exact", k_granule: int = 1):
     c = layer.cfg
-    r = oracle.route(to_f64(layer.x), to_f64(layer.w_router), to_f64(layer.router_bias), to_f64(layer.k),
+    ke, status = oracle.execution_budgets(to_f64(layer.k), c.k_max, k_policy, k_granule)
+    r = oracle.route(to_f64(layer.x), to_f64(layer.w_router), to_f64(layer.router_bias), ke,
                      c.k_max, c.routed_scale, invalid="zero")
+    r["status"] = status
     p = oracle.permute(r["tok_off"], r["ids"], layer.w_gate.shape[0])
     return r, p
 
@@ -87,13 +94,14 @@ def check_routing(got: dict, r: dict, p: dict) -> None:
     assert got["n_active"] == p["n_active"]
 
 
-def oracle_out(layer: Layer, tokens) -> np.ndarray:
+def oracle_out(layer: Layer, tokens, k_policy: str = "exact", k_granule: int = 1) -> np.ndarray:
     c = layer.cfg
     sh = None
     if layer.ws_gate is not None:
         sh = (to_f64(layer.ws_gate), to_f64(layer.ws_up), to_f64(layer.ws_down))
+    ke, _ = oracle.execution_budgets(to_f64(layer.k), c.k_max, k_policy, k_granule)
     ref, _ = oracle.forward(to_f64(layer.x), to_f64(layer.w_router), to_f64(layer.router_bias),
-                            to_f64(layer.k), c.k_max, ExpertView(layer.w_gate), ExpertView(layer.w_up),
+                            ke, c.k_max, ExpertView(layer.w_gate), ExpertView(layer.w_up),
                             ExpertView(layer.w_down), shared=sh, routed_scale=c.routed_scale,
                             tokens=tokens, invalid="zero")
     return ref

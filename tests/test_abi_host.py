@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def _desc(**kw):
     base = dict(T=64, d=4096, E=8, I=14336, k_max=2, I_shared=0, dtype=moe.MOE_BF16, path=0,
-                router=0, routed_scale=1.0)
+                router=0, routed_scale=1.0, k_policy=0, k_granule=1)
     base.update(kw)
     return _lib.moe_desc(**base)
 
@@ -58,6 +58,8 @@ def test_workspace_sizes():
     (dict(d=100), 2), (dict(I=64), 2), (dict(E=0), 2), (dict(E=1025, k_max=1), 2),
     (dict(k_max=9), 2), (dict(k_max=0), 2), (dict(T=-1), 2), (dict(I_shared=100), 2),
     (dict(T=1 << 28, k_max=8), 2), (dict(dtype=7), 3), (dict(path=5), 3), (dict(router=3), 3),
+    (dict(k_policy=3), 3), (dict(k_policy=-1), 3), (dict(k_policy=2, k_granule=0), 2),
+    (dict(k_policy=2, k_granule=3), 2),
     (dict(router=2, dtype=0), 3),
     (dict(routed_scale=float("inf")), 2),
 ])

@@ -104,6 +104,34 @@ def test_invalid_k_flagged_and_dropped():
     assert not got["out"][1].any() and not got["out"][3].any()
 
 
+@pytest.mark.parametrize("T", [64, 300])
+@pytest.mark.parametrize("router", ["float64", "screened"])
+@pytest.mark.parametrize("policy,granule", [("batch_max", 1), ("round_up", 4), ("round_up", 2)])
+def test_budget_policies(policy, granule, router, T):
+    """Over-serving comparators (MoE-Prism §III-C1: a mixed dispatch runs the
+    batch maximum; §V-D1: whole experts of N sub-experts run N ceil(k/N)):
+    the same kernels run the transformed budgets.  Routing bit-exact against
+    the oracle on the transformed budgets, outputs to tolerance, invalid
+    budgets flagged and dropped, moe_forward equal to the staged calls."""
+    E, d, I, kmax = 64, 256, 256, 8
+    rng = np.random.default_rng(T + granule)
+    k = rng.integers(0, kmax + 1, size=T)
+    k[3], k[7] = kmax + 2, -1
+    layer = make_custom_layer(T=T, d=d, E=E, I=I, k=k, dtype="bf16", k_max=kmax, zipf=0.8, seed=9,
+                              device="cuda")
+    got = run_stages(layer, router=router, k_policy=policy, k_granule=granule)
+    r, p = oracle_routing(layer, policy, granule)
+    assert r["status"] == moe.MOE_DEV_BAD_K
+    check_routing(got, r, p)
+    tokens = sample_tokens(T, 40)
+    err = compare_out(got["out"], oracle_out(layer, tokens, policy, granule), "bf16", tokens)
+    assert not got["out"][3].any() and not got["out"][7].any()
+    fout, _, status = run_forward(layer, router=router, k_policy=policy, k_granule=granule)
+    assert status == moe.MOE_DEV_BAD_K
+    torch.testing.assert_close(fout, got["out"], rtol=0, atol=0)
+    _say(f"[budgets] {policy}/{granule} {router} T={T}: A={got['A']} {err}")
+
+
 @pytest.mark.parametrize("router", ["float64", "screened"])
 def test_exact_ties_break_to_lower_index(router):
     """Zero hidden states make every logit equal its bias; duplicated router

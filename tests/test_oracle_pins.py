@@ -328,3 +328,89 @@ def test_zero_input_ties_to_lowest_index():
 
 def test_activated_weight_bytes():
     assert oracle.activated_weight_bytes(8, 4096, 14336, 2) == 3 * 8 * 4096 * 14336 * 2
+
+
+# ---------------------------------------------------------------- executed budgets
+
+def _smallest_multiple_at_least(k: int, n: int) -> int:
+    m = 0
+    while m < k:
+        m += n
+    return m
+
+
+def test_execution_budgets_exact_is_identity_on_valid():
+    k = np.array([0, 1, 4, 8, 3])
+    ke, st = oracle.execution_budgets(k, 8)
+    assert ke.tolist() == k.tolist() and st == 0
+
+
+def test_execution_budgets_invalid_tokens_run_nothing():
+    k = np.array([2, -1, 9, 5])
+    for pol, g in (("exact", 1), ("batch_max", 1), ("round_up", 4)):
+        ke, st = oracle.execution_budgets(k, 8, pol, g)
+        assert st == 1 and ke[1] == 0 and ke[2] == 0, pol
+    # the batch maximum is taken over the valid budgets only (9 is invalid)
+    assert oracle.execution_budgets(k, 8, "batch_max")[0].tolist() == [5, 0, 0, 5]
+
+
+def test_execution_budgets_batch_max_brute_force():
+    """Every valid token runs the largest valid budget of the batch (MoE-Prism
+    §III-C1), checked token by token against a direct maximum."""
+    rng = np.random.default_rng(41)
+    for _ in range(50):
+        T = int(rng.integers(1, 40))
+        k = rng.integers(-2, 11, size=T)
+        ke, st = oracle.execution_budgets(k, 8, "batch_max")
+        valid = [int(v) for v in k if 0 <= v <= 8]
+        kb = max(valid) if valid else 0
+        for t in range(T):
+            assert ke[t] == (kb if 0 <= k[t] <= 8 else 0)
+        assert st == int(len(valid) < T)
+        assert all(ke[t] >= k[t] for t in range(T) if 0 <= k[t] <= 8)
+
+
+def test_execution_budgets_round_up_formula():
+    """k_exec = N ceil(k / N) (MoE-Prism §V-D1): with N = 4, 5 runs 8 and 4
+    runs 4; checked against the smallest multiple of N not below k."""
+    ke, _ = oracle.execution_budgets(np.array([0, 1, 4, 5, 7, 8, 12, 13, 32]), 32, "round_up", 4)
+    assert ke.tolist() == [0, 4, 4, 8, 8, 8, 12, 16, 32]
+    for n in (1, 2, 3, 4, 8):
+        k_max = 24
+        k = np.arange(0, k_max + 1)
+        ke, st = oracle.execution_budgets(k, k_max, "round_up", n)
+        assert st == 0
+        assert ke.tolist() == [_smallest_multiple_at_least(int(v), n) for v in k]
+        assert (ke % n == 0).all() and (ke <= k_max).all()
+    with pytest.raises(ValueError):
+        oracle.execution_budgets(np.array([1]), 6, "round_up", 4)   # 6 is not a multiple of 4
+
+
+def test_over_serving_adds_assignments_never_removes():
+    """Under both comparators a token's executed set contains its exact set
+    (the same logits, a longer prefix of the same order)."""
+    L = make_custom_layer(T=10, d=32, E=16, I=16, k=[1, 3, 2, 0, 5, 8, 4, 2, 7, 6], seed=44)
+    a = _arrays(L)
+    r0 = oracle.route(a["x"], a["w_router"], a["bias"], a["k"], 8)
+    for pol, g in (("batch_max", 1), ("round_up", 4)):
+        ke, _ = oracle.execution_budgets(a["k"], 8, pol, g)
+        r1 = oracle.route(a["x"], a["w_router"], a["bias"], ke, 8)
+        for t in range(10):
+            s0 = r0["ids"][r0["tok_off"][t]:r0["tok_off"][t + 1]].tolist()
+            s1 = r1["ids"][r1["tok_off"][t]:r1["tok_off"][t + 1]].tolist()
+            assert s1[:len(s0)] == s0
+
+
+def test_eq7_budget_generator():
+    """Eq. (7) of MoE-Prism §IV-B2: rounded normal draws clipped to [1, k_max];
+    seeded, so the same draw every time."""
+    from workloads import draw_k_eq7
+    k = draw_k_eq7(20000, 16.0, 8.0, 32, seed=3).numpy()
+    assert k.dtype == np.int32 and k.min() >= 1 and k.max() <= 32
+    np.testing.assert_array_equal(k, draw_k_eq7(20000, 16.0, 8.0, 32, seed=3).numpy())
+    # P(k = 1) = P(x < 1.5), P(k = 32) = P(x >= 31.5) for x ~ N(16, 64)
+    p_lo = 0.5 * (1 + math.erf((1.5 - 16) / (8 * math.sqrt(2))))
+    p_hi = 1 - 0.5 * (1 + math.erf((31.5 - 16) / (8 * math.sqrt(2))))
+    assert abs((k == 1).mean() - p_lo) < 0.01 and abs((k == 32).mean() - p_hi) < 0.01
+    inner = k[(k > 1) & (k < 32)]
+    assert abs(inner.mean() - 16.0) < 0.3

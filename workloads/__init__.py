@@ -59,6 +59,7 @@ __all__ = [
     "to_f64",
     "torch_dtype",
     "ExpertView",
+    "draw_k_eq7",
 ]
 
 
@@ -191,6 +192,16 @@ def draw_k(cfg: LayerConfig, T: Optional[int] = None) -> torch.Tensor:
     idx = torch.multinomial(probs, T, replacement=True, generator=g)
     vals = torch.tensor(cfg.k_values, dtype=torch.int32)
     return vals[idx]
+
+
+def draw_k_eq7(T: int, mu: float, sigma: float, k_max: int, seed: int) -> torch.Tensor:
+    """Budgets from a rounded, clipped normal law (MoE-Prism, arXiv 2510.19366,
+    §IV-B2, Eq. (7)): k = clip(round(x), 1, k_max), x ~ N(mu, sigma^2), i.i.d.
+    per token.  Rounding is half to even (numpy/torch round)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(derived_seed(seed, "k", 7))
+    x = mu + sigma * torch.randn(T, generator=g, dtype=torch.float64)
+    return torch.clamp(torch.round(x), 1, k_max).to(torch.int32)
 
 
 def zipf_bias(E: int, s: float) -> torch.Tensor:
