@@ -25,6 +25,9 @@ precision):
 * Executed budgets: a token runs its own k_t, or under the over-serving
   comparators the batch's largest budget (§III-C1) or k_t rounded up to a
   multiple of N (§V-D1).
+* Expert folding (ExFold summary, arXiv 2608.24938): token-level top-K and
+  batch-level expert-pool folding of the routes into kept targets with
+  scalar projectors S and projection losses L (fold_token, fold_pool).
 * Expert FFN: SwiGLU, §III-B1 Eq. (1): A = SiLU(X W_gate) * (X W_up) and
   X' = A W_down, with SiLU(z) = z * sigmoid(z).  Weights are stored in the
   [out, in] layout, so X W_gate of the page is x @ w_gate[e].T here.
@@ -49,6 +52,9 @@ import numpy as np
 
 __all__ = [
     "execution_budgets",
+    "fold_token",
+    "fold_pool",
+    "forward_routes",
     "router_logits",
     "select_experts",
     "route",
@@ -255,6 +261,138 @@ def forward(x, w_router, bias, k, k_max: int, w_gate, w_up, w_down,
     if shared is not None:
         out += swiglu_expert(xs, shared[0], shared[1], shared[2])
     return out, r
+
+
+# ---------------------------------------------------------------------------
+# Expert folding (ExFold summary, arXiv 2608.24938: Unified Expert Folding;
+# Phase-Specific Selection and Unified Folding; Phase-Specific Routing and
+# Folding).  Routes a token keeps are executed; each route it drops is folded
+# into a kept target: the target is the one with the smallest projection loss
+# L[source][target], and the dropped route's weight, times the scalar
+# projector S[source][target], is added to the target's weight.  Expert
+# parameters and the router are untouched; only routing metadata changes.
+# Decisions are taken on float32 values (scores are float32 products, losses
+# are compared as stored); weights are accumulated here in float64.
+
+def _routes(tok_off, ids, w):
+    tok_off = np.asarray(tok_off, dtype=np.int64)
+    return tok_off, np.asarray(ids, dtype=np.int64), np.asarray(w, dtype=np.float64)
+
+
+def _csr(rows):
+    """Per-token lists of (expert, weight) -> (tok_off, ids, w)."""
+    tok_off = np.zeros(len(rows) + 1, dtype=np.int64)
+    tok_off[1:] = np.cumsum([len(r) for r in rows])
+    ids = np.array([e for r in rows for e, _ in r], dtype=np.int64)
+    w = np.array([v for r in rows for _, v in r], dtype=np.float64)
+    return tok_off, ids, w
+
+
+def fold_token(tok_off, ids, w, S, L, H, K: int):
+    """Token-level top-K folding (prefill; ExFold: K_pre dominant experts per
+    token).  A token with more than K routes keeps the K with the largest
+    estimated contribution, router weight times the expert's calibrated output
+    magnitude H[e] (the ranking the ablations find best), ties to the earlier
+    route; each dropped route goes to the kept route of smallest
+    L[dropped][kept] (ties to the earlier kept route).  Kept routes stay in
+    their original order.  Returns (tok_off, ids, w) of the folded routes."""
+    tok_off, ids, w = _routes(tok_off, ids, w)
+    S = np.asarray(S, dtype=np.float32)
+    L = np.asarray(L, dtype=np.float32)
+    H = np.asarray(H, dtype=np.float32)
+    rows = []
+    for t in range(tok_off.shape[0] - 1):
+        a0, a1 = int(tok_off[t]), int(tok_off[t + 1])
+        e = [int(v) for v in ids[a0:a1]]
+        wt = [float(v) for v in w[a0:a1]]
+        n = a1 - a0
+        if n <= K:
+            rows.append(list(zip(e, wt)))
+            continue
+        score = [np.float32(np.float32(wt[j]) * H[e[j]]) for j in range(n)]
+        order = sorted(range(n), key=lambda j: (-score[j], j))
+        kept = sorted(order[:K])
+        neww = {i: wt[i] for i in kept}
+        for j in range(n):
+            if j in neww:
+                continue
+            tgt = min(kept, key=lambda i: (L[e[j], e[i]], i))
+            neww[tgt] += wt[j] * float(S[e[j], e[tgt]])
+        rows.append([(e[i], neww[i]) for i in kept])
+    return _csr(rows)
+
+
+def fold_pool(tok_off, ids, w, S, L, H, D: int, E: int):
+    """Batch-level expert-pool folding (decode; ExFold: D dominant experts per
+    batch, dynamic pool).  The pool is the D activated experts with the largest
+    aggregate routed contribution H[e] * sum of the weights routed to e (the
+    sum in float64 over tokens in order), ties to the lower index; every route
+    to an expert outside the pool goes to the pool expert of smallest
+    L[source][p] (ties to the lower index).  A token's routes that land on the
+    same expert are coalesced into one, at the place of the first of them, with
+    the weights added in route order (the target executes once).
+    Returns (tok_off, ids, w, pool bool [E])."""
+    tok_off, ids, w = _routes(tok_off, ids, w)
+    S = np.asarray(S, dtype=np.float32)
+    L = np.asarray(L, dtype=np.float32)
+    H = np.asarray(H, dtype=np.float32)
+    T = tok_off.shape[0] - 1
+    agg = np.zeros(E, dtype=np.float64)
+    count = np.zeros(E, dtype=np.int64)
+    for t in range(T):
+        for a in range(int(tok_off[t]), int(tok_off[t + 1])):
+            agg[ids[a]] += float(np.float32(w[a]))
+            count[ids[a]] += 1
+    score = agg * H.astype(np.float64)
+    active = [e for e in range(E) if count[e] > 0]
+    pool_list = sorted(active, key=lambda e: (-score[e], e))[:D]
+    pool = np.zeros(E, dtype=bool)
+    pool[pool_list] = True
+    members = sorted(pool_list)
+    rows = []
+    for t in range(T):
+        out = {}
+        order = []
+        for a in range(int(tok_off[t]), int(tok_off[t + 1])):
+            e = int(ids[a])
+            if pool[e]:
+                tgt, c = e, float(w[a])
+            else:
+                tgt = min(members, key=lambda p: (L[e, p], p))
+                c = float(w[a]) * float(S[e, tgt])
+            if tgt not in out:
+                out[tgt] = 0.0
+                order.append(tgt)
+            out[tgt] += c
+        rows.append([(p, out[p]) for p in order])
+    tok_off2, ids2, w2 = _csr(rows)
+    return tok_off2, ids2, w2, pool
+
+
+def forward_routes(x, tok_off, ids, w, w_gate, w_up, w_down, shared: Optional[Sequence[Any]] = None,
+                   tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Layer output for explicit routes (CSR tok_off / ids / w over the whole
+    batch), for the tokens listed in ``tokens`` (all by default): the weighted
+    sum of the routed experts' SwiGLU outputs plus the shared expert."""
+    x = np.asarray(x)
+    tok_off, ids, w = _routes(tok_off, ids, w)
+    if tokens is None:
+        tokens = np.arange(x.shape[0])
+    tokens = np.asarray(tokens, dtype=np.int64)
+    xs = _f64(x[tokens])
+    out = np.zeros((len(tokens), xs.shape[1]), dtype=np.float64)
+    by_expert = {}
+    for i, t in enumerate(tokens):
+        for a in range(int(tok_off[t]), int(tok_off[t + 1])):
+            by_expert.setdefault(int(ids[a]), []).append((i, float(w[a])))
+    for e, lst in by_expert.items():
+        rows = [i for i, _ in lst]
+        ye = swiglu_expert(xs[rows], w_gate[e], w_up[e], w_down[e])
+        for j, (i, wt) in enumerate(lst):
+            out[i] += wt * ye[j]
+    if shared is not None:
+        out += swiglu_expert(xs, shared[0], shared[1], shared[2])
+    return out
 
 
 def activated_weight_bytes(n_active: int, d: int, I: int, elem_bytes: int) -> int:

@@ -414,3 +414,89 @@ def test_eq7_budget_generator():
     assert abs((k == 1).mean() - p_lo) < 0.01 and abs((k == 32).mean() - p_hi) < 0.01
     inner = k[(k > 1) & (k < 32)]
     assert abs(inner.mean() - 16.0) < 0.3
+
+
+# ---------------------------------------------------------------- expert folding
+
+def _fold_golden():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "fold_hand_worked.json")) as f:
+        return json.load(f)
+
+
+def test_fold_token_hand_worked():
+    g = _fold_golden()
+    S, L = np.array(g["S"], np.float32), np.array(g["L"], np.float32)
+    tk = g["token"]
+    for c in tk["cases"]:
+        to, ids, w = oracle.fold_token(tk["tok_off"], tk["ids"], tk["w"], S, L, np.array(c["H"], np.float32), c["K"])
+        assert to.tolist() == c["tok_off"] and ids.tolist() == c["ids"], c["note"]
+        np.testing.assert_allclose(w, c["w"], rtol=1e-6, err_msg=c["note"])
+
+
+def test_fold_pool_hand_worked():
+    g = _fold_golden()
+    S, L = np.array(g["S"], np.float32), np.array(g["L"], np.float32)
+    pl = g["pool"]
+    for c in pl["cases"]:
+        to, ids, w, pool = oracle.fold_pool(pl["tok_off"], pl["ids"], pl["w"], S, L, np.array(pl["H"], np.float32),
+                                            c["D"], g["E"])
+        assert np.flatnonzero(pool).tolist() == c["pool"], c["note"]
+        assert to.tolist() == c["tok_off"] and ids.tolist() == c["ids"], c["note"]
+        np.testing.assert_allclose(w, c["w"], rtol=1e-6, err_msg=c["note"])
+
+
+def _random_routes(T, E, kmax, seed):
+    rng = np.random.default_rng(seed)
+    k = rng.integers(0, kmax + 1, size=T)
+    tok_off = np.concatenate([[0], np.cumsum(k)])
+    ids = np.concatenate([rng.permutation(E)[:kk] for kk in k]) if k.sum() else np.zeros(0, np.int64)
+    w = rng.random(int(k.sum())).astype(np.float32)
+    return tok_off, ids.astype(np.int64), w.astype(np.float64)
+
+
+def test_fold_invariants():
+    """Budgets respected, weights conserved when every projector is 1, kept
+    routes keep their order, pool routes stay inside the pool, no expert twice
+    in a token, and nothing changes when the budget covers everything."""
+    from workloads import make_fold_tables
+    E = 24
+    S, L, H = (t.numpy() for t in make_fold_tables(E, seed=5))
+    ones = np.ones((E, E), np.float32)
+    for seed in range(6):
+        tok_off, ids, w = _random_routes(40, E, 9, seed)
+        T = 40
+        k = np.diff(tok_off)
+        for K in (1, 3, 9):
+            to, i2, w2 = oracle.fold_token(tok_off, ids, w, S, L, H, K)
+            assert (np.diff(to) == np.minimum(k, K)).all()
+            for t in range(T):
+                src = ids[tok_off[t]:tok_off[t + 1]].tolist()
+                got = i2[to[t]:to[t + 1]].tolist()
+                assert all(e in src for e in got)
+                assert got == [e for e in src if e in got]          # original order kept
+            _, _, w1 = oracle.fold_token(tok_off, ids, w, ones, L, H, K)
+            for t in range(T):
+                assert np.isclose(w1[to[t]:to[t + 1]].sum(), w[tok_off[t]:tok_off[t + 1]].sum())
+        _, i_same, w_same = oracle.fold_token(tok_off, ids, w, S, L, H, 9)
+        assert (i_same == ids).all() and (w_same == w).all()
+        n_act = len(set(ids.tolist()))
+        for D in (1, 4, 10):
+            to, i2, w2, pool = oracle.fold_pool(tok_off, ids, w, S, L, H, D, E)
+            assert pool.sum() == min(D, n_act) and all(pool[e] for e in i2)
+            for t in range(T):
+                got = i2[to[t]:to[t + 1]].tolist()
+                assert len(got) == len(set(got)) and len(got) <= k[t]
+            _, _, w1, _ = oracle.fold_pool(tok_off, ids, w, ones, L, H, D, E)
+            for t in range(T):
+                assert np.isclose(w1[to[t]:to[t + 1]].sum(), w[tok_off[t]:tok_off[t + 1]].sum())
+        to, i_same, w_same, pool = oracle.fold_pool(tok_off, ids, w, S, L, H, n_act, E)
+        assert (to == tok_off).all() and (i_same == ids).all() and np.allclose(w_same, w)
+
+
+def test_forward_routes_matches_forward():
+    L = make_custom_layer(T=9, d=32, E=8, I=16, k=[1, 3, 2, 0, 5, 8, 4, 2, 7], I_shared=8, seed=21)
+    a = _arrays(L)
+    ref, r = _oracle_forward(a, 8)
+    got = oracle.forward_routes(a["x"], r["tok_off"], r["ids"], r["w"], a["w_gate"], a["w_up"], a["w_down"],
+                                shared=a["shared"])
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)

@@ -60,6 +60,7 @@ __all__ = [
     "torch_dtype",
     "ExpertView",
     "draw_k_eq7",
+    "make_fold_tables",
 ]
 
 
@@ -202,6 +203,22 @@ def draw_k_eq7(T: int, mu: float, sigma: float, k_max: int, seed: int) -> torch.
     g.manual_seed(derived_seed(seed, "k", 7))
     x = mu + sigma * torch.randn(T, generator=g, dtype=torch.float64)
     return torch.clamp(torch.round(x), 1, k_max).to(torch.int32)
+
+
+def make_fold_tables(E: int, seed: int = 0):
+    """Synthetic stand-ins for the calibrated folding tables of ExFold (the
+    calibrated ones need a model and data): scalar projectors S [E][E] drawn
+    from N(1, 0.25^2) and clipped to [-4, 4] with S[e][e] = 1, projection
+    losses L [E][E] uniform in [0, 1) with L[e][e] = 0, output magnitudes H [E]
+    uniform in [0.5, 2).  float32, CPU tensors."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(derived_seed(seed, "k", 11))
+    S = torch.clamp(1.0 + 0.25 * torch.randn(E, E, generator=g), -4.0, 4.0)
+    S.fill_diagonal_(1.0)
+    L = torch.rand(E, E, generator=g)
+    L.fill_diagonal_(0.0)
+    H = 0.5 + 1.5 * torch.rand(E, generator=g)
+    return S.float(), L.float(), H.float()
 
 
 def zipf_bias(E: int, s: float) -> torch.Tensor:
