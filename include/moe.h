@@ -102,8 +102,15 @@ typedef enum {
   MOE_OP_PERMUTE = 1,
   MOE_OP_FFN = 2,
   MOE_OP_COMBINE = 3,
-  MOE_OP_FORWARD = 4
+  MOE_OP_FORWARD = 4,
+  MOE_OP_FOLD = 5
 } moe_op;
+
+/* Expert-folding selectors, for moe_fold. */
+typedef enum {
+  MOE_FOLD_TOKEN = 0,  /* per token: keep at most `budget` routes (prefill) */
+  MOE_FOLD_POOL = 1    /* per batch: keep a pool of `budget` experts (decode) */
+} moe_fold_mode;
 
 /* Device status bits written by moe_route / moe_forward. */
 #define MOE_DEV_BAD_K 1  /* some k_t was outside [0, k_max]; it was run as k_t = 0 */
@@ -238,6 +245,42 @@ moe_status moe_ffn_gateup(const moe_desc* desc, const void* x, const void* w_gat
 moe_status moe_ffn_down(const moe_desc* desc, const void* h, const void* w_down,
                         const int32_t* expert_off, void* y_perm, void* ws, size_t ws_bytes,
                         moe_stream_t stream);
+
+/*
+ * Expert folding of the routing metadata (ExFold summary, arXiv 2608.24938:
+ * Unified Expert Folding; Phase-Specific Selection and Unified Folding;
+ * Phase-Specific Routing and Folding).  The routes of moe_route are cut to a
+ * budget, and every dropped route is folded into a kept one: its target is the
+ * kept expert of smallest projection loss L[source][target], and the dropped
+ * weight times the scalar projector S[source][target] is added to the
+ * target's weight.  Expert weights and the router are untouched; the folded
+ * routes feed moe_permute / moe_ffn / moe_combine like moe_route's.
+ *   mode = MOE_FOLD_TOKEN: a token with more than `budget` routes keeps the
+ *     `budget` largest by topk_w * H[e] (ties: earlier route), in their
+ *     original order; ties in L go to the earlier kept route.
+ *   mode = MOE_FOLD_POOL: the pool is the `budget` activated experts with the
+ *     largest H[e] * (sum of the weights routed to e, float64, in token
+ *     order), ties to the lower index; a route outside the pool goes to the
+ *     pool expert of smallest L (ties: lower index); a token's routes that
+ *     land on one expert are merged at the first one's place, weights added
+ *     in route order.  Needs expert_off / perm_src of moe_permute on the
+ *     input routes (the weights are summed in that row order).
+ *   S, L         float [E][E] (row: dropped source, column: target)
+ *   H            float [E], expert output magnitudes (>= 0)
+ *   tok_off, topk_ids, topk_w   input routes (moe_route's CSR)
+ *   expert_off, perm_src        MOE_FOLD_POOL only (else may be NULL)
+ *   tok_off_out  int32 [T+1] out; ids_out int32 [T*k_max] out; w_out float [T*k_max] out
+ *   pool_out     int32 [E] out (1: in the pool), or NULL; MOE_FOLD_POOL only
+ *   ws           scratch of moe_workspace_size(MOE_OP_FOLD) bytes
+ * A route whose expert id is outside [0, E) is dropped without a target.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (budget < 1, or k_max > 64),
+ * MOE_ERR_UNSUPPORTED (mode), MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH.
+ */
+moe_status moe_fold(const moe_desc* desc, int32_t mode, int32_t budget, const float* S, const float* L,
+                    const float* H, const int32_t* tok_off, const int32_t* topk_ids, const float* topk_w,
+                    const int32_t* expert_off, const int32_t* perm_src, int32_t* tok_off_out,
+                    int32_t* ids_out, float* w_out, int32_t* pool_out, void* ws, size_t ws_bytes,
+                    moe_stream_t stream);
 
 /*
  * Weighted combine back to token order:

@@ -16,11 +16,12 @@ from . import _lib
 from ._lib import (MOE_BF16, MOE_DEV_BAD_K, MOE_F32, MOE_OP_COMBINE, MOE_OP_FFN,  # noqa: F401
                    MOE_OP_FORWARD, MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_PATH_AUTO, MOE_PATH_GEMM,
                    MOE_PATH_STREAM, MOE_ROUTER_AUTO, MOE_ROUTER_FLOAT64, MOE_ROUTER_SCREENED, MOE_K_EXACT,
-                   MOE_K_BATCH_MAX, MOE_K_ROUND_UP, moe_desc)
+                   MOE_K_BATCH_MAX, MOE_K_ROUND_UP, MOE_OP_FOLD, MOE_FOLD_TOKEN, MOE_FOLD_POOL, moe_desc)
 
 __all__ = [
     "MoeError", "make_desc", "workspace_size", "resolve_path", "alloc_workspace", "moe_route", "moe_permute",
-    "moe_ffn", "moe_ffn_plan", "moe_ffn_gateup", "moe_ffn_down", "moe_combine", "moe_forward", "forward",
+    "moe_ffn", "moe_ffn_plan", "moe_ffn_gateup", "moe_ffn_down", "moe_combine", "moe_fold", "moe_forward",
+    "forward",
     "library_path",
 ]
 
@@ -128,6 +129,19 @@ def moe_ffn_down(desc, h, w_down, expert_off, y_perm, ws=None, stream=None) -> N
     _check("moe_ffn_down", _lib.load().moe_ffn_down(
         ctypes.byref(desc), _ptr(h), _ptr(w_down), _ptr(expert_off), _ptr(y_perm), _ptr(ws),
         _nbytes(ws), _stream(stream)))
+
+
+_FOLD_MODES = {"token": MOE_FOLD_TOKEN, "pool": MOE_FOLD_POOL}
+
+
+def moe_fold(desc, mode: str, budget: int, S, L, H, tok_off, topk_ids, topk_w, expert_off, perm_src,
+             tok_off_out, ids_out, w_out, pool_out, ws, stream=None) -> None:
+    """mode "token" (at most `budget` routes per token) or "pool" (a pool of
+    `budget` experts; expert_off / perm_src of moe_permute on the input routes)."""
+    _check("moe_fold", _lib.load().moe_fold(
+        ctypes.byref(desc), _FOLD_MODES[mode], budget, _ptr(S), _ptr(L), _ptr(H), _ptr(tok_off),
+        _ptr(topk_ids), _ptr(topk_w), _ptr(expert_off), _ptr(perm_src), _ptr(tok_off_out), _ptr(ids_out),
+        _ptr(w_out), _ptr(pool_out), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_combine(desc, y_perm, y_shared, tok_off, topk_w, inv_perm, out, stream=None) -> None:

@@ -14,7 +14,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_GEMM = 0, 1, 2
 MOE_ROUTER_AUTO, MOE_ROUTER_FLOAT64, MOE_ROUTER_SCREENED = 0, 1, 2
 MOE_K_EXACT, MOE_K_BATCH_MAX, MOE_K_ROUND_UP = 0, 1, 2
-MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_FORWARD = 0, 1, 2, 3, 4
+MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_FORWARD, MOE_OP_FOLD = 0, 1, 2, 3, 4, 5
+MOE_FOLD_TOKEN, MOE_FOLD_POOL = 0, 1
 MOE_DEV_BAD_K = 1
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
@@ -41,6 +42,8 @@ SIGNATURES = {
     "moe_ffn_gateup": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
     "moe_ffn_down": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
     "moe_combine": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr],
+    "moe_fold": [_P, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
+                 c_ptr, c_ptr, c_ptr, c_size, c_ptr],
     "moe_forward": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
                     c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
     "moe_status_str": [c_i32],

@@ -99,4 +99,22 @@ hipError_t launch_ffn_down_gemm(const void* h, const void* wd, const int4* block
 hipError_t launch_combine(int dtype, const void* y, const void* y_shared, const int32_t* tok_off,
                           const float* wts, const int32_t* inv_perm, void* out, int T, int d, hipStream_t st);
 
+// fold.hip -- expert folding of the routing metadata.  mode 0: keep at most
+// `budget` routes per token; mode 1: keep a pool of `budget` experts (needs
+// expert_off / perm_src of the input routes).  Scratch: ids / w [T * k_max]
+// (folded routes at the input offsets), cnt [T], pool / members [E],
+// n_members [1].  k_t <= 64.
+struct FoldScratch {
+  int32_t* ids;
+  float* w;
+  int32_t* cnt;
+  int32_t* pool;
+  int32_t* members;
+  int32_t* n_members;
+};
+hipError_t launch_fold(int mode, int budget, const float* S, const float* L, const float* H, const int32_t* tok_off,
+                       const int32_t* ids, const float* w, const int32_t* expert_off, const int32_t* perm_src, int T,
+                       int E, int32_t* tok_off_out, int32_t* ids_out, float* w_out, int32_t* pool_out,
+                       const FoldScratch& ws, hipStream_t st);
+
 }  // namespace moe

@@ -3,6 +3,7 @@
 // arithmetic runs in the HIP kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -127,6 +128,16 @@ void plan_forward(const moe_desc& d, Carver& c, FwdWs& w) {
   w.y_sh = d.I_shared ? c.take_bytes((size_t)d.T * d.d * elt_size(d)) : nullptr;
 }
 
+void plan_fold(const moe_desc& d, Carver& c, FoldScratch& w) {
+  const size_t A = a_cap(d);
+  w.ids = c.take<int32_t>(A);
+  w.w = c.take<float>(A);
+  w.cnt = c.take<int32_t>((size_t)d.T);
+  w.pool = c.take<int32_t>(d.E);
+  w.members = c.take<int32_t>(d.E);
+  w.n_members = c.take<int32_t>(1);
+}
+
 size_t ws_size(const moe_desc& d, int op) {
   Carver c(nullptr);
   switch (op) {
@@ -134,7 +145,15 @@ size_t ws_size(const moe_desc& d, int op) {
     case MOE_OP_PERMUTE: { PermWs w; plan_permute(d, c, w); break; }
     case MOE_OP_FFN: { FfnWs w; plan_ffn(d, c, w); break; }
     case MOE_OP_COMBINE: break;
-    default: { FwdWs w; plan_forward(d, c, w); break; }
+    case MOE_OP_FOLD: { FoldScratch w; plan_fold(d, c, w); break; }
+    default: {  // the forward's own regions; large enough for every other op
+      FwdWs w;
+      plan_forward(d, c, w);
+      Carver f(nullptr);
+      FoldScratch fw;
+      plan_fold(d, f, fw);
+      return std::max(c.total(), f.total());
+    }
   }
   return c.total();
 }
@@ -256,7 +275,7 @@ extern "C" {
 moe_status moe_workspace_size(const moe_desc* desc, int32_t op, size_t* bytes) {
   MOE_TRY(check_desc(desc));
   if (!bytes) return MOE_ERR_NULL;
-  if (op < MOE_OP_ROUTE || op > MOE_OP_FORWARD) return MOE_ERR_UNSUPPORTED;
+  if (op < MOE_OP_ROUTE || op > MOE_OP_FOLD) return MOE_ERR_UNSUPPORTED;
   *bytes = ws_size(*desc, op);
   return MOE_OK;
 }
@@ -385,6 +404,27 @@ moe_status moe_combine(const moe_desc* desc, const void* y_perm, const void* y_s
     return MOE_ERR_NULL;
   if (!aligned16(y_perm) || !aligned16(out) || (y_shared && !aligned16(y_shared))) return MOE_ERR_ALIGN;
   return do_combine(d, y_perm, y_shared, tok_off, topk_w, inv_perm, out, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_fold(const moe_desc* desc, int32_t mode, int32_t budget, const float* S, const float* L,
+                    const float* H, const int32_t* tok_off, const int32_t* topk_ids, const float* topk_w,
+                    const int32_t* expert_off, const int32_t* perm_src, int32_t* tok_off_out,
+                    int32_t* ids_out, float* w_out, int32_t* pool_out, void* ws, size_t ws_bytes,
+                    moe_stream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  if (mode != MOE_FOLD_TOKEN && mode != MOE_FOLD_POOL) return MOE_ERR_UNSUPPORTED;
+  if (budget < 1 || d.k_max > 64) return MOE_ERR_SHAPE;
+  if (!S || !L || !H || !tok_off || !tok_off_out || !tok_ptr(d, topk_ids) || !tok_ptr(d, topk_w) ||
+      !tok_ptr(d, ids_out) || !tok_ptr(d, w_out))
+    return MOE_ERR_NULL;
+  if (mode == MOE_FOLD_POOL && (!expert_off || !tok_ptr(d, perm_src))) return MOE_ERR_NULL;
+  MOE_TRY(check_ws(d, MOE_OP_FOLD, ws, ws_bytes));
+  Carver c(ws);
+  FoldScratch fw;
+  plan_fold(d, c, fw);
+  return launched(launch_fold(mode, budget, S, L, H, tok_off, topk_ids, topk_w, expert_off, perm_src, d.T, d.E,
+                              tok_off_out, ids_out, w_out, pool_out, fw, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router, const float* router_bias,

@@ -108,3 +108,21 @@ def test_resolve_path_rule():
     assert m.resolve_path(m.make_desc(8192, 256, 8, 128, 8, dtype=torch.float32)) == ("stream", "stream")
     with pytest.raises(m.MoeError):
         m.resolve_path(m.make_desc(64, 256, 8, 128, 2, dtype=torch.float32, path="gemm"))
+
+
+def test_fold_validates_before_launch():
+    lib = _lib.load()
+    d = _desc(T=4, d=128, E=4, I=128, k_max=2)
+    P = lambda v: ctypes.c_void_p(v)
+    x = P(1 << 20)  # never dereferenced: every call below fails validation first
+    args = lambda mode, budget, **kw: [ctypes.byref(kw.get("desc", d)), mode, budget] + \
+        [kw.get(n, x) for n in ("S", "L", "H", "tok_off", "ids", "w", "eoff", "psrc", "to", "io", "wo")] + \
+        [None, kw.get("ws", None), kw.get("ws_bytes", 0), None]
+    assert lib.moe_fold(*args(7, 2)) == 3                      # unknown mode
+    assert lib.moe_fold(*args(0, 0)) == 2                      # budget < 1
+    assert lib.moe_fold(*args(0, 2, desc=_desc(T=4, d=128, E=128, I=128, k_max=65))) == 2
+    assert lib.moe_fold(*args(0, 2, S=None)) == 1
+    assert lib.moe_fold(*args(1, 2, eoff=None)) == 1          # pool mode needs the permutation
+    assert lib.moe_fold(*args(0, 2)) == 4                      # workspace missing
+    st, n = _ws(d, moe.MOE_OP_FOLD)
+    assert st == 0 and n > 0 and n <= _ws(d, moe.MOE_OP_FORWARD)[1]

@@ -16,7 +16,9 @@ import torch
 import mixture_experts_layer_token_amd as moe
 from tests.gpu_util import (check_routing, compare_out, oracle_out, oracle_routing, run_forward,
                             run_stages, sample_tokens)
-from workloads import CONFIGS, make_custom_layer, make_layer
+import oracle
+from tests.gpu_util import desc_of
+from workloads import CONFIGS, ExpertView, make_custom_layer, make_layer, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -283,3 +285,136 @@ def test_split_ffn_calls_match_moe_ffn(name, path):
     A = got["A"]
     assert torch.equal(y[:A].view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32),
                        y_ref[:A].view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32))
+
+
+# ---------------------------------------------------------------- expert folding
+
+def _synthetic_routes(T, E, kmax, seed, dev):
+    """Seeded routes (distinct experts per token, float32 weights) as both
+    sides' input: the folding stage is tested on its own."""
+    rng = np.random.default_rng(seed)
+    k = rng.integers(0, kmax + 1, size=T)
+    k[0] = kmax
+    tok_off = np.concatenate([[0], np.cumsum(k)]).astype(np.int64)
+    ids = np.concatenate([rng.permutation(E)[:kk] for kk in k]).astype(np.int64)
+    w = rng.random(int(k.sum())).astype(np.float32)
+    w[5] = w[6] = w[7]   # equal weights: ties in the token ranking
+    i32 = lambda a: torch.as_tensor(a.astype(np.int32), device=dev)
+    return tok_off, ids, w, i32(tok_off), i32(ids), torch.as_tensor(w, device=dev)
+
+
+def _gpu_fold(desc, mode, budget, tables, to_d, ids_d, w_d, dev):
+    S, L, H = (t.to(dev) for t in tables)
+    T, E, km = desc.T, desc.E, desc.k_max
+    i32 = dict(dtype=torch.int32, device=dev)
+    eoff = psrc = None
+    if mode == "pool":
+        counts = torch.empty(E, **i32)
+        eoff = torch.empty(E + 1, **i32)
+        ptok = torch.empty(max(T * km, 1), **i32)
+        psrc = torch.empty_like(ptok)
+        inv = torch.empty_like(ptok)
+        nact = torch.empty(1, **i32)
+        moe.moe_permute(desc, to_d, ids_d, counts, eoff, ptok, psrc, inv, nact,
+                        moe.alloc_workspace(desc, moe.MOE_OP_PERMUTE, dev))
+    to_o = torch.full((T + 1,), -7, **i32)
+    ids_o = torch.full((max(T * km, 1),), -7, **i32)
+    w_o = torch.full((max(T * km, 1),), float("nan"), dtype=torch.float32, device=dev)
+    pool = torch.full((E,), -7, **i32)
+    moe.moe_fold(desc, mode, budget, S, L, H, to_d, ids_d, w_d, eoff, psrc, to_o, ids_o, w_o, pool,
+                 moe.alloc_workspace(desc, moe.MOE_OP_FOLD, dev))
+    torch.cuda.synchronize()
+    n = int(to_o[T].item())
+    return (to_o.cpu().numpy().astype(np.int64), ids_o[:n].cpu().numpy().astype(np.int64),
+            w_o[:n].cpu().double().numpy(), pool.cpu().numpy())
+
+
+@pytest.mark.parametrize("T,E,kmax,budget", [(300, 64, 16, 4), (64, 128, 8, 3), (8192, 256, 32, 8), (5, 8, 4, 1)])
+def test_fold_token_matches_oracle(T, E, kmax, budget):
+    """Token-level folding (ExFold, prefill): kept routes and targets
+    bit-exact, folded weights to float32 rounding of the additions."""
+    from workloads import make_fold_tables
+    dev = "cuda"
+    tok_off, ids, w, to_d, ids_d, w_d = _synthetic_routes(T, E, kmax, T + E, dev)
+    tables = make_fold_tables(E, seed=E)
+    desc = moe.make_desc(T, 128, E, 128, kmax)
+    got_to, got_ids, got_w, _ = _gpu_fold(desc, "token", budget, tables, to_d, ids_d, w_d, dev)
+    S, L, H = (t.numpy() for t in tables)
+    ref_to, ref_ids, ref_w = oracle.fold_token(tok_off, ids, w.astype(np.float64), S, L, H, budget)
+    np.testing.assert_array_equal(got_to, ref_to)
+    np.testing.assert_array_equal(got_ids, ref_ids)
+    np.testing.assert_allclose(got_w, ref_w, rtol=1e-5, atol=1e-6)
+    _say(f"[fold token] T={T} E={E} K={budget}: routes {tok_off[-1]} -> {ref_to[-1]}")
+
+
+@pytest.mark.parametrize("T,E,kmax,budget", [(256, 128, 8, 32), (300, 64, 16, 8), (64, 8, 2, 4), (40, 32, 6, 1)])
+def test_fold_pool_matches_oracle(T, E, kmax, budget):
+    """Expert-pool folding (ExFold, decode): pool, targets and merged routes
+    bit-exact, weights to float32 rounding."""
+    from workloads import make_fold_tables
+    dev = "cuda"
+    tok_off, ids, w, to_d, ids_d, w_d = _synthetic_routes(T, E, kmax, 3 * T + E, dev)
+    tables = make_fold_tables(E, seed=E + 1)
+    desc = moe.make_desc(T, 128, E, 128, kmax)
+    got_to, got_ids, got_w, got_pool = _gpu_fold(desc, "pool", budget, tables, to_d, ids_d, w_d, dev)
+    S, L, H = (t.numpy() for t in tables)
+    ref_to, ref_ids, ref_w, ref_pool = oracle.fold_pool(tok_off, ids, w.astype(np.float64), S, L, H, budget, E)
+    np.testing.assert_array_equal(got_pool, ref_pool.astype(np.int64))
+    np.testing.assert_array_equal(got_to, ref_to)
+    np.testing.assert_array_equal(got_ids, ref_ids)
+    np.testing.assert_allclose(got_w, ref_w, rtol=1e-5, atol=1e-6)
+    _say(f"[fold pool] T={T} E={E} D={budget}: experts {len(set(ids.tolist()))} -> {int(ref_pool.sum())}")
+
+
+@pytest.mark.parametrize("name,mode,budget", [("qwen3_30b_a3b_decode", "pool", 32), ("subexpert_prefill", "token", 8)])
+def test_folded_layer_matches_oracle(name, mode, budget):
+    """Route -> fold -> permute -> FFN -> combine on a workload against the
+    oracle's route -> fold -> explicit-route forward (sampled tokens)."""
+    from workloads import make_fold_tables
+    cfg = CONFIGS[name]
+    layer = make_layer(cfg, "cuda")
+    dev = layer.device
+    desc = desc_of(layer)
+    T, d, E, km = desc.T, desc.d, desc.E, desc.k_max
+    i32 = dict(dtype=torch.int32, device=dev)
+    tok_off = torch.empty(T + 1, **i32)
+    ids = torch.empty(T * km, **i32)
+    w = torch.empty(T * km, dtype=torch.float32, device=dev)
+    status = torch.empty(1, **i32)
+    moe.moe_route(desc, layer.x, layer.w_router, layer.router_bias, layer.k, tok_off, ids, w, status,
+                  moe.alloc_workspace(desc, moe.MOE_OP_ROUTE, dev))
+    tables = make_fold_tables(E, seed=1)
+    to_f, ids_f, w_f, _ = _gpu_fold(desc, mode, budget, tables, tok_off, ids, w, dev)
+    # the rest of the layer on the folded routes
+    to_d = torch.as_tensor(to_f.astype(np.int32), device=dev)
+    ids_d = torch.as_tensor(ids_f.astype(np.int32), device=dev)
+    w_d = torch.as_tensor(w_f.astype(np.float32), device=dev)
+    counts = torch.empty(E, **i32)
+    eoff = torch.empty(E + 1, **i32)
+    ptok = torch.empty(T * km, **i32)
+    psrc = torch.empty_like(ptok)
+    inv = torch.empty_like(ptok)
+    nact = torch.empty(1, **i32)
+    moe.moe_permute(desc, to_d, ids_d, counts, eoff, ptok, psrc, inv, nact,
+                    moe.alloc_workspace(desc, moe.MOE_OP_PERMUTE, dev))
+    y = torch.empty((T * km, d), dtype=layer.x.dtype, device=dev)
+    moe.moe_ffn(desc, layer.x, layer.w_gate, layer.w_up, layer.w_down, None, None, None, eoff, ptok, y, None,
+                moe.alloc_workspace(desc, moe.MOE_OP_FFN, dev))
+    out = torch.empty((T, d), dtype=layer.x.dtype, device=dev)
+    moe.moe_combine(desc, y, None, to_d, w_d, inv, out)
+    torch.cuda.synchronize()
+    # oracle: its own routing, its own folding, explicit-route forward
+    r, _ = oracle_routing(layer)
+    S, L, H = (t.numpy() for t in tables)
+    if mode == "pool":
+        rt, ri, rw, pool = oracle.fold_pool(r["tok_off"], r["ids"], r["w"], S, L, H, budget, E)
+        assert int(nact.item()) == int(pool.sum()) <= budget
+    else:
+        rt, ri, rw = oracle.fold_token(r["tok_off"], r["ids"], r["w"], S, L, H, budget)
+    np.testing.assert_array_equal(to_f, rt)
+    np.testing.assert_array_equal(ids_f, ri)
+    tokens = sample_tokens(T, SAMPLE[name])
+    ref = oracle.forward_routes(to_f64(layer.x), rt, ri, rw, ExpertView(layer.w_gate), ExpertView(layer.w_up),
+                                ExpertView(layer.w_down), tokens=tokens)
+    err = compare_out(out, ref, cfg.dtype, tokens)
+    _say(f"[fold layer] {name} {mode}={budget}: n_active {int(nact.item())} {err}")
