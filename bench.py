@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--k-dist", default="",
                     help="eq7:MU,SIGMA draws the budgets k = clip(round(N(MU, SIGMA^2)), 1, k_max) "
                          "instead of the workload's own law")
+    ap.add_argument("--fold", default="",
+                    help="token:K or pool:D: fold the routes (ExFold) before the permutation, with "
+                         "synthetic projector / loss tables; the step then runs the staged calls")
     ap.add_argument("--k-policy", default="exact",
                     help="budget each token executes: exact (its own k_t; the headline), batch_max "
                          "(every token runs the batch maximum) or round_up:N (k_t rounded up to a "
@@ -179,6 +182,43 @@ def main():
         moe.moe_forward(desc, layer.x, layer.w_router, layer.router_bias, layer.k, layer.w_gate,
                         layer.w_up, layer.w_down, *sh, out, stats, status, ws)
 
+    fold = None
+    if args.fold:
+        # route -> (permute: pool mode) -> fold -> permute -> FFN -> combine
+        fmode, _, fb = args.fold.partition(":")
+        from workloads import make_fold_tables
+        fold = dict(mode=fmode, budget=int(fb),
+                    tables=[t.to(dev) for t in make_fold_tables(E, seed=cfg.seed)])
+        i32 = dict(dtype=torch.int32, device=dev)
+        A_cap = T * cfg.k_max
+        f = {n: torch.empty(T + 1, **i32) for n in ("to0", "to1")}
+        f.update({n: torch.empty(A_cap, **i32) for n in ("ids0", "ids1", "pt0", "ps0", "iv0", "pt1", "ps1", "iv1")})
+        f.update({n: torch.empty(A_cap, dtype=torch.float32, device=dev) for n in ("w0", "w1")})
+        f.update({n: torch.empty(E + 1, **i32) for n in ("eo0", "eo1")})
+        f.update({n: torch.empty(E, **i32) for n in ("c0", "c1")})
+        f.update({n: torch.empty(1, **i32) for n in ("na0", "na1")})
+        f["y"] = torch.empty((A_cap, d), dtype=layer.x.dtype, device=dev)
+        f["ysh"] = torch.empty((T, d), dtype=layer.x.dtype, device=dev) if Is else None
+        f["ws"] = {op: moe.alloc_workspace(desc, op, dev)
+                   for op in (moe.MOE_OP_ROUTE, moe.MOE_OP_PERMUTE, moe.MOE_OP_FOLD, moe.MOE_OP_FFN)}
+        fold["buf"] = f
+
+        def step():
+            S_, L_, H_ = fold["tables"]
+            wsd = f["ws"]
+            moe.moe_route(desc, layer.x, layer.w_router, layer.router_bias, layer.k, f["to0"], f["ids0"], f["w0"],
+                          status, wsd[moe.MOE_OP_ROUTE])
+            if fmode == "pool":
+                moe.moe_permute(desc, f["to0"], f["ids0"], f["c0"], f["eo0"], f["pt0"], f["ps0"], f["iv0"],
+                                f["na0"], wsd[moe.MOE_OP_PERMUTE])
+            moe.moe_fold(desc, fmode, fold["budget"], S_, L_, H_, f["to0"], f["ids0"], f["w0"], f["eo0"],
+                         f["ps0"], f["to1"], f["ids1"], f["w1"], None, wsd[moe.MOE_OP_FOLD])
+            moe.moe_permute(desc, f["to1"], f["ids1"], f["c1"], f["eo1"], f["pt1"], f["ps1"], f["iv1"], f["na1"],
+                            wsd[moe.MOE_OP_PERMUTE])
+            moe.moe_ffn(desc, layer.x, layer.w_gate, layer.w_up, layer.w_down, *sh, f["eo1"], f["pt1"], f["y"],
+                        f["ysh"], wsd[moe.MOE_OP_FFN])
+            moe.moe_combine(desc, f["y"], f["ysh"], f["to1"], f["w1"], f["iv1"], out)
+
     if args.calib_copy:
         src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -220,8 +260,11 @@ def main():
         wall = time.perf_counter() - w0
     ms_step = t_start.elapsed_time(t_end) / args.steps
     assert int(status.item()) == 0
-    st = stats.cpu().numpy()
-    n_act, A = int(st[E]), int(st[E + 1])
+    if fold is None:
+        st = stats.cpu().numpy()
+        n_act, A = int(st[E]), int(st[E + 1])
+    else:
+        n_act, A = int(fold["buf"]["na1"].item()), int(fold["buf"]["to1"][T].item())
     esz = layer.x.element_size()
 
     # ---- dominant kernel: the gate/up SwiGLU FFN, timed inside the layer.
@@ -258,6 +301,14 @@ def main():
         for i in range(max(3, args.warmup // 4) + n_in):
             moe.moe_route(desc_r, layer.x, layer.w_router, layer.router_bias, layer.k, tok_off, ids, wts, status,
                           ws_route)
+            if fold is not None:
+                fb_ = fold["buf"]
+                moe.moe_permute(desc_r, tok_off, ids, counts, eoff, ptok, psrc, inv, nact, ws_perm)
+                moe.moe_fold(desc_r, fold["mode"], fold["budget"], *fold["tables"], tok_off, ids, wts, eoff, psrc,
+                             fb_["to1"], fb_["ids1"], fb_["w1"], None, fb_["ws"][moe.MOE_OP_FOLD])
+                tok_off.copy_(fb_["to1"])
+                ids.copy_(fb_["ids1"])
+                wts.copy_(fb_["w1"])
             moe.moe_permute(desc_r, tok_off, ids, counts, eoff, ptok, psrc, inv, nact, ws_perm)
             moe.moe_ffn_plan(desc_r, eoff, ws_ffn)
             j = i - max(3, args.warmup // 4)
@@ -308,7 +359,7 @@ def main():
     roof["intensity_flop_per_byte"] = round(intensity, 1)
     roof["ridge_flop_per_byte"] = round(ridge, 1)
     roof["traffic"] = (measured_traffic(cfg.name, routed_path)
-                       if args.k_policy == "exact" and not args.k_dist else None)
+                       if args.k_policy == "exact" and not args.k_dist and not args.fold else None)
 
     # ---- whole layer against its own roofline ----
     w_bytes = 3 * n_act * d * I * esz
@@ -323,7 +374,7 @@ def main():
                                          (PEAK_BF16_TFLOPS if esz == 2 else PEAK_FP32_TFLOPS), 4)}
 
     cpu = None
-    if not args.no_cpu_baseline and args.k_policy == "exact":
+    if not args.no_cpu_baseline and args.k_policy == "exact" and not args.fold:
         n = args.cpu_sample or {"mixtral_decode": 64, "qwen3_30b_a3b_decode": 256, "tiny_fp32": 16,
                                 "subexpert_prefill": 64, "dsv3_decode": 16, "dsv3_prefill": 16}[cfg.name]
         print(f"[bench] timing the CPU oracle on {n} tokens", file=sys.stderr, flush=True)
@@ -347,6 +398,7 @@ def main():
                    "k_values": k_desc, "k_max": cfg.k_max, "A": A, "n_active": n_act,
                    "execution": "eager" if args.eager else "hip_graph", "ffn_path": routed_path,
                    "router": args.router, "k_policy": args.k_policy, "k_dist": args.k_dist or "workload",
+                   "fold": args.fold or "none",
                    "wall_s": round(wall, 3)},
         "layer": layer_info,
         "roofline": roof,

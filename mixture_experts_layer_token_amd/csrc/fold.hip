@@ -16,8 +16,9 @@
 //   fold_routes_kernel one wave per token, one route per lane: keep / target /
 //                      merge decisions by shuffles, folded routes written at
 //                      the token's original offset, their count to cnt[t];
-//   fold_scan_kernel   one workgroup: tok_off_out = exclusive scan of cnt;
-//   fold_compact_kernel one wave per token: routes to their final offset.
+//   fold_scan_kernel   one workgroup: tok_off_out = exclusive scan of cnt (for
+//                      at most 1024 tokens it also moves the routes);
+//   fold_copy_kernel   one wave per token: routes to their final offsets.
 // Every decision is a comparison of float32 values (scores are float32
 // products, losses as stored) or of the float64 aggregates, taken in a fixed
 // order; weights are added in route order.  Bit-reproducible.
@@ -29,6 +30,11 @@ namespace moe {
 constexpr int FOLD_MAX_K = 64;  // routes per token (one lane each)
 
 // ---- pool selection (one workgroup of 1024 threads, E <= 1024) ----
+// The routed weights are gathered into LDS in row (expert, token) order,
+// FOLD_CHUNK rows at a time, by all threads; each expert's thread then adds
+// its rows in order from LDS.
+constexpr int FOLD_CHUNK = 16384;
+
 __global__ __launch_bounds__(1024) void fold_pool_kernel(const float* __restrict__ H,
                                                          const float* __restrict__ w,
                                                          const int32_t* __restrict__ expert_off,
@@ -36,19 +42,28 @@ __global__ __launch_bounds__(1024) void fold_pool_kernel(const float* __restrict
                                                          int32_t* __restrict__ pool, int32_t* __restrict__ members,
                                                          int32_t* __restrict__ n_members,
                                                          int32_t* __restrict__ pool_out) {
+  __shared__ float wl[FOLD_CHUNK];
   __shared__ double agg[1024];
   __shared__ int32_t act[1024];
   __shared__ int32_t wsum[16];
   const int e = threadIdx.x;
-  double a = 0.0;
-  int on = 0;
+  const int A = expert_off[E];
+  int p0 = 0, p1 = 0;
   if (e < E) {
-    const int p0 = expert_off[e], p1 = expert_off[e + 1];
-    double s = 0.0;
-    for (int p = p0; p < p1; ++p) s += (double)w[perm_src[p]];
-    a = s * (double)H[e];
-    on = p1 > p0;
+    p0 = expert_off[e];
+    p1 = expert_off[e + 1];
   }
+  double s = 0.0;
+  for (int c0 = 0; c0 < A; c0 += FOLD_CHUNK) {
+    const int n = min(FOLD_CHUNK, A - c0);
+    for (int i = e; i < n; i += 1024) wl[i] = w[perm_src[c0 + i]];
+    __syncthreads();
+    const int b = max(p0, c0), t = min(p1, c0 + n);
+    for (int p = b; p < t; ++p) s += (double)wl[p - c0];
+    __syncthreads();
+  }
+  const double a = e < E ? s * (double)H[e] : 0.0;
+  const int on = p1 > p0;
   agg[e] = a;
   act[e] = on;
   __syncthreads();
@@ -76,8 +91,15 @@ __global__ __launch_bounds__(256) void fold_routes_kernel(
     const int32_t* __restrict__ n_members, int32_t* __restrict__ ids_tmp, float* __restrict__ w_tmp,
     int32_t* __restrict__ cnt) {
   __shared__ int32_t kept_e[4][FOLD_MAX_K];
+  __shared__ int32_t mem_l[MODE == 1 ? 1024 : 1];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
+  int nm = 0;
+  if (MODE == 1) {
+    nm = n_members[0];
+    for (int i = threadIdx.x; i < nm; i += 256) mem_l[i] = members[i];
+    __syncthreads();
+  }
   if (t >= T) return;
   const int a0 = tok_off[t];
   const int kt = min(tok_off[t + 1] - a0, FOLD_MAX_K);
@@ -131,13 +153,13 @@ __global__ __launch_bounds__(256) void fold_routes_kernel(
       tgt = e;
       c = wj;
     } else if (valid) {
-      const int nm = n_members[0];
       if (nm > 0) {
         const float* Lr = L + (size_t)e * E;
-        int best = members[0];
+        int best = mem_l[0];
         float bl = Lr[best];
+#pragma unroll 8
         for (int m = 1; m < nm; ++m) {
-          const int p = members[m];
+          const int p = mem_l[m];
           const float l = Lr[p];
           if (l < bl) {
             bl = l;
@@ -173,9 +195,16 @@ __global__ __launch_bounds__(256) void fold_routes_kernel(
   if (lane == 0) cnt[t] = __popcll(em);
 }
 
-// ---- tok_off_out = exclusive scan of cnt (one workgroup) ----
-__global__ __launch_bounds__(1024) void fold_scan_kernel(const int32_t* __restrict__ cnt, int T,
-                                                         int32_t* __restrict__ tok_off_out) {
+// ---- tok_off_out = exclusive scan of cnt (one workgroup; a thread owns a
+// contiguous run of tokens).  COPY: the same threads also move their tokens'
+// routes to the final offsets (small batches); else fold_copy_kernel does. ----
+template <bool COPY>
+__global__ __launch_bounds__(1024) void fold_scan_kernel(const int32_t* __restrict__ cnt,
+                                                         const int32_t* __restrict__ tok_off, int T,
+                                                         const int32_t* __restrict__ ids_tmp,
+                                                         const float* __restrict__ w_tmp,
+                                                         int32_t* __restrict__ tok_off_out,
+                                                         int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
   __shared__ int32_t wsum[16];
   const int tid = threadIdx.x;
   const int per = (T + 1023) / 1024;
@@ -185,18 +214,26 @@ __global__ __launch_bounds__(1024) void fold_scan_kernel(const int32_t* __restri
   const int incl = block_scan_incl<1024>(s, wsum);
   int run = incl - s;
   for (int i = beg; i < end; ++i) {
+    const int n = cnt[i];
     tok_off_out[i] = run;
-    run += cnt[i];
+    if (COPY) {
+      const int a0 = tok_off[i];
+      for (int j = 0; j < n; ++j) {
+        ids_out[run + j] = ids_tmp[a0 + j];
+        w_out[run + j] = w_tmp[a0 + j];
+      }
+    }
+    run += n;
   }
   if (tid == 1023) tok_off_out[T] = incl;
 }
 
 // ---- routes to their final offsets: one wave per token ----
-__global__ __launch_bounds__(256) void fold_compact_kernel(const int32_t* __restrict__ tok_off,
-                                                           const int32_t* __restrict__ tok_off_out, int T,
-                                                           const int32_t* __restrict__ ids_tmp,
-                                                           const float* __restrict__ w_tmp,
-                                                           int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+__global__ __launch_bounds__(256) void fold_copy_kernel(const int32_t* __restrict__ tok_off,
+                                                        const int32_t* __restrict__ tok_off_out, int T,
+                                                        const int32_t* __restrict__ ids_tmp,
+                                                        const float* __restrict__ w_tmp,
+                                                        int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -228,10 +265,16 @@ hipError_t launch_fold(int mode, int budget, const float* S, const float* L, con
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(fold_scan_kernel, dim3(1), dim3(1024), 0, st, ws.cnt, T, tok_off_out);
+  if (T <= 1024) {  // one token per thread at most: copy in the scan
+    hipLaunchKernelGGL(fold_scan_kernel<true>, dim3(1), dim3(1024), 0, st, ws.cnt, tok_off, T, ws.ids, ws.w,
+                       tok_off_out, ids_out, w_out);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(fold_scan_kernel<false>, dim3(1), dim3(1024), 0, st, ws.cnt, tok_off, T, ws.ids, ws.w,
+                     tok_off_out, ids_out, w_out);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || T == 0) return err;
-  hipLaunchKernelGGL(fold_compact_kernel, dim3((T + 3) / 4), dim3(256), 0, st, tok_off, tok_off_out, T, ws.ids, ws.w,
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(fold_copy_kernel, dim3((T + 3) / 4), dim3(256), 0, st, tok_off, tok_off_out, T, ws.ids, ws.w,
                      ids_out, w_out);
   return hipGetLastError();
 }
