@@ -28,6 +28,9 @@ precision):
 * Expert folding (ExFold summary, arXiv 2608.24938): token-level top-K and
   batch-level expert-pool folding of the routes into kept targets with
   scalar projectors S and projection losses L (fold_token, fold_pool).
+* Proxy gating of a split layer (MoE-Prism §III-B2, training-free path):
+  whole-expert routing, then the top kappa_j sub-experts by a gate-neuron
+  proxy score, each inheriting its expert's weight (proxy_route).
 * Expert FFN: SwiGLU, §III-B1 Eq. (1): A = SiLU(X W_gate) * (X W_up) and
   X' = A W_down, with SiLU(z) = z * sigmoid(z).  Weights are stored in the
   [out, in] layout, so X W_gate of the page is x @ w_gate[e].T here.
@@ -55,6 +58,9 @@ __all__ = [
     "fold_token",
     "fold_pool",
     "forward_routes",
+    "kappa_balanced",
+    "proxy_scores",
+    "proxy_route",
     "router_logits",
     "select_experts",
     "route",
@@ -393,6 +399,69 @@ def forward_routes(x, tok_off, ids, w, w_gate, w_up, w_down, shared: Optional[Se
     if shared is not None:
         out += swiglu_expert(xs, shared[0], shared[1], shared[2])
     return out
+
+
+# ---------------------------------------------------------------------------
+# Training-free proxy (complex-gate) routing of a split layer (MoE-Prism,
+# arXiv 2510.19366, §III-B2, Training-Free Proxy Gating).  The original
+# router picks m whole experts per token and their weights; among the N
+# sub-experts of the j-th one, the kappa_j with the largest proxy scores run,
+# each inheriting the whole expert's weight (no second softmax).  The proxy
+# score of a sub-expert is the mean absolute SwiGLU activation over its r
+# gate neurons.  Sub-expert n of whole expert e has index N*e + n.
+
+def kappa_balanced(k: int, m: int, N: int) -> list:
+    """A budget k split over the m selected experts: as evenly as possible,
+    the remainder to the experts of higher router probability (the page
+    leaves the configured vectors open).  Needs 0 <= k <= m*N."""
+    if not 0 <= k <= m * N:
+        raise ValueError("budget outside [0, m*N]")
+    q, rem = divmod(k, m)
+    return [q + (1 if j < rem else 0) for j in range(m)]
+
+
+def proxy_scores(x_row, w_gate, w_up, gate_idx, e: int, N: int) -> np.ndarray:
+    """s_n(x) = (1/r) sum over the gate neurons c of sub-expert N*e + n of
+    |SiLU(x . w_gate[sub][c]) * (x . w_up[sub][c])| for n < N (float64)."""
+    x = _f64(x_row)
+    out = np.zeros(N, dtype=np.float64)
+    for n in range(N):
+        sub = N * e + n
+        c = np.asarray(gate_idx[sub], dtype=np.int64)
+        g = _f64(w_gate[sub])[c] @ x
+        u = _f64(w_up[sub])[c] @ x
+        out[n] = np.abs(silu(g) * u).mean()
+    return out
+
+
+def proxy_route(x, w_router_base, bias, k, k_max: int, m: int, N: int, kappa, gate_idx, w_gate, w_up,
+                routed_scale: float = 1.0):
+    """Routes of the split layer under proxy gating.  ``kappa[k]`` is the
+    vector (kappa_1 .. kappa_m) for budget k (sub-expert units).  A k_t outside
+    [0, k_max] runs nothing and sets status 1.  Within a whole expert the
+    chosen sub-experts are listed by proxy score (descending, ties to the lower
+    n).  Returns a dict with tok_off, ids, w (float64), status and the proxy
+    scores [T][m][N] for the validity check of the selections."""
+    k = np.asarray(k, dtype=np.int64)
+    T = k.shape[0]
+    base = route(x, w_router_base, bias, np.full(T, m), m, routed_scale)
+    status = int(((k < 0) | (k > k_max)).any())
+    rows, scores = [], np.zeros((T, m, N), dtype=np.float64)
+    for t in range(T):
+        kt = int(k[t])
+        row = []
+        if 0 <= kt <= k_max:
+            kv = kappa[kt]
+            for j in range(m):
+                a = int(base["tok_off"][t]) + j
+                e = int(base["ids"][a])
+                s = proxy_scores(x[t], w_gate, w_up, gate_idx, e, N)
+                scores[t, j] = s
+                order = sorted(range(N), key=lambda n: (-s[n], n))[:int(kv[j])]
+                row += [(N * e + n, float(base["w"][a])) for n in order]
+        rows.append(row)
+    tok_off, ids, w = _csr(rows)
+    return {"tok_off": tok_off, "ids": ids, "w": w, "status": status, "scores": scores, "base": base}
 
 
 def activated_weight_bytes(n_active: int, d: int, I: int, elem_bytes: int) -> int:

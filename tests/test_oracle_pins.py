@@ -500,3 +500,94 @@ def test_forward_routes_matches_forward():
     got = oracle.forward_routes(a["x"], r["tok_off"], r["ids"], r["w"], a["w_gate"], a["w_up"], a["w_down"],
                                 shared=a["shared"])
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- proxy gating (split layer)
+
+def test_kappa_balanced():
+    for m in (1, 3, 8):
+        for N in (1, 2, 4):
+            for k in range(m * N + 1):
+                kv = oracle.kappa_balanced(k, m, N)
+                assert sum(kv) == k and all(0 <= v <= N for v in kv)
+                assert max(kv) - min(kv) <= 1 and kv == sorted(kv, reverse=True)
+    with pytest.raises(ValueError):
+        oracle.kappa_balanced(9, 2, 4)
+
+
+def test_proxy_scores_match_scalar_definition():
+    """s_n = mean over the gate neurons of |SiLU(g) u|, recomputed neuron by
+    neuron with exact sums (math.fsum) and scipy's logistic function."""
+    L = make_custom_layer(T=3, d=24, E=8, I=16, k=[1, 1, 1], seed=31)
+    a = _arrays(L)
+    rng = np.random.default_rng(2)
+    gate_idx = np.stack([rng.permutation(16)[:5] for _ in range(8)])
+    for t in range(3):
+        for e in range(2):
+            s = oracle.proxy_scores(a["x"][t], a["w_gate"], a["w_up"], gate_idx, e, 4)
+            for n in range(4):
+                sub = 4 * e + n
+                vals = []
+                for c in gate_idx[sub]:
+                    g = math.fsum(float(p) * float(q) for p, q in zip(a["x"][t], a["w_gate"][sub][c]))
+                    u = math.fsum(float(p) * float(q) for p, q in zip(a["x"][t], a["w_up"][sub][c]))
+                    vals.append(abs(g * float(scipy.special.expit(g)) * u))
+                assert abs(s[n] - math.fsum(vals) / len(vals)) <= 1e-12 * max(1.0, abs(s[n]))
+
+
+def _split_layer(T, d, E0, I0, N, m, seed):
+    """A whole-expert layer and its contiguous split into N sub-experts per
+    expert (neuron slices, MoE-Prism Eq. (3))."""
+    L = make_custom_layer(T=T, d=d, E=E0, I=I0, k=[m] * T, seed=seed)
+    a = _arrays(L)
+    I = I0 // N
+    wg = np.stack([a["w_gate"][e][n * I:(n + 1) * I] for e in range(E0) for n in range(N)])
+    wu = np.stack([a["w_up"][e][n * I:(n + 1) * I] for e in range(E0) for n in range(N)])
+    wd = np.stack([a["w_down"][e][:, n * I:(n + 1) * I] for e in range(E0) for n in range(N)])
+    return a, wg, wu, wd
+
+
+def test_proxy_route_all_subexperts_reconstruct_whole_experts():
+    """Choosing all N sub-experts of every selected expert (k = m N) gives the
+    whole-expert layer's top-m output (MoE-Prism §III-B2: selecting all N
+    reconstructs the original contribution)."""
+    T, d, E0, I0, N, m = 7, 32, 6, 24, 4, 3
+    a, wg, wu, wd = _split_layer(T, d, E0, I0, N, m, seed=33)
+    gate_idx = np.stack([np.arange(3)] * (E0 * N))
+    kappa = {m * N: [N] * m}
+    r = oracle.proxy_route(a["x"], a["w_router"], a["bias"], [m * N] * T, m * N, m, N, kappa, gate_idx, wg, wu)
+    got = oracle.forward_routes(a["x"], r["tok_off"], r["ids"], r["w"], wg, wu, wd)
+    ref, _ = _oracle_forward(a, m, k=np.full(T, m))
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_proxy_route_selection_properties():
+    T, d, E0, I0, N, m = 9, 32, 6, 24, 4, 3
+    a, wg, wu, wd = _split_layer(T, d, E0, I0, N, m, seed=34)
+    rng = np.random.default_rng(3)
+    gate_idx = np.stack([rng.permutation(I0 // N)[:4] for _ in range(E0 * N)])
+    k = np.array([0, 1, 2, 5, 7, 12, 3, 13, -1])
+    kappa = [oracle.kappa_balanced(v, m, N) for v in range(m * N + 1)]
+    r = oracle.proxy_route(a["x"], a["w_router"], a["bias"], k, m * N, m, N, kappa, gate_idx, wg, wu)
+    assert r["status"] == 1
+    base = r["base"]
+    for t in range(T):
+        got = r["ids"][r["tok_off"][t]:r["tok_off"][t + 1]].tolist()
+        if not 0 <= k[t] <= m * N:
+            assert got == []
+            continue
+        assert len(got) == k[t]
+        pos = 0
+        for j in range(m):
+            e = int(base["ids"][base["tok_off"][t] + j])
+            kj = kappa[k[t]][j]
+            mine = got[pos:pos + kj]
+            pos += kj
+            assert all(v // N == e for v in mine)                   # sub-experts of the j-th expert
+            s = r["scores"][t, j]
+            chosen = [v % N for v in mine]
+            rest = [n for n in range(N) if n not in chosen]
+            assert all(s[c] >= s[o] for c in chosen for o in rest)  # the top kappa_j by proxy score
+            assert chosen == sorted(chosen, key=lambda n: (-s[n], n))
+            wj = base["w"][base["tok_off"][t] + j]
+            assert all(r["w"][r["tok_off"][t] + q] == wj for q in range(pos - kj, pos))
