@@ -438,19 +438,25 @@ def proxy_route(x, w_router_base, bias, k, k_max: int, m: int, N: int, kappa, ga
                 routed_scale: float = 1.0):
     """Routes of the split layer under proxy gating.  ``kappa[k]`` is the
     vector (kappa_1 .. kappa_m) for budget k (sub-expert units).  A k_t outside
-    [0, k_max] runs nothing and sets status 1.  Within a whole expert the
+    [0, k_max], or whose vector breaks 0 <= kappa_j <= N or sum_j kappa_j = k_t,
+    runs nothing and sets status 1.  Within a whole expert the
     chosen sub-experts are listed by proxy score (descending, ties to the lower
     n).  Returns a dict with tok_off, ids, w (float64), status and the proxy
     scores [T][m][N] for the validity check of the selections."""
     k = np.asarray(k, dtype=np.int64)
     T = k.shape[0]
     base = route(x, w_router_base, bias, np.full(T, m), m, routed_scale)
-    status = int(((k < 0) | (k > k_max)).any())
+
+    def runs(kt):
+        # a configured vector has every kappa_j in [0, N] and sums to the budget
+        return 0 <= kt <= k_max and all(0 <= int(v) <= N for v in kappa[kt]) and sum(int(v) for v in kappa[kt]) == kt
+
+    status = int(any(not runs(int(kt)) for kt in k))
     rows, scores = [], np.zeros((T, m, N), dtype=np.float64)
     for t in range(T):
         kt = int(k[t])
         row = []
-        if 0 <= kt <= k_max:
+        if runs(kt):
             kv = kappa[kt]
             for j in range(m):
                 a = int(base["tok_off"][t]) + j

@@ -591,3 +591,24 @@ def test_proxy_route_selection_properties():
             assert chosen == sorted(chosen, key=lambda n: (-s[n], n))
             wj = base["w"][base["tok_off"][t] + j]
             assert all(r["w"][r["tok_off"][t] + q] == wj for q in range(pos - kj, pos))
+
+
+def test_proxy_route_rejects_vectors_off_the_budget():
+    """A configured vector must have every kappa_j in [0, N] and sum to its
+    budget (MoE-Prism §III-B2): a token whose budget maps to a vector that
+    breaks this runs nothing and sets the status; the others are unaffected."""
+    T, d, E0, I0, N, m = 6, 32, 6, 24, 4, 3
+    a, wg, wu, _ = _split_layer(T, d, E0, I0, N, m, seed=35)
+    gate_idx = np.stack([np.arange(3)] * (E0 * N))
+    good = [oracle.kappa_balanced(v, m, N) for v in range(m * N + 1)]
+    bad = [list(v) for v in good]
+    bad[5] = [5, 0, 0]          # entry above N
+    bad[4] = [2, 1, 0]          # sums to 3, not 4
+    k = np.array([5, 4, 3, 2, 6, 4])
+    r_bad = oracle.proxy_route(a["x"], a["w_router"], a["bias"], k, m * N, m, N, bad, gate_idx, wg, wu)
+    r_good = oracle.proxy_route(a["x"], a["w_router"], a["bias"], k, m * N, m, N, good, gate_idx, wg, wu)
+    assert r_bad["status"] == 1 and r_good["status"] == 0
+    for t in range(T):
+        got = r_bad["ids"][r_bad["tok_off"][t]:r_bad["tok_off"][t + 1]].tolist()
+        ref = r_good["ids"][r_good["tok_off"][t]:r_good["tok_off"][t + 1]].tolist()
+        assert got == ([] if k[t] in (4, 5) else ref)
