@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--fold", default="",
                     help="token:K or pool:D: fold the routes (ExFold) before the permutation, with "
                          "synthetic projector / loss tables; the step then runs the staged calls")
+    ap.add_argument("--proxy", type=int, default=0,
+                    help="R > 0: route the split layer by training-free proxy gating (MoE-Prism) with R "
+                         "gate neurons per sub-expert over a synthetic whole-expert router picking "
+                         "k_max / split experts; the step then runs the staged calls")
     ap.add_argument("--k-policy", default="exact",
                     help="budget each token executes: exact (its own k_t; the headline), batch_max "
                          "(every token runs the batch maximum) or round_up:N (k_t rounded up to a "
@@ -219,6 +223,36 @@ def main():
                         f["ysh"], wsd[moe.MOE_OP_FFN])
             moe.moe_combine(desc, f["y"], f["ysh"], f["to1"], f["w1"], f["iv1"], out)
 
+    proxy = None
+    if args.proxy:
+        # whole-expert route -> proxy SwiGLU -> proxy routes -> permute -> FFN -> combine
+        if cfg.split < 2 or args.fold or args.k_policy != "exact":
+            raise SystemExit("--proxy needs a split workload, no --fold and the exact k policy")
+        from workloads import make_proxy_inputs
+        Np, rp = cfg.split, args.proxy
+        mp = -(-cfg.k_max // Np)
+        w_base, gate_idx = make_proxy_inputs(cfg, rp, dev)
+        wp_g, wp_u = moe.proxy_pack(layer.w_gate, layer.w_up, gate_idx, Np)
+        pr = moe.ProxyRouter(desc, Np, rp, mp, moe.moe_proxy_kappa_balanced(cfg.k_max, mp, Np), dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        A_cap = T * cfg.k_max
+        pb = {n: torch.empty(A_cap, **i32) for n in ("pt", "ps", "iv")}
+        pb.update(eo=torch.empty(E + 1, **i32), c=torch.empty(E, **i32), na=torch.empty(1, **i32),
+                  y=torch.empty((A_cap, d), dtype=layer.x.dtype, device=dev),
+                  ysh=torch.empty((T, d), dtype=layer.x.dtype, device=dev) if Is else None,
+                  wsp=moe.alloc_workspace(desc, moe.MOE_OP_PERMUTE, dev),
+                  wsf=moe.alloc_workspace(desc, moe.MOE_OP_FFN, dev))
+        proxy = dict(r=rp, m=mp, N=Np, router=pr, buf=pb,
+                     run=lambda: pr.run(layer.x, w_base, None, layer.k, wp_g, wp_u))
+
+        def step():
+            proxy["run"]()
+            moe.moe_permute(desc, pr.tok_off, pr.ids, pb["c"], pb["eo"], pb["pt"], pb["ps"], pb["iv"], pb["na"],
+                            pb["wsp"])
+            moe.moe_ffn(desc, layer.x, layer.w_gate, layer.w_up, layer.w_down, *sh, pb["eo"], pb["pt"], pb["y"],
+                        pb["ysh"], pb["wsf"])
+            moe.moe_combine(desc, pb["y"], pb["ysh"], pr.tok_off, pr.w, pb["iv"], out)
+
     if args.calib_copy:
         src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -259,8 +293,12 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    if proxy is not None:
+        status = proxy["router"].status
     assert int(status.item()) == 0
-    if fold is None:
+    if proxy is not None:
+        n_act, A = int(proxy["buf"]["na"].item()), int(proxy["router"].tok_off[T].item())
+    elif fold is None:
         st = stats.cpu().numpy()
         n_act, A = int(st[E]), int(st[E + 1])
     else:
@@ -299,8 +337,14 @@ def main():
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_in)]
     with torch.cuda.stream(stream):
         for i in range(max(3, args.warmup // 4) + n_in):
-            moe.moe_route(desc_r, layer.x, layer.w_router, layer.router_bias, layer.k, tok_off, ids, wts, status,
-                          ws_route)
+            if proxy is not None:
+                proxy["run"]()
+                tok_off.copy_(proxy["router"].tok_off)
+                ids.copy_(proxy["router"].ids)
+                wts.copy_(proxy["router"].w)
+            else:
+                moe.moe_route(desc_r, layer.x, layer.w_router, layer.router_bias, layer.k, tok_off, ids, wts,
+                              status, ws_route)
             if fold is not None:
                 fb_ = fold["buf"]
                 moe.moe_permute(desc_r, tok_off, ids, counts, eoff, ptok, psrc, inv, nact, ws_perm)
@@ -334,6 +378,22 @@ def main():
         k_end.record(stream)
         torch.cuda.synchronize()
     alone_ms = k_start.elapsed_time(k_end) / n_in
+    proxy_info = None
+    if proxy is not None:
+        # the proxy routing stage (whole-expert route, permute, plan, proxy
+        # SwiGLU, selection) back to back on its own
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                proxy["run"]()
+            p_start = torch.cuda.Event(enable_timing=True)
+            p_end = torch.cuda.Event(enable_timing=True)
+            p_start.record(stream)
+            for _ in range(n_in):
+                proxy["run"]()
+            p_end.record(stream)
+            torch.cuda.synchronize()
+        proxy_info = {"r": proxy["r"], "m": proxy["m"], "N": proxy["N"], "Ip": proxy["router"].Ip,
+                      "stage_us": round(p_start.elapsed_time(p_end) / n_in * 1e3, 2)}
     gu_bytes = 2 * n_act * I * d * esz + T * d * esz + A * I * esz   # weights + x rows + H
     gu_flops = 4.0 * d * I * A
     # The bound is the roofline's: arithmetic intensity (algorithmic FLOPs per
@@ -359,7 +419,8 @@ def main():
     roof["intensity_flop_per_byte"] = round(intensity, 1)
     roof["ridge_flop_per_byte"] = round(ridge, 1)
     roof["traffic"] = (measured_traffic(cfg.name, routed_path)
-                       if args.k_policy == "exact" and not args.k_dist and not args.fold else None)
+                       if args.k_policy == "exact" and not args.k_dist and not args.fold and not args.proxy
+                       else None)
 
     # ---- whole layer against its own roofline ----
     w_bytes = 3 * n_act * d * I * esz
@@ -374,7 +435,7 @@ def main():
                                          (PEAK_BF16_TFLOPS if esz == 2 else PEAK_FP32_TFLOPS), 4)}
 
     cpu = None
-    if not args.no_cpu_baseline and args.k_policy == "exact" and not args.fold:
+    if not args.no_cpu_baseline and args.k_policy == "exact" and not args.fold and not args.proxy:
         n = args.cpu_sample or {"mixtral_decode": 64, "qwen3_30b_a3b_decode": 256, "tiny_fp32": 16,
                                 "subexpert_prefill": 64, "dsv3_decode": 16, "dsv3_prefill": 16}[cfg.name]
         print(f"[bench] timing the CPU oracle on {n} tokens", file=sys.stderr, flush=True)
@@ -398,7 +459,7 @@ def main():
                    "k_values": k_desc, "k_max": cfg.k_max, "A": A, "n_active": n_act,
                    "execution": "eager" if args.eager else "hip_graph", "ffn_path": routed_path,
                    "router": args.router, "k_policy": args.k_policy, "k_dist": args.k_dist or "workload",
-                   "fold": args.fold or "none",
+                   "fold": args.fold or "none", "proxy": proxy_info or "none",
                    "wall_s": round(wall, 3)},
         "layer": layer_info,
         "roofline": roof,

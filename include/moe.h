@@ -283,6 +283,63 @@ moe_status moe_fold(const moe_desc* desc, int32_t mode, int32_t budget, const fl
                     moe_stream_t stream);
 
 /*
+ * Training-free proxy gating of a split layer (MoE-Prism, arXiv 2510.19366,
+ * §III-B2, Training-Free Proxy Gating).  `desc` describes the split layer: E
+ * sub-experts of width I, sub-expert n of whole expert e at index N*e + n
+ * (E a multiple of N), budgets k_t counted in sub-experts, k_max <= m*N and
+ * m*N <= 64.  The whole-expert router picks m experts per token (moe_route on
+ * a descriptor with E/N experts, k_max = m and every k_t = m); the N
+ * sub-experts of the j-th pick get proxy scores s_n = mean over the r gate
+ * neurons c of |SiLU(x . w_gate[c]) * (x . w_up[c])|; the kappa_j best run
+ * (ties: lower n), each with the pick's routing weight (no second softmax).
+ *
+ * The proxy weight set of whole expert e has Ip = N*r rounded up to a multiple
+ * of 128 rows: row n*r + i is gate neuron i of sub-expert N*e + n, the rows
+ * from N*r on are zero, so that the grouped FFN's gate/up call computes the
+ * activations of every routed (token, pick) pair.
+ *
+ * moe_proxy_pack: gathers the gate-neuron rows once per layer.
+ *   gate_idx  int32 [E][r]: neurons (rows of the sub-expert's w_gate / w_up);
+ *             one outside [0, I) packs as a zero row (its activation is 0)
+ *   w_gate, w_up  ELT [E][I][d];  wp_gate, wp_up  ELT [E/N][Ip][d] out
+ * moe_proxy_route: routes of the split layer from the proxy activations.
+ *   k       int32 [T] sub-expert budgets
+ *   kappa   int32 [k_max+1][m]: kappa vector of each budget k (0 <= kappa_j
+ *           <= N, sum_j kappa_j = k); a token with budget k_t runs k_t routes
+ *   base_tok_off, base_ids, base_w   the whole-expert routes (moe_route)
+ *   base_inv_perm  their inverse permutation (moe_permute on those routes)
+ *   hp      ELT [T*m][Ip]: moe_ffn_gateup's output on the permuted
+ *           whole-expert rows for a descriptor (T, d, E/N, Ip, m) and the
+ *           weights wp_gate / wp_up
+ *   tok_off int32 [T+1], topk_ids int32 [T*k_max], topk_w float [T*k_max] out
+ *           (CSR like moe_route's; within a pick, chosen sub-experts by score)
+ *   dev_status int32 [1] out or NULL: MOE_DEV_BAD_K for a k_t outside
+ *           [0, k_max] or whose kappa row has an entry outside [0, N] or does
+ *           not sum to k_t (such a token runs nothing)
+ * The scores are taken in float32 from the ELT activations, so sub-experts
+ * whose proxy scores differ by less than that rounding may rank either way.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (N, r, m out of range), MOE_ERR_ALIGN
+ * (moe_proxy_pack's weights), MOE_ERR_LAUNCH.
+ */
+/*
+ * moe_proxy_kappa_balanced (host only, no device call): the kappa table of
+ * moe_proxy_route with each budget k split as evenly as possible over the m
+ * picks, the remainder going to the earlier picks (higher router
+ * probability): kappa[k][j] = k / m + (j < k % m).
+ *   kappa  int32 [k_max+1][m] host memory, out.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (m < 1, N < 1, k_max < 0 or k_max > m*N).
+ */
+moe_status moe_proxy_kappa_balanced(int32_t k_max, int32_t m, int32_t N, int32_t* kappa);
+moe_status moe_proxy_pack(const moe_desc* desc, int32_t N, int32_t r, const int32_t* gate_idx,
+                          const void* w_gate, const void* w_up, void* wp_gate, void* wp_up,
+                          moe_stream_t stream);
+moe_status moe_proxy_route(const moe_desc* desc, int32_t N, int32_t r, int32_t m, const int32_t* k,
+                           const int32_t* kappa, const int32_t* base_tok_off, const int32_t* base_ids,
+                           const float* base_w, const int32_t* base_inv_perm, const void* hp,
+                           int32_t* tok_off, int32_t* topk_ids, float* topk_w, int32_t* dev_status,
+                           moe_stream_t stream);
+
+/*
  * Weighted combine back to token order:
  *   out[t] = sum_{j < k_t} topk_w[tok_off[t]+j] * y_perm[inv_perm[tok_off[t]+j]]
  *            (+ y_shared[t] when y_shared != NULL)

@@ -20,8 +20,10 @@ from ._lib import (MOE_BF16, MOE_DEV_BAD_K, MOE_F32, MOE_OP_COMBINE, MOE_OP_FFN,
 
 __all__ = [
     "MoeError", "make_desc", "workspace_size", "resolve_path", "alloc_workspace", "moe_route", "moe_permute",
-    "moe_ffn", "moe_ffn_plan", "moe_ffn_gateup", "moe_ffn_down", "moe_combine", "moe_fold", "moe_forward",
-    "forward",
+    "moe_ffn", "moe_ffn_plan", "moe_ffn_gateup", "moe_ffn_down", "moe_combine", "moe_fold", "moe_proxy_kappa_balanced",
+    "moe_proxy_pack",
+    "moe_proxy_route", "moe_forward",
+    "forward", "proxy_width", "proxy_pack", "ProxyRouter",
     "library_path",
 ]
 
@@ -144,6 +146,28 @@ def moe_fold(desc, mode: str, budget: int, S, L, H, tok_off, topk_ids, topk_w, e
         _ptr(w_out), _ptr(pool_out), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
+def moe_proxy_kappa_balanced(k_max: int, m: int, N: int) -> torch.Tensor:
+    """int32 [k_max+1][m] CPU tensor: each budget split evenly over the m
+    whole-expert picks, the remainder to the earlier picks."""
+    kappa = torch.empty((k_max + 1, m), dtype=torch.int32)
+    _check("moe_proxy_kappa_balanced", _lib.load().moe_proxy_kappa_balanced(k_max, m, N, _ptr(kappa)))
+    return kappa
+
+
+def moe_proxy_pack(desc, N: int, r: int, gate_idx, w_gate, w_up, wp_gate, wp_up, stream=None) -> None:
+    _check("moe_proxy_pack", _lib.load().moe_proxy_pack(
+        ctypes.byref(desc), N, r, _ptr(gate_idx), _ptr(w_gate), _ptr(w_up), _ptr(wp_gate), _ptr(wp_up),
+        _stream(stream)))
+
+
+def moe_proxy_route(desc, N: int, r: int, m: int, k, kappa, base_tok_off, base_ids, base_w, base_inv_perm, hp,
+                    tok_off, topk_ids, topk_w, dev_status, stream=None) -> None:
+    _check("moe_proxy_route", _lib.load().moe_proxy_route(
+        ctypes.byref(desc), N, r, m, _ptr(k), _ptr(kappa), _ptr(base_tok_off), _ptr(base_ids), _ptr(base_w),
+        _ptr(base_inv_perm), _ptr(hp), _ptr(tok_off), _ptr(topk_ids), _ptr(topk_w), _ptr(dev_status),
+        _stream(stream)))
+
+
 def moe_combine(desc, y_perm, y_shared, tok_off, topk_w, inv_perm, out, stream=None) -> None:
     _check("moe_combine", _lib.load().moe_combine(
         ctypes.byref(desc), _ptr(y_perm), _ptr(y_shared), _ptr(tok_off), _ptr(topk_w),
@@ -179,3 +203,71 @@ def forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: Optional[torch
     moe_forward(desc, x, w_router, router_bias, k, w_gate, w_up, w_down, sg, su, sd, out, stats,
                 status, ws, stream)
     return out, stats, status
+
+
+def proxy_width(N: int, r: int) -> int:
+    """Rows of one whole expert's packed proxy weights: N*r rounded up to 128."""
+    return (N * r + 127) // 128 * 128
+
+
+def proxy_pack(w_gate: torch.Tensor, w_up: torch.Tensor, gate_idx: torch.Tensor, N: int, stream=None):
+    """Allocate and fill the packed proxy weights (wp_gate, wp_up), each
+    [E/N, Ip, d], of a split layer with sub-expert weights [E, I, d]."""
+    E, I, d = w_gate.shape
+    r = gate_idx.shape[1]
+    desc = make_desc(0, d, E, I, 1, dtype=w_gate.dtype)
+    Ip = proxy_width(N, r)
+    wp_g = torch.empty((E // N, Ip, d), dtype=w_gate.dtype, device=w_gate.device)
+    wp_u = torch.empty_like(wp_g)
+    moe_proxy_pack(desc, N, r, gate_idx, w_gate, w_up, wp_g, wp_u, stream)
+    return wp_g, wp_u
+
+
+class ProxyRouter:
+    """Buffers and calls of proxy-gated routing for a fixed shape: the
+    whole-expert router (moe_route with every k_t = m), its permutation, the
+    proxy SwiGLU (moe_ffn_plan + moe_ffn_gateup on the packed weights) and
+    moe_proxy_route.  ``run`` only launches (no allocation), so it can be
+    captured in a HIP graph."""
+
+    def __init__(self, desc: moe_desc, N: int, r: int, m: int, kappa: torch.Tensor, device="cuda"):
+        self.desc, self.N, self.r, self.m = desc, N, r, m
+        T, d = desc.T, desc.d
+        self.Ip = proxy_width(N, r)
+        dtype = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}[desc.dtype]
+        self.base = make_desc(T, d, desc.E // N, self.Ip, m, dtype=dtype, routed_scale=desc.routed_scale)
+        i32 = dict(dtype=torch.int32, device=device)
+        A = max(T * m, 1)
+        self.kappa = kappa.to(device=device, dtype=torch.int32).contiguous()
+        self.k_base = torch.full((max(T, 1),), m, **i32)
+        self.b_tok_off = torch.empty(T + 1, **i32)
+        self.b_ids = torch.empty(A, **i32)
+        self.b_w = torch.empty(A, dtype=torch.float32, device=device)
+        self.b_status = torch.empty(1, **i32)
+        self.b_counts = torch.empty(self.base.E, **i32)
+        self.b_eoff = torch.empty(self.base.E + 1, **i32)
+        self.b_ptok = torch.empty(A, **i32)
+        self.b_psrc = torch.empty(A, **i32)
+        self.b_inv = torch.empty(A, **i32)
+        self.b_nact = torch.empty(1, **i32)
+        self.hp = torch.empty((A, self.Ip), dtype=dtype, device=device)
+        self.ws_route = alloc_workspace(self.base, MOE_OP_ROUTE, device)
+        self.ws_perm = alloc_workspace(self.base, MOE_OP_PERMUTE, device)
+        self.ws_ffn = alloc_workspace(self.base, MOE_OP_FFN, device)
+        km = desc.k_max
+        self.tok_off = torch.empty(T + 1, **i32)
+        self.ids = torch.empty(max(T * km, 1), **i32)
+        self.w = torch.empty(max(T * km, 1), dtype=torch.float32, device=device)
+        self.status = torch.empty(1, **i32)
+
+    def run(self, x, w_router_base, router_bias, k, wp_gate, wp_up, stream=None):
+        b = self.base
+        moe_route(b, x, w_router_base, router_bias, self.k_base, self.b_tok_off, self.b_ids, self.b_w,
+                  self.b_status, self.ws_route, stream)
+        moe_permute(b, self.b_tok_off, self.b_ids, self.b_counts, self.b_eoff, self.b_ptok, self.b_psrc,
+                    self.b_inv, self.b_nact, self.ws_perm, stream)
+        moe_ffn_plan(b, self.b_eoff, self.ws_ffn, stream)
+        moe_ffn_gateup(b, x, wp_gate, wp_up, self.b_eoff, self.b_ptok, self.hp, self.ws_ffn, stream)
+        moe_proxy_route(self.desc, self.N, self.r, self.m, k, self.kappa, self.b_tok_off, self.b_ids, self.b_w,
+                        self.b_inv, self.hp, self.tok_off, self.ids, self.w, self.status, stream)
+        return self.tok_off, self.ids, self.w, self.status

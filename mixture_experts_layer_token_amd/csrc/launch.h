@@ -117,4 +117,13 @@ hipError_t launch_fold(int mode, int budget, const float* S, const float* L, con
                        int E, int32_t* tok_off_out, int32_t* ids_out, float* w_out, int32_t* pool_out,
                        const FoldScratch& ws, hipStream_t st);
 
+// proxy.hip -- training-free proxy gating of a split layer.
+hipError_t launch_proxy_pack(int dtype, const int32_t* gate_idx, const void* wg, const void* wu, int E_base, int I_sub,
+                             int d, int N, int r, int Ip, void* pg, void* pu, hipStream_t st);
+hipError_t launch_proxy_route(int dtype, const int32_t* k, const int32_t* kappa, int T, int k_max, int m, int N, int r,
+                              int Ip,
+                              const int32_t* base_tok_off, const int32_t* base_ids, const float* base_w,
+                              const int32_t* base_inv, const void* hp, int E_base, int32_t* tok_off, int32_t* ids,
+                              float* wts, int32_t* status, hipStream_t st);
+
 }  // namespace moe

@@ -427,6 +427,52 @@ moe_status moe_fold(const moe_desc* desc, int32_t mode, int32_t budget, const fl
                               tok_off_out, ids_out, w_out, pool_out, fw, static_cast<hipStream_t>(stream)));
 }
 
+static int proxy_width(int32_t N, int32_t r) {
+  return (int)(((int64_t)N * r + kDimQuantum - 1) / kDimQuantum * kDimQuantum);
+}
+
+static moe_status proxy_shape(const moe_desc& d, int32_t N, int32_t r, int32_t m) {
+  if (N < 1 || r < 1 || r > d.I || m < 1 || d.E % N || (int64_t)m * N > 64 || m > d.E / N ||
+      d.k_max > m * N || (int64_t)N * r > 65536)
+    return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+moe_status moe_proxy_kappa_balanced(int32_t k_max, int32_t m, int32_t N, int32_t* kappa) {
+  if (!kappa) return MOE_ERR_NULL;
+  if (m < 1 || N < 1 || k_max < 0 || (int64_t)k_max > (int64_t)m * N) return MOE_ERR_SHAPE;
+  for (int32_t k = 0; k <= k_max; ++k)
+    for (int32_t j = 0; j < m; ++j) kappa[(size_t)k * m + j] = k / m + (j < k % m ? 1 : 0);
+  return MOE_OK;
+}
+
+moe_status moe_proxy_pack(const moe_desc* desc, int32_t N, int32_t r, const int32_t* gate_idx, const void* w_gate,
+                          const void* w_up, void* wp_gate, void* wp_up, moe_stream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  if (N < 1 || r < 1 || r > d.I || d.E % N || (int64_t)N * r > 65536) return MOE_ERR_SHAPE;
+  if (!gate_idx || !w_gate || !w_up || !wp_gate || !wp_up) return MOE_ERR_NULL;
+  if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(wp_gate) || !aligned16(wp_up)) return MOE_ERR_ALIGN;
+  return launched(launch_proxy_pack(d.dtype, gate_idx, w_gate, w_up, d.E / N, d.I, d.d, N, r, proxy_width(N, r),
+                                    wp_gate, wp_up, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_proxy_route(const moe_desc* desc, int32_t N, int32_t r, int32_t m, const int32_t* k,
+                           const int32_t* kappa, const int32_t* base_tok_off, const int32_t* base_ids,
+                           const float* base_w, const int32_t* base_inv_perm, const void* hp, int32_t* tok_off,
+                           int32_t* topk_ids, float* topk_w, int32_t* dev_status, moe_stream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  MOE_TRY(proxy_shape(d, N, r, m));
+  if (!kappa || !tok_off || !tok_ptr(d, k) || !tok_ptr(d, base_tok_off) || !tok_ptr(d, base_ids) ||
+      !tok_ptr(d, base_w) || !tok_ptr(d, base_inv_perm) || !tok_ptr(d, hp) || !tok_ptr(d, topk_ids) ||
+      !tok_ptr(d, topk_w))
+    return MOE_ERR_NULL;
+  return launched(launch_proxy_route(d.dtype, k, kappa, d.T, d.k_max, m, N, r, proxy_width(N, r), base_tok_off,
+                                     base_ids, base_w, base_inv_perm, hp, d.E / N, tok_off, topk_ids, topk_w,
+                                     dev_status, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router, const float* router_bias,
                        const int32_t* k, const void* w_gate, const void* w_up, const void* w_down,
                        const void* ws_gate, const void* ws_up, const void* ws_down, void* out, int32_t* stats,

@@ -126,3 +126,39 @@ def test_fold_validates_before_launch():
     assert lib.moe_fold(*args(0, 2)) == 4                      # workspace missing
     st, n = _ws(d, moe.MOE_OP_FOLD)
     assert st == 0 and n > 0 and n <= _ws(d, moe.MOE_OP_FORWARD)[1]
+
+
+def test_proxy_kappa_table_matches_oracle():
+    """The library's host-side kappa table against the oracle's balanced split."""
+    import oracle
+    for k_max, m, N in [(32, 8, 4), (7, 3, 4), (1, 1, 1), (0, 2, 2), (64, 16, 4), (12, 4, 3)]:
+        got = moe.moe_proxy_kappa_balanced(k_max, m, N).tolist()
+        assert got == [oracle.kappa_balanced(k, m, N) for k in range(k_max + 1)]
+    for k_max, m, N in [(9, 2, 4), (1, 0, 4), (1, 2, 0), (-1, 2, 2)]:
+        with pytest.raises(moe.MoeError):
+            moe.moe_proxy_kappa_balanced(k_max, m, N)
+    assert _lib.load().moe_proxy_kappa_balanced(4, 2, 2, None) == 1
+
+
+def test_proxy_validates_before_launch():
+    lib = _lib.load()
+    d = _desc(T=4, d=128, E=16, I=128, k_max=8)
+    P = lambda v: ctypes.c_void_p(v)
+    x = P(1 << 20)  # never dereferenced: every call below fails validation first
+    route = lambda N, r, m, desc=d, **kw: lib.moe_proxy_route(
+        ctypes.byref(desc), N, r, m, *[kw.get(n, x) for n in ("k", "kappa", "bto", "bids", "bw", "binv", "hp",
+                                                               "to", "ids", "w")], None, None)
+    assert route(3, 8, 4) == 2                     # E not a multiple of N
+    assert route(4, 8, 1) == 2                     # k_max > m*N
+    assert route(4, 0, 2) == 2                     # r < 1
+    assert route(4, 8, 5) == 2                     # m > E/N
+    assert route(4, 129, 2) == 2                   # r > I
+    big = _desc(T=4, d=128, E=256, I=128, k_max=8)
+    assert route(4, 8, 17, desc=big) == 2          # m*N > 64
+    assert route(4, 8, 2, hp=None) == 1
+    assert route(4, 8, 2, kappa=None) == 1
+    pack = lambda N, r, **kw: lib.moe_proxy_pack(ctypes.byref(d), N, r, *[kw.get(n, x) for n in (
+        "gi", "wg", "wu", "pg", "pu")], None)
+    assert pack(3, 8) == 2
+    assert pack(4, 8, gi=None) == 1
+    assert pack(4, 8, pg=P((1 << 20) + 2)) == 5

@@ -61,6 +61,7 @@ __all__ = [
     "ExpertView",
     "draw_k_eq7",
     "make_fold_tables",
+    "make_proxy_inputs",
 ]
 
 
@@ -305,3 +306,18 @@ class ExpertView:
 
     def __len__(self) -> int:
         return self.stacked.shape[0]
+
+
+def make_proxy_inputs(cfg: LayerConfig, r: int, device="cpu"):
+    """Inputs of proxy gating on a split layer (cfg.split = N sub-experts per
+    whole expert): the whole-expert router w_router_base [E/N][d] (same law as
+    the layer's router) and gate_idx int32 [E][r], r distinct neurons of each
+    sub-expert drawn uniformly and sorted (a stand-in for the neurons a
+    co-activation calibration would keep, which needs a model and data)."""
+    device = torch.device(device)
+    dt = torch_dtype(cfg.dtype)
+    w_base = _gauss((cfg.E_base, cfg.d), 1.0 / math.sqrt(cfg.d), derived_seed(cfg.seed, "w_router", 1), device, dt)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(derived_seed(cfg.seed, "k", 13))
+    idx = torch.stack([torch.sort(torch.randperm(cfg.I, generator=g)[:r]).values for _ in range(cfg.E)])
+    return w_base, idx.to(torch.int32).to(device)
