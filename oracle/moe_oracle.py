@@ -31,6 +31,10 @@ precision):
 * Proxy gating of a split layer (MoE-Prism §III-B2, training-free path):
   whole-expert routing, then the top kappa_j sub-experts by a gate-neuron
   proxy score, each inheriting its expert's weight (proxy_route).
+* Compositional paths (PCoMoE, arXiv 2609.01024): scores over a fixed active
+  path mask, per-token top-k_t paths, and the source-grouped output in which
+  each distinct source's expansion runs once (path_route, path_sources,
+  path_forward).
 * Expert FFN: SwiGLU, §III-B1 Eq. (1): A = SiLU(X W_gate) * (X W_up) and
   X' = A W_down, with SiLU(z) = z * sigmoid(z).  Weights are stored in the
   [out, in] layout, so X W_gate of the page is x @ w_gate[e].T here.
@@ -61,6 +65,10 @@ __all__ = [
     "kappa_balanced",
     "proxy_scores",
     "proxy_route",
+    "path_scores",
+    "path_route",
+    "path_sources",
+    "path_forward",
     "router_logits",
     "select_experts",
     "route",
@@ -468,6 +476,118 @@ def proxy_route(x, w_router_base, bias, k, k_max: int, m: int, N: int, kappa, ga
         rows.append(row)
     tok_off, ids, w = _csr(rows)
     return {"tok_off": tok_off, "ids": ids, "w": w, "status": status, "scores": scores, "base": base}
+
+
+# ---------------------------------------------------------------------------
+# Compositional path routing and source-grouped execution (PCoMoE, arXiv
+# 2609.01024).  Expert e splits at its expansion/projection boundary into
+# U_e(h) = SiLU(W_gate[e] h) * (W_up[e] h) and D_e(z) = W_down[e] z, so that
+# F_e = D_e(U_e); a path (i, j) is D_j(U_i(h)) and the diagonal (e, e) is the
+# vanilla expert.  Only the active paths of a fixed mask are candidates.
+
+def path_scores(g_row, t_row, p_src, p_tgt, p_bias, lam: float) -> np.ndarray:
+    """Scores of the active paths of one token (compatibility-aware path
+    gating, Fig. 7): the source's base routing logit plus the pair's
+    compatibility bias plus lambda times the target's prior logit,
+        s_p = fp32( (g[src_p] + b_p) + lam * t[tgt_p] )
+    evaluated in float64 in that order and rounded once to float32.  t_row
+    None drops the target term."""
+    g = _f64(g_row)[np.asarray(p_src, dtype=np.int64)]
+    acc = g + _f64(p_bias)
+    if t_row is not None:
+        acc = acc + float(lam) * _f64(t_row)[np.asarray(p_tgt, dtype=np.int64)]
+    return acc.astype(np.float32)
+
+
+def path_route(x, w_router, bias, w_tgt, lam: float, p_src, p_tgt, p_bias, k, k_max: int,
+               routed_scale: float = 1.0):
+    """Per-token top-k_t over the active paths (compositional path routing).
+
+    The active set is the list (p_src, p_tgt, p_bias), strictly increasing in
+    (src, tgt).  g are the router logits of w_router (+ bias) and t those of
+    w_tgt (no bias; None drops the term), both under the routing contract of
+    router_logits.  The k_t paths with the largest scores are taken, equal
+    scores in list order; their weights are the softmax over the selected
+    scores times routed_scale (the vanilla renormalised softmax, which the
+    diagonal-only mask reproduces exactly).  A k_t outside [0, k_max] runs
+    nothing and sets status 1.  Returns a dict with tok_off, src, tgt, w
+    (float64), status and the scores [T][P]."""
+    k = np.asarray(k, dtype=np.int64)
+    T = k.shape[0]
+    P = len(p_src)
+    g = router_logits(x, w_router, bias)
+    t = router_logits(x, w_tgt, None) if w_tgt is not None else None
+    status = int(((k < 0) | (k > k_max)).any())
+    scores = np.zeros((T, P), dtype=np.float32)
+    rows = []
+    for tt in range(T):
+        s = path_scores(g[tt], None if t is None else t[tt], p_src, p_tgt, p_bias, lam)
+        scores[tt] = s
+        kt = int(k[tt])
+        row = []
+        if 0 <= kt <= k_max:
+            order = np.argsort(-s, kind="stable")[:kt]
+            sel = s[order].astype(np.float64)
+            p = np.exp(sel - sel[0]) if kt else sel
+            for q, idx in enumerate(order):
+                row.append((int(p_src[idx]), int(p_tgt[idx]), routed_scale * p[q] / p.sum()))
+        rows.append(row)
+    tok_off = np.zeros(T + 1, dtype=np.int64)
+    tok_off[1:] = np.cumsum([len(r) for r in rows])
+    src = np.array([a for r in rows for a, _, _ in r], dtype=np.int64)
+    tgt = np.array([b for r in rows for _, b, _ in r], dtype=np.int64)
+    w = np.array([c for r in rows for _, _, c in r], dtype=np.float64)
+    return {"tok_off": tok_off, "src": src, "tgt": tgt, "w": w, "status": status, "scores": scores}
+
+
+def path_sources(tok_off, src):
+    """Source groups (source-grouped compute reuse, Fig. 8): per token, the
+    distinct sources of its paths in ascending order.  Returns (src_tok_off,
+    src_ids, path_src_route) where path_src_route[a] is the source route of
+    path a."""
+    tok_off = np.asarray(tok_off, dtype=np.int64)
+    src = np.asarray(src, dtype=np.int64)
+    T = tok_off.shape[0] - 1
+    s_off = np.zeros(T + 1, dtype=np.int64)
+    ids, p2s = [], np.zeros(src.shape[0], dtype=np.int64)
+    for t in range(T):
+        mine = src[tok_off[t]:tok_off[t + 1]]
+        uniq = sorted(set(int(v) for v in mine))
+        for a in range(int(tok_off[t]), int(tok_off[t + 1])):
+            p2s[a] = len(ids) + uniq.index(int(src[a]))
+        ids += uniq
+        s_off[t + 1] = len(ids)
+    return s_off, np.array(ids, dtype=np.int64), p2s
+
+
+def path_forward(x, tok_off, src, tgt, w, w_gate, w_up, w_down, tokens: Optional[Sequence[int]] = None,
+                 counter: Optional[dict] = None) -> np.ndarray:
+    """Layer output over paths, source-grouped: for each token, U_i runs once
+    per distinct source i and D_j once per path (i, j):
+        y = sum_i sum_{j in T_i} beta_ij D_j(U_i(h)).
+    counter, if given, receives the number of U and D evaluations."""
+    x = np.asarray(x)
+    tok_off = np.asarray(tok_off, dtype=np.int64)
+    if tokens is None:
+        tokens = np.arange(x.shape[0])
+    tokens = np.asarray(tokens, dtype=np.int64)
+    out = np.zeros((len(tokens), x.shape[1]), dtype=np.float64)
+    n_u = n_d = 0
+    for r, t in enumerate(tokens):
+        h = _f64(x[t])
+        groups = {}
+        for a in range(int(tok_off[t]), int(tok_off[t + 1])):
+            groups.setdefault(int(src[a]), []).append((int(tgt[a]), float(w[a])))
+        for i, paths in groups.items():
+            z = silu(_f64(w_gate[i]) @ h) * (_f64(w_up[i]) @ h)
+            n_u += 1
+            for j, b in paths:
+                out[r] += b * (_f64(w_down[j]) @ z)
+                n_d += 1
+    if counter is not None:
+        counter["U"] = n_u
+        counter["D"] = n_d
+    return out
 
 
 def activated_weight_bytes(n_active: int, d: int, I: int, elem_bytes: int) -> int:

@@ -612,3 +612,107 @@ def test_proxy_route_rejects_vectors_off_the_budget():
         got = r_bad["ids"][r_bad["tok_off"][t]:r_bad["tok_off"][t + 1]].tolist()
         ref = r_good["ids"][r_good["tok_off"][t]:r_good["tok_off"][t + 1]].tolist()
         assert got == ([] if k[t] in (4, 5) else ref)
+
+
+# ---------------------------------------------------------------- compositional paths (PCoMoE)
+
+def test_path_route_hand_worked():
+    g = json.load(open(os.path.join(HERE, "golden", "path_hand_worked.json")))
+    arr = lambda v: np.array(v, dtype=np.float64)
+    P = np.array(g["paths"], dtype=np.float64)
+    r = oracle.path_route(arr(g["x"]), arr(g["w_router"]), None, arr(g["w_tgt"]), g["lam"], P[:, 0].astype(int),
+                          P[:, 1].astype(int), P[:, 2], np.array(g["k"]), g["k_max"], g["routed_scale"])
+    assert r["tok_off"].tolist() == g["tok_off"]
+    assert r["src"].tolist() == g["src"] and r["tgt"].tolist() == g["tgt"]
+    np.testing.assert_allclose(r["w"], g["w"], rtol=1e-15)
+    assert r["status"] == g["status"]
+    s_off, s_ids, p2s = oracle.path_sources(r["tok_off"], r["src"])
+    assert s_off.tolist() == g["src_tok_off"] and s_ids.tolist() == g["src_ids"]
+    assert p2s.tolist() == g["path_src_route"]
+
+
+def _path_layer(seed, E=6, d=24, I=16, T=11):
+    L = make_custom_layer(T=T, d=d, E=E, I=I, k=[2] * T, seed=seed)
+    a = _arrays(L)
+    rng = np.random.default_rng(seed)
+    a["w_tgt"] = rng.standard_normal((E, d)) / math.sqrt(d)
+    return a
+
+
+def test_path_diagonal_mask_reproduces_vanilla():
+    """Diagonal-only paths with zero biases and no target term (or lambda = 0)
+    give the vanilla routes and weights bit for bit, and the vanilla output
+    (PCoMoE: restricting to diagonal paths recovers the original layer)."""
+    E, T = 6, 11
+    a = _path_layer(41, E=E, T=T)
+    k = np.array([0, 1, 2, 3, 6, 4, 2, 1, 5, 3, 2])
+    diag = np.arange(E)
+    ref = oracle.route(a["x"], a["w_router"], a["bias"], k, E, 1.5)
+    for w_tgt, lam in ((None, 0.7), (a["w_tgt"], 0.0)):
+        r = oracle.path_route(a["x"], a["w_router"], a["bias"], w_tgt, lam, diag, diag, np.zeros(E), k, E, 1.5)
+        assert (r["tok_off"] == ref["tok_off"]).all()
+        assert (r["src"] == ref["ids"]).all() and (r["tgt"] == ref["ids"]).all()
+        assert (r["w"] == ref["w"]).all()
+    out = oracle.path_forward(a["x"], r["tok_off"], r["src"], r["tgt"], r["w"], a["w_gate"], a["w_up"], a["w_down"])
+    want, _ = oracle.forward(a["x"], a["w_router"], a["bias"], k, E, a["w_gate"], a["w_up"], a["w_down"],
+                             routed_scale=1.5)
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-14)
+
+
+def test_path_forward_is_the_sum_over_paths():
+    """Source-grouped evaluation equals the plain sum over paths of
+    beta * W_down[j] (SiLU(W_gate[i] h) * (W_up[i] h)), each path on its own
+    (scipy's logistic function), and runs U once per distinct source."""
+    E = 6
+    a = _path_layer(42, E=E)
+    src = np.array([0, 0, 1, 2, 2, 5, 3, 3, 3, 4, 1])
+    tgt = np.array([0, 3, 1, 2, 0, 5, 3, 1, 4, 4, 2])
+    p_bias = np.linspace(-0.5, 0.3, len(src))
+    k = np.array([3, 4, 0, 2, 5, 1, 3, 2, 6, 4, 3])
+    r = oracle.path_route(a["x"], a["w_router"], None, a["w_tgt"], 0.4, src, tgt, p_bias, k, 6)
+    cnt = {}
+    got = oracle.path_forward(a["x"], r["tok_off"], r["src"], r["tgt"], r["w"], a["w_gate"], a["w_up"],
+                              a["w_down"], counter=cnt)
+    want = np.zeros_like(got)
+    n_src = 0
+    for t in range(a["x"].shape[0]):
+        lo, hi = r["tok_off"][t], r["tok_off"][t + 1]
+        n_src += len(set(r["src"][lo:hi].tolist()))
+        for q in range(lo, hi):
+            i, j = r["src"][q], r["tgt"][q]
+            gl = a["w_gate"][i] @ a["x"][t]
+            z = gl * scipy.special.expit(gl) * (a["w_up"][i] @ a["x"][t])
+            want[t] += r["w"][q] * (a["w_down"][j] @ z)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+    assert cnt == {"U": n_src, "D": int(r["tok_off"][-1])}
+    assert n_src < r["tok_off"][-1]           # some paths share their source
+
+
+def test_path_route_invariances():
+    """A constant added to every pair bias changes no selection and no
+    weight (softmax shift invariance, up to the one float32 rounding); a large
+    bias on one pair puts it first for every token with k_t >= 1; every
+    selection is the top k_t of the scores."""
+    E = 6
+    a = _path_layer(43, E=E)
+    src = np.array([0, 0, 1, 1, 2, 3, 3, 4, 5, 5])
+    tgt = np.array([0, 4, 1, 2, 2, 3, 0, 4, 1, 5])
+    p_bias = np.array([0, -0.3, 0, -0.1, 0, 0, -0.2, 0, -0.4, 0])
+    k = np.array([1, 2, 3, 4, 5, 6, 7, 8, 2, 3, 1])
+    base = oracle.path_route(a["x"], a["w_router"], None, a["w_tgt"], 0.6, src, tgt, p_bias, k, 10)
+    shifted = oracle.path_route(a["x"], a["w_router"], None, a["w_tgt"], 0.6, src, tgt, p_bias + 0.25, k, 10)
+    assert (base["src"] == shifted["src"]).all() and (base["tgt"] == shifted["tgt"]).all()
+    np.testing.assert_allclose(base["w"], shifted["w"], rtol=1e-6)
+    boosted = p_bias.copy()
+    boosted[6] = 50.0
+    b = oracle.path_route(a["x"], a["w_router"], None, a["w_tgt"], 0.6, src, tgt, boosted, k, 10)
+    for t in range(len(k)):
+        assert (b["src"][b["tok_off"][t]], b["tgt"][b["tok_off"][t]]) == (3, 0)
+    for t in range(len(k)):
+        s = base["scores"][t]
+        chosen = base["src"][base["tok_off"][t]:base["tok_off"][t + 1]] * E + \
+            base["tgt"][base["tok_off"][t]:base["tok_off"][t + 1]]
+        pos = [int(np.nonzero(src * E + tgt == c)[0][0]) for c in chosen]
+        rest = [p for p in range(len(src)) if p not in pos]
+        assert all(s[p] >= s[q] for p in pos for q in rest)
+        assert all(s[pos[i]] >= s[pos[i + 1]] for i in range(len(pos) - 1))
