@@ -103,7 +103,8 @@ typedef enum {
   MOE_OP_FFN = 2,
   MOE_OP_COMBINE = 3,
   MOE_OP_FORWARD = 4,
-  MOE_OP_FOLD = 5
+  MOE_OP_FOLD = 5,
+  MOE_OP_PATH = 6   /* moe_path_route and moe_path_sources */
 } moe_op;
 
 /* Expert-folding selectors, for moe_fold. */
@@ -338,6 +339,70 @@ moe_status moe_proxy_route(const moe_desc* desc, int32_t N, int32_t r, int32_t m
                            const float* base_w, const int32_t* base_inv_perm, const void* hp,
                            int32_t* tok_off, int32_t* topk_ids, float* topk_w, int32_t* dev_status,
                            moe_stream_t stream);
+
+/*
+ * Compositional paths (PCoMoE, arXiv 2609.01024).  Expert e splits at its
+ * expansion/projection boundary into U_e(h) = SiLU(h . w_gate[e]) * (h .
+ * w_up[e]) and D_e(z) = z . w_down[e]; a path (i, j) is D_j(U_i(h)), and the
+ * diagonal (e, e) is the vanilla expert.  A fixed list of active paths (the
+ * pruned mask, materialised offline) holds the candidates; a token runs its
+ * k_t best paths (k_t counted in paths, k_max <= 64 and <= the list length),
+ * and each distinct source's expansion runs once per token (source-grouped
+ * reuse):  out = sum_i sum_{j in T_i} beta_ij D_j(U_i(h)).
+ *
+ * moe_path_table_bytes / moe_path_table: validate the active list on the host
+ * and upload it (once per layer).  src, tgt int32 [P] and bias float [P] are
+ * host arrays: 1 <= P <= 1024, entries in [0, E), (src, tgt) strictly
+ * increasing, biases finite.  `table` is device memory of
+ * moe_path_table_bytes(P) bytes (16-byte aligned); the call returns once the
+ * copy is complete.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (any rule above),
+ * MOE_ERR_ALIGN, MOE_ERR_LAUNCH.
+ *
+ * moe_path_route: per token, the router logits g = x . w_router^T (+ bias) and,
+ * when w_tgt is not NULL, the target prior t = x . w_tgt^T, both under
+ * moe_route's contract (float64 accumulation, one rounding to float32); path
+ * scores s_p = fp32((g[src_p] + bias_p) + lambda * t[tgt_p]) in float64
+ * (compatibility-aware path gating, Fig. 7); the k_t best paths (score
+ * descending, equal scores in list order) with weights beta = routed_scale *
+ * softmax over the selected scores (the renormalised softmax, so the
+ * diagonal-only list with zero biases reproduces moe_route exactly).
+ *   w_tgt     ELT [E][d] or NULL; lambda ignored when NULL
+ *   k         int32 [T]; budgets follow desc.k_policy as in moe_route
+ *   tok_off   int32 [T+1] out; path_src, path_tgt int32 [T*k_max] out;
+ *   path_w    float [T*k_max] out; dev_status as in moe_route
+ *   ws        scratch of moe_workspace_size(MOE_OP_PATH) bytes
+ * moe_path_sources: the source groups (Fig. 8): per token its distinct
+ * sources in ascending order (src_tok_off int32 [T+1], src_ids int32
+ * [T*k_max]), the source route of every path (path_src_route int32
+ * [T*k_max]), and unit_off int32 [T*k_max+1] = min(a, A): the offsets of the
+ * paths taken one per row, for moe_permute of path_tgt under a descriptor of
+ * T*k_max tokens with k_max = 1 (a token may reach one target through two
+ * sources).  ws: as moe_path_route's.
+ * moe_path_rows: row_map[q] = src_inv_perm[path_src_route[perm_path[q]]] for
+ * q < A = tok_off[T]: the expansion row (of moe_ffn_gateup over the source
+ * routes) that target-ordered path row q reads; perm_path is the perm_tok of
+ * the one-per-row permutation above (its "tokens" are the paths).
+ * moe_ffn_down_rows: moe_ffn_down where permuted row p reads h row
+ * row_map[p] (int32 [T*k_max]).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (k_max > 64 or > P, P out of range,
+ * lambda not finite), MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH.
+ */
+moe_status moe_path_table_bytes(int32_t P, size_t* bytes);
+moe_status moe_path_table(int32_t E, int32_t P, const int32_t* src, const int32_t* tgt, const float* bias,
+                          void* table, size_t table_bytes, moe_stream_t stream);
+moe_status moe_path_route(const moe_desc* desc, const void* x, const void* w_router, const float* router_bias,
+                          const void* w_tgt, float lambda, const void* table, int32_t P, const int32_t* k,
+                          int32_t* tok_off, int32_t* path_src, int32_t* path_tgt, float* path_w,
+                          int32_t* dev_status, void* ws, size_t ws_bytes, moe_stream_t stream);
+moe_status moe_path_sources(const moe_desc* desc, const int32_t* tok_off, const int32_t* path_src,
+                            int32_t* src_tok_off, int32_t* src_ids, int32_t* path_src_route, int32_t* unit_off,
+                            void* ws, size_t ws_bytes, moe_stream_t stream);
+moe_status moe_path_rows(const moe_desc* desc, const int32_t* tok_off, const int32_t* perm_path,
+                         const int32_t* path_src_route, const int32_t* src_inv_perm, int32_t* row_map,
+                         moe_stream_t stream);
+moe_status moe_ffn_down_rows(const moe_desc* desc, const void* h, const int32_t* row_map, const void* w_down,
+                             const int32_t* expert_off, void* y_perm, void* ws, size_t ws_bytes,
+                             moe_stream_t stream);
 
 /*
  * Weighted combine back to token order:

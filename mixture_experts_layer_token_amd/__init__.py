@@ -16,12 +16,13 @@ from . import _lib
 from ._lib import (MOE_BF16, MOE_DEV_BAD_K, MOE_F32, MOE_OP_COMBINE, MOE_OP_FFN,  # noqa: F401
                    MOE_OP_FORWARD, MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_PATH_AUTO, MOE_PATH_GEMM,
                    MOE_PATH_STREAM, MOE_ROUTER_AUTO, MOE_ROUTER_FLOAT64, MOE_ROUTER_SCREENED, MOE_K_EXACT,
-                   MOE_K_BATCH_MAX, MOE_K_ROUND_UP, MOE_OP_FOLD, MOE_FOLD_TOKEN, MOE_FOLD_POOL, moe_desc)
+                   MOE_K_BATCH_MAX, MOE_K_ROUND_UP, MOE_OP_FOLD, MOE_OP_PATH, MOE_FOLD_TOKEN, MOE_FOLD_POOL, moe_desc)
 
 __all__ = [
     "MoeError", "make_desc", "workspace_size", "resolve_path", "alloc_workspace", "moe_route", "moe_permute",
     "moe_ffn", "moe_ffn_plan", "moe_ffn_gateup", "moe_ffn_down", "moe_combine", "moe_fold", "moe_proxy_kappa_balanced",
-    "moe_proxy_pack",
+    "moe_proxy_pack", "moe_path_table", "moe_path_route", "moe_path_sources", "moe_path_rows", "moe_ffn_down_rows",
+    "PathLayer",
     "moe_proxy_route", "moe_forward",
     "forward", "proxy_width", "proxy_pack", "ProxyRouter",
     "library_path",
@@ -271,3 +272,101 @@ class ProxyRouter:
         moe_proxy_route(self.desc, self.N, self.r, self.m, k, self.kappa, self.b_tok_off, self.b_ids, self.b_w,
                         self.b_inv, self.hp, self.tok_off, self.ids, self.w, self.status, stream)
         return self.tok_off, self.ids, self.w, self.status
+
+
+def moe_path_table(E: int, src, tgt, bias, device="cuda", stream=None) -> torch.Tensor:
+    """Validate the active path list (host sequences, strictly increasing
+    (src, tgt)) and upload it; returns the device table (uint8 tensor)."""
+    P = len(src)
+    n = ctypes.c_size_t(0)
+    _check("moe_path_table_bytes", _lib.load().moe_path_table_bytes(P, ctypes.byref(n)))
+    s = torch.as_tensor(src, dtype=torch.int32).contiguous()
+    t = torch.as_tensor(tgt, dtype=torch.int32).contiguous()
+    b = torch.as_tensor(bias, dtype=torch.float32).contiguous()
+    table = torch.empty(n.value, dtype=torch.uint8, device=device)
+    _check("moe_path_table", _lib.load().moe_path_table(E, P, _ptr(s), _ptr(t), _ptr(b), _ptr(table), n.value,
+                                                         _stream(stream)))
+    return table
+
+
+def moe_path_route(desc, x, w_router, router_bias, w_tgt, lam: float, table, P: int, k, tok_off, path_src, path_tgt,
+                   path_w, dev_status, ws, stream=None) -> None:
+    _check("moe_path_route", _lib.load().moe_path_route(
+        ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_tgt), lam, _ptr(table), P, _ptr(k),
+        _ptr(tok_off), _ptr(path_src), _ptr(path_tgt), _ptr(path_w), _ptr(dev_status), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
+
+
+def moe_path_sources(desc, tok_off, path_src, src_tok_off, src_ids, path_src_route, unit_off, ws,
+                     stream=None) -> None:
+    _check("moe_path_sources", _lib.load().moe_path_sources(
+        ctypes.byref(desc), _ptr(tok_off), _ptr(path_src), _ptr(src_tok_off), _ptr(src_ids), _ptr(path_src_route),
+        _ptr(unit_off), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_path_rows(desc, tok_off, perm_path, path_src_route, src_inv_perm, row_map, stream=None) -> None:
+    _check("moe_path_rows", _lib.load().moe_path_rows(
+        ctypes.byref(desc), _ptr(tok_off), _ptr(perm_path), _ptr(path_src_route), _ptr(src_inv_perm), _ptr(row_map),
+        _stream(stream)))
+
+
+def moe_ffn_down_rows(desc, h, row_map, w_down, expert_off, y_perm, ws, stream=None) -> None:
+    _check("moe_ffn_down_rows", _lib.load().moe_ffn_down_rows(
+        ctypes.byref(desc), _ptr(h), _ptr(row_map), _ptr(w_down), _ptr(expert_off), _ptr(y_perm), _ptr(ws),
+        _nbytes(ws), _stream(stream)))
+
+
+class PathLayer:
+    """Buffers and calls of the compositional-path layer for a fixed shape:
+    path routing, source groups, the expansions over the source routes
+    (permute + gate/up), the projections over the paths grouped by target
+    (one-per-row permute, row map, down with row gather) and the combine.
+    ``run`` only launches (no allocation), so it can be captured in a graph."""
+
+    def __init__(self, desc: moe_desc, table: torch.Tensor, P: int, lam: float = 0.0, device="cuda"):
+        self.desc, self.table, self.P, self.lam = desc, table, P, float(lam)
+        T, d, E, I, km = desc.T, desc.d, desc.E, desc.I, desc.k_max
+        dtype = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}[desc.dtype]
+        # the paths one per row: T*k_max "tokens" of one route each
+        self.unit = moe_desc(T * km, d, E, I, 1, 0, desc.dtype, desc.path, desc.router, desc.routed_scale,
+                             MOE_K_EXACT, 1)
+        i32 = dict(dtype=torch.int32, device=device)
+        A = max(T * km, 1)
+        self.tok_off = torch.empty(T + 1, **i32)
+        self.src = torch.empty(A, **i32)
+        self.tgt = torch.empty(A, **i32)
+        self.w = torch.empty(A, dtype=torch.float32, device=device)
+        self.status = torch.empty(1, **i32)
+        self.src_off = torch.empty(T + 1, **i32)
+        self.src_ids = torch.empty(A, **i32)
+        self.p2s = torch.empty(A, **i32)
+        self.unit_off = torch.empty(T * km + 1, **i32)
+        self.s_counts, self.t_counts = torch.empty(E, **i32), torch.empty(E, **i32)
+        self.s_eoff, self.t_eoff = torch.empty(E + 1, **i32), torch.empty(E + 1, **i32)
+        self.s_ptok, self.s_psrc, self.s_inv = (torch.empty(A, **i32) for _ in range(3))
+        self.t_ptok, self.t_psrc, self.t_inv = (torch.empty(A, **i32) for _ in range(3))
+        self.s_nact, self.t_nact = torch.empty(1, **i32), torch.empty(1, **i32)
+        self.row_map = torch.empty(A, **i32)
+        self.h = torch.empty((A, I), dtype=dtype, device=device)
+        self.y = torch.empty((A, d), dtype=dtype, device=device)
+        self.ws_path = alloc_workspace(desc, MOE_OP_PATH, device)
+        self.ws_perm = alloc_workspace(desc, MOE_OP_PERMUTE, device)
+        self.ws_uperm = alloc_workspace(self.unit, MOE_OP_PERMUTE, device)
+        self.ws_ffn = alloc_workspace(desc, MOE_OP_FFN, device)
+
+    def run(self, x, w_router, router_bias, w_tgt, k, w_gate, w_up, w_down, out, stream=None):
+        d, u = self.desc, self.unit
+        moe_path_route(d, x, w_router, router_bias, w_tgt, self.lam, self.table, self.P, k, self.tok_off, self.src,
+                       self.tgt, self.w, self.status, self.ws_path, stream)
+        moe_path_sources(d, self.tok_off, self.src, self.src_off, self.src_ids, self.p2s, self.unit_off,
+                         self.ws_path, stream)
+        moe_permute(d, self.src_off, self.src_ids, self.s_counts, self.s_eoff, self.s_ptok, self.s_psrc, self.s_inv,
+                    self.s_nact, self.ws_perm, stream)
+        moe_ffn_plan(d, self.s_eoff, self.ws_ffn, stream)
+        moe_ffn_gateup(d, x, w_gate, w_up, self.s_eoff, self.s_ptok, self.h, self.ws_ffn, stream)
+        moe_permute(u, self.unit_off, self.tgt, self.t_counts, self.t_eoff, self.t_ptok, self.t_psrc, self.t_inv,
+                    self.t_nact, self.ws_uperm, stream)
+        moe_path_rows(d, self.tok_off, self.t_ptok, self.p2s, self.s_inv, self.row_map, stream)
+        moe_ffn_plan(u, self.t_eoff, self.ws_ffn, stream)
+        moe_ffn_down_rows(u, self.h, self.row_map, w_down, self.t_eoff, self.y, self.ws_ffn, stream)
+        moe_combine(d, self.y, None, self.tok_off, self.w, self.t_inv, out, stream)

@@ -14,7 +14,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_GEMM = 0, 1, 2
 MOE_ROUTER_AUTO, MOE_ROUTER_FLOAT64, MOE_ROUTER_SCREENED = 0, 1, 2
 MOE_K_EXACT, MOE_K_BATCH_MAX, MOE_K_ROUND_UP = 0, 1, 2
-MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_FORWARD, MOE_OP_FOLD = 0, 1, 2, 3, 4, 5
+MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_FORWARD, MOE_OP_FOLD, MOE_OP_PATH = 0, 1, 2, 3, 4, 5, 6
 MOE_FOLD_TOKEN, MOE_FOLD_POOL = 0, 1
 MOE_DEV_BAD_K = 1
 
@@ -44,6 +44,13 @@ SIGNATURES = {
     "moe_combine": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr],
     "moe_fold": [_P, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
                  c_ptr, c_ptr, c_ptr, c_size, c_ptr],
+    "moe_path_table_bytes": [c_i32, ctypes.POINTER(c_size)],
+    "moe_path_table": [c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
+    "moe_path_route": [_P, c_ptr, c_ptr, c_ptr, c_ptr, ctypes.c_float, c_ptr, c_i32, c_ptr, c_ptr, c_ptr, c_ptr,
+                       c_ptr, c_ptr, c_ptr, c_size, c_ptr],
+    "moe_path_sources": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
+    "moe_path_rows": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr],
+    "moe_ffn_down_rows": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
     "moe_proxy_kappa_balanced": [c_i32, c_i32, c_i32, c_ptr],
     "moe_proxy_pack": [_P, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr],
     "moe_proxy_route": [_P, c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,

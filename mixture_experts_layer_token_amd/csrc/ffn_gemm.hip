@@ -336,16 +336,17 @@ hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const 
   return launch_gemm_variant<0, 128, 128, 2, 4, 3>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st, sec);
 }
 
-hipError_t launch_ffn_down_gemm(const void* h, const void* wd, const int4* blocks, int bound, int dense_rows,
-                                int rows_hint, void* y, int N, int K, hipStream_t st, const GemmSecond& sec) {
+hipError_t launch_ffn_down_gemm(const void* h, const int32_t* row_map, const void* wd, const int4* blocks, int bound,
+                                int dense_rows, int rows_hint, void* y, int N, int K, hipStream_t st,
+                                const GemmSecond& sec) {
   if (rows_hint >= GBM) {
     if (N % 256 == 0)
-      return launch_gemm_variant<1, 256, 256, 4, 2, 2>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
-    return launch_gemm_variant<1, 256, 128, 4, 2, 2>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
+      return launch_gemm_variant<1, 256, 256, 4, 2, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
+    return launch_gemm_variant<1, 256, 128, 4, 2, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
   }
   if (N % 256 == 0)
-    return launch_gemm_variant<1, 128, 256, 2, 2, 3>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
-  return launch_gemm_variant<1, 128, 128, 2, 2, 3>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
+    return launch_gemm_variant<1, 128, 256, 2, 2, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
+  return launch_gemm_variant<1, 128, 128, 2, 2, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
 }
 
 }  // namespace moe

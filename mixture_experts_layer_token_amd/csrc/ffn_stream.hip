@@ -484,10 +484,10 @@ hipError_t launch_ffn_gateup_stream(int dtype, const void* in, const int32_t* ro
   return stream_t<float, 0>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st);
 }
 
-hipError_t launch_ffn_down_stream(int dtype, const void* h, const void* wd, const int4* blocks, int bound,
-                                  int dense_rows, void* y, int N, int K, hipStream_t st) {
-  if (dtype == DT_BF16) return stream_t<bf16_t, 1>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st);
-  return stream_t<float, 1>(h, nullptr, wd, wd, blocks, bound, dense_rows, y, N, K, st);
+hipError_t launch_ffn_down_stream(int dtype, const void* h, const int32_t* row_map, const void* wd,
+                                  const int4* blocks, int bound, int dense_rows, void* y, int N, int K, hipStream_t st) {
+  if (dtype == DT_BF16) return stream_t<bf16_t, 1>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, st);
+  return stream_t<float, 1>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, st);
 }
 
 }  // namespace moe

@@ -68,8 +68,8 @@ int stream_row_block();
 hipError_t launch_ffn_gateup_stream(int dtype, const void* in, const int32_t* row_map, const void* wg,
                                     const void* wu, const int4* blocks, int bound, int dense_rows, void* h, int N,
                                     int K, hipStream_t st);
-hipError_t launch_ffn_down_stream(int dtype, const void* h, const void* wd, const int4* blocks, int bound,
-                                  int dense_rows, void* y, int N, int K, hipStream_t st);
+hipError_t launch_ffn_down_stream(int dtype, const void* h, const int32_t* row_map, const void* wd,
+                                  const int4* blocks, int bound, int dense_rows, void* y, int N, int K, hipStream_t st);
 
 // ffn_gemm.hip -- grouped-GEMM FFN (bf16): same semantics as the streaming
 // kernels, over the row-block table with RB = gemm_row_block() (`bound`
@@ -91,8 +91,8 @@ int gemm_row_block();
 hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
                                   const int4* blocks, int bound, int dense_rows, int rows_hint, void* h, int N,
                                   int K, hipStream_t st, const GemmSecond& sec = GemmSecond{});
-hipError_t launch_ffn_down_gemm(const void* h, const void* wd, const int4* blocks, int bound, int dense_rows,
-                                int rows_hint, void* y, int N, int K, hipStream_t st,
+hipError_t launch_ffn_down_gemm(const void* h, const int32_t* row_map, const void* wd, const int4* blocks, int bound,
+                                int dense_rows, int rows_hint, void* y, int N, int K, hipStream_t st,
                                 const GemmSecond& sec = GemmSecond{});
 
 // combine.hip
@@ -125,5 +125,16 @@ hipError_t launch_proxy_route(int dtype, const int32_t* k, const int32_t* kappa,
                               const int32_t* base_tok_off, const int32_t* base_ids, const float* base_w,
                               const int32_t* base_inv, const void* hp, int E_base, int32_t* tok_off, int32_t* ids,
                               float* wts, int32_t* status, hipStream_t st);
+
+// path.hip -- compositional path routing (PCoMoE).  `table`: int32 src[P],
+// int32 tgt[P], float bias[P].
+hipError_t launch_path_topk(const double* part_g, const double* part_t, int S, const float* bias,
+                            const void* table, int P, float lam, const int32_t* tok_off, int T, int E, int k_max,
+                            float scale, int32_t* osrc, int32_t* otgt, float* wts, hipStream_t st);
+hipError_t launch_path_sources(const int32_t* tok_off, const int32_t* psrc, int T, int E, int k_max, int32_t* cnt,
+                               int32_t* tmp, int32_t* src_off, int32_t* src_ids, int32_t* p2s, int32_t* unit_off,
+                               hipStream_t st);
+hipError_t launch_path_rows(const int32_t* tok_off, int T, int k_max, const int32_t* perm_path, const int32_t* p2s,
+                            const int32_t* src_inv, int32_t* row_map, hipStream_t st);
 
 }  // namespace moe

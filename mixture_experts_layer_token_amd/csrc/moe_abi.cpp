@@ -138,6 +138,16 @@ void plan_fold(const moe_desc& d, Carver& c, FoldScratch& w) {
   w.n_members = c.take<int32_t>(1);
 }
 
+struct PathWs { double* part_g; double* part_t; int splits; int32_t* cnt; int32_t* tmp; };
+void plan_path(const moe_desc& d, Carver& c, PathWs& w) {
+  w.splits = router_splits(d.T, d.d, d.E);
+  const size_t ste = (size_t)w.splits * d.T * d.E;
+  w.part_g = c.take<double>(ste);
+  w.part_t = c.take<double>(ste);
+  w.cnt = c.take<int32_t>((size_t)d.T);
+  w.tmp = c.take<int32_t>(a_cap(d));
+}
+
 size_t ws_size(const moe_desc& d, int op) {
   Carver c(nullptr);
   switch (op) {
@@ -146,13 +156,16 @@ size_t ws_size(const moe_desc& d, int op) {
     case MOE_OP_FFN: { FfnWs w; plan_ffn(d, c, w); break; }
     case MOE_OP_COMBINE: break;
     case MOE_OP_FOLD: { FoldScratch w; plan_fold(d, c, w); break; }
+    case MOE_OP_PATH: { PathWs w; plan_path(d, c, w); break; }
     default: {  // the forward's own regions; large enough for every other op
       FwdWs w;
       plan_forward(d, c, w);
-      Carver f(nullptr);
+      Carver f(nullptr), p(nullptr);
       FoldScratch fw;
       plan_fold(d, f, fw);
-      return std::max(c.total(), f.total());
+      PathWs pw;
+      plan_path(d, p, pw);
+      return std::max({c.total(), f.total(), p.total()});
     }
   }
   return c.total();
@@ -241,13 +254,15 @@ moe_status do_gateup(const moe_desc& d, const void* x, const void* wg, const voi
   return launched(launch_ffn_gateup_stream(d.dtype, x, perm_tok, wg, wu, fw.blocks, fw.bound, 0, h, d.I, d.d, st));
 }
 
+// `row_map`: the h row of each permuted row (NULL: row p reads h row p).
 moe_status do_down(const moe_desc& d, const void* h, const void* wd, const int32_t* expert_off, void* y,
-                   const FfnWs& fw, bool build_blocks, hipStream_t st, const GemmSecond& sec = GemmSecond{}) {
+                   const FfnWs& fw, bool build_blocks, hipStream_t st, const GemmSecond& sec = GemmSecond{},
+                   const int32_t* row_map = nullptr) {
   hipError_t e = build_blocks ? launch_row_blocks(expert_off, d.E, fw.rb, fw.bound, fw.blocks, st) : hipSuccess;
   if (e != hipSuccess) return launched(e);
   if (routed_gemm(d))
-    return launched(launch_ffn_down_gemm(h, wd, fw.blocks, fw.bound, 0, rows_hint(d), y, d.d, d.I, st, sec));
-  return launched(launch_ffn_down_stream(d.dtype, h, wd, fw.blocks, fw.bound, 0, y, d.d, d.I, st));
+    return launched(launch_ffn_down_gemm(h, row_map, wd, fw.blocks, fw.bound, 0, rows_hint(d), y, d.d, d.I, st, sec));
+  return launched(launch_ffn_down_stream(d.dtype, h, row_map, wd, fw.blocks, fw.bound, 0, y, d.d, d.I, st));
 }
 
 moe_status do_shared(const moe_desc& d, const void* x, const void* sg, const void* su, const void* sd, void* h_sh,
@@ -255,11 +270,12 @@ moe_status do_shared(const moe_desc& d, const void* x, const void* sg, const voi
   hipError_t e;
   if (shared_gemm(d)) {
     e = launch_ffn_gateup_gemm(x, nullptr, sg, su, nullptr, 0, d.T, d.T, h_sh, d.I_shared, d.d, st);
-    if (e == hipSuccess) e = launch_ffn_down_gemm(h_sh, sd, nullptr, 0, d.T, d.T, y_sh, d.d, d.I_shared, st);
+    if (e == hipSuccess) e = launch_ffn_down_gemm(h_sh, nullptr, sd, nullptr, 0, d.T, d.T, y_sh, d.d, d.I_shared, st);
     return launched(e);
   }
   e = launch_ffn_gateup_stream(d.dtype, x, nullptr, sg, su, nullptr, 0, d.T, h_sh, d.I_shared, d.d, st);
-  if (e == hipSuccess) e = launch_ffn_down_stream(d.dtype, h_sh, sd, nullptr, 0, d.T, y_sh, d.d, d.I_shared, st);
+  if (e == hipSuccess)
+    e = launch_ffn_down_stream(d.dtype, h_sh, nullptr, sd, nullptr, 0, d.T, y_sh, d.d, d.I_shared, st);
   return launched(e);
 }
 
@@ -275,7 +291,7 @@ extern "C" {
 moe_status moe_workspace_size(const moe_desc* desc, int32_t op, size_t* bytes) {
   MOE_TRY(check_desc(desc));
   if (!bytes) return MOE_ERR_NULL;
-  if (op < MOE_OP_ROUTE || op > MOE_OP_FOLD) return MOE_ERR_UNSUPPORTED;
+  if (op < MOE_OP_ROUTE || op > MOE_OP_PATH) return MOE_ERR_UNSUPPORTED;
   *bytes = ws_size(*desc, op);
   return MOE_OK;
 }
@@ -471,6 +487,112 @@ moe_status moe_proxy_route(const moe_desc* desc, int32_t N, int32_t r, int32_t m
   return launched(launch_proxy_route(d.dtype, k, kappa, d.T, d.k_max, m, N, r, proxy_width(N, r), base_tok_off,
                                      base_ids, base_w, base_inv_perm, hp, d.E / N, tok_off, topk_ids, topk_w,
                                      dev_status, static_cast<hipStream_t>(stream)));
+}
+
+static constexpr int32_t kMaxPaths = 1024;
+
+moe_status moe_path_table_bytes(int32_t P, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL;
+  if (P < 1 || P > kMaxPaths) return MOE_ERR_SHAPE;
+  *bytes = (size_t)P * 12;
+  return MOE_OK;
+}
+
+moe_status moe_path_table(int32_t E, int32_t P, const int32_t* src, const int32_t* tgt, const float* bias,
+                          void* table, size_t table_bytes, moe_stream_t stream) {
+  if (!src || !tgt || !bias || !table) return MOE_ERR_NULL;
+  if (E < 1 || E > 1024 || P < 1 || P > kMaxPaths || table_bytes < (size_t)P * 12) return MOE_ERR_SHAPE;
+  if (!aligned16(table)) return MOE_ERR_ALIGN;
+  for (int32_t p = 0; p < P; ++p) {
+    if (src[p] < 0 || src[p] >= E || tgt[p] < 0 || tgt[p] >= E || !std::isfinite(bias[p])) return MOE_ERR_SHAPE;
+    if (p > 0 && (int64_t)src[p] * E + tgt[p] <= (int64_t)src[p - 1] * E + tgt[p - 1]) return MOE_ERR_SHAPE;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* dst = static_cast<char*>(table);
+  hipError_t e = hipMemcpyAsync(dst, src, (size_t)P * 4, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(dst + (size_t)P * 4, tgt, (size_t)P * 4, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(dst + (size_t)P * 8, bias, (size_t)P * 4, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return launched(e);
+}
+
+static moe_status path_shape(const moe_desc& d, int32_t P) {
+  if (P < 1 || P > kMaxPaths || d.k_max > 64 || d.k_max > P) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+moe_status moe_path_route(const moe_desc* desc, const void* x, const void* w_router, const float* router_bias,
+                          const void* w_tgt, float lambda, const void* table, int32_t P, const int32_t* k,
+                          int32_t* tok_off, int32_t* path_src, int32_t* path_tgt, float* path_w,
+                          int32_t* dev_status, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  MOE_TRY(path_shape(d, P));
+  if (!std::isfinite(lambda)) return MOE_ERR_SHAPE;
+  if (!tok_ptr(d, x) || !w_router || !table || !tok_ptr(d, k) || !tok_off || !tok_ptr(d, path_src) ||
+      !tok_ptr(d, path_tgt) || !tok_ptr(d, path_w))
+    return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_router) || (w_tgt && !aligned16(w_tgt)) || !aligned16(table))
+    return MOE_ERR_ALIGN;
+  MOE_TRY(check_ws(d, MOE_OP_PATH, ws, ws_bytes));
+  Carver c(ws);
+  PathWs pw;
+  plan_path(d, c, pw);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_router(d.dtype, x, w_router, k, d.T, d.d, d.E, d.k_max, budget(d), pw.splits, pw.part_g,
+                               tok_off, dev_status, st);
+  if (e == hipSuccess && w_tgt)
+    e = launch_router(d.dtype, x, w_tgt, k, d.T, d.d, d.E, d.k_max, budget(d), pw.splits, pw.part_t, tok_off,
+                      dev_status, st);
+  if (e == hipSuccess)
+    e = launch_path_topk(pw.part_g, w_tgt ? pw.part_t : nullptr, pw.splits, router_bias, table, P, lambda, tok_off,
+                         d.T, d.E, d.k_max, d.routed_scale, path_src, path_tgt, path_w, st);
+  return launched(e);
+}
+
+moe_status moe_path_sources(const moe_desc* desc, const int32_t* tok_off, const int32_t* path_src,
+                            int32_t* src_tok_off, int32_t* src_ids, int32_t* path_src_route, int32_t* unit_off,
+                            void* ws, size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  if (d.k_max > 64) return MOE_ERR_SHAPE;
+  if (!tok_off || !tok_ptr(d, path_src) || !src_tok_off || !tok_ptr(d, src_ids) || !tok_ptr(d, path_src_route) ||
+      !unit_off)
+    return MOE_ERR_NULL;
+  MOE_TRY(check_ws(d, MOE_OP_PATH, ws, ws_bytes));
+  Carver c(ws);
+  PathWs pw;
+  plan_path(d, c, pw);
+  return launched(launch_path_sources(tok_off, path_src, d.T, d.E, d.k_max, pw.cnt, pw.tmp, src_tok_off, src_ids,
+                                      path_src_route, unit_off, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_path_rows(const moe_desc* desc, const int32_t* tok_off, const int32_t* perm_path,
+                         const int32_t* path_src_route, const int32_t* src_inv_perm, int32_t* row_map,
+                         moe_stream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  if (!tok_off || !tok_ptr(d, perm_path) || !tok_ptr(d, path_src_route) || !tok_ptr(d, src_inv_perm) ||
+      !tok_ptr(d, row_map))
+    return MOE_ERR_NULL;
+  return launched(launch_path_rows(tok_off, d.T, d.k_max, perm_path, path_src_route, src_inv_perm, row_map,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_ffn_down_rows(const moe_desc* desc, const void* h, const int32_t* row_map, const void* w_down,
+                             const int32_t* expert_off, void* y_perm, void* ws, size_t ws_bytes,
+                             moe_stream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc& d = *desc;
+  MOE_TRY(path_ok(d));
+  MOE_TRY(check_ws(d, MOE_OP_FFN, ws, ws_bytes));
+  if (!tok_ptr(d, h) || !tok_ptr(d, row_map) || !w_down || !expert_off || !tok_ptr(d, y_perm)) return MOE_ERR_NULL;
+  if (!aligned16(h) || !aligned16(w_down) || !aligned16(y_perm)) return MOE_ERR_ALIGN;
+  Carver c(ws);
+  FfnWs fw;
+  plan_ffn(d, c, fw);
+  return do_down(d, h, w_down, expert_off, y_perm, fw, false, static_cast<hipStream_t>(stream), GemmSecond{},
+                 row_map);
 }
 
 moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router, const float* router_bias,

@@ -67,31 +67,34 @@ __device__ __forceinline__ bool budget_ok(const int32_t* __restrict__ kappa, int
 }
 
 // ---- routes per token and their offsets (one workgroup of 1024 threads) ----
+// The budget check is done once per budget into LDS (runs[kt] = kt or -1), so
+// that each token costs one LDS read.
 __global__ __launch_bounds__(1024) void proxy_offsets_kernel(const int32_t* __restrict__ k,
                                                              const int32_t* __restrict__ kappa, int T, int k_max,
                                                              int m, int N, int32_t* __restrict__ tok_off,
                                                              int32_t* __restrict__ status) {
   __shared__ int32_t wsum[16];
+  __shared__ int32_t runs[65];
   __shared__ int32_t bad_any;
   const int tid = threadIdx.x;
+  if (tid <= k_max) runs[tid] = budget_ok(kappa, m, N, k_max, tid) ? tid : -1;
+  if (tid == 0) bad_any = 0;
+  __syncthreads();
+  auto routes = [&](int kt) { return (kt < 0 || kt > k_max) ? -1 : runs[kt]; };
   const int per = (T + 1023) / 1024;
   const int beg = min(tid * per, T), end = min(beg + per, T);
   int s = 0, bad = 0;
   for (int i = beg; i < end; ++i) {
-    const int kt = k[i];
-    const bool ok = budget_ok(kappa, m, N, k_max, kt);
-    bad |= !ok;
-    s += ok ? kt : 0;
+    const int c = routes(k[i]);
+    bad |= c < 0;
+    s += max(c, 0);
   }
-  if (tid == 0) bad_any = 0;
-  __syncthreads();
   if (bad) atomicOr(&bad_any, 1);
   const int incl = block_scan_incl<1024>(s, wsum);
   int run = incl - s;
   for (int i = beg; i < end; ++i) {
     tok_off[i] = run;
-    const int kt = k[i];
-    run += budget_ok(kappa, m, N, k_max, kt) ? kt : 0;
+    run += max(routes(k[i]), 0);
   }
   if (tid == 1023) tok_off[T] = incl;
   if (tid == 0 && status) status[0] = bad_any ? MOE_DEV_BAD_K_BIT : 0;

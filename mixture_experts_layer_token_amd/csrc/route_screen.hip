@@ -36,14 +36,19 @@ namespace moe {
 // [64w, 64w + 64) of the span as a 4 x 4 grid of 16 x 16 MFMA tiles.  The four
 // waves read the same token rows (hits in the CU's L1 after the first), so the
 // bytes fetched per MFMA are a quarter of a one-tile-per-wave split.
-// Workgroup (0, 0, 0) first writes the token offsets (pass 2 needs them).
+// One extra workgroup (x = gridDim.x - 1, y = z = 0) writes the token offsets
+// (pass 2 needs them) alongside the tiles; the other x = gridDim.x - 1 groups
+// have nothing to do.
 __global__ __launch_bounds__(256) void router_screen_mfma_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int T, int d, int E, float* __restrict__ approx,
     float* __restrict__ absum, const int32_t* __restrict__ k, int k_max, BudgetPolicy pol,
     int32_t* __restrict__ tok_off, int32_t* __restrict__ status) {
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
-    __shared__ int32_t scan_part[257];
-    token_offsets_block<256>(k, T, k_max, pol, tok_off, status, scan_part, scan_part + 256);
+  if (blockIdx.x == gridDim.x - 1) {
+    if (blockIdx.y == 0 && blockIdx.z == 0) {
+      __shared__ int32_t scan_part[257];
+      token_offsets_block<256>(k, T, k_max, pol, tok_off, status, scan_part, scan_part + 256);
+    }
+    return;
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
@@ -330,7 +335,7 @@ static void launch_select(dim3 grid, size_t lds, hipStream_t st, const bf16_t* x
 hipError_t launch_router_screen(const void* x, const void* w, const float* bias, const int32_t* k, int T, int d,
                                 int E, int k_max, BudgetPolicy pol, int S, float scale, float* approx, float* absum,
                                 int32_t* tok_off, int32_t* status, int32_t* ids, float* wts, hipStream_t st) {
-  hipLaunchKernelGGL(router_screen_mfma_kernel, dim3(max(1, (T + 63) / 64), (E + 255) / 256, S), dim3(256), 0, st,
+  hipLaunchKernelGGL(router_screen_mfma_kernel, dim3((T + 63) / 64 + 1, (E + 255) / 256, S), dim3(256), 0, st,
                      (const bf16_t*)x, (const bf16_t*)w, T, d, E, approx, absum, k, k_max, pol, tok_off, status);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || T == 0) return err;

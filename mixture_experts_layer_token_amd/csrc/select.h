@@ -124,13 +124,13 @@ __device__ __forceinline__ void wave_select(const uint32_t (&key)[KPL], int k, b
   }
 }
 
-// Selects the top k (1 <= k <= present keys) and writes ids[j], wts[j] for
-// j = 0 .. k-1 in selection order.  `scratch` is this wave's LDS area of at
-// least k + 1 uint64 slots.
-template <int KPL>
-__device__ __forceinline__ void wave_topk_softmax(const uint32_t (&key)[KPL], int k, float scale,
-                                                  int32_t* __restrict__ ids, float* __restrict__ wts,
-                                                  uint64_t* scratch) {
+// Selects the top k (1 <= k <= present keys), calls emit(j, slot) for the
+// selected key of this lane's slot `slot` that lands at position j, and writes
+// wts[j], for j = 0 .. k-1 in selection order.  `scratch` is this wave's LDS
+// area of at least k + 1 uint64 slots.
+template <int KPL, class Emit>
+__device__ __forceinline__ void wave_topk_softmax_emit(const uint32_t (&key)[KPL], int k, float scale, Emit emit,
+                                                       float* __restrict__ wts, uint64_t* scratch) {
   const int lane = threadIdx.x & 63;
   bool sel[KPL];
   wave_select<KPL>(key, k, sel);
@@ -181,7 +181,7 @@ __device__ __forceinline__ void wave_topk_softmax(const uint32_t (&key)[KPL], in
     p[s] = 0.f;
     if (rank[s] >= 0) {
       p[s] = expf(key_logit(key[s]) - l0);
-      ids[rank[s]] = lane + 64 * s;
+      emit(rank[s], s);
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -203,6 +203,15 @@ __device__ __forceinline__ void wave_topk_softmax(const uint32_t (&key)[KPL], in
 #pragma unroll
   for (int s = 0; s < KPL; ++s)
     if (rank[s] >= 0) wts[rank[s]] = p[s] * inv;
+}
+
+// The same, writing ids[j] = the selected expert (lane + 64 * slot).
+template <int KPL>
+__device__ __forceinline__ void wave_topk_softmax(const uint32_t (&key)[KPL], int k, float scale,
+                                                  int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                  uint64_t* scratch) {
+  const int lane = threadIdx.x & 63;
+  wave_topk_softmax_emit<KPL>(key, k, scale, [&](int j, int s) { ids[j] = lane + 64 * s; }, wts, scratch);
 }
 
 }  // namespace moe

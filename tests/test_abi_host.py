@@ -162,3 +162,42 @@ def test_proxy_validates_before_launch():
     assert pack(3, 8) == 2
     assert pack(4, 8, gi=None) == 1
     assert pack(4, 8, pg=P((1 << 20) + 2)) == 5
+
+
+def test_path_table_validates_on_the_host():
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    n = ctypes.c_size_t(0)
+    assert lib.moe_path_table_bytes(6, ctypes.byref(n)) == 0 and n.value == 72
+    assert lib.moe_path_table_bytes(0, ctypes.byref(n)) == 2
+    assert lib.moe_path_table_bytes(1025, ctypes.byref(n)) == 2
+    i32 = lambda v: (ctypes.c_int32 * len(v))(*v)
+    f32 = lambda v: (ctypes.c_float * len(v))(*v)
+    fake = P(1 << 20)   # never written: every call below fails validation first
+    call = lambda E, s, t, b: lib.moe_path_table(E, len(s), i32(s), i32(t), f32(b), fake, 12 * len(s), None)
+    assert call(3, [0, 1, 1], [0, 2, 1], [0, 0, 0]) == 2          # not increasing
+    assert call(3, [0, 0], [1, 1], [0, 0]) == 2                   # duplicate
+    assert call(3, [0, 3], [0, 0], [0, 0]) == 2                   # source out of range
+    assert call(3, [0, 1], [0, -1], [0, 0]) == 2                  # target out of range
+    assert call(3, [0, 1], [0, 1], [0, float("nan")]) == 2        # bias not finite
+    assert lib.moe_path_table(3, 1, None, i32([0]), f32([0]), fake, 12, None) == 1
+    assert lib.moe_path_table(3, 1, i32([0]), i32([0]), f32([0]), P((1 << 20) + 4), 12, None) == 5
+
+
+def test_path_route_validates_before_launch():
+    lib = _lib.load()
+    d = _desc(T=4, d=128, E=8, I=128, k_max=2)
+    x = ctypes.c_void_p(1 << 20)
+    route = lambda P, lam=0.5, desc=d, **kw: lib.moe_path_route(
+        ctypes.byref(desc), kw.get("x", x), x, None, None, lam, kw.get("table", x), P,
+        *[kw.get(n, x) for n in ("k", "to", "src", "tgt", "w")], None, kw.get("ws", None), 0, None)
+    assert route(1) == 2                                     # k_max > P
+    assert route(2000) == 2                                  # P too large
+    assert route(8, lam=float("inf")) == 2
+    assert route(8, table=None) == 1
+    assert route(8) == 4                                     # workspace missing
+    assert route(8, desc=_desc(T=4, d=128, E=128, I=128, k_max=65)) == 2
+    st, n = _ws(d, moe.MOE_OP_PATH)
+    assert st == 0 and 0 < n <= _ws(d, moe.MOE_OP_FORWARD)[1]
+    assert lib.moe_path_sources(ctypes.byref(d), None, x, x, x, x, x, None, 0, None) == 1
+    assert lib.moe_ffn_down_rows(ctypes.byref(d), x, None, x, x, x, None, 0, None) in (1, 4)

@@ -62,6 +62,8 @@ __all__ = [
     "draw_k_eq7",
     "make_fold_tables",
     "make_proxy_inputs",
+    "make_path_mask",
+    "make_target_router",
 ]
 
 
@@ -321,3 +323,34 @@ def make_proxy_inputs(cfg: LayerConfig, r: int, device="cpu"):
     g.manual_seed(derived_seed(cfg.seed, "k", 13))
     idx = torch.stack([torch.sort(torch.randperm(cfg.I, generator=g)[:r]).values for _ in range(cfg.E)])
     return w_base, idx.to(torch.int32).to(device)
+
+
+def make_path_mask(E: int, extra: int, seed: int = 0, offset: float = -0.5, noise: float = 0.1):
+    """A synthetic active path list for compositional path routing (the
+    learned, pruned mask needs training): every diagonal path (e, e) with bias
+    0, plus `extra` off-diagonal targets per source drawn without replacement,
+    each with bias offset + U(-noise, noise) (a negative prior with bounded
+    noise, as at initialisation).  Returns (src, tgt, bias) numpy arrays
+    sorted by (src, tgt): int32, int32, float32."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(derived_seed(seed, "k", 17))
+    rows = []
+    for i in range(E):
+        others = [j for j in range(E) if j != i]
+        pick = torch.randperm(len(others), generator=g)[:extra].tolist()
+        rows.append((i, i, 0.0))
+        for q in pick:
+            b = offset + noise * (2.0 * torch.rand(1, generator=g).item() - 1.0)
+            rows.append((i, others[q], b))
+    rows.sort()
+    src = np.array([r[0] for r in rows], dtype=np.int32)
+    tgt = np.array([r[1] for r in rows], dtype=np.int32)
+    bias = np.array([r[2] for r in rows], dtype=np.float32)
+    return src, tgt, bias
+
+
+def make_target_router(cfg: LayerConfig, device="cpu") -> torch.Tensor:
+    """The projection-side prior's weights w_tgt [E][d] (same law as the
+    router's)."""
+    return _gauss((cfg.E, cfg.d), 1.0 / math.sqrt(cfg.d), derived_seed(cfg.seed, "w_router", 2), torch.device(device),
+                  torch_dtype(cfg.dtype))
