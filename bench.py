@@ -59,6 +59,10 @@ def parse():
                     help="R > 0: route the split layer by training-free proxy gating (MoE-Prism) with R "
                          "gate neurons per sub-expert over a synthetic whole-expert router picking "
                          "k_max / split experts; the step then runs the staged calls")
+    ap.add_argument("--paths", default="",
+                    help="EXTRA[:LAMBDA]: run the layer as compositional paths (PCoMoE) over a synthetic active "
+                         "list of the diagonal plus EXTRA off-diagonal paths per source, with a synthetic "
+                         "target prior scaled by LAMBDA (default 0.5); the step then runs the staged calls")
     ap.add_argument("--k-policy", default="exact",
                     help="budget each token executes: exact (its own k_t; the headline), batch_max "
                          "(every token runs the batch maximum) or round_up:N (k_t rounded up to a "
@@ -253,6 +257,27 @@ def main():
                         pb["ysh"], pb["wsf"])
             moe.moe_combine(desc, pb["y"], pb["ysh"], pr.tok_off, pr.w, pb["iv"], out)
 
+    paths = None
+    if args.paths:
+        # path route -> sources -> expansions once per source -> projections by target -> combine
+        if args.fold or args.proxy:
+            raise SystemExit("--paths excludes --fold and --proxy")
+        from workloads import make_path_mask, make_target_router
+        extra, _, lam = args.paths.partition(":")
+        lam = float(lam) if lam else 0.5
+        p_src, p_tgt, p_bias = make_path_mask(E, int(extra), seed=cfg.seed)
+        table = moe.moe_path_table(E, p_src, p_tgt, p_bias, dev)
+        pl = moe.PathLayer(desc, table, len(p_src), lam, dev)
+        w_tgt = make_target_router(cfg, dev)
+        paths = dict(layer=pl, P=len(p_src), extra=int(extra), lam=lam,
+                     run=lambda o: pl.run(layer.x, layer.w_router, layer.router_bias, w_tgt, layer.k, layer.w_gate,
+                                          layer.w_up, layer.w_down, o))
+        if Is:
+            raise SystemExit("--paths runs routed experts only (no shared expert)")
+
+        def step():
+            paths["run"](out)
+
     if args.calib_copy:
         src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -295,8 +320,15 @@ def main():
     ms_step = t_start.elapsed_time(t_end) / args.steps
     if proxy is not None:
         status = proxy["router"].status
+    if paths is not None:
+        status = paths["layer"].status
     assert int(status.item()) == 0
-    if proxy is not None:
+    if paths is not None:
+        # the gate/up launch runs over the source routes (one expansion per source)
+        n_act, A = int(paths["layer"].s_nact.item()), int(paths["layer"].src_off[T].item())
+        paths["routes"] = int(paths["layer"].tok_off[T].item())
+        paths["targets_active"] = int(paths["layer"].t_nact.item())
+    elif proxy is not None:
         n_act, A = int(proxy["buf"]["na"].item()), int(proxy["router"].tok_off[T].item())
     elif fold is None:
         st = stats.cpu().numpy()
@@ -337,7 +369,11 @@ def main():
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_in)]
     with torch.cuda.stream(stream):
         for i in range(max(3, args.warmup // 4) + n_in):
-            if proxy is not None:
+            if paths is not None:
+                paths["run"](out_r)
+                tok_off.copy_(paths["layer"].src_off)
+                ids.copy_(paths["layer"].src_ids)
+            elif proxy is not None:
                 proxy["run"]()
                 tok_off.copy_(proxy["router"].tok_off)
                 ids.copy_(proxy["router"].ids)
@@ -420,12 +456,16 @@ def main():
     roof["ridge_flop_per_byte"] = round(ridge, 1)
     roof["traffic"] = (measured_traffic(cfg.name, routed_path)
                        if args.k_policy == "exact" and not args.k_dist and not args.fold and not args.proxy
-                       else None)
+                       and not args.paths else None)
 
     # ---- whole layer against its own roofline ----
     w_bytes = 3 * n_act * d * I * esz
-    all_bytes = w_bytes + 3 * d * Is * esz + E * d * esz + 2 * T * d * esz
     ffn_flops = 6.0 * d * I * A + 6.0 * d * Is * T
+    if paths is not None:
+        # expansions (gate/up) over the active sources, projections over the active targets
+        w_bytes = (2 * n_act + paths["targets_active"]) * d * I * esz
+        ffn_flops = 4.0 * d * I * A + 2.0 * d * I * paths["routes"]
+    all_bytes = w_bytes + 3 * d * Is * esz + E * d * esz + 2 * T * d * esz
     layer_s = ms_step * 1e-3
     layer_info = {"activated_weight_GBps": round(w_bytes / layer_s / 1e9, 1),
                   "activated_weight_frac_hbm": round(w_bytes / layer_s / 1e9 / PEAK_HBM_GBS, 4),
@@ -435,7 +475,8 @@ def main():
                                          (PEAK_BF16_TFLOPS if esz == 2 else PEAK_FP32_TFLOPS), 4)}
 
     cpu = None
-    if not args.no_cpu_baseline and args.k_policy == "exact" and not args.fold and not args.proxy:
+    if (not args.no_cpu_baseline and args.k_policy == "exact" and not args.fold and not args.proxy
+            and not args.paths):
         n = args.cpu_sample or {"mixtral_decode": 64, "qwen3_30b_a3b_decode": 256, "tiny_fp32": 16,
                                 "subexpert_prefill": 64, "dsv3_decode": 16, "dsv3_prefill": 16}[cfg.name]
         print(f"[bench] timing the CPU oracle on {n} tokens", file=sys.stderr, flush=True)
@@ -460,6 +501,9 @@ def main():
                    "execution": "eager" if args.eager else "hip_graph", "ffn_path": routed_path,
                    "router": args.router, "k_policy": args.k_policy, "k_dist": args.k_dist or "workload",
                    "fold": args.fold or "none", "proxy": proxy_info or "none",
+                   "paths": ({"P": paths["P"], "extra_per_source": paths["extra"], "lambda": paths["lam"],
+                              "routes": paths["routes"], "expansions": A, "sources_active": n_act,
+                              "targets_active": paths["targets_active"]} if paths else "none"),
                    "wall_s": round(wall, 3)},
         "layer": layer_info,
         "roofline": roof,
