@@ -62,6 +62,21 @@ hipError_t launch_row_blocks(const int32_t* grp_off, int G, int RB, int bound, i
   return hipGetLastError();
 }
 
+// Calls f(a, e) for each assignment a in [a0, a1) of one token with its expert
+// id e; the ids are loaded eight at a time, so that their latencies overlap
+// instead of adding up (a token's k_t loads otherwise wait one after another).
+template <class F>
+__device__ __forceinline__ void for_token_ids(const int32_t* __restrict__ ids, int a0, int a1, F f) {
+  for (int b = a0; b < a1; b += 8) {
+    int e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = (b + j < a1) ? ids[b + j] : -1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (b + j < a1) f(b + j, e[j]);
+  }
+}
+
 __device__ __forceinline__ void build_masks(uint32_t* masks, const int32_t* __restrict__ tok_off,
                                             const int32_t* __restrict__ ids, int T, int E) {
   const int tid = threadIdx.x;
@@ -69,12 +84,10 @@ __device__ __forceinline__ void build_masks(uint32_t* masks, const int32_t* __re
   __syncthreads();
   const int t = blockIdx.x * PERM_BLOCK + tid;
   if (t < T) {
-    const int a0 = tok_off[t], a1 = tok_off[t + 1];
     const uint32_t bit = 1u << (tid & 31);
-    for (int a = a0; a < a1; ++a) {
-      const int e = ids[a];
+    for_token_ids(ids, tok_off[t], tok_off[t + 1], [&](int, int e) {
       if ((unsigned)e < (unsigned)E) atomicOr(&masks[e * MASK_WORDS + (tid >> 5)], bit);
-    }
+    });
   }
   __syncthreads();
 }
@@ -184,12 +197,10 @@ __global__ __launch_bounds__(PERM_BLOCK) void expert_scatter_kernel(
   {
     const int t = blk * PERM_BLOCK + tid;
     if (t < T) {
-      const int a0 = tok_off[t], a1 = tok_off[t + 1];
       const uint32_t bit = 1u << (tid & 31);
-      for (int a = a0; a < a1; ++a) {
-        const int e = ids[a];
+      for_token_ids(ids, tok_off[t], tok_off[t + 1], [&](int, int e) {
         if ((unsigned)e < (unsigned)E) atomicOr(&masks[e * MASK_WORDS + (tid >> 5)], bit);
-      }
+      });
     }
   }
   __syncthreads();
@@ -304,12 +315,10 @@ __global__ __launch_bounds__(PERM_BLOCK) void permute_one_block_kernel(
     close_row_blocks(blocks, nblocks, bound, tid, PERM_BLOCK);
   }
   if (tid >= T) return;
-  const int a0 = tok_off[tid], a1 = tok_off[tid + 1];
   const int wi = tid >> 5;
   const uint32_t below = (1u << (tid & 31)) - 1u;
-  for (int a = a0; a < a1; ++a) {
-    const int e = ids[a];
-    if ((unsigned)e >= (unsigned)E) continue;  // not produced by moe_route; ignored
+  for_token_ids(ids, tok_off[tid], tok_off[tid + 1], [&](int a, int e) {
+    if ((unsigned)e >= (unsigned)E) return;  // not produced by moe_route; ignored
     const uint32_t* m = masks + e * MASK_WORDS;
     int rank = __popc(m[wi] & below);
     for (int w = 0; w < wi; ++w) rank += __popc(m[w]);
@@ -317,7 +326,7 @@ __global__ __launch_bounds__(PERM_BLOCK) void permute_one_block_kernel(
     perm_tok[pos] = tid;
     perm_src[pos] = a;
     inv_perm[a] = pos;
-  }
+  });
 }
 
 hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int E, int k_max, int32_t* block_counts,

@@ -150,3 +150,36 @@ def test_paths_mixtral_decode_full_size():
                                tokens=tokens)
     err = compare_out(out, want, cfg.dtype, tokens)
     _say(f"[path] mixtral_decode: routes {g['A']}, expansions {int(pl.src_off[-1].item())}, {err}")
+
+
+@pytest.mark.parametrize("T,E,k_max,extra", [(0, 8, 2, 1), (1, 8, 8, 7), (257, 1024, 64, 0), (300, 64, 64, 15)])
+def test_paths_edges(T, E, k_max, extra):
+    """Empty batch, a single token over every pair of 8 experts, the largest
+    list (1,024 paths over 1,024 experts) with k_max = 64, and 64 paths per
+    token over a 16-wide list per source."""
+    rng = np.random.default_rng(T + E)
+    k = rng.integers(0, k_max + 1, size=T)
+    if T:
+        k[0] = k_max
+    layer = make_custom_layer(T, 128, E, 128, k, dtype="f32", k_max=k_max, seed=13, device="cuda")
+    w_tgt = make_target_router(layer.cfg, "cuda")
+    src, tgt, bias = make_path_mask(E, extra, seed=7)
+    pl, out = _run(layer, k_max, src, tgt, bias, w_tgt, 0.625)
+    g = _host(pl)
+    ref = oracle.path_route(to_f64(layer.x), to_f64(layer.w_router), None, to_f64(w_tgt), np.float32(0.625), src,
+                            tgt, bias.astype(np.float64), to_f64(layer.k), k_max)
+    np.testing.assert_array_equal(g["tok_off"], ref["tok_off"])
+    np.testing.assert_array_equal(g["src"], ref["src"])
+    np.testing.assert_array_equal(g["tgt"], ref["tgt"])
+    np.testing.assert_allclose(g["w"], ref["w"], rtol=2e-6, atol=2e-7)
+    s_off, s_ids, p2s = oracle.path_sources(ref["tok_off"], ref["src"])
+    np.testing.assert_array_equal(g["src_off"], s_off)
+    np.testing.assert_array_equal(g["src_ids"], s_ids)
+    np.testing.assert_array_equal(g["p2s"], p2s)
+    if T:
+        tokens = sample_tokens(T, 24)
+        want = oracle.path_forward(to_f64(layer.x), ref["tok_off"], ref["src"], ref["tgt"], ref["w"],
+                                   ExpertView(layer.w_gate), ExpertView(layer.w_up), ExpertView(layer.w_down),
+                                   tokens=tokens)
+        compare_out(out, want, "f32", tokens)
+    _say(f"[path] edge T={T} E={E} k_max={k_max} P={len(src)}: routes {g['A']}")

@@ -283,3 +283,26 @@ def test_proxy_bad_kappa_rows_and_graph_replay():
         np.testing.assert_array_equal(to_f64(pr.tok_off), got_to)
         np.testing.assert_array_equal(to_f64(pr.ids)[:A], first[0])
         assert torch.equal(pr.w[:A], first[1])
+
+
+@pytest.mark.parametrize("T,N,m,E,r", [(0, 4, 2, 32, 4), (1, 8, 8, 128, 16), (129, 8, 8, 128, 3)])
+def test_proxy_edges(T, N, m, E, r):
+    """Empty batch, one token, and the widest pick set (m*N = 64 lanes) with a
+    ragged token count and r not dividing the padded width."""
+    k_max = m * N
+    cfg = _small_cfg("f32", T=T, E=E, N=N, k_max=k_max)
+    layer = make_layer(cfg, "cuda")
+    w_base, gate_idx = make_proxy_inputs(cfg, r, "cuda")
+    kappa = moe.moe_proxy_kappa_balanced(k_max, m, N)
+    desc, pr, _, _ = _gpu_proxy(layer, N, r, m, kappa, w_base, gate_idx)
+    ref = oracle.proxy_route(to_f64(layer.x), to_f64(w_base), None, to_f64(layer.k), k_max, m, N, kappa.tolist(),
+                             to_f64(gate_idx), to_f64(layer.w_gate), to_f64(layer.w_up), cfg.routed_scale)
+    got_to = to_f64(pr.tok_off)
+    np.testing.assert_array_equal(got_to, ref["tok_off"])
+    assert int(pr.status.item()) == ref["status"] == 0
+    if T:
+        A = int(got_to[-1])
+        picks, differ, _ = _check_selection(got_to, to_f64(pr.ids)[:A], pr.w[:A].cpu().double().numpy(), ref,
+                                            range(T), kappa.tolist(), to_f64(layer.k), N, m, k_max,
+                                            SCORE_TOL["f32"])
+        assert differ == 0

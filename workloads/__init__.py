@@ -190,7 +190,7 @@ def draw_k(cfg: LayerConfig, T: Optional[int] = None) -> torch.Tensor:
     T = cfg.T if T is None else T
     g = torch.Generator(device="cpu")
     g.manual_seed(derived_seed(cfg.seed, "k"))
-    if len(cfg.k_values) == 1:
+    if len(cfg.k_values) == 1 or T == 0:
         return torch.full((T,), int(cfg.k_values[0]), dtype=torch.int32)
     probs = torch.tensor(cfg.k_probs, dtype=torch.float64)
     idx = torch.multinomial(probs, T, replacement=True, generator=g)
