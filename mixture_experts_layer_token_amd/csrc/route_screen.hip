@@ -36,26 +36,27 @@ namespace moe {
 // [64w, 64w + 64) of the span as a 4 x 4 grid of 16 x 16 MFMA tiles.  The four
 // waves read the same token rows (hits in the CU's L1 after the first), so the
 // bytes fetched per MFMA are a quarter of a one-tile-per-wave split.
-// One extra workgroup (x = gridDim.x - 1, y = z = 0) writes the token offsets
-// (pass 2 needs them) alongside the tiles; the other x = gridDim.x - 1 groups
-// have nothing to do.
+// One more slice index (z = S) holds the token-offset scan (pass 2 needs it)
+// in its first workgroup; its other workgroups exit at once.  Dispatched after
+// the tiles, the scan shares a CU with one of them instead of delaying one.
 __global__ __launch_bounds__(256) void router_screen_mfma_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int T, int d, int E, float* __restrict__ approx,
     float* __restrict__ absum, const int32_t* __restrict__ k, int k_max, BudgetPolicy pol,
     int32_t* __restrict__ tok_off, int32_t* __restrict__ status) {
-  if (blockIdx.x == gridDim.x - 1) {
-    if (blockIdx.y == 0 && blockIdx.z == 0) {
+  if (blockIdx.z == gridDim.z - 1) {
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
       __shared__ int32_t scan_part[257];
       token_offsets_block<256>(k, T, k_max, pol, tok_off, status, scan_part, scan_part + 256);
     }
     return;
   }
+  if (T == 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
   const int t0 = blockIdx.x * 64;
   const int e0 = blockIdx.y * 256 + wave * 64;
   if (e0 >= E) return;
-  const int S = gridDim.z, chunks = d / 32;
+  const int S = gridDim.z - 1, chunks = d / 32;
   const int k_beg = (int)(((long long)blockIdx.z * chunks) / S) * 32;
   const int k_end = (int)(((long long)(blockIdx.z + 1) * chunks) / S) * 32;
   // operand rows (clamped in range; results of clamped rows are not stored)
@@ -147,6 +148,18 @@ __device__ __forceinline__ void dot8(const uint4& xv, const uint4& wv, double (&
     const float p1 = __uint_as_float(xs[q] & 0xffff0000u) * __uint_as_float(ws[q] & 0xffff0000u);
     acc[q] += (double)p0;
     acc[q] += (double)p1;
+  }
+}
+
+// The same with the token's eight elements already widened to float64: one
+// fused multiply-add per element (the product of two bf16 values is exact in
+// float64, so fma(x, w, acc) rounds exactly as acc + x*w does above).
+__device__ __forceinline__ void dot8_wide(const double (&xd)[8], const uint4& wv, double (&acc)[4]) {
+  const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[q] = fma(xd[2 * q], (double)__uint_as_float(ws[q] << 16), acc[q]);
+    acc[q] = fma(xd[2 * q + 1], (double)__uint_as_float(ws[q] & 0xffff0000u), acc[q]);
   }
 }
 
@@ -245,12 +258,19 @@ __global__ __launch_bounds__(256) void router_screen_select_kernel(
   constexpr int PASS = 512 * XC;
   const int npass = (d + PASS - 1) / PASS;
   const int items = ncand * npass;
-  uint4 xres[XR ? XC : 1];
+  // resident token row (XR), widened to float64 once
+  double xd[XR ? XC : 1][8];
   if constexpr (XR) {
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
       const int off = 512 * i + 8 * lane;
-      xres[i] = off < d ? *reinterpret_cast<const uint4*>(xrow + off) : zero_u4();
+      const uint4 v = off < d ? *reinterpret_cast<const uint4*>(xrow + off) : zero_u4();
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xd[i][2 * q] = (double)__uint_as_float(u[q] << 16);
+        xd[i][2 * q + 1] = (double)__uint_as_float(u[q] & 0xffff0000u);
+      }
     }
   }
   auto load_item = [&](uint4 (&xv)[XC], uint4 (&wr)[XC], int it) {
@@ -266,7 +286,10 @@ __global__ __launch_bounds__(256) void router_screen_select_kernel(
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
   auto finish_item = [&](int it, const uint4 (&xv)[XC], const uint4 (&wr)[XC]) {
 #pragma unroll
-    for (int i = 0; i < XC; ++i) dot8(XR ? xres[i] : xv[i], wr[i], acc);
+    for (int i = 0; i < XC; ++i) {
+      if constexpr (XR) dot8_wide(xd[i], wr[i], acc);
+      else dot8(xv[i], wr[i], acc);
+    }
     const int c = it / npass;
     if (it - c * npass == npass - 1) {  // candidate complete
       red[(c % SEL_GRP) * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
@@ -335,7 +358,7 @@ static void launch_select(dim3 grid, size_t lds, hipStream_t st, const bf16_t* x
 hipError_t launch_router_screen(const void* x, const void* w, const float* bias, const int32_t* k, int T, int d,
                                 int E, int k_max, BudgetPolicy pol, int S, float scale, float* approx, float* absum,
                                 int32_t* tok_off, int32_t* status, int32_t* ids, float* wts, hipStream_t st) {
-  hipLaunchKernelGGL(router_screen_mfma_kernel, dim3((T + 63) / 64 + 1, (E + 255) / 256, S), dim3(256), 0, st,
+  hipLaunchKernelGGL(router_screen_mfma_kernel, dim3(max(1, (T + 63) / 64), (E + 255) / 256, S + 1), dim3(256), 0, st,
                      (const bf16_t*)x, (const bf16_t*)w, T, d, E, approx, absum, k, k_max, pol, tok_off, status);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || T == 0) return err;

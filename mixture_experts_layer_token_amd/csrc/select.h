@@ -38,16 +38,29 @@ __device__ __forceinline__ int budget_exec(int v, int k_max, BudgetPolicy pol, i
   return v;
 }
 
+// A thread's first KR budgets are loaded once, together, and kept in
+// registers for the three passes (batches up to KR * NT tokens never re-read).
 template <int NT>
 __device__ void token_offsets_block(const int32_t* __restrict__ k, int T, int k_max, BudgetPolicy pol,
                                     int32_t* __restrict__ tok_off, int32_t* __restrict__ status, int32_t* part,
                                     int32_t* bad_any) {
+  constexpr int KR = 32;
   const int tid = threadIdx.x;
   const int per = (T + NT - 1) / NT;
   const int beg = min(tid * per, T), end = min(beg + per, T);
+  int kr[KR];
+#pragma unroll
+  for (int j = 0; j < KR; ++j) kr[j] = (beg + j < end) ? k[beg + j] : 0;
   int bad = 0, kmx = 0;
-#pragma unroll 8
-  for (int i = beg; i < end; ++i) {
+#pragma unroll
+  for (int j = 0; j < KR; ++j) {
+    if (beg + j < end) {
+      const bool ok = budget_valid(kr[j], k_max);
+      bad |= !ok;
+      kmx = max(kmx, ok ? kr[j] : 0);
+    }
+  }
+  for (int i = beg + KR; i < end; ++i) {
     const int v = k[i];
     const bool ok = budget_valid(v, k_max);
     bad |= !ok;
@@ -56,15 +69,23 @@ __device__ void token_offsets_block(const int32_t* __restrict__ k, int T, int k_
   // batch maximum of the valid budgets (only BATCH_MAX uses it)
   const int kb = pol.policy == K_BATCH_MAX ? block_max<NT>(kmx, part) : 0;
   int s = 0;
-#pragma unroll 8
-  for (int i = beg; i < end; ++i) s += budget_exec(k[i], k_max, pol, kb);
+#pragma unroll
+  for (int j = 0; j < KR; ++j)
+    if (beg + j < end) s += budget_exec(kr[j], k_max, pol, kb);
+  for (int i = beg + KR; i < end; ++i) s += budget_exec(k[i], k_max, pol, kb);
   if (tid == 0) *bad_any = 0;
   __syncthreads();
   if (bad) atomicOr(bad_any, 1);
   const int incl = block_scan_incl<NT>(s, part);  // its barriers also publish bad_any
   int run = incl - s;
-#pragma unroll 8
-  for (int i = beg; i < end; ++i) {
+#pragma unroll
+  for (int j = 0; j < KR; ++j) {
+    if (beg + j < end) {
+      tok_off[beg + j] = run;
+      run += budget_exec(kr[j], k_max, pol, kb);
+    }
+  }
+  for (int i = beg + KR; i < end; ++i) {
     tok_off[i] = run;
     run += budget_exec(k[i], k_max, pol, kb);
   }

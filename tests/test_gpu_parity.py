@@ -80,9 +80,10 @@ def test_shapes_and_ragged(dtype, T, E, d, I, kmax, Is):
     compare_out(got["out"], oracle_out(layer, tokens), dtype, tokens)
 
 
-def test_zero_tokens():
+@pytest.mark.parametrize("router", ["float64", "screened"])
+def test_zero_tokens(router):
     layer = make_custom_layer(T=0, d=128, E=4, I=128, k=[], dtype="bf16", k_max=2, device="cuda")
-    out, stats, status = run_forward(layer)
+    out, stats, status = run_forward(layer, router=router)
     assert out.shape == (0, 128) and status == 0
     assert stats[:4].tolist() == [0] * 4 and stats[4] == 0 and stats[5] == 0
 
