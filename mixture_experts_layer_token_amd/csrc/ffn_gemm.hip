@@ -75,7 +75,12 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   static_assert(XI * 8 * NW == BM && WI * 8 * NW == WROWS, "DMA split");
   static_assert(TMW >= 1 && TNW >= 1 && GBM % BM == 0, "tiling");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
-  __shared__ __attribute__((aligned(1024))) char lds[STAGES * SBYTES];
+  // The down projection's epilogue stages its output tile here as well (rows
+  // of EPITCH bytes: 16 bytes of padding keep the rows 16-byte aligned and
+  // spread the staging writes over the banks).
+  constexpr int EPITCH = BNW * 2 + 16;
+  constexpr int LDS_BYTES = (MODE == 1 && BM * EPITCH > STAGES * SBYTES) ? BM * EPITCH : STAGES * SBYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   // ---- which (row block, row tile, N tile) this workgroup owns.  Row tiles
   // of the second, dense problem (rows_s > 0: an always-on expert over rows
@@ -278,6 +283,41 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
 
   // ---- epilogue: element e of acc[q][i] is D[n = 8*(e/4) + 4*lh + e%4][m = l32]
   // of the 32x32 tile (n: weight row, m: tile row) ----
+  if constexpr (MODE == 1) {
+    // The down projection writes d-wide rows: stored straight from the
+    // fragments, every 8-byte store touches 32 rows, and the store stream of a
+    // tile costs about a quarter of the kernel.  So the tile is staged in LDS
+    // (the ring is free now) and leaves row by row in 16-byte chunks, whole
+    // 128-byte lines per eight lanes.
+    vm_wait<0>();
+    lgkm_wait0();
+    compiler_fence();
+    __syncthreads();
+    compiler_fence();
+#pragma unroll
+    for (int i = 0; i < TMW; ++i) {
+      const int r = wm * (BM / WM) + i * 32 + l32;
+      char* srow = lds + r * EPITCH + (wn * (BNW / WN) + 4 * lh) * 2;
+#pragma unroll
+      for (int tj = 0; tj < TNW; ++tj)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const f32x16_t& y = acc[tj][i];
+          const uint32_t o0 = (uint32_t)f32_to_bf16(y[4 * e4 + 0]) | ((uint32_t)f32_to_bf16(y[4 * e4 + 1]) << 16);
+          const uint32_t o1 = (uint32_t)f32_to_bf16(y[4 * e4 + 2]) | ((uint32_t)f32_to_bf16(y[4 * e4 + 3]) << 16);
+          *reinterpret_cast<uint2*>(srow + (tj * 32 + 8 * e4) * 2) = make_uint2(o0, o1);
+        }
+    }
+    __syncthreads();
+    constexpr int CPR = BNW * 2 / 16;  // 16-byte chunks per row
+    const int live_rows = min(BM, rows - m0);
+    for (int q = tid; q < live_rows * CPR; q += 64 * NW) {
+      const int r = q / CPR, ch = q - r * CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + r * EPITCH + ch * 16);
+      *reinterpret_cast<uint4*>(out + (size_t)(row0 + m0 + r) * N + n0 + ch * 8) = v;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TMW; ++i) {
     const int m = m0 + wm * (BM / WM) + i * 32 + l32;
