@@ -128,6 +128,16 @@ hipError_t launch_proxy_route(int dtype, const int32_t* k, const int32_t* kappa,
 
 // path.hip -- compositional path routing (PCoMoE).  `table`: int32 src[P],
 // int32 tgt[P], float bias[P].
+// The screened router's MFMA pass alone (partials and the token scan).
+hipError_t launch_router_screen_partials(const void* x, const void* w, const int32_t* k, int T, int d, int E,
+                                         int k_max, BudgetPolicy pol, int S, float* approx, float* absum,
+                                         int32_t* tok_off, int32_t* status, hipStream_t st);
+// Screened path selection (bf16, E <= 256): MFMA-pass bounds on every path
+// score, exact logits only for the sources and targets of the candidates.
+hipError_t launch_path_screen(const void* x, const void* w_router, const void* w_tgt, const float* bias,
+                              const float* ag, const float* sg, const float* at, const float* st_, int S,
+                              const void* table, int P, float lam, const int32_t* tok_off, int T, int d, int E,
+                              int k_max, float scale, int32_t* osrc, int32_t* otgt, float* wts, hipStream_t st);
 hipError_t launch_path_topk(const double* part_g, const double* part_t, int S, const float* bias,
                             const void* table, int P, float lam, const int32_t* tok_off, int T, int E, int k_max,
                             float scale, int32_t* osrc, int32_t* otgt, float* wts, hipStream_t st);

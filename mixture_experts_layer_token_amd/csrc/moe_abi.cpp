@@ -138,12 +138,31 @@ void plan_fold(const moe_desc& d, Carver& c, FoldScratch& w) {
   w.n_members = c.take<int32_t>(1);
 }
 
-struct PathWs { double* part_g; double* part_t; int splits; int32_t* cnt; int32_t* tmp; };
+// Path routing: the screened selection (MFMA bounds, exact logits for the
+// candidates' sources and targets) where the router would screen and E <= 256;
+// otherwise every logit in float64.
+struct PathWs {
+  bool screened;
+  int splits;
+  double *part_g, *part_t;     // float64 partials (unscreened)
+  float *ag, *sg, *at, *st;    // MFMA partials and |x||w| sums (screened)
+  int32_t *cnt, *tmp;
+};
 void plan_path(const moe_desc& d, Carver& c, PathWs& w) {
-  w.splits = router_splits(d.T, d.d, d.E);
+  w.screened = d.E <= 256 && screened_router(d);
+  w.splits = w.screened ? router_screen_splits(d.T, d.d, d.E) : router_splits(d.T, d.d, d.E);
   const size_t ste = (size_t)w.splits * d.T * d.E;
-  w.part_g = c.take<double>(ste);
-  w.part_t = c.take<double>(ste);
+  w.part_g = w.part_t = nullptr;
+  w.ag = w.sg = w.at = w.st = nullptr;
+  if (w.screened) {
+    w.ag = c.take<float>(ste);
+    w.sg = c.take<float>(ste);
+    w.at = c.take<float>(ste);
+    w.st = c.take<float>(ste);
+  } else {
+    w.part_g = c.take<double>(ste);
+    w.part_t = c.take<double>(ste);
+  }
   w.cnt = c.take<int32_t>((size_t)d.T);
   w.tmp = c.take<int32_t>(a_cap(d));
 }
@@ -539,6 +558,17 @@ moe_status moe_path_route(const moe_desc* desc, const void* x, const void* w_rou
   PathWs pw;
   plan_path(d, c, pw);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pw.screened) {
+    hipError_t e = launch_router_screen_partials(x, w_router, k, d.T, d.d, d.E, d.k_max, budget(d), pw.splits, pw.ag,
+                                                 pw.sg, tok_off, dev_status, st);
+    if (e == hipSuccess && w_tgt)
+      e = launch_router_screen_partials(x, w_tgt, k, d.T, d.d, d.E, d.k_max, budget(d), pw.splits, pw.at, pw.st,
+                                        tok_off, dev_status, st);
+    if (e == hipSuccess)
+      e = launch_path_screen(x, w_router, w_tgt, router_bias, pw.ag, pw.sg, pw.at, pw.st, pw.splits, table, P,
+                             lambda, tok_off, d.T, d.d, d.E, d.k_max, d.routed_scale, path_src, path_tgt, path_w, st);
+    return launched(e);
+  }
   hipError_t e = launch_router(d.dtype, x, w_router, k, d.T, d.d, d.E, d.k_max, budget(d), pw.splits, pw.part_g,
                                tok_off, dev_status, st);
   if (e == hipSuccess && w_tgt)

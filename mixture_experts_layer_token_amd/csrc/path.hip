@@ -20,12 +20,18 @@
 //   path_rows_kernel        elementwise: the expansion row each
 //                           target-ordered path reads.
 //
+//   path_screen_kernel      (large bf16 batches) the same selection from the
+//                           screened router's MFMA pass: bounds on every
+//                           path score, exact logits only for the sources and
+//                           targets of the paths that can still be selected.
+//
 // Source-grouped reuse then needs no kernel of its own: the expansions run as
 // the grouped FFN's gate/up over the source routes, the projections as its
 // down projection over the paths grouped by target, reading their expansion
 // rows through the row map.
 #include "common.h"
 #include "launch.h"
+#include "screen.h"
 #include "select.h"
 
 namespace moe {
@@ -91,6 +97,202 @@ __global__ __launch_bounds__(256) void path_topk_kernel(const double* __restrict
         otgt[base + j] = sj[s];
       },
       wts + base, scratch);
+}
+
+// ---- screened path selection (bf16, E <= 256), one wave per token ----
+// Each logit lies within r = d * 2^-22 * sum|x||w| of its MFMA value (the
+// screened router's bound), widened by 2^-22 of its size for the rounding of
+// the exact logit to float32; the float32 logits g, t are then inside
+// [lo, hi] rounded outwards.  A path score is a monotone function of (g, t),
+// evaluated exactly as for the exact score, so its bounds are the function at
+// the interval ends.  L = the k_t-th largest lower bound (rounded down to
+// float32); a path whose upper bound is below L minus four float32 ulps is
+// beaten by k_t paths whose scores are at least L, strictly: it cannot be
+// selected.  The others get exact logits (float64 sums, screen.h) for their
+// source and target, exact scores, and the selection of select.h on those.
+// Groups of 4 rows in the cross-lane sums keep a wave's LDS area at ~8 KB
+// (E = 256), four waves per workgroup.
+constexpr int PS_GRP = 4;
+
+template <int KPL, int KE, int XC, bool XR>
+__global__ __launch_bounds__(256) void path_screen_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr, const bf16_t* __restrict__ wt,
+    const float* __restrict__ bias, const float* __restrict__ ag, const float* __restrict__ sg,
+    const float* __restrict__ at, const float* __restrict__ stt, int S, const int32_t* __restrict__ psrc,
+    const int32_t* __restrict__ ptgt, const float* __restrict__ pb, int P, float lam,
+    const int32_t* __restrict__ tok_off, int T, int d, int E, float scale, int32_t* __restrict__ osrc,
+    int32_t* __restrict__ otgt, float* __restrict__ wts, int red_words, int words) {
+  extern __shared__ uint64_t ps_lds[];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= T) return;
+  const int base = tok_off[t];
+  const int kt = tok_off[t + 1] - base;
+  const bool has_t = wt != nullptr;
+  // per-wave LDS: [red_words: row shares, later the top-k scratch][2E int32:
+  // work list][E floats each: g lo, g hi, t lo, t hi -- the lo arrays then
+  // hold the exact logits of the needed experts][2 x 256-bit masks: sources,
+  // targets needed]
+  uint64_t* const area = ps_lds + (size_t)wv * words;
+  double* const red = reinterpret_cast<double*>(area);
+  int32_t* const clist = reinterpret_cast<int32_t*>(area + red_words);
+  float* const glo = reinterpret_cast<float*>(area + red_words + E);
+  float* const ghi = glo + E;
+  float* const tlo = ghi + E;
+  float* const thi = tlo + E;
+  float* const gx = glo;
+  float* const tx = tlo;
+  uint32_t* const need = reinterpret_cast<uint32_t*>(thi + E);
+  const double rad_scale = (double)d * 0x1p-22;
+  const size_t sstride = (size_t)T * E;
+  const int nm = has_t ? 2 : 1;
+  // slice partials of the lane's experts, all (expert, matrix) pairs of a
+  // slice requested together, slices added in ascending order
+  float sa[2][KE], sq[2][KE];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int s = 0; s < KE; ++s) sa[m][s] = sq[m][s] = 0.f;
+  for (int z = 0; z < S; ++z) {
+    float va[2][KE], vq[2][KE];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int s = 0; s < KE; ++s) {
+        const int e = lane + 64 * s;
+        const bool on = e < E && m < nm;
+        const size_t off = (size_t)z * sstride + (size_t)t * E + (on ? e : 0);
+        va[m][s] = on ? (m ? at : ag)[off] : 0.f;
+        vq[m][s] = on ? (m ? stt : sg)[off] : 0.f;
+      }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int s = 0; s < KE; ++s) {
+        sa[m][s] += va[m][s];
+        sq[m][s] += vq[m][s];
+      }
+  }
+#pragma unroll
+  for (int s = 0; s < KE; ++s) {
+    const int e = lane + 64 * s;
+    if (e < E) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (m >= nm) continue;
+        const double c = (double)sa[m][s] + ((m == 0 && bias) ? (double)bias[e] : 0.0);
+        const double r = rad_scale * (double)sq[m][s] + fabs(c) * 0x1p-22 + 0x1p-126;
+        (m ? tlo : glo)[e] = __double2float_rd(c - r);
+        (m ? thi : ghi)[e] = __double2float_ru(c + r);
+      }
+    }
+  }
+  if (lane < 16) need[lane] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (kt == 0) return;
+  // Path data are re-read from the (cached) table in each phase rather than
+  // kept in registers: with up to 16 slots per lane, registers are what
+  // limits the waves per SIMD here.
+  auto score_bounds = [&](int p, double& lo, double& hi) {
+    const int i = psrc[p], j = ptgt[p];
+    const double b = (double)pb[p];
+    lo = (double)glo[i] + b;
+    hi = (double)ghi[i] + b;
+    if (has_t) {
+      const double tl = (double)tlo[j], th = (double)thi[j];
+      lo += (double)lam * (lam >= 0.f ? tl : th);
+      hi += (double)lam * (lam >= 0.f ? th : tl);
+    }
+  };
+  // L: the k_t-th largest lower bound, rounded down to float32
+  float L;
+  {
+    uint32_t lkey[KPL];
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) {
+      const int p = lane + 64 * s;
+      lkey[s] = 0;
+      if (p < P) {
+        double lo, hi;
+        score_bounds(p, lo, hi);
+        lkey[s] = logit_key(__double2float_rd(lo));
+      }
+    }
+    L = key_logit(wave_kth_largest<KPL>(lkey, kt));
+  }
+  const double cut = (double)L - (fabs((double)L) * 0x1p-21 + 0x1p-126);
+  uint32_t cand = 0;  // bit s: slot s can still be selected
+#pragma unroll
+  for (int s = 0; s < KPL; ++s) {
+    const int p = lane + 64 * s;
+    if (p < P) {
+      double lo, hi;
+      score_bounds(p, lo, hi);
+      if (hi >= cut) {
+        cand |= 1u << s;
+        const int i = psrc[p], j = ptgt[p];
+        atomicOr(&need[i >> 5], 1u << (i & 31));
+        if (has_t) atomicOr(&need[8 + (j >> 5)], 1u << (j & 31));
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // work list: the needed sources, then the needed targets, ascending
+  int n = 0;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int m = 0; m < nm; ++m) {
+#pragma unroll
+    for (int s = 0; s < KE; ++s) {
+      const int e = lane + 64 * s;
+      const bool on = e < E && ((need[8 * m + (e >> 5)] >> (e & 31)) & 1u);
+      const uint64_t mask = __ballot(on);
+      if (on) clist[n + __popcll(mask & below)] = e | (m << 16);
+      n += __popcll(mask);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // exact logits of the needed experts, over their (no longer needed) lower bounds
+  exact_dots<XC, XR, PS_GRP>(
+      x + (size_t)t * d, d, n,
+      [&](int c) {
+        const int v = clist[c];
+        return ((v >> 16) ? wt : wr) + (size_t)(v & 0xffff) * d;
+      },
+      red,
+      [&](int c, double v) {
+        const int u = clist[c], e = u & 0xffff;
+        if (u >> 16) tx[e] = (float)v;
+        else gx[e] = (float)(v + (bias ? (double)bias[e] : 0.0));
+      });
+  // exact scores of the candidates (the arithmetic of path_topk_kernel)
+  uint32_t key[KPL];
+#pragma unroll
+  for (int s = 0; s < KPL; ++s) {
+    key[s] = 0;
+    if ((cand >> s) & 1u) {
+      const int p = lane + 64 * s;
+      double v = (double)gx[psrc[p]] + (double)pb[p];
+      if (has_t) v += (double)lam * (double)tx[ptgt[p]];
+      key[s] = logit_key((float)v);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  wave_topk_softmax_emit<KPL>(
+      key, kt, scale,
+      [&](int j, int s) {
+        const int p = lane + 64 * s;
+        osrc[base + j] = psrc[p];
+        otgt[base + j] = ptgt[p];
+      },
+      wts + base, area);
 }
 
 // ---- distinct sources per token: LDS bitmap over the experts ----
@@ -220,6 +422,49 @@ hipError_t launch_path_topk(const double* part_g, const double* part_t, int S, c
   else if (P <= 512) MOE_PATH(8);
   else MOE_PATH(16);
 #undef MOE_PATH
+  return hipGetLastError();
+}
+
+template <int KPL>
+static void launch_screen_kpl(dim3 grid, size_t lds, hipStream_t st, const bf16_t* x, const bf16_t* wr,
+                              const bf16_t* wt, const float* bias, const float* ag, const float* sg, const float* at,
+                              const float* stt, int S, const int32_t* psrc, const int32_t* ptgt, const float* pb,
+                              int P, float lam, const int32_t* tok_off, int T, int d, int E, float scale,
+                              int32_t* osrc, int32_t* otgt, float* wts, int red_words, int words) {
+  if (d <= 2048)
+    hipLaunchKernelGGL((path_screen_kernel<KPL, 4, 4, true>), grid, dim3(256), lds, st, x, wr, wt, bias, ag, sg, at,
+                       stt, S, psrc, ptgt, pb, P, lam, tok_off, T, d, E, scale, osrc, otgt, wts, red_words, words);
+  else
+    hipLaunchKernelGGL((path_screen_kernel<KPL, 4, 4, false>), grid, dim3(256), lds, st, x, wr, wt, bias, ag, sg, at,
+                       stt, S, psrc, ptgt, pb, P, lam, tok_off, T, d, E, scale, osrc, otgt, wts, red_words, words);
+}
+
+hipError_t launch_path_screen(const void* x, const void* w_router, const void* w_tgt, const float* bias,
+                              const float* ag, const float* sg, const float* at, const float* stt, int S,
+                              const void* table, int P, float lam, const int32_t* tok_off, int T, int d, int E,
+                              int k_max, float scale, int32_t* osrc, int32_t* otgt, float* wts, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (E > 256) return hipErrorInvalidValue;
+  const int32_t* psrc = static_cast<const int32_t*>(table);
+  const int32_t* ptgt = psrc + P;
+  const float* pb = reinterpret_cast<const float*>(ptgt + P);
+  const int red_words = max(PS_GRP * 64, k_max + 1);
+  const int words = red_words + 3 * E + 8;
+  const size_t lds = (size_t)4 * words * sizeof(uint64_t);
+  const dim3 grid((T + 3) / 4);
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  const bf16_t* wr = static_cast<const bf16_t*>(w_router);
+  const bf16_t* wt = static_cast<const bf16_t*>(w_tgt);
+#define MOE_PSCR(KPL)                                                                                             \
+  launch_screen_kpl<KPL>(grid, lds, st, xb, wr, wt, bias, ag, sg, at, stt, S, psrc, ptgt, pb, P, lam, tok_off, T, d, \
+                         E, scale, osrc, otgt, wts, red_words, words)
+  if (P <= 64) MOE_PSCR(1);
+  else if (P <= 128) MOE_PSCR(2);
+  else if (P <= 256) MOE_PSCR(4);
+  else if (P <= 512) MOE_PSCR(8);
+  else if (P <= 768) MOE_PSCR(12);
+  else MOE_PSCR(16);
+#undef MOE_PSCR
   return hipGetLastError();
 }
 

@@ -125,7 +125,9 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __rest
   const int b0 = min(q * per, nblk), b1 = min(b0 + per, nblk);
   int part = 0;
   if (e < E) {
-#pragma unroll 8
+    // 32 loads in flight per round: with many blocks (large batches) the run
+    // is hundreds of loads long
+#pragma unroll 32
     for (int bb = b0; bb < b1; ++bb) part += block_counts[(size_t)bb * E + e];
   }
   qsum[tid] = part;
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __rest
   }
   if (e < E) {
     int r = before;
-#pragma unroll 8
+#pragma unroll 32
     for (int bb = b0; bb < b1; ++bb) {
       block_base[(size_t)bb * E + e] = r;
       r += block_counts[(size_t)bb * E + e];

@@ -27,6 +27,7 @@
 // experts defining L are candidates).
 #include "common.h"
 #include "launch.h"
+#include "screen.h"
 #include "select.h"
 
 namespace moe {
@@ -136,38 +137,7 @@ __global__ __launch_bounds__(256) void router_screen_mfma_kernel(
   }
 }
 
-// Lane share of an exact dot product over one 8-element chunk: the products
-// of bf16 values are exact in float32, each is widened and added in float64.
-// acc[q] takes elements 2q and 2q+1 (four independent chains).
-__device__ __forceinline__ void dot8(const uint4& xv, const uint4& wv, double (&acc)[4]) {
-  const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-  const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float p0 = __uint_as_float(xs[q] << 16) * __uint_as_float(ws[q] << 16);
-    const float p1 = __uint_as_float(xs[q] & 0xffff0000u) * __uint_as_float(ws[q] & 0xffff0000u);
-    acc[q] += (double)p0;
-    acc[q] += (double)p1;
-  }
-}
-
-// The same with the token's eight elements already widened to float64: one
-// fused multiply-add per element (the product of two bf16 values is exact in
-// float64, so fma(x, w, acc) rounds exactly as acc + x*w does above).
-__device__ __forceinline__ void dot8_wide(const double (&xd)[8], const uint4& wv, double (&acc)[4]) {
-  const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    acc[q] = fma(xd[2 * q], (double)__uint_as_float(ws[q] << 16), acc[q]);
-    acc[q] = fma(xd[2 * q + 1], (double)__uint_as_float(ws[q] & 0xffff0000u), acc[q]);
-  }
-}
-
 // ---- pass 2: candidates, exact logits, top-k_t and weights; one wave per token.
-// Exact dot products run in passes of 512 * XC elements (lane l takes
-// elements [8l + 512 i, +8) of chunk i).
-constexpr int SEL_GRP = 8;  // candidates whose cross-lane sums are done together
-
 // XR: the token row fits one pass (d <= 512 * XC) and is loaded once, before
 // the candidates, instead of once per candidate.
 template <int KPL, int XC, bool XR>
@@ -249,78 +219,10 @@ __global__ __launch_bounds__(256) void router_screen_select_kernel(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // Exact logits.  Work items (candidate c, pass p) in order, p fastest; the
-  // router row and token row chunks of item i+1 are requested before item i
-  // is summed.  Each lane's share of a candidate goes to red[c % SEL_GRP][lane];
-  // every SEL_GRP candidates, lane j adds the 64 shares of candidate j of the
-  // group in lane order and stores the rounded logit's key.
-  const bf16_t* xrow = x + (size_t)t * d;
-  constexpr int PASS = 512 * XC;
-  const int npass = (d + PASS - 1) / PASS;
-  const int items = ncand * npass;
-  // resident token row (XR), widened to float64 once
-  double xd[XR ? XC : 1][8];
-  if constexpr (XR) {
-#pragma unroll
-    for (int i = 0; i < XC; ++i) {
-      const int off = 512 * i + 8 * lane;
-      const uint4 v = off < d ? *reinterpret_cast<const uint4*>(xrow + off) : zero_u4();
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        xd[i][2 * q] = (double)__uint_as_float(u[q] << 16);
-        xd[i][2 * q + 1] = (double)__uint_as_float(u[q] & 0xffff0000u);
-      }
-    }
-  }
-  auto load_item = [&](uint4 (&xv)[XC], uint4 (&wr)[XC], int it) {
-    const int c = it / npass, p0 = (it - c * npass) * PASS;
-    const bf16_t* row = w + (size_t)clist[c] * d;
-#pragma unroll
-    for (int i = 0; i < XC; ++i) {
-      const int off = p0 + 512 * i + 8 * lane;
-      if constexpr (!XR) xv[i] = off < d ? *reinterpret_cast<const uint4*>(xrow + off) : zero_u4();
-      wr[i] = off < d ? *reinterpret_cast<const uint4*>(row + off) : zero_u4();
-    }
-  };
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  auto finish_item = [&](int it, const uint4 (&xv)[XC], const uint4 (&wr)[XC]) {
-#pragma unroll
-    for (int i = 0; i < XC; ++i) {
-      if constexpr (XR) dot8_wide(xd[i], wr[i], acc);
-      else dot8(xv[i], wr[i], acc);
-    }
-    const int c = it / npass;
-    if (it - c * npass == npass - 1) {  // candidate complete
-      red[(c % SEL_GRP) * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-      acc[0] = acc[1] = acc[2] = acc[3] = 0.0;
-      if (c % SEL_GRP == SEL_GRP - 1 || c == ncand - 1) {
-        const int g0 = c - c % SEL_GRP;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane <= c - g0) {
-          double v = 0.0;
-          for (int l = 0; l < 64; ++l) v += red[lane * 64 + l];
-          cval[g0 + lane] = v;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
-    }
-  };
-  uint4 xa[XC], wa[XC], xb[XC], wb[XC];
-  if (items > 0) load_item(xa, wa, 0);
-  for (int it = 0; it < items; it += 2) {
-    if (it + 1 < items) load_item(xb, wb, it + 1);
-    finish_item(it, xa, wa);
-    if (it + 2 < items) load_item(xa, wa, it + 2);
-    if (it + 1 < items) finish_item(it + 1, xb, wb);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // exact logits of the candidates
+  exact_dots<XC, XR, SEL_GRP>(
+      x + (size_t)t * d, d, ncand, [&](int c) { return w + (size_t)clist[c] * d; }, red,
+      [&](int c, double v) { cval[c] = v; });
   // keys of the candidates (bias added in float64 before the one rounding)
   uint32_t key[KPL];
 #pragma unroll
@@ -355,12 +257,18 @@ static void launch_select(dim3 grid, size_t lds, hipStream_t st, const bf16_t* x
                        absum, S, tok_off, T, d, E, scale, ids, wts, red_words, words);
 }
 
+hipError_t launch_router_screen_partials(const void* x, const void* w, const int32_t* k, int T, int d, int E,
+                                         int k_max, BudgetPolicy pol, int S, float* approx, float* absum,
+                                         int32_t* tok_off, int32_t* status, hipStream_t st) {
+  hipLaunchKernelGGL(router_screen_mfma_kernel, dim3(max(1, (T + 63) / 64), (E + 255) / 256, S + 1), dim3(256), 0, st,
+                     (const bf16_t*)x, (const bf16_t*)w, T, d, E, approx, absum, k, k_max, pol, tok_off, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_router_screen(const void* x, const void* w, const float* bias, const int32_t* k, int T, int d,
                                 int E, int k_max, BudgetPolicy pol, int S, float scale, float* approx, float* absum,
                                 int32_t* tok_off, int32_t* status, int32_t* ids, float* wts, hipStream_t st) {
-  hipLaunchKernelGGL(router_screen_mfma_kernel, dim3(max(1, (T + 63) / 64), (E + 255) / 256, S + 1), dim3(256), 0, st,
-                     (const bf16_t*)x, (const bf16_t*)w, T, d, E, approx, absum, k, k_max, pol, tok_off, status);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch_router_screen_partials(x, w, k, T, d, E, k_max, pol, S, approx, absum, tok_off, status, st);
   if (err != hipSuccess || T == 0) return err;
   dim3 grid((T + 3) / 4);
   const int red_words = max(SEL_GRP * 64, k_max + 1);

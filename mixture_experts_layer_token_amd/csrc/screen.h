@@ -1,0 +1,121 @@
+// Exact dot products for the screened routers (the MoE router and the
+// compositional-path router): a token row against a list of weight rows under
+// the routing contract -- products of bf16 values are exact in float32 and in
+// float64, the sums are taken in float64 -- one wave per token.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// Lane share of an exact dot product over one 8-element chunk: the products
+// of bf16 values are exact in float32, each is widened and added in float64.
+// acc[q] takes elements 2q and 2q+1 (four independent chains).
+__device__ __forceinline__ void dot8(const uint4& xv, const uint4& wv, double (&acc)[4]) {
+  const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+  const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float p0 = __uint_as_float(xs[q] << 16) * __uint_as_float(ws[q] << 16);
+    const float p1 = __uint_as_float(xs[q] & 0xffff0000u) * __uint_as_float(ws[q] & 0xffff0000u);
+    acc[q] += (double)p0;
+    acc[q] += (double)p1;
+  }
+}
+
+// The same with the token's eight elements already widened to float64: one
+// fused multiply-add per element (the product of two bf16 values is exact in
+// float64, so fma(x, w, acc) rounds exactly as acc + x*w does above).
+__device__ __forceinline__ void dot8_wide(const double (&xd)[8], const uint4& wv, double (&acc)[4]) {
+  const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[q] = fma(xd[2 * q], (double)__uint_as_float(ws[q] << 16), acc[q]);
+    acc[q] = fma(xd[2 * q + 1], (double)__uint_as_float(ws[q] & 0xffff0000u), acc[q]);
+  }
+}
+
+// Exact dot products run in passes of 512 * XC elements (lane l takes
+// elements [8l + 512 i, +8) of chunk i).
+constexpr int SEL_GRP = 8;  // rows whose cross-lane sums are done together
+
+// Exact dot products of the token row xrow with n rows (row_of(c), c < n),
+// under the routing contract: exact products, float64 accumulation.  Work
+// items (row c, pass p) in order, p fastest; the rows' chunks of item i+1 are
+// requested before item i is summed.  Each lane's share of a row goes to
+// red[c % GRP][lane] (GRP * 64 doubles of LDS); every GRP rows, lane j adds
+// the 64 shares of row j of the group in lane order and calls sink(c, sum).
+// One wave; ends with the wave's LDS writes visible.
+template <int XC, bool XR, int GRP, class RowOf, class Sink>
+__device__ __forceinline__ void exact_dots(const bf16_t* __restrict__ xrow, int d, int n, RowOf row_of, double* red,
+                                           Sink sink) {
+  const int lane = threadIdx.x & 63;
+  constexpr int PASS = 512 * XC;
+  const int npass = (d + PASS - 1) / PASS;
+  const int items = n * npass;
+  // resident token row (XR), widened to float64 once
+  double xd[XR ? XC : 1][8];
+  if constexpr (XR) {
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int off = 512 * i + 8 * lane;
+      const uint4 v = off < d ? *reinterpret_cast<const uint4*>(xrow + off) : zero_u4();
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xd[i][2 * q] = (double)__uint_as_float(u[q] << 16);
+        xd[i][2 * q + 1] = (double)__uint_as_float(u[q] & 0xffff0000u);
+      }
+    }
+  }
+  auto load_item = [&](uint4 (&xv)[XC], uint4 (&wr)[XC], int it) {
+    const int c = it / npass, p0 = (it - c * npass) * PASS;
+    const bf16_t* row = row_of(c);
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int off = p0 + 512 * i + 8 * lane;
+      if constexpr (!XR) xv[i] = off < d ? *reinterpret_cast<const uint4*>(xrow + off) : zero_u4();
+      wr[i] = off < d ? *reinterpret_cast<const uint4*>(row + off) : zero_u4();
+    }
+  };
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  auto finish_item = [&](int it, const uint4 (&xv)[XC], const uint4 (&wr)[XC]) {
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      if constexpr (XR) dot8_wide(xd[i], wr[i], acc);
+      else dot8(xv[i], wr[i], acc);
+    }
+    const int c = it / npass;
+    if (it - c * npass == npass - 1) {  // row complete
+      red[(c % GRP) * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      acc[0] = acc[1] = acc[2] = acc[3] = 0.0;
+      if (c % GRP == GRP - 1 || c == n - 1) {
+        const int g0 = c - c % GRP;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane <= c - g0) {
+          double v = 0.0;
+          for (int l = 0; l < 64; ++l) v += red[lane * 64 + l];
+          sink(g0 + lane, v);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    }
+  };
+  uint4 xa[XC], wa[XC], xb[XC], wb[XC];
+  if (items > 0) load_item(xa, wa, 0);
+  for (int it = 0; it < items; it += 2) {
+    if (it + 1 < items) load_item(xb, wb, it + 1);
+    finish_item(it, xa, wa);
+    if (it + 2 < items) load_item(xa, wa, it + 2);
+    if (it + 1 < items) finish_item(it + 1, xb, wb);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace moe

@@ -34,10 +34,11 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def _run(layer, k_max, src, tgt, bias, w_tgt, lam, path="auto"):
+def _run(layer, k_max, src, tgt, bias, w_tgt, lam, path="auto", router="auto"):
     T, d = layer.x.shape
     E, I, _ = layer.w_gate.shape
-    desc = moe.make_desc(T, d, E, I, k_max, dtype=layer.x.dtype, routed_scale=layer.cfg.routed_scale, path=path)
+    desc = moe.make_desc(T, d, E, I, k_max, dtype=layer.x.dtype, routed_scale=layer.cfg.routed_scale, path=path,
+                         router=router)
     table = moe.moe_path_table(E, src, tgt, bias)
     pl = moe.PathLayer(desc, table, len(src), lam, layer.device)
     out = torch.empty((T, d), dtype=layer.x.dtype, device=layer.device)
@@ -183,3 +184,67 @@ def test_paths_edges(T, E, k_max, extra):
                                    tokens=tokens)
         compare_out(out, want, "f32", tokens)
     _say(f"[path] edge T={T} E={E} k_max={k_max} P={len(src)}: routes {g['A']}")
+
+
+@pytest.mark.parametrize("T,E,d,k_max,extra,lam,tgt,bias", [(700, 8, 256, 2, 2, 0.5, True, False),
+                                                            (513, 64, 512, 8, 3, -0.75, True, True),
+                                                            (300, 256, 2304, 16, 2, 0.5, True, False),
+                                                            (257, 256, 256, 32, 3, 0.0, False, True),
+                                                            (96, 32, 128, 6, 31, 1.5, True, False)])
+def test_screened_path_router_bit_exact(T, E, d, k_max, extra, lam, tgt, bias):
+    """The screened path selection (MFMA bounds, exact logits for the
+    candidates' sources and targets) gives the float64 path router's routes
+    and weights bit for bit, and the oracle's routes (with a router bias, a
+    negative lambda, no target prior, every pair active, d past one pass)."""
+    rng = np.random.default_rng(T * E)
+    k = rng.integers(0, k_max + 1, size=T)
+    k[0] = k_max
+    layer = make_custom_layer(T, d, E, 128, k, dtype="bf16", k_max=k_max, zipf=1.1 if bias else 0.0, seed=E,
+                              device="cuda")
+    w_tgt = make_target_router(layer.cfg, "cuda") if tgt else None
+    src, tgt_ids, pbias = make_path_mask(E, extra, seed=E + 1)
+    outs = {}
+    for router in ("float64", "screened"):
+        pl, out = _run(layer, k_max, src, tgt_ids, pbias, w_tgt, lam, router=router)
+        outs[router] = (_host(pl), out, pl.w[:int(pl.tok_off[-1].item())].clone())
+    a, b = outs["float64"][0], outs["screened"][0]
+    for key in ("tok_off", "src", "tgt", "src_off", "src_ids", "p2s"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    assert torch.equal(outs["float64"][2], outs["screened"][2]), "weights differ"
+    assert torch.equal(outs["float64"][1], outs["screened"][1]), "outputs differ"
+    ref = oracle.path_route(to_f64(layer.x), to_f64(layer.w_router), to_f64(layer.router_bias),
+                            None if w_tgt is None else to_f64(w_tgt), np.float32(lam), src, tgt_ids,
+                            pbias.astype(np.float64), to_f64(layer.k), k_max)
+    np.testing.assert_array_equal(b["src"], ref["src"])
+    np.testing.assert_array_equal(b["tgt"], ref["tgt"])
+    np.testing.assert_allclose(b["w"], ref["w"], rtol=2e-6, atol=2e-7)
+    _say(f"[path] screened T={T} E={E} d={d} P={len(src)}: routes {b['A']} bit-exact")
+
+
+def test_screened_path_router_full_size():
+    """Sub-expert prefill batch (8,192 tokens, 256 experts, k <= 32, 768
+    paths): the auto-selected screened path router equals the float64 one on
+    every token."""
+    cfg = CONFIGS["subexpert_prefill"]
+    layer = make_layer(cfg, "cuda")
+    w_tgt = make_target_router(cfg, "cuda")
+    src, tgt, bias = make_path_mask(cfg.E, 2, seed=0)
+    res = {}
+    for router in ("float64", "auto"):
+        pl, out = _run(layer, cfg.k_max, src, tgt, bias, w_tgt, 0.5, router=router)
+        res[router] = (_host(pl), pl.w[:int(pl.tok_off[-1].item())].clone(), out)
+        del pl
+    a, b = res["float64"][0], res["auto"][0]
+    for key in ("tok_off", "src", "tgt", "src_off", "src_ids", "p2s"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    assert torch.equal(res["float64"][1], res["auto"][1])
+    assert torch.equal(res["float64"][2], res["auto"][2])
+    tokens = sample_tokens(cfg.T, 24)
+    ref = oracle.path_route(to_f64(layer.x)[tokens], to_f64(layer.w_router), None, to_f64(w_tgt), np.float32(0.5),
+                            src, tgt, bias.astype(np.float64), to_f64(layer.k)[tokens], cfg.k_max)
+    for i, t in enumerate(tokens):
+        lo, hi = b["tok_off"][t], b["tok_off"][t + 1]
+        r0, r1 = ref["tok_off"][i], ref["tok_off"][i + 1]
+        np.testing.assert_array_equal(b["src"][lo:hi], ref["src"][r0:r1])
+        np.testing.assert_array_equal(b["tgt"][lo:hi], ref["tgt"][r0:r1])
+    _say(f"[path] screened full size: routes {b['A']} bit-exact with the float64 path router")
