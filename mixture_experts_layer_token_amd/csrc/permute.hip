@@ -105,8 +105,32 @@ __global__ __launch_bounds__(PERM_BLOCK) void expert_hist_kernel(const int32_t* 
   }
 }
 
+// Many blocks (large batches): one workgroup per expert adds the expert's
+// block counts and writes their exclusive prefix (block_base) and total
+// (counts), so the one-workgroup scan below only scans the experts.
+__global__ __launch_bounds__(256) void expert_block_scan_kernel(const int32_t* __restrict__ block_counts, int nblk,
+                                                                int E, int32_t* __restrict__ block_base,
+                                                                int32_t* __restrict__ counts) {
+  __shared__ int32_t wsum[4];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int per = (nblk + 255) / 256;
+  const int b0 = min(tid * per, nblk), b1 = min(b0 + per, nblk);
+  int s = 0;
+#pragma unroll 16
+  for (int bb = b0; bb < b1; ++bb) s += block_counts[(size_t)bb * E + e];
+  const int incl = block_scan_incl<256>(s, wsum);
+  int r = incl - s;
+#pragma unroll 16
+  for (int bb = b0; bb < b1; ++bb) {
+    block_base[(size_t)bb * E + e] = r;
+    r += block_counts[(size_t)bb * E + e];
+  }
+  if (tid == 255) counts[e] = incl;
+}
+
 // One workgroup: per-expert running sums over blocks, then the exclusive scan
-// over experts.  Q = 1024 / E' threads share an expert (E' = E rounded up to a
+// over experts.  With `presummed` the totals are already in counts and the
+// block bases written (expert_block_scan_kernel).  Q = 1024 / E' threads share an expert (E' = E rounded up to a
 // power of two): thread (e, q) sums a contiguous run of blocks, the runs'
 // sums are scanned per expert, then every thread writes its blocks' bases.
 __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __restrict__ block_counts, int nblk,
@@ -115,7 +139,7 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ expert_off,
                                                            int32_t* __restrict__ n_active,
                                                            int32_t* __restrict__ stats, int RB, int bound,
-                                                           int4* __restrict__ blocks) {
+                                                           int4* __restrict__ blocks, int presummed) {
   __shared__ int32_t sc[1024];
   __shared__ int32_t qsum[1024];
   __shared__ int32_t nact, nblocks;
@@ -124,7 +148,9 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __rest
   const int per = (nblk + Q - 1) / Q;
   const int b0 = min(q * per, nblk), b1 = min(b0 + per, nblk);
   int part = 0;
-  if (e < E) {
+  if (presummed) {
+    part = (q == 0 && e < E) ? counts[e] : 0;
+  } else if (e < E) {
     // 32 loads in flight per round: with many blocks (large batches) the run
     // is hundreds of loads long
 #pragma unroll 32
@@ -140,7 +166,7 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(const int32_t* __rest
     if (j < q) before += v;
     run += v;
   }
-  if (e < E) {
+  if (e < E && !presummed) {
     int r = before;
 #pragma unroll 32
     for (int bb = b0; bb < b1; ++bb) {
@@ -351,8 +377,15 @@ hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int
   }
   int Q = 1;  // threads per expert in the scan: a power of two with Q * E <= 1024
   while (Q * 2 * E <= 1024) Q *= 2;
+  // beyond 64 blocks per thread group the block sums move to one workgroup per expert
+  const int presummed = nblk > 64 * Q ? 1 : 0;
+  if (presummed) {
+    hipLaunchKernelGGL(expert_block_scan_kernel, dim3(E), dim3(256), 0, st, block_counts, nblk, E, block_base, counts);
+    hipError_t e1 = hipGetLastError();
+    if (e1 != hipSuccess) return e1;
+  }
   hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, st, block_counts, nblk, E, Q, block_base, counts,
-                     expert_off, n_active, stats, RB, bound, blocks);
+                     expert_off, n_active, stats, RB, bound, blocks, presummed);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nblk == 0) return err;
   hipLaunchKernelGGL(expert_scatter_kernel, dim3(nblk * SCATTER_SPLIT), dim3(PERM_BLOCK), 2 * lds, st, tok_off, ids,
