@@ -561,11 +561,13 @@ def path_sources(tok_off, src):
 
 
 def path_forward(x, tok_off, src, tgt, w, w_gate, w_up, w_down, tokens: Optional[Sequence[int]] = None,
-                 counter: Optional[dict] = None) -> np.ndarray:
+                 counter: Optional[dict] = None, shared: Optional[Sequence[Any]] = None) -> np.ndarray:
     """Layer output over paths, source-grouped: for each token, U_i runs once
     per distinct source i and D_j once per path (i, j):
-        y = sum_i sum_{j in T_i} beta_ij D_j(U_i(h)).
-    counter, if given, receives the number of U and D evaluations."""
+        y = sum_i sum_{j in T_i} beta_ij D_j(U_i(h)),
+    plus the always-on shared expert with weight 1 when given (as in the
+    vanilla layer, MoE-Prism §II-B).  counter, if given, receives the number
+    of U and D evaluations."""
     x = np.asarray(x)
     tok_off = np.asarray(tok_off, dtype=np.int64)
     if tokens is None:
@@ -584,6 +586,8 @@ def path_forward(x, tok_off, src, tgt, w, w_gate, w_up, w_down, tokens: Optional
             for j, b in paths:
                 out[r] += b * (_f64(w_down[j]) @ z)
                 n_d += 1
+    if shared is not None:
+        out += swiglu_expert(_f64(x[tokens]), shared[0], shared[1], shared[2])
     if counter is not None:
         counter["U"] = n_u
         counter["D"] = n_d

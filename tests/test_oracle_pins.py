@@ -657,6 +657,15 @@ def test_path_diagonal_mask_reproduces_vanilla():
     want, _ = oracle.forward(a["x"], a["w_router"], a["bias"], k, E, a["w_gate"], a["w_up"], a["w_down"],
                              routed_scale=1.5)
     np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-14)
+    # with an always-on shared expert, on a layer that has one
+    L = make_custom_layer(T=T, d=24, E=E, I=16, k=k, I_shared=8, seed=44)
+    b = _arrays(L)
+    r = oracle.path_route(b["x"], b["w_router"], b["bias"], None, 0.0, diag, diag, np.zeros(E), k, E)
+    out = oracle.path_forward(b["x"], r["tok_off"], r["src"], r["tgt"], r["w"], b["w_gate"], b["w_up"], b["w_down"],
+                              shared=b["shared"])
+    want, _ = oracle.forward(b["x"], b["w_router"], b["bias"], k, E, b["w_gate"], b["w_up"], b["w_down"],
+                             shared=b["shared"])
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-14)
 
 
 def test_path_forward_is_the_sum_over_paths():
