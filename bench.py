@@ -269,11 +269,10 @@ def main():
         table = moe.moe_path_table(E, p_src, p_tgt, p_bias, dev)
         pl = moe.PathLayer(desc, table, len(p_src), lam, dev)
         w_tgt = make_target_router(cfg, dev)
+        sh_w = (layer.ws_gate, layer.ws_up, layer.ws_down) if Is else None
         paths = dict(layer=pl, P=len(p_src), extra=int(extra), lam=lam,
                      run=lambda o: pl.run(layer.x, layer.w_router, layer.router_bias, w_tgt, layer.k, layer.w_gate,
-                                          layer.w_up, layer.w_down, o))
-        if Is:
-            raise SystemExit("--paths runs routed experts only (no shared expert)")
+                                          layer.w_up, layer.w_down, o, shared=sh_w))
 
         def step():
             paths["run"](out)
@@ -464,7 +463,7 @@ def main():
     if paths is not None:
         # expansions (gate/up) over the active sources, projections over the active targets
         w_bytes = (2 * n_act + paths["targets_active"]) * d * I * esz
-        ffn_flops = 4.0 * d * I * A + 2.0 * d * I * paths["routes"]
+        ffn_flops = 4.0 * d * I * A + 2.0 * d * I * paths["routes"] + 6.0 * d * Is * T
     all_bytes = w_bytes + 3 * d * Is * esz + E * d * esz + 2 * T * d * esz
     layer_s = ms_step * 1e-3
     layer_info = {"activated_weight_GBps": round(w_bytes / layer_s / 1e9, 1),

@@ -349,13 +349,19 @@ class PathLayer:
         self.row_map = torch.empty(A, **i32)
         self.h = torch.empty((A, I), dtype=dtype, device=device)
         self.y = torch.empty((A, d), dtype=dtype, device=device)
+        # the always-on shared expert: moe_ffn over an empty routed set
+        self.zero_eoff = torch.zeros(E + 1, **i32)
+        self.y_sh = torch.empty((max(T, 1), d), dtype=dtype, device=device) if desc.I_shared else None
         self.ws_path = alloc_workspace(desc, MOE_OP_PATH, device)
         self.ws_perm = alloc_workspace(desc, MOE_OP_PERMUTE, device)
         self.ws_uperm = alloc_workspace(self.unit, MOE_OP_PERMUTE, device)
         self.ws_ffn = alloc_workspace(desc, MOE_OP_FFN, device)
 
-    def run(self, x, w_router, router_bias, w_tgt, k, w_gate, w_up, w_down, out, stream=None):
+    def run(self, x, w_router, router_bias, w_tgt, k, w_gate, w_up, w_down, out, shared=None, stream=None):
+        """shared = (ws_gate, ws_up, ws_down) when the descriptor has I_shared > 0."""
         d, u = self.desc, self.unit
+        if d.I_shared and shared is None:
+            raise ValueError("the descriptor has a shared expert: pass its weights")
         moe_path_route(d, x, w_router, router_bias, w_tgt, self.lam, self.table, self.P, k, self.tok_off, self.src,
                        self.tgt, self.w, self.status, self.ws_path, stream)
         moe_path_sources(d, self.tok_off, self.src, self.src_off, self.src_ids, self.p2s, self.unit_off,
@@ -369,4 +375,7 @@ class PathLayer:
         moe_path_rows(d, self.tok_off, self.t_ptok, self.p2s, self.s_inv, self.row_map, stream)
         moe_ffn_plan(u, self.t_eoff, self.ws_ffn, stream)
         moe_ffn_down_rows(u, self.h, self.row_map, w_down, self.t_eoff, self.y, self.ws_ffn, stream)
-        moe_combine(d, self.y, None, self.tok_off, self.w, self.t_inv, out, stream)
+        if d.I_shared:
+            moe_ffn(d, x, w_gate, w_up, w_down, *shared, self.zero_eoff, self.s_ptok, self.y, self.y_sh, self.ws_ffn,
+                    stream)
+        moe_combine(d, self.y, self.y_sh if d.I_shared else None, self.tok_off, self.w, self.t_inv, out, stream)

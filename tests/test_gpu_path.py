@@ -37,12 +37,15 @@ def _gpu():
 def _run(layer, k_max, src, tgt, bias, w_tgt, lam, path="auto", router="auto"):
     T, d = layer.x.shape
     E, I, _ = layer.w_gate.shape
-    desc = moe.make_desc(T, d, E, I, k_max, dtype=layer.x.dtype, routed_scale=layer.cfg.routed_scale, path=path,
-                         router=router)
+    Is = layer.ws_gate.shape[0] if layer.ws_gate is not None else 0
+    desc = moe.make_desc(T, d, E, I, k_max, I_shared=Is, dtype=layer.x.dtype, routed_scale=layer.cfg.routed_scale,
+                         path=path, router=router)
     table = moe.moe_path_table(E, src, tgt, bias)
     pl = moe.PathLayer(desc, table, len(src), lam, layer.device)
     out = torch.empty((T, d), dtype=layer.x.dtype, device=layer.device)
-    pl.run(layer.x, layer.w_router, layer.router_bias, w_tgt, layer.k, layer.w_gate, layer.w_up, layer.w_down, out)
+    sh = (layer.ws_gate, layer.ws_up, layer.ws_down) if Is else None
+    pl.run(layer.x, layer.w_router, layer.router_bias, w_tgt, layer.k, layer.w_gate, layer.w_up, layer.w_down, out,
+           shared=sh)
     torch.cuda.synchronize()
     return pl, out
 
@@ -248,3 +251,33 @@ def test_screened_path_router_full_size():
         np.testing.assert_array_equal(b["src"][lo:hi], ref["src"][r0:r1])
         np.testing.assert_array_equal(b["tgt"][lo:hi], ref["tgt"][r0:r1])
     _say(f"[path] screened full size: routes {b['A']} bit-exact with the float64 path router")
+
+
+@pytest.mark.parametrize("T,Is,I", [(300, 256, 256), (90, 128, 256), (600, 256, 256)])
+def test_paths_with_shared_expert(T, Is, I):
+    """A layer with an always-on shared expert: the diagonal-only list
+    reproduces moe_forward bit for bit (the shared expert fused into the
+    routed GEMM launches when it is as wide as a routed expert, separate
+    otherwise), and a general list matches the oracle."""
+    E, k_max = 16, 4
+    rng = np.random.default_rng(T + Is)
+    k = rng.integers(0, k_max + 1, size=T)
+    layer = make_custom_layer(T, 256, E, I, k, dtype="bf16", k_max=k_max, I_shared=Is, seed=17, device="cuda")
+    diag = np.arange(E, dtype=np.int32)
+    want, _, _ = moe.forward(layer.x, layer.w_router, layer.router_bias, layer.k, layer.w_gate, layer.w_up,
+                             layer.w_down, (layer.ws_gate, layer.ws_up, layer.ws_down), k_max=k_max)
+    pl, out = _run(layer, k_max, diag, diag, np.zeros(E, np.float32), None, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(out, want), "diagonal paths with a shared expert differ from moe_forward"
+    w_tgt = make_target_router(layer.cfg, "cuda")
+    src, tgt, bias = make_path_mask(E, 3, seed=2)
+    pl, out = _run(layer, k_max, src, tgt, bias, w_tgt, 0.5)
+    ref = oracle.path_route(to_f64(layer.x), to_f64(layer.w_router), None, to_f64(w_tgt), np.float32(0.5), src, tgt,
+                            bias.astype(np.float64), to_f64(layer.k), k_max)
+    tokens = sample_tokens(T, 40)
+    want = oracle.path_forward(to_f64(layer.x), ref["tok_off"], ref["src"], ref["tgt"], ref["w"],
+                               ExpertView(layer.w_gate), ExpertView(layer.w_up), ExpertView(layer.w_down),
+                               tokens=tokens, shared=(to_f64(layer.ws_gate), to_f64(layer.ws_up),
+                                                      to_f64(layer.ws_down)))
+    err = compare_out(out, want, "bf16", tokens)
+    _say(f"[path] shared expert T={T} I_shared={Is}: {err}")
