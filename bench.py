@@ -46,6 +46,9 @@ def parse():
                          "GPU clocks have settled before timing")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--eager", action="store_true", help="time plain launches instead of a HIP graph")
+    ap.add_argument("--graph-steps", type=int, default=4,
+                    help="layer steps captured back to back in one HIP graph, as a model's layers would be (the "
+                         "largest divisor of --steps not above this); 1 = one graph replay per step")
     ap.add_argument("--router", default="auto", choices=["auto", "float64", "screened"],
                     help="router algorithm (both give identical routing; they differ in cost)")
     ap.add_argument("--path", default="auto", choices=["auto", "stream", "gemm"], help="FFN path")
@@ -290,10 +293,14 @@ def main():
         step()
     stream.synchronize()
     graph = None
+    # steps per graph replay: a divisor of --steps, so that exactly --steps run
+    g_steps = 1
     if not args.eager:
+        g_steps = max(g for g in range(1, max(1, args.graph_steps) + 1) if args.steps % g == 0)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            step()
+            for _ in range(g_steps):
+                step()
     run = graph.replay if graph is not None else step
 
     with torch.cuda.stream(stream):
@@ -301,8 +308,8 @@ def main():
         n = 0
         while n < args.warmup or time.perf_counter() - w_start < args.warmup_seconds:
             run()
-            n += 1
-            if n % 8 == 0:
+            n += g_steps
+            if (n // g_steps) % 8 == 0:
                 stream.synchronize()
         stream.synchronize()
         n_warm = n
@@ -311,7 +318,7 @@ def main():
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         t_start.record(stream)
-        for _ in range(args.steps):
+        for _ in range(args.steps // g_steps):
             run()
         t_end.record(stream)
         torch.cuda.synchronize()
@@ -497,7 +504,8 @@ def main():
         "data": "synthetic (seeded Gaussian layer, random-init weights)",
         "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "I": I, "I_shared": Is,
                    "k_values": k_desc, "k_max": cfg.k_max, "A": A, "n_active": n_act,
-                   "execution": "eager" if args.eager else "hip_graph", "ffn_path": routed_path,
+                   "execution": "eager" if args.eager else f"hip_graph ({g_steps} steps per replay)",
+                   "ffn_path": routed_path,
                    "router": args.router, "k_policy": args.k_policy, "k_dist": args.k_dist or "workload",
                    "fold": args.fold or "none", "proxy": proxy_info or "none",
                    "paths": ({"P": paths["P"], "extra_per_source": paths["extra"], "lambda": paths["lam"],
