@@ -236,7 +236,9 @@ __device__ __forceinline__ void stream_block(const T* __restrict__ in, const int
 // `ring` holds 3 stages of 16 KB: [weights 64 x 128 B][activations 64 x 128 B].
 constexpr int SHARED_STAGES = 3, SHARED_STAGE_BYTES = 2 * 64 * 128;
 
-template <typename T, int MODE, int KC, int TPW>
+// VAR bit 1: the weight DMA carries the non-temporal hint (the weights are
+// read once per layer).
+template <typename T, int MODE, int KC, int TPW, int VAR = 0>
 __device__ __forceinline__ void stream_block_shared(const T* __restrict__ in, const int32_t* __restrict__ row_map,
                                                     const T* w0, const T* w1, int K, int mg, int rows,
                                                     T* __restrict__ out, int N, int n0, char* ring) {
@@ -278,7 +280,8 @@ __device__ __forceinline__ void stream_block_shared(const T* __restrict__ in, co
     char* sb = ring + (s % NST) * SB + wave * 2048;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[q] + s * STEP), (lds_ptr_t)(sb + q * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[q] + s * STEP), (lds_ptr_t)(sb + q * 1024), 16, 0,
+                                       (VAR & 2) ? 2 : 0);
       if (xon[q])
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)(xsrc[q] + s * STEP), (lds_ptr_t)(sb + XOFS + q * 1024), 16, 0,
                                          0);
@@ -340,7 +343,10 @@ __device__ __forceinline__ void stream_block_shared(const T* __restrict__ in, co
 // on the same XCD and share its L2 copy of the weight tile.  Blocks hold up to
 // 32*SMT rows (two row groups of 16*SMT).  OCC: waves per SIMD the register
 // allocation must allow (1: no constraint).
-template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL, int OCC>
+// VAR (shared-tile configurations only): bit 0 runs every block through the
+// shared-tile body (the direct body is then not compiled in, which also frees
+// its registers); bit 1 as in stream_block_shared.
+template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL, int OCC, int VAR = 0>
 __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void ffn_stream_kernel(
     const T* __restrict__ in, const int32_t* __restrict__ row_map, const T* __restrict__ w0,
     const T* __restrict__ w1, const int4* __restrict__ blocks, int dense_rows, T* __restrict__ out, int N, int K,
@@ -387,7 +393,7 @@ __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OC
   const T* const wrow_b = (MODE == 0 ? w1 : w0) + g * gstride + (size_t)(n0 + lr) * K + lofs;
   // With a short K (under four steps per wave when split WK ways) every
   // block takes the shared-tile body, whose waves each run the whole K.
-  const int light_max = (!SHARED || K / WK / STEP >= 4) ? GR : 0;
+  const int light_max = !SHARED ? GR : ((VAR & 1) ? 0 : (K / WK / STEP >= 4 ? GR : 0));
   if (rows <= light_max) {
     // one row group; the WK waves split K
     const int Kw = K / WK, kbeg = wk * Kw, nsteps = Kw / STEP;
@@ -398,7 +404,7 @@ __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OC
       stream_block<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kbeg, wrow_b + kbeg, K, kbeg,
                                                                 lofs, nsteps, mg, rows, out, N, n0, red, wn, wk, 0);
   } else if constexpr (SHARED) {
-    stream_block_shared<T, MODE, KC, TPW>(in, row_map, w0 + g * gstride, (MODE == 0 ? w1 : w0) + g * gstride, K, mg,
+    stream_block_shared<T, MODE, KC, TPW, VAR>(in, row_map, w0 + g * gstride, (MODE == 0 ? w1 : w0) + g * gstride, K, mg,
                                           rows, out, N, n0, smem);
   } else {
     // two row groups; WK/2 waves split K within each
@@ -422,7 +428,8 @@ __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OC
 template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL = true, int OCC = 1>
 constexpr int stream_nb() { return WN * ((MODE == 0) ? 8 * TPW : 16 * TPW); }
 
-template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL = true, int OCC = 1>
+template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL = true, int OCC = 1,
+          int VAR = 0>
 hipError_t launch_stream_variant(const T* in, const int32_t* row_map, const T* w0, const T* w1, const int4* blocks,
                                  int nblk, int dense_rows, T* out, int N, int K, hipStream_t st) {
   constexpr int NB = stream_nb<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, OCC>();
@@ -430,7 +437,7 @@ hipError_t launch_stream_variant(const T* in, const int32_t* row_map, const T* w
   const long long total = (long long)tiles * nblk;
   if (total == 0) return hipSuccess;
   if (total > 0x7fffffffLL / (64 * WN * WK)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((ffn_stream_kernel<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, OCC>), dim3((unsigned)total),
+  hipLaunchKernelGGL((ffn_stream_kernel<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, OCC, VAR>), dim3((unsigned)total),
                      dim3(64 * WN * WK), 0, st, in, row_map, w0, w1, blocks, dense_rows, out, N, K, tiles);
   return hipGetLastError();
 }
@@ -450,6 +457,39 @@ constexpr int S_DEEP_STEPS = 16;     // steps per wave from which bf16 runs two 
 
 int stream_row_block() { return S_ROWS; }
 
+// Body and cache hint of the bf16 1 x 4-wave kernel (VAR above), from
+// interleaved timings on the decode shapes: the shared-tile body with
+// non-temporal weight DMA streams the gate/up pair faster unless the expert
+// is very wide (N >= 8192: Mixtral-shaped, 332 vs 343 us) -- DSV3-shaped
+// 2272 -> 2014 us, Qwen3-shaped 83 -> 75 us -- and the down projection of a
+// long K (>= 8192: 165 -> 139 us); a short-K down projection (K <= 1024)
+// gains from the shared body alone (37 -> 32 us); others keep the mix.
+static int stream_var(int MODE, int N, int K) {
+  if (MODE == 0) return N >= 8192 ? 0 : 3;
+  if (K >= 8192) return 3;
+  return K <= 1024 ? 1 : 0;
+}
+
+template <typename T, int MODE, int WN, int WK, int PD>
+static hipError_t stream_pd(const T* x, const int32_t* row_map, const T* w0, const T* w1, const int4* blocks,
+                            int nblk, int dense_rows, T* out, int N, int K, hipStream_t st) {
+  constexpr int KC = (sizeof(T) == 2) ? 16 : 8;
+  if constexpr (sizeof(T) == 2 && WN == 1 && WK == 4) {
+    switch (stream_var(MODE, N, K)) {
+      case 3:
+        return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, PD, true, 1, 3>(x, row_map, w0, w1, blocks,
+                                                                                     nblk, dense_rows, out, N, K, st);
+      case 1:
+        return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, PD, true, 1, 1>(x, row_map, w0, w1, blocks,
+                                                                                     nblk, dense_rows, out, N, K, st);
+      default:
+        break;
+    }
+  }
+  return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, PD>(x, row_map, w0, w1, blocks, nblk, dense_rows,
+                                                                      out, N, K, st);
+}
+
 template <typename T, int MODE, int WN, int WK>
 static hipError_t stream_wk(const T* x, const int32_t* row_map, const T* w0, const T* w1, const int4* blocks,
                             int nblk, int dense_rows, T* out, int N, int K, hipStream_t st) {
@@ -457,11 +497,9 @@ static hipError_t stream_wk(const T* x, const int32_t* row_map, const T* w0, con
   constexpr int STEP = 4 * KC;
   if constexpr (sizeof(T) == 2) {
     if (K / WK / STEP >= S_DEEP_STEPS)
-      return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, 2>(x, row_map, w0, w1, blocks, nblk, dense_rows,
-                                                                         out, N, K, st);
+      return stream_pd<T, MODE, WN, WK, 2>(x, row_map, w0, w1, blocks, nblk, dense_rows, out, N, K, st);
   }
-  return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, 1>(x, row_map, w0, w1, blocks, nblk, dense_rows, out,
-                                                                     N, K, st);
+  return stream_pd<T, MODE, WN, WK, 1>(x, row_map, w0, w1, blocks, nblk, dense_rows, out, N, K, st);
 }
 
 template <typename T, int MODE>
