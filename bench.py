@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--router", default="auto", choices=["auto", "float64", "screened"],
                     help="router algorithm (both give identical routing; they differ in cost)")
     ap.add_argument("--path", default="auto", choices=["auto", "stream", "gemm"], help="FFN path")
+    ap.add_argument("--weight-layout", default="blocked", choices=["blocked", "rowmajor"],
+                    help="storage order of the expert weights (blocked: converted once by moe_pack_weights "
+                         "before timing, as at load time)")
     ap.add_argument("--k-dist", default="",
                     help="eq7:MU,SIGMA draws the budgets k = clip(round(N(MU, SIGMA^2)), 1, k_max) "
                          "instead of the workload's own law")
@@ -92,7 +95,7 @@ def kernel_source_hash(path: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, path: str):
+def measured_traffic(workload: str, path: str, layout: str):
     """Per-launch HBM bytes of the gate/up kernel from the committed rocprofv3
     counter runs, or None when absent or taken on other kernel source."""
     try:
@@ -100,6 +103,8 @@ def measured_traffic(workload: str, path: str):
     except (OSError, KeyError, ValueError):
         return None
     if rec.get("path") != path or rec.get("source_hash") != kernel_source_hash(path):
+        return None
+    if rec.get("weight_layout", "rowmajor") != layout:
         return None
     return rec.get("bytes_per_launch")
 
@@ -174,6 +179,15 @@ def main():
         mu, sigma = (float(v) for v in params.split(","))
         from workloads import draw_k_eq7
         layer.k = draw_k_eq7(cfg.T, mu, sigma, cfg.k_max, cfg.seed).to(dev)
+    # the CPU baseline reads the row-major weights; the GPU runs read `layer`
+    layer_rm = layer
+    if args.weight_layout == "blocked":
+        import copy
+        layer = copy.copy(layer_rm)
+        for name in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+            t = getattr(layer_rm, name)
+            if t is not None:
+                setattr(layer, name, moe.pack_weights(t))
     torch.cuda.synchronize()
 
     T, d, E, I = cfg.T, cfg.d, cfg.E, cfg.I
@@ -181,6 +195,7 @@ def main():
     kpol, _, kgran = args.k_policy.partition(":")
     kgran = int(kgran) if kgran else 1
     kp = dict(k_policy=kpol, k_granule=kgran)
+    kp["weight_layout"] = args.weight_layout
     desc = moe.make_desc(T, d, E, I, cfg.k_max, I_shared=Is, dtype=layer.x.dtype,
                          routed_scale=cfg.routed_scale, path=args.path, router=args.router, **kp)
     ws = moe.alloc_workspace(desc, moe.MOE_OP_FORWARD, dev)
@@ -239,7 +254,7 @@ def main():
         Np, rp = cfg.split, args.proxy
         mp = -(-cfg.k_max // Np)
         w_base, gate_idx = make_proxy_inputs(cfg, rp, dev)
-        wp_g, wp_u = moe.proxy_pack(layer.w_gate, layer.w_up, gate_idx, Np)
+        wp_g, wp_u = moe.proxy_pack(layer.w_gate, layer.w_up, gate_idx, Np, weight_layout=args.weight_layout)
         pr = moe.ProxyRouter(desc, Np, rp, mp, moe.moe_proxy_kappa_balanced(cfg.k_max, mp, Np), dev)
         i32 = dict(dtype=torch.int32, device=dev)
         A_cap = T * cfg.k_max
@@ -460,7 +475,7 @@ def main():
     roof["algorithmic_per_launch"] = gu_flops if mfma_bound else gu_bytes
     roof["intensity_flop_per_byte"] = round(intensity, 1)
     roof["ridge_flop_per_byte"] = round(ridge, 1)
-    roof["traffic"] = (measured_traffic(cfg.name, routed_path)
+    roof["traffic"] = (measured_traffic(cfg.name, routed_path, args.weight_layout)
                        if args.k_policy == "exact" and not args.k_dist and not args.fold and not args.proxy
                        and not args.paths else None)
 
@@ -486,7 +501,7 @@ def main():
         n = args.cpu_sample or {"mixtral_decode": 64, "qwen3_30b_a3b_decode": 256, "tiny_fp32": 16,
                                 "subexpert_prefill": 64, "dsv3_decode": 16, "dsv3_prefill": 16}[cfg.name]
         print(f"[bench] timing the CPU oracle on {n} tokens", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(layer, n)
+        cpu = cpu_baseline(layer_rm, n)
 
     k_desc = args.k_dist if args.k_dist else "/".join(str(v) for v in cfg.k_values)
     rec = {
@@ -505,7 +520,7 @@ def main():
         "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "I": I, "I_shared": Is,
                    "k_values": k_desc, "k_max": cfg.k_max, "A": A, "n_active": n_act,
                    "execution": "eager" if args.eager else f"hip_graph ({g_steps} steps per replay)",
-                   "ffn_path": routed_path,
+                   "ffn_path": routed_path, "weight_layout": args.weight_layout,
                    "router": args.router, "k_policy": args.k_policy, "k_dist": args.k_dist or "workload",
                    "fold": args.fold or "none", "proxy": proxy_info or "none",
                    "paths": ({"P": paths["P"], "extra_per_source": paths["extra"], "lambda": paths["lam"],

@@ -33,6 +33,10 @@
  *  - Weight layout is the [out, in] convention:
  *      w_router [E][d], w_gate [E][I][d], w_up [E][I][d], w_down [E][d][I],
  *      ws_gate [Is][d], ws_up [Is][d], ws_down [d][Is]  (Is = I_shared).
+ *    The expert weights (every w_gate/w_up/w_down/ws_* argument, and the
+ *    proxy weights of moe_proxy_pack) are stored either row-major or in the
+ *    blocked order of desc->weight_layout; the router weights are always
+ *    row-major.
  *  - A = sum_t k_t is the number of (token, expert) assignments.  Arrays
  *    indexed by assignment have capacity T * k_max entries; only the first A
  *    are written.
@@ -113,6 +117,22 @@ typedef enum {
   MOE_FOLD_POOL = 1    /* per batch: keep a pool of `budget` experts (decode) */
 } moe_fold_mode;
 
+/* Storage order of the expert weight matrices.  Both describe the same
+ * [N][K] matrices (N output rows, K inputs); only the byte order differs.
+ * BLOCKED64 cuts each matrix into (N/64) x (K/EB) blocks of 64 rows x 128
+ * bytes (EB = 128 / sizeof(ELT): 64 bf16 or 32 float), block (nb, kb) at
+ * element offset (nb * (K/EB) + kb) * 64 * EB, rows of the block one after
+ * another: element (n, k) sits at
+ *     ((n / 64) * (K / EB) + k / EB) * 64 * EB + (n % 64) * EB + k % EB,
+ * and the matrices of a stack follow each other as in the row-major layout
+ * (matrix e at e * N * K).  One 64-element step of K over a 64-row tile is
+ * then 8 KB of contiguous memory instead of 64 lines one matrix row apart, which
+ * is how the FFN kernels read it (moe_pack_weights converts). */
+typedef enum {
+  MOE_W_ROWMAJOR = 0,
+  MOE_W_BLOCKED64 = 1
+} moe_weight_layout;
+
 /* Device status bits written by moe_route / moe_forward. */
 #define MOE_DEV_BAD_K 1  /* some k_t was outside [0, k_max]; it was run as k_t = 0 */
 
@@ -127,6 +147,8 @@ typedef enum {
  *   routed_scale: finite (1.0 for the plain renormalised softmax)
  *   k_policy: a moe_k_policy value; k_granule: N >= 1 for MOE_K_ROUND_UP,
  *   with k_max a multiple of N (ignored by the other policies)
+ *   weight_layout: a moe_weight_layout value (0, row-major, when the field is
+ *   zero-initialised)
  */
 typedef struct moe_desc {
   int32_t T;            /* tokens in the batch */
@@ -141,6 +163,7 @@ typedef struct moe_desc {
   float routed_scale;   /* factor applied to the renormalised routing weights */
   int32_t k_policy;     /* moe_k_policy: budget each token executes */
   int32_t k_granule;    /* N of MOE_K_ROUND_UP */
+  int32_t weight_layout; /* moe_weight_layout of every expert weight argument */
 } moe_desc;
 
 /* Stream handle: a hipStream_t, or NULL for the null stream. */
@@ -154,6 +177,23 @@ typedef void* moe_stream_t;
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED.
  */
 moe_status moe_workspace_size(const moe_desc* desc, int32_t op, size_t* bytes);
+
+/*
+ * Re-lay G row-major [N][K] matrices (contiguous, matrix g at g * N * K) into
+ * the MOE_W_BLOCKED64 order; a weight stack is converted once, when it is
+ * loaded, and then passed with desc->weight_layout = MOE_W_BLOCKED64.  A pure
+ * permutation of elements (bit-exact).
+ *   dtype   MOE_F32 or MOE_BF16 (sets EB above)
+ *   G       matrices, >= 0 (0: nothing is launched)
+ *   N, K    rows and columns of each: N a multiple of 64, K a multiple of
+ *           128 / sizeof(ELT), both >= 1, G * N * K < 2^40
+ *   src     ELT [G][N][K] row-major (16-byte aligned)
+ *   dst     ELT, G * N * K elements out (16-byte aligned); must not overlap src
+ * Errors: MOE_ERR_NULL, MOE_ERR_UNSUPPORTED (dtype), MOE_ERR_SHAPE (sizes, or
+ * src and dst overlap), MOE_ERR_ALIGN, MOE_ERR_LAUNCH.
+ */
+moe_status moe_pack_weights(int32_t dtype, int32_t G, int32_t N, int32_t K, const void* src, void* dst,
+                            moe_stream_t stream);
 
 /*
  * The FFN path `desc->path` resolves to, for the routed experts and for the

@@ -16,10 +16,11 @@ from . import _lib
 from ._lib import (MOE_BF16, MOE_DEV_BAD_K, MOE_F32, MOE_OP_COMBINE, MOE_OP_FFN,  # noqa: F401
                    MOE_OP_FORWARD, MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_PATH_AUTO, MOE_PATH_GEMM,
                    MOE_PATH_STREAM, MOE_ROUTER_AUTO, MOE_ROUTER_FLOAT64, MOE_ROUTER_SCREENED, MOE_K_EXACT,
-                   MOE_K_BATCH_MAX, MOE_K_ROUND_UP, MOE_OP_FOLD, MOE_OP_PATH, MOE_FOLD_TOKEN, MOE_FOLD_POOL, moe_desc)
+                   MOE_K_BATCH_MAX, MOE_K_ROUND_UP, MOE_OP_FOLD, MOE_OP_PATH, MOE_FOLD_TOKEN, MOE_FOLD_POOL,
+                   MOE_W_ROWMAJOR, MOE_W_BLOCKED64, moe_desc)
 
 __all__ = [
-    "MoeError", "make_desc", "workspace_size", "resolve_path", "alloc_workspace", "moe_route", "moe_permute",
+    "MoeError", "make_desc", "pack_weights", "workspace_size", "resolve_path", "alloc_workspace", "moe_route", "moe_permute",
     "moe_ffn", "moe_ffn_plan", "moe_ffn_gateup", "moe_ffn_down", "moe_combine", "moe_fold", "moe_proxy_kappa_balanced",
     "moe_proxy_pack", "moe_path_table", "moe_path_route", "moe_path_sources", "moe_path_rows", "moe_ffn_down_rows",
     "PathLayer",
@@ -32,6 +33,7 @@ _DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 _PATHS = {"auto": MOE_PATH_AUTO, "stream": MOE_PATH_STREAM, "gemm": MOE_PATH_GEMM}
 _ROUTERS = {"auto": MOE_ROUTER_AUTO, "float64": MOE_ROUTER_FLOAT64, "screened": MOE_ROUTER_SCREENED}
 _K_POLICIES = {"exact": MOE_K_EXACT, "batch_max": MOE_K_BATCH_MAX, "round_up": MOE_K_ROUND_UP}
+_LAYOUTS = {"rowmajor": MOE_W_ROWMAJOR, "blocked": MOE_W_BLOCKED64}
 
 
 class MoeError(RuntimeError):
@@ -48,12 +50,29 @@ def library_path() -> str:
 
 def make_desc(T: int, d: int, E: int, I: int, k_max: int, *, I_shared: int = 0,
               dtype=torch.bfloat16, path: str = "auto", router: str = "auto",
-              routed_scale: float = 1.0, k_policy: str = "exact", k_granule: int = 1) -> moe_desc:
+              routed_scale: float = 1.0, k_policy: str = "exact", k_granule: int = 1,
+              weight_layout: str = "rowmajor") -> moe_desc:
     """Layer descriptor.  k_policy: "exact" (each token runs its own k_t),
     "batch_max" (every valid token runs the batch's largest budget) or
-    "round_up" (k_t rounded up to a multiple of k_granule)."""
+    "round_up" (k_t rounded up to a multiple of k_granule).  weight_layout:
+    "rowmajor" or "blocked" (expert weights converted by pack_weights)."""
     return moe_desc(T, d, E, I, k_max, I_shared, _DTYPES[dtype], _PATHS[path], _ROUTERS[router],
-                    routed_scale, _K_POLICIES[k_policy], k_granule)
+                    routed_scale, _K_POLICIES[k_policy], k_granule, _LAYOUTS[weight_layout])
+
+
+def pack_weights(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """moe_pack_weights: a new tensor of w's shape ([G, N, K] or [N, K]) whose
+    storage holds w's matrices in the blocked order (64-row x 128-byte blocks).
+    Its elements are no longer addressed by (n, k) in torch terms; pass it to
+    the entry points with weight_layout="blocked"."""
+    if w.dim() not in (2, 3) or not w.is_contiguous():
+        raise ValueError("pack_weights expects a contiguous [G, N, K] or [N, K] tensor")
+    G = w.shape[0] if w.dim() == 3 else 1
+    N, K = w.shape[-2], w.shape[-1]
+    out = torch.empty_like(w)
+    _check("moe_pack_weights", _lib.load().moe_pack_weights(
+        _DTYPES[w.dtype], G, N, K, _ptr(w), _ptr(out), _stream(stream)))
+    return out
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -187,14 +206,15 @@ def forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: Optional[torch
             k: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
             shared: Optional[Sequence[torch.Tensor]] = None, *, k_max: int, routed_scale: float = 1.0,
             path: str = "auto", router: str = "auto", k_policy: str = "exact", k_granule: int = 1,
-            ws: Optional[torch.Tensor] = None, stream=None):
+            weight_layout: str = "rowmajor", ws: Optional[torch.Tensor] = None, stream=None):
     """Allocate the outputs (and a workspace unless given) and run moe_forward.
     Returns (out [T, d], stats int32 [E+2] = counts, n_active, A, dev_status int32 [1])."""
     T, d = x.shape
     E, I, _ = w_gate.shape
     Is = shared[0].shape[0] if shared is not None else 0
     desc = make_desc(T, d, E, I, k_max, I_shared=Is, dtype=x.dtype, path=path, router=router,
-                     routed_scale=routed_scale, k_policy=k_policy, k_granule=k_granule)
+                     routed_scale=routed_scale, k_policy=k_policy, k_granule=k_granule,
+                     weight_layout=weight_layout)
     if ws is None:
         ws = alloc_workspace(desc, MOE_OP_FORWARD, x.device)
     out = torch.empty((T, d), dtype=x.dtype, device=x.device)
@@ -211,12 +231,14 @@ def proxy_width(N: int, r: int) -> int:
     return (N * r + 127) // 128 * 128
 
 
-def proxy_pack(w_gate: torch.Tensor, w_up: torch.Tensor, gate_idx: torch.Tensor, N: int, stream=None):
+def proxy_pack(w_gate: torch.Tensor, w_up: torch.Tensor, gate_idx: torch.Tensor, N: int, stream=None,
+               weight_layout: str = "rowmajor"):
     """Allocate and fill the packed proxy weights (wp_gate, wp_up), each
-    [E/N, Ip, d], of a split layer with sub-expert weights [E, I, d]."""
+    [E/N, Ip, d], of a split layer with sub-expert weights [E, I, d] (input
+    and output in `weight_layout`)."""
     E, I, d = w_gate.shape
     r = gate_idx.shape[1]
-    desc = make_desc(0, d, E, I, 1, dtype=w_gate.dtype)
+    desc = make_desc(0, d, E, I, 1, dtype=w_gate.dtype, weight_layout=weight_layout)
     Ip = proxy_width(N, r)
     wp_g = torch.empty((E // N, Ip, d), dtype=w_gate.dtype, device=w_gate.device)
     wp_u = torch.empty_like(wp_g)
@@ -237,6 +259,7 @@ class ProxyRouter:
         self.Ip = proxy_width(N, r)
         dtype = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}[desc.dtype]
         self.base = make_desc(T, d, desc.E // N, self.Ip, m, dtype=dtype, routed_scale=desc.routed_scale)
+        self.base.weight_layout = desc.weight_layout
         i32 = dict(dtype=torch.int32, device=device)
         A = max(T * m, 1)
         self.kappa = kappa.to(device=device, dtype=torch.int32).contiguous()
@@ -329,7 +352,7 @@ class PathLayer:
         dtype = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}[desc.dtype]
         # the paths one per row: T*k_max "tokens" of one route each
         self.unit = moe_desc(T * km, d, E, I, 1, 0, desc.dtype, desc.path, desc.router, desc.routed_scale,
-                             MOE_K_EXACT, 1)
+                             MOE_K_EXACT, 1, desc.weight_layout)
         i32 = dict(dtype=torch.int32, device=device)
         A = max(T * km, 1)
         self.tok_off = torch.empty(T + 1, **i32)

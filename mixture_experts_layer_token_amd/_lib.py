@@ -17,6 +17,7 @@ MOE_K_EXACT, MOE_K_BATCH_MAX, MOE_K_ROUND_UP = 0, 1, 2
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_FORWARD, MOE_OP_FOLD, MOE_OP_PATH = 0, 1, 2, 3, 4, 5, 6
 MOE_FOLD_TOKEN, MOE_FOLD_POOL = 0, 1
 MOE_DEV_BAD_K = 1
+MOE_W_ROWMAJOR, MOE_W_BLOCKED64 = 0, 1
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
                 4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_ALIGN", 6: "MOE_ERR_LAUNCH"}
@@ -25,7 +26,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
 class moe_desc(ctypes.Structure):
     _fields_ = [("T", c_i32), ("d", c_i32), ("E", c_i32), ("I", c_i32), ("k_max", c_i32),
                 ("I_shared", c_i32), ("dtype", c_i32), ("path", c_i32), ("router", c_i32),
-                ("routed_scale", ctypes.c_float), ("k_policy", c_i32), ("k_granule", c_i32)]
+                ("routed_scale", ctypes.c_float), ("k_policy", c_i32), ("k_granule", c_i32),
+                ("weight_layout", c_i32)]
 
 
 _P = ctypes.POINTER(moe_desc)
@@ -34,6 +36,7 @@ _P = ctypes.POINTER(moe_desc)
 SIGNATURES = {
     "moe_workspace_size": [_P, c_i32, ctypes.POINTER(c_size)],
     "moe_resolve_path": [_P, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)],
+    "moe_pack_weights": [c_i32, c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr],
     "moe_route": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
     "moe_permute": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
     "moe_ffn": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,

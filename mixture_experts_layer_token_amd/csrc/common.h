@@ -137,4 +137,32 @@ __device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 7; }
 // byte offset of 16-byte chunk c of tile row r
 __device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ lds_swz(r)) * 16); }
 
+// ---- expert weight storage (moe_weight_layout) ----
+// Row-major: element (n, k) of a [N][K] matrix at n * K + k.  Blocked: the
+// matrix is cut into 64-row x 128-byte blocks (EB = 128 / sizeof(T)
+// elements of K), block (n / 64, k / EB) at (n / 64 * (K / EB) + k / EB) *
+// 64 * EB, rows of a block contiguous.  With both, every 16-byte chunk that
+// starts at a multiple of 16 bytes of a row is contiguous, and a run of K
+// that stays inside one EB-aligned step advances by 1 per element.
+template <typename T>
+__host__ __device__ __forceinline__ size_t w_offset(int n, int k, int K, int blocked) {
+  constexpr int EB = 128 / (int)sizeof(T);
+  if (!blocked) return (size_t)n * K + k;
+  return ((size_t)(n >> 6) * (K / EB) + k / EB) * (64 * EB) + (size_t)(n & 63) * EB + (k % EB);
+}
+// Elements between the same (row, k % EB) position of two consecutive
+// EB-wide steps of K.
+template <typename T>
+__host__ __device__ __forceinline__ int w_kstep(int blocked) {
+  constexpr int EB = 128 / (int)sizeof(T);
+  return blocked ? 64 * EB : EB;
+}
+// Elements between rows n and n + dn inside one 64-row block (blocked), or
+// anywhere (row-major).
+template <typename T>
+__host__ __device__ __forceinline__ size_t w_rowstep(int dn, int K, int blocked) {
+  constexpr int EB = 128 / (int)sizeof(T);
+  return blocked ? (size_t)dn * EB : (size_t)dn * K;
+}
+
 }  // namespace moe

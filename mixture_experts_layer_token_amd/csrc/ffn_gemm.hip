@@ -20,6 +20,10 @@
 // weights as the A operand (a lane ends with 4 consecutive output columns of a
 // row: 8-byte stores).
 //
+// Weights are read row-major or in the blocked order (64-row x 128-byte
+// blocks, w_offset in common.h): a lane's DMA source is set once, and a stage
+// advances it by one row of 64 elements or by one whole 8 KB block.
+//
 // LDS layout.  A stage holds each tile row as 128 bytes (64 bf16 of K) with no
 // padding; the eight 16-byte chunks of row r are XOR-permuted by (r >> 1) & 7.
 // A DMA instruction writes 1 KB (64 lanes x 16 bytes) to consecutive LDS
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     const bf16_t* __restrict__ in, const int32_t* __restrict__ row_map, const bf16_t* __restrict__ w0,
     const bf16_t* __restrict__ w1, const int4* __restrict__ blocks, int bound, int dense_rows,
     bf16_t* __restrict__ out, int N, int K, const bf16_t* __restrict__ in_s, const bf16_t* __restrict__ w0s,
-    const bf16_t* __restrict__ w1s, bf16_t* __restrict__ out_s, int rows_s) {
+    const bf16_t* __restrict__ w1s, bf16_t* __restrict__ out_s, int rows_s, int blocked) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = (MODE == 0) ? 2 : 1;
   constexpr int WROWS = NMAT * BNW;                          // weight rows per stage
@@ -159,8 +163,9 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     const int c = (lane & 7) ^ lds_swz(r);
     const bf16_t* wb = (MODE == 0 && r >= BNW) ? w1 : w0;
     const int wr = (MODE == 0 && r >= BNW) ? r - BNW : r;
-    wsrc[j] = wb + g * gstride + (size_t)(n0 + wr) * K + c * 8;
+    wsrc[j] = wb + g * gstride + w_offset<bf16_t>(n0 + wr, c * 8, K, blocked);
   }
+  const int kw = w_kstep<bf16_t>(blocked);  // weight elements per 64-wide stage of K (BK = 64 = EB)
   int per_stage = WI;  // DMA instructions this wave issues per stage
 #pragma unroll
   for (int j = 0; j < XI; ++j) per_stage += xany[j] ? 1 : 0;
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)(xsrc[j] + ko), (lds_ptr_t)(sb + (j * NW + wave) * 1024), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < WI; ++j)
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[j] + ko), (lds_ptr_t)(sb + XBYTES + (j * NW + wave) * 1024),
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[j] + kt * kw), (lds_ptr_t)(sb + XBYTES + (j * NW + wave) * 1024),
                                        16, 0, 0);
   };
 
@@ -350,7 +355,7 @@ int gemm_row_block() { return GBM; }
 template <int MODE, int BM, int BNW, int WM, int WN, int STAGES>
 static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, const void* w0, const void* w1,
                                       const int4* blocks, int bound, int dense_rows, void* out, int N, int K,
-                                      hipStream_t st, const GemmSecond& sec = GemmSecond{}) {
+                                      int blocked, hipStream_t st, const GemmSecond& sec = GemmSecond{}) {
   if (N % BNW != 0 || K % BK != 0) return hipErrorInvalidValue;
   const int rb_bound = blocks ? bound : (dense_rows + GBM - 1) / GBM;
   const long long total = ((long long)rb_bound + (sec.rows + GBM - 1) / GBM) * (GBM / BM) * (N / BNW);
@@ -360,7 +365,7 @@ static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, co
   hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, STAGES>), dim3((unsigned)nwg), dim3(64 * WM * WN), 0,
                      st, (const bf16_t*)in, row_map, (const bf16_t*)w0, (const bf16_t*)w1, blocks, bound, dense_rows,
                      (bf16_t*)out, N, K, (const bf16_t*)sec.in, (const bf16_t*)sec.w0, (const bf16_t*)sec.w1,
-                     (bf16_t*)sec.out, sec.rows);
+                     (bf16_t*)sec.out, sec.rows, blocked);
   return hipGetLastError();
 }
 
@@ -370,23 +375,23 @@ static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, co
 // 3-stage ring keeps more of them in flight).
 hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
                                   const int4* blocks, int bound, int dense_rows, int rows_hint, void* h, int N,
-                                  int K, hipStream_t st, const GemmSecond& sec) {
+                                  int K, int blocked, hipStream_t st, const GemmSecond& sec) {
   if (rows_hint >= GBM)
-    return launch_gemm_variant<0, 256, 128, 4, 2, 2>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st, sec);
-  return launch_gemm_variant<0, 128, 128, 2, 4, 3>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st, sec);
+    return launch_gemm_variant<0, 256, 128, 4, 2, 2>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, blocked, st, sec);
+  return launch_gemm_variant<0, 128, 128, 2, 4, 3>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, blocked, st, sec);
 }
 
 hipError_t launch_ffn_down_gemm(const void* h, const int32_t* row_map, const void* wd, const int4* blocks, int bound,
-                                int dense_rows, int rows_hint, void* y, int N, int K, hipStream_t st,
+                                int dense_rows, int rows_hint, void* y, int N, int K, int blocked, hipStream_t st,
                                 const GemmSecond& sec) {
   if (rows_hint >= GBM) {
     if (N % 256 == 0)
-      return launch_gemm_variant<1, 256, 256, 4, 2, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
-    return launch_gemm_variant<1, 256, 128, 4, 2, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
+      return launch_gemm_variant<1, 256, 256, 4, 2, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked, st, sec);
+    return launch_gemm_variant<1, 256, 128, 4, 2, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked, st, sec);
   }
   if (N % 256 == 0)
-    return launch_gemm_variant<1, 128, 256, 2, 2, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
-  return launch_gemm_variant<1, 128, 128, 2, 2, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, st, sec);
+    return launch_gemm_variant<1, 128, 256, 2, 2, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked, st, sec);
+  return launch_gemm_variant<1, 128, 128, 2, 2, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked, st, sec);
 }
 
 }  // namespace moe

@@ -105,7 +105,7 @@ template <typename T, int MODE, int KC, int WN, int WKR, int SM, int TPW, int PD
 __device__ __forceinline__ void stream_block(const T* __restrict__ in, const int32_t* __restrict__ row_map,
                                              const T* wa, const T* wb, int K, int kbeg, int lofs, int nsteps,
                                              int mg, int rows, T* __restrict__ out, int N, int n0, f32x4_t* red,
-                                             int wn, int wk, int slot0) {
+                                             int wn, int wk, int slot0, int tstride, int kstr) {
   constexpr int LE = 16 / sizeof(T);                     // elements per 16-byte load
   constexpr int LPS = KC / LE;                           // loads per tile row per K step
   constexpr int STEP = 4 * KC;                           // K elements per wave step
@@ -114,8 +114,9 @@ __device__ __forceinline__ void stream_block(const T* __restrict__ in, const int
   constexpr int HALF = TPW / 2;
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int tstride = 16 * K;                // elements between consecutive 16-row tiles
-  // tile j's row pointer is wbase(j) + (j % half) * tstride
+  // tile j's row pointer is wbase(j) + (j % half) * tstride (tstride: weight
+  // elements between consecutive 16-row tiles; kstr: between consecutive
+  // steps of K, both set by the weight layout)
   auto wrow = [&](int j) -> const T* {
     if (MODE == 0) return (j < HALF ? wa : wb) + (j % HALF) * tstride;
     return wa + j * tstride;
@@ -144,11 +145,11 @@ __device__ __forceinline__ void stream_block(const T* __restrict__ in, const int
   uint4 Wr[NS][TPW][LPS];
   uint4 Xr[NS][SM][LPS];
   auto issue = [&](uint4 (&w)[TPW][LPS], uint4 (&x)[SM][LPS], int step) {
-    const int ko = step * STEP;
+    const int ko = step * STEP, kw = step * kstr;
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
-      for (int i = 0; i < LPS; ++i) w[j][i] = ldw<T, false>(wrow(j) + ko + i * LSTR);
+      for (int i = 0; i < LPS; ++i) w[j][i] = ldw<T, false>(wrow(j) + kw + i * LSTR);
 #pragma unroll
     for (int mt = 0; mt < SM; ++mt)
 #pragma unroll
@@ -241,7 +242,7 @@ constexpr int SHARED_STAGES = 3, SHARED_STAGE_BYTES = 2 * 64 * 128;
 template <typename T, int MODE, int KC, int TPW, int VAR = 0>
 __device__ __forceinline__ void stream_block_shared(const T* __restrict__ in, const int32_t* __restrict__ row_map,
                                                     const T* w0, const T* w1, int K, int mg, int rows,
-                                                    T* __restrict__ out, int N, int n0, char* ring) {
+                                                    T* __restrict__ out, int N, int n0, char* ring, int blocked) {
   constexpr int LE = 16 / sizeof(T);
   constexpr int LPS = KC / LE;
   constexpr int STEP = 4 * KC;
@@ -257,8 +258,9 @@ __device__ __forceinline__ void stream_block_shared(const T* __restrict__ in, co
   // DMA instruction q of wave w fills LDS rows 16w + 8q .. +7 of the weight
   // and the activation region (1 KB each); lane i writes chunk slot i % 8 of
   // row R = 16w + 8q + i / 8 and so fetches K chunk (i % 8) ^ swz(R).
-  const T* tb = MODE == 0 ? (wave < HALF ? w0 : w1) + (size_t)(n0 + 16 * (wave % HALF)) * K
-                          : w0 + (size_t)(n0 + 16 * wave) * K;
+  const T* tb = MODE == 0 ? (wave < HALF ? w0 : w1) : w0;
+  const int trow = MODE == 0 ? n0 + 16 * (wave % HALF) : n0 + 16 * wave;  // first row of this wave's tile
+  const int kstr = blocked ? w_kstep<T>(1) : STEP;                         // weight elements per step
   // Activation rows past the block's end: an instruction whose eight rows
   // are all missing is not issued (wave-uniform); within a partly filled one
   // a missing row repeats the block's first row (its outputs are not stored).
@@ -269,7 +271,7 @@ __device__ __forceinline__ void stream_block_shared(const T* __restrict__ in, co
   for (int q = 0; q < 2; ++q) {
     const int r = 8 * q + (lane >> 3), R = 16 * wave + r;
     const int c = (lane & 7) ^ lds_swz(R);
-    wsrc[q] = tb + (size_t)r * K + c * LE;
+    wsrc[q] = tb + w_offset<T>(trow + r, c * LE, K, blocked);
     xon[q] = 16 * wave + 8 * q < rows;
     const int m = R < rows ? R : 0;
     const int src = row_map ? row_map[mg + m] : mg + m;
@@ -280,7 +282,7 @@ __device__ __forceinline__ void stream_block_shared(const T* __restrict__ in, co
     char* sb = ring + (s % NST) * SB + wave * 2048;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[q] + s * STEP), (lds_ptr_t)(sb + q * 1024), 16, 0,
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[q] + s * kstr), (lds_ptr_t)(sb + q * 1024), 16, 0,
                                        (VAR & 2) ? 2 : 0);
       if (xon[q])
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)(xsrc[q] + s * STEP), (lds_ptr_t)(sb + XOFS + q * 1024), 16, 0,
@@ -350,7 +352,7 @@ template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD
 __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void ffn_stream_kernel(
     const T* __restrict__ in, const int32_t* __restrict__ row_map, const T* __restrict__ w0,
     const T* __restrict__ w1, const int4* __restrict__ blocks, int dense_rows, T* __restrict__ out, int N, int K,
-    int tiles) {
+    int tiles, int blocked) {
   static_assert(MODE == 1 || TPW % 2 == 0, "gate/up tiles come in pairs");
   static_assert(KC % (16 / sizeof(T)) == 0, "K step must be whole 16-byte loads");
   static_assert(WK % 2 == 0, "two row groups split the K waves in halves");
@@ -389,37 +391,45 @@ __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OC
   const int n0 = tile * NB + wn * CPW;
   const int lofs = IL ? lg * LE : lg * KC;   // lane's first element within a step
   const size_t gstride = (size_t)N * K;
-  const T* const wrow_a = w0 + g * gstride + (size_t)(n0 + lr) * K + lofs;
-  const T* const wrow_b = (MODE == 0 ? w1 : w0) + g * gstride + (size_t)(n0 + lr) * K + lofs;
+  // A wave's rows n0 .. n0 + CPW - 1 lie in one 64-row block of the blocked
+  // layout (n0 is a multiple of CPW), and each K step is one EB-wide column
+  // of blocks (STEP = EB), so both layouts are plain pointer strides here.
+  static_assert(STEP * sizeof(T) == 128 && 64 % CPW == 0, "layout strides");
+  const size_t wofs = w_offset<T>(n0 + lr, lofs, K, blocked);
+  const T* const wrow_a = w0 + g * gstride + wofs;
+  const T* const wrow_b = (MODE == 0 ? w1 : w0) + g * gstride + wofs;
+  const int tstride = (int)w_rowstep<T>(16, K, blocked), kstr = blocked ? w_kstep<T>(1) : STEP;
   // With a short K (under four steps per wave when split WK ways) every
   // block takes the shared-tile body, whose waves each run the whole K.
   const int light_max = !SHARED ? GR : ((VAR & 1) ? 0 : (K / WK / STEP >= 4 ? GR : 0));
   if (rows <= light_max) {
     // one row group; the WK waves split K
     const int Kw = K / WK, kbeg = wk * Kw, nsteps = Kw / STEP;
+    const size_t kw0 = w_offset<T>(0, kbeg, K, blocked);
     if (SMT > 1 && rows <= 16)
-      stream_block<T, MODE, KC, WN, WK, 1, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kbeg, wrow_b + kbeg, K, kbeg, lofs,
-                                                              nsteps, mg, rows, out, N, n0, red, wn, wk, 0);
+      stream_block<T, MODE, KC, WN, WK, 1, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kw0, wrow_b + kw0, K, kbeg, lofs,
+                                                              nsteps, mg, rows, out, N, n0, red, wn, wk, 0, tstride, kstr);
     else
-      stream_block<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kbeg, wrow_b + kbeg, K, kbeg,
-                                                                lofs, nsteps, mg, rows, out, N, n0, red, wn, wk, 0);
+      stream_block<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kw0, wrow_b + kw0, K, kbeg,
+                                                                lofs, nsteps, mg, rows, out, N, n0, red, wn, wk, 0, tstride, kstr);
   } else if constexpr (SHARED) {
     stream_block_shared<T, MODE, KC, TPW, VAR>(in, row_map, w0 + g * gstride, (MODE == 0 ? w1 : w0) + g * gstride, K, mg,
-                                          rows, out, N, n0, smem);
+                                          rows, out, N, n0, smem, blocked);
   } else {
     // two row groups; WK/2 waves split K within each
     constexpr int WKR = WK / 2;
     const int grp = wk / WKR, wkr = wk - grp * WKR;
     const int Kw = K / WKR, kbeg = wkr * Kw, nsteps = Kw / STEP;
+    const size_t kw0 = w_offset<T>(0, kbeg, K, blocked);
     const int mgg = mg + grp * GR, rg = min(GR, rows - grp * GR);
     if (SMT > 1 && rg <= 16)
-      stream_block<T, MODE, KC, WN, WKR, 1, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kbeg, wrow_b + kbeg, K, kbeg,
+      stream_block<T, MODE, KC, WN, WKR, 1, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kw0, wrow_b + kw0, K, kbeg,
                                                                lofs, nsteps, mgg, rg, out, N, n0, red, wn, wkr,
-                                                               grp * (WKR - 1));
+                                                               grp * (WKR - 1), tstride, kstr);
     else
-      stream_block<T, MODE, KC, WN, WKR, SMT, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kbeg, wrow_b + kbeg, K, kbeg,
+      stream_block<T, MODE, KC, WN, WKR, SMT, TPW, PD, IL, SLOT>(in, row_map, wrow_a + kw0, wrow_b + kw0, K, kbeg,
                                                                  lofs, nsteps, mgg, rg, out, N, n0, red, wn, wkr,
-                                                                 grp * (WKR - 1));
+                                                                 grp * (WKR - 1), tstride, kstr);
   }
 }
 
@@ -431,14 +441,14 @@ constexpr int stream_nb() { return WN * ((MODE == 0) ? 8 * TPW : 16 * TPW); }
 template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL = true, int OCC = 1,
           int VAR = 0>
 hipError_t launch_stream_variant(const T* in, const int32_t* row_map, const T* w0, const T* w1, const int4* blocks,
-                                 int nblk, int dense_rows, T* out, int N, int K, hipStream_t st) {
+                                 int nblk, int dense_rows, T* out, int N, int K, int blocked, hipStream_t st) {
   constexpr int NB = stream_nb<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, OCC>();
   const int tiles = N / NB;
   const long long total = (long long)tiles * nblk;
   if (total == 0) return hipSuccess;
   if (total > 0x7fffffffLL / (64 * WN * WK)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((ffn_stream_kernel<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, OCC, VAR>), dim3((unsigned)total),
-                     dim3(64 * WN * WK), 0, st, in, row_map, w0, w1, blocks, dense_rows, out, N, K, tiles);
+                     dim3(64 * WN * WK), 0, st, in, row_map, w0, w1, blocks, dense_rows, out, N, K, tiles, blocked);
   return hipGetLastError();
 }
 
@@ -464,7 +474,13 @@ int stream_row_block() { return S_ROWS; }
 // 2272 -> 2014 us, Qwen3-shaped 83 -> 75 us -- and the down projection of a
 // long K (>= 8192: 165 -> 139 us); a short-K down projection (K <= 1024)
 // gains from the shared body alone (37 -> 32 us); others keep the mix.
-static int stream_var(int MODE, int N, int K) {
+// With blocked weights every tile step is one contiguous 2 KB run, and the
+// shared body with the hint wins everywhere except the short-K down
+// projection, which keeps the shared body without it (Mixtral-shaped gate/up
+// 331 -> 295 us, DSV3-shaped down 1116 -> 1029 us, Qwen3-shaped gate/up
+// 76 -> 73 us; the Qwen3-shaped down loses the hint: 32.5 vs 40 us).
+static int stream_var(int MODE, int N, int K, int blocked) {
+  if (blocked) return (MODE == 1 && K <= 1024) ? 1 : 3;
   if (MODE == 0) return N >= 8192 ? 0 : 3;
   if (K >= 8192) return 3;
   return K <= 1024 ? 1 : 0;
@@ -472,60 +488,61 @@ static int stream_var(int MODE, int N, int K) {
 
 template <typename T, int MODE, int WN, int WK, int PD>
 static hipError_t stream_pd(const T* x, const int32_t* row_map, const T* w0, const T* w1, const int4* blocks,
-                            int nblk, int dense_rows, T* out, int N, int K, hipStream_t st) {
+                            int nblk, int dense_rows, T* out, int N, int K, int blocked, hipStream_t st) {
   constexpr int KC = (sizeof(T) == 2) ? 16 : 8;
   if constexpr (sizeof(T) == 2 && WN == 1 && WK == 4) {
-    switch (stream_var(MODE, N, K)) {
+    switch (stream_var(MODE, N, K, blocked)) {
       case 3:
         return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, PD, true, 1, 3>(x, row_map, w0, w1, blocks,
-                                                                                     nblk, dense_rows, out, N, K, st);
+                                                                                     nblk, dense_rows, out, N, K, blocked, st);
       case 1:
         return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, PD, true, 1, 1>(x, row_map, w0, w1, blocks,
-                                                                                     nblk, dense_rows, out, N, K, st);
+                                                                                     nblk, dense_rows, out, N, K, blocked, st);
       default:
         break;
     }
   }
   return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, PD>(x, row_map, w0, w1, blocks, nblk, dense_rows,
-                                                                      out, N, K, st);
+                                                                      out, N, K, blocked, st);
 }
 
 template <typename T, int MODE, int WN, int WK>
 static hipError_t stream_wk(const T* x, const int32_t* row_map, const T* w0, const T* w1, const int4* blocks,
-                            int nblk, int dense_rows, T* out, int N, int K, hipStream_t st) {
+                            int nblk, int dense_rows, T* out, int N, int K, int blocked, hipStream_t st) {
   constexpr int KC = (sizeof(T) == 2) ? 16 : 8;
   constexpr int STEP = 4 * KC;
   if constexpr (sizeof(T) == 2) {
     if (K / WK / STEP >= S_DEEP_STEPS)
-      return stream_pd<T, MODE, WN, WK, 2>(x, row_map, w0, w1, blocks, nblk, dense_rows, out, N, K, st);
+      return stream_pd<T, MODE, WN, WK, 2>(x, row_map, w0, w1, blocks, nblk, dense_rows, out, N, K, blocked, st);
   }
-  return stream_pd<T, MODE, WN, WK, 1>(x, row_map, w0, w1, blocks, nblk, dense_rows, out, N, K, st);
+  return stream_pd<T, MODE, WN, WK, 1>(x, row_map, w0, w1, blocks, nblk, dense_rows, out, N, K, blocked, st);
 }
 
 template <typename T, int MODE>
 static hipError_t stream_t(const void* in, const int32_t* row_map, const void* w0, const void* w1, const int4* blocks,
-                           int bound, int dense_rows, void* out, int N, int K, hipStream_t st) {
+                           int bound, int dense_rows, void* out, int N, int K, int blocked, hipStream_t st) {
   constexpr int KC = (sizeof(T) == 2) ? 16 : 8;
   constexpr int STEP = 4 * KC;
   const int nblk = blocks ? bound : (dense_rows + S_ROWS - 1) / S_ROWS;
   const T* x = (const T*)in;
   if (K % (4 * STEP) == 0)
-    return stream_wk<T, MODE, 1, 4>(x, row_map, (const T*)w0, (const T*)w1, blocks, nblk, dense_rows, (T*)out, N, K, st);
-  return stream_wk<T, MODE, 2, 2>(x, row_map, (const T*)w0, (const T*)w1, blocks, nblk, dense_rows, (T*)out, N, K, st);
+    return stream_wk<T, MODE, 1, 4>(x, row_map, (const T*)w0, (const T*)w1, blocks, nblk, dense_rows, (T*)out, N, K, blocked, st);
+  return stream_wk<T, MODE, 2, 2>(x, row_map, (const T*)w0, (const T*)w1, blocks, nblk, dense_rows, (T*)out, N, K, blocked, st);
 }
 
 hipError_t launch_ffn_gateup_stream(int dtype, const void* in, const int32_t* row_map, const void* wg,
                                     const void* wu, const int4* blocks, int bound, int dense_rows, void* h, int N,
-                                    int K, hipStream_t st) {
+                                    int K, int blocked, hipStream_t st) {
   if (dtype == DT_BF16)
-    return stream_t<bf16_t, 0>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st);
-  return stream_t<float, 0>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, st);
+    return stream_t<bf16_t, 0>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, blocked, st);
+  return stream_t<float, 0>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, blocked, st);
 }
 
 hipError_t launch_ffn_down_stream(int dtype, const void* h, const int32_t* row_map, const void* wd,
-                                  const int4* blocks, int bound, int dense_rows, void* y, int N, int K, hipStream_t st) {
-  if (dtype == DT_BF16) return stream_t<bf16_t, 1>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, st);
-  return stream_t<float, 1>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, st);
+                                  const int4* blocks, int bound, int dense_rows, void* y, int N, int K, int blocked,
+                                  hipStream_t st) {
+  if (dtype == DT_BF16) return stream_t<bf16_t, 1>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked, st);
+  return stream_t<float, 1>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked, st);
 }
 
 }  // namespace moe

@@ -63,13 +63,15 @@ hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int
 // Work: the row-block table `blocks` (RB = stream_row_block(), `bound` entries)
 // of the expert groups; blocks == nullptr means one dense group of
 // `dense_rows` rows starting at 0 (weights of group 0).  src(r) = row_map[r]
-// when row_map != nullptr, else r.
+// when row_map != nullptr, else r.  `blocked`: the weights are stored in the
+// blocked order of w_offset (common.h), else row-major.
 int stream_row_block();
 hipError_t launch_ffn_gateup_stream(int dtype, const void* in, const int32_t* row_map, const void* wg,
                                     const void* wu, const int4* blocks, int bound, int dense_rows, void* h, int N,
-                                    int K, hipStream_t st);
+                                    int K, int blocked, hipStream_t st);
 hipError_t launch_ffn_down_stream(int dtype, const void* h, const int32_t* row_map, const void* wd,
-                                  const int4* blocks, int bound, int dense_rows, void* y, int N, int K, hipStream_t st);
+                                  const int4* blocks, int bound, int dense_rows, void* y, int N, int K, int blocked,
+                                  hipStream_t st);
 
 // ffn_gemm.hip -- grouped-GEMM FFN (bf16): same semantics as the streaming
 // kernels, over the row-block table with RB = gemm_row_block() (`bound`
@@ -90,10 +92,13 @@ struct GemmSecond {
 int gemm_row_block();
 hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
                                   const int4* blocks, int bound, int dense_rows, int rows_hint, void* h, int N,
-                                  int K, hipStream_t st, const GemmSecond& sec = GemmSecond{});
+                                  int K, int blocked, hipStream_t st, const GemmSecond& sec = GemmSecond{});
 hipError_t launch_ffn_down_gemm(const void* h, const int32_t* row_map, const void* wd, const int4* blocks, int bound,
-                                int dense_rows, int rows_hint, void* y, int N, int K, hipStream_t st,
+                                int dense_rows, int rows_hint, void* y, int N, int K, int blocked, hipStream_t st,
                                 const GemmSecond& sec = GemmSecond{});
+
+// layout.hip -- row-major -> blocked copy of G [N][K] matrices (w_offset).
+hipError_t launch_pack_weights(int dtype, long long G, int N, int K, const void* src, void* dst, hipStream_t st);
 
 // combine.hip
 hipError_t launch_combine(int dtype, const void* y, const void* y_shared, const int32_t* tok_off,
@@ -119,7 +124,7 @@ hipError_t launch_fold(int mode, int budget, const float* S, const float* L, con
 
 // proxy.hip -- training-free proxy gating of a split layer.
 hipError_t launch_proxy_pack(int dtype, const int32_t* gate_idx, const void* wg, const void* wu, int E_base, int I_sub,
-                             int d, int N, int r, int Ip, void* pg, void* pu, hipStream_t st);
+                             int d, int N, int r, int Ip, void* pg, void* pu, int blocked, hipStream_t st);
 hipError_t launch_proxy_route(int dtype, const int32_t* k, const int32_t* kappa, int T, int k_max, int m, int N, int r,
                               int Ip,
                               const int32_t* base_tok_off, const int32_t* base_ids, const float* base_w,

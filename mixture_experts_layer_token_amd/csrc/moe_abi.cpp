@@ -34,6 +34,7 @@ moe_status check_desc(const moe_desc* d) {
   if (!std::isfinite(d->routed_scale)) return MOE_ERR_SHAPE;
   if (d->k_policy < MOE_K_EXACT || d->k_policy > MOE_K_ROUND_UP) return MOE_ERR_UNSUPPORTED;
   if (d->k_policy == MOE_K_ROUND_UP && (d->k_granule < 1 || d->k_max % d->k_granule)) return MOE_ERR_SHAPE;
+  if (d->weight_layout != MOE_W_ROWMAJOR && d->weight_layout != MOE_W_BLOCKED64) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -269,8 +270,10 @@ moe_status do_gateup(const moe_desc& d, const void* x, const void* wg, const voi
   if (e != hipSuccess) return launched(e);
   if (routed_gemm(d))
     return launched(
-        launch_ffn_gateup_gemm(x, perm_tok, wg, wu, fw.blocks, fw.bound, 0, rows_hint(d), h, d.I, d.d, st, sec));
-  return launched(launch_ffn_gateup_stream(d.dtype, x, perm_tok, wg, wu, fw.blocks, fw.bound, 0, h, d.I, d.d, st));
+        launch_ffn_gateup_gemm(x, perm_tok, wg, wu, fw.blocks, fw.bound, 0, rows_hint(d), h, d.I, d.d, d.weight_layout, st,
+                               sec));
+  return launched(launch_ffn_gateup_stream(d.dtype, x, perm_tok, wg, wu, fw.blocks, fw.bound, 0, h, d.I, d.d,
+                                           d.weight_layout, st));
 }
 
 // `row_map`: the h row of each permuted row (NULL: row p reads h row p).
@@ -280,21 +283,24 @@ moe_status do_down(const moe_desc& d, const void* h, const void* wd, const int32
   hipError_t e = build_blocks ? launch_row_blocks(expert_off, d.E, fw.rb, fw.bound, fw.blocks, st) : hipSuccess;
   if (e != hipSuccess) return launched(e);
   if (routed_gemm(d))
-    return launched(launch_ffn_down_gemm(h, row_map, wd, fw.blocks, fw.bound, 0, rows_hint(d), y, d.d, d.I, st, sec));
-  return launched(launch_ffn_down_stream(d.dtype, h, row_map, wd, fw.blocks, fw.bound, 0, y, d.d, d.I, st));
+    return launched(launch_ffn_down_gemm(h, row_map, wd, fw.blocks, fw.bound, 0, rows_hint(d), y, d.d, d.I,
+                                              d.weight_layout, st, sec));
+  return launched(launch_ffn_down_stream(d.dtype, h, row_map, wd, fw.blocks, fw.bound, 0, y, d.d, d.I, d.weight_layout, st));
 }
 
 moe_status do_shared(const moe_desc& d, const void* x, const void* sg, const void* su, const void* sd, void* h_sh,
                      void* y_sh, hipStream_t st) {
   hipError_t e;
   if (shared_gemm(d)) {
-    e = launch_ffn_gateup_gemm(x, nullptr, sg, su, nullptr, 0, d.T, d.T, h_sh, d.I_shared, d.d, st);
-    if (e == hipSuccess) e = launch_ffn_down_gemm(h_sh, nullptr, sd, nullptr, 0, d.T, d.T, y_sh, d.d, d.I_shared, st);
+    e = launch_ffn_gateup_gemm(x, nullptr, sg, su, nullptr, 0, d.T, d.T, h_sh, d.I_shared, d.d, d.weight_layout, st);
+    if (e == hipSuccess)
+      e = launch_ffn_down_gemm(h_sh, nullptr, sd, nullptr, 0, d.T, d.T, y_sh, d.d, d.I_shared, d.weight_layout, st);
     return launched(e);
   }
-  e = launch_ffn_gateup_stream(d.dtype, x, nullptr, sg, su, nullptr, 0, d.T, h_sh, d.I_shared, d.d, st);
+  e = launch_ffn_gateup_stream(d.dtype, x, nullptr, sg, su, nullptr, 0, d.T, h_sh, d.I_shared, d.d, d.weight_layout, st);
   if (e == hipSuccess)
-    e = launch_ffn_down_stream(d.dtype, h_sh, nullptr, sd, nullptr, 0, d.T, y_sh, d.d, d.I_shared, st);
+    e = launch_ffn_down_stream(d.dtype, h_sh, nullptr, sd, nullptr, 0, d.T, y_sh, d.d, d.I_shared, d.weight_layout,
+                                   st);
   return launched(e);
 }
 
@@ -313,6 +319,22 @@ moe_status moe_workspace_size(const moe_desc* desc, int32_t op, size_t* bytes) {
   if (op < MOE_OP_ROUTE || op > MOE_OP_PATH) return MOE_ERR_UNSUPPORTED;
   *bytes = ws_size(*desc, op);
   return MOE_OK;
+}
+
+moe_status moe_pack_weights(int32_t dtype, int32_t G, int32_t N, int32_t K, const void* src, void* dst,
+                            moe_stream_t stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const int elt = dtype == MOE_BF16 ? 2 : 4, eb = 128 / elt;
+  if (G < 0 || N < 1 || K < 1 || N % 64 || K % eb) return MOE_ERR_SHAPE;
+  const long long n = (long long)G * N * K;
+  if (n >= (1ll << 40)) return MOE_ERR_SHAPE;
+  if (n == 0) return MOE_OK;
+  if (!src || !dst) return MOE_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_ALIGN;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t bytes = (uintptr_t)n * elt;
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_SHAPE;
+  return launched(launch_pack_weights(dtype, G, N, K, src, dst, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_resolve_path(const moe_desc* desc, int32_t* routed_path, int32_t* shared_path) {
@@ -489,7 +511,7 @@ moe_status moe_proxy_pack(const moe_desc* desc, int32_t N, int32_t r, const int3
   if (!gate_idx || !w_gate || !w_up || !wp_gate || !wp_up) return MOE_ERR_NULL;
   if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(wp_gate) || !aligned16(wp_up)) return MOE_ERR_ALIGN;
   return launched(launch_proxy_pack(d.dtype, gate_idx, w_gate, w_up, d.E / N, d.I, d.d, N, r, proxy_width(N, r),
-                                    wp_gate, wp_up, static_cast<hipStream_t>(stream)));
+                                    wp_gate, wp_up, d.weight_layout, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_proxy_route(const moe_desc* desc, int32_t N, int32_t r, int32_t m, const int32_t* k,

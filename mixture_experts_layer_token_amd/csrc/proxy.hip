@@ -25,30 +25,35 @@ namespace moe {
 
 // ---- gather of the gate-neuron rows: one wave per packed row, 16 B per lane ----
 // Packed row q of whole expert e (q < Ip): neuron i = q % r of sub-expert
-// N*e + q / r while q < N*r, a zero row after that.
+// N*e + q / r while q < N*r, a zero row after that.  Source and packed
+// matrices share the weight layout (`blocked`: w_offset in common.h).
 template <typename T>
 __global__ __launch_bounds__(256) void proxy_pack_kernel(const int32_t* __restrict__ gate_idx, const T* __restrict__ wg,
                                                          const T* __restrict__ wu, int E_base, int I_sub, int d, int N,
-                                                         int r, int Ip, T* __restrict__ pg, T* __restrict__ pu) {
+                                                         int r, int Ip, T* __restrict__ pg, T* __restrict__ pu,
+                                                         int blocked) {
   constexpr int LE = 16 / sizeof(T);
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= E_base * Ip) return;
   const int e = row / Ip, q = row - e * Ip;
   bool ok = q < N * r;
   size_t src = 0;
+  int c = 0;
   if (ok) {
     const int sub = N * e + q / r;
-    const int c = gate_idx[(size_t)sub * r + q % r];
+    c = gate_idx[(size_t)sub * r + q % r];
     ok = c >= 0 && c < I_sub;
-    src = ((size_t)sub * I_sub + (ok ? c : 0)) * d;
+    if (!ok) c = 0;
+    src = (size_t)sub * I_sub * d;
   }
-  T* dg = pg + (size_t)row * d;
-  T* du = pu + (size_t)row * d;
+  T* dg = pg + (size_t)e * Ip * d;
+  T* du = pu + (size_t)e * Ip * d;
   for (int o = lane * LE; o < d; o += 64 * LE) {
-    const uint4 vg = ok ? *reinterpret_cast<const uint4*>(wg + src + o) : zero_u4();
-    const uint4 vu = ok ? *reinterpret_cast<const uint4*>(wu + src + o) : zero_u4();
-    *reinterpret_cast<uint4*>(dg + o) = vg;
-    *reinterpret_cast<uint4*>(du + o) = vu;
+    const size_t so = src + w_offset<T>(c, o, d, blocked), dof = w_offset<T>(q, o, d, blocked);
+    const uint4 vg = ok ? *reinterpret_cast<const uint4*>(wg + so) : zero_u4();
+    const uint4 vu = ok ? *reinterpret_cast<const uint4*>(wu + so) : zero_u4();
+    *reinterpret_cast<uint4*>(dg + dof) = vg;
+    *reinterpret_cast<uint4*>(du + dof) = vu;
   }
 }
 
@@ -144,16 +149,16 @@ __global__ __launch_bounds__(256) void proxy_select_kernel(
 }
 
 hipError_t launch_proxy_pack(int dtype, const int32_t* gate_idx, const void* wg, const void* wu, int E_base, int I_sub,
-                             int d, int N, int r, int Ip, void* pg, void* pu, hipStream_t st) {
+                             int d, int N, int r, int Ip, void* pg, void* pu, int blocked, hipStream_t st) {
   const int64_t rows = (int64_t)E_base * Ip;
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)((rows + 3) / 4));
   if (dtype == DT_BF16)
     hipLaunchKernelGGL(proxy_pack_kernel<bf16_t>, grid, dim3(256), 0, st, gate_idx, (const bf16_t*)wg,
-                       (const bf16_t*)wu, E_base, I_sub, d, N, r, Ip, (bf16_t*)pg, (bf16_t*)pu);
+                       (const bf16_t*)wu, E_base, I_sub, d, N, r, Ip, (bf16_t*)pg, (bf16_t*)pu, blocked);
   else
     hipLaunchKernelGGL(proxy_pack_kernel<float>, grid, dim3(256), 0, st, gate_idx, (const float*)wg, (const float*)wu,
-                       E_base, I_sub, d, N, r, Ip, (float*)pg, (float*)pu);
+                       E_base, I_sub, d, N, r, Ip, (float*)pg, (float*)pu, blocked);
   return hipGetLastError();
 }
 

@@ -62,6 +62,7 @@ def test_workspace_sizes():
     (dict(k_policy=2, k_granule=3), 2),
     (dict(router=2, dtype=0), 3),
     (dict(routed_scale=float("inf")), 2),
+    (dict(weight_layout=2), 3), (dict(weight_layout=-1), 3),
 ])
 def test_bad_descriptors_rejected(kw, code):
     assert _ws(_desc(**kw), moe.MOE_OP_FORWARD)[0] == code
@@ -201,3 +202,20 @@ def test_path_route_validates_before_launch():
     assert st == 0 and 0 < n <= _ws(d, moe.MOE_OP_FORWARD)[1]
     assert lib.moe_path_sources(ctypes.byref(d), None, x, x, x, x, x, None, 0, None) == 1
     assert lib.moe_ffn_down_rows(ctypes.byref(d), x, None, x, x, x, None, 0, None) in (1, 4)
+
+
+def test_pack_weights_validates_before_launch():
+    lib = _lib.load()
+    P = lambda v: ctypes.c_void_p(v)
+    a, b = P(1 << 20), P(1 << 30)
+    bf, f32 = moe.MOE_BF16, moe.MOE_F32
+    assert lib.moe_pack_weights(7, 1, 64, 128, a, b, None) == 3             # dtype
+    assert lib.moe_pack_weights(bf, -1, 64, 128, a, b, None) == 2           # G < 0
+    assert lib.moe_pack_weights(bf, 1, 96, 128, a, b, None) == 2            # N % 64
+    assert lib.moe_pack_weights(bf, 1, 64, 96, a, b, None) == 2             # K % 64 (bf16)
+    assert lib.moe_pack_weights(f32, 1, 64, 48, a, b, None) == 2            # K % 32 (fp32)
+    assert lib.moe_pack_weights(bf, 1 << 20, 1 << 14, 1 << 14, a, b, None) == 2  # 2^48 elements
+    assert lib.moe_pack_weights(bf, 1, 64, 128, None, b, None) == 1         # NULL
+    assert lib.moe_pack_weights(bf, 1, 64, 128, P((1 << 20) + 8), b, None) == 5  # alignment
+    assert lib.moe_pack_weights(bf, 2, 64, 128, a, P((1 << 20) + 64 * 128 * 2), None) == 2  # overlap
+    assert lib.moe_pack_weights(bf, 0, 64, 128, None, None, None) == 0      # empty: nothing launched
