@@ -229,13 +229,15 @@ __device__ __forceinline__ void stream_block(const T* __restrict__ in, const int
 // (16 rows x 128 bytes each) and the block's 64 activation rows (128 bytes
 // each) -- is copied into LDS by global->LDS DMA loads of whole 128-byte
 // lines (wave w fetches weight tile w and activation rows 16w..16w+15), two
-// steps ahead in a ring of three stages.  Every wave then multiplies all four
+// steps ahead in a ring of three stages (or more, VAR below).  Every wave then multiplies all four
 // weight tiles with its own 16 activation rows and runs over the whole K, so
 // there is no reduction.  The weights of such a block leave the L2 once, as
 // full lines, instead of once per 32-row half as 64-byte half lines.  With no
 // register loads in the loop, every wait is an explicit count.
 // `ring` holds 3 stages of 16 KB: [weights 64 x 128 B][activations 64 x 128 B].
-constexpr int SHARED_STAGES = 3, SHARED_STAGE_BYTES = 2 * 64 * 128;
+constexpr int SHARED_STAGE_BYTES = 2 * 64 * 128;
+// VAR bits 2-3: extra ring stages (3 + n stages, n + 2 steps ahead).
+template <int VAR> constexpr int shared_stages() { return 3 + ((VAR >> 2) & 3); }
 
 // VAR bit 1: the weight DMA carries the non-temporal hint (the weights are
 // read once per layer).
@@ -247,7 +249,7 @@ __device__ __forceinline__ void stream_block_shared(const T* __restrict__ in, co
   constexpr int LPS = KC / LE;
   constexpr int STEP = 4 * KC;
   constexpr int HALF = TPW / 2;
-  constexpr int NST = SHARED_STAGES;
+  constexpr int NST = shared_stages<VAR>(), AHEAD = NST - 1;
   constexpr int SB = SHARED_STAGE_BYTES, XOFS = SB / 2;
   static_assert(STEP * sizeof(T) == 128 && LPS == 2, "a step is one 128-byte line per row");
   static_assert(TPW == 4, "one weight tile and 16 activation rows per wave");
@@ -295,18 +297,18 @@ __device__ __forceinline__ void stream_block_shared(const T* __restrict__ in, co
 
   // Every step issues the same loads (past the end, the last step again: in
   // bounds, into a stage nobody reads any more), so the counts are constant.
-  issue(0);
-  issue(min(1, nsteps - 1));
+#pragma unroll
+  for (int p = 0; p < AHEAD; ++p) issue(min(p, nsteps - 1));
   for (int s = 0; s < nsteps; ++s) {
-    // step s landed for this wave (step s + 1's loads may be in flight);
-    // after the barrier every wave's part has landed and every wave is done
-    // reading the stage that step s + 2 refills
-    vm_wait_dyn<4>(per_step);
+    // step s landed for this wave (steps s + 1 .. s + AHEAD - 1 may be in
+    // flight); after the barrier every wave's part has landed and every wave
+    // is done reading the stage that step s + AHEAD refills
+    vm_wait_dyn<4 * (AHEAD - 1)>((AHEAD - 1) * per_step);
     lgkm_wait0();
     compiler_fence();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    issue(min(s + 2, nsteps - 1));
+    issue(min(s + AHEAD, nsteps - 1));
     const char* sb = ring + (s % NST) * SB;
     uint4 W[TPW][LPS], X[LPS];
 #pragma unroll
@@ -365,8 +367,8 @@ __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OC
   // shared-tile mode for 33..64-row blocks (see stream_block_shared)
   constexpr bool SHARED = WN == 1 && WK == 4 && TPW == 4 && IL && KC * sizeof(T) == 32;
   constexpr int RED_BYTES = (WK - 1) * WN * SLOT * (int)sizeof(f32x4_t);
-  constexpr int LDS_BYTES = SHARED && SHARED_STAGES * SHARED_STAGE_BYTES > RED_BYTES
-                                ? SHARED_STAGES * SHARED_STAGE_BYTES : RED_BYTES;
+  constexpr int RING_BYTES = shared_stages<VAR>() * SHARED_STAGE_BYTES;
+  constexpr int LDS_BYTES = SHARED && RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   f32x4_t* const red = reinterpret_cast<f32x4_t*>(smem);
 
@@ -478,9 +480,13 @@ int stream_row_block() { return S_ROWS; }
 // shared body with the hint wins everywhere except the short-K down
 // projection, which keeps the shared body without it (Mixtral-shaped gate/up
 // 331 -> 295 us, DSV3-shaped down 1116 -> 1029 us, Qwen3-shaped gate/up
-// 76 -> 73 us; the Qwen3-shaped down loses the hint: 32.5 vs 40 us).
+// 76 -> 73 us; the Qwen3-shaped down loses the hint: 32.5 vs 40 us); a
+// down projection of mid-size K (DSV3-shaped, K = 2048) gains from a ring one
+// stage deeper (1030 -> 1014 us), which the others do not (Mixtral-shaped
+// down 141 vs 143 us, gate/up 292 vs 350 us: two workgroups per CU instead
+// of three).
 static int stream_var(int MODE, int N, int K, int blocked) {
-  if (blocked) return (MODE == 1 && K <= 1024) ? 1 : 3;
+  if (blocked) return MODE == 0 ? 3 : (K <= 1024 ? 1 : (K < 8192 ? 7 : 3));
   if (MODE == 0) return N >= 8192 ? 0 : 3;
   if (K >= 8192) return 3;
   return K <= 1024 ? 1 : 0;
@@ -494,6 +500,9 @@ static hipError_t stream_pd(const T* x, const int32_t* row_map, const T* w0, con
     switch (stream_var(MODE, N, K, blocked)) {
       case 3:
         return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, PD, true, 1, 3>(x, row_map, w0, w1, blocks,
+                                                                                     nblk, dense_rows, out, N, K, blocked, st);
+      case 7:
+        return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, PD, true, 1, 7>(x, row_map, w0, w1, blocks,
                                                                                      nblk, dense_rows, out, N, K, blocked, st);
       case 1:
         return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, PD, true, 1, 1>(x, row_map, w0, w1, blocks,

@@ -119,6 +119,7 @@ def test_blocked_workload_matches_oracle(name, path):
     (520, 8, 256, 256, 4, 256),      # shared expert fused into the GEMM launches
     (48, 4, 2176, 2176, 2, 2176),    # K % 256 = 128 (2 x 2 stream waves), long K
     (300, 8, 128, 128, 8, 0),        # smallest d and I
+    (64, 8, 256, 2048, 2, 0),        # down K = 2048: the deeper-ring streaming body
 ])
 def test_blocked_shapes_match_oracle(dtype, path, T, E, d, I, kmax, Is):
     if dtype == "f32" and path == "gemm":
