@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--graph-steps", type=int, default=4,
                     help="layer steps captured back to back in one HIP graph, as a model's layers would be (the "
                          "largest divisor of --steps not above this); 1 = one graph replay per step")
-    ap.add_argument("--router", default="auto", choices=["auto", "float64", "screened"],
+    ap.add_argument("--router", default="auto", choices=["auto", "float64", "screened", "fused"],
                     help="router algorithm (both give identical routing; they differ in cost)")
     ap.add_argument("--path", default="auto", choices=["auto", "stream", "gemm"], help="FFN path")
     ap.add_argument("--weight-layout", default="blocked", choices=["blocked", "rowmajor"],

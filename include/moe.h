@@ -80,10 +80,15 @@ typedef enum {
 /* Router algorithm.  Both produce identical ids, order and weights (the
  * routing contract below); they differ only in cost. */
 typedef enum {
-  MOE_ROUTER_AUTO = 0,      /* screened for bf16 when T * E * d >= 2^30, else float64 */
+  MOE_ROUTER_AUTO = 0,      /* screened for bf16 when T * E * d >= 2^30; else fused when
+                               T <= 1024, E <= 256 and E * d <= 2^16; else float64 */
   MOE_ROUTER_FLOAT64 = 1,   /* every logit summed in float64 (split-K tiles) */
-  MOE_ROUTER_SCREENED = 2   /* bf16 only: MFMA logits with a proven error bound pick the
+  MOE_ROUTER_SCREENED = 2,  /* bf16 only: MFMA logits with a proven error bound pick the
                                candidates; only candidates get the float64 sum */
+  MOE_ROUTER_FUSED = 3      /* small batches only (T <= 1024, E <= 256, E * d <= 2^19; other
+                               shapes: MOE_ERR_UNSUPPORTED): every logit summed in float64
+                               by one workgroup per token, offsets and selection in the
+                               same launch */
 } moe_router;
 
 /* Budget each token executes, from its requested k_t (validated first: a

@@ -15,7 +15,7 @@ import torch
 from . import _lib
 from ._lib import (MOE_BF16, MOE_DEV_BAD_K, MOE_F32, MOE_OP_COMBINE, MOE_OP_FFN,  # noqa: F401
                    MOE_OP_FORWARD, MOE_OP_PERMUTE, MOE_OP_ROUTE, MOE_PATH_AUTO, MOE_PATH_GEMM,
-                   MOE_PATH_STREAM, MOE_ROUTER_AUTO, MOE_ROUTER_FLOAT64, MOE_ROUTER_SCREENED, MOE_K_EXACT,
+                   MOE_PATH_STREAM, MOE_ROUTER_AUTO, MOE_ROUTER_FLOAT64, MOE_ROUTER_SCREENED, MOE_ROUTER_FUSED, MOE_K_EXACT,
                    MOE_K_BATCH_MAX, MOE_K_ROUND_UP, MOE_OP_FOLD, MOE_OP_PATH, MOE_FOLD_TOKEN, MOE_FOLD_POOL,
                    MOE_W_ROWMAJOR, MOE_W_BLOCKED64, moe_desc)
 
@@ -31,7 +31,8 @@ __all__ = [
 
 _DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 _PATHS = {"auto": MOE_PATH_AUTO, "stream": MOE_PATH_STREAM, "gemm": MOE_PATH_GEMM}
-_ROUTERS = {"auto": MOE_ROUTER_AUTO, "float64": MOE_ROUTER_FLOAT64, "screened": MOE_ROUTER_SCREENED}
+_ROUTERS = {"auto": MOE_ROUTER_AUTO, "float64": MOE_ROUTER_FLOAT64, "screened": MOE_ROUTER_SCREENED,
+            "fused": MOE_ROUTER_FUSED}
 _K_POLICIES = {"exact": MOE_K_EXACT, "batch_max": MOE_K_BATCH_MAX, "round_up": MOE_K_ROUND_UP}
 _LAYOUTS = {"rowmajor": MOE_W_ROWMAJOR, "blocked": MOE_W_BLOCKED64}
 

@@ -12,7 +12,7 @@ c_size = ctypes.c_size_t
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_GEMM = 0, 1, 2
-MOE_ROUTER_AUTO, MOE_ROUTER_FLOAT64, MOE_ROUTER_SCREENED = 0, 1, 2
+MOE_ROUTER_AUTO, MOE_ROUTER_FLOAT64, MOE_ROUTER_SCREENED, MOE_ROUTER_FUSED = 0, 1, 2, 3
 MOE_K_EXACT, MOE_K_BATCH_MAX, MOE_K_ROUND_UP = 0, 1, 2
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_FORWARD, MOE_OP_FOLD, MOE_OP_PATH = 0, 1, 2, 3, 4, 5, 6
 MOE_FOLD_TOKEN, MOE_FOLD_POOL = 0, 1

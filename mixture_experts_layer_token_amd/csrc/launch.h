@@ -28,6 +28,13 @@ hipError_t launch_router(int dtype, const void* x, const void* w, const int32_t*
 // Sums the S slices in order, adds the bias, rounds to float32, selects top-k_t.
 hipError_t launch_topk(const double* part, int S, const float* bias, const int32_t* tok_off, int T, int E,
                        int k_max, float scale, int32_t* ids, float* wts, hipStream_t st);
+// Small batches in one launch (one workgroup per token, float64 over the whole
+// d): offsets, status, ids and weights as launch_router + launch_topk.
+int fused_router_ok(int T, int d, int E);
+int fused_router_auto(int T, int d, int E);
+hipError_t launch_router_fused(int dtype, const void* x, const void* w, const float* bias, const int32_t* k, int T,
+                               int d, int E, int k_max, BudgetPolicy pol, float scale, int32_t* tok_off,
+                               int32_t* status, int32_t* ids, float* wts, hipStream_t st);
 
 // route_screen.hip -- bf16 only: MFMA logits with an error bound screen the
 // candidates; exact fp64 logits for candidates; same selection and weights.

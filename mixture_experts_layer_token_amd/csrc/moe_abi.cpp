@@ -24,7 +24,8 @@ moe_status check_desc(const moe_desc* d) {
   if (!d) return MOE_ERR_NULL;
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_GEMM) return MOE_ERR_UNSUPPORTED;
-  if (d->router < MOE_ROUTER_AUTO || d->router > MOE_ROUTER_SCREENED) return MOE_ERR_UNSUPPORTED;
+  if (d->router < MOE_ROUTER_AUTO || d->router > MOE_ROUTER_FUSED) return MOE_ERR_UNSUPPORTED;
+  if (d->router == MOE_ROUTER_FUSED && !fused_router_ok(d->T, d->d, d->E)) return MOE_ERR_UNSUPPORTED;
   if (d->router == MOE_ROUTER_SCREENED && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->T < 0 || d->E < 1 || d->E > 1024 || d->k_max < 1 || d->k_max > d->E) return MOE_ERR_SHAPE;
   if (d->d < kDimQuantum || d->d > 65536 || d->d % kDimQuantum) return MOE_ERR_SHAPE;
@@ -61,7 +62,7 @@ BudgetPolicy budget(const moe_desc& d) {
 }
 int n_blocks(const moe_desc& d) { return (d.T + PERM_BLOCK - 1) / PERM_BLOCK; }
 
-struct RouteWs { double* part; int splits; float* approx; float* absum; bool screened; };
+struct RouteWs { double* part; int splits; float* approx; float* absum; bool screened; bool fused; };
 struct PermWs { int32_t* block_counts; int32_t* block_base; };
 struct FfnWs { int4* blocks; int bound; int rb; void* h; void* h_sh; };
 
@@ -69,12 +70,26 @@ struct FfnWs { int4* blocks; int bound; int rb; void* h; void* h_sh; };
 // smaller ones sum every logit in float64 directly.
 bool screened_router(const moe_desc& d) {
   if (d.router == MOE_ROUTER_SCREENED) return true;
-  if (d.router == MOE_ROUTER_FLOAT64) return false;
+  if (d.router == MOE_ROUTER_FLOAT64 || d.router == MOE_ROUTER_FUSED) return false;
   return d.dtype == MOE_BF16 && (double)d.T * d.E * d.d >= 1073741824.0;
+}
+// Small batches with few router rows (T <= 1024, E <= 256, E * d <= 2^16)
+// route in one launch under AUTO; MOE_ROUTER_FUSED asks for it up to 2^19.
+bool fused_router(const moe_desc& d) {
+  if (d.router == MOE_ROUTER_FUSED) return true;
+  if (d.router != MOE_ROUTER_AUTO || screened_router(d)) return false;
+  return fused_router_auto(d.T, d.d, d.E) != 0;
 }
 
 void plan_route(const moe_desc& d, Carver& c, RouteWs& w) {
   w.screened = screened_router(d);
+  w.fused = fused_router(d);
+  if (w.fused) {  // no partial sums
+    w.part = nullptr;
+    w.approx = w.absum = nullptr;
+    w.splits = 0;
+    return;
+  }
   w.splits = w.screened ? router_screen_splits(d.T, d.d, d.E) : router_splits(d.T, d.d, d.E);
   const size_t ste = (size_t)w.splits * d.T * d.E;
   const size_t bytes = w.screened ? 2 * ste * sizeof(float) : ste * sizeof(double);
@@ -242,6 +257,9 @@ bool fused_shared(const moe_desc& d) {
 
 moe_status do_route(const moe_desc& d, const void* x, const void* wr, const float* bias, const int32_t* k,
                     int32_t* tok_off, int32_t* ids, float* w, int32_t* status, const RouteWs& ws, hipStream_t st) {
+  if (ws.fused)
+    return launched(launch_router_fused(d.dtype, x, wr, bias, k, d.T, d.d, d.E, d.k_max, budget(d), d.routed_scale,
+                                        tok_off, status, ids, w, st));
   if (ws.screened)
     return launched(launch_router_screen(x, wr, bias, k, d.T, d.d, d.E, d.k_max, budget(d), ws.splits, d.routed_scale,
                                          ws.approx,

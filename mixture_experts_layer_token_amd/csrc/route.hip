@@ -24,6 +24,24 @@ namespace moe {
 // One more slice index (z = S) holds the token-offset scan in its first
 // workgroup, so the scan runs beside the tiles instead of before one of them.
 constexpr int RT = 64, RK = 32;
+constexpr int FUSED_MAX_T = 1024;
+
+// acc + sum of the products of the 16-byte chunks a (x) and b (w), each
+// product exact in float64, added in element order.
+template <typename T>
+__device__ __forceinline__ double dot16_f64(uint4 a, uint4 b, double acc) {
+  const uint32_t ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (sizeof(T) == 2) {
+      acc = fma((double)__uint_as_float(ua[i] << 16), (double)__uint_as_float(ub[i] << 16), acc);
+      acc = fma((double)__uint_as_float(ua[i] & 0xffff0000u), (double)__uint_as_float(ub[i] & 0xffff0000u), acc);
+    } else {
+      acc = fma((double)__uint_as_float(ua[i]), (double)__uint_as_float(ub[i]), acc);
+    }
+  }
+  return acc;
+}
 
 // NR rows x RK elements of src (rows past nrows read as zero) into dst[k][row].
 template <int NR, int LD, typename T>
@@ -167,6 +185,106 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ pa
   if (kt == 0) return;
   wave_topk_softmax<KPL>(key, kt, scale, ids + base, wts + base,
                          topk_scratch + (threadIdx.x >> 6) * scratch_slots);
+}
+
+// ---------------------------------------------------------------------------
+// Fused router for small batches: one workgroup per token sums every logit of
+// its token over the whole d in float64 and selects, in one launch.  Each
+// workgroup first runs the budget scan of the whole batch (at most
+// FUSED_MAX_T budgets) into LDS, so no second launch has to wait for the
+// offsets; the first workgroup also writes tok_off and the status.  Thread
+// (e, s) of the 256 sums expert e over the 16-byte chunks s, s + S, ... of d
+// (EP = E rounded up to a power of two, S = 256 / EP slices), and the slice
+// sums of an expert are added in ascending slice order, so the float64
+// summation order is fixed.
+int fused_router_ok(int T, int d, int E) { return T <= FUSED_MAX_T && E <= 256 && (long long)E * d <= (1 << 19); }
+// AUTO takes it only where one workgroup's router rows are few: every
+// workgroup streams all E * d router weights, so the Qwen3-shaped layer
+// (E * d = 2^18) routes faster split over K (139 vs 155 us per layer), the
+// Mixtral-shaped one (2^15) faster fused.
+int fused_router_auto(int T, int d, int E) { return fused_router_ok(T, d, E) && (long long)E * d <= (1 << 16); }
+
+template <typename T, int KPL>
+__global__ __launch_bounds__(256) void router_fused_kernel(const T* __restrict__ x, const T* __restrict__ w,
+                                                           const float* __restrict__ bias,
+                                                           const int32_t* __restrict__ k, int T_, int d, int E,
+                                                           int EP, int k_max, BudgetPolicy pol, float scale,
+                                                           int32_t* __restrict__ tok_off, int32_t* __restrict__ status,
+                                                           int32_t* __restrict__ ids, float* __restrict__ wts) {
+  constexpr int LE = 16 / sizeof(T);
+  __shared__ int32_t offs[FUSED_MAX_T + 1];
+  __shared__ int32_t scan_part[257];
+  __shared__ double red[256];
+  __shared__ uint64_t scratch[257];
+  const int tid = threadIdx.x, t = blockIdx.x;
+  token_offsets_block<256>(k, T_, k_max, pol, offs, t == 0 ? status : nullptr, scan_part, scan_part + 256);
+  __syncthreads();
+  if (t == 0)
+    for (int i = tid; i <= T_; i += 256) tok_off[i] = offs[i];
+  if (t >= T_) return;
+  const int base = offs[t], kt = offs[t + 1] - base;
+
+  const int S = 256 / EP, e = tid % EP, sl = tid / EP;
+  const int nch = d / LE;
+  double acc = 0.0;
+  if (e < E) {
+    const T* xr = x + (size_t)t * d;
+    const T* wr = w + (size_t)e * d;
+    // eight chunks in flight per thread, added in ascending chunk order
+    constexpr int U = 8;
+    for (int c0 = sl; c0 < nch; c0 += U * S) {
+      uint4 xa[U], wa[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * S;
+        xa[u] = c < nch ? *reinterpret_cast<const uint4*>(xr + c * LE) : zero_u4();
+        wa[u] = c < nch ? *reinterpret_cast<const uint4*>(wr + c * LE) : zero_u4();
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (c0 + u * S < nch) acc = dot16_f64<T>(xa[u], wa[u], acc);
+    }
+  }
+  red[sl * EP + e] = acc;
+  __syncthreads();
+  if (tid >= 64 || kt == 0) return;
+  const int lane = tid;
+  uint32_t key[KPL];
+#pragma unroll
+  for (int q = 0; q < KPL; ++q) {
+    const int ee = lane + 64 * q;
+    key[q] = 0;
+    if (ee < E) {
+      double l = 0.0;
+      for (int s2 = 0; s2 < S; ++s2) l += red[s2 * EP + ee];
+      if (bias) l += (double)bias[ee];
+      key[q] = logit_key((float)l);
+    }
+  }
+  wave_topk_softmax<KPL>(key, kt, scale, ids + base, wts + base, scratch);
+}
+
+hipError_t launch_router_fused(int dtype, const void* x, const void* w, const float* bias, const int32_t* k, int T,
+                               int d, int E, int k_max, BudgetPolicy pol, float scale, int32_t* tok_off,
+                               int32_t* status, int32_t* ids, float* wts, hipStream_t st) {
+  if (!fused_router_ok(T, d, E)) return hipErrorInvalidValue;
+  int EP = 1;
+  while (EP < E) EP *= 2;
+  const dim3 grid(max(T, 1));
+#define MOE_FUSED(TY, KPL)                                                                                       \
+  hipLaunchKernelGGL((router_fused_kernel<TY, KPL>), grid, dim3(256), 0, st, (const TY*)x, (const TY*)w, bias, k, T, \
+                     d, E, EP, k_max, pol, scale, tok_off, status, ids, wts)
+  if (dtype == DT_BF16) {
+    if (E <= 64) MOE_FUSED(bf16_t, 1);
+    else if (E <= 128) MOE_FUSED(bf16_t, 2);
+    else MOE_FUSED(bf16_t, 4);
+  } else {
+    if (E <= 64) MOE_FUSED(float, 1);
+    else if (E <= 128) MOE_FUSED(float, 2);
+    else MOE_FUSED(float, 4);
+  }
+#undef MOE_FUSED
+  return hipGetLastError();
 }
 
 int router_splits(int T, int d, int E) {

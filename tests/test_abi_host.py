@@ -47,9 +47,13 @@ def test_workspace_sizes():
     A = 64 * 2
     # forward holds at least H [A, I] and Y [A, d] in bf16
     assert fwd >= A * 14336 * 2 + A * 4096 * 2
-    for op in (moe.MOE_OP_ROUTE, moe.MOE_OP_PERMUTE, moe.MOE_OP_FFN):
+    for op in (moe.MOE_OP_PERMUTE, moe.MOE_OP_FFN):
         st, n = _ws(d, op)
         assert st == 0 and 0 < n <= fwd
+    # the small-batch router needs no partial sums; the split-K one does
+    assert _ws(d, moe.MOE_OP_ROUTE) == (0, 0)
+    st, n = _ws(_desc(router=moe.MOE_ROUTER_FLOAT64), moe.MOE_OP_ROUTE)
+    assert st == 0 and 0 < n <= _ws(_desc(router=moe.MOE_ROUTER_FLOAT64), moe.MOE_OP_FORWARD)[1]
     assert _ws(d, moe.MOE_OP_COMBINE) == (0, 0)
     assert _ws(_desc(T=0), moe.MOE_OP_FORWARD)[0] == 0
 
@@ -57,7 +61,8 @@ def test_workspace_sizes():
 @pytest.mark.parametrize("kw,code", [
     (dict(d=100), 2), (dict(I=64), 2), (dict(E=0), 2), (dict(E=1025, k_max=1), 2),
     (dict(k_max=9), 2), (dict(k_max=0), 2), (dict(T=-1), 2), (dict(I_shared=100), 2),
-    (dict(T=1 << 28, k_max=8), 2), (dict(dtype=7), 3), (dict(path=5), 3), (dict(router=3), 3),
+    (dict(T=1 << 28, k_max=8), 2), (dict(dtype=7), 3), (dict(path=5), 3), (dict(router=4), 3),
+    (dict(router=3, E=256, k_max=2), 3), (dict(router=3, T=1025), 3),
     (dict(k_policy=3), 3), (dict(k_policy=-1), 3), (dict(k_policy=2, k_granule=0), 2),
     (dict(k_policy=2, k_granule=3), 2),
     (dict(router=2, dtype=0), 3),
@@ -70,7 +75,8 @@ def test_bad_descriptors_rejected(kw, code):
 
 def test_entry_points_validate_before_launch():
     lib = _lib.load()
-    d = _desc(T=4, d=128, E=4, I=128, k_max=2)
+    # the split-K router, which needs a workspace (the small-batch router needs none)
+    d = _desc(T=4, d=128, E=4, I=128, k_max=2, router=moe.MOE_ROUTER_FLOAT64)
     P = lambda v: ctypes.c_void_p(v)
     # NULL pointers
     assert lib.moe_route(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None) == 1

@@ -80,7 +80,7 @@ def test_shapes_and_ragged(dtype, T, E, d, I, kmax, Is):
     compare_out(got["out"], oracle_out(layer, tokens), dtype, tokens)
 
 
-@pytest.mark.parametrize("router", ["float64", "screened"])
+@pytest.mark.parametrize("router", ["float64", "screened", "fused"])
 def test_zero_tokens(router):
     layer = make_custom_layer(T=0, d=128, E=4, I=128, k=[], dtype="bf16", k_max=2, device="cuda")
     out, stats, status = run_forward(layer, router=router)
@@ -108,7 +108,7 @@ def test_invalid_k_flagged_and_dropped():
 
 
 @pytest.mark.parametrize("T", [64, 300])
-@pytest.mark.parametrize("router", ["float64", "screened"])
+@pytest.mark.parametrize("router", ["float64", "screened", "fused"])
 @pytest.mark.parametrize("policy,granule", [("batch_max", 1), ("round_up", 4), ("round_up", 2)])
 def test_budget_policies(policy, granule, router, T):
     """Over-serving comparators (MoE-Prism §III-C1: a mixed dispatch runs the
@@ -135,7 +135,7 @@ def test_budget_policies(policy, granule, router, T):
     _say(f"[budgets] {policy}/{granule} {router} T={T}: A={got['A']} {err}")
 
 
-@pytest.mark.parametrize("router", ["float64", "screened"])
+@pytest.mark.parametrize("router", ["float64", "screened", "fused"])
 def test_exact_ties_break_to_lower_index(router):
     """Zero hidden states make every logit equal its bias; duplicated router
     rows make exactly tied logits for any x."""
@@ -152,6 +152,27 @@ def test_exact_ties_break_to_lower_index(router):
         for e in sel:
             if e % 2 == 1:
                 assert e - 1 in sel          # an odd copy is only taken after its even twin
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T,E,d,kmax", [(1024, 256, 2048, 16), (1, 1, 128, 1), (77, 3, 384, 3),
+                                        (300, 128, 4096, 8), (64, 8, 4096, 2)])
+def test_fused_router_matches_split_and_oracle(dtype, T, E, d, kmax):
+    """The one-launch router of small batches: routing bit-exact against the
+    oracle and equal to the split-K float64 router (ids, weights, offsets),
+    at the largest batch and E x d it takes, E = 1 and a non-power-of-two E."""
+    rng = np.random.default_rng(T * 7 + E)
+    k = rng.integers(0, kmax + 1, size=T)
+    k[0] = kmax
+    layer = make_custom_layer(T=T, d=d, E=E, I=128, k=k, dtype=dtype, k_max=kmax, zipf=0.9, seed=T + E,
+                              device="cuda")
+    a = run_stages(layer, router="fused")
+    b = run_stages(layer, router="float64")
+    r, p = oracle_routing(layer)
+    check_routing(a, r, p)
+    for key in ("tok_off", "ids", "w", "perm_tok", "inv_perm"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    assert a["status"] == b["status"] == 0
 
 
 def test_deterministic_bits():
