@@ -19,7 +19,7 @@ __device__ __forceinline__ void unpack(const uint4& v, float (&f)[8]) {
 // The rows of CB assignments are requested together, one batch ahead of the
 // batch being summed; the sum runs in ascending j (the loads overlap, the
 // arithmetic order does not change).
-constexpr int CB = 4;
+constexpr int CB = 8;
 
 template <typename T>
 __device__ __forceinline__ void load_chunk(const T* p, float (&f)[16 / sizeof(T)]);
@@ -75,7 +75,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
         const int a = a0 + b * CB + j;
-        r[j] = a < a1 ? *reinterpret_cast<const uint4*>(y + (size_t)inv_perm[a] * d + c * LE) : zero_u4();
+        // Y is read exactly once: non-temporal loads keep it from displacing
+        // anything in the caches
+        r[j] = zero_u4();
+        if (a < a1) {
+          const u32x4_t v = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4_t*>(y + (size_t)inv_perm[a] * d + c * LE));
+          r[j] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
       }
     };
     auto consume = [&](const uint4 (&r)[CB], int b) {
