@@ -38,6 +38,17 @@
 // first fragments of stage kt+1 are read during the last MFMAs of stage kt.
 // One barrier per stage; the DMA waits are explicit vmcnt counts.
 //
+// Ring depth per operand (DEEP).  The activation and weight parts of a stage
+// live in rings of their own (XS and WS buffers).  DEEP = 0: both STAGES
+// deep, the stage's x then w loads issued together.  DEEP = 2 (the 256-row
+// tiles): the weights get a third buffer (the 32 KB of LDS a two-stage ring
+// of 256-row tiles leaves free), so they run two stages ahead and the
+// gathered rows one: the loads go out
+// as D0 S0 D1 S1 D2, then after the barrier of stage kt S(kt+2) and D(kt+3)
+// (D = the deeper operand), and stage kt+1 only waits for everything but
+// D(kt+2).  Sub-expert-shaped layer, bit-identical outputs: down 400 -> 377
+// us, gate/up 475 -> 462 us (DEEP = 1, rows deeper, was slower: 385 / 501).
+//
 // Scheduling of tiles.  The rows of each expert are cut into row blocks of 256
 // listed in a row-block table built on the device from the per-expert counts;
 // a row block is GBM/BM row tiles, each times the N tiles.  The grid is sized
@@ -62,7 +73,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 }  // namespace
 
 // MODE 0: gate/up pair + SwiGLU epilogue.  MODE 1: down projection.
-template <int MODE, int BM, int BNW, int WM, int WN, int STAGES>
+// DEEP: 0 uniform ring, 1 activations one stage deeper, 2 weights one stage
+// deeper (STAGES = 2 only).
+template <int MODE, int BM, int BNW, int WM, int WN, int STAGES, int DEEP = 0>
 __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     const bf16_t* __restrict__ in, const int32_t* __restrict__ row_map, const bf16_t* __restrict__ w0,
     const bf16_t* __restrict__ w1, const int4* __restrict__ blocks, int bound, int dense_rows,
@@ -83,7 +96,10 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   // of EPITCH bytes: 16 bytes of padding keep the rows 16-byte aligned and
   // spread the staging writes over the banks).
   constexpr int EPITCH = BNW * 2 + 16;
-  constexpr int LDS_BYTES = (MODE == 1 && BM * EPITCH > STAGES * SBYTES) ? BM * EPITCH : STAGES * SBYTES;
+  constexpr int XS = STAGES + (DEEP == 1 ? 1 : 0), WS = STAGES + (DEEP == 2 ? 1 : 0);
+  constexpr int WBYTES = WROWS * 128, RING = XS * XBYTES + WS * WBYTES;
+  static_assert(DEEP == 0 || STAGES == 2, "one deeper operand over a two-stage ring");
+  constexpr int LDS_BYTES = (MODE == 1 && BM * EPITCH > RING) ? BM * EPITCH : RING;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   // ---- which (row block, row tile, N tile) this workgroup owns.  Row tiles
@@ -169,18 +185,28 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   int per_stage = WI;  // DMA instructions this wave issues per stage
 #pragma unroll
   for (int j = 0; j < XI; ++j) per_stage += xany[j] ? 1 : 0;
-  auto issue = [&](int kt, int buf) {
-    char* sb = lds + buf * SBYTES;
+  const int xcnt = per_stage - WI;  // x DMA instructions of this wave per stage
+  auto xbuf = [&](int kt) { return lds + (kt % XS) * XBYTES; };
+  auto wbuf = [&](int kt) { return lds + XS * XBYTES + (kt % WS) * WBYTES; };
+  auto issue_x = [&](int kt) {
+    char* sb = xbuf(kt);
     const int ko = kt * BK;
 #pragma unroll
     for (int j = 0; j < XI; ++j)
       if (xany[j] && xon[j])
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)(xsrc[j] + ko), (lds_ptr_t)(sb + (j * NW + wave) * 1024), 16, 0, 0);
+  };
+  auto issue_w = [&](int kt) {
+    char* sb = wbuf(kt);
 #pragma unroll
     for (int j = 0; j < WI; ++j)
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[j] + kt * kw), (lds_ptr_t)(sb + XBYTES + (j * NW + wave) * 1024),
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[j] + kt * kw), (lds_ptr_t)(sb + (j * NW + wave) * 1024),
                                        16, 0, 0);
   };
+  // deep / shallow operand of the DEEP ring
+  auto issue_d = [&](int kt) { if (DEEP == 1) issue_x(kt); else issue_w(kt); };
+  auto issue_s = [&](int kt) { if (DEEP == 1) issue_w(kt); else issue_x(kt); };
+  const int dcnt = DEEP == 1 ? xcnt : WI, scnt = DEEP == 1 ? WI : xcnt;
 
   f32x16_t acc[NMAT * TNW][TMW];
 #pragma unroll
@@ -205,8 +231,8 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     u32x4_t fw[2][NMAT * TNW], fx[2][TMW > 0 ? TMW : 1];
     auto load_frags = [&](int buf, int s, int slot) {
       if constexpr (LIVE > 0) {
-        const char* xs = lds + buf * SBYTES;
-        const char* ws = xs + XBYTES;
+        const char* xs = xbuf(buf);
+        const char* ws = wbuf(buf);
 #pragma unroll
         for (int i = 0; i < LIVE; ++i)
           fx[slot][i] = *reinterpret_cast<const u32x4_t*>(xs + lds_off(wm * (BM / WM) + i * 32 + l32, 2 * s + lh));
@@ -240,17 +266,25 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
       if constexpr (NFRAG > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NFRAG - NPAIR, 0);
     };
 
+    if constexpr (DEEP == 0) {
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s)
-      if (s < nk) issue(s, s);
-    // stage 0 landed: the stages issued after it may still be in flight
-    vm_wait_dyn<(STAGES - 1) * (XI + WI)>((min(nk, STAGES) - 1) * per_stage);
+      for (int s = 0; s < STAGES; ++s)
+        if (s < nk) { issue_x(s); issue_w(s); }
+      // stage 0 landed: the stages issued after it may still be in flight
+      vm_wait_dyn<(STAGES - 1) * (XI + WI)>((min(nk, STAGES) - 1) * per_stage);
+    } else {
+      // D0 S0 D1 S1 D2; stage 0 needs D0 and S0
+      issue_d(0); issue_s(0);
+      if (1 < nk) { issue_d(1); issue_s(1); }
+      if (2 < nk) issue_d(2);
+      vm_wait_dyn<2 * (XI + WI)>((1 < nk ? dcnt + scnt : 0) + (2 < nk ? dcnt : 0));
+    }
     compiler_fence();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
     load_frags(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt % STAGES;
+      const int buf = kt;  // stage index; the buffers are taken modulo their ring sizes
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         if (s + 1 < KS) {
@@ -261,14 +295,24 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
           // is refilled.  On the last stage nothing is waited for and the reads
           // below touch a buffer whose values are never used, which keeps the
           // step branch-free so its reads interleave with its MFMAs.
-          const int later = max(0, min(nk - 1, kt + STAGES - 1) - (kt + 1));
-          vm_wait_dyn<(STAGES - 2) * (XI + WI)>(later * per_stage);
+          if constexpr (DEEP == 0) {
+            const int later = max(0, min(nk - 1, kt + STAGES - 1) - (kt + 1));
+            vm_wait_dyn<(STAGES - 2) * (XI + WI)>(later * per_stage);
+          } else {
+            // D(kt+1) and S(kt+1) landed; only D(kt+2) may still be in flight
+            vm_wait_dyn<(XI > WI ? XI : WI)>(kt + 2 < nk ? dcnt : 0);
+          }
           lgkm_wait0();
           compiler_fence();
           __builtin_amdgcn_s_barrier();
           compiler_fence();
-          if (kt + STAGES < nk) issue(kt + STAGES, buf);
-          load_frags((kt + 1) % STAGES, 0, 0);
+          if constexpr (DEEP == 0) {
+            if (kt + STAGES < nk) { issue_x(kt + STAGES); issue_w(kt + STAGES); }
+          } else {
+            if (kt + 2 < nk) issue_s(kt + 2);
+            if (kt + 3 < nk) issue_d(kt + 3);
+          }
+          load_frags(kt + 1, 0, 0);
         }
         mma(s & 1);
         interleave();
@@ -352,7 +396,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
 
 int gemm_row_block() { return GBM; }
 
-template <int MODE, int BM, int BNW, int WM, int WN, int STAGES>
+template <int MODE, int BM, int BNW, int WM, int WN, int STAGES, int DEEP = 0>
 static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, const void* w0, const void* w1,
                                       const int4* blocks, int bound, int dense_rows, void* out, int N, int K,
                                       int blocked, hipStream_t st, const GemmSecond& sec = GemmSecond{}) {
@@ -362,7 +406,7 @@ static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, co
   if (total == 0) return hipSuccess;
   const long long nwg = ((total + 7) / 8) * 8;
   if (nwg > 0x7fffffffLL / (64 * WM * WN)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, STAGES>), dim3((unsigned)nwg), dim3(64 * WM * WN), 0,
+  hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, STAGES, DEEP>), dim3((unsigned)nwg), dim3(64 * WM * WN), 0,
                      st, (const bf16_t*)in, row_map, (const bf16_t*)w0, (const bf16_t*)w1, blocks, bound, dense_rows,
                      (bf16_t*)out, N, K, (const bf16_t*)sec.in, (const bf16_t*)sec.w0, (const bf16_t*)sec.w1,
                      (bf16_t*)sec.out, sec.rows, blocked);
@@ -377,7 +421,8 @@ hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const 
                                   const int4* blocks, int bound, int dense_rows, int rows_hint, void* h, int N,
                                   int K, int blocked, hipStream_t st, const GemmSecond& sec) {
   if (rows_hint >= GBM)
-    return launch_gemm_variant<0, 256, 128, 4, 2, 2>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, blocked, st, sec);
+    return launch_gemm_variant<0, 256, 128, 4, 2, 2, 2>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, blocked, st,
+                                                      sec);
   return launch_gemm_variant<0, 128, 128, 2, 4, 3>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, blocked, st, sec);
 }
 
@@ -386,8 +431,10 @@ hipError_t launch_ffn_down_gemm(const void* h, const int32_t* row_map, const voi
                                 const GemmSecond& sec) {
   if (rows_hint >= GBM) {
     if (N % 256 == 0)
-      return launch_gemm_variant<1, 256, 256, 4, 2, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked, st, sec);
-    return launch_gemm_variant<1, 256, 128, 4, 2, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked, st, sec);
+      return launch_gemm_variant<1, 256, 256, 4, 2, 2, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked,
+                                                         st, sec);
+    return launch_gemm_variant<1, 256, 128, 4, 2, 2, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked, st,
+                                                       sec);
   }
   if (N % 256 == 0)
     return launch_gemm_variant<1, 128, 256, 2, 2, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked, st, sec);
