@@ -184,6 +184,8 @@ typedef void* moe_stream_t;
 moe_status moe_workspace_size(const moe_desc* desc, int32_t op, size_t* bytes);
 
 /*
+ * Not a step of the method (the pages fix no storage order for the expert
+ * weights): a load-time conversion of this library.
  * Re-lay G row-major [N][K] matrices (contiguous, matrix g at g * N * K) into
  * the MOE_W_BLOCKED64 order; a weight stack is converted once, when it is
  * loaded, and then passed with desc->weight_layout = MOE_W_BLOCKED64.  A pure
