@@ -241,7 +241,10 @@ moe_status moe_route(const moe_desc* desc, const void* x, const void* w_router,
  *   expert_off    int32 [E+1] out: exclusive scan of expert_counts
  *   perm_tok      int32 [T*k_max] out: token of sorted row p
  *   perm_src      int32 [T*k_max] out: assignment index tok_off[t]+j of sorted row p
- *   inv_perm      int32 [T*k_max] out: sorted row of assignment a
+ *   inv_perm      int32 [T*k_max] out: sorted row of assignment a; -1 for an
+ *                 assignment whose expert id is outside [0, E) (never
+ *                 produced by moe_route: such an entry gets no row, is not
+ *                 counted, and moe_combine skips it)
  *   n_active      int32 [1] out: experts with at least one assignment
  *                 (the activated experts whose weights a batch loads; METRO
  *                 reading notes, arXiv 2512.09277, Q1)
@@ -360,7 +363,10 @@ moe_status moe_fold(const moe_desc* desc, int32_t mode, int32_t budget, const fl
  *           whole-expert rows for a descriptor (T, d, E/N, Ip, m) and the
  *           weights wp_gate / wp_up
  *   tok_off int32 [T+1], topk_ids int32 [T*k_max], topk_w float [T*k_max] out
- *           (CSR like moe_route's; within a pick, chosen sub-experts by score)
+ *           (CSR like moe_route's; within a pick, chosen sub-experts by
+ *           score; a whole-expert pick outside [0, E/N) fills its kappa_j
+ *           slots with id -1 and weight 0, which moe_permute and moe_combine
+ *           skip)
  *   dev_status int32 [1] out or NULL: MOE_DEV_BAD_K for a k_t outside
  *           [0, k_max] or whose kappa row has an entry outside [0, N] or does
  *           not sum to k_t (such a token runs nothing)
@@ -452,19 +458,39 @@ moe_status moe_ffn_down_rows(const moe_desc* desc, const void* h, const int32_t*
                              moe_stream_t stream);
 
 /*
- * Weighted combine back to token order:
+ * Weighted combine back to token order: the routed output of a token is the
+ * sum of its selected experts' FFN outputs, each scaled by its normalised
+ * router weight (MoE-Prism, arXiv 2510.19366, §III-B2, training-free proxy
+ * gating: the routed output is the w_j-weighted sum of the executed experts'
+ * FFNs; PCoMoE, arXiv 2609.01024, Compositional Path Routing: the vanilla layer
+ * is the weighted expert summation), plus the always-on shared expert with
+ * weight 1 (§II-B: shared experts are outside the routed budget):
  *   out[t] = sum_{j < k_t} topk_w[tok_off[t]+j] * y_perm[inv_perm[tok_off[t]+j]]
  *            (+ y_shared[t] when y_shared != NULL)
  * summed in float32 in ascending j, rounded once to ELT.  A token with
- * k_t = 0 gets y_shared[t] (or 0).
- *   out  ELT [T][d] out
+ * k_t = 0 gets y_shared[t] (or 0).  An assignment whose inv_perm entry is
+ * negative (moe_permute writes -1 for an expert id outside [0, E)) adds
+ * nothing.
+ *   y_perm    ELT [T*k_max][d] in: expert outputs in permuted row order
+ *   y_shared  ELT [T][d] in, or NULL
+ *   tok_off, topk_w, inv_perm: as written by moe_route / moe_permute
+ *   out       ELT [T][d] out
+ * Errors: MOE_ERR_NULL, MOE_ERR_ALIGN (y_perm, y_shared, out), MOE_ERR_LAUNCH.
  */
 moe_status moe_combine(const moe_desc* desc, const void* y_perm, const void* y_shared,
                        const int32_t* tok_off, const float* topk_w, const int32_t* inv_perm,
                        void* out, moe_stream_t stream);
 
 /*
- * The whole layer: route, permute, FFN (+ shared expert) and combine.
+ * The whole layer: route, permute, FFN (+ shared expert) and combine.  Per
+ * token t with budget k_t (MoE-Prism §III-C1: the request carries its own
+ * routing budget, counted in routed experts, §II-B), the output is the
+ * renormalised-softmax-weighted sum over the k_t highest-logit experts of the
+ * SwiGLU expert FFN (§III-B1, Eq. (1): A = SiLU(X W_gate) * (X W_up), output
+ * A W_down), plus the shared expert's output; the steps are those of
+ * moe_route, moe_permute, moe_ffn and moe_combine above.
+ *   x, w_router, router_bias, k: as in moe_route
+ *   w_gate, w_up, w_down, ws_gate, ws_up, ws_down: as in moe_ffn
  *   out        ELT [T][d] out
  *   stats      int32 [E+2] out, or NULL: expert_counts[E], n_active, A
  *   dev_status int32 [1] out, or NULL: as in moe_route
@@ -476,6 +502,20 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router
                        const void* w_up, const void* w_down, const void* ws_gate,
                        const void* ws_up, const void* ws_down, void* out, int32_t* stats,
                        int32_t* dev_status, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Streaming-read probe (measurement only, not a step of the layer): reads
+ * `bytes` bytes of device memory at src once with 16-byte loads, carrying
+ * the non-temporal hint when `nontemporal` is non-zero, as a plain kernel
+ * that does nothing else; timing it gives the HBM read rate this part
+ * reaches, the practical ceiling of a weight stream.
+ *   src   device, 16-byte aligned; bytes rounded down to a multiple of 16
+ *   sink  device int32 [1]; written only in the practically impossible case
+ *         that the folded data equal a fixed constant (it keeps the loads)
+ * Errors: MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_LAUNCH.
+ */
+moe_status moe_probe_read(const void* src, size_t bytes, int32_t nontemporal, int32_t* sink,
+                          moe_stream_t stream);
 
 /* Static description of a status code.  Never NULL. */
 const char* moe_status_str(moe_status status);

@@ -25,7 +25,7 @@ __all__ = [
     "moe_proxy_pack", "moe_path_table", "moe_path_route", "moe_path_sources", "moe_path_rows", "moe_ffn_down_rows",
     "PathLayer",
     "moe_proxy_route", "moe_forward",
-    "forward", "proxy_width", "proxy_pack", "ProxyRouter",
+    "forward", "proxy_width", "proxy_pack", "ProxyRouter", "probe_read",
     "library_path",
 ]
 
@@ -72,12 +72,50 @@ def pack_weights(w: torch.Tensor, stream=None) -> torch.Tensor:
     N, K = w.shape[-2], w.shape[-1]
     out = torch.empty_like(w)
     _check("moe_pack_weights", _lib.load().moe_pack_weights(
-        _DTYPES[w.dtype], G, N, K, _ptr(w), _ptr(out), _stream(stream)))
+        _DTYPES[w.dtype], G, N, K, _dev(w, "w"), _dev(out, "out"), _stream(stream)))
     return out
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Address of a host tensor (the host-side arguments of moe_path_table and
+    moe_proxy_kappa_balanced)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("host argument must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_ELT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
+
+
+def _elt(desc: moe_desc) -> torch.dtype:
+    return _ELT[desc.dtype]
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype: Optional[torch.dtype] = None, numel: Optional[int] = None):
+    """Address of a device argument, after checking what the C ABI cannot:
+    a contiguous tensor on a GPU, of the element type the call reads, holding
+    at least `numel` elements.  (An int64 budget vector passed as int32, for
+    instance, would otherwise be read as pairs of 32-bit halves.)"""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {numel} needed")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_I32, _F32 = torch.int32, torch.float32
+
+
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -116,41 +154,54 @@ def _nbytes(t: Optional[torch.Tensor]) -> int:
 
 def moe_route(desc, x, w_router, router_bias, k, tok_off, topk_ids, topk_w, dev_status, ws,
               stream=None) -> None:
+    T, d, E, el = desc.T, desc.d, desc.E, _elt(desc)
     _check("moe_route", _lib.load().moe_route(
-        ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(k), _ptr(tok_off),
-        _ptr(topk_ids), _ptr(topk_w), _ptr(dev_status), _ptr(ws), _nbytes(ws), _stream(stream)))
+        ctypes.byref(desc), _dev(x, "x", el, T * d), _dev(w_router, "w_router", el, E * d),
+        _dev(router_bias, "router_bias", _F32, E), _dev(k, "k", _I32, T), _dev(tok_off, "tok_off", _I32, T + 1),
+        _dev(topk_ids, "topk_ids", _I32), _dev(topk_w, "topk_w", _F32), _dev(dev_status, "dev_status", _I32, 1),
+        _dev(ws, "ws"), _nbytes(ws), _stream(stream)))
 
 
 def moe_permute(desc, tok_off, topk_ids, expert_counts, expert_off, perm_tok, perm_src, inv_perm,
                 n_active, ws, stream=None) -> None:
+    T, E = desc.T, desc.E
     _check("moe_permute", _lib.load().moe_permute(
-        ctypes.byref(desc), _ptr(tok_off), _ptr(topk_ids), _ptr(expert_counts), _ptr(expert_off),
-        _ptr(perm_tok), _ptr(perm_src), _ptr(inv_perm), _ptr(n_active), _ptr(ws), _nbytes(ws),
-        _stream(stream)))
+        ctypes.byref(desc), _dev(tok_off, "tok_off", _I32, T + 1), _dev(topk_ids, "topk_ids", _I32),
+        _dev(expert_counts, "expert_counts", _I32, E), _dev(expert_off, "expert_off", _I32, E + 1),
+        _dev(perm_tok, "perm_tok", _I32), _dev(perm_src, "perm_src", _I32), _dev(inv_perm, "inv_perm", _I32),
+        _dev(n_active, "n_active", _I32, 1), _dev(ws, "ws"), _nbytes(ws), _stream(stream)))
 
 
 def moe_ffn(desc, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, expert_off, perm_tok, y_perm,
             y_shared, ws, stream=None) -> None:
+    T, d, E, I, Is, el = desc.T, desc.d, desc.E, desc.I, desc.I_shared, _elt(desc)
     _check("moe_ffn", _lib.load().moe_ffn(
-        ctypes.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(ws_gate),
-        _ptr(ws_up), _ptr(ws_down), _ptr(expert_off), _ptr(perm_tok), _ptr(y_perm), _ptr(y_shared),
-        _ptr(ws), _nbytes(ws), _stream(stream)))
+        ctypes.byref(desc), _dev(x, "x", el, T * d), _dev(w_gate, "w_gate", el, E * I * d),
+        _dev(w_up, "w_up", el, E * I * d), _dev(w_down, "w_down", el, E * d * I), _dev(ws_gate, "ws_gate", el, Is * d),
+        _dev(ws_up, "ws_up", el, Is * d), _dev(ws_down, "ws_down", el, d * Is), _dev(expert_off, "expert_off", _I32, E + 1),
+        _dev(perm_tok, "perm_tok", _I32), _dev(y_perm, "y_perm", el), _dev(y_shared, "y_shared", el, T * d),
+        _dev(ws, "ws"), _nbytes(ws), _stream(stream)))
 
 
 def moe_ffn_plan(desc, expert_off, ws, stream=None) -> None:
     _check("moe_ffn_plan", _lib.load().moe_ffn_plan(
-        ctypes.byref(desc), _ptr(expert_off), _ptr(ws), _nbytes(ws), _stream(stream)))
+        ctypes.byref(desc), _dev(expert_off, "expert_off", _I32, desc.E + 1), _dev(ws, "ws"), _nbytes(ws),
+        _stream(stream)))
 
 
 def moe_ffn_gateup(desc, x, w_gate, w_up, expert_off, perm_tok, h, ws=None, stream=None) -> None:
+    T, d, E, I, el = desc.T, desc.d, desc.E, desc.I, _elt(desc)
     _check("moe_ffn_gateup", _lib.load().moe_ffn_gateup(
-        ctypes.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(expert_off), _ptr(perm_tok),
-        _ptr(h), _ptr(ws), _nbytes(ws), _stream(stream)))
+        ctypes.byref(desc), _dev(x, "x", el, T * d), _dev(w_gate, "w_gate", el, E * I * d),
+        _dev(w_up, "w_up", el, E * I * d), _dev(expert_off, "expert_off", _I32, E + 1),
+        _dev(perm_tok, "perm_tok", _I32), _dev(h, "h", el), _dev(ws, "ws"), _nbytes(ws), _stream(stream)))
 
 
 def moe_ffn_down(desc, h, w_down, expert_off, y_perm, ws=None, stream=None) -> None:
+    d, E, I, el = desc.d, desc.E, desc.I, _elt(desc)
     _check("moe_ffn_down", _lib.load().moe_ffn_down(
-        ctypes.byref(desc), _ptr(h), _ptr(w_down), _ptr(expert_off), _ptr(y_perm), _ptr(ws),
+        ctypes.byref(desc), _dev(h, "h", el), _dev(w_down, "w_down", el, E * d * I),
+        _dev(expert_off, "expert_off", _I32, E + 1), _dev(y_perm, "y_perm", el), _dev(ws, "ws"),
         _nbytes(ws), _stream(stream)))
 
 
@@ -162,9 +213,11 @@ def moe_fold(desc, mode: str, budget: int, S, L, H, tok_off, topk_ids, topk_w, e
     """mode "token" (at most `budget` routes per token) or "pool" (a pool of
     `budget` experts; expert_off / perm_src of moe_permute on the input routes)."""
     _check("moe_fold", _lib.load().moe_fold(
-        ctypes.byref(desc), _FOLD_MODES[mode], budget, _ptr(S), _ptr(L), _ptr(H), _ptr(tok_off),
-        _ptr(topk_ids), _ptr(topk_w), _ptr(expert_off), _ptr(perm_src), _ptr(tok_off_out), _ptr(ids_out),
-        _ptr(w_out), _ptr(pool_out), _ptr(ws), _nbytes(ws), _stream(stream)))
+        ctypes.byref(desc), _FOLD_MODES[mode], budget, _dev(S, "S", _F32), _dev(L, "L", _F32), _dev(H, "H", _F32),
+        _dev(tok_off, "tok_off", _I32, desc.T + 1), _dev(topk_ids, "topk_ids", _I32), _dev(topk_w, "topk_w", _F32),
+        _dev(expert_off, "expert_off", _I32), _dev(perm_src, "perm_src", _I32),
+        _dev(tok_off_out, "tok_off_out", _I32, desc.T + 1), _dev(ids_out, "ids_out", _I32), _dev(w_out, "w_out", _F32),
+        _dev(pool_out, "pool_out", _I32), _dev(ws, "ws"), _nbytes(ws), _stream(stream)))
 
 
 def moe_proxy_kappa_balanced(k_max: int, m: int, N: int) -> torch.Tensor:
@@ -177,30 +230,48 @@ def moe_proxy_kappa_balanced(k_max: int, m: int, N: int) -> torch.Tensor:
 
 def moe_proxy_pack(desc, N: int, r: int, gate_idx, w_gate, w_up, wp_gate, wp_up, stream=None) -> None:
     _check("moe_proxy_pack", _lib.load().moe_proxy_pack(
-        ctypes.byref(desc), N, r, _ptr(gate_idx), _ptr(w_gate), _ptr(w_up), _ptr(wp_gate), _ptr(wp_up),
+        ctypes.byref(desc), N, r, _dev(gate_idx, "gate_idx", _I32), _dev(w_gate, "w_gate", _elt(desc)),
+        _dev(w_up, "w_up", _elt(desc)), _dev(wp_gate, "wp_gate", _elt(desc)), _dev(wp_up, "wp_up", _elt(desc)),
         _stream(stream)))
 
 
 def moe_proxy_route(desc, N: int, r: int, m: int, k, kappa, base_tok_off, base_ids, base_w, base_inv_perm, hp,
                     tok_off, topk_ids, topk_w, dev_status, stream=None) -> None:
     _check("moe_proxy_route", _lib.load().moe_proxy_route(
-        ctypes.byref(desc), N, r, m, _ptr(k), _ptr(kappa), _ptr(base_tok_off), _ptr(base_ids), _ptr(base_w),
-        _ptr(base_inv_perm), _ptr(hp), _ptr(tok_off), _ptr(topk_ids), _ptr(topk_w), _ptr(dev_status),
+        ctypes.byref(desc), N, r, m, _dev(k, "k", _I32, desc.T), _dev(kappa, "kappa", _I32),
+        _dev(base_tok_off, "base_tok_off", _I32), _dev(base_ids, "base_ids", _I32), _dev(base_w, "base_w", _F32),
+        _dev(base_inv_perm, "base_inv_perm", _I32), _dev(hp, "hp", _elt(desc)), _dev(tok_off, "tok_off", _I32, desc.T + 1),
+        _dev(topk_ids, "topk_ids", _I32), _dev(topk_w, "topk_w", _F32), _dev(dev_status, "dev_status", _I32),
         _stream(stream)))
 
 
 def moe_combine(desc, y_perm, y_shared, tok_off, topk_w, inv_perm, out, stream=None) -> None:
+    T, d, el = desc.T, desc.d, _elt(desc)
     _check("moe_combine", _lib.load().moe_combine(
-        ctypes.byref(desc), _ptr(y_perm), _ptr(y_shared), _ptr(tok_off), _ptr(topk_w),
-        _ptr(inv_perm), _ptr(out), _stream(stream)))
+        ctypes.byref(desc), _dev(y_perm, "y_perm", el), _dev(y_shared, "y_shared", el, T * d),
+        _dev(tok_off, "tok_off", _I32, T + 1), _dev(topk_w, "topk_w", _F32), _dev(inv_perm, "inv_perm", _I32),
+        _dev(out, "out", el, T * d), _stream(stream)))
+
+
+def probe_read(src: torch.Tensor, sink: torch.Tensor, nontemporal: bool = False, stream=None) -> None:
+    """moe_probe_read over all of `src` (a contiguous device tensor; `sink`:
+    an int32 device tensor of one element): the streaming-read probe the
+    benchmark times as the practical HBM ceiling."""
+    _check("moe_probe_read", _lib.load().moe_probe_read(
+        _dev(src, "src"), src.numel() * src.element_size(), 1 if nontemporal else 0, _dev(sink, "sink", _I32, 1),
+        _stream(stream)))
 
 
 def moe_forward(desc, x, w_router, router_bias, k, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
                 out, stats, dev_status, ws, stream=None) -> None:
+    T, d, E, I, Is, el = desc.T, desc.d, desc.E, desc.I, desc.I_shared, _elt(desc)
     _check("moe_forward", _lib.load().moe_forward(
-        ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(k), _ptr(w_gate),
-        _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(out), _ptr(stats),
-        _ptr(dev_status), _ptr(ws), _nbytes(ws), _stream(stream)))
+        ctypes.byref(desc), _dev(x, "x", el, T * d), _dev(w_router, "w_router", el, E * d),
+        _dev(router_bias, "router_bias", _F32, E), _dev(k, "k", _I32, T), _dev(w_gate, "w_gate", el, E * I * d),
+        _dev(w_up, "w_up", el, E * I * d), _dev(w_down, "w_down", el, E * d * I), _dev(ws_gate, "ws_gate", el, Is * d),
+        _dev(ws_up, "ws_up", el, Is * d), _dev(ws_down, "ws_down", el, d * Is), _dev(out, "out", el, T * d),
+        _dev(stats, "stats", _I32, E + 2), _dev(dev_status, "dev_status", _I32, 1), _dev(ws, "ws"), _nbytes(ws),
+        _stream(stream)))
 
 
 def forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: Optional[torch.Tensor],
@@ -308,7 +379,7 @@ def moe_path_table(E: int, src, tgt, bias, device="cuda", stream=None) -> torch.
     t = torch.as_tensor(tgt, dtype=torch.int32).contiguous()
     b = torch.as_tensor(bias, dtype=torch.float32).contiguous()
     table = torch.empty(n.value, dtype=torch.uint8, device=device)
-    _check("moe_path_table", _lib.load().moe_path_table(E, P, _ptr(s), _ptr(t), _ptr(b), _ptr(table), n.value,
+    _check("moe_path_table", _lib.load().moe_path_table(E, P, _ptr(s), _ptr(t), _ptr(b), _dev(table, "table"), n.value,
                                                          _stream(stream)))
     return table
 
@@ -316,27 +387,35 @@ def moe_path_table(E: int, src, tgt, bias, device="cuda", stream=None) -> torch.
 def moe_path_route(desc, x, w_router, router_bias, w_tgt, lam: float, table, P: int, k, tok_off, path_src, path_tgt,
                    path_w, dev_status, ws, stream=None) -> None:
     _check("moe_path_route", _lib.load().moe_path_route(
-        ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_tgt), lam, _ptr(table), P, _ptr(k),
-        _ptr(tok_off), _ptr(path_src), _ptr(path_tgt), _ptr(path_w), _ptr(dev_status), _ptr(ws), _nbytes(ws),
+        ctypes.byref(desc), _dev(x, "x", _elt(desc)), _dev(w_router, "w_router", _elt(desc)),
+        _dev(router_bias, "router_bias", _F32), _dev(w_tgt, "w_tgt", _elt(desc)), lam, _dev(table, "table"), P,
+        _dev(k, "k", _I32, desc.T), _dev(tok_off, "tok_off", _I32, desc.T + 1), _dev(path_src, "path_src", _I32),
+        _dev(path_tgt, "path_tgt", _I32), _dev(path_w, "path_w", _F32), _dev(dev_status, "dev_status", _I32),
+        _dev(ws, "ws"), _nbytes(ws),
         _stream(stream)))
 
 
 def moe_path_sources(desc, tok_off, path_src, src_tok_off, src_ids, path_src_route, unit_off, ws,
                      stream=None) -> None:
     _check("moe_path_sources", _lib.load().moe_path_sources(
-        ctypes.byref(desc), _ptr(tok_off), _ptr(path_src), _ptr(src_tok_off), _ptr(src_ids), _ptr(path_src_route),
-        _ptr(unit_off), _ptr(ws), _nbytes(ws), _stream(stream)))
+        ctypes.byref(desc), _dev(tok_off, "tok_off", _I32), _dev(path_src, "path_src", _I32),
+        _dev(src_tok_off, "src_tok_off", _I32), _dev(src_ids, "src_ids", _I32),
+        _dev(path_src_route, "path_src_route", _I32), _dev(unit_off, "unit_off", _I32), _dev(ws, "ws"), _nbytes(ws),
+        _stream(stream)))
 
 
 def moe_path_rows(desc, tok_off, perm_path, path_src_route, src_inv_perm, row_map, stream=None) -> None:
     _check("moe_path_rows", _lib.load().moe_path_rows(
-        ctypes.byref(desc), _ptr(tok_off), _ptr(perm_path), _ptr(path_src_route), _ptr(src_inv_perm), _ptr(row_map),
+        ctypes.byref(desc), _dev(tok_off, "tok_off", _I32), _dev(perm_path, "perm_path", _I32),
+        _dev(path_src_route, "path_src_route", _I32), _dev(src_inv_perm, "src_inv_perm", _I32),
+        _dev(row_map, "row_map", _I32),
         _stream(stream)))
 
 
 def moe_ffn_down_rows(desc, h, row_map, w_down, expert_off, y_perm, ws, stream=None) -> None:
     _check("moe_ffn_down_rows", _lib.load().moe_ffn_down_rows(
-        ctypes.byref(desc), _ptr(h), _ptr(row_map), _ptr(w_down), _ptr(expert_off), _ptr(y_perm), _ptr(ws),
+        ctypes.byref(desc), _dev(h, "h", _elt(desc)), _dev(row_map, "row_map", _I32), _dev(w_down, "w_down", _elt(desc)),
+        _dev(expert_off, "expert_off", _I32), _dev(y_perm, "y_perm", _elt(desc)), _dev(ws, "ws"),
         _nbytes(ws), _stream(stream)))
 
 

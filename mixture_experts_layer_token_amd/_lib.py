@@ -60,6 +60,7 @@ SIGNATURES = {
                         c_ptr, c_ptr, c_ptr],
     "moe_forward": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
                     c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
+    "moe_probe_read": [c_ptr, c_size, c_i32, c_ptr, c_ptr],
     "moe_status_str": [c_i32],
 }
 

@@ -1,6 +1,9 @@
-// Weighted combine back to token order:
+// Weighted combine back to token order (MoE-Prism, arXiv 2510.19366, §III-B2:
+// the routed output is the router-weighted sum of the executed experts' FFNs;
+// shared experts add with weight 1, §II-B):
 //   out[t] = sum_{j < k_t} w[t, j] * Y[inv_perm[tok_off[t] + j]]  (+ Y_shared[t])
 // in float32, j ascending (deterministic), rounded once to the element type.
+// An assignment whose inv_perm entry is negative has no row and adds nothing.
 #include "common.h"
 #include "launch.h"
 
@@ -75,12 +78,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
         const int a = a0 + b * CB + j;
+        const int p = a < a1 ? inv_perm[a] : -1;  // -1: an assignment without a row
         // Y is read exactly once: non-temporal loads keep it from displacing
         // anything in the caches
         r[j] = zero_u4();
-        if (a < a1) {
+        if (p >= 0) {
           const u32x4_t v = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4_t*>(y + (size_t)inv_perm[a] * d + c * LE));
+              reinterpret_cast<const u32x4_t*>(y + (size_t)p * d + c * LE));
           r[j] = make_uint4(v[0], v[1], v[2], v[3]);
         }
       }
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
         const int a = a0 + b * CB + j;
-        if (a < a1) {
+        if (a < a1 && inv_perm[a] >= 0) {
           float f[LE];
           unpack_chunk<T>(r[j], f);
           const float w = wts[a];

@@ -74,8 +74,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // MODE 0: gate/up pair + SwiGLU epilogue.  MODE 1: down projection.
 // DEEP: 0 uniform ring, 1 activations one stage deeper, 2 weights one stage
-// deeper (STAGES = 2 only).
-template <int MODE, int BM, int BNW, int WM, int WN, int STAGES, int DEEP = 0>
+// deeper (STAGES = 2 only).  SEC: the launch carries the second, dense
+// problem (rows_s > 0); a separate instantiation, so that profiles list the
+// launches with the always-on expert's tiles apart from the routed-only ones.
+template <int MODE, int BM, int BNW, int WM, int WN, int STAGES, int DEEP = 0, bool SEC = false>
 __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     const bf16_t* __restrict__ in, const int32_t* __restrict__ row_map, const bf16_t* __restrict__ w0,
     const bf16_t* __restrict__ w1, const int4* __restrict__ blocks, int bound, int dense_rows,
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   // grouped one, so every XCD interleaves both. ----
   const int nN = N / BNW;
   const int r_mt = (blocks ? blocks[bound].x : (dense_rows + GBM - 1) / GBM) * SUB;
-  const int s_mt = ((rows_s + GBM - 1) / GBM) * SUB;
+  const int s_mt = SEC ? ((rows_s + GBM - 1) / GBM) * SUB : 0;
   const int mt_all = r_mt + s_mt;
   const int total = mt_all * nN;
   const int per = (total + 7) >> 3;
@@ -406,10 +408,16 @@ static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, co
   if (total == 0) return hipSuccess;
   const long long nwg = ((total + 7) / 8) * 8;
   if (nwg > 0x7fffffffLL / (64 * WM * WN)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, STAGES, DEEP>), dim3((unsigned)nwg), dim3(64 * WM * WN), 0,
-                     st, (const bf16_t*)in, row_map, (const bf16_t*)w0, (const bf16_t*)w1, blocks, bound, dense_rows,
-                     (bf16_t*)out, N, K, (const bf16_t*)sec.in, (const bf16_t*)sec.w0, (const bf16_t*)sec.w1,
-                     (bf16_t*)sec.out, sec.rows, blocked);
+  if (sec.rows > 0)
+    hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, STAGES, DEEP, true>), dim3((unsigned)nwg),
+                       dim3(64 * WM * WN), 0, st, (const bf16_t*)in, row_map, (const bf16_t*)w0, (const bf16_t*)w1,
+                       blocks, bound, dense_rows, (bf16_t*)out, N, K, (const bf16_t*)sec.in, (const bf16_t*)sec.w0,
+                       (const bf16_t*)sec.w1, (bf16_t*)sec.out, sec.rows, blocked);
+  else
+    hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, STAGES, DEEP, false>), dim3((unsigned)nwg),
+                       dim3(64 * WM * WN), 0, st, (const bf16_t*)in, row_map, (const bf16_t*)w0, (const bf16_t*)w1,
+                       blocks, bound, dense_rows, (bf16_t*)out, N, K, nullptr, nullptr, nullptr, nullptr, 0,
+                       blocked);
   return hipGetLastError();
 }
 

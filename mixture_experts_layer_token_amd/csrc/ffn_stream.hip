@@ -350,11 +350,16 @@ __device__ __forceinline__ void stream_block_shared(const T* __restrict__ in, co
 // VAR (shared-tile configurations only): bit 0 runs every block through the
 // shared-tile body (the direct body is then not compiled in, which also frees
 // its registers); bit 1 as in stream_block_shared.
-template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL, int OCC, int VAR = 0>
+// DENSE: one dense group of dense_rows rows (the always-on shared expert;
+// blocks is then NULL); a separate instantiation, so that profiles list
+// those launches apart from the routed ones.
+template <typename T, int MODE, int KC, int WN, int WK, int SMT, int TPW, int PD, bool IL, int OCC, int VAR = 0,
+          bool DENSE = false>
 __global__ __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void ffn_stream_kernel(
     const T* __restrict__ in, const int32_t* __restrict__ row_map, const T* __restrict__ w0,
     const T* __restrict__ w1, const int4* __restrict__ blocks, int dense_rows, T* __restrict__ out, int N, int K,
     int tiles, int blocked) {
+  if (DENSE) blocks = nullptr;
   static_assert(MODE == 1 || TPW % 2 == 0, "gate/up tiles come in pairs");
   static_assert(KC % (16 / sizeof(T)) == 0, "K step must be whole 16-byte loads");
   static_assert(WK % 2 == 0, "two row groups split the K waves in halves");
@@ -449,8 +454,12 @@ hipError_t launch_stream_variant(const T* in, const int32_t* row_map, const T* w
   const long long total = (long long)tiles * nblk;
   if (total == 0) return hipSuccess;
   if (total > 0x7fffffffLL / (64 * WN * WK)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((ffn_stream_kernel<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, OCC, VAR>), dim3((unsigned)total),
-                     dim3(64 * WN * WK), 0, st, in, row_map, w0, w1, blocks, dense_rows, out, N, K, tiles, blocked);
+  if (blocks)
+    hipLaunchKernelGGL((ffn_stream_kernel<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, OCC, VAR, false>), dim3((unsigned)total),
+                       dim3(64 * WN * WK), 0, st, in, row_map, w0, w1, blocks, dense_rows, out, N, K, tiles, blocked);
+  else
+    hipLaunchKernelGGL((ffn_stream_kernel<T, MODE, KC, WN, WK, SMT, TPW, PD, IL, OCC, VAR, true>), dim3((unsigned)total),
+                       dim3(64 * WN * WK), 0, st, in, row_map, w0, w1, blocks, dense_rows, out, N, K, tiles, blocked);
   return hipGetLastError();
 }
 

@@ -159,4 +159,8 @@ hipError_t launch_path_sources(const int32_t* tok_off, const int32_t* psrc, int 
 hipError_t launch_path_rows(const int32_t* tok_off, int T, int k_max, const int32_t* perm_path, const int32_t* p2s,
                             const int32_t* src_inv, int32_t* row_map, hipStream_t st);
 
+// probe.hip -- streaming-read probe (measurement only): reads `bytes` of src
+// once (16-byte loads, non-temporal if asked); sink receives at most 4 bytes.
+hipError_t launch_read_probe(const void* src, size_t bytes, int nontemporal, uint32_t* sink, hipStream_t st);
+
 }  // namespace moe

@@ -701,6 +701,13 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router
   return do_combine(d, fw.y, fw.y_sh, fw.tok_off, fw.w, fw.inv_perm, out, st);
 }
 
+moe_status moe_probe_read(const void* src, size_t bytes, int32_t nontemporal, int32_t* sink, moe_stream_t stream) {
+  if (bytes >= 16 && (!src || !sink)) return MOE_ERR_NULL;
+  if (!aligned16(src)) return MOE_ERR_ALIGN;
+  return launched(launch_read_probe(src, bytes, nontemporal, reinterpret_cast<uint32_t*>(sink),
+                                    static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_str(moe_status s) {
   switch (s) {
     case MOE_OK: return "ok";

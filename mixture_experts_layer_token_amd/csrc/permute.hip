@@ -254,7 +254,10 @@ __global__ __launch_bounds__(PERM_BLOCK) void expert_scatter_kernel(
     if (a0 + j >= a1) continue;
     const int a = a0 + j;
     const int e = ids[a];
-    if ((unsigned)e >= (unsigned)E) continue;  // not produced by moe_route; ignored
+    if ((unsigned)e >= (unsigned)E) {  // not produced by moe_route: no row, and the combine skips it
+      inv_perm[a] = -1;
+      continue;
+    }
     const int wi = tl >> 5;
     const int pos = wpre[e * MASK_WORDS + wi] + __popc(masks[e * MASK_WORDS + wi] & ((1u << (tl & 31)) - 1u));
     perm_tok[pos] = t;
@@ -270,7 +273,10 @@ __global__ __launch_bounds__(PERM_BLOCK) void expert_scatter_kernel(
     const uint32_t below = (1u << (tl & 31)) - 1u;
     for (int a = a0 + 64; a < a1; ++a) {
       const int e = ids[a];
-      if ((unsigned)e >= (unsigned)E) continue;
+      if ((unsigned)e >= (unsigned)E) {
+        inv_perm[a] = -1;
+        continue;
+      }
       const int pos = wpre[e * MASK_WORDS + wi] + __popc(masks[e * MASK_WORDS + wi] & below);
       perm_tok[pos] = t;
       perm_src[pos] = a;
@@ -346,7 +352,10 @@ __global__ __launch_bounds__(PERM_BLOCK) void permute_one_block_kernel(
   const int wi = tid >> 5;
   const uint32_t below = (1u << (tid & 31)) - 1u;
   for_token_ids(ids, tok_off[tid], tok_off[tid + 1], [&](int a, int e) {
-    if ((unsigned)e >= (unsigned)E) return;  // not produced by moe_route; ignored
+    if ((unsigned)e >= (unsigned)E) {  // not produced by moe_route: no row, and the combine skips it
+      inv_perm[a] = -1;
+      return;
+    }
     const uint32_t* m = masks + e * MASK_WORDS;
     int rank = __popc(m[wi] & below);
     for (int w = 0; w < wi; ++w) rank += __popc(m[w]);

@@ -132,7 +132,15 @@ __global__ __launch_bounds__(256) void proxy_select_kernel(
       for (int i = 0; i < r; ++i) s += fabsf(Elt<T>::to_f32(row[i]));
       s /= (float)r;
     } else {
-      kj = 0;  // a pick outside the whole experts runs nothing
+      // a pick outside the whole experts runs nothing: its kappa_j slots,
+      // already counted in the offsets, become holes (id -1, weight 0) that
+      // the permutation and the combine skip
+      if (n < kj) {
+        const int pos = tok_off[t] + before + n;
+        ids[pos] = -1;
+        wts[pos] = 0.f;
+      }
+      kj = 0;
     }
   }
   // rank among the N sub-experts of the same pick: larger score, then lower n

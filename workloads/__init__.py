@@ -55,6 +55,7 @@ __all__ = [
     "CONFIGS",
     "derived_seed",
     "make_layer",
+    "make_tokens",
     "make_custom_layer",
     "to_f64",
     "torch_dtype",
@@ -229,6 +230,16 @@ def zipf_bias(E: int, s: float) -> torch.Tensor:
     return torch.tensor([-s * math.log(e + 1) for e in range(E)], dtype=torch.float32)
 
 
+def make_tokens(cfg: LayerConfig, device="cpu"):
+    """The batch of ``cfg`` alone: hidden states x [T, d] and budgets k [T],
+    drawn exactly as :func:`make_layer` draws them.  Two configs that differ
+    only in T (the DeepSeek-V3-shaped decode and prefill batches) share their
+    weights, so a second batch can run over weights already drawn."""
+    device = torch.device(device)
+    x = _gauss((cfg.T, cfg.d), 1.0, derived_seed(cfg.seed, "x"), device, torch_dtype(cfg.dtype))
+    return x, draw_k(cfg).to(device)
+
+
 def make_layer(cfg: LayerConfig, device="cpu") -> Layer:
     """Draw the layer described by ``cfg`` directly on ``device``.
 
@@ -239,10 +250,9 @@ def make_layer(cfg: LayerConfig, device="cpu") -> Layer:
     dt = torch_dtype(cfg.dtype)
     T, d, E, I = cfg.T, cfg.d, cfg.E, cfg.I
     s = cfg.seed
-    x = _gauss((T, d), 1.0, derived_seed(s, "x"), device, dt)
+    x, k = make_tokens(cfg, device)
     w_router = _gauss((E, d), 1.0 / math.sqrt(d), derived_seed(s, "w_router"), device, dt)
     bias = zipf_bias(E, cfg.zipf_bias).to(device) if cfg.zipf_bias else None
-    k = draw_k(cfg).to(device)
 
     w_gate = torch.empty((E, I, d), dtype=dt, device=device)
     w_up = torch.empty((E, I, d), dtype=dt, device=device)
