@@ -67,7 +67,9 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = 3, /* unknown dtype / path / op */
   MOE_ERR_WORKSPACE = 4,   /* workspace missing or too small */
   MOE_ERR_ALIGN = 5,       /* a buffer is not 16-byte aligned (workspace: 256) */
-  MOE_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch */
+  MOE_ERR_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch */
+  MOE_ERR_SCRATCH = 7      /* moe_forward_noalloc: the layer needs more scratch than the
+                              library-held array holds (MOE_NOALLOC_SCRATCH_BYTES) */
 } moe_status;
 
 /* FFN execution path.  Both compute the same function. */
@@ -516,6 +518,32 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router
  */
 moe_status moe_probe_read(const void* src, size_t bytes, int32_t nontemporal, int32_t* sink,
                           moe_stream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP-graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_forward with its scratch in a library-held device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU instead of a caller workspace.  Same
+ * arguments, kernels and results as moe_forward, minus ws / ws_bytes; the
+ * caller still passes every input and output.  Calls nothing that allocates.
+ *   - The array is a static device variable: each GPU the library runs on
+ *     holds its own copy until the process ends.  Its address is looked up
+ *     on the first call on a device (with that device current).
+ *   - Layers whose forward needs more scratch than the array holds are
+ *     rejected with MOE_ERR_SCRATCH before anything is launched (the decode
+ *     shapes fit: about 30 MiB at most; large prefill batches do not).
+ *   - Every call on a GPU uses that GPU's one array: calls that overlap in
+ *     time on one GPU (two streams, two host threads) race and give wrong
+ *     results.  Nothing in the array needs clearing between calls (every
+ *     region is written before it is read).
+ * Errors: those of moe_forward (other than MOE_ERR_WORKSPACE), MOE_ERR_SCRATCH.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_desc* desc, const void* x, const void* w_router,
+                               const float* router_bias, const int32_t* k, const void* w_gate,
+                               const void* w_up, const void* w_down, const void* ws_gate,
+                               const void* ws_up, const void* ws_down, void* out, int32_t* stats,
+                               int32_t* dev_status, moe_stream_t stream);
 
 /* Static description of a status code.  Never NULL. */
 const char* moe_status_str(moe_status status);

@@ -24,7 +24,7 @@ __all__ = [
     "moe_ffn", "moe_ffn_plan", "moe_ffn_gateup", "moe_ffn_down", "moe_combine", "moe_fold", "moe_proxy_kappa_balanced",
     "moe_proxy_pack", "moe_path_table", "moe_path_route", "moe_path_sources", "moe_path_rows", "moe_ffn_down_rows",
     "PathLayer",
-    "moe_proxy_route", "moe_forward",
+    "moe_proxy_route", "moe_forward", "moe_forward_noalloc",
     "forward", "proxy_width", "proxy_pack", "ProxyRouter", "probe_read",
     "library_path",
 ]
@@ -272,6 +272,19 @@ def moe_forward(desc, x, w_router, router_bias, k, w_gate, w_up, w_down, ws_gate
         _dev(ws_up, "ws_up", el, Is * d), _dev(ws_down, "ws_down", el, d * Is), _dev(out, "out", el, T * d),
         _dev(stats, "stats", _I32, E + 2), _dev(dev_status, "dev_status", _I32, 1), _dev(ws, "ws"), _nbytes(ws),
         _stream(stream)))
+
+
+def moe_forward_noalloc(desc, x, w_router, router_bias, k, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                        out, stats, dev_status, stream=None) -> None:
+    """moe_forward with the library-held scratch array (no workspace argument;
+    for callers that cannot allocate device memory)."""
+    T, d, E, I, Is, el = desc.T, desc.d, desc.E, desc.I, desc.I_shared, _elt(desc)
+    _check("moe_forward_noalloc", _lib.load().moe_forward_noalloc(
+        ctypes.byref(desc), _dev(x, "x", el, T * d), _dev(w_router, "w_router", el, E * d),
+        _dev(router_bias, "router_bias", _F32, E), _dev(k, "k", _I32, T), _dev(w_gate, "w_gate", el, E * I * d),
+        _dev(w_up, "w_up", el, E * I * d), _dev(w_down, "w_down", el, E * d * I), _dev(ws_gate, "ws_gate", el, Is * d),
+        _dev(ws_up, "ws_up", el, Is * d), _dev(ws_down, "ws_down", el, d * Is), _dev(out, "out", el, T * d),
+        _dev(stats, "stats", _I32, E + 2), _dev(dev_status, "dev_status", _I32, 1), _stream(stream)))
 
 
 def forward(x: torch.Tensor, w_router: torch.Tensor, router_bias: Optional[torch.Tensor],

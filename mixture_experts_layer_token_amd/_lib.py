@@ -18,9 +18,10 @@ MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_FORWARD, MOE_OP
 MOE_FOLD_TOKEN, MOE_FOLD_POOL = 0, 1
 MOE_DEV_BAD_K = 1
 MOE_W_ROWMAJOR, MOE_W_BLOCKED64 = 0, 1
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
-                4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_ALIGN", 6: "MOE_ERR_LAUNCH"}
+                4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_ALIGN", 6: "MOE_ERR_LAUNCH", 7: "MOE_ERR_SCRATCH"}
 
 
 class moe_desc(ctypes.Structure):
@@ -61,6 +62,8 @@ SIGNATURES = {
     "moe_forward": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
                     c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
     "moe_probe_read": [c_ptr, c_size, c_i32, c_ptr, c_ptr],
+    "moe_forward_noalloc": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
+                            c_ptr, c_ptr, c_ptr, c_ptr],
     "moe_status_str": [c_i32],
 }
 

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libmoe_mi355x.so")
 ARCH = "gfx950"
 
 SOURCES = ["route.hip", "route_screen.hip", "permute.hip", "fold.hip", "proxy.hip", "path.hip", "ffn_stream.hip",
-           "ffn_gemm.hip", "layout.hip", "combine.hip", "probe.hip", "moe_abi.cpp"]
+           "ffn_gemm.hip", "layout.hip", "combine.hip", "probe.hip", "noalloc.hip", "moe_abi.cpp"]
 
 # Packed fp32 instructions are switched off (-packed-fp32-ops); the host pass
 # warns that it does not know the feature, which is harmless.

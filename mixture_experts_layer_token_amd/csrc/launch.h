@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/moe.h"
+
 namespace moe {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
@@ -158,6 +160,19 @@ hipError_t launch_path_sources(const int32_t* tok_off, const int32_t* psrc, int 
                                hipStream_t st);
 hipError_t launch_path_rows(const int32_t* tok_off, int T, int k_max, const int32_t* perm_path, const int32_t* p2s,
                             const int32_t* src_inv, int32_t* row_map, hipStream_t st);
+
+// moe_abi.cpp -- the forward of moe_forward over a caller-chosen scratch
+// region.  own_regions: `ws` holds only the forward's own regions
+// (forward_scratch_bytes), as the no-allocation entry point supplies;
+// otherwise the moe_workspace_size(MOE_OP_FORWARD) rule applies.
+size_t forward_scratch_bytes(const moe_desc& d);
+// Descriptor and path valid, and the forward's own regions fit in `capacity`
+// bytes (else MOE_ERR_SCRATCH).
+moe_status forward_scratch_check(const moe_desc* desc, size_t capacity);
+moe_status forward_impl(const moe_desc* desc, const void* x, const void* w_router, const float* router_bias,
+                        const int32_t* k, const void* w_gate, const void* w_up, const void* w_down,
+                        const void* ws_gate, const void* ws_up, const void* ws_down, void* out, int32_t* stats,
+                        int32_t* dev_status, void* ws, size_t ws_bytes, moe_stream_t stream, bool own_regions);
 
 // probe.hip -- streaming-read probe (measurement only): reads `bytes` of src
 // once (16-byte loads, non-temporal if asked); sink receives at most 4 bytes.

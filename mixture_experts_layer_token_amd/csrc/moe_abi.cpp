@@ -669,6 +669,52 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router
                        const int32_t* k, const void* w_gate, const void* w_up, const void* w_down,
                        const void* ws_gate, const void* ws_up, const void* ws_down, void* out, int32_t* stats,
                        int32_t* dev_status, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  return moe::forward_impl(desc, x, w_router, router_bias, k, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, out,
+                           stats, dev_status, ws, ws_bytes, stream, false);
+}
+
+moe_status moe_probe_read(const void* src, size_t bytes, int32_t nontemporal, int32_t* sink, moe_stream_t stream) {
+  if (bytes >= 16 && (!src || !sink)) return MOE_ERR_NULL;
+  if (!aligned16(src)) return MOE_ERR_ALIGN;
+  return launched(launch_read_probe(src, bytes, nontemporal, reinterpret_cast<uint32_t*>(sink),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "descriptor values outside the supported range";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dtype, path or op";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_ALIGN: return "buffer not aligned (16 bytes; workspace 256 bytes)";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_SCRATCH: return "the layer needs more scratch than the library-held array holds";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"
+
+namespace moe {
+
+size_t forward_scratch_bytes(const moe_desc& d) {
+  Carver c(nullptr);
+  FwdWs w;
+  plan_forward(d, c, w);
+  return c.total();
+}
+
+moe_status forward_scratch_check(const moe_desc* desc, size_t capacity) {
+  MOE_TRY(check_desc(desc));
+  MOE_TRY(path_ok(*desc));
+  return forward_scratch_bytes(*desc) > capacity ? MOE_ERR_SCRATCH : MOE_OK;
+}
+
+moe_status forward_impl(const moe_desc* desc, const void* x, const void* w_router, const float* router_bias,
+                        const int32_t* k, const void* w_gate, const void* w_up, const void* w_down,
+                        const void* ws_gate, const void* ws_up, const void* ws_down, void* out, int32_t* stats,
+                        int32_t* dev_status, void* ws, size_t ws_bytes, moe_stream_t stream, bool own_regions) {
   MOE_TRY(check_desc(desc));
   const moe_desc& d = *desc;
   MOE_TRY(path_ok(d));
@@ -679,7 +725,14 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router
       !aligned16(out))
     return MOE_ERR_ALIGN;
   if (d.I_shared && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(ws_down))) return MOE_ERR_ALIGN;
-  MOE_TRY(check_ws(d, MOE_OP_FORWARD, ws, ws_bytes));
+  if (own_regions) {
+    // the forward's own regions only (the caller's array is not shared with the other ops)
+    if (!ws) return MOE_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_ALIGN;
+    if (forward_scratch_bytes(d) > ws_bytes) return MOE_ERR_SCRATCH;
+  } else {
+    MOE_TRY(check_ws(d, MOE_OP_FORWARD, ws, ws_bytes));
+  }
   Carver c(ws);
   FwdWs fw;
   plan_forward(d, c, fw);
@@ -701,24 +754,4 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const void* w_router
   return do_combine(d, fw.y, fw.y_sh, fw.tok_off, fw.w, fw.inv_perm, out, st);
 }
 
-moe_status moe_probe_read(const void* src, size_t bytes, int32_t nontemporal, int32_t* sink, moe_stream_t stream) {
-  if (bytes >= 16 && (!src || !sink)) return MOE_ERR_NULL;
-  if (!aligned16(src)) return MOE_ERR_ALIGN;
-  return launched(launch_read_probe(src, bytes, nontemporal, reinterpret_cast<uint32_t*>(sink),
-                                    static_cast<hipStream_t>(stream)));
-}
-
-const char* moe_status_str(moe_status s) {
-  switch (s) {
-    case MOE_OK: return "ok";
-    case MOE_ERR_NULL: return "a required pointer is NULL";
-    case MOE_ERR_SHAPE: return "descriptor values outside the supported range";
-    case MOE_ERR_UNSUPPORTED: return "unsupported dtype, path or op";
-    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
-    case MOE_ERR_ALIGN: return "buffer not aligned (16 bytes; workspace 256 bytes)";
-    case MOE_ERR_LAUNCH: return "kernel launch failed";
-  }
-  return "unknown status";
-}
-
-}  // extern "C"
+}  // namespace moe

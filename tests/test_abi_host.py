@@ -225,3 +225,17 @@ def test_pack_weights_validates_before_launch():
     assert lib.moe_pack_weights(bf, 1, 64, 128, P((1 << 20) + 8), b, None) == 5  # alignment
     assert lib.moe_pack_weights(bf, 2, 64, 128, a, P((1 << 20) + 64 * 128 * 2), None) == 2  # overlap
     assert lib.moe_pack_weights(bf, 0, 64, 128, None, None, None) == 0      # empty: nothing launched
+
+
+def test_noalloc_rejects_layers_beyond_its_scratch():
+    """moe_forward_noalloc checks the descriptor and the scratch size on the
+    host before touching the device: a layer whose forward needs more than the
+    library-held array is refused with MOE_ERR_SCRATCH, a bad descriptor with
+    the usual code."""
+    lib = _lib.load()
+    big = _desc(T=8192, d=2048, E=256, I=384, k_max=32)   # the sub-expert prefill batch: ~1.2 GB of scratch
+    assert lib.moe_forward_noalloc(ctypes.byref(big), *([None] * 14)) == 7
+    assert lib.moe_status_str(7) == b"the layer needs more scratch than the library-held array holds"
+    assert lib.moe_forward_noalloc(ctypes.byref(_desc(E=0)), *([None] * 14)) == 2
+    assert lib.moe_forward_noalloc(None, *([None] * 14)) == 1
+    assert _lib.MOE_NOALLOC_SCRATCH_BYTES == 64 << 20
