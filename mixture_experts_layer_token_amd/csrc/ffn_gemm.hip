@@ -38,16 +38,20 @@
 // first fragments of stage kt+1 are read during the last MFMAs of stage kt.
 // One barrier per stage; the DMA waits are explicit vmcnt counts.
 //
-// Ring depth per operand (DEEP).  The activation and weight parts of a stage
-// live in rings of their own (XS and WS buffers).  DEEP = 0: both STAGES
-// deep, the stage's x then w loads issued together.  DEEP = 2 (the 256-row
-// tiles): the weights get a third buffer (the 32 KB of LDS a two-stage ring
-// of 256-row tiles leaves free), so they run two stages ahead and the
-// gathered rows one: the loads go out
-// as D0 S0 D1 S1 D2, then after the barrier of stage kt S(kt+2) and D(kt+3)
-// (D = the deeper operand), and stage kt+1 only waits for everything but
-// D(kt+2).  Sub-expert-shaped layer, bit-identical outputs: down 400 -> 377
-// us, gate/up 475 -> 462 us (DEEP = 1, rows deeper, was slower: 385 / 501).
+// Ring depth per operand.  The activation and weight parts of a stage live
+// in rings of their own, XS and WS buffers deep.  The barrier of stage kt
+// (after the wait for stage kt+1) frees buffer kt of both rings and issues
+// x(kt+XS), then w(kt+WS); the prologue runs the same schedule for the
+// virtual barriers -max(XS, WS) .. -1.  So the weights run WS-1 stages ahead
+// and the gathered rows XS-1, and the wait for a stage counts exactly the
+// DMA instructions issued after its later operand.  The 256-row tiles take
+// XS = 2, WS = 3 (the 32 KB of LDS a two-stage ring leaves free holds a third
+// weight buffer): sub-expert-shaped layer, bit-identical outputs, down 400 ->
+// 377 us, gate/up 475 -> 462 us (rows deeper instead, XS = 3, WS = 2: 385 /
+// 501).  NTW = 1 puts the non-temporal hint on the grouped problem's weight
+// DMA (each routed expert's weights are read by one or two row tiles); the
+// second problem's weights (re-read by all its row tiles) keep ordinary
+// loads.
 //
 // Scheduling of tiles.  The rows of each expert are cut into row blocks of 256
 // listed in a row-block table built on the device from the per-expert counts;
@@ -73,11 +77,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 }  // namespace
 
 // MODE 0: gate/up pair + SwiGLU epilogue.  MODE 1: down projection.
-// DEEP: 0 uniform ring, 1 activations one stage deeper, 2 weights one stage
-// deeper (STAGES = 2 only).  SEC: the launch carries the second, dense
+// XS, WS: ring depths of the activation and weight tiles.  NTW: non-temporal
+// hint on the routed weights.  SEC: the launch carries the second, dense
 // problem (rows_s > 0); a separate instantiation, so that profiles list the
 // launches with the always-on expert's tiles apart from the routed-only ones.
-template <int MODE, int BM, int BNW, int WM, int WN, int STAGES, int DEEP = 0, bool SEC = false>
+template <int MODE, int BM, int BNW, int WM, int WN, int XS, int WS, int NTW = 0, bool SEC = false>
 __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     const bf16_t* __restrict__ in, const int32_t* __restrict__ row_map, const bf16_t* __restrict__ w0,
     const bf16_t* __restrict__ w1, const int4* __restrict__ blocks, int bound, int dense_rows,
@@ -86,21 +90,21 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   constexpr int NW = WM * WN;
   constexpr int NMAT = (MODE == 0) ? 2 : 1;
   constexpr int WROWS = NMAT * BNW;                          // weight rows per stage
-  constexpr int XBYTES = BM * 128, SBYTES = XBYTES + WROWS * 128;
+  constexpr int XBYTES = BM * 128;
   constexpr int XI = BM / 8 / NW, WI = WROWS / 8 / NW;        // DMA instructions per wave per stage
   constexpr int TMW = BM / WM / 32, TNW = BNW / WN / 32;      // 32x32 tiles per wave
   constexpr int SUB = GBM / BM;
   constexpr int KS = BK / 16;                                 // k16 steps per stage
   static_assert(XI * 8 * NW == BM && WI * 8 * NW == WROWS, "DMA split");
   static_assert(TMW >= 1 && TNW >= 1 && GBM % BM == 0, "tiling");
-  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(XS >= 2 && WS >= 2 && XS <= 4 && WS <= 4, "ring depths");
+  constexpr int MAXS = XS > WS ? XS : WS, MINS = XS < WS ? XS : WS;
   // The down projection's epilogue stages its output tile here as well (rows
   // of EPITCH bytes: 16 bytes of padding keep the rows 16-byte aligned and
   // spread the staging writes over the banks).
   constexpr int EPITCH = BNW * 2 + 16;
-  constexpr int XS = STAGES + (DEEP == 1 ? 1 : 0), WS = STAGES + (DEEP == 2 ? 1 : 0);
   constexpr int WBYTES = WROWS * 128, RING = XS * XBYTES + WS * WBYTES;
-  static_assert(DEEP == 0 || STAGES == 2, "one deeper operand over a two-stage ring");
+  static_assert(RING <= 160 * 1024, "LDS");
   constexpr int LDS_BYTES = (MODE == 1 && BM * EPITCH > RING) ? BM * EPITCH : RING;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
@@ -184,10 +188,9 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     wsrc[j] = wb + g * gstride + w_offset<bf16_t>(n0 + wr, c * 8, K, blocked);
   }
   const int kw = w_kstep<bf16_t>(blocked);  // weight elements per 64-wide stage of K (BK = 64 = EB)
-  int per_stage = WI;  // DMA instructions this wave issues per stage
+  int xcnt = 0;  // x DMA instructions this wave issues per stage
 #pragma unroll
-  for (int j = 0; j < XI; ++j) per_stage += xany[j] ? 1 : 0;
-  const int xcnt = per_stage - WI;  // x DMA instructions of this wave per stage
+  for (int j = 0; j < XI; ++j) xcnt += xany[j] ? 1 : 0;
   auto xbuf = [&](int kt) { return lds + (kt % XS) * XBYTES; };
   auto wbuf = [&](int kt) { return lds + XS * XBYTES + (kt % WS) * WBYTES; };
   auto issue_x = [&](int kt) {
@@ -198,17 +201,34 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
       if (xany[j] && xon[j])
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)(xsrc[j] + ko), (lds_ptr_t)(sb + (j * NW + wave) * 1024), 16, 0, 0);
   };
-  auto issue_w = [&](int kt) {
+  auto issue_w = [&](int kt, auto nt_c) {
+    constexpr int AUX = decltype(nt_c)::value ? 2 : 0;  // 2: non-temporal
     char* sb = wbuf(kt);
 #pragma unroll
     for (int j = 0; j < WI; ++j)
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[j] + kt * kw), (lds_ptr_t)(sb + (j * NW + wave) * 1024),
-                                       16, 0, 0);
+                                       16, 0, AUX);
   };
-  // deep / shallow operand of the DEEP ring
-  auto issue_d = [&](int kt) { if (DEEP == 1) issue_x(kt); else issue_w(kt); };
-  auto issue_s = [&](int kt) { if (DEEP == 1) issue_w(kt); else issue_x(kt); };
-  const int dcnt = DEEP == 1 ? xcnt : WI, scnt = DEEP == 1 ? WI : xcnt;
+  const int nk = K / BK;
+  auto on = [&](int t) { return t >= 0 && t < nk; };  // t is a stage of K
+  // barrier j: x(j + XS), then w(j + WS)
+  auto barrier_issue = [&](int j, auto nt_c) {
+    if (on(j + XS)) issue_x(j + XS);
+    if (on(j + WS)) issue_w(j + WS, nt_c);
+  };
+  // DMA instructions this wave issued after the later of x(s) and w(s), once
+  // the barriers up to s - 2 have issued theirs
+  auto after = [&](int s) {
+    const int bx = s - XS, bw = s - WS, L = bx > bw ? bx : bw;
+    int n = (bx > bw && on(L + WS)) ? WI : 0;  // the same barrier's w, issued after x(s)
+#pragma unroll
+    for (int q = 1; q <= MINS - 2; ++q) {      // barriers L + 1 .. s - 2
+      const int j = L + q;
+      n += (on(j + XS) ? xcnt : 0) + (on(j + WS) ? WI : 0);
+    }
+    return n;
+  };
+  constexpr int WAITMAX = (MAXS * (XI + WI) < 63) ? MAXS * (XI + WI) : 63;
 
   f32x16_t acc[NMAT * TNW][TMW];
 #pragma unroll
@@ -221,14 +241,13 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   // ---- fragments: lane l supplies tile row (l % 32) and K chunk 2s + l/32 of
   // k16 step s (A = weights, B = activations) ----
   const int l32 = lane & 31, lh = lane >> 5;
-  const int nk = K / BK;
   // Row tiles of this wave that hold rows of the block (wave-uniform): the
   // MFMAs and fragment reads of the empty 32-row tiles of a partly filled
   // block are skipped (LIVE = 0: the wave only loads and synchronises).
   const int wrows = rows - m0 - wm * (BM / WM);
   const int live = wrows <= 0 ? 0 : min(TMW, (wrows + 31) / 32);
 
-  auto main_loop = [&](auto live_c) {
+  auto main_loop = [&](auto live_c, auto nt_c) {
     constexpr int LIVE = decltype(live_c)::value;
     u32x4_t fw[2][NMAT * TNW], fx[2][TMW > 0 ? TMW : 1];
     auto load_frags = [&](int buf, int s, int slot) {
@@ -268,19 +287,11 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
       if constexpr (NFRAG > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NFRAG - NPAIR, 0);
     };
 
-    if constexpr (DEEP == 0) {
 #pragma unroll
-      for (int s = 0; s < STAGES; ++s)
-        if (s < nk) { issue_x(s); issue_w(s); }
-      // stage 0 landed: the stages issued after it may still be in flight
-      vm_wait_dyn<(STAGES - 1) * (XI + WI)>((min(nk, STAGES) - 1) * per_stage);
-    } else {
-      // D0 S0 D1 S1 D2; stage 0 needs D0 and S0
-      issue_d(0); issue_s(0);
-      if (1 < nk) { issue_d(1); issue_s(1); }
-      if (2 < nk) issue_d(2);
-      vm_wait_dyn<2 * (XI + WI)>((1 < nk ? dcnt + scnt : 0) + (2 < nk ? dcnt : 0));
-    }
+    for (int j = -MAXS; j < 0; ++j) barrier_issue(j, nt_c);
+    // stage 0 landed; what barrier -1 and the ones before it issued after it
+    // may still be in flight
+    vm_wait_dyn<WAITMAX>(after(0) + (on(XS - 1) ? xcnt : 0) + (on(WS - 1) ? WI : 0));
     compiler_fence();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
@@ -297,23 +308,12 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
           // is refilled.  On the last stage nothing is waited for and the reads
           // below touch a buffer whose values are never used, which keeps the
           // step branch-free so its reads interleave with its MFMAs.
-          if constexpr (DEEP == 0) {
-            const int later = max(0, min(nk - 1, kt + STAGES - 1) - (kt + 1));
-            vm_wait_dyn<(STAGES - 2) * (XI + WI)>(later * per_stage);
-          } else {
-            // D(kt+1) and S(kt+1) landed; only D(kt+2) may still be in flight
-            vm_wait_dyn<(XI > WI ? XI : WI)>(kt + 2 < nk ? dcnt : 0);
-          }
+          vm_wait_dyn<WAITMAX>(kt + 1 < nk ? after(kt + 1) : 0);
           lgkm_wait0();
           compiler_fence();
           __builtin_amdgcn_s_barrier();
           compiler_fence();
-          if constexpr (DEEP == 0) {
-            if (kt + STAGES < nk) { issue_x(kt + STAGES); issue_w(kt + STAGES); }
-          } else {
-            if (kt + 2 < nk) issue_s(kt + 2);
-            if (kt + 3 < nk) issue_d(kt + 3);
-          }
+          barrier_issue(kt, nt_c);
           load_frags(kt + 1, 0, 0);
         }
         mma(s & 1);
@@ -321,16 +321,19 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
       }
     }
   };
-  auto dispatch = [&](auto self, auto c) {
+  auto dispatch = [&](auto self, auto c, auto nt_c) {
     constexpr int L = decltype(c)::value;
     if constexpr (L == 0) {
-      main_loop(c);
+      main_loop(c, nt_c);
     } else {
-      if (live >= L) main_loop(c);
-      else self(self, std::integral_constant<int, L - 1>{});
+      if (live >= L) main_loop(c, nt_c);
+      else self(self, std::integral_constant<int, L - 1>{}, nt_c);
     }
   };
-  dispatch(dispatch, std::integral_constant<int, TMW>{});
+  if (NTW && !second)
+    dispatch(dispatch, std::integral_constant<int, TMW>{}, std::integral_constant<bool, NTW != 0>{});
+  else
+    dispatch(dispatch, std::integral_constant<int, TMW>{}, std::false_type{});
 
   // ---- epilogue: element e of acc[q][i] is D[n = 8*(e/4) + 4*lh + e%4][m = l32]
   // of the 32x32 tile (n: weight row, m: tile row) ----
@@ -398,7 +401,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
 
 int gemm_row_block() { return GBM; }
 
-template <int MODE, int BM, int BNW, int WM, int WN, int STAGES, int DEEP = 0>
+template <int MODE, int BM, int BNW, int WM, int WN, int XS, int WS, int NTW = 0>
 static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, const void* w0, const void* w1,
                                       const int4* blocks, int bound, int dense_rows, void* out, int N, int K,
                                       int blocked, hipStream_t st, const GemmSecond& sec = GemmSecond{}) {
@@ -409,12 +412,12 @@ static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, co
   const long long nwg = ((total + 7) / 8) * 8;
   if (nwg > 0x7fffffffLL / (64 * WM * WN)) return hipErrorInvalidValue;
   if (sec.rows > 0)
-    hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, STAGES, DEEP, true>), dim3((unsigned)nwg),
+    hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, XS, WS, NTW, true>), dim3((unsigned)nwg),
                        dim3(64 * WM * WN), 0, st, (const bf16_t*)in, row_map, (const bf16_t*)w0, (const bf16_t*)w1,
                        blocks, bound, dense_rows, (bf16_t*)out, N, K, (const bf16_t*)sec.in, (const bf16_t*)sec.w0,
                        (const bf16_t*)sec.w1, (bf16_t*)sec.out, sec.rows, blocked);
   else
-    hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, STAGES, DEEP, false>), dim3((unsigned)nwg),
+    hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, XS, WS, NTW, false>), dim3((unsigned)nwg),
                        dim3(64 * WM * WN), 0, st, (const bf16_t*)in, row_map, (const bf16_t*)w0, (const bf16_t*)w1,
                        blocks, bound, dense_rows, (bf16_t*)out, N, K, nullptr, nullptr, nullptr, nullptr, 0,
                        blocked);
@@ -429,9 +432,10 @@ hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const 
                                   const int4* blocks, int bound, int dense_rows, int rows_hint, void* h, int N,
                                   int K, int blocked, hipStream_t st, const GemmSecond& sec) {
   if (rows_hint >= GBM)
-    return launch_gemm_variant<0, 256, 128, 4, 2, 2, 2>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, blocked, st,
-                                                      sec);
-  return launch_gemm_variant<0, 128, 128, 2, 4, 3>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, blocked, st, sec);
+    return launch_gemm_variant<0, 256, 128, 4, 2, 2, 3>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K,
+                                                        blocked, st, sec);
+  return launch_gemm_variant<0, 128, 128, 2, 4, 3, 3>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, blocked,
+                                                      st, sec);
 }
 
 hipError_t launch_ffn_down_gemm(const void* h, const int32_t* row_map, const void* wd, const int4* blocks, int bound,
@@ -439,14 +443,16 @@ hipError_t launch_ffn_down_gemm(const void* h, const int32_t* row_map, const voi
                                 const GemmSecond& sec) {
   if (rows_hint >= GBM) {
     if (N % 256 == 0)
-      return launch_gemm_variant<1, 256, 256, 4, 2, 2, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked,
-                                                         st, sec);
-    return launch_gemm_variant<1, 256, 128, 4, 2, 2, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked, st,
-                                                       sec);
+      return launch_gemm_variant<1, 256, 256, 4, 2, 2, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K,
+                                                          blocked, st, sec);
+    return launch_gemm_variant<1, 256, 128, 4, 2, 2, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked,
+                                                        st, sec);
   }
   if (N % 256 == 0)
-    return launch_gemm_variant<1, 128, 256, 2, 2, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked, st, sec);
-  return launch_gemm_variant<1, 128, 128, 2, 2, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked, st, sec);
+    return launch_gemm_variant<1, 128, 256, 2, 2, 3, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked,
+                                                        st, sec);
+  return launch_gemm_variant<1, 128, 128, 2, 2, 3, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked,
+                                                      st, sec);
 }
 
 }  // namespace moe

@@ -76,7 +76,6 @@ __all__ = [
     "silu",
     "swiglu_expert",
     "forward",
-    "activated_weight_bytes",
 ]
 
 
@@ -592,10 +591,3 @@ def path_forward(x, tok_off, src, tgt, w, w_gate, w_up, w_down, tokens: Optional
         counter["U"] = n_u
         counter["D"] = n_d
     return out
-
-
-def activated_weight_bytes(n_active: int, d: int, I: int, elem_bytes: int) -> int:
-    """Routed-expert weight bytes a batch must load: gate, up and down of every
-    activated expert (METRO reading notes, Q1: decode runtime follows these
-    loads; activations are a small fraction of the traffic)."""
-    return 3 * n_active * d * I * elem_bytes

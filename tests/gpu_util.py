@@ -125,3 +125,40 @@ def sample_tokens(T: int, n: int) -> np.ndarray:
     if T <= n:
         return np.arange(T)
     return np.unique(np.linspace(0, T - 1, n).round().astype(np.int64))
+
+
+def covering_tokens(got: dict, T: int, block: int = 64, shared: bool = False) -> np.ndarray:
+    """Tokens whose outputs, taken together, touch every (expert, block of
+    `block` permuted rows) at least once -- the row tiles of both FFN paths
+    are unions of such blocks (64, 128 or 256 rows), so a fault confined to
+    one row tile shows in some checked output row -- and, with `shared`, every
+    `block`-token range of the always-on expert's rows.  Plus the first and
+    the last token.  `got` is run_stages' host copy of the routing."""
+    eoff, ptok = got["expert_off"], got["perm_tok"]
+    chosen = {0, T - 1} if T > 0 else set()
+    for e in range(len(eoff) - 1):
+        for p0 in range(int(eoff[e]), int(eoff[e + 1]), block):
+            chosen.add(int(ptok[p0]))
+    if shared:
+        chosen.update(range(0, T, block))
+    return np.array(sorted(chosen), dtype=np.int64)
+
+
+def compare_rows(a: torch.Tensor, b: torch.Tensor, dtype: str) -> dict:
+    """Every row of two device outputs of the same layer against each other,
+    to the output tolerance (rel. L2 over the whole output; max abs)."""
+    a64, b64 = a.double(), b.double()
+    diff = (a64 - b64)
+    nref = float(torch.linalg.vector_norm(b64))
+    rel = float(torch.linalg.vector_norm(diff)) / nref if nref > 0 else float(torch.linalg.vector_norm(diff))
+    mx = float(diff.abs().max()) if diff.numel() else 0.0
+    # per row as well: a fault confined to a few rows would vanish in the global norm
+    rn = torch.linalg.vector_norm(diff, dim=1) / torch.linalg.vector_norm(b64, dim=1).clamp_min(1e-30)
+    worst = float(rn.max()) if rn.numel() else 0.0
+    tol = TOL[dtype]
+    assert rel <= tol["rel_l2"], f"relative L2 error {rel:.3e} > {tol['rel_l2']}"
+    assert worst <= 4 * tol["rel_l2"], f"worst row relative L2 error {worst:.3e}"
+    if tol["max_abs"] is not None:
+        assert mx <= tol["max_abs"], f"max abs error {mx:.3e} > {tol['max_abs']}"
+    return dict(rel_l2=rel, worst_row=worst, max_abs=mx)
+

@@ -14,17 +14,20 @@ import pytest
 import torch
 
 import mixture_experts_layer_token_amd as moe
-from tests.gpu_util import (check_routing, compare_out, oracle_out, oracle_routing, run_forward,
-                            run_stages, sample_tokens)
+from tests.gpu_util import (check_routing, compare_out, compare_rows, covering_tokens, oracle_out,
+                            oracle_routing, run_forward, run_stages, sample_tokens)
 import oracle
 from tests.gpu_util import desc_of
 from workloads import CONFIGS, ExpertView, make_custom_layer, make_layer, to_f64
 
 pytestmark = pytest.mark.gpu
 
-# output rows checked against the oracle per workload (all rows when fewer)
-SAMPLE = {"tiny_fp32": 16, "mixtral_decode": 64, "qwen3_30b_a3b_decode": 64,
-          "subexpert_prefill": 24, "dsv3_decode": 10, "dsv3_prefill": 8}
+# Output rows checked against the oracle per workload: all rows of the
+# smaller batches; on the prefill batches a covering set, one token for every
+# (expert, 64-row block) of the permutation and every 64-token block of the
+# shared expert (covering_tokens), plus a spread sample.
+SAMPLE = {"tiny_fp32": 16, "mixtral_decode": 64, "qwen3_30b_a3b_decode": 256,
+          "subexpert_prefill": 24, "dsv3_decode": 128, "dsv3_prefill": 8}
 
 
 def _say(msg):
@@ -54,8 +57,29 @@ def test_workload_parity(name):
     np.testing.assert_array_equal(stats[:cfg.E], p["counts"])
     assert stats[cfg.E] == p["n_active"] and stats[cfg.E + 1] == got["A"]
     tokens = sample_tokens(cfg.T, SAMPLE[name])
+    if cfg.T > SAMPLE[name]:
+        tokens = np.union1d(tokens, covering_tokens(got, cfg.T, 64, shared=cfg.I_shared > 0))
+    _say(f"[parity] {name}: oracle on {len(tokens)} of {cfg.T} tokens")
     err = compare_out(fout, oracle_out(layer, tokens), cfg.dtype, tokens)
     _say(f"[parity] {name}: A={got['A']} n_active={p['n_active']} {err}")
+
+
+@pytest.mark.parametrize("name", [n for n, c in CONFIGS.items() if c.dtype == "bf16"])
+def test_workload_paths_agree_on_every_row(name):
+    """The two FFN implementations (weight-streaming kernels, grouped GEMM),
+    which share no kernel code, agree on every output row of the full-size
+    batch to the output tolerance: a fault in any one row tile, column tile or
+    shared-expert tile of either path would show here, while the oracle checks
+    the covering rows above."""
+    cfg = CONFIGS[name]
+    _say(f"[paths-all-rows] {name}: drawing layer")
+    layer = make_layer(cfg, "cuda")
+    a, sa, st_a = run_forward(layer, path="stream")
+    b, sb, st_b = run_forward(layer, path="gemm")
+    assert st_a == st_b == 0
+    np.testing.assert_array_equal(sa, sb)
+    err = compare_rows(a, b, cfg.dtype)
+    _say(f"[paths-all-rows] {name}: {err}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -253,7 +277,8 @@ def test_workload_other_path(name, path):
     layer = make_layer(cfg, "cuda")
     fout, stats, status = run_forward(layer, path=path)
     assert status == 0
-    tokens = sample_tokens(cfg.T, 16)
+    got = run_stages(layer, path=path)
+    tokens = np.union1d(sample_tokens(cfg.T, 16), covering_tokens(got, cfg.T, 64, shared=cfg.I_shared > 0))
     compare_out(fout, oracle_out(layer, tokens), cfg.dtype, tokens)
 
 

@@ -6,8 +6,10 @@ route must carry its pick's weight.  The chosen sub-experts are compared as
 sets per pick: where the GPU's set differs from the oracle's, the differing
 sub-experts must be a near tie under the oracle's float64 proxy scores (the
 GPU scores float32 means of ELT activations), and the sets must agree on
-nearly every pick.  Layer outputs are compared with the oracle's forward on
-its own routes over the sampled tokens whose selections agree.
+nearly every pick.  Layer outputs are compared on every sampled token with
+the oracle's forward on the GPU's own routes (which the selection check has
+just validated), and on the sampled tokens whose selections agree with the
+oracle's forward on its own routes.
 """
 import gc
 import sys
@@ -181,7 +183,12 @@ def test_proxy_routes_and_layer(dtype, N, r, m, E):
                                      tokens=tokens)
     err = compare_out(out, want_out, dtype, tokens)
     assert not out[7].any() and not out[11].any()
-    _say(f"[proxy] {dtype} N={N} r={r} m={m}: routes {A}, picks {picks}, differ {differ}, {err}")
+    # every sampled token, on the routes the GPU chose
+    every = np.asarray(list(sample_tokens(cfg.T, 40)) + [7, 11])
+    want_gpu = oracle.forward_routes(to_f64(layer.x), got_to, got_ids, got_w, ExpertView(layer.w_gate),
+                                     ExpertView(layer.w_up), ExpertView(layer.w_down), tokens=every)
+    err_all = compare_out(out, want_gpu, dtype, every)
+    _say(f"[proxy] {dtype} N={N} r={r} m={m}: routes {A}, picks {picks}, differ {differ}, {err}, all {err_all}")
 
 
 def test_proxy_full_budget_reconstructs_whole_experts():
@@ -242,7 +249,11 @@ def test_proxy_full_size_sampled():
     want = oracle.forward_routes(x64[tokens], ref["tok_off"], ref["ids"], ref["w"], ExpertView(layer.w_gate),
                                  ExpertView(layer.w_up), ExpertView(layer.w_down), tokens=rows)
     err = compare_out(out, want, cfg.dtype, tokens[rows])
-    _say(f"[proxy] subexpert_prefill r={r}: routes {A}, sampled picks {picks}, differ {differ}, {err}")
+    # every sampled token, on the routes the GPU chose
+    want_gpu = oracle.forward_routes(x64, got_to, got_ids, got_w, ExpertView(layer.w_gate), ExpertView(layer.w_up),
+                                     ExpertView(layer.w_down), tokens=tokens)
+    err_all = compare_out(out, want_gpu, cfg.dtype, tokens)
+    _say(f"[proxy] subexpert_prefill r={r}: routes {A}, sampled picks {picks}, differ {differ}, {err}, all {err_all}")
 
 
 def test_proxy_bad_kappa_rows_and_graph_replay():

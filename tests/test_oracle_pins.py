@@ -326,10 +326,6 @@ def test_zero_input_ties_to_lowest_index():
     assert not out.any()
 
 
-def test_activated_weight_bytes():
-    assert oracle.activated_weight_bytes(8, 4096, 14336, 2) == 3 * 8 * 4096 * 14336 * 2
-
-
 # ---------------------------------------------------------------- executed budgets
 
 def _smallest_multiple_at_least(k: int, n: int) -> int:
