@@ -486,16 +486,19 @@ int stream_row_block() { return S_ROWS; }
 // long K (>= 8192: 165 -> 139 us); a short-K down projection (K <= 1024)
 // gains from the shared body alone (37 -> 32 us); others keep the mix.
 // With blocked weights every tile step is one contiguous 2 KB run, and the
-// shared body with the hint wins everywhere except the short-K down
-// projection, which keeps the shared body without it (Mixtral-shaped gate/up
-// 331 -> 295 us, DSV3-shaped down 1116 -> 1029 us, Qwen3-shaped gate/up
-// 76 -> 73 us; the Qwen3-shaped down loses the hint: 32.5 vs 40 us); a
-// down projection of mid-size K (DSV3-shaped, K = 2048) gains from a ring one
-// stage deeper (1030 -> 1014 us), which the others do not (Mixtral-shaped
-// down 141 vs 143 us, gate/up 292 vs 350 us: two workgroups per CU instead
-// of three).
+// shared body with the hint wins everywhere (Mixtral-shaped gate/up 331 ->
+// 295 us, DSV3-shaped down 1116 -> 1029 us, Qwen3-shaped gate/up 76 -> 73
+// us).  Timed with a 1 GiB cache-evicting write before every launch (as in a
+// model, where the other layers' weights pass through the 256 MB last-level
+// cache between two calls of one layer), the short-K down projection keeps
+// the hint too: Qwen3-shaped, K = 768, 79 us without it, 47 us with it (warm,
+// without the write, its weights stay in that cache and the plain loads win:
+// 36 vs 43 us).  A down projection of mid-size K (DSV3-shaped, K = 2048)
+// gains from a ring one stage deeper (1049 -> 1031 us), which the others do
+// not (Mixtral-shaped down 152 vs 154 us, Qwen3-shaped down 47 vs 49 us,
+// gate/up 305 vs 333 us: two workgroups per CU instead of three).
 static int stream_var(int MODE, int N, int K, int blocked) {
-  if (blocked) return MODE == 0 ? 3 : (K <= 1024 ? 1 : (K < 8192 ? 7 : 3));
+  if (blocked) return MODE == 0 ? 3 : ((K > 1024 && K < 8192) ? 7 : 3);
   if (MODE == 0) return N >= 8192 ? 0 : 3;
   if (K >= 8192) return 3;
   return K <= 1024 ? 1 : 0;

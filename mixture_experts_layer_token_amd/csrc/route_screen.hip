@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256) void router_screen_select_kernel(
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // exact logits of the candidates
-  exact_dots<XC, XR, SEL_GRP>(
+  exact_dots<XC, XR, SEL_GRP, XR ? 4 : 2>(
       x + (size_t)t * d, d, ncand, [&](int c) { return w + (size_t)clist[c] * d; }, red,
       [&](int c, double v) { cval[c] = v; });
   // keys of the candidates (bias added in float64 before the one rounding)
@@ -231,6 +231,111 @@ __global__ __launch_bounds__(256) void router_screen_select_kernel(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   wave_topk_softmax<KPL>(key, kt, scale, ids + base, wts + base, area);
+}
+
+// ---- pass 2 for a wide hidden size: one workgroup of four waves per token.
+// Wave 0 takes the bounds and the candidate list as above; then every wave
+// takes a quarter of d, keeps that slice of the token row in registers
+// (widened to float64) and sums the candidates' exact partial dots over it
+// with DEPTH candidates' weight chunks in flight, so that the token row is
+// read once instead of once per candidate; wave 0 adds the four partials in
+// wave order (float64), adds the bias, rounds once and selects.  XCS:
+// 512-element chunks per wave slice (d / 4 <= 512 * XCS).
+template <int KPL, int XCS, int DEPTH>
+__global__ __launch_bounds__(256) void router_screen_select_wg_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const float* __restrict__ bias,
+    const float* __restrict__ approx, const float* __restrict__ absum, int S, const int32_t* __restrict__ tok_off,
+    int T, int d, int E, float scale, int32_t* __restrict__ ids, float* __restrict__ wts, int red_words) {
+  extern __shared__ uint64_t sel_lds[];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x;
+  // LDS: [4][red_words: lane shares of SEL_GRP candidates; wave 0's later the
+  // top-k scratch][4][E doubles: partial sums by candidate][E int32: candidate
+  // list][1 int32: candidate count]
+  double* const red = reinterpret_cast<double*>(sel_lds + (size_t)wv * red_words);
+  double* const part = reinterpret_cast<double*>(sel_lds + (size_t)4 * red_words);
+  int32_t* const clist = reinterpret_cast<int32_t*>(sel_lds + (size_t)4 * red_words + (size_t)4 * E);
+  int32_t* const ncand_l = clist + E;
+  const int base = tok_off[t];
+  const int kt = tok_off[t + 1] - base;
+
+  double cen[KPL], rad[KPL];
+  float bs[KPL];
+  int cidx[KPL];
+  if (wv == 0) {
+    const double rad_scale = (double)d * 0x1p-22;
+    uint32_t lkey[KPL];
+    const size_t sstride = (size_t)T * E;
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) {
+      const int e = lane + 64 * s;
+      cen[s] = 0.0;
+      rad[s] = 0.0;
+      lkey[s] = 0;
+      bs[s] = 0.f;
+      if (e < E) {
+        if (bias) bs[s] = bias[e];
+        float a = 0.f, m = 0.f;
+        const float* pa = approx + (size_t)t * E + e;
+        const float* pm = absum + (size_t)t * E + e;
+        for (int q0 = 0; q0 < S; q0 += 8) {
+          float va[8], vm[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            va[i] = (q0 + i < S) ? pa[(size_t)(q0 + i) * sstride] : 0.f;
+            vm[i] = (q0 + i < S) ? pm[(size_t)(q0 + i) * sstride] : 0.f;
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            a += va[i];
+            m += vm[i];
+          }
+        }
+        cen[s] = (double)a + (double)bs[s];
+        rad[s] = rad_scale * (double)m + 0x1p-126;
+        lkey[s] = logit_key(__double2float_rd(cen[s] - rad[s]));
+      }
+    }
+    int ncand = 0;
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) cidx[s] = -1;
+    if (kt > 0) {
+      const float L = key_logit(wave_kth_largest<KPL>(lkey, kt));
+      const double cut = (double)L - (fabs((double)L) * 0x1p-21 + 0x1p-126);
+      const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+      for (int s = 0; s < KPL; ++s) {
+        const int e = lane + 64 * s;
+        const bool cand = (e < E) && (cen[s] + rad[s] >= cut);
+        const uint64_t mask = __ballot(cand);
+        cidx[s] = cand ? ncand + __popcll(mask & below) : -1;
+        if (cand) clist[cidx[s]] = e;
+        ncand += __popcll(mask);
+      }
+    }
+    if (lane == 0) *ncand_l = ncand;
+  }
+  __syncthreads();
+  const int ncand = *ncand_l;
+  // this wave's slice of the exact dots
+  const int dq = d / 4, k0 = wv * dq;
+  double* const mine = part + (size_t)wv * E;
+  exact_dots<XCS, true, SEL_GRP, DEPTH>(
+      x + (size_t)t * d + k0, dq, ncand, [&](int c) { return w + (size_t)clist[c] * d + k0; }, red,
+      [&](int c, double v) { mine[c] = v; });
+  __syncthreads();
+  if (wv != 0 || kt == 0) return;
+  uint32_t key[KPL];
+#pragma unroll
+  for (int s = 0; s < KPL; ++s) {
+    key[s] = 0u;
+    if (cidx[s] >= 0) {
+      const int c = cidx[s];
+      const double v = ((part[c] + part[E + c]) + part[2 * E + c]) + part[3 * E + c];
+      key[s] = logit_key((float)(v + (double)bs[s]));
+    }
+  }
+  wave_topk_softmax<KPL>(key, kt, scale, ids + base, wts + base, sel_lds);
 }
 
 // Slices: enough workgroups (64 tokens x 256 experts each) to give every CU
@@ -270,6 +375,21 @@ hipError_t launch_router_screen(const void* x, const void* w, const float* bias,
                                 int32_t* tok_off, int32_t* status, int32_t* ids, float* wts, hipStream_t st) {
   hipError_t err = launch_router_screen_partials(x, w, k, T, d, E, k_max, pol, S, approx, absum, tok_off, status, st);
   if (err != hipSuccess || T == 0) return err;
+  if (d >= 4096 && d <= 8192) {
+    // wide rows: a workgroup per token, the row split over its four waves
+    const int red_words = max(SEL_GRP * 64, k_max + 1);
+    const size_t lds = ((size_t)4 * red_words + (size_t)4 * E) * sizeof(uint64_t) + ((size_t)E + 1) * sizeof(int32_t);
+#define MOE_SELW(KPL)                                                                                              \
+  hipLaunchKernelGGL((router_screen_select_wg_kernel<KPL, 4, 3>), dim3(T), dim3(256), lds, st, (const bf16_t*)x,     \
+                     (const bf16_t*)w, bias, approx, absum, S, tok_off, T, d, E, scale, ids, wts, red_words)
+    if (E <= 64) MOE_SELW(1);
+    else if (E <= 128) MOE_SELW(2);
+    else if (E <= 256) MOE_SELW(4);
+    else if (E <= 512) MOE_SELW(8);
+    else MOE_SELW(16);
+#undef MOE_SELW
+    return hipGetLastError();
+  }
   dim3 grid((T + 3) / 4);
   const int red_words = max(SEL_GRP * 64, k_max + 1);
   const int words = red_words + (E + 1) / 2 + E;

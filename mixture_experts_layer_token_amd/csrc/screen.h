@@ -41,12 +41,12 @@ constexpr int SEL_GRP = 8;  // rows whose cross-lane sums are done together
 
 // Exact dot products of the token row xrow with n rows (row_of(c), c < n),
 // under the routing contract: exact products, float64 accumulation.  Work
-// items (row c, pass p) in order, p fastest; the rows' chunks of item i+1 are
-// requested before item i is summed.  Each lane's share of a row goes to
-// red[c % GRP][lane] (GRP * 64 doubles of LDS); every GRP rows, lane j adds
-// the 64 shares of row j of the group in lane order and calls sink(c, sum).
-// One wave; ends with the wave's LDS writes visible.
-template <int XC, bool XR, int GRP, class RowOf, class Sink>
+// items (row c, pass p) in order, p fastest; the rows' chunks of items
+// i+1 .. i+DEPTH-1 are requested before item i is summed.  Each lane's share
+// of a row goes to red[c % GRP][lane] (GRP * 64 doubles of LDS); every GRP
+// rows, lane j adds the 64 shares of row j of the group in lane order and
+// calls sink(c, sum).  One wave; ends with the wave's LDS writes visible.
+template <int XC, bool XR, int GRP, int DEPTH = 2, class RowOf, class Sink>
 __device__ __forceinline__ void exact_dots(const bf16_t* __restrict__ xrow, int d, int n, RowOf row_of, double* red,
                                            Sink sink) {
   const int lane = threadIdx.x & 63;
@@ -105,13 +105,19 @@ __device__ __forceinline__ void exact_dots(const bf16_t* __restrict__ xrow, int 
       }
     }
   };
-  uint4 xa[XC], wa[XC], xb[XC], wb[XC];
-  if (items > 0) load_item(xa, wa, 0);
-  for (int it = 0; it < items; it += 2) {
-    if (it + 1 < items) load_item(xb, wb, it + 1);
-    finish_item(it, xa, wa);
-    if (it + 2 < items) load_item(xa, wa, it + 2);
-    if (it + 1 < items) finish_item(it + 1, xb, wb);
+  // a register ring of DEPTH items, indexed by compile-time positions
+  static_assert(DEPTH >= 2 && DEPTH <= 8, "pipeline depth");
+  uint4 xq[DEPTH][XC], wq[DEPTH][XC];
+#pragma unroll
+  for (int q = 0; q < DEPTH - 1; ++q)
+    if (q < items) load_item(xq[q], wq[q], q);
+  for (int it = 0; it < items; it += DEPTH) {
+#pragma unroll
+    for (int q = 0; q < DEPTH; ++q) {
+      const int i = it + q;
+      if (i + DEPTH - 1 < items) load_item(xq[(q + DEPTH - 1) % DEPTH], wq[(q + DEPTH - 1) % DEPTH], i + DEPTH - 1);
+      if (i < items) finish_item(i, xq[q], wq[q]);
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
