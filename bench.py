@@ -212,7 +212,7 @@ def read_ceiling(dev, stream):
     del buf
     torch.cuda.synchronize()
     return {"GBps": max(res.values()), "ordinary_GBps": res["ordinary"], "nontemporal_GBps": res["nontemporal"],
-            "bytes": nbytes, "kernel": "moe_probe_read (16-byte loads, 4 KB runs round-robin, 6 workgroups/CU)"}
+            "bytes": nbytes, "kernel": "moe_probe_read (16-byte loads, 4 KB runs round-robin, 2 workgroups/CU)"}
 
 
 class Bench:
