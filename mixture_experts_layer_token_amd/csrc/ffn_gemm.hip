@@ -18,7 +18,7 @@
 // while the current one is multiplied.  A wave holds (BM/WM) x (BNW/WN)
 // outputs per matrix as 32x32 tiles of v_mfma_f32_32x32x16_bf16 with the
 // weights as the A operand (a lane ends with 4 consecutive output columns of a
-// row: 8-byte stores).
+// row; the epilogue gathers the tile in LDS and stores whole lines).
 //
 // Weights are read row-major or in the blocked order (64-row x 128-byte
 // blocks, w_offset in common.h): a lane's DMA source is set once, and a stage
@@ -78,10 +78,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // MODE 0: gate/up pair + SwiGLU epilogue.  MODE 1: down projection.
 // XS, WS: ring depths of the activation and weight tiles.  NTW: non-temporal
-// hint on the routed weights.  SEC: the launch carries the second, dense
+// hint on the routed weights.  EPI: how the output tile is stored (0: from the
+// fragments, gate/up only; 1: staged in LDS; 2: staged, non-temporal).  SEC:
+// the launch carries the second, dense
 // problem (rows_s > 0); a separate instantiation, so that profiles list the
 // launches with the always-on expert's tiles apart from the routed-only ones.
-template <int MODE, int BM, int BNW, int WM, int WN, int XS, int WS, int NTW = 0, bool SEC = false>
+template <int MODE, int BM, int BNW, int WM, int WN, int XS, int WS, int NTW = 0, int EPI = 1, bool SEC = false>
 __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     const bf16_t* __restrict__ in, const int32_t* __restrict__ row_map, const bf16_t* __restrict__ w0,
     const bf16_t* __restrict__ w1, const int4* __restrict__ blocks, int bound, int dense_rows,
@@ -99,13 +101,13 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   static_assert(TMW >= 1 && TNW >= 1 && GBM % BM == 0, "tiling");
   static_assert(XS >= 2 && WS >= 2 && XS <= 4 && WS <= 4, "ring depths");
   constexpr int MAXS = XS > WS ? XS : WS, MINS = XS < WS ? XS : WS;
-  // The down projection's epilogue stages its output tile here as well (rows
-  // of EPITCH bytes: 16 bytes of padding keep the rows 16-byte aligned and
-  // spread the staging writes over the banks).
+  // The epilogue stages the output tile here as well (rows of EPITCH bytes:
+  // 16 bytes of padding keep the rows 16-byte aligned and spread the staging
+  // writes over the banks).
   constexpr int EPITCH = BNW * 2 + 16;
   constexpr int WBYTES = WROWS * 128, RING = XS * XBYTES + WS * WBYTES;
   static_assert(RING <= 160 * 1024, "LDS");
-  constexpr int LDS_BYTES = (MODE == 1 && BM * EPITCH > RING) ? BM * EPITCH : RING;
+  constexpr int LDS_BYTES = (EPI > 0 && BM * EPITCH > RING) ? BM * EPITCH : RING;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   // ---- which (row block, row tile, N tile) this workgroup owns.  Row tiles
@@ -336,53 +338,60 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     dispatch(dispatch, std::integral_constant<int, TMW>{}, std::false_type{});
 
   // ---- epilogue: element e of acc[q][i] is D[n = 8*(e/4) + 4*lh + e%4][m = l32]
-  // of the 32x32 tile (n: weight row, m: tile row) ----
-  if constexpr (MODE == 1) {
-    // The down projection writes d-wide rows: stored straight from the
-    // fragments, every 8-byte store touches 32 rows, and the store stream of a
-    // tile costs about a quarter of the kernel.  So the tile is staged in LDS
-    // (the ring is free now) and leaves row by row in 16-byte chunks, whole
-    // 128-byte lines per eight lanes.
-    vm_wait<0>();
-    lgkm_wait0();
-    compiler_fence();
-    __syncthreads();
-    compiler_fence();
+  // of the 32x32 tile (n: weight row, m: tile row).  A lane holds 4 adjacent
+  // columns of a row, so stores straight from the fragments are 8 bytes wide
+  // and each store instruction touches 32 rows, 16 bytes of each.
+  //   EPI 0: so stored (gate/up only).  Where each expert's weights are
+  //     re-read by several row tiles (the layer is compute-bound) this is the
+  //     fastest: 464 us against 480 us staged (256 experts x 437..588 rows,
+  //     d = 2048, I = 384).
+  //   EPI 1, 2: the tile (H, or the down projection's Y) is staged in LDS
+  //     (the ring is free now) and leaves row by row in 16-byte chunks, whole
+  //     128-byte lines per eight lanes; with EPI 2 as non-temporal stores.
+  //     The down projection's d-wide rows always take this path (stored from
+  //     the fragments its store stream cost about a quarter of the kernel).
+  //     Where the launch streams weights, ordinary stores of H (about 100 MB
+  //     against 15 GB of weights in a 256-expert, 7168-wide prefill) slowed
+  //     the weight stream of the whole gate/up launch by 7%, and by a fifth
+  //     with the MFMAs taken out; the next kernel reads H or Y once, in
+  //     another order, so those launches store non-temporally. ----
+  static_assert(EPI >= 0 && EPI <= 2 && (MODE == 0 || EPI > 0), "epilogue");
+  if constexpr (EPI == 0) {
 #pragma unroll
     for (int i = 0; i < TMW; ++i) {
-      const int r = wm * (BM / WM) + i * 32 + l32;
-      char* srow = lds + r * EPITCH + (wn * (BNW / WN) + 4 * lh) * 2;
+      const int m = m0 + wm * (BM / WM) + i * 32 + l32;
+      if (m >= rows) continue;
+      bf16_t* orow = out + (size_t)(row0 + m) * N + n0 + wn * (BNW / WN) + 4 * lh;
 #pragma unroll
       for (int tj = 0; tj < TNW; ++tj)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-          const f32x16_t& y = acc[tj][i];
-          const uint32_t o0 = (uint32_t)f32_to_bf16(y[4 * e4 + 0]) | ((uint32_t)f32_to_bf16(y[4 * e4 + 1]) << 16);
-          const uint32_t o1 = (uint32_t)f32_to_bf16(y[4 * e4 + 2]) | ((uint32_t)f32_to_bf16(y[4 * e4 + 3]) << 16);
-          *reinterpret_cast<uint2*>(srow + (tj * 32 + 8 * e4) * 2) = make_uint2(o0, o1);
+          const f32x16_t& gt = acc[tj][i];
+          const f32x16_t& up = acc[TNW + tj][i];
+          const uint32_t o0 = (uint32_t)f32_to_bf16(silu(gt[4 * e4 + 0]) * up[4 * e4 + 0]) |
+                              ((uint32_t)f32_to_bf16(silu(gt[4 * e4 + 1]) * up[4 * e4 + 1]) << 16);
+          const uint32_t o1 = (uint32_t)f32_to_bf16(silu(gt[4 * e4 + 2]) * up[4 * e4 + 2]) |
+                              ((uint32_t)f32_to_bf16(silu(gt[4 * e4 + 3]) * up[4 * e4 + 3]) << 16);
+          *reinterpret_cast<uint2*>(orow + tj * 32 + 8 * e4) = make_uint2(o0, o1);
         }
-    }
-    __syncthreads();
-    constexpr int CPR = BNW * 2 / 16;  // 16-byte chunks per row
-    const int live_rows = min(BM, rows - m0);
-    for (int q = tid; q < live_rows * CPR; q += 64 * NW) {
-      const int r = q / CPR, ch = q - r * CPR;
-      const uint4 v = *reinterpret_cast<const uint4*>(lds + r * EPITCH + ch * 16);
-      *reinterpret_cast<uint4*>(out + (size_t)(row0 + m0 + r) * N + n0 + ch * 8) = v;
     }
     return;
   }
+  vm_wait<0>();
+  lgkm_wait0();
+  compiler_fence();
+  __syncthreads();
+  compiler_fence();
 #pragma unroll
   for (int i = 0; i < TMW; ++i) {
-    const int m = m0 + wm * (BM / WM) + i * 32 + l32;
-    if (m >= rows) continue;
-    bf16_t* orow = out + (size_t)(row0 + m) * N + n0 + wn * (BNW / WN) + 4 * lh;
+    const int r = wm * (BM / WM) + i * 32 + l32;
+    char* srow = lds + r * EPITCH + (wn * (BNW / WN) + 4 * lh) * 2;
 #pragma unroll
     for (int tj = 0; tj < TNW; ++tj)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         uint32_t o0, o1;
-        if (MODE == 0) {
+        if constexpr (MODE == 0) {
           const f32x16_t& gt = acc[tj][i];
           const f32x16_t& up = acc[TNW + tj][i];
           o0 = (uint32_t)f32_to_bf16(silu(gt[4 * e4 + 0]) * up[4 * e4 + 0]) |
@@ -394,14 +403,24 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
           o0 = (uint32_t)f32_to_bf16(y[4 * e4 + 0]) | ((uint32_t)f32_to_bf16(y[4 * e4 + 1]) << 16);
           o1 = (uint32_t)f32_to_bf16(y[4 * e4 + 2]) | ((uint32_t)f32_to_bf16(y[4 * e4 + 3]) << 16);
         }
-        *reinterpret_cast<uint2*>(orow + tj * 32 + 8 * e4) = make_uint2(o0, o1);
+        *reinterpret_cast<uint2*>(srow + (tj * 32 + 8 * e4) * 2) = make_uint2(o0, o1);
       }
+  }
+  __syncthreads();
+  constexpr int CPR = BNW * 2 / 16;  // 16-byte chunks per row
+  const int live_rows = min(BM, rows - m0);
+  for (int q = tid; q < live_rows * CPR; q += 64 * NW) {
+    const int r = q / CPR, ch = q - r * CPR;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + r * EPITCH + ch * 16);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + m0 + r) * N + n0 + ch * 8);
+    if constexpr (EPI == 2) __builtin_nontemporal_store(v, dst);
+    else *dst = v;
   }
 }
 
 int gemm_row_block() { return GBM; }
 
-template <int MODE, int BM, int BNW, int WM, int WN, int XS, int WS, int NTW = 0>
+template <int MODE, int BM, int BNW, int WM, int WN, int XS, int WS, int NTW = 0, int EPI = 1>
 static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, const void* w0, const void* w1,
                                       const int4* blocks, int bound, int dense_rows, void* out, int N, int K,
                                       int blocked, hipStream_t st, const GemmSecond& sec = GemmSecond{}) {
@@ -412,12 +431,12 @@ static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, co
   const long long nwg = ((total + 7) / 8) * 8;
   if (nwg > 0x7fffffffLL / (64 * WM * WN)) return hipErrorInvalidValue;
   if (sec.rows > 0)
-    hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, XS, WS, NTW, true>), dim3((unsigned)nwg),
+    hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, XS, WS, NTW, EPI, true>), dim3((unsigned)nwg),
                        dim3(64 * WM * WN), 0, st, (const bf16_t*)in, row_map, (const bf16_t*)w0, (const bf16_t*)w1,
                        blocks, bound, dense_rows, (bf16_t*)out, N, K, (const bf16_t*)sec.in, (const bf16_t*)sec.w0,
                        (const bf16_t*)sec.w1, (bf16_t*)sec.out, sec.rows, blocked);
   else
-    hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, XS, WS, NTW, false>), dim3((unsigned)nwg),
+    hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, XS, WS, NTW, EPI, false>), dim3((unsigned)nwg),
                        dim3(64 * WM * WN), 0, st, (const bf16_t*)in, row_map, (const bf16_t*)w0, (const bf16_t*)w1,
                        blocks, bound, dense_rows, (bf16_t*)out, N, K, nullptr, nullptr, nullptr, nullptr, 0,
                        blocked);
@@ -427,15 +446,23 @@ static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, co
 // Tile height: 256-row tiles when groups hold hundreds of rows (fewer weight
 // re-reads per flop); 128-row tiles when they hold about a hundred, where a
 // 256-row tile would be mostly empty (there the layer streams weights, and the
-// 3-stage ring keeps more of them in flight).
+// 3-stage ring keeps more of them in flight).  Cache hints and epilogue as
+// measured with flushed caches.  The 128-row tiles stream weights: gate/up
+// with non-temporal weight DMA and output stores (2510 us against 2615 with
+// neither, 256 experts x 96 rows, d = 7168, I = 2048); down with
+// non-temporal stores alone (1486 us; 1520 with the weight hint as well, 1569
+// with neither).  The 256-row tiles re-read each expert's weights from the
+// cache and keep ordinary loads and stores (256 experts x 437..588 rows,
+// d = 2048, I = 384: gate/up 454 and down 373 us in the layer, 470 and 384
+// with both hints).
 hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
                                   const int4* blocks, int bound, int dense_rows, int rows_hint, void* h, int N,
                                   int K, int blocked, hipStream_t st, const GemmSecond& sec) {
   if (rows_hint >= GBM)
-    return launch_gemm_variant<0, 256, 128, 4, 2, 2, 3>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K,
-                                                        blocked, st, sec);
-  return launch_gemm_variant<0, 128, 128, 2, 4, 3, 3>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K, blocked,
-                                                      st, sec);
+    return launch_gemm_variant<0, 256, 128, 4, 2, 2, 3, 0, 0>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K,
+                                                              blocked, st, sec);
+  return launch_gemm_variant<0, 128, 128, 2, 4, 3, 3, 1, 2>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K,
+                                                            blocked, st, sec);
 }
 
 hipError_t launch_ffn_down_gemm(const void* h, const int32_t* row_map, const void* wd, const int4* blocks, int bound,
@@ -449,10 +476,10 @@ hipError_t launch_ffn_down_gemm(const void* h, const int32_t* row_map, const voi
                                                         st, sec);
   }
   if (N % 256 == 0)
-    return launch_gemm_variant<1, 128, 256, 2, 2, 3, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked,
-                                                        st, sec);
-  return launch_gemm_variant<1, 128, 128, 2, 2, 3, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked,
-                                                      st, sec);
+    return launch_gemm_variant<1, 128, 256, 2, 2, 3, 3, 0, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K,
+                                                              blocked, st, sec);
+  return launch_gemm_variant<1, 128, 128, 2, 2, 3, 3, 0, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K,
+                                                            blocked, st, sec);
 }
 
 }  // namespace moe

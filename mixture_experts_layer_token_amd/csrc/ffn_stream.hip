@@ -70,19 +70,29 @@ __device__ __forceinline__ void mma_tile<float>(f32x4_t& acc, const uint4& a, co
   acc = mfma_f32_4(__uint_as_float(a.w), __uint_as_float(b.w), acc);
 }
 
+// Four consecutive outputs of a row.  Non-temporal stores: the next kernel
+// reads H or Y once, and ordinary stores interleaved with the weight stream
+// slowed it (see the grouped GEMM's epilogue).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
 
 template <>
 __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
-  const uint32_t lo = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-  const uint32_t hi = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
-  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+  u32x2_t v;
+  v.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  v.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
 }
 
 template <>
 __device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  f32x4_t v;
+  v.x = a;
+  v.y = b;
+  v.z = c;
+  v.w = d;
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
 }
 
 // MODE 0: gate/up + SwiGLU.  MODE 1: down projection.
