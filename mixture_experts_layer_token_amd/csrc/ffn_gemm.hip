@@ -53,14 +53,19 @@
 // second problem's weights (re-read by all its row tiles) keep ordinary
 // loads.
 //
-// Scheduling of tiles.  The rows of each expert are cut into row blocks of 256
-// listed in a row-block table built on the device from the per-expert counts;
-// a row block is GBM/BM row tiles, each times the N tiles.  The grid is sized
-// by the table's bound, which depends only on the layer shape; each workgroup
-// reads the real block count and maps its id so that XCD x (ids x, x+8, ...)
-// takes one contiguous range of (row tile, N tile) pairs: the N tiles of a row
-// tile, then the next row tile of the same expert, which keeps an expert's
-// weights and gathered rows in that XCD's L2.
+// Scheduling of tiles.  The rows of each expert are cut into row blocks of BM
+// rows (the tile height) listed in a row-block table built on the device from
+// the per-expert counts; a row block is one row tile, times the N tiles.  The
+// grid is sized by the table's bound, which depends only on the layer shape;
+// each workgroup reads the real block count and maps its id so that XCD x
+// (ids x, x+8, ...) takes one contiguous range of (row tile, N tile) pairs:
+// the N tiles of a row tile, then the next row tile of the same expert, which
+// keeps an expert's weights and gathered rows in that XCD's L2.  (A persistent
+// variant, one workgroup per CU running its tiles on one continuous DMA
+// schedule with the epilogue overlapping the next tile's first stages, was
+// bit-identical but slower: gate/up 2545 against 2500 us, 256 experts x 96
+// rows, d = 7168, I = 2048; idle CUs between tiles do not cost bandwidth
+// while the others stream.)
 #include <type_traits>
 
 #include "common.h"
@@ -70,7 +75,6 @@ namespace moe {
 
 namespace {
 
-constexpr int GBM = 256;  // rows per row block of the tile table (a multiple of every BM used)
 constexpr int BK = 64;    // K elements per stage: one 128-byte LDS row per tile row
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -95,10 +99,9 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   constexpr int XBYTES = BM * 128;
   constexpr int XI = BM / 8 / NW, WI = WROWS / 8 / NW;        // DMA instructions per wave per stage
   constexpr int TMW = BM / WM / 32, TNW = BNW / WN / 32;      // 32x32 tiles per wave
-  constexpr int SUB = GBM / BM;
   constexpr int KS = BK / 16;                                 // k16 steps per stage
   static_assert(XI * 8 * NW == BM && WI * 8 * NW == WROWS, "DMA split");
-  static_assert(TMW >= 1 && TNW >= 1 && GBM % BM == 0, "tiling");
+  static_assert(TMW >= 1 && TNW >= 1, "tiling");
   static_assert(XS >= 2 && WS >= 2 && XS <= 4 && WS <= 4, "ring depths");
   constexpr int MAXS = XS > WS ? XS : WS, MINS = XS < WS ? XS : WS;
   // The epilogue stages the output tile here as well (rows of EPITCH bytes:
@@ -115,8 +118,8 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   // [0, rows_s) with weights w0s/w1s) are spread evenly through those of the
   // grouped one, so every XCD interleaves both. ----
   const int nN = N / BNW;
-  const int r_mt = (blocks ? blocks[bound].x : (dense_rows + GBM - 1) / GBM) * SUB;
-  const int s_mt = SEC ? ((rows_s + GBM - 1) / GBM) * SUB : 0;
+  const int r_mt = blocks ? blocks[bound].x : (dense_rows + BM - 1) / BM;
+  const int s_mt = SEC ? (rows_s + BM - 1) / BM : 0;
   const int mt_all = r_mt + s_mt;
   const int total = mt_all * nN;
   const int per = (total + 7) >> 3;
@@ -132,12 +135,12 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     second = hi > lo;
     mk = second ? lo : mtile - hi;
   }
-  const int rb = mk / SUB;
+  const int rb = mk;
   int g, row0, rows;  // group, first row and rows of the row block
   if (second) {
     g = 0;
-    row0 = rb * GBM;
-    rows = min(GBM, rows_s - row0);
+    row0 = rb * BM;
+    rows = min(BM, rows_s - row0);
     in = in_s;
     row_map = nullptr;
     w0 = w0s;
@@ -150,11 +153,9 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
     rows = b.z;
   } else {
     g = 0;
-    row0 = rb * GBM;
-    rows = min(GBM, dense_rows - row0);
+    row0 = rb * BM;
+    rows = min(BM, dense_rows - row0);
   }
-  const int m0 = (mk % SUB) * BM;  // first row of the tile within the row block
-  if (m0 >= rows) return;          // the block's rows end in an earlier sub-tile
   const int n0 = nt * BNW;         // first output column
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   for (int j = 0; j < XI; ++j) {
     const int r = 8 * (j * NW + wave) + (lane >> 3);
     const int c = (lane & 7) ^ lds_swz(r);
-    int m = m0 + r;
+    int m = r;
     xon[j] = m < rows;
     xany[j] = __builtin_amdgcn_ballot_w64(xon[j]) != 0;
     if (m >= rows) m = rows - 1;
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   // Row tiles of this wave that hold rows of the block (wave-uniform): the
   // MFMAs and fragment reads of the empty 32-row tiles of a partly filled
   // block are skipped (LIVE = 0: the wave only loads and synchronises).
-  const int wrows = rows - m0 - wm * (BM / WM);
+  const int wrows = rows - wm * (BM / WM);
   const int live = wrows <= 0 ? 0 : min(TMW, (wrows + 31) / 32);
 
   auto main_loop = [&](auto live_c, auto nt_c) {
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   if constexpr (EPI == 0) {
 #pragma unroll
     for (int i = 0; i < TMW; ++i) {
-      const int m = m0 + wm * (BM / WM) + i * 32 + l32;
+      const int m = wm * (BM / WM) + i * 32 + l32;
       if (m >= rows) continue;
       bf16_t* orow = out + (size_t)(row0 + m) * N + n0 + wn * (BNW / WN) + 4 * lh;
 #pragma unroll
@@ -408,25 +409,27 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   }
   __syncthreads();
   constexpr int CPR = BNW * 2 / 16;  // 16-byte chunks per row
-  const int live_rows = min(BM, rows - m0);
+  const int live_rows = min(BM, rows);
   for (int q = tid; q < live_rows * CPR; q += 64 * NW) {
     const int r = q / CPR, ch = q - r * CPR;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + r * EPITCH + ch * 16);
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + m0 + r) * N + n0 + ch * 8);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + r) * N + n0 + ch * 8);
     if constexpr (EPI == 2) __builtin_nontemporal_store(v, dst);
     else *dst = v;
   }
 }
 
-int gemm_row_block() { return GBM; }
+// Tile height of the configuration launch_ffn_*_gemm picks for rows_hint, which
+// is also the row-block height of the tile table.
+int gemm_row_block(int rows_hint) { return rows_hint >= 256 ? 256 : 128; }
 
 template <int MODE, int BM, int BNW, int WM, int WN, int XS, int WS, int NTW = 0, int EPI = 1>
 static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, const void* w0, const void* w1,
                                       const int4* blocks, int bound, int dense_rows, void* out, int N, int K,
                                       int blocked, hipStream_t st, const GemmSecond& sec = GemmSecond{}) {
   if (N % BNW != 0 || K % BK != 0) return hipErrorInvalidValue;
-  const int rb_bound = blocks ? bound : (dense_rows + GBM - 1) / GBM;
-  const long long total = ((long long)rb_bound + (sec.rows + GBM - 1) / GBM) * (GBM / BM) * (N / BNW);
+  const int rb_bound = blocks ? bound : (dense_rows + BM - 1) / BM;
+  const long long total = ((long long)rb_bound + (sec.rows + BM - 1) / BM) * (N / BNW);
   if (total == 0) return hipSuccess;
   const long long nwg = ((total + 7) / 8) * 8;
   if (nwg > 0x7fffffffLL / (64 * WM * WN)) return hipErrorInvalidValue;
@@ -445,21 +448,28 @@ static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, co
 
 // Tile height: 256-row tiles when groups hold hundreds of rows (fewer weight
 // re-reads per flop); 128-row tiles when they hold about a hundred, where a
-// 256-row tile would be mostly empty (there the layer streams weights, and the
-// 3-stage ring keeps more of them in flight).  Cache hints and epilogue as
-// measured with flushed caches.  The 128-row tiles stream weights: gate/up
-// with non-temporal weight DMA and output stores (2510 us against 2615 with
-// neither, 256 experts x 96 rows, d = 7168, I = 2048); down with
-// non-temporal stores alone (1486 us; 1520 with the weight hint as well, 1569
-// with neither).  The 256-row tiles re-read each expert's weights from the
-// cache and keep ordinary loads and stores (256 experts x 437..588 rows,
-// d = 2048, I = 384: gate/up 454 and down 373 us in the layer, 470 and 384
-// with both hints).
+// 256-row tile would be mostly empty (there the layer streams weights).
+// Measured with flushed caches (256 experts x 96 rows, d = 7168, I = 2048;
+// 256 experts x 437..588 rows, d = 2048, I = 384):
+//  - the 128-row tiles stream weights.  Gate/up: non-temporal weight DMA and
+//    output stores, and 256 columns per tile where I allows (2452 us; 2540
+//    with 128 columns and a 3-deep ring, 2650 with neither hint): each
+//    gathered activation stage then feeds twice the weights, and those
+//    activation loads were the costliest part of the launch (2313 us without
+//    them).  Down: non-temporal stores alone (1520 with the weight hint as
+//    well), 8 waves and 512 columns where d allows (1388 us; 1424 with 256
+//    columns, 1493 with 256 columns and 4 waves).
+//  - the 256-row tiles re-read each expert's weights from the cache and keep
+//    ordinary loads and stores (gate/up 454 and down 373 us in the layer, 470
+//    and 384 with both hints).
 hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
                                   const int4* blocks, int bound, int dense_rows, int rows_hint, void* h, int N,
                                   int K, int blocked, hipStream_t st, const GemmSecond& sec) {
-  if (rows_hint >= GBM)
+  if (gemm_row_block(rows_hint) == 256)
     return launch_gemm_variant<0, 256, 128, 4, 2, 2, 3, 0, 0>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K,
+                                                              blocked, st, sec);
+  if (N % 256 == 0)
+    return launch_gemm_variant<0, 128, 256, 2, 4, 2, 2, 1, 2>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K,
                                                               blocked, st, sec);
   return launch_gemm_variant<0, 128, 128, 2, 4, 3, 3, 1, 2>(in, row_map, wg, wu, blocks, bound, dense_rows, h, N, K,
                                                             blocked, st, sec);
@@ -468,15 +478,18 @@ hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const 
 hipError_t launch_ffn_down_gemm(const void* h, const int32_t* row_map, const void* wd, const int4* blocks, int bound,
                                 int dense_rows, int rows_hint, void* y, int N, int K, int blocked, hipStream_t st,
                                 const GemmSecond& sec) {
-  if (rows_hint >= GBM) {
+  if (gemm_row_block(rows_hint) == 256) {
     if (N % 256 == 0)
       return launch_gemm_variant<1, 256, 256, 4, 2, 2, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K,
                                                           blocked, st, sec);
     return launch_gemm_variant<1, 256, 128, 4, 2, 2, 3>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K, blocked,
                                                         st, sec);
   }
+  if (N % 512 == 0)
+    return launch_gemm_variant<1, 128, 512, 2, 4, 2, 2, 0, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K,
+                                                              blocked, st, sec);
   if (N % 256 == 0)
-    return launch_gemm_variant<1, 128, 256, 2, 2, 3, 3, 0, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K,
+    return launch_gemm_variant<1, 128, 256, 2, 4, 2, 3, 0, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K,
                                                               blocked, st, sec);
   return launch_gemm_variant<1, 128, 128, 2, 2, 3, 3, 0, 2>(h, row_map, wd, wd, blocks, bound, dense_rows, y, N, K,
                                                             blocked, st, sec);

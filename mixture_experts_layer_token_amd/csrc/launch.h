@@ -83,7 +83,7 @@ hipError_t launch_ffn_down_stream(int dtype, const void* h, const int32_t* row_m
                                   hipStream_t st);
 
 // ffn_gemm.hip -- grouped-GEMM FFN (bf16): same semantics as the streaming
-// kernels, over the row-block table with RB = gemm_row_block() (`bound`
+// kernels, over the row-block table with RB = gemm_row_block(rows_hint) (`bound`
 // entries + count; blocks == nullptr: one dense group of dense_rows rows).
 // rows_hint (an estimate of rows per group, from the shape only) picks the
 // tile height.  N must be a multiple of 128 and K of 64.
@@ -98,7 +98,7 @@ struct GemmSecond {
   void* out = nullptr;
   int rows = 0;
 };
-int gemm_row_block();
+int gemm_row_block(int rows_hint);
 hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
                                   const int4* blocks, int bound, int dense_rows, int rows_hint, void* h, int N,
                                   int K, int blocked, hipStream_t st, const GemmSecond& sec = GemmSecond{});

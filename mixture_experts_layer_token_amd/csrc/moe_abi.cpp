@@ -106,7 +106,8 @@ void plan_permute(const moe_desc& d, Carver& c, PermWs& w) {
 // Rows per entry of the routed FFN's row-block table: the GEMM's row block,
 // or the streaming kernel's rows per workgroup.
 bool routed_gemm(const moe_desc& d);
-int ffn_rb(const moe_desc& d) { return routed_gemm(d) ? gemm_row_block() : stream_row_block(); }
+int rows_hint(const moe_desc& d);
+int ffn_rb(const moe_desc& d) { return routed_gemm(d) ? gemm_row_block(rows_hint(d)) : stream_row_block(); }
 
 void plan_ffn(const moe_desc& d, Carver& c, FfnWs& w) {
   w.rb = ffn_rb(d);

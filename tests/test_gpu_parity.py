@@ -253,6 +253,8 @@ def test_graph_capture_replays_any_k():
     (40, 32, 384, 128, 4, 0),        # few rows per expert (GEMM tail-only tiles)
     (520, 8, 256, 256, 4, 256),      # shared expert as wide as the routed ones: fused into the GEMM launches
     (48, 4, 2176, 2176, 2, 2176),    # K % 256 = 128 (2 x 2 stream waves) and long K (deep stream pipeline)
+    (200, 16, 512, 256, 8, 256),     # 128-row GEMM tiles: 256-column gate/up, 512-column down, fused shared expert
+    (90, 8, 768, 512, 6, 0),         # 128-row GEMM tiles: 256-column gate/up and down (d % 512 != 0)
 ])
 def test_ffn_paths_bf16(path, T, E, d, I, kmax, Is):
     """Both FFN paths compute the same function on the same routing."""
