@@ -46,16 +46,27 @@ constexpr int SEL_GRP = 8;  // rows whose cross-lane sums are done together
 // of a row goes to red[c % GRP][lane] (GRP * 64 doubles of LDS); every GRP
 // rows, lane j adds the 64 shares of row j of the group in lane order and
 // calls sink(c, sum).  One wave; ends with the wave's LDS writes visible.
-template <int XC, bool XR, int GRP, int DEPTH = 2, class RowOf, class Sink>
+// XR: the token row stays in registers for all rows, widened to float64, or
+// with XB as its bf16 words (a quarter of the registers; dot8 then forms the
+// same exact products and adds them in the same order, so the sums are the
+// same bits).
+template <int XC, bool XR, int GRP, int DEPTH = 2, bool XB = false, class RowOf, class Sink>
 __device__ __forceinline__ void exact_dots(const bf16_t* __restrict__ xrow, int d, int n, RowOf row_of, double* red,
                                            Sink sink) {
   const int lane = threadIdx.x & 63;
   constexpr int PASS = 512 * XC;
   const int npass = (d + PASS - 1) / PASS;
   const int items = n * npass;
-  // resident token row (XR), widened to float64 once
-  double xd[XR ? XC : 1][8];
-  if constexpr (XR) {
+  // resident token row (XR): as bf16 words (XB) or widened to float64 once
+  uint4 xb[XR && XB ? XC : 1];
+  double xd[XR && !XB ? XC : 1][8];
+  if constexpr (XR && XB) {
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int off = 512 * i + 8 * lane;
+      xb[i] = off < d ? *reinterpret_cast<const uint4*>(xrow + off) : zero_u4();
+    }
+  } else if constexpr (XR) {
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
       const int off = 512 * i + 8 * lane;
@@ -82,7 +93,8 @@ __device__ __forceinline__ void exact_dots(const bf16_t* __restrict__ xrow, int 
   auto finish_item = [&](int it, const uint4 (&xv)[XC], const uint4 (&wr)[XC]) {
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
-      if constexpr (XR) dot8_wide(xd[i], wr[i], acc);
+      if constexpr (XR && XB) dot8(xb[i], wr[i], acc);
+      else if constexpr (XR) dot8_wide(xd[i], wr[i], acc);
       else dot8(xv[i], wr[i], acc);
     }
     const int c = it / npass;
