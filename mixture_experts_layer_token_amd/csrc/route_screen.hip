@@ -9,7 +9,7 @@
 // logits that cannot enter the top-k_t.
 //
 // Pass 1 (MFMA): a[t][e] = sum x_i w_i and s[t][e] = sum |x_i||w_i| in fp32 with
-// v_mfma_f32_16x16x32_bf16, K split over S slices (partial sums per slice, added
+// v_mfma_f32_32x32x16_bf16, K split over S slices (partial sums per slice, added
 // in slice order by pass 2).  Products of bf16 values are exact in fp32, so in
 // any summation order of depth n the error is at most n * u * S with
 // u = 2^-24 (2^-23 if the hardware truncates) and S <= s / (1 - n u); the
@@ -32,105 +32,161 @@
 
 namespace moe {
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
 // ---- pass 1: partial approximate logits and |x||w| sums of one K slice.
-// A workgroup covers 64 tokens x 256 experts: wave w takes experts
-// [64w, 64w + 64) of the span as a 4 x 4 grid of 16 x 16 MFMA tiles.  The four
-// waves read the same token rows (hits in the CU's L1 after the first), so the
-// bytes fetched per MFMA are a quarter of a one-tile-per-wave split.
-// One more slice index (z = S) holds the token-offset scan (pass 2 needs it)
-// in its first workgroup; its other workgroups exit at once.  Dispatched after
-// the tiles, the scan shares a CU with one of them instead of delaying one.
-__global__ __launch_bounds__(256) void router_screen_mfma_kernel(
+// A workgroup of 8 waves covers 64 tokens x 256 experts of one K slice.  K
+// advances 64 at a time through an LDS ring of STG stages (token rows 64 x
+// 128 B and router rows 256 x 128 B per stage, 40 KB) filled by global->LDS
+// DMA in whole 128-byte lines; wave w multiplies experts [32w, 32w + 32)
+// against the 64 tokens with v_mfma_f32_32x32x16_bf16 (value and |x||w|
+// sums), its fragments read from rows XOR-swizzled as in the grouped GEMM
+// (lds_off).  One more slice index (z = S) holds the token-offset scan (pass
+// 2 needs it) in its first workgroup; its other workgroups exit at once.
+// The kernel this replaced read the operands straight into registers, 64
+// bytes of each of 16 rows per load instruction, a pattern that moves
+// L2-resident data into a CU at about a third of the rate of whole lines:
+// 4,096 tokens x 256 experts, d = 7168, 73 -> 48 us.  Of the 48, ~12 us
+// store the 32 MB of partial sums, ~7 us are the scan workgroup waiting for
+// a CU after the tiles (run inside the first tile workgroup it cost more),
+// ~6 us launch and barriers.
+constexpr int SCR_NW = 8, SCR_TOK = 64, SCR_EXP = 256;
+constexpr int SCR_XB = SCR_TOK * 128, SCR_SB = SCR_XB + SCR_EXP * 128;  // bytes per stage: 8 KB + 32 KB
+
+template <int STG>
+__global__ __launch_bounds__(64 * SCR_NW) void router_screen_tile_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int T, int d, int E, float* __restrict__ approx,
     float* __restrict__ absum, const int32_t* __restrict__ k, int k_max, BudgetPolicy pol,
     int32_t* __restrict__ tok_off, int32_t* __restrict__ status) {
+  static_assert(STG >= 2 && STG * SCR_SB <= 160 * 1024, "LDS ring");
+  __shared__ __attribute__((aligned(1024))) char lds[STG * SCR_SB];
   if (blockIdx.z == gridDim.z - 1) {
     if (blockIdx.x == 0 && blockIdx.y == 0) {
-      __shared__ int32_t scan_part[257];
-      token_offsets_block<256>(k, T, k_max, pol, tok_off, status, scan_part, scan_part + 256);
+      int32_t* part = reinterpret_cast<int32_t*>(lds);
+      token_offsets_block<64 * SCR_NW>(k, T, k_max, pol, tok_off, status, part, part + SCR_NW);
     }
     return;
   }
   if (T == 0) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int t0 = blockIdx.x * 64;
-  const int e0 = blockIdx.y * 256 + wave * 64;
-  if (e0 >= E) return;
-  const int S = gridDim.z - 1, chunks = d / 32;
-  const int k_beg = (int)(((long long)blockIdx.z * chunks) / S) * 32;
-  const int k_end = (int)(((long long)(blockIdx.z + 1) * chunks) / S) * 32;
-  // operand rows (clamped in range; results of clamped rows are not stored)
-  const bf16_t* wr[4];
-  const bf16_t* xr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    wr[i] = w + (size_t)min(e0 + i * 16 + lr, E - 1) * d + lg * 8;
-    xr[i] = x + (size_t)min(t0 + i * 16 + lr, T - 1) * d + lg * 8;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int S = gridDim.z - 1, z = blockIdx.z;
+  const int t0 = blockIdx.x * SCR_TOK, e0 = blockIdx.y * SCR_EXP;
+  const int chunks = d / 64;
+  const int k_beg = (int)(((long long)z * chunks) / S) * 64;
+  const int k_end = (int)(((long long)(z + 1) * chunks) / S) * 64;
+  const int nk = (k_end - k_beg) / 64;
+
+  // DMA sources (rows clamped in range; results of clamped rows are not
+  // stored): x rows 8*wave .. +7, router rows 8*(j*8 + wave) .. +7
+  const int rsub = lane >> 3;
+  const bf16_t* xsrc;
+  {
+    const int r = 8 * wave + rsub;
+    const int c = (lane & 7) ^ lds_swz(r);
+    xsrc = x + (size_t)min(t0 + r, T - 1) * d + k_beg + c * 8;
   }
-  f32x4_t acc[4][4], aab[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      aab[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-  const u32x4_t sign_off = {0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
-  if (k_beg < k_end) {
-    u32x4_t a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = *reinterpret_cast<const u32x4_t*>(wr[i] + k_beg);
-      b[i] = *reinterpret_cast<const u32x4_t*>(xr[i] + k_beg);
-    }
-    for (int kk = k_beg; kk < k_end; kk += 32) {
-      const int kn = (kk + 32 < k_end) ? kk + 32 : kk;  // next step (the last re-reads, cached)
-      u32x4_t na[4], nb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        na[i] = *reinterpret_cast<const u32x4_t*>(wr[i] + kn);
-        nb[i] = *reinterpret_cast<const u32x4_t*>(xr[i] + kn);
-      }
-      u32x4_t aa[4], ab[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        aa[i] = a[i] & sign_off;
-        ab[i] = b[i] & sign_off;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[i][j] = Mfma<bf16_t>::step(a[i], b[j], acc[i][j]);
-          aab[i][j] = Mfma<bf16_t>::step(aa[i], ab[j], aab[i][j]);
-        }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = na[i];
-        b[i] = nb[i];
-      }
-    }
-  }
-  // lane holds D[e = 4*lg + r][t = lr] of each tile
-  float* const ap = approx + (size_t)blockIdx.z * T * E;
-  float* const sp = absum + (size_t)blockIdx.z * T * E;
+  const bf16_t* wsrc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int t = t0 + j * 16 + lr;
+    const int r = 8 * (j * SCR_NW + wave) + rsub;
+    const int c = (lane & 7) ^ lds_swz(r);
+    wsrc[j] = w + (size_t)min(e0 + r, E - 1) * d + k_beg + c * 8;
+  }
+  auto issue = [&](int st) {
+    char* sb = lds + (st % STG) * SCR_SB;
+    const int ko = st * 64;
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(xsrc + ko), (lds_ptr_t)(sb + wave * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wsrc[j] + ko), (lds_ptr_t)(sb + SCR_XB + (j * SCR_NW + wave) * 1024),
+                                       16, 0, 0);
+  };
+  constexpr int PER = 5;  // DMA instructions per wave per stage
+
+  f32x16_t acc[2], aab[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      acc[i][e] = 0.f;
+      aab[i][e] = 0.f;
+    }
+  const u32x4_t sign_off = {0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
+  // Schedule of the grouped GEMM: the fragments of k16 step s+1 are read
+  // during the MFMAs of step s; the barrier that hands over stage kt+1 sits
+  // before the last step of stage kt, after which stage kt's buffer (its last
+  // fragments are in registers) is refilled with stage kt + STG.
+  u32x4_t fw[2], fx[2][2];
+  auto load_frags = [&](int kt, int s, int slot) {
+    const char* sb = lds + (kt % STG) * SCR_SB;
+    fw[slot] = *reinterpret_cast<const u32x4_t*>(sb + SCR_XB + lds_off(32 * wave + l32, 2 * s + lh));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fx[slot][i] = *reinterpret_cast<const u32x4_t*>(sb + lds_off(32 * i + l32, 2 * s + lh));
+  };
+  auto mma = [&](int slot) {
+    const u32x4_t aw = fw[slot] & sign_off;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fw[slot]),
+                                                       __builtin_bit_cast(bf16x8_t, fx[slot][i]), acc[i], 0, 0, 0);
+      aab[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aw),
+                                                       __builtin_bit_cast(bf16x8_t, fx[slot][i] & sign_off), aab[i], 0,
+                                                       0, 0);
+    }
+  };
+  if (nk > 0) {
+#pragma unroll
+    for (int p = 0; p < STG; ++p)
+      if (p < nk) issue(p);
+    vm_wait_dyn<PER * (STG - 1)>(PER * min(STG - 1, nk - 1));  // stage 0 landed
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    load_frags(0, 0, 0);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s + 1 < 4) {
+        load_frags(kt, s + 1, (s + 1) & 1);
+      } else {
+        // stage kt+1 landed (stages up to kt + STG - 1 may be in flight) and
+        // this wave's reads of stage kt are complete; on the last stage the
+        // reads below touch a buffer whose values are never used
+        vm_wait_dyn<PER * (STG - 2)>(kt + 1 < nk ? PER * min(STG - 2, nk - 2 - kt) : 0);
+        lgkm_wait0();
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        if (kt + STG < nk) issue(kt + STG);
+        load_frags(kt + 1, 0, 0);
+      }
+      mma(s & 1);
+    }
+  }
+  // element e of acc[i] is D[n = 8*(e/4) + 4*lh + e%4][m = l32]: expert
+  // e0 + 32*wave + n, token t0 + 32*i + m
+  float* const ap = approx + (size_t)z * T * E;
+  float* const sp = absum + (size_t)z * T * E;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = t0 + 32 * i + l32;
     if (t >= T) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = e0 + i * 16 + 4 * lg;
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int e = e0 + 32 * wave + 8 * e4 + 4 * lh;
       if ((E & 3) == 0 && e + 3 < E) {
-        *reinterpret_cast<float4*>(ap + (size_t)t * E + e) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        *reinterpret_cast<float4*>(sp + (size_t)t * E + e) = make_float4(aab[i][j][0], aab[i][j][1], aab[i][j][2], aab[i][j][3]);
+        *reinterpret_cast<float4*>(ap + (size_t)t * E + e) =
+            make_float4(acc[i][4 * e4], acc[i][4 * e4 + 1], acc[i][4 * e4 + 2], acc[i][4 * e4 + 3]);
+        *reinterpret_cast<float4*>(sp + (size_t)t * E + e) =
+            make_float4(aab[i][4 * e4], aab[i][4 * e4 + 1], aab[i][4 * e4 + 2], aab[i][4 * e4 + 3]);
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (e + r < E) {
-            ap[(size_t)t * E + e + r] = acc[i][j][r];
-            sp[(size_t)t * E + e + r] = aab[i][j][r];
+            ap[(size_t)t * E + e + r] = acc[i][4 * e4 + r];
+            sp[(size_t)t * E + e + r] = aab[i][4 * e4 + r];
           }
       }
     }
@@ -341,7 +397,7 @@ __global__ __launch_bounds__(256) void router_screen_select_wg_kernel(
 }
 
 // Slices: enough workgroups (64 tokens x 256 experts each) to give every CU
-// one, at least two 32-element steps per slice, and at most 2^22 partial
+// one, at least one 64-element stage per slice, and at most 2^22 partial
 // entries per array.
 int router_screen_splits(int T, int d, int E) {
   const long long wgs = (long long)max(1, (T + 63) / 64) * ((E + 255) / 256);
@@ -367,8 +423,10 @@ static void launch_select(dim3 grid, size_t lds, hipStream_t st, const bf16_t* x
 hipError_t launch_router_screen_partials(const void* x, const void* w, const int32_t* k, int T, int d, int E,
                                          int k_max, BudgetPolicy pol, int S, float* approx, float* absum,
                                          int32_t* tok_off, int32_t* status, hipStream_t st) {
-  hipLaunchKernelGGL(router_screen_mfma_kernel, dim3(max(1, (T + 63) / 64), (E + 255) / 256, S + 1), dim3(256), 0, st,
-                     (const bf16_t*)x, (const bf16_t*)w, T, d, E, approx, absum, k, k_max, pol, tok_off, status);
+  if (d % 64 != 0) return hipErrorInvalidValue;  // d is a multiple of 128 for any valid descriptor
+  const dim3 grid(max(1, (T + 63) / 64), (E + 255) / 256, S + 1);
+  hipLaunchKernelGGL((router_screen_tile_kernel<3>), grid, dim3(64 * SCR_NW), 0, st, (const bf16_t*)x,
+                     (const bf16_t*)w, T, d, E, approx, absum, k, k_max, pol, tok_off, status);
   return hipGetLastError();
 }
 
