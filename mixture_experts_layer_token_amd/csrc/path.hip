@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void path_screen_kernel(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // exact logits of the needed experts, over their (no longer needed) lower bounds
-  exact_dots<XC, XR, PS_GRP>(
+  exact_dots<XC, XR, PS_GRP, 2, true>(
       x + (size_t)t * d, d, n,
       [&](int c) {
         const int v = clist[c];

@@ -275,8 +275,10 @@ __global__ __launch_bounds__(256) void router_screen_select_kernel(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // exact logits of the candidates
-  exact_dots<XC, XR, SEL_GRP, XR ? 4 : 2>(
+  // exact logits of the candidates (a resident row is kept as bf16 words, 3
+  // candidates' rows in flight: 128 registers, 4 waves per SIMD; 8,192 tokens
+  // x 256 experts, d = 2048: 161 -> 145 us for the whole route call)
+  exact_dots<XC, XR, SEL_GRP, XR ? 3 : 2, true>(
       x + (size_t)t * d, d, ncand, [&](int c) { return w + (size_t)clist[c] * d; }, red,
       [&](int c, double v) { cval[c] = v; });
   // keys of the candidates (bias added in float64 before the one rounding)
