@@ -325,7 +325,7 @@ class Bench:
         sh, out = self.sh, self.out
 
         def step():
-            # whole-expert route -> proxy SwiGLU -> proxy routes -> permute -> FFN -> combine
+            # whole-expert route -> proxy scores and routes -> permute -> FFN -> combine
             proxy["run"]()
             moe.moe_permute(desc, pr.tok_off, pr.ids, pb["c"], pb["eo"], pb["pt"], pb["ps"], pb["iv"], pb["na"],
                             pb["wsp"])

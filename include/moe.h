@@ -348,22 +348,30 @@ moe_status moe_fold(const moe_desc* desc, int32_t mode, int32_t budget, const fl
  *
  * The proxy weight set of whole expert e has Ip = N*r rounded up to a multiple
  * of 128 rows: row n*r + i is gate neuron i of sub-expert N*e + n, the rows
- * from N*r on are zero, so that the grouped FFN's gate/up call computes the
- * activations of every routed (token, pick) pair.
+ * from N*r on are zero.
+ *
+ * Precision (the pages fix none; the contract is the router's): g = x .
+ * w_gate[c] and u = x . w_up[c] are exact products summed in float64 and
+ * rounded once to float32 each; |SiLU(g) u| = |g / (1 + exp(-g)) * u| and
+ * the mean over the r neurons (summed in neuron order, then divided by r) are
+ * float64, and the picks are decided on those float64 scores.
  *
  * moe_proxy_pack: gathers the gate-neuron rows once per layer.
  *   gate_idx  int32 [E][r]: neurons (rows of the sub-expert's w_gate / w_up);
  *             one outside [0, I) packs as a zero row (its activation is 0)
  *   w_gate, w_up  ELT [E][I][d];  wp_gate, wp_up  ELT [E/N][Ip][d] out
- * moe_proxy_route: routes of the split layer from the proxy activations.
+ * moe_proxy_route: routes of the split layer from the proxy scores.
  *   k       int32 [T] sub-expert budgets
  *   kappa   int32 [k_max+1][m]: kappa vector of each budget k (0 <= kappa_j
  *           <= N, sum_j kappa_j = k); a token with budget k_t runs k_t routes
- *   base_tok_off, base_ids, base_w   the whole-expert routes (moe_route)
- *   base_inv_perm  their inverse permutation (moe_permute on those routes)
- *   hp      ELT [T*m][Ip]: moe_ffn_gateup's output on the permuted
- *           whole-expert rows for a descriptor (T, d, E/N, Ip, m) and the
- *           weights wp_gate / wp_up
+ *   base_tok_off, base_ids, base_w   the whole-expert routes (moe_route on
+ *           a descriptor with E/N experts, k_max = m, every k_t = m)
+ *   base_expert_off, base_perm_tok, base_perm_src   moe_permute's expert_off,
+ *           perm_tok and perm_src on those routes (the scores are taken per
+ *           block of up to 64 permuted rows of one whole expert)
+ *   x       ELT [T][d] the tokens' hidden states
+ *   wp_gate, wp_up  ELT [E/N][Ip][d]: moe_proxy_pack's output (desc's
+ *           weight layout)
  *   tok_off int32 [T+1], topk_ids int32 [T*k_max], topk_w float [T*k_max] out
  *           (CSR like moe_route's; within a pick, chosen sub-experts by
  *           score; a whole-expert pick outside [0, E/N) fills its kappa_j
@@ -372,10 +380,8 @@ moe_status moe_fold(const moe_desc* desc, int32_t mode, int32_t budget, const fl
  *   dev_status int32 [1] out or NULL: MOE_DEV_BAD_K for a k_t outside
  *           [0, k_max] or whose kappa row has an entry outside [0, N] or does
  *           not sum to k_t (such a token runs nothing)
- * The scores are taken in float32 from the ELT activations, so sub-experts
- * whose proxy scores differ by less than that rounding may rank either way.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (N, r, m out of range), MOE_ERR_ALIGN
- * (moe_proxy_pack's weights), MOE_ERR_LAUNCH.
+ * (the weights, or x), MOE_ERR_LAUNCH.
  */
 /*
  * moe_proxy_kappa_balanced (host only, no device call): the kappa table of
@@ -391,7 +397,8 @@ moe_status moe_proxy_pack(const moe_desc* desc, int32_t N, int32_t r, const int3
                           moe_stream_t stream);
 moe_status moe_proxy_route(const moe_desc* desc, int32_t N, int32_t r, int32_t m, const int32_t* k,
                            const int32_t* kappa, const int32_t* base_tok_off, const int32_t* base_ids,
-                           const float* base_w, const int32_t* base_inv_perm, const void* hp,
+                           const float* base_w, const int32_t* base_expert_off, const int32_t* base_perm_tok,
+                           const int32_t* base_perm_src, const void* x, const void* wp_gate, const void* wp_up,
                            int32_t* tok_off, int32_t* topk_ids, float* topk_w, int32_t* dev_status,
                            moe_stream_t stream);
 

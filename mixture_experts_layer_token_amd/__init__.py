@@ -235,12 +235,15 @@ def moe_proxy_pack(desc, N: int, r: int, gate_idx, w_gate, w_up, wp_gate, wp_up,
         _stream(stream)))
 
 
-def moe_proxy_route(desc, N: int, r: int, m: int, k, kappa, base_tok_off, base_ids, base_w, base_inv_perm, hp,
-                    tok_off, topk_ids, topk_w, dev_status, stream=None) -> None:
+def moe_proxy_route(desc, N: int, r: int, m: int, k, kappa, base_tok_off, base_ids, base_w, base_expert_off,
+                    base_perm_tok, base_perm_src, x, wp_gate, wp_up, tok_off, topk_ids, topk_w, dev_status,
+                    stream=None) -> None:
     _check("moe_proxy_route", _lib.load().moe_proxy_route(
         ctypes.byref(desc), N, r, m, _dev(k, "k", _I32, desc.T), _dev(kappa, "kappa", _I32),
         _dev(base_tok_off, "base_tok_off", _I32), _dev(base_ids, "base_ids", _I32), _dev(base_w, "base_w", _F32),
-        _dev(base_inv_perm, "base_inv_perm", _I32), _dev(hp, "hp", _elt(desc)), _dev(tok_off, "tok_off", _I32, desc.T + 1),
+        _dev(base_expert_off, "base_expert_off", _I32), _dev(base_perm_tok, "base_perm_tok", _I32),
+        _dev(base_perm_src, "base_perm_src", _I32), _dev(x, "x", _elt(desc)), _dev(wp_gate, "wp_gate", _elt(desc)), _dev(wp_up, "wp_up", _elt(desc)),
+        _dev(tok_off, "tok_off", _I32, desc.T + 1),
         _dev(topk_ids, "topk_ids", _I32), _dev(topk_w, "topk_w", _F32), _dev(dev_status, "dev_status", _I32),
         _stream(stream)))
 
@@ -333,10 +336,11 @@ def proxy_pack(w_gate: torch.Tensor, w_up: torch.Tensor, gate_idx: torch.Tensor,
 
 class ProxyRouter:
     """Buffers and calls of proxy-gated routing for a fixed shape: the
-    whole-expert router (moe_route with every k_t = m), its permutation, the
-    proxy SwiGLU (moe_ffn_plan + moe_ffn_gateup on the packed weights) and
-    moe_proxy_route.  ``run`` only launches (no allocation), so it can be
-    captured in a HIP graph."""
+    whole-expert router (moe_route with every k_t = m), its permutation, and
+    moe_proxy_route, which scores the picks' sub-experts from x and the packed
+    weights.
+    ``run`` only launches (no allocation), so it can be captured in a HIP
+    graph."""
 
     def __init__(self, desc: moe_desc, N: int, r: int, m: int, kappa: torch.Tensor, device="cuda"):
         self.desc, self.N, self.r, self.m = desc, N, r, m
@@ -359,10 +363,8 @@ class ProxyRouter:
         self.b_psrc = torch.empty(A, **i32)
         self.b_inv = torch.empty(A, **i32)
         self.b_nact = torch.empty(1, **i32)
-        self.hp = torch.empty((A, self.Ip), dtype=dtype, device=device)
         self.ws_route = alloc_workspace(self.base, MOE_OP_ROUTE, device)
         self.ws_perm = alloc_workspace(self.base, MOE_OP_PERMUTE, device)
-        self.ws_ffn = alloc_workspace(self.base, MOE_OP_FFN, device)
         km = desc.k_max
         self.tok_off = torch.empty(T + 1, **i32)
         self.ids = torch.empty(max(T * km, 1), **i32)
@@ -375,10 +377,9 @@ class ProxyRouter:
                   self.b_status, self.ws_route, stream)
         moe_permute(b, self.b_tok_off, self.b_ids, self.b_counts, self.b_eoff, self.b_ptok, self.b_psrc,
                     self.b_inv, self.b_nact, self.ws_perm, stream)
-        moe_ffn_plan(b, self.b_eoff, self.ws_ffn, stream)
-        moe_ffn_gateup(b, x, wp_gate, wp_up, self.b_eoff, self.b_ptok, self.hp, self.ws_ffn, stream)
         moe_proxy_route(self.desc, self.N, self.r, self.m, k, self.kappa, self.b_tok_off, self.b_ids, self.b_w,
-                        self.b_inv, self.hp, self.tok_off, self.ids, self.w, self.status, stream)
+                        self.b_eoff, self.b_ptok, self.b_psrc, x, wp_gate, wp_up, self.tok_off, self.ids, self.w,
+                        self.status, stream)
         return self.tok_off, self.ids, self.w, self.status
 
 

@@ -58,7 +58,7 @@ SIGNATURES = {
     "moe_proxy_kappa_balanced": [c_i32, c_i32, c_i32, c_ptr],
     "moe_proxy_pack": [_P, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr],
     "moe_proxy_route": [_P, c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
-                        c_ptr, c_ptr, c_ptr],
+                        c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr],
     "moe_forward": [_P, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
                     c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
     "moe_probe_read": [c_ptr, c_size, c_i32, c_ptr, c_ptr],

@@ -135,10 +135,10 @@ hipError_t launch_fold(int mode, int budget, const float* S, const float* L, con
 hipError_t launch_proxy_pack(int dtype, const int32_t* gate_idx, const void* wg, const void* wu, int E_base, int I_sub,
                              int d, int N, int r, int Ip, void* pg, void* pu, int blocked, hipStream_t st);
 hipError_t launch_proxy_route(int dtype, const int32_t* k, const int32_t* kappa, int T, int k_max, int m, int N, int r,
-                              int Ip,
-                              const int32_t* base_tok_off, const int32_t* base_ids, const float* base_w,
-                              const int32_t* base_inv, const void* hp, int E_base, int32_t* tok_off, int32_t* ids,
-                              float* wts, int32_t* status, hipStream_t st);
+                              int Ip, const int32_t* base_tok_off, const int32_t* base_ids, const float* base_w,
+                              const int32_t* base_eoff, const int32_t* base_ptok, const int32_t* base_psrc,
+                              const void* x, const void* wpg, const void* wpu, int E_base, int d, int blocked,
+                              int32_t* tok_off, int32_t* ids, float* wts, int32_t* status, hipStream_t st);
 
 // path.hip -- compositional path routing (PCoMoE).  `table`: int32 src[P],
 // int32 tgt[P], float bias[P].

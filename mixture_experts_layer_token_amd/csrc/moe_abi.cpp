@@ -535,18 +535,22 @@ moe_status moe_proxy_pack(const moe_desc* desc, int32_t N, int32_t r, const int3
 
 moe_status moe_proxy_route(const moe_desc* desc, int32_t N, int32_t r, int32_t m, const int32_t* k,
                            const int32_t* kappa, const int32_t* base_tok_off, const int32_t* base_ids,
-                           const float* base_w, const int32_t* base_inv_perm, const void* hp, int32_t* tok_off,
-                           int32_t* topk_ids, float* topk_w, int32_t* dev_status, moe_stream_t stream) {
+                           const float* base_w, const int32_t* base_expert_off, const int32_t* base_perm_tok,
+                           const int32_t* base_perm_src, const void* x, const void* wp_gate, const void* wp_up,
+                           int32_t* tok_off, int32_t* topk_ids, float* topk_w, int32_t* dev_status,
+                           moe_stream_t stream) {
   MOE_TRY(check_desc(desc));
   const moe_desc& d = *desc;
   MOE_TRY(proxy_shape(d, N, r, m));
   if (!kappa || !tok_off || !tok_ptr(d, k) || !tok_ptr(d, base_tok_off) || !tok_ptr(d, base_ids) ||
-      !tok_ptr(d, base_w) || !tok_ptr(d, base_inv_perm) || !tok_ptr(d, hp) || !tok_ptr(d, topk_ids) ||
-      !tok_ptr(d, topk_w))
+      !tok_ptr(d, base_w) || !base_expert_off || !tok_ptr(d, base_perm_tok) || !tok_ptr(d, base_perm_src) ||
+      !tok_ptr(d, x) || !wp_gate || !wp_up || !tok_ptr(d, topk_ids) || !tok_ptr(d, topk_w))
     return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(wp_gate) || !aligned16(wp_up)) return MOE_ERR_ALIGN;
   return launched(launch_proxy_route(d.dtype, k, kappa, d.T, d.k_max, m, N, r, proxy_width(N, r), base_tok_off,
-                                     base_ids, base_w, base_inv_perm, hp, d.E / N, tok_off, topk_ids, topk_w,
-                                     dev_status, static_cast<hipStream_t>(stream)));
+                                     base_ids, base_w, base_expert_off, base_perm_tok, base_perm_src, x, wp_gate,
+                                     wp_up, d.E / N, d.d, d.weight_layout, tok_off, topk_ids, topk_w, dev_status,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 static constexpr int32_t kMaxPaths = 1024;

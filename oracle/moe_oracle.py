@@ -429,15 +429,24 @@ def kappa_balanced(k: int, m: int, N: int) -> list:
 
 def proxy_scores(x_row, w_gate, w_up, gate_idx, e: int, N: int) -> np.ndarray:
     """s_n(x) = (1/r) sum over the gate neurons c of sub-expert N*e + n of
-    |SiLU(x . w_gate[sub][c]) * (x . w_up[sub][c])| for n < N (float64)."""
+    |SiLU(g_c) * u_c| for n < N (MoE-Prism §III-B2, proxy-gating paragraph).
+
+    The page fixes no precision; the contract is the router's: g_c = x .
+    w_gate[sub][c] and u_c = x . w_up[sub][c] are taken in float64 (exact
+    products) and rounded once to float32 each; the activations and their sum
+    over c (in the order of gate_idx, then divided by r) are float64."""
     x = _f64(x_row)
     out = np.zeros(N, dtype=np.float64)
     for n in range(N):
         sub = N * e + n
         c = np.asarray(gate_idx[sub], dtype=np.int64)
-        g = _f64(w_gate[sub])[c] @ x
-        u = _f64(w_up[sub])[c] @ x
-        out[n] = np.abs(silu(g) * u).mean()
+        g = (_f64(w_gate[sub])[c] @ x).astype(np.float32).astype(np.float64)
+        u = (_f64(w_up[sub])[c] @ x).astype(np.float32).astype(np.float64)
+        acts = np.abs(silu(g) * u)
+        total = 0.0
+        for v in acts:
+            total += float(v)
+        out[n] = total / len(c)
     return out
 
 

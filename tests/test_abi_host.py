@@ -153,8 +153,8 @@ def test_proxy_validates_before_launch():
     P = lambda v: ctypes.c_void_p(v)
     x = P(1 << 20)  # never dereferenced: every call below fails validation first
     route = lambda N, r, m, desc=d, **kw: lib.moe_proxy_route(
-        ctypes.byref(desc), N, r, m, *[kw.get(n, x) for n in ("k", "kappa", "bto", "bids", "bw", "binv", "hp",
-                                                               "to", "ids", "w")], None, None)
+        ctypes.byref(desc), N, r, m, *[kw.get(n, x) for n in ("k", "kappa", "bto", "bids", "bw", "beo", "bpt", "bps",
+                                                               "x", "pg", "pu", "to", "ids", "w")], None, None)
     assert route(3, 8, 4) == 2                     # E not a multiple of N
     assert route(4, 8, 1) == 2                     # k_max > m*N
     assert route(4, 0, 2) == 2                     # r < 1
@@ -162,8 +162,11 @@ def test_proxy_validates_before_launch():
     assert route(4, 129, 2) == 2                   # r > I
     big = _desc(T=4, d=128, E=256, I=128, k_max=8)
     assert route(4, 8, 17, desc=big) == 2          # m*N > 64
-    assert route(4, 8, 2, hp=None) == 1
+    assert route(4, 8, 2, x=None) == 1
+    assert route(4, 8, 2, pu=None) == 1
+    assert route(4, 8, 2, beo=None) == 1
     assert route(4, 8, 2, kappa=None) == 1
+    assert route(4, 8, 2, pg=P((1 << 20) + 2)) == 5  # packed weights not 16-byte aligned
     pack = lambda N, r, **kw: lib.moe_proxy_pack(ctypes.byref(d), N, r, *[kw.get(n, x) for n in (
         "gi", "wg", "wu", "pg", "pu")], None)
     assert pack(3, 8) == 2

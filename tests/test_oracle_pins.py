@@ -513,7 +513,8 @@ def test_kappa_balanced():
 
 def test_proxy_scores_match_scalar_definition():
     """s_n = mean over the gate neurons of |SiLU(g) u|, recomputed neuron by
-    neuron with exact sums (math.fsum) and scipy's logistic function."""
+    neuron with exact sums (math.fsum, then one rounding to float32 each, the
+    precision contract) and scipy's logistic function."""
     L = make_custom_layer(T=3, d=24, E=8, I=16, k=[1, 1, 1], seed=31)
     a = _arrays(L)
     rng = np.random.default_rng(2)
@@ -525,8 +526,8 @@ def test_proxy_scores_match_scalar_definition():
                 sub = 4 * e + n
                 vals = []
                 for c in gate_idx[sub]:
-                    g = math.fsum(float(p) * float(q) for p, q in zip(a["x"][t], a["w_gate"][sub][c]))
-                    u = math.fsum(float(p) * float(q) for p, q in zip(a["x"][t], a["w_up"][sub][c]))
+                    g = float(np.float32(math.fsum(float(p) * float(q) for p, q in zip(a["x"][t], a["w_gate"][sub][c]))))
+                    u = float(np.float32(math.fsum(float(p) * float(q) for p, q in zip(a["x"][t], a["w_up"][sub][c]))))
                     vals.append(abs(g * float(scipy.special.expit(g)) * u))
                 assert abs(s[n] - math.fsum(vals) / len(vals)) <= 1e-12 * max(1.0, abs(s[n]))
 
