@@ -19,9 +19,8 @@ __device__ __forceinline__ void unpack(const uint4& v, float (&f)[8]) {
 }
 
 // One workgroup per token; a thread owns 16-byte column chunks c, c+256, ...
-// The rows of CB assignments are requested together, one batch ahead of the
-// batch being summed; the sum runs in ascending j (the loads overlap, the
-// arithmetic order does not change).
+// The rows of CB assignments are requested together; the sum runs in
+// ascending j (the loads overlap, the arithmetic order does not change).
 constexpr int CB = 8;
 
 template <typename T>
@@ -46,20 +45,29 @@ __device__ __forceinline__ void unpack_chunk<float>(const uint4& v, float (&f)[4
   f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y); f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
 }
 template <typename T>
-__device__ __forceinline__ void store_chunk(T* p, const float* f);
+__device__ __forceinline__ void store_chunk_nt(T* p, const float* f);
 template <>
-__device__ __forceinline__ void store_chunk<bf16_t>(bf16_t* p, const float* f) {
-  uint32_t o[4];
+__device__ __forceinline__ void store_chunk_nt<bf16_t>(bf16_t* p, const float* f) {
+  u32x4_t o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
-  *reinterpret_cast<uint4*>(p) = make_uint4(o[0], o[1], o[2], o[3]);
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(p));
 }
 template <>
-__device__ __forceinline__ void store_chunk<float>(float* p, const float* f) {
-  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+__device__ __forceinline__ void store_chunk_nt<float>(float* p, const float* f) {
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(f[i]);
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(p));
 }
 
-template <typename T>
+// A thread takes CC column chunks at a time (c, c + 256, ..., c + 256 (CC -
+// 1)): the rows of a batch are requested for all of them before any is summed,
+// so a token whose k_t fits one batch waits for memory once per CC chunks,
+// not once per chunk.  The launch picks CC from d (1 where a thread has one
+// chunk: more would only cost registers).  The output rows are stored with
+// the non-temporal hint (nothing reads them back in the layer).
+template <typename T, int CC>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const T* __restrict__ ysh,
                                                       const int32_t* __restrict__ tok_off,
                                                       const float* __restrict__ wts,
@@ -68,66 +76,81 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
   constexpr int LE = 16 / sizeof(T);
   const int t = blockIdx.x;
   const int a0 = tok_off[t], a1 = tok_off[t + 1];
-  const int nb = (a1 - a0 + CB - 1) / CB;
-  for (int c = threadIdx.x; c < d / LE; c += 256) {
-    float acc[LE];
+  const int nch = d / LE;
+  for (int c0 = threadIdx.x; c0 < nch; c0 += 256 * CC) {
+    float acc[CC][LE];
 #pragma unroll
-    for (int i = 0; i < LE; ++i) acc[i] = 0.f;
-    uint4 rb[2][CB];
-    auto issue = [&](uint4 (&r)[CB], int b) {
+    for (int q = 0; q < CC; ++q)
+#pragma unroll
+      for (int i = 0; i < LE; ++i) acc[q][i] = 0.f;
+    for (int b = a0; b < a1; b += CB) {
+      uint4 r[CB][CC];
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
-        const int a = a0 + b * CB + j;
+        const int a = b + j;
         const int p = a < a1 ? inv_perm[a] : -1;  // -1: an assignment without a row
-        // Y is read exactly once: non-temporal loads keep it from displacing
-        // anything in the caches
-        r[j] = zero_u4();
-        if (p >= 0) {
-          const u32x4_t v = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4_t*>(y + (size_t)p * d + c * LE));
-          r[j] = make_uint4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+        for (int q = 0; q < CC; ++q) {
+          const int c = c0 + 256 * q;
+          r[j][q] = zero_u4();
+          // Y is read exactly once: non-temporal loads keep it from displacing
+          // anything in the caches
+          if (p >= 0 && c < nch) {
+            const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(y + (size_t)p * d + c * LE));
+            r[j][q] = make_uint4(v[0], v[1], v[2], v[3]);
+          }
         }
       }
-    };
-    auto consume = [&](const uint4 (&r)[CB], int b) {
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
-        const int a = a0 + b * CB + j;
+        const int a = b + j;
         if (a < a1 && inv_perm[a] >= 0) {
-          float f[LE];
-          unpack_chunk<T>(r[j], f);
           const float w = wts[a];
 #pragma unroll
-          for (int i = 0; i < LE; ++i) acc[i] = fmaf(w, f[i], acc[i]);
+          for (int q = 0; q < CC; ++q) {
+            float f[LE];
+            unpack_chunk<T>(r[j][q], f);
+#pragma unroll
+            for (int i = 0; i < LE; ++i) acc[q][i] = fmaf(w, f[i], acc[q][i]);
+          }
         }
       }
-    };
-    if (nb > 0) issue(rb[0], 0);
-    for (int b = 0; b < nb; b += 2) {
-      if (b + 1 < nb) issue(rb[1], b + 1);
-      consume(rb[0], b);
-      if (b + 2 < nb) issue(rb[0], b + 2);
-      if (b + 1 < nb) consume(rb[1], b + 1);
     }
-    if (ysh) {
-      float f[LE];
-      load_chunk<T>(ysh + (size_t)t * d + c * LE, f);
 #pragma unroll
-      for (int i = 0; i < LE; ++i) acc[i] += f[i];
+    for (int q = 0; q < CC; ++q) {
+      const int c = c0 + 256 * q;
+      if (c < nch) {
+        if (ysh) {
+          float f[LE];
+          load_chunk<T>(ysh + (size_t)t * d + c * LE, f);
+#pragma unroll
+          for (int i = 0; i < LE; ++i) acc[q][i] += f[i];
+        }
+        store_chunk_nt<T>(out + (size_t)t * d + c * LE, acc[q]);
+      }
     }
-    store_chunk<T>(out + (size_t)t * d + c * LE, acc);
   }
+}
+
+template <typename T>
+static void launch_combine_t(const T* y, const T* y_shared, const int32_t* tok_off, const float* wts,
+                             const int32_t* inv_perm, T* out, int T_, int d, hipStream_t st) {
+  const int nch = d / (16 / (int)sizeof(T));
+  if (nch > 512)
+    hipLaunchKernelGGL((combine_kernel<T, 4>), dim3(T_), dim3(256), 0, st, y, y_shared, tok_off, wts, inv_perm, out, d);
+  else if (nch > 256)
+    hipLaunchKernelGGL((combine_kernel<T, 2>), dim3(T_), dim3(256), 0, st, y, y_shared, tok_off, wts, inv_perm, out, d);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, 1>), dim3(T_), dim3(256), 0, st, y, y_shared, tok_off, wts, inv_perm, out, d);
 }
 
 hipError_t launch_combine(int dtype, const void* y, const void* y_shared, const int32_t* tok_off,
                           const float* wts, const int32_t* inv_perm, void* out, int T, int d, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(256), 0, st, (const bf16_t*)y, (const bf16_t*)y_shared,
-                       tok_off, wts, inv_perm, (bf16_t*)out, d);
+    launch_combine_t<bf16_t>((const bf16_t*)y, (const bf16_t*)y_shared, tok_off, wts, inv_perm, (bf16_t*)out, T, d, st);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)y, (const float*)y_shared,
-                       tok_off, wts, inv_perm, (float*)out, d);
+    launch_combine_t<float>((const float*)y, (const float*)y_shared, tok_off, wts, inv_perm, (float*)out, T, d, st);
   return hipGetLastError();
 }
 
