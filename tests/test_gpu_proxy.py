@@ -238,10 +238,12 @@ def test_proxy_bad_kappa_rows_and_graph_replay():
         assert torch.equal(pr.w[:A], first[1])
 
 
-@pytest.mark.parametrize("T,N,m,E,r", [(0, 4, 2, 32, 4), (1, 8, 8, 128, 16), (129, 8, 8, 128, 3)])
+@pytest.mark.parametrize("T,N,m,E,r", [(0, 4, 2, 32, 4), (1, 8, 8, 128, 16), (129, 8, 8, 128, 3),
+                                        (37, 64, 1, 128, 2)])
 def test_proxy_edges(T, N, m, E, r):
-    """Empty batch, one token, and the widest pick set (m*N = 64 lanes) with a
-    ragged token count and r not dividing the padded width."""
+    """Empty batch, one token, the widest pick set (m*N = 64) with a ragged
+    token count and r not dividing the padded width, and the most sub-experts
+    per pick (N = 64: the largest score table and ranking)."""
     k_max = m * N
     cfg = _small_cfg("f32", T=T, E=E, N=N, k_max=k_max)
     layer = make_layer(cfg, "cuda")
