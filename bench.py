@@ -94,6 +94,10 @@ def parse():
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens in the CPU-oracle sample (0 = workload default)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time the vendor library's dense bf16 GEMM (torch.matmul) on matrices of the "
+                         "routed FFN's shapes and FLOPs (A x d by d x 2I, A x I by I x d): a reference for "
+                         "the grouped kernels' MFMA fraction, outside the layer's timing")
     ap.add_argument("--calib-copy", action="store_true",
                     help="before timing, run a plain elementwise copy (torch.neg) of 512 MiB fp32 three "
                          "times: the known-size kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE")
@@ -213,6 +217,49 @@ def read_ceiling(dev, stream):
     torch.cuda.synchronize()
     return {"GBps": max(res.values()), "ordinary_GBps": res["ordinary"], "nontemporal_GBps": res["nontemporal"],
             "bytes": nbytes, "kernel": "moe_probe_read (16-byte loads, 4 KB runs round-robin, 2 workgroups/CU)"}
+
+
+def library_gemm(dev, stream, A, d, I, flush):
+    """Dense bf16 GEMMs of the vendor library (torch.matmul) with the routed
+    FFN's FLOPs: [A, d] x [d, 2I] (gate and up side by side) and [A, I] x
+    [I, d], no gather, no grouping, no SwiGLU.  The right operand is timed
+    both as [N, K] (K contiguous, the experts' storage; a transposed 2-D view)
+    and as [K, N]; the faster is reported.  Median of 9 launches, each after
+    the cache-evicting write."""
+    import torch
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    for name, (M, K, N) in (("gateup", (A, d, 2 * I)), ("down", (A, I, d))):
+        a = torch.randn(M, K, device=dev, dtype=torch.bfloat16, generator=g)
+        c = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+        best = None
+        for layout in ("NK", "KN"):
+            w = torch.randn((N, K) if layout == "NK" else (K, N), device=dev, dtype=torch.bfloat16, generator=g)
+            rhs = w.t() if layout == "NK" else w
+            ts = []
+            with torch.cuda.stream(stream):
+                for i in range(12):
+                    flush()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    torch.matmul(a, rhs, out=c)
+                    e1.record(stream)
+                    e1.synchronize()
+                    if i >= 3:
+                        ts.append(e0.elapsed_time(e1) * 1e3)
+            ts.sort()
+            us = ts[len(ts) // 2]
+            if best is None or us < best[0]:
+                best = (us, layout)
+            del w, rhs
+        us, layout = best
+        tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        out[name] = {"M": M, "K": K, "N": N, "weights": layout, "us": round(us, 1), "TFLOPs": round(tf, 1),
+                     "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del a, c
+    torch.cuda.synchronize()
+    return out
 
 
 class Bench:
@@ -678,6 +725,7 @@ def main():
                   "roofline": droof}
 
     ceiling = None if args.no_probe else read_ceiling(dev, stream)
+    lib_gemm = library_gemm(dev, stream, A, cfg.d, cfg.I, flush) if args.library_gemm else None
 
     cpu = None
     if (not args.no_cpu_baseline and args.k_policy == "exact" and not args.fold and not args.proxy
@@ -742,6 +790,8 @@ def main():
         "decode": decode,
         "cpu_baseline": cpu,
     }
+    if lib_gemm is not None:
+        rec["library_gemm"] = lib_gemm
     print(json.dumps(rec), flush=True)
 
 
