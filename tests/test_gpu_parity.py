@@ -159,11 +159,12 @@ def test_budget_policies(policy, granule, router, T):
     _say(f"[budgets] {policy}/{granule} {router} T={T}: A={got['A']} {err}")
 
 
+@pytest.mark.parametrize("E", [16, 32])
 @pytest.mark.parametrize("router", ["float64", "screened", "fused"])
-def test_exact_ties_break_to_lower_index(router):
+def test_exact_ties_break_to_lower_index(router, E):
     """Zero hidden states make every logit equal its bias; duplicated router
     rows make exactly tied logits for any x."""
-    T, E = 40, 16
+    T = 40
     layer = make_custom_layer(T=T, d=128, E=E, I=128, k=[5] * T, dtype="bf16", k_max=8, device="cuda")
     layer.x[: T // 2].zero_()
     layer.w_router[1::2].copy_(layer.w_router[0::2])           # experts 2j and 2j+1 tie
@@ -180,11 +181,16 @@ def test_exact_ties_break_to_lower_index(router):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("T,E,d,kmax", [(1024, 256, 2048, 16), (1, 1, 128, 1), (77, 3, 384, 3),
-                                        (300, 128, 4096, 8), (64, 8, 4096, 2)])
+                                        (300, 128, 4096, 8), (64, 8, 4096, 2),
+                                        # Qwen3-shaped rows, T at its limit, few and non-power-of-two E,
+                                        # d at its limit, k_t up to E
+                                        (256, 128, 2048, 8), (1024, 128, 2048, 8), (5, 32, 128, 4),
+                                        (129, 96, 2048, 8), (33, 64, 8192, 6), (70, 32, 4224, 32)])
 def test_fused_router_matches_split_and_oracle(dtype, T, E, d, kmax):
     """The one-launch router of small batches: routing bit-exact against the
     oracle and equal to the split-K float64 router (ids, weights, offsets),
-    at the largest batch and E x d it takes, E = 1 and a non-power-of-two E."""
+    at the largest batch and E x d it takes, E = 1 and non-power-of-two E, d
+    at its limit (8192 with E = 64) and k_t up to E."""
     rng = np.random.default_rng(T * 7 + E)
     k = rng.integers(0, kmax + 1, size=T)
     k[0] = kmax
