@@ -190,9 +190,14 @@ def cpu_baseline(layer, n_tokens: int, min_seconds: float = 10.0):
                       f"average (BLAS pool {blas} threads)"}
 
 
-def read_ceiling(dev, stream):
+def read_ceiling(dev, stream, flush, kernel_bytes=None):
     """GB/s of the streaming-read probe (moe_probe_read) over 4 GiB, ordinary
-    and non-temporal loads, best of 5 launches each."""
+    and non-temporal loads, best of 5 launches each.  With kernel_bytes, also
+    the non-temporal probe over the dominant kernel's own algorithmic bytes
+    (at most 4 GiB), each launch after the same cache-evicting write as the
+    timed steps, median of 5: the read rate a plain stream of that size
+    reaches from a cold cache (it falls with the size: the ramp and the tail
+    of a launch weigh more on a short one)."""
     import torch
 
     import mixture_experts_layer_token_amd as moe
@@ -213,10 +218,27 @@ def read_ceiling(dev, stream):
                 ms = a.elapsed_time(b)
                 best = ms if best is None else min(best, ms)
             res["nontemporal" if nt else "ordinary"] = round(nbytes / (best * 1e-3) / 1e9, 1)
+        at_size = None
+        if kernel_bytes:
+            n_at = min(int(kernel_bytes), nbytes) // 16 * 4   # int32 elements, whole 16-byte chunks
+            part = buf[:n_at]
+            per = []
+            for _ in range(5):
+                flush()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                moe.probe_read(part, sink, True)
+                b.record(stream)
+                b.synchronize()
+                per.append(a.elapsed_time(b))
+            med = statistics.median(per)
+            at_size = {"bytes": n_at * 4, "GBps": round(n_at * 4 / (med * 1e-3) / 1e9, 1),
+                       "timing": "non-temporal loads, 1 GiB cache-evicting write before each launch, median of 5"}
     del buf
     torch.cuda.synchronize()
     return {"GBps": max(res.values()), "ordinary_GBps": res["ordinary"], "nontemporal_GBps": res["nontemporal"],
-            "bytes": nbytes, "kernel": "moe_probe_read (16-byte loads, 4 KB runs round-robin, 2 workgroups/CU)"}
+            "bytes": nbytes, "kernel": "moe_probe_read (16-byte loads, 4 KB runs round-robin, 2 workgroups/CU)",
+            "at_kernel_bytes": at_size}
 
 
 def library_gemm(dev, stream, A, d, I, flush):
@@ -724,7 +746,18 @@ def main():
                   "ffn_path": dec_b.routed_path, "timing": dec_b.timing, "layer": dec_b.layer_info(dn, dA),
                   "roofline": droof}
 
-    ceiling = None if args.no_probe else read_ceiling(dev, stream)
+    ceiling = None
+    if not args.no_probe:
+        hbm = roof.get("bound") == "hbm"
+        ceiling = read_ceiling(dev, stream, flush, roof["algorithmic_per_launch"] if hbm else None)
+        if hbm and ceiling["at_kernel_bytes"]:
+            # the dominant kernel against the plain read of its own size
+            roof["frac_of_read_at_size"] = round(roof["achieved"] / ceiling["at_kernel_bytes"]["GBps"], 4)
+        if decode is not None and decode["roofline"].get("bound") == "hbm":
+            dr = decode["roofline"]
+            at = read_ceiling(dev, stream, flush, dr["algorithmic_per_launch"])["at_kernel_bytes"]
+            decode["read_ceiling_at_kernel_bytes"] = at
+            dr["frac_of_read_at_size"] = round(dr["achieved"] / at["GBps"], 4)
     lib_gemm = library_gemm(dev, stream, A, cfg.d, cfg.I, flush) if args.library_gemm else None
 
     cpu = None
