@@ -113,28 +113,25 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   constexpr int LDS_BYTES = (EPI > 0 && BM * EPITCH > RING) ? BM * EPITCH : RING;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
-  // ---- which (row block, row tile, N tile) this workgroup owns.  Row tiles
+  // ---- which (row block, row tile, N tile) this workgroup owns.  The tiles
   // of the second, dense problem (rows_s > 0: an always-on expert over rows
-  // [0, rows_s) with weights w0s/w1s) are spread evenly through those of the
-  // grouped one, so every XCD interleaves both. ----
+  // [0, rows_s) with weights w0s/w1s) come after the grouped problem's in
+  // every XCD's range, so these compute-bound tiles take the CUs that the end
+  // of the weight stream leaves idle (256 experts x 96 rows, d = 7168, with a
+  // 4,096-row shared expert: 4.46 ms per layer against 4.50-4.54 ms with the
+  // dense tiles spread evenly through the grouped ones). ----
   const int nN = N / BNW;
   const int r_mt = blocks ? blocks[bound].x : (dense_rows + BM - 1) / BM;
   const int s_mt = SEC ? (rows_s + BM - 1) / BM : 0;
-  const int mt_all = r_mt + s_mt;
-  const int total = mt_all * nN;
-  const int per = (total + 7) >> 3;
+  // XCD x (ids x, x + 8, ...) takes tiles [x * Rp, (x + 1) * Rp) of the
+  // grouped problem, then tiles [x * Sp, (x + 1) * Sp) of the second one
+  const int R = r_mt * nN, S2 = s_mt * nN, Rp = (R + 7) >> 3, Sp = (S2 + 7) >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  if (slot >= per) return;
-  const int logical = xcd * per + slot;
-  if (logical >= total) return;
-  const int mtile = logical / nN, nt = logical - mtile * nN;
-  bool second = false;
-  int mk = mtile;  // row tile index within its problem
-  if (s_mt > 0) {
-    const int lo = (int)((long long)mtile * s_mt / mt_all), hi = (int)((long long)(mtile + 1) * s_mt / mt_all);
-    second = hi > lo;
-    mk = second ? lo : mtile - hi;
-  }
+  if (slot >= Rp + Sp) return;
+  const bool second = SEC && slot >= Rp;
+  const int li = second ? xcd * Sp + (slot - Rp) : xcd * Rp + slot;
+  if (li >= (second ? S2 : R)) return;
+  const int mk = li / nN, nt = li - mk * nN;  // row tile within its problem, N tile
   const int rb = mk;
   int g, row0, rows;  // group, first row and rows of the row block
   if (second) {
@@ -431,7 +428,8 @@ static hipError_t launch_gemm_variant(const void* in, const int32_t* row_map, co
   const int rb_bound = blocks ? bound : (dense_rows + BM - 1) / BM;
   const long long total = ((long long)rb_bound + (sec.rows + BM - 1) / BM) * (N / BNW);
   if (total == 0) return hipSuccess;
-  const long long nwg = ((total + 7) / 8) * 8;
+  // eight XCD ranges, each a whole share of both problems' tiles (the kernel's mapping)
+  const long long nwg = 8 * ((rb_bound * (N / BNW) + 7) / 8 + ((long long)((sec.rows + BM - 1) / BM) * (N / BNW) + 7) / 8);
   if (nwg > 0x7fffffffLL / (64 * WM * WN)) return hipErrorInvalidValue;
   if (sec.rows > 0)
     hipLaunchKernelGGL((ffn_gemm_kernel<MODE, BM, BNW, WM, WN, XS, WS, NTW, EPI, true>), dim3((unsigned)nwg),
