@@ -12,9 +12,15 @@
 // v_mfma_f32_32x32x16_bf16, K split over S slices (partial sums per slice, added
 // in slice order by pass 2).  Products of bf16 values are exact in fp32, so in
 // any summation order of depth n the error is at most n * u * S with
-// u = 2^-24 (2^-23 if the hardware truncates) and S <= s / (1 - n u); the
-// slices make n <= d/S + S <= d.  The radius used is r = d * 2^-22 * s (+ a
-// tiny floor), which covers both roundings with a factor of two to spare.
+// u = 2^-24 (2^-23 if the hardware truncates) and S <= s / (1 - n u).  A slice
+// holds at most Lmax = ceil(d / 64 / S) * 64 products, each added once (in
+// whatever order the MFMA adds them), and pass 2 adds the S slice values in
+// fp32: n <= Lmax + S.  The radius used is r = n * 2^-22 * s + n * 2^-126,
+// which covers both roundings with a factor of two to spare, and a product
+// flushed to zero below the normal range at most 2^-126 each.  (The bound
+// n <= d held before as well; with S slices it is about S times tighter, so
+// fewer logits need the exact pass: on 4,096 tokens, d = 7168, S = 4, the
+// depth falls from 7,168 to 1,796.)
 //
 // Pass 2 (one wave per token): lower_e = a + b - r, upper_e = a + b + r (fp64).
 // L = the k_t-th largest lower bound, each rounded down to fp32 first (a
@@ -33,6 +39,13 @@
 namespace moe {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Summation depth n of the screen's float32 sums (see above): the longest
+// slice's products plus the S slice additions of pass 2.
+__device__ __forceinline__ double screen_depth(int d, int S) {
+  const int chunks = d / 64;
+  return (double)(((chunks + S - 1) / S) * 64 + S);
+}
 
 // ---- pass 1: partial approximate logits and |x||w| sums of one K slice.
 // A workgroup of 8 waves covers 64 tokens x 256 experts of one K slice.  K
@@ -218,7 +231,8 @@ __global__ __launch_bounds__(256) void router_screen_select_kernel(
 
   // bounds from the slice partials (added in slice order); the bias of the
   // lane's experts stays in registers
-  const double rad_scale = (double)d * 0x1p-22;
+  const double depth = screen_depth(d, S);
+  const double rad_scale = depth * 0x1p-22, rad_floor = depth * 0x1p-126;
   double cen[KPL], rad[KPL];
   float bs[KPL];
   uint32_t lkey[KPL];
@@ -250,7 +264,7 @@ __global__ __launch_bounds__(256) void router_screen_select_kernel(
         }
       }
       cen[s] = (double)a + (double)bs[s];
-      rad[s] = rad_scale * (double)m + 0x1p-126;
+      rad[s] = rad_scale * (double)m + rad_floor;
       lkey[s] = logit_key(__double2float_rd(cen[s] - rad[s]));
     }
   }
@@ -323,7 +337,8 @@ __global__ __launch_bounds__(256) void router_screen_select_wg_kernel(
   float bs[KPL];
   int cidx[KPL];
   if (wv == 0) {
-    const double rad_scale = (double)d * 0x1p-22;
+    const double depth = screen_depth(d, S);
+    const double rad_scale = depth * 0x1p-22, rad_floor = depth * 0x1p-126;
     uint32_t lkey[KPL];
     const size_t sstride = (size_t)T * E;
 #pragma unroll
@@ -352,7 +367,7 @@ __global__ __launch_bounds__(256) void router_screen_select_wg_kernel(
           }
         }
         cen[s] = (double)a + (double)bs[s];
-        rad[s] = rad_scale * (double)m + 0x1p-126;
+        rad[s] = rad_scale * (double)m + rad_floor;
         lkey[s] = logit_key(__double2float_rd(cen[s] - rad[s]));
       }
     }
