@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256) void path_topk_kernel(const double* __restrict
 }
 
 // ---- screened path selection (bf16, E <= 256), one wave per token ----
-// Each logit lies within r = d * 2^-22 * sum|x||w| of its MFMA value (the
+// Each logit lies within r = n * 2^-22 * sum|x||w| + n * 2^-126 of its MFMA
+// value, n the summation depth of the screening pass (screen_depth: the
 // screened router's bound), widened by 2^-22 of its size for the rounding of
 // the exact logit to float32; the float32 logits g, t are then inside
 // [lo, hi] rounded outwards.  A path score is a monotone function of (g, t),
@@ -143,7 +144,8 @@ __global__ __launch_bounds__(256) void path_screen_kernel(
   float* const gx = glo;
   float* const tx = tlo;
   uint32_t* const need = reinterpret_cast<uint32_t*>(thi + E);
-  const double rad_scale = (double)d * 0x1p-22;
+  const double depth = screen_depth(d, S);
+  const double rad_scale = depth * 0x1p-22, rad_floor = depth * 0x1p-126;
   const size_t sstride = (size_t)T * E;
   const int nm = has_t ? 2 : 1;
   // slice partials of the lane's experts, all (expert, matrix) pairs of a
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256) void path_screen_kernel(
       for (int m = 0; m < 2; ++m) {
         if (m >= nm) continue;
         const double c = (double)sa[m][s] + ((m == 0 && bias) ? (double)bias[e] : 0.0);
-        const double r = rad_scale * (double)sq[m][s] + fabs(c) * 0x1p-22 + 0x1p-126;
+        const double r = rad_scale * (double)sq[m][s] + fabs(c) * 0x1p-22 + rad_floor;
         (m ? tlo : glo)[e] = __double2float_rd(c - r);
         (m ? thi : ghi)[e] = __double2float_ru(c + r);
       }

@@ -40,12 +40,6 @@ namespace moe {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// Summation depth n of the screen's float32 sums (see above): the longest
-// slice's products plus the S slice additions of pass 2.
-__device__ __forceinline__ double screen_depth(int d, int S) {
-  const int chunks = d / 64;
-  return (double)(((chunks + S - 1) / S) * 64 + S);
-}
 
 // ---- pass 1: partial approximate logits and |x||w| sums of one K slice.
 // A workgroup of 8 waves covers 64 tokens x 256 experts of one K slice.  K

@@ -8,6 +8,17 @@
 
 namespace moe {
 
+// Summation depth n of the screening pass's float32 sums (the MFMA pass of
+// route_screen.hip, which both screened routers use): K is cut into S slices
+// of whole 64-element stages, each slice sums its products in float32 in
+// whatever order the MFMA adds them, and the S slice sums are added in
+// float32: n <= the longest slice's products + S.  The error of such a sum is
+// at most n * u * sum |x_i w_i| (u the float32 unit roundoff).
+__device__ __forceinline__ double screen_depth(int d, int S) {
+  const int chunks = d / 64;
+  return (double)(((chunks + S - 1) / S) * 64 + S);
+}
+
 // Lane share of an exact dot product over one 8-element chunk: the products
 // of bf16 values are exact in float32, each is widened and added in float64.
 // acc[q] takes elements 2q and 2q+1 (four independent chains).
