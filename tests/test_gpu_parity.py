@@ -261,6 +261,8 @@ def test_graph_capture_replays_any_k():
     (48, 4, 2176, 2176, 2, 2176),    # K % 256 = 128 (2 x 2 stream waves) and long K (deep stream pipeline)
     (200, 16, 512, 256, 8, 256),     # 128-row GEMM tiles: 256-column gate/up, 512-column down, fused shared expert
     (90, 8, 768, 512, 6, 0),         # 128-row GEMM tiles: 256-column gate/up and down (d % 512 != 0)
+    (8, 2, 128, 128, 1, 128),        # fused shared expert, fewer tiles than XCDs in both problems of a launch
+    (130, 3, 256, 256, 2, 256),      # fused shared expert: two shared row tiles, a handful of routed ones
 ])
 def test_ffn_paths_bf16(path, T, E, d, I, kmax, Is):
     """Both FFN paths compute the same function on the same routing."""
