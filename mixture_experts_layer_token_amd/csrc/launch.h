@@ -67,6 +67,20 @@ hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int
                           int bound, int4* blocks, hipStream_t st);
 
 // ffn_stream.hip -- weight-streaming grouped FFN.
+// A second, dense problem of the same N and K that a routed FFN launch (either
+// path) can carry: rows [0, rows) of `in` (no row map) against weights w0 / w1
+// into `out` -- the always-on shared expert.  In the grouped GEMM its tiles
+// come after the routed ones in each XCD's range (compute-bound tiles that
+// fill the CUs the end of the weight stream leaves idle); in the streaming
+// kernel its blocks come first (they are that launch's longest items).
+struct GemmSecond {
+  const void* in = nullptr;
+  const void* w0 = nullptr;
+  const void* w1 = nullptr;
+  void* out = nullptr;
+  int rows = 0;
+};
+
 //  gate/up: H[r] = SiLU(in[src(r)] . wg[g]^T) * (in[src(r)] . wu[g]^T), N = I, K = d
 //  down:    Y[r] = H[r] . wd[g]^T,                                     N = d, K = I
 // Work: the row-block table `blocks` (RB = stream_row_block(), `bound` entries)
@@ -77,27 +91,17 @@ hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int
 int stream_row_block();
 hipError_t launch_ffn_gateup_stream(int dtype, const void* in, const int32_t* row_map, const void* wg,
                                     const void* wu, const int4* blocks, int bound, int dense_rows, void* h, int N,
-                                    int K, int blocked, hipStream_t st);
+                                    int K, int blocked, hipStream_t st, const GemmSecond& sec = GemmSecond{});
 hipError_t launch_ffn_down_stream(int dtype, const void* h, const int32_t* row_map, const void* wd,
                                   const int4* blocks, int bound, int dense_rows, void* y, int N, int K, int blocked,
-                                  hipStream_t st);
+                                  hipStream_t st, const GemmSecond& sec = GemmSecond{});
 
 // ffn_gemm.hip -- grouped-GEMM FFN (bf16): same semantics as the streaming
 // kernels, over the row-block table with RB = gemm_row_block(rows_hint) (`bound`
 // entries + count; blocks == nullptr: one dense group of dense_rows rows).
 // rows_hint (an estimate of rows per group, from the shape only) picks the
-// tile height.  N must be a multiple of 128 and K of 64.
-// `sec` optionally adds a second, dense problem of the same N and K to the
-// launch: rows [0, sec.rows) of sec.in (no row map) against weights
-// sec.w0 / sec.w1 into sec.out -- the always-on shared expert, whose
-// compute-bound tiles then interleave with the grouped, weight-streaming ones.
-struct GemmSecond {
-  const void* in = nullptr;
-  const void* w0 = nullptr;
-  const void* w1 = nullptr;
-  void* out = nullptr;
-  int rows = 0;
-};
+// tile height.  N must be a multiple of 128 and K of 64.  `sec`: the second,
+// dense problem above.
 int gemm_row_block(int rows_hint);
 hipError_t launch_ffn_gateup_gemm(const void* in, const int32_t* row_map, const void* wg, const void* wu,
                                   const int4* blocks, int bound, int dense_rows, int rows_hint, void* h, int N,

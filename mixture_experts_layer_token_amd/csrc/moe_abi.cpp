@@ -250,8 +250,10 @@ bool shared_gemm(const moe_desc& d) {
 // The shared expert runs inside the routed grouped-GEMM launches (its row
 // tiles interleaved with the routed ones) when both take the GEMM path and
 // its intermediate size equals the routed one.
+// The shared expert rides in the routed FFN launches (as their last tiles)
+// when it is as wide as a routed expert and both take the same path.
 bool fused_shared(const moe_desc& d) {
-  return d.I_shared > 0 && d.I_shared == d.I && routed_gemm(d) && shared_gemm(d);
+  return d.I_shared > 0 && d.I_shared == d.I && routed_gemm(d) == shared_gemm(d);
 }
 
 // ---- stage bodies (arguments already validated) ----
@@ -292,7 +294,7 @@ moe_status do_gateup(const moe_desc& d, const void* x, const void* wg, const voi
         launch_ffn_gateup_gemm(x, perm_tok, wg, wu, fw.blocks, fw.bound, 0, rows_hint(d), h, d.I, d.d, d.weight_layout, st,
                                sec));
   return launched(launch_ffn_gateup_stream(d.dtype, x, perm_tok, wg, wu, fw.blocks, fw.bound, 0, h, d.I, d.d,
-                                           d.weight_layout, st));
+                                           d.weight_layout, st, sec));
 }
 
 // `row_map`: the h row of each permuted row (NULL: row p reads h row p).
@@ -304,7 +306,8 @@ moe_status do_down(const moe_desc& d, const void* h, const void* wd, const int32
   if (routed_gemm(d))
     return launched(launch_ffn_down_gemm(h, row_map, wd, fw.blocks, fw.bound, 0, rows_hint(d), y, d.d, d.I,
                                               d.weight_layout, st, sec));
-  return launched(launch_ffn_down_stream(d.dtype, h, row_map, wd, fw.blocks, fw.bound, 0, y, d.d, d.I, d.weight_layout, st));
+  return launched(launch_ffn_down_stream(d.dtype, h, row_map, wd, fw.blocks, fw.bound, 0, y, d.d, d.I, d.weight_layout, st,
+                                         sec));
 }
 
 moe_status do_shared(const moe_desc& d, const void* x, const void* sg, const void* su, const void* sd, void* h_sh,
