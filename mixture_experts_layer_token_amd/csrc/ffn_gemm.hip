@@ -113,13 +113,15 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   constexpr int LDS_BYTES = (EPI > 0 && BM * EPITCH > RING) ? BM * EPITCH : RING;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
-  // ---- which (row block, row tile, N tile) this workgroup owns.  The tiles
-  // of the second, dense problem (rows_s > 0: an always-on expert over rows
-  // [0, rows_s) with weights w0s/w1s) come after the grouped problem's in
-  // every XCD's range, so these compute-bound tiles take the CUs that the end
-  // of the weight stream leaves idle (256 experts x 96 rows, d = 7168, with a
-  // 4,096-row shared expert: 4.46 ms per layer against 4.50-4.54 ms with the
-  // dense tiles spread evenly through the grouped ones). ----
+  // ---- which (row block, row tile, N tile) this workgroup owns.  In every
+  // XCD's range the tiles of the second, dense problem (rows_s > 0: an
+  // always-on expert over rows [0, rows_s) with weights w0s/w1s) come after
+  // the grouped problem's in the gate/up launch, so these compute-bound tiles
+  // (K = d) take the CUs that the end of the weight stream leaves idle (256
+  // experts x 96 rows, d = 7168, a 4,096-row shared expert: 4.46 ms per layer
+  // against 4.50-4.54 ms with the dense tiles spread evenly through the
+  // grouped ones), and before them in the down launch, whose dense tiles are
+  // short (K = I): 4.350 against 4.418 ms (three interleaved pairs). ----
   const int nN = N / BNW;
   const int r_mt = blocks ? blocks[bound].x : (dense_rows + BM - 1) / BM;
   const int s_mt = SEC ? (rows_s + BM - 1) / BM : 0;
@@ -128,8 +130,9 @@ __global__ __launch_bounds__(64 * WM * WN) void ffn_gemm_kernel(
   const int R = r_mt * nN, S2 = s_mt * nN, Rp = (R + 7) >> 3, Sp = (S2 + 7) >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   if (slot >= Rp + Sp) return;
-  const bool second = SEC && slot >= Rp;
-  const int li = second ? xcd * Sp + (slot - Rp) : xcd * Rp + slot;
+  constexpr bool SFIRST = SEC && MODE == 1;  // the down projection's dense tiles lead its ranges
+  const bool second = SEC && (SFIRST ? slot < Sp : slot >= Rp);
+  const int li = second ? xcd * Sp + (SFIRST ? slot : slot - Rp) : xcd * Rp + (SFIRST ? slot - Sp : slot);
   if (li >= (second ? S2 : R)) return;
   const int mk = li / nN, nt = li - mk * nN;  // row tile within its problem, N tile
   const int rb = mk;
