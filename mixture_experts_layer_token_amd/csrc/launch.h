@@ -70,8 +70,9 @@ hipError_t launch_permute(const int32_t* tok_off, const int32_t* ids, int T, int
 // A second, dense problem of the same N and K that a routed FFN launch (either
 // path) can carry: rows [0, rows) of `in` (no row map) against weights w0 / w1
 // into `out` -- the always-on shared expert.  In the grouped GEMM its tiles
-// come after the routed ones in each XCD's range (compute-bound tiles that
-// fill the CUs the end of the weight stream leaves idle); in the streaming
+// come after the routed ones in each XCD's range in the gate/up launch
+// (compute-bound tiles that fill the CUs the end of the weight stream leaves
+// idle) and before them in the down launch (short tiles); in the streaming
 // kernel its blocks come first (they are that launch's longest items).
 struct GemmSecond {
   const void* in = nullptr;
