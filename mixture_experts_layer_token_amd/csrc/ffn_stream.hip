@@ -247,7 +247,8 @@ __device__ __forceinline__ void stream_block(const T* __restrict__ in, const int
 // `ring` holds 3 stages of 16 KB: [weights 64 x 128 B][activations 64 x 128 B].
 constexpr int SHARED_STAGE_BYTES = 2 * 64 * 128;
 // VAR bits 2-3: extra ring stages (3 + n stages, n + 2 steps ahead).
-template <int VAR> constexpr int shared_stages() { return 3 + ((VAR >> 2) & 3); }
+// VAR bit 4: a two-stage ring instead (one step ahead; 32 KB of LDS).
+template <int VAR> constexpr int shared_stages() { return (VAR & 16) ? 2 : 3 + ((VAR >> 2) & 3); }
 
 // VAR bit 1: the weight DMA carries the non-temporal hint (the weights are
 // read once per layer).
@@ -536,8 +537,13 @@ int stream_row_block() { return S_ROWS; }
 // 36 vs 43 us).  A down projection of mid-size K (DSV3-shaped, K = 2048)
 // gains from a ring one stage deeper (1049 -> 1031 us), which the others do
 // not (Mixtral-shaped down 152 vs 154 us, Qwen3-shaped down 47 vs 49 us,
-// gate/up 305 vs 333 us: two workgroups per CU instead of three).
+// gate/up 305 vs 333 us: two workgroups per CU instead of three).  The other
+// way, a two-stage ring (32 KB: five workgroups per CU instead of three) wins
+// where both N and K are at most 2048, i.e. many short items: Qwen3-shaped
+// gate/up 76 -> 71 us, layer 0.1605 -> 0.1578 ms; it loses on the long
+// streams (Mixtral-shaped layer +10 %, DSV3-shaped decode +1 %).
 static int stream_var(int MODE, int N, int K, int blocked) {
+  if (blocked && N <= 2048 && K <= 2048) return 19;
   if (blocked) return MODE == 0 ? 3 : ((K > 1024 && K < 8192) ? 7 : 3);
   if (MODE == 0) return N >= 8192 ? 0 : 3;
   if (K >= 8192) return 3;
@@ -554,6 +560,9 @@ static hipError_t stream_pd(const T* x, const int32_t* row_map, const T* w0, con
       case 3:
         return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, PD, true, 1, 3>(x, row_map, w0, w1, blocks,
                                                                                      nblk, dense_rows, out, N, K, blocked, st, sec);
+      case 19:
+        return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, PD, true, 1, 19>(x, row_map, w0, w1, blocks,
+                                                                                      nblk, dense_rows, out, N, K, blocked, st, sec);
       case 7:
         return launch_stream_variant<T, MODE, KC, WN, WK, S_SMT, S_TPW, PD, true, 1, 7>(x, row_map, w0, w1, blocks,
                                                                                      nblk, dense_rows, out, N, K, blocked, st, sec);
