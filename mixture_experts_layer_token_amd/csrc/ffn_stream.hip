@@ -539,11 +539,13 @@ int stream_row_block() { return S_ROWS; }
 // not (Mixtral-shaped down 152 vs 154 us, Qwen3-shaped down 47 vs 49 us,
 // gate/up 305 vs 333 us: two workgroups per CU instead of three).  The other
 // way, a two-stage ring (32 KB: five workgroups per CU instead of three) wins
-// where both N and K are at most 2048, i.e. many short items: Qwen3-shaped
-// gate/up 76 -> 71 us, layer 0.1605 -> 0.1578 ms; it loses on the long
-// streams (Mixtral-shaped layer +10 %, DSV3-shaped decode +1 %).
+// for a gate/up pair where both N and K are at most 2048, i.e. many short
+// items: Qwen3-shaped gate/up 76 -> 71 us, layer 0.1605 -> 0.1578 ms, and
+// 0.1547 ms with its down projection (K = 768) left on three stages; it
+// loses on the long streams (Mixtral-shaped layer +10 %, DSV3-shaped decode
+// +1 %).
 static int stream_var(int MODE, int N, int K, int blocked) {
-  if (blocked && N <= 2048 && K <= 2048) return 19;
+  if (blocked && MODE == 0 && N <= 2048 && K <= 2048) return 19;
   if (blocked) return MODE == 0 ? 3 : ((K > 1024 && K < 8192) ? 7 : 3);
   if (MODE == 0) return N >= 8192 ? 0 : 3;
   if (K >= 8192) return 3;
