@@ -114,9 +114,11 @@ hipError_t launch_ffn_down_gemm(const void* h, const int32_t* row_map, const voi
 // layout.hip -- row-major -> blocked copy of G [N][K] matrices (w_offset).
 hipError_t launch_pack_weights(int dtype, long long G, int N, int K, const void* src, void* dst, hipStream_t st);
 
-// combine.hip
+// combine.hip -- k_max (the largest budget) sets how many rows a thread
+// requests at once.
 hipError_t launch_combine(int dtype, const void* y, const void* y_shared, const int32_t* tok_off,
-                          const float* wts, const int32_t* inv_perm, void* out, int T, int d, hipStream_t st);
+                          const float* wts, const int32_t* inv_perm, void* out, int T, int d, int k_max,
+                          hipStream_t st);
 
 // fold.hip -- expert folding of the routing metadata.  mode 0: keep at most
 // `budget` routes per token; mode 1: keep a pool of `budget` experts (needs

@@ -328,7 +328,7 @@ moe_status do_shared(const moe_desc& d, const void* x, const void* sg, const voi
 
 moe_status do_combine(const moe_desc& d, const void* y, const void* y_sh, const int32_t* tok_off, const float* w,
                       const int32_t* inv_perm, void* out, hipStream_t st) {
-  return launched(launch_combine(d.dtype, y, y_sh, tok_off, w, inv_perm, out, d.T, d.d, st));
+  return launched(launch_combine(d.dtype, y, y_sh, tok_off, w, inv_perm, out, d.T, d.d, d.k_max, st));
 }
 
 }  // namespace
